@@ -1,0 +1,371 @@
+"""Pins for the CPU oracle: each step is checked against something other than
+itself -- a closed form, an invariant, a textbook special case or brute force.
+
+Sources: IceCache paper page (Figure 2 caption steps (1)-(3), Figure 3
+caption), IceCache blog page (technical details: one tree and one P-DCI search
+per head; the tree is updated without a rebuild).
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from sparse_attention_dci_amd import workloads as W
+
+SCALE = float(1 << 29)
+
+
+def _rand_dirs(rng, mL, d, dtype="bf16"):
+    import torch
+    u = rng.standard_normal((mL, d + 1))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    t = torch.from_numpy(u).to(W.torch_dtype(dtype)).float().numpy()
+    return np.ascontiguousarray(t)
+
+
+def _mixture(n, d, clusters, seed, g=1, dtype="bf16"):
+    K, V, q, _ = W.stream(n, d, clusters, g, seed, dtype)
+    return K.float().numpy(), V.float().numpy(), q.float().numpy()
+
+
+# ------------------------------------------------------------------ transform
+
+def test_transform_unit_norm_and_mips_order(ora):
+    K, _, q = _mixture(2000, 64, 16, 11)
+    c = ora.norm_bound(K)
+    kt = ora.transform(K, c)
+    # |T_K(k)| = 1 for every key no longer than c (c is rounded to fp32, so allow
+    # the rounding of c itself)
+    assert np.max(np.abs(np.linalg.norm(kt, axis=1) - 1.0)) < 1e-6
+    # nearest neighbour of T_Q(q) under T_K == largest inner product with q
+    qv = q[0].astype(np.float64)
+    tq = np.concatenate([qv / np.linalg.norm(qv), [0.0]])
+    dist = np.linalg.norm(kt - tq, axis=1)
+    ip = K.astype(np.float64) @ qv
+    assert np.array_equal(np.argsort(dist, kind="stable")[:200],
+                          np.argsort(-ip, kind="stable")[:200])
+
+
+def test_norm_bound_is_max_norm(ora):
+    K, _, _ = _mixture(500, 128, 8, 12)
+    c = ora.norm_bound(K)
+    assert c == np.float32(np.linalg.norm(K.astype(np.float64), axis=1).max())
+    assert ora.norm_bound(np.zeros((4, 128), np.float32)) == 1.0
+    assert ora.norm_bound(np.zeros((0, 128), np.float32)) == 1.0
+
+
+# ------------------------------------------------------------------ projection
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_projection_is_transform_dot_direction(ora, dtype):
+    rng = np.random.default_rng(5)
+    K, _, _ = _mixture(1500, 128, 32, 13, dtype=dtype)
+    U = _rand_dirs(rng, 12, 128, dtype)
+    c = ora.norm_bound(K)
+    codes, cell = ora.project(K, U, c, 6)
+    kt = ora.transform(K, c)
+    exact = (kt @ U.astype(np.float64).T) * SCALE
+    assert np.max(np.abs(codes - exact)) <= 0.5 + 1e-3
+    # cell bit t = sign of the raw projection <k, u_t[:d]>
+    r = K.astype(np.float64) @ U[:, :128].astype(np.float64).T
+    bits = (r[:, :6] >= 0).astype(np.uint32) << np.arange(6, dtype=np.uint32)
+    assert np.array_equal(cell, bits.sum(1).astype(np.uint32))
+
+
+def test_projection_special_keys(ora):
+    """Closed forms: the zero key maps to [0, 1], a key c*e_j to [e_j, 0]."""
+    rng = np.random.default_rng(6)
+    d = 128
+    U = _rand_dirs(rng, 8, d)
+    c = 4.0
+    K = np.zeros((1 + d, d), np.float32)
+    for j in range(d):
+        K[1 + j, j] = c
+    codes, _ = ora.project(K, U, c, 3)
+    assert np.array_equal(codes[0], np.rint(U[:, d].astype(np.float64) * SCALE).astype(np.int32))
+    for j in range(d):
+        assert np.array_equal(codes[1 + j], np.rint(U[:, j].astype(np.float64) * SCALE))
+    # a key longer than c (late insert) clamps the extra coordinate at zero
+    Kl = np.zeros((1, d), np.float32)
+    Kl[0, 0] = 2 * c
+    codes, _ = ora.project(Kl, U, c, 3)
+    assert np.array_equal(codes[0], np.rint(2.0 * U[:, 0].astype(np.float64) * SCALE))
+
+
+def test_projection_saturates(ora):
+    d = 4
+    U = np.zeros((1, d + 1), np.float32)
+    U[0, 0] = 1.0
+    K = np.array([[9.0, 0, 0, 0], [-9.0, 0, 0, 0]], np.float32)
+    codes, _ = ora.project(K, U, 1.0, 1)
+    assert codes[0, 0] == (1 << 30) - 1 and codes[1, 0] == -((1 << 30) - 1)
+
+
+# ------------------------------------------------------------------ query prep
+
+def test_query_prep_is_normalised_mean_projection(ora):
+    rng = np.random.default_rng(7)
+    U = _rand_dirs(rng, 16, 128)
+    q = rng.standard_normal((4, 128)).astype(np.float32)
+    qkv, qcode = ora.query_prep(q, U)
+    assert np.allclose(qkv, q.astype(np.float64).mean(0), rtol=0, atol=1e-6)
+    # the mean is kept in fp32; its projection after normalisation is exact to
+    # the code's rounding
+    qm = qkv.astype(np.float64)
+    exact = (qm / np.linalg.norm(qm)) @ U[:, :128].astype(np.float64).T * SCALE
+    assert np.max(np.abs(qcode - exact)) <= 0.5 + 1e-3
+    # T_Q ignores the query's scale (power-of-two scaling is exact)
+    _, qcode2 = ora.query_prep(4.0 * q, U)
+    assert np.array_equal(qcode, qcode2)
+    # zero query projects to the origin
+    _, qz = ora.query_prep(np.zeros((2, 128), np.float32), U)
+    assert not qz.any()
+
+
+# ------------------------------------------------------------------ sorted lists
+
+def test_sorted_lists_match_lexsort(ora):
+    rng = np.random.default_rng(8)
+    codes = rng.integers(-50, 50, size=(3000, 5)).astype(np.int32)  # many exact ties
+    for t in range(5):
+        lc, li = ora.sort_list(codes, t)
+        order = np.lexsort((np.arange(3000), codes[:, t]))
+        assert np.array_equal(li, order) and np.array_equal(lc, codes[order, t])
+        assert np.array_equal(np.sort(li), np.arange(3000))
+
+
+# ------------------------------------------------------------------ tree / pages
+
+def _check_tree(st, n):
+    p = st.prm.p
+    page_of, slot_of = st.page_of[:n], st.slot_of[:n]
+    tok = st.page_tokens[:st.npages]
+    plen = st.page_len[:st.npages]
+    # every token exactly once, consistent both ways
+    flat = tok[tok >= 0]
+    assert np.array_equal(np.sort(flat), np.arange(n))
+    assert np.array_equal(tok[page_of, slot_of], np.arange(n))
+    assert np.all((plen >= 1) & (plen <= p))
+    assert np.array_equal((tok >= 0).sum(1), plen)
+    # a page holds one cell's tokens, in token order, in slots 0..len-1
+    for g in range(st.npages):
+        ts = tok[g, :plen[g]]
+        assert np.all(st.cell[ts] == st.page_cell[g])
+        assert np.all(np.diff(ts) > 0)
+    # page ids rise with the page's first token
+    assert np.all(np.diff(tok[:, 0]) > 0)
+    # independent construction: per cell, chunk the token-ordered members by p
+    pages = []
+    for cval in np.unique(st.cell[:n]):
+        members = np.nonzero(st.cell[:n] == cval)[0]
+        for s in range(0, len(members), p):
+            pages.append(tuple(members[s:s + p]))
+    pages.sort(key=lambda t: t[0])
+    assert len(pages) == st.npages
+    for g, mem in enumerate(pages):
+        assert tuple(tok[g, :plen[g]]) == mem
+
+
+@pytest.mark.parametrize("p", [8, 16, 32])
+def test_tree_invariants(ora, p):
+    K, V, _ = _mixture(3000, 128, 24, 21)
+    U = _rand_dirs(np.random.default_rng(9), 8, 128)
+    prm = ora.Params(d=128, p=p, k=4 * p, m=4, L=2)
+    st = ora.OracleStream(prm, K, V, U)
+    assert st.D == ora.tree_depth(3000, p, 8)
+    _check_tree(st, 3000)
+    # each cell has at most one partial page and it is the cell's last page
+    for cval in np.unique(st.page_cell[:st.npages]):
+        gs = np.nonzero(st.page_cell[:st.npages] == cval)[0]
+        assert np.all(st.page_len[gs[:-1]] == p)
+
+
+def test_tree_depth_reading(ora):
+    # about four pages per cell: these are the depths of the five workloads
+    assert ora.tree_depth(4096, 16, 8) == 6
+    assert ora.tree_depth(36864, 16, 32) == 9
+    assert ora.tree_depth(131072, 16, 40) == 11
+    assert ora.tree_depth(262144, 32, 72) == 11
+    assert ora.tree_depth(0, 16, 8) == 1
+    assert ora.tree_depth(10 ** 9, 16, 64) == ora.MAX_TREE_DEPTH
+    assert ora.tree_depth(4096, 16, 4) == 4  # never deeper than the directions
+
+
+# ------------------------------------------------------------------ insert == rebuild
+
+def test_insert_equals_rebuild(ora):
+    n0, t = 1200, 70
+    K, V, q = _mixture(n0 + t, 128, 12, 31, g=4)
+    U = _rand_dirs(np.random.default_rng(10), 12, 128)
+    prm = ora.Params(d=128, p=16, k=64, m=4, L=3, g=4)
+    a = ora.OracleStream(prm, K[:n0], V[:n0], U, n_cap=n0 + t)
+    for i in range(n0, n0 + t):
+        a.insert(K[i], V[i])
+    prm_b = ora.Params(**{**prm.__dict__, "c": a.c, "D": a.D})
+    b = ora.OracleStream(prm_b, K, V, U, n_cap=n0 + t)
+    n = n0 + t
+    assert np.array_equal(a.codes[:n], b.codes[:n]) and np.array_equal(a.cell[:n], b.cell[:n])
+    assert np.array_equal(a.lcode, b.lcode) and np.array_equal(a.lid, b.lid)
+    assert a.npages == b.npages
+    for f in ("page_of", "slot_of", "page_len", "page_cell", "page_tokens"):
+        assert np.array_equal(getattr(a, f), getattr(b, f)), f
+    _check_tree(a, n)
+    ra, rb = a.query(q), b.query(q)
+    for f in ("C", "topk", "page_ids"):
+        assert np.array_equal(ra[f], rb[f]), f
+    assert np.array_equal(a.attend(q, ra["page_ids"]), b.attend(q, rb["page_ids"]))
+
+
+# ------------------------------------------------------------------ P-DCI
+
+def _random_case(rng, n, m, L, spread):
+    mL = m * L
+    codes = rng.integers(-spread, spread + 1, size=(n, mL)).astype(np.int32)
+    qcode = rng.integers(-spread, spread + 1, size=mL).astype(np.int32)
+    return codes, qcode
+
+
+def test_pdci_literal_equals_closed_form(ora):
+    rng = np.random.default_rng(41)
+    cases = 0
+    for trial in range(300):
+        n = int(rng.integers(1, 60))
+        m = int(rng.integers(1, 5))
+        spread = int(rng.choice([2, 5, 1000, 10 ** 8]))  # small spreads force exact ties
+        codes, qcode = _random_case(rng, n, m, 1, spread)
+        k0 = int(rng.integers(0, n + 2))
+        k1 = int(rng.choice([0, int(rng.integers(1, m * n + 2))]))
+        lists = [ora.sort_list(codes, j) for j in range(m)]
+        lc = np.stack([x[0] for x in lists])
+        li = np.stack([x[1] for x in lists])
+        s_lit, v_lit = ora.pdci_literal(lc, li, m, qcode, k0, k1)
+        s_cf, v_cf = ora.pdci_closed(codes, m, 0, qcode, k0, k1)
+        assert np.array_equal(s_lit, s_cf), (trial, n, m, spread, k0, k1)
+        assert v_lit == v_cf, (trial, n, m, spread, k0, k1)
+        if k1 > 0:
+            assert v_lit <= k1
+        cases += 1
+    assert cases == 300
+
+
+def test_pdci_one_list_is_textbook_knn(ora):
+    """m = L = 1: the first k0 candidates are the k0 nearest codes (ties by token)."""
+    rng = np.random.default_rng(42)
+    for _ in range(50):
+        n = int(rng.integers(1, 200))
+        codes, qcode = _random_case(rng, n, 1, 1, int(rng.choice([3, 10 ** 6])))
+        k0 = int(rng.integers(1, n + 1))
+        lc, li = ora.sort_list(codes, 0)
+        s, v = ora.pdci_literal(lc[None], li[None], 1, qcode, k0, 0)
+        dist = np.abs(codes[:, 0].astype(np.int64) - qcode[0])
+        expect = np.lexsort((np.arange(n), dist))[:k0]
+        assert np.array_equal(s, expect)
+        assert v == k0  # one visit per candidate with a single list
+
+
+def test_pdci_limits(ora):
+    rng = np.random.default_rng(43)
+    codes, qcode = _random_case(rng, 100, 3, 1, 10 ** 6)
+    lists = [ora.sort_list(codes, j) for j in range(3)]
+    lc = np.stack([x[0] for x in lists])
+    li = np.stack([x[1] for x in lists])
+    s, v = ora.pdci_literal(lc, li, 3, qcode, 0, 0)
+    assert len(s) == 0 and v == 0
+    s, v = ora.pdci_literal(lc, li, 3, qcode, 1000, 0)  # k0 > n: every entry visited
+    assert sorted(s) == list(range(100)) and v == 300
+    s, v = ora.pdci_literal(lc, li, 3, qcode, 1000, 2)  # two visits complete nobody
+    assert len(s) == 0 and v == 2
+
+
+def _exact_scores(K, q):
+    qf = [Fraction(float(x)) for x in q]
+    return [sum(a * Fraction(float(b)) for a, b in zip(qf, row)) for row in K]
+
+
+def test_unbounded_pdci_gives_exact_topk(ora):
+    """With an unbounded candidate budget the candidates are every token, so the
+    reranked top-k is the brute-force exact top-k (the pages' TOP-k baseline)."""
+    K, V, q = _mixture(300, 16, 6, 51, g=2)
+    U = _rand_dirs(np.random.default_rng(11), 6, 16)
+    prm = ora.Params(d=16, p=8, k=40, m=3, L=2, g=2, k0=10 ** 6)
+    st = ora.OracleStream(prm, K, V, U)
+    r = st.query(q)
+    assert np.array_equal(r["C"], np.arange(300))
+    qkv = r["qkv"]
+    ex = _exact_scores(K, qkv)
+    order = sorted(range(300), key=lambda i: (-ex[i], i))
+    assert list(r["topk"]) == order[:40]
+    assert list(r["ranked"]) == order
+
+
+def test_page_selection_under_exact_ranking(ora):
+    """With every token a candidate, the pages come out in the order of their
+    best member (largest score, then smallest token)."""
+    K, V, q = _mixture(400, 16, 5, 52, g=1)
+    U = _rand_dirs(np.random.default_rng(12), 4, 16)
+    prm = ora.Params(d=16, p=8, k=48, m=2, L=2, g=1, k0=10 ** 6)
+    st = ora.OracleStream(prm, K, V, U)
+    r = st.query(q)
+    ex = _exact_scores(K, r["qkv"])
+    best = {}
+    for i in range(400):
+        g = int(st.page_of[i])
+        key = (-ex[i], i)
+        if g not in best or key < best[g]:
+            best[g] = key
+    expect = sorted(best, key=lambda g: best[g])[:prm.P]
+    assert list(r["page_ids"]) == expect
+
+
+# ------------------------------------------------------------------ attention
+
+def test_attention_all_pages_is_full_attention(ora):
+    K, V, q = _mixture(700, 128, 9, 61, g=4)
+    U = _rand_dirs(np.random.default_rng(13), 8, 128)
+    prm = ora.Params(d=128, p=16, k=64, m=4, L=2, g=4)
+    st = ora.OracleStream(prm, K, V, U)
+    out = st.attend(q, np.arange(st.npages, dtype=np.int32))
+    z = q.astype(np.float64) @ K.astype(np.float64).T / np.sqrt(128.0)
+    w = np.exp(z - z.max(1, keepdims=True))
+    full = (w / w.sum(1, keepdims=True)) @ V.astype(np.float64)
+    assert np.max(np.abs(out - full)) < 1e-12
+
+
+def test_attention_degenerate_cases(ora):
+    d, p = 8, 4
+    rng = np.random.default_rng(14)
+    pk = rng.standard_normal((3, p, d)).astype(np.float32)
+    pv = rng.standard_normal((3, p, d)).astype(np.float32)
+    q = rng.standard_normal((2, d)).astype(np.float32)
+    # one token: the output is its value
+    out = ora.attention(q, pk, pv, p, np.array([1], np.int32), np.array([4, 1, 4], np.int32))
+    assert np.allclose(out, np.broadcast_to(pv[1, 0], (2, d)), atol=0, rtol=1e-15)
+    # equal logits (zero query): the mean of the values
+    out = ora.attention(np.zeros((1, d), np.float32), pk, pv, p, np.array([0, 2], np.int32),
+                        np.array([4, 1, 4], np.int32))
+    assert np.allclose(out[0], np.concatenate([pv[0], pv[2]]).astype(np.float64).mean(0),
+                       atol=1e-14)
+    # no page: zero output
+    out = ora.attention(q, pk, pv, p, np.zeros(0, np.int32), np.array([4, 1, 4], np.int32))
+    assert not out.any()
+
+
+# ------------------------------------------------------------------ needle
+
+def test_needle_is_retrieved(ora):
+    """A planted 16-token cluster along the query direction (passkey retrieval,
+    IceCache paper page, Figure 6) is in the brute-force top-16 and every one of
+    its tokens lands in a selected page."""
+    n, g = 8192, 4
+    K, V, q, p0 = W.stream(n, 128, 64, g, 71, "bf16", needle=16)
+    K, V, q = K.float().numpy(), V.float().numpy(), q.float().numpy()
+    U = _rand_dirs(np.random.default_rng(15), 40, 128)
+    prm = ora.Params(d=128, p=16, k=256, m=10, L=4, g=g)
+    st = ora.OracleStream(prm, K, V, U)
+    r = st.query(q)
+    qm = q.astype(np.float64).mean(0)
+    top16 = set(np.argsort(-(K.astype(np.float64) @ qm))[:16])
+    needle = set(range(p0, p0 + 16))
+    assert needle == top16
+    sel = set(r["page_ids"].tolist())
+    assert all(int(st.page_of[i]) in sel for i in needle)
