@@ -1,0 +1,244 @@
+"""Decode-step benchmark of the IceCache hot path on one MI355X.
+
+Workload: one Llama-3.1-8B-shaped layer at 36,864 tokens of context (8 KV
+heads, 32 query heads, head_dim 128, bf16 KV, page 16, budget 256 tokens,
+DCI m=8, L=4), synthetic mixture keys.  A decode step is the whole decode-time
+path on that layer: insert the new token's key/value into every head's index,
+query (P-DCI candidates, exact rerank, page selection) and paged sparse
+attention.  The prefill build of the index is timed separately (build_ms).
+
+Eight copies of the layer (eight "layers" with their own inputs, ~2.3 GB of
+index) are built and the steps rotate over them, so each step finds its
+index cold in the 256 MB last-level cache, as in a real 32-layer decode.
+
+Prints one JSON line (the last line of stdout).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+WORKLOAD = "llama8b_layer_36k"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_attention_dci_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".cpp", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w, kernel: str, ntok: int, n_cand: float, attended: float) -> float:
+    """Bytes the decode path has to move per launch of `kernel` for the whole layer
+    (S streams): the per-unit figures times the units one launch processes."""
+    S, d, mL, L, g = w.streams, w.d, w.mL, w.L, w.g
+    elem = 2 if w.dtype == "bf16" else 4
+    if kernel == "qscan":      # every token's m*L projection codes, 4 B each
+        return S * ntok * mL * 4.0
+    if kernel == "qcollect":   # every token's L composite distances + candidate key rows
+        return S * (ntok * L * 4.0 + n_cand * d * elem)
+    if kernel == "attn_part":  # K and V rows of every attended token + queries
+        return S * (attended * 2 * d * elem + g * d * elem)
+    if kernel == "insert":     # new k, v in; pool rows, codes and list entries out
+        return S * (4.0 * d * elem + mL * 12.0)
+    return 0.0
+
+
+def cpu_baseline(w, K, V, q, U, k_new, v_new, reps: int):
+    """The oracle, as it stands, on one layer's decode step for every stream."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
+    import oracle
+    oracle.build()
+    prm = oracle.Params(d=w.d, p=w.p, k=w.k, m=w.m, L=w.L, g=w.g)
+    Kn, Vn, qn, Un = (t.float().cpu().numpy() for t in (K, V, q, U))
+    kn, vn = k_new.float().cpu().numpy(), v_new.float().cpu().numpy()
+    threads = min(w.streams, os.cpu_count() or 1)
+
+    def build(s):
+        return oracle.OracleStream(prm, Kn[s], Vn[s], Un, n_cap=w.n + reps)
+
+    with cf.ThreadPoolExecutor(threads) as ex:
+        streams = list(ex.map(build, range(w.streams)))
+
+    def step(s):
+        st = streams[s]
+        st.insert(kn[s], vn[s])
+        qs = np.ascontiguousarray(qn[s * w.g:(s + 1) * w.g])
+        r = st.query(qs)
+        st.attend(qs, r["page_ids"])
+        return r
+
+    times = []
+    with cf.ThreadPoolExecutor(threads) as ex:
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            list(ex.map(step, range(w.streams)))
+            times.append(time.perf_counter() - t0)
+    return min(times) * 1e6, threads
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the streams of different layers and heads are independent, so a multi-GPU "
+              "run would shard whole layers with no exchange)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_attention_dci_amd import binding, workloads as W
+
+    w = W.WORKLOADS[WORKLOAD]
+    dev = torch.device("cuda:0")
+    R = args.layers
+    total_steps = args.warmup + 2 * args.steps
+    per_layer = (total_steps + R - 1) // R + 1
+    cap = w.n + per_layer
+
+    log(f"[bench] building {R} layers of {WORKLOAD}")
+    layers, build_ms = [], []
+    keep = None
+    for r in range(R):
+        K, V, q, U, _ = W.layer_inputs(w, layer=r, device=dev)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        idx = binding.Index(K, V, U, page_size=w.p, budget_k=w.k, m=w.m, L=w.L, gqa_group=w.g,
+                            capacity=cap)
+        e1.record()
+        torch.cuda.synchronize()
+        build_ms.append(e0.elapsed_time(e1))
+        idx.release_build_buffers()
+        layers.append((idx, q))
+        if r == 0:
+            keep = (K, V, q, U)
+        else:
+            del K, V
+    log(f"[bench] build ms per layer: {[round(x, 2) for x in build_ms]}")
+
+    steps_in = [W.step_inputs(w, layer=t % R, step=t, device=dev) for t in range(total_steps)]
+    outs = [(torch.empty(w.streams, w.k // w.p, dtype=torch.int32, device=dev),
+             torch.empty(w.streams, dtype=torch.int32, device=dev),
+             torch.empty(w.streams * w.g, w.d, dtype=torch.float32, device=dev))
+            for _ in range(R)]
+
+    def step(t):
+        r = t % R
+        idx, _ = layers[r]
+        k_new, v_new, q = steps_in[t]
+        pg, npg, out = outs[r]
+        idx.insert(k_new, v_new)
+        idx.query_pages(q, page_ids=pg, n_pages=npg)
+        idx.sparse_attn(q, pg, npg, out=out)
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    log("[bench] timing")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(args.warmup, args.warmup + args.steps):
+        step(t)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel durations, HIP events on the launch stream, a second pass
+    for idx, _ in layers:
+        idx.timing(True)
+    for t in range(args.warmup + args.steps, total_steps):
+        step(t)
+    torch.cuda.synchronize()
+    per_kernel = {}
+    for idx, _ in layers:
+        for name, (ms, cnt) in idx.timing_read().items():
+            a, b = per_kernel.get(name, (0.0, 0))
+            per_kernel[name] = (a + ms, b + cnt)
+        idx.timing(False)
+    avg_us = {k: 1e3 * ms / c for k, (ms, c) in per_kernel.items() if c}
+    log(f"[bench] per-kernel average us: { {k: round(v, 2) for k, v in avg_us.items()} }")
+    dominant = max(avg_us, key=avg_us.get)
+    ntok = w.n + per_layer // 2
+    n_cand = w.L * w.k * 0.9   # the union of the composites' k0 candidates, about L*k0
+    attended = float(w.k)
+    alg = algorithmic_bytes(w, dominant, ntok, n_cand, attended)
+    achieved = alg / (avg_us[dominant] * 1e-6) / 1e9
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as fh:
+            tr = json.load(fh)
+        if tr.get("source_hash") == kernel_source_hash() and dominant in tr.get("kernels", {}):
+            traffic = tr["kernels"][dominant]
+    roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": traffic, "avg_us": round(avg_us[dominant], 3),
+                "alg_bytes": int(alg)}
+    step_alg = sum(algorithmic_bytes(w, k, ntok, n_cand, attended)
+                   for k in ("insert", "qscan", "qcollect", "attn_part"))
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] oracle cpu baseline")
+        K, V, q, U = keep
+        k_new, v_new, _ = W.step_inputs(w, layer=0, step=10 ** 6, device=dev)
+        us, threads = cpu_baseline(w, K, V, q, U, k_new, v_new, args.cpu_reps)
+        cpu = {"value": round(us, 1), "unit": "us", "cores": threads, "kind": "oracle",
+               "sample": f"one decode step (insert + literal P-DCI query + rerank + page "
+                         f"selection + fp64 attention) of all {w.streams} KV heads of one "
+                         f"{w.n}-token layer, best of {args.cpu_reps}; oracle build untimed"}
+
+    res = {
+        "metric": "decode-step us (P-DCI query + sparse paged attn) @36k ctx; achieved HBM GB/s",
+        "value": round(ms_per_step * 1e3, 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32 codes + fp64 rerank + fp32 attention over bf16 KV",
+        "data": "synthetic (seeded Gaussian-mixture keys, N(0,1) values)",
+        "config": {"workload": WORKLOAD, "kv_heads": w.streams, "query_heads": w.streams * w.g,
+                   "context": w.n, "head_dim": w.d, "page_size": w.p, "budget_k": w.k,
+                   "m": w.m, "L": w.L, "layers_rotated": R,
+                   "step": "insert + query_pages + sparse_attn"},
+        "build_ms": round(sorted(build_ms)[len(build_ms) // 2], 3),
+        "step_alg_gbs": round(step_alg / (ms_per_step * 1e-3) / 1e9, 1),
+        "kernel_avg_us": {k: round(v, 3) for k, v in avg_us.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,198 @@
+/*
+ * ice.h -- C ABI of the IceCache decode hot path on AMD Instinct MI355X.
+ *
+ * IceCache (IceCache paper page, abstract and Figures 2-3) keeps each
+ * attention head's keys in a DCI-tree whose leaves are physical KV pages:
+ *   (1) prefill indexes the keys by similarity in a transformed key space;
+ *   (2) each decode step runs a tree search (prioritized DCI, one search per
+ *       head -- IceCache blog page, technical details) for the query's top-k
+ *       tokens;
+ *   (3) the pages holding those tokens are selected and every token in them
+ *       takes part in sparse attention with the query.
+ * The tree is updated in place as tokens arrive (blog page: no rebuild).
+ *
+ * Terms.  A "stream" is one KV head of one layer of one sequence; an index
+ * holds S streams of the same shape and each stream has its own tree, lists
+ * and pages.  All tensors are row-major.  "dtype" is the element type of K, V,
+ * the query and the directions: fp32 or bf16.
+ *
+ * Memory.  Every pointer named "device" is HIP device memory owned by the
+ * caller.  The library never allocates device memory: the index lives in the
+ * caller's workspace (size from ice_workspace_bytes, 256-byte aligned), and
+ * the build uses a caller scratch buffer (ice_build_scratch_bytes) that may be
+ * reused or freed once the build's stream work has finished.  The only host
+ * allocation is the small ice_index handle.
+ *
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
+ * stream).  Every call enqueues kernels and returns without synchronising.
+ * One index must be used from one stream at a time; calls on one index in
+ * stream order see each other's results.
+ *
+ * Errors.  Arguments and capacities are checked on the host before anything
+ * is enqueued; a call that fails a check returns a negative status and has no
+ * effect.  ICE_ERR_HIP reports a launch error (asynchronous faults surface on
+ * the caller's next synchronisation).  NaN/Inf inputs are outside the
+ * contract.  Keys longer than the stored norm bound c are allowed (see
+ * ice_insert).
+ */
+#ifndef ICE_H
+#define ICE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ICE_OK = 0,
+  ICE_ERR_INVALID_ARG = -1, /* a bad size, pointer or parameter */
+  ICE_ERR_CAPACITY = -2,    /* an insert past capacity_tokens */
+  ICE_ERR_UNSUPPORTED = -3, /* a valid setting this build does not implement */
+  ICE_ERR_WORKSPACE = -4,   /* workspace or scratch too small or misaligned */
+  ICE_ERR_HIP = -5          /* a HIP launch error */
+} ice_status;
+
+typedef enum { ICE_F32 = 0, ICE_BF16 = 1 } ice_dtype;
+
+/* Index parameters.  The pages state the problem in these terms: a token
+ * budget k, a page size p, and the DCI parameters m and L (IceCache paper
+ * page, abstract: budgets in tokens; the DCI and prioritized-DCI papers are
+ * cited in the paper's citation map). */
+typedef struct {
+  int32_t head_dim;   /* d: 64 or 128                                          */
+  int32_t page_size;  /* p: 8, 16, 32 or 64 tokens per page                    */
+  int32_t budget_k;   /* k: tokens; a multiple of p; P = k / p pages per query */
+  int32_t m;          /* simple indices (lists) per composite index, >= 1      */
+  int32_t L;          /* composite indices, >= 1; m * L <= 128                 */
+  int32_t gqa_group;  /* g: query heads per KV head, 1..16                      */
+  int32_t k0;         /* candidates retrieved per composite; 0 -> budget_k      */
+  int64_t k1;         /* visit budget per composite; 0 -> unbounded (the only
+                         value this build implements; others: UNSUPPORTED)      */
+  int32_t tree_depth; /* D, 1..13 and <= m*L; 0 -> derived from the build size:
+                         D = round(log2(n_tokens / (4p))) clamped to [1, min(mL,13)] */
+  float c;            /* key-norm bound of the transform; 0 -> the largest key
+                         norm of each stream at build, rounded to fp32          */
+  int32_t dtype;      /* ice_dtype of K, V, q and the directions                */
+} ice_params;
+
+typedef struct ice_index ice_index; /* opaque host handle */
+
+/* Bytes of workspace for an index of n_streams streams built from n_tokens
+ * tokens each with room for capacity_tokens >= n_tokens.  0 on bad input. */
+size_t ice_workspace_bytes(const ice_params *prm, int32_t n_streams, int64_t n_tokens,
+                           int64_t capacity_tokens);
+
+/* Bytes of build scratch for ice_build_index.  0 on bad input. */
+size_t ice_build_scratch_bytes(const ice_params *prm, int32_t n_streams, int64_t n_tokens);
+
+/* Prefill indexing (IceCache paper page, Figure 2 step (1)).
+ *   K, V   device [S][n_tokens][d] dtype: the keys and values of each stream.
+ *   dirs   device [m*L][d+1] dtype: the DCI directions (unit vectors drawn by
+ *          the caller; composite l owns directions l*m .. l*m+m-1).
+ * For each stream: c (the key-norm bound), the transformed keys
+ * [k/c, sqrt(max(0, 1 - |k|^2/c^2))] projected on every direction and stored as
+ * fixed-point codes round(x * 2^29) saturated at +-(2^30-1); one list per
+ * direction sorted by (code, token); the DCI-tree cell of each token (the sign
+ * pattern of <k, u_t[:d]> on the first D directions); the cells' tokens, in
+ * token order, cut into pages of p numbered by their first token; and a page
+ * pool holding a copy of every key and value at its page slot.
+ * K, V and dirs are read only by work enqueued here; once it has finished the
+ * caller may free them.  The workspace must outlive the index.
+ * On success *out receives a new handle. */
+ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_tokens,
+                           int64_t capacity_tokens, const void *K, const void *V,
+                           const void *dirs, void *workspace, size_t workspace_bytes,
+                           void *scratch, size_t scratch_bytes, void *stream,
+                           ice_index **out);
+
+/* Dynamic update (IceCache blog page: the tree takes new tokens with no
+ * rebuild).  Appends one token to every stream.
+ *   k_new, v_new  device [S][d] dtype.
+ * The token gets index n (the stream's current length), is projected with the
+ * stored c (the extra coordinate clamps at 0 for keys longer than c), enters
+ * every list after all equal codes, and joins the last page of its cell when
+ * that page has room, else opens page number n_pages.  The result equals a
+ * rebuild over n+1 tokens with the same c, D and directions.
+ * ICE_ERR_CAPACITY when the index already holds capacity_tokens tokens. */
+ice_status ice_insert(ice_index *idx, const void *k_new, const void *v_new, void *stream);
+
+/* Query: P-DCI candidates, exact rerank, page selection (IceCache paper page,
+ * Figure 2 steps (2)-(3)).
+ *   q         device [S*g][d] dtype: query heads, head j uses stream j / g.
+ *   page_ids  device [S][P] int32 out: selected pages in selection order,
+ *             -1 after the last.
+ *   n_pages   device [S] int32 out.
+ *   topk_ids  device [S][k] int32 out or NULL: the reranked top-k tokens,
+ *             -1 after the last.
+ * Per stream: the g query heads are averaged in fp32 (q_kv) and normalised;
+ * composite l's candidates are the k0 tokens with the smallest
+ * max_j |code_j - qcode_j| over its m directions (ties by token), which is
+ * the set a prioritized-DCI walk over the sorted lists retrieves; the union
+ * of all composites is scored exactly, <q_kv, k> in fp64, and ranked by
+ * (score desc, token asc); pages are taken in rank order, each the first time
+ * one of its tokens appears, up to P = k/p pages.  Outputs are bit-exact and
+ * deterministic. */
+ice_status ice_query_pages(ice_index *idx, const void *q, int32_t *page_ids, int32_t *n_pages,
+                           int32_t *topk_ids, void *stream);
+
+/* Sparse attention over every token of the selected pages (IceCache paper
+ * page, Figure 2 step (3)).
+ *   q         device [S*g][d] dtype.
+ *   page_ids  device [S][P] int32, n_pages device [S] int32 (as written by
+ *             ice_query_pages; any valid page numbers may be passed).
+ *   out       device [S*g][d] fp32: softmax(q k^T / sqrt(d)) V per head,
+ *             accumulated in fp32; zero when a stream selects no page. */
+ice_status ice_sparse_attn(const ice_index *idx, const void *q, const int32_t *page_ids,
+                           const int32_t *n_pages, float *out, void *stream);
+
+/* Frees the handle (not the workspace). NULL is allowed. */
+void ice_destroy_index(ice_index *idx);
+
+const char *ice_status_string(ice_status s);
+
+/* Byte offsets of the index arrays inside the workspace, for inspection and
+ * tests.  Element types and shapes (S streams, Ncap = capacity_tokens,
+ * Pcap = page_capacity, mL = m*L):
+ *   norm_c        float   [S]            the key-norm bound c
+ *   codes         int32   [S][Ncap][mL]  projection codes, token-major
+ *   list_code/id  int32   [S][mL][Ncap]  per-direction lists: entries
+ *                 [0, n_build) sorted by (code, token); entries inserted later
+ *                 follow in insertion order (the logical list merges both)
+ *   loc           int32   [S][Ncap]      page * p + slot of every token
+ *   page_tokens   int32   [S][Pcap][p]   token of each page slot, -1 = empty
+ *   page_len      int32   [S][Pcap]
+ *   page_cell     int32   [S][Pcap]      -1 for unused pages
+ *   npages        int32   [S]
+ *   cell_count    int32   [S][n_cells]   tokens per cell
+ *   pool_k/v      dtype   [S][Pcap][p][d]
+ *   qcode         int32   [S][mL]        last query's projection codes
+ *   cand          int32   [S][L][k0]     last query's candidates per composite,
+ *                 cand_count int32 [S][L] of them valid, in no fixed order */
+typedef struct {
+  int64_t n_streams, n_tokens, n_build, capacity_tokens, page_capacity, n_cells;
+  int32_t tree_depth, mL, k0, elem_bytes;
+  int64_t norm_c, codes, list_code, list_id, loc, page_tokens, page_len, page_cell, npages,
+      cell_count, pool_k, pool_v, qcode, cand, cand_count;
+  int64_t workspace_bytes;
+} ice_layout;
+
+ice_status ice_index_layout(const ice_index *idx, ice_layout *out);
+
+/* Per-kernel timing for benchmarks.  When enabled, every decode-time call
+ * (ice_insert, ice_query_pages, ice_sparse_attn) records HIP events on its
+ * stream around each kernel it launches; ice_timing_read waits for the
+ * recorded events, writes the summed milliseconds and launch counts per
+ * kernel (arrays of ICE_TIMED_KERNELS, in the order of ice_timing_name) and
+ * clears the record.  The event records add a little time between kernels;
+ * leave timing off for end-to-end latency. */
+#define ICE_TIMED_KERNELS 6
+ice_status ice_timing_enable(ice_index *idx, int enable);
+ice_status ice_timing_read(ice_index *idx, double *total_ms, int64_t *launches);
+const char *ice_timing_name(int kernel);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ICE_H */

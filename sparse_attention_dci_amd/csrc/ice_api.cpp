@@ -1,0 +1,452 @@
+// Host side of the C ABI declared in include/ice.h: argument checks (all
+// before any HIP call), the workspace layout, and kernel launches on the
+// caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "ice.h"
+#include "ice_common.h"
+
+using ice::Dev;
+
+namespace ice {
+
+// Per-kernel event timing of the decode-time calls (off unless enabled).
+struct Timer {
+  hipEvent_t last = nullptr;
+  struct Rec {
+    int kid;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> events;
+  hipEvent_t make() {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    events.push_back(e);
+    return e;
+  }
+  void clear() {
+    for (hipEvent_t e : events) hipEventDestroy(e);
+    events.clear();
+    recs.clear();
+    last = nullptr;
+  }
+};
+
+void timer_begin(Timer *tm, hipStream_t st) {
+  if (!tm) return;
+  tm->last = tm->make();
+  if (tm->last) hipEventRecord(tm->last, st);
+}
+
+void timer_mark(Timer *tm, int kid, hipStream_t st) {
+  if (!tm) return;
+  hipEvent_t e = tm->make();
+  if (!e) return;
+  hipEventRecord(e, st);
+  if (tm->last) tm->recs.push_back({kid, tm->last, e});
+  tm->last = e;
+}
+
+}  // namespace ice
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+constexpr int kAttnTps = 32;
+constexpr int64_t kMaxPages = 65536;
+
+int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// D = round(log2(n / (4p))) clamped to [1, min(mL, 13)]; round(log2 x) >= t
+// exactly when 2^(2t-1) <= x^2, evaluated in integers.
+int derive_depth(int64_t n, int p, int mL) {
+  int t = 0;
+  const unsigned __int128 n2 = (unsigned __int128)n * (unsigned __int128)n;
+  const unsigned __int128 q2 = (unsigned __int128)(4 * p) * (unsigned __int128)(4 * p);
+  for (int cand = 1; cand < 40; ++cand) {  // n < 2^31 ends the loop long before overflow
+    const unsigned __int128 lhs = ((unsigned __int128)1 << (2 * cand - 1)) * q2;
+    if (lhs > n2) break;
+    t = cand;
+  }
+  int cap = mL < ice::kMaxTreeDepth ? mL : ice::kMaxTreeDepth;
+  if (t > cap) t = cap;
+  if (t < 1) t = 1;
+  return t;
+}
+
+struct Layout {
+  int D, nchunk, k0, elem, attn_nsplit;
+  int64_t ncell, pcap;
+  int64_t dirs, norm_c, inv_c, inv_c2, maxnsq, codes, list_code, list_id, loc, page_tokens,
+      page_len, page_cell, npages, cell_count, cell_last, pool_k, pool_v, mark, qkv, qcode, mbuf,
+      hist, cand, cand_count, bnd, bnd_count, cs_key, cs_id, c_count, attn_part;
+  int64_t total;
+};
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// Parameter checks shared by every entry point that takes ice_params.
+ice_status check_params(const ice_params *prm, int32_t S, int64_t n, int64_t ncap) {
+  if (!prm) return ICE_ERR_INVALID_ARG;
+  if (prm->head_dim != 64 && prm->head_dim != 128) return ICE_ERR_INVALID_ARG;
+  const int p = prm->page_size;
+  if (!(p == 8 || p == 16 || p == 32 || p == 64)) return ICE_ERR_INVALID_ARG;
+  if (prm->budget_k <= 0 || prm->budget_k % p != 0) return ICE_ERR_INVALID_ARG;
+  if (prm->m < 1 || prm->L < 1 || (int64_t)prm->m * prm->L > ice::kMaxMl)
+    return ICE_ERR_INVALID_ARG;
+  if (prm->gqa_group < 1 || prm->gqa_group > ice::kMaxGroup) return ICE_ERR_INVALID_ARG;
+  if (prm->k0 < 0 || prm->k1 < 0) return ICE_ERR_INVALID_ARG;
+  if (prm->tree_depth < 0 || prm->tree_depth > ice::kMaxTreeDepth ||
+      prm->tree_depth > prm->m * prm->L)
+    return ICE_ERR_INVALID_ARG;
+  if (!(prm->c >= 0.0f) || std::isinf(prm->c)) return ICE_ERR_INVALID_ARG;
+  if (prm->dtype != ICE_F32 && prm->dtype != ICE_BF16) return ICE_ERR_INVALID_ARG;
+  if (S < 1 || n < 0 || ncap < n || ncap < 1 || ncap > 0x7fffffffLL - 1)
+    return ICE_ERR_INVALID_ARG;
+  if (prm->k1 != 0) return ICE_ERR_UNSUPPORTED;
+  const int64_t k0 = prm->k0 > 0 ? prm->k0 : prm->budget_k;
+  if (k0 * prm->L > ice::kMaxCand) return ICE_ERR_UNSUPPORTED;
+  return ICE_OK;
+}
+
+ice_status make_layout(const ice_params *prm, int32_t S, int64_t n, int64_t ncap, Layout *L) {
+  ice_status st = check_params(prm, S, n, ncap);
+  if (st != ICE_OK) return st;
+  const int d = prm->head_dim, p = prm->page_size, mL = prm->m * prm->L;
+  Layout y;
+  std::memset(&y, 0, sizeof(y));
+  y.D = prm->tree_depth > 0 ? prm->tree_depth : derive_depth(n, p, mL);
+  y.ncell = (int64_t)1 << y.D;
+  y.pcap = (ncap + p - 1) / p + y.ncell;
+  if (y.pcap > kMaxPages) return ICE_ERR_UNSUPPORTED;
+  y.nchunk = (mL + ice::kDirChunk - 1) / ice::kDirChunk;
+  y.k0 = prm->k0 > 0 ? prm->k0 : prm->budget_k;
+  y.elem = prm->dtype == ICE_F32 ? 4 : 2;
+  y.attn_nsplit = (prm->budget_k + kAttnTps - 1) / kAttnTps;
+  const int64_t Sl = S, Ll = prm->L, g = prm->gqa_group;
+  int64_t o = 0;
+  auto seg = [&](int64_t bytes) {
+    int64_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  y.dirs = seg((int64_t)y.nchunk * (d + 1) * ice::kDirChunk * 8);
+  y.norm_c = seg(Sl * 4);
+  y.inv_c = seg(Sl * 8);
+  y.inv_c2 = seg(Sl * 8);
+  y.maxnsq = seg(Sl * 8);
+  y.codes = seg(Sl * ncap * mL * 4);
+  y.list_code = seg(Sl * mL * ncap * 4);
+  y.list_id = seg(Sl * mL * ncap * 4);
+  y.loc = seg(Sl * ncap * 4);
+  y.page_tokens = seg(Sl * y.pcap * p * 4);
+  y.page_len = seg(Sl * y.pcap * 4);
+  y.page_cell = seg(Sl * y.pcap * 4);
+  y.npages = seg(Sl * 4);
+  y.cell_count = seg(Sl * y.ncell * 4);
+  y.cell_last = seg(Sl * y.ncell * 4);
+  y.pool_k = seg(Sl * y.pcap * p * d * y.elem);
+  y.pool_v = seg(Sl * y.pcap * p * d * y.elem);
+  y.mark = seg(Sl * ncap * 4);
+  y.qkv = seg(Sl * d * 4);
+  y.qcode = seg(Sl * mL * 4);
+  y.mbuf = seg(Sl * Ll * ncap * 4);
+  y.hist = seg(Sl * Ll * ice::kHistBins * 4);
+  y.cand = seg(Sl * Ll * y.k0 * 4);
+  y.cand_count = seg(Sl * Ll * 4);
+  y.bnd = seg(Sl * Ll * ncap * 8);
+  y.bnd_count = seg(Sl * Ll * 4);
+  y.cs_key = seg(Sl * Ll * y.k0 * 8);
+  y.cs_id = seg(Sl * Ll * y.k0 * 4);
+  y.c_count = seg(Sl * 4);
+  y.attn_part = seg(Sl * y.attn_nsplit * g * (d + 2) * 4);
+  y.total = o;
+  *L = y;
+  return ICE_OK;
+}
+
+int64_t scratch_size(const ice_params *prm, int32_t S, int64_t n) {
+  const int64_t mL = (int64_t)prm->m * prm->L;
+  int64_t o = 0;
+  o = align_up(o + (int64_t)S * mL * n * 4);  // codes_dm
+  o = align_up(o + (int64_t)S * mL * n * 4);  // tmp_code
+  o = align_up(o + (int64_t)S * mL * n * 4);  // tmp_id
+  o = align_up(o + (int64_t)S * n * 4);       // cell
+  return o;
+}
+
+bool aligned(const void *ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+}  // namespace
+
+struct ice_index {
+  ice_params prm;
+  int32_t S;
+  int64_t n, nbuild, ncap;
+  Layout lay;
+  char *ws;
+  Dev dv;
+  uint32_t epoch;
+  ice::Timer *timer;
+};
+
+extern "C" {
+
+size_t ice_workspace_bytes(const ice_params *prm, int32_t n_streams, int64_t n_tokens,
+                           int64_t capacity_tokens) {
+  Layout y;
+  if (make_layout(prm, n_streams, n_tokens, capacity_tokens, &y) != ICE_OK) return 0;
+  return (size_t)y.total;
+}
+
+size_t ice_build_scratch_bytes(const ice_params *prm, int32_t n_streams, int64_t n_tokens) {
+  if (check_params(prm, n_streams, n_tokens, n_tokens > 0 ? n_tokens : 1) != ICE_OK) return 0;
+  const int64_t s = scratch_size(prm, n_streams, n_tokens);
+  return (size_t)(s > 0 ? s : kAlign);
+}
+
+ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_tokens,
+                           int64_t capacity_tokens, const void *K, const void *V,
+                           const void *dirs, void *workspace, size_t workspace_bytes,
+                           void *scratch, size_t scratch_bytes, void *stream,
+                           ice_index **out) {
+  if (!out) return ICE_ERR_INVALID_ARG;
+  *out = nullptr;
+  Layout y;
+  ice_status st = make_layout(prm, n_streams, n_tokens, capacity_tokens, &y);
+  if (st != ICE_OK) return st;
+  if (!dirs || !aligned(dirs, 4)) return ICE_ERR_INVALID_ARG;
+  if (n_tokens > 0 && (!K || !V || !aligned(K, 16) || !aligned(V, 16)))
+    return ICE_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < (size_t)y.total)
+    return ICE_ERR_WORKSPACE;
+  const int64_t need_scratch = scratch_size(prm, n_streams, n_tokens);
+  if (n_tokens > 0 && (!scratch || !aligned(scratch, kAlign) || scratch_bytes < (size_t)need_scratch))
+    return ICE_ERR_WORKSPACE;
+
+  ice_index *idx = new (std::nothrow) ice_index;
+  if (!idx) return ICE_ERR_INVALID_ARG;
+  idx->prm = *prm;
+  idx->S = n_streams;
+  idx->n = n_tokens;
+  idx->nbuild = n_tokens;
+  idx->ncap = capacity_tokens;
+  idx->lay = y;
+  idx->ws = (char *)workspace;
+  idx->epoch = 0;
+  idx->timer = nullptr;
+  Dev &dv = idx->dv;
+  std::memset(&dv, 0, sizeof(dv));
+  char *w = (char *)workspace;
+  dv.S = n_streams;
+  dv.d = prm->head_dim;
+  dv.p = prm->page_size;
+  dv.m = prm->m;
+  dv.L = prm->L;
+  dv.mL = prm->m * prm->L;
+  dv.g = prm->gqa_group;
+  dv.D = y.D;
+  dv.k = prm->budget_k;
+  dv.P = prm->budget_k / prm->page_size;
+  dv.k0 = y.k0;
+  dv.dtype = prm->dtype;
+  dv.elem = y.elem;
+  dv.ncap = capacity_tokens;
+  dv.pcap = y.pcap;
+  dv.ncell = y.ncell;
+  dv.nbuild = n_tokens;
+  dv.nchunk = y.nchunk;
+  dv.attn_tps = kAttnTps;
+  dv.attn_nsplit = y.attn_nsplit;
+  dv.dirs = (double *)(w + y.dirs);
+  dv.norm_c = (float *)(w + y.norm_c);
+  dv.inv_c = (double *)(w + y.inv_c);
+  dv.inv_c2 = (double *)(w + y.inv_c2);
+  dv.maxnsq = (unsigned long long *)(w + y.maxnsq);
+  dv.codes = (int32_t *)(w + y.codes);
+  dv.list_code = (int32_t *)(w + y.list_code);
+  dv.list_id = (int32_t *)(w + y.list_id);
+  dv.loc = (int32_t *)(w + y.loc);
+  dv.page_tokens = (int32_t *)(w + y.page_tokens);
+  dv.page_len = (int32_t *)(w + y.page_len);
+  dv.page_cell = (int32_t *)(w + y.page_cell);
+  dv.npages = (int32_t *)(w + y.npages);
+  dv.cell_count = (int32_t *)(w + y.cell_count);
+  dv.cell_last = (int32_t *)(w + y.cell_last);
+  dv.pool_k = w + y.pool_k;
+  dv.pool_v = w + y.pool_v;
+  dv.mark = (uint32_t *)(w + y.mark);
+  dv.qkv = (float *)(w + y.qkv);
+  dv.qcode = (int32_t *)(w + y.qcode);
+  dv.mbuf = (uint32_t *)(w + y.mbuf);
+  dv.hist = (uint32_t *)(w + y.hist);
+  dv.cand = (int32_t *)(w + y.cand);
+  dv.cand_count = (uint32_t *)(w + y.cand_count);
+  dv.bnd = (unsigned long long *)(w + y.bnd);
+  dv.bnd_count = (uint32_t *)(w + y.bnd_count);
+  dv.cs_key = (unsigned long long *)(w + y.cs_key);
+  dv.cs_id = (int32_t *)(w + y.cs_id);
+  dv.c_count = (uint32_t *)(w + y.c_count);
+  dv.attn_part = (float *)(w + y.attn_part);
+
+  ice::BuildScratch bs;
+  std::memset(&bs, 0, sizeof(bs));
+  if (n_tokens > 0) {
+    char *sc = (char *)scratch;
+    const int64_t mL = dv.mL;
+    int64_t o = 0;
+    bs.codes_dm = (int32_t *)(sc + o);
+    o = align_up(o + (int64_t)n_streams * mL * n_tokens * 4);
+    bs.tmp_code = (int32_t *)(sc + o);
+    o = align_up(o + (int64_t)n_streams * mL * n_tokens * 4);
+    bs.tmp_id = (int32_t *)(sc + o);
+    o = align_up(o + (int64_t)n_streams * mL * n_tokens * 4);
+    bs.cell = (uint32_t *)(sc + o);
+  }
+  hipError_t e = ice::launch_build(dv, bs, n_tokens, K, V, dirs, prm->c, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    delete idx;
+    return ICE_ERR_HIP;
+  }
+  *out = idx;
+  return ICE_OK;
+}
+
+ice_status ice_insert(ice_index *idx, const void *k_new, const void *v_new, void *stream) {
+  if (!idx || !k_new || !v_new || !aligned(k_new, 4) || !aligned(v_new, 4))
+    return ICE_ERR_INVALID_ARG;
+  if (idx->n >= idx->ncap) return ICE_ERR_CAPACITY;
+  hipError_t e = ice::launch_insert(idx->dv, idx->n, k_new, v_new, (hipStream_t)stream,
+                                    idx->timer);
+  if (e != hipSuccess) return ICE_ERR_HIP;
+  idx->n += 1;
+  return ICE_OK;
+}
+
+ice_status ice_query_pages(ice_index *idx, const void *q, int32_t *page_ids, int32_t *n_pages,
+                           int32_t *topk_ids, void *stream) {
+  if (!idx || !q || !page_ids || !n_pages || !aligned(q, 4) || !aligned(page_ids, 4) ||
+      !aligned(n_pages, 4) || (topk_ids && !aligned(topk_ids, 4)))
+    return ICE_ERR_INVALID_ARG;
+  // Epochs tag the tokens a query has already scored; restart them before
+  // they wrap.
+  if (idx->epoch == 0xffffffffu) {
+    hipError_t e = ice::launch_build_reset_marks(idx->dv, (hipStream_t)stream);
+    if (e != hipSuccess) return ICE_ERR_HIP;
+    idx->epoch = 0;
+  }
+  idx->epoch += 1;
+  hipError_t e = ice::launch_query(idx->dv, idx->n, q, idx->epoch, page_ids, n_pages, topk_ids,
+                                   (hipStream_t)stream, idx->timer);
+  return e == hipSuccess ? ICE_OK : ICE_ERR_HIP;
+}
+
+ice_status ice_sparse_attn(const ice_index *idx, const void *q, const int32_t *page_ids,
+                           const int32_t *n_pages, float *out, void *stream) {
+  if (!idx || !q || !page_ids || !n_pages || !out || !aligned(q, 4) || !aligned(page_ids, 4) ||
+      !aligned(n_pages, 4) || !aligned(out, 4))
+    return ICE_ERR_INVALID_ARG;
+  hipError_t e = ice::launch_attn(idx->dv, q, page_ids, n_pages, out, (hipStream_t)stream,
+                                  idx->timer);
+  return e == hipSuccess ? ICE_OK : ICE_ERR_HIP;
+}
+
+void ice_destroy_index(ice_index *idx) {
+  if (!idx) return;
+  if (idx->timer) {
+    idx->timer->clear();
+    delete idx->timer;
+  }
+  delete idx;
+}
+
+ice_status ice_timing_enable(ice_index *idx, int enable) {
+  if (!idx) return ICE_ERR_INVALID_ARG;
+  if (enable && !idx->timer) {
+    idx->timer = new (std::nothrow) ice::Timer;
+    if (!idx->timer) return ICE_ERR_INVALID_ARG;
+  } else if (!enable && idx->timer) {
+    idx->timer->clear();
+    delete idx->timer;
+    idx->timer = nullptr;
+  }
+  return ICE_OK;
+}
+
+ice_status ice_timing_read(ice_index *idx, double *total_ms, int64_t *launches) {
+  if (!idx || !total_ms || !launches) return ICE_ERR_INVALID_ARG;
+  for (int k = 0; k < ICE_TIMED_KERNELS; ++k) {
+    total_ms[k] = 0.0;
+    launches[k] = 0;
+  }
+  if (!idx->timer) return ICE_OK;
+  for (const auto &r : idx->timer->recs) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(r.b) != hipSuccess) return ICE_ERR_HIP;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return ICE_ERR_HIP;
+    total_ms[r.kid] += ms;
+    launches[r.kid] += 1;
+  }
+  idx->timer->clear();
+  return ICE_OK;
+}
+
+const char *ice_timing_name(int kernel) {
+  static const char *names[ICE_TIMED_KERNELS] = {"insert",   "qscan",     "qcollect",
+                                                 "qfinal",   "attn_part", "attn_combine"};
+  return (kernel >= 0 && kernel < ICE_TIMED_KERNELS) ? names[kernel] : "";
+}
+
+const char *ice_status_string(ice_status s) {
+  switch (s) {
+    case ICE_OK: return "ok";
+    case ICE_ERR_INVALID_ARG: return "invalid argument";
+    case ICE_ERR_CAPACITY: return "index capacity exhausted";
+    case ICE_ERR_UNSUPPORTED: return "unsupported setting";
+    case ICE_ERR_WORKSPACE: return "workspace or scratch too small or misaligned";
+    case ICE_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+ice_status ice_index_layout(const ice_index *idx, ice_layout *out) {
+  if (!idx || !out) return ICE_ERR_INVALID_ARG;
+  const Layout &y = idx->lay;
+  std::memset(out, 0, sizeof(*out));
+  out->n_streams = idx->S;
+  out->n_tokens = idx->n;
+  out->n_build = idx->nbuild;
+  out->capacity_tokens = idx->ncap;
+  out->page_capacity = y.pcap;
+  out->n_cells = y.ncell;
+  out->tree_depth = y.D;
+  out->mL = idx->prm.m * idx->prm.L;
+  out->k0 = y.k0;
+  out->elem_bytes = y.elem;
+  out->norm_c = y.norm_c;
+  out->codes = y.codes;
+  out->list_code = y.list_code;
+  out->list_id = y.list_id;
+  out->loc = y.loc;
+  out->page_tokens = y.page_tokens;
+  out->page_len = y.page_len;
+  out->page_cell = y.page_cell;
+  out->npages = y.npages;
+  out->cell_count = y.cell_count;
+  out->pool_k = y.pool_k;
+  out->pool_v = y.pool_v;
+  out->qcode = y.qcode;
+  out->cand = y.cand;
+  out->cand_count = y.cand_count;
+  out->workspace_bytes = y.total;
+  return ICE_OK;
+}
+
+}  // extern "C"

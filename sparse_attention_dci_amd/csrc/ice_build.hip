@@ -1,0 +1,487 @@
+// Prefill indexing and the per-token insert (IceCache paper page, Figure 2
+// step (1); blog page, technical details: the tree takes new tokens without
+// a rebuild).
+//
+// Build = directions to fp64 -> key norms (max -> c) -> projection codes and
+// tree cells -> per-direction LSD radix sort -> pages in token order -> pool
+// scatter.  Every floating-point step reproduces a fixed fp64 evaluation
+// order (products of key and direction elements are exact in fp64), so the
+// codes, lists, cells and pages are bit-identical to a sequential CPU
+// evaluation of the same definitions.
+#include "ice_device.h"
+
+namespace ice {
+
+// ---------------------------------------------------------------- fills
+
+__global__ void k_fill_i32(int32_t *p, int64_t n, int32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+__global__ void k_fill_u64(unsigned long long *p, int64_t n, unsigned long long v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+static hipError_t fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)blocks), dim3(256), 0, st, p, n, v);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- directions
+
+// dirs [mL][d+1] (dtype) -> [nchunk][d+1][16] fp64, zero past mL.
+template <int DT>
+__global__ void k_dirs(Dev dv, const void *dirs) {
+  const int64_t total = (int64_t)dv.nchunk * (dv.d + 1) * kDirChunk;
+  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < total;
+       x += (int64_t)gridDim.x * blockDim.x) {
+    const int j = (int)(x % kDirChunk);
+    const int64_t r = x / kDirChunk;
+    const int e = (int)(r % (dv.d + 1));
+    const int ch = (int)(r / (dv.d + 1));
+    const int t = ch * kDirChunk + j;
+    dv.dirs[x] = t < dv.mL ? (double)load_elem<DT>(dirs, (int64_t)t * (dv.d + 1) + e) : 0.0;
+  }
+}
+
+// ---------------------------------------------------------------- norms
+
+// Largest |k|^2 per stream (fp64, ascending element order), as the bit
+// pattern of a non-negative double (order-preserving as an integer).
+template <int DT>
+__global__ __launch_bounds__(256) void k_norms(Dev dv, const void *K, int64_t n) {
+  const int s = blockIdx.y;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  double nsq = 0.0;
+  if (i < n) {
+    const int64_t base = ((int64_t)s * n + i) * dv.d;
+    for (int e0 = 0; e0 < dv.d; e0 += 8) {
+      float x[8];
+      load8<DT>(K, base + e0, x);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const double v = (double)x[j];
+        nsq = fma(v, v, nsq);  // v*v is exact
+      }
+    }
+  }
+  unsigned long long b = (unsigned long long)__double_as_longlong(nsq);
+  for (int off = 32; off >= 1; off >>= 1) {
+    unsigned long long o = __shfl_xor(b, off);
+    b = o > b ? o : b;
+  }
+  __shared__ unsigned long long wmax[4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) wmax[w] = b;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long m = wmax[0];
+    for (int k = 1; k < 4; ++k) m = wmax[k] > m ? wmax[k] : m;
+    atomicMax(&dv.maxnsq[s], m);
+  }
+}
+
+// ---------------------------------------------------------------- projection
+
+// c, 1/c and 1/c^2 of stream s: the fixed bound, or the largest key norm
+// rounded to fp32 (1 when every key is zero).
+__device__ __forceinline__ float stream_bound(const Dev &dv, int s, float c_fixed) {
+  if (c_fixed > 0.0f) return c_fixed;
+  const double mx = __longlong_as_double((long long)dv.maxnsq[s]);
+  const float c = (float)__dsqrt_rn(mx);
+  return c > 0.0f ? c : 1.0f;
+}
+
+// One thread = one token x one chunk of 16 directions (blockIdx.y).
+//   r_t = sum_e k_e u_te (fp64, ascending e, exact products)
+//   x_t = r_t * (1/c) + sqrt(max(0, 1 - |k|^2 (1/c)^2)) * u_td
+//   code_t = round(x_t * 2^29), saturated; cell = sign bits of r_t, t < D.
+template <int DT>
+__global__ __launch_bounds__(256) void k_project(Dev dv, BuildScratch bs, const void *K,
+                                                 int64_t n, float c_fixed) {
+  const int s = blockIdx.z, ch = blockIdx.y;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int d = dv.d, mL = dv.mL;
+  const float c = stream_bound(dv, s, c_fixed);
+  const double inv_c = __ddiv_rn(1.0, (double)c);
+  const double inv_c2 = __dmul_rn(inv_c, inv_c);
+  if (blockIdx.x == 0 && ch == 0 && threadIdx.x == 0) {
+    dv.norm_c[s] = c;
+    dv.inv_c[s] = inv_c;
+    dv.inv_c2[s] = inv_c2;
+  }
+  if (i >= n) return;
+  const double *__restrict__ dir = dv.dirs + (size_t)ch * (d + 1) * kDirChunk;
+  double r[kDirChunk];
+#pragma unroll
+  for (int t = 0; t < kDirChunk; ++t) r[t] = 0.0;
+  double nsq = 0.0;
+  const int64_t base = ((int64_t)s * n + i) * d;
+  for (int e0 = 0; e0 < d; e0 += 8) {
+    float x[8];
+    load8<DT>(K, base + e0, x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const double v = (double)x[j];
+      nsq = fma(v, v, nsq);
+      const double *u = dir + (e0 + j) * kDirChunk;
+#pragma unroll
+      for (int t = 0; t < kDirChunk; ++t) r[t] = fma(v, u[t], r[t]);
+    }
+  }
+  double b = __dsub_rn(1.0, __dmul_rn(nsq, inv_c2));
+  if (b < 0.0) b = 0.0;
+  const double sv = __dsqrt_rn(b);
+  const int t0 = ch * kDirChunk;
+  const int nt = min(kDirChunk, mL - t0);
+  int32_t *crow = dv.codes + ((int64_t)s * dv.ncap + i) * mL + t0;
+  const double *ud = dir + (size_t)d * kDirChunk;
+#pragma unroll
+  for (int t = 0; t < kDirChunk; ++t) {
+    if (t < nt) {
+      const double x = __dadd_rn(__dmul_rn(r[t], inv_c), __dmul_rn(sv, ud[t]));
+      const int32_t code = to_code(x);
+      crow[t] = code;
+      bs.codes_dm[((int64_t)s * mL + t0 + t) * n + i] = code;
+    }
+  }
+  if (ch == 0) {
+    uint32_t cl = 0;
+#pragma unroll
+    for (int t = 0; t < kDirChunk; ++t)
+      if (t < dv.D && r[t] >= 0.0) cl |= (1u << t);
+    bs.cell[(int64_t)s * n + i] = cl;
+  }
+}
+
+// ---------------------------------------------------------------- list sort
+
+// Block-wide exclusive scan of one value per thread (256 threads).
+__device__ __forceinline__ uint32_t block_excl_scan256(uint32_t v, uint32_t *wsum) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t incl = v;
+  for (int off = 1; off < 64; off <<= 1) {
+    uint32_t y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  uint32_t pre = 0;
+  for (int k = 0; k < w; ++k) pre += wsum[k];
+  __syncthreads();
+  return pre + incl - v;
+}
+
+// One block sorts one (stream, direction) list ascending by (code, token):
+// four stable LSD passes of 8 bits over the order-preserving unsigned image
+// of the code.  Pass 0 reads the direction-major codes with implicit tokens;
+// passes alternate between the scratch pair and the index lists, ending in
+// the index lists.  Inside a pass, tiles of 256 entries are ranked in entry
+// order: lanes with the same digit are matched with ballots, waves are
+// ordered through per-wave digit counts.
+__global__ __launch_bounds__(256) void k_sort_lists(Dev dv, BuildScratch bs, int64_t n) {
+  const int lst = blockIdx.x;  // s * mL + t
+  const int s = lst / dv.mL, t = lst % dv.mL;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int32_t *in0 = bs.codes_dm + (int64_t)lst * n;
+  int32_t *tc = bs.tmp_code + (int64_t)lst * n;
+  int32_t *ti = bs.tmp_id + (int64_t)lst * n;
+  int32_t *oc = dv.list_code + ((int64_t)s * dv.mL + t) * dv.ncap;
+  int32_t *oi = dv.list_id + ((int64_t)s * dv.mL + t) * dv.ncap;
+
+  __shared__ uint32_t cnt[256];
+  __shared__ uint32_t base[256];
+  __shared__ uint32_t wcnt[4][256];
+  __shared__ uint32_t woff[4][256];
+  __shared__ uint32_t wsum[4];
+
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 8 * pass;
+    const int32_t *sc = pass == 0 ? in0 : ((pass & 1) ? tc : oc);
+    const int32_t *si = pass == 0 ? nullptr : ((pass & 1) ? ti : oi);
+    int32_t *dc = (pass & 1) ? oc : tc;
+    int32_t *di = (pass & 1) ? oi : ti;
+
+    cnt[tid] = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) wcnt[k][tid] = 0;
+    __syncthreads();
+    for (int64_t x = tid; x < n; x += 256) {
+      const uint32_t key = (uint32_t)sc[x] ^ 0x80000000u;
+      atomicAdd(&cnt[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    base[tid] = block_excl_scan256(cnt[tid], wsum);
+    __syncthreads();
+
+    for (int64_t t0 = 0; t0 < n; t0 += 256) {
+      const int64_t x = t0 + tid;
+      const bool valid = x < n;
+      int32_t code = 0, id = 0;
+      uint32_t dig = 0;
+      if (valid) {
+        code = sc[x];
+        id = si ? si[x] : (int32_t)x;
+        dig = (((uint32_t)code ^ 0x80000000u) >> shift) & 255u;
+      }
+      const unsigned long long act = __ballot(valid);
+      const unsigned long long mt = match_bits(dig, 8, act);
+      const int lrank = popc64(mt & lanemask_lt());
+      const bool leader = valid && ((mt >> lane) >> 1) == 0ull;
+      if (leader) wcnt[w][dig] = (uint32_t)popc64(mt);
+      __syncthreads();
+      {
+        uint32_t o = base[tid];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          woff[k][tid] = o;
+          o += wcnt[k][tid];
+          wcnt[k][tid] = 0;
+        }
+        base[tid] = o;
+      }
+      __syncthreads();
+      if (valid) {
+        const uint32_t pos = woff[w][dig] + (uint32_t)lrank;
+        dc[pos] = code;
+        di[pos] = id;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- pages
+
+// One wave per stream walks the tokens in order, 64 at a time, and applies
+// the insert rule to each: a token takes the next slot of its cell's open
+// page, and a token whose in-cell rank is a multiple of p opens the next page
+// number.  Tokens of the same cell inside one step are ranked with ballots,
+// and a token whose page opens in the same step finds the opener's lane.
+// The result is the cells' tokens, in token order, cut into pages of p and
+// numbered by first token.
+__global__ __launch_bounds__(64) void k_pages(Dev dv, BuildScratch bs, int64_t n) {
+  extern __shared__ int32_t lds[];
+  int32_t *cnt = lds;
+  int32_t *open = lds + dv.ncell;
+  const int s = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int p = dv.p;
+  for (int64_t c = lane; c < dv.ncell; c += 64) {
+    cnt[c] = 0;
+    open[c] = -1;
+  }
+  __syncthreads();
+  int32_t npg = 0;
+  const unsigned long long lt = lanemask_lt();
+  for (int64_t t0 = 0; t0 < n; t0 += 64) {
+    const int64_t i = t0 + lane;
+    const bool valid = i < n;
+    const uint32_t c = valid ? bs.cell[(int64_t)s * n + i] : 0u;
+    const unsigned long long act = __ballot(valid);
+    const unsigned long long mt = match_bits(c, dv.D, act);
+    const int base = valid ? cnt[c] : 0;
+    const int prev_open = valid ? open[c] : -1;
+    const int rank = base + popc64(mt & lt);
+    const int slot = rank & (p - 1);
+    const bool first = valid && slot == 0;
+    const unsigned long long fm = __ballot(first);
+    const int cs = rank - slot;
+    int pid;
+    if (cs >= base) {
+      const int fl = valid ? nth_set_bit(mt, cs - base) : 0;
+      pid = npg + popc64(fm & ((1ull << fl) - 1ull));
+    } else {
+      pid = prev_open;
+    }
+    const bool leader = valid && ((mt >> lane) >> 1) == 0ull;
+    __builtin_amdgcn_wave_barrier();
+    if (leader) {
+      cnt[c] = rank + 1;
+      open[c] = pid;
+    }
+    npg += popc64(fm);
+    if (valid) {
+      dv.loc[(int64_t)s * dv.ncap + i] = pid * p + slot;
+      dv.page_tokens[((int64_t)s * dv.pcap + pid) * p + slot] = (int32_t)i;
+      if (first) dv.page_cell[(int64_t)s * dv.pcap + pid] = (int32_t)c;
+      if (slot == p - 1 || leader) dv.page_len[(int64_t)s * dv.pcap + pid] = slot + 1;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  if (lane == 0) dv.npages[s] = npg;
+  for (int64_t c = lane; c < dv.ncell; c += 64) {
+    dv.cell_count[(int64_t)s * dv.ncell + c] = cnt[c];
+    dv.cell_last[(int64_t)s * dv.ncell + c] = open[c];
+  }
+}
+
+// Copy every key and value row to its page slot (16 bytes per thread).
+__global__ __launch_bounds__(256) void k_scatter(Dev dv, const void *K, const void *V,
+                                                 int64_t n) {
+  const int64_t row_bytes = (int64_t)dv.d * dv.elem;
+  const int64_t cpr = row_bytes / 16;
+  const int64_t total = (int64_t)dv.S * n * cpr;
+  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < total;
+       x += (int64_t)gridDim.x * 256) {
+    const int64_t row = x / cpr;
+    const int64_t cc = x % cpr;
+    const int64_t s = row / n, i = row % n;
+    const int64_t lc = dv.loc[s * dv.ncap + i];
+    const int64_t dst = ((s * dv.pcap * dv.p) + lc) * row_bytes + cc * 16;
+    const int64_t src = row * row_bytes + cc * 16;
+    *reinterpret_cast<uint4 *>((char *)dv.pool_k + dst) =
+        *reinterpret_cast<const uint4 *>((const char *)K + src);
+    *reinterpret_cast<uint4 *>((char *)dv.pool_v + dst) =
+        *reinterpret_cast<const uint4 *>((const char *)V + src);
+  }
+}
+
+// ---------------------------------------------------------------- insert
+
+// One block per stream appends token n: projection with the stored bound,
+// list entries at position n of each direction's insert region, the page
+// rule, and the pool rows.  Lane t < mL forms r_t; lane 255 forms |k|^2.
+template <int DT>
+__global__ __launch_bounds__(256) void k_insert(Dev dv, int64_t n, const void *k_new,
+                                                const void *v_new) {
+  const int s = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int d = dv.d, mL = dv.mL, p = dv.p;
+  __shared__ float kv[128];
+  __shared__ double nsq_s;
+  __shared__ uint32_t cell_s;
+  __shared__ int32_t loc_s;
+  if (tid < d) kv[tid] = load_elem<DT>(k_new, (int64_t)s * d + tid);
+  __syncthreads();
+  double r = 0.0;
+  const double *dir = dv.dirs + (size_t)(tid / kDirChunk) * (d + 1) * kDirChunk + (tid % kDirChunk);
+  if (tid < mL) {
+    for (int e = 0; e < d; ++e) r = fma((double)kv[e], dir[(size_t)e * kDirChunk], r);
+  } else if (tid == 255) {
+    double a = 0.0;
+    for (int e = 0; e < d; ++e) a = fma((double)kv[e], (double)kv[e], a);
+    nsq_s = a;
+  }
+  // cell = sign bits of r on the first D directions (all in wave 0)
+  if (tid < 64) {
+    const unsigned long long bal = __ballot(tid < dv.D && r >= 0.0);
+    if (tid == 0) cell_s = (uint32_t)bal & ((1u << dv.D) - 1u);
+  }
+  __syncthreads();
+  if (tid < mL) {
+    double b = __dsub_rn(1.0, __dmul_rn(nsq_s, dv.inv_c2[s]));
+    if (b < 0.0) b = 0.0;
+    const double sv = __dsqrt_rn(b);
+    const double x = __dadd_rn(__dmul_rn(r, dv.inv_c[s]), __dmul_rn(sv, dir[(size_t)d * kDirChunk]));
+    const int32_t code = to_code(x);
+    dv.codes[((int64_t)s * dv.ncap + n) * mL + tid] = code;
+    dv.list_code[((int64_t)s * mL + tid) * dv.ncap + n] = code;
+    dv.list_id[((int64_t)s * mL + tid) * dv.ncap + n] = (int32_t)n;
+  }
+  if (tid == 0) {
+    const uint32_t c = cell_s;
+    const int64_t ci = (int64_t)s * dv.ncell + c;
+    const int32_t cntc = dv.cell_count[ci];
+    const int32_t slot = cntc & (p - 1);
+    int32_t pid;
+    if (slot == 0) {
+      pid = dv.npages[s];
+      dv.npages[s] = pid + 1;
+      dv.cell_last[ci] = pid;
+      dv.page_cell[(int64_t)s * dv.pcap + pid] = (int32_t)c;
+    } else {
+      pid = dv.cell_last[ci];
+    }
+    dv.cell_count[ci] = cntc + 1;
+    dv.page_tokens[((int64_t)s * dv.pcap + pid) * p + slot] = (int32_t)n;
+    dv.page_len[(int64_t)s * dv.pcap + pid] = slot + 1;
+    const int32_t lc = pid * p + slot;
+    dv.loc[(int64_t)s * dv.ncap + n] = lc;
+    loc_s = lc;
+  }
+  __syncthreads();
+  const int64_t row = ((int64_t)s * dv.pcap * p + loc_s) * d;
+  if (tid < d) {
+    if constexpr (DT == 0) {
+      reinterpret_cast<float *>(dv.pool_k)[row + tid] = reinterpret_cast<const float *>(k_new)[(int64_t)s * d + tid];
+      reinterpret_cast<float *>(dv.pool_v)[row + tid] = reinterpret_cast<const float *>(v_new)[(int64_t)s * d + tid];
+    } else {
+      reinterpret_cast<uint16_t *>(dv.pool_k)[row + tid] = reinterpret_cast<const uint16_t *>(k_new)[(int64_t)s * d + tid];
+      reinterpret_cast<uint16_t *>(dv.pool_v)[row + tid] = reinterpret_cast<const uint16_t *>(v_new)[(int64_t)s * d + tid];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <int DT>
+static hipError_t build_impl(const Dev &dv, const BuildScratch &bs, int64_t n, const void *K,
+                             const void *V, const void *dirs, float c_fixed, hipStream_t st) {
+  hipError_t e;
+  // index state
+  if ((e = fill_i32(dv.page_tokens, (int64_t)dv.S * dv.pcap * dv.p, -1, st))) return e;
+  if ((e = fill_i32(dv.page_len, (int64_t)dv.S * dv.pcap, 0, st))) return e;
+  if ((e = fill_i32(dv.page_cell, (int64_t)dv.S * dv.pcap, -1, st))) return e;
+  if ((e = fill_i32((int32_t *)dv.mark, (int64_t)dv.S * dv.ncap, 0, st))) return e;
+  if ((e = fill_i32((int32_t *)dv.hist, (int64_t)dv.S * dv.L * kHistBins, 0, st))) return e;
+  if ((e = fill_i32((int32_t *)dv.cand_count, (int64_t)dv.S * dv.L, 0, st))) return e;
+  hipLaunchKernelGGL(k_fill_u64, dim3(1), dim3(256), 0, st, dv.maxnsq, (int64_t)dv.S, 0ull);
+  {
+    const int64_t total = (int64_t)dv.nchunk * (dv.d + 1) * kDirChunk;
+    hipLaunchKernelGGL(k_dirs<DT>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, dv,
+                       dirs);
+  }
+  const unsigned nb = (unsigned)((n + 255) / 256);
+  if (n > 0) {
+    if (c_fixed <= 0.0f)
+      hipLaunchKernelGGL(k_norms<DT>, dim3(nb, dv.S), dim3(256), 0, st, dv, K, n);
+    hipLaunchKernelGGL(k_project<DT>, dim3(nb, dv.nchunk, dv.S), dim3(256), 0, st, dv, bs, K,
+                       n, c_fixed);
+    hipLaunchKernelGGL(k_sort_lists, dim3(dv.S * dv.mL), dim3(256), 0, st, dv, bs, n);
+  } else {
+    // an empty build still fixes c, 1/c and 1/c^2
+    hipLaunchKernelGGL(k_project<DT>, dim3(1, 1, dv.S), dim3(256), 0, st, dv, bs, K, n,
+                       c_fixed);
+  }
+  hipLaunchKernelGGL(k_pages, dim3(dv.S), dim3(64), (size_t)dv.ncell * 2 * sizeof(int32_t), st,
+                     dv, bs, n);
+  if (n > 0) {
+    const int64_t total = (int64_t)dv.S * n * ((int64_t)dv.d * dv.elem / 16);
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(k_scatter, dim3((unsigned)blocks), dim3(256), 0, st, dv, K, V, n);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_build(const Dev &dv, const BuildScratch &bs, int64_t n, const void *K,
+                        const void *V, const void *dirs, float c_fixed, hipStream_t st) {
+  return dv.dtype == 0 ? build_impl<0>(dv, bs, n, K, V, dirs, c_fixed, st)
+                       : build_impl<1>(dv, bs, n, K, V, dirs, c_fixed, st);
+}
+
+hipError_t launch_build_reset_marks(const Dev &dv, hipStream_t st) {
+  return fill_i32((int32_t *)dv.mark, (int64_t)dv.S * dv.ncap, 0, st);
+}
+
+hipError_t launch_insert(const Dev &dv, int64_t n, const void *k_new, const void *v_new,
+                         hipStream_t st, Timer *tm) {
+  timer_begin(tm, st);
+  if (dv.dtype == 0)
+    hipLaunchKernelGGL(k_insert<0>, dim3(dv.S), dim3(256), 0, st, dv, n, k_new, v_new);
+  else
+    hipLaunchKernelGGL(k_insert<1>, dim3(dv.S), dim3(256), 0, st, dv, n, k_new, v_new);
+  timer_mark(tm, KID_INSERT, st);
+  return hipGetLastError();
+}
+
+}  // namespace ice

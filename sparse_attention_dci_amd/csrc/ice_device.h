@@ -1,0 +1,102 @@
+// Device helpers for the gfx950 kernels (64-wide wavefronts).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ice_common.h"
+
+namespace ice {
+
+constexpr int kWave = 64;
+
+// Element loads: K, V, q and directions are fp32 or bf16 (dtype 0 / 1).
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+template <int DT>
+__device__ __forceinline__ float load_elem(const void *base, int64_t i) {
+  if constexpr (DT == 0) {
+    return reinterpret_cast<const float *>(base)[i];
+  } else {
+    return bf16_bits_to_float(reinterpret_cast<const uint16_t *>(base)[i]);
+  }
+}
+
+// Eight consecutive elements starting at an index that is a multiple of 8.
+template <int DT>
+__device__ __forceinline__ void load8(const void *base, int64_t i, float (&v)[8]) {
+  if constexpr (DT == 0) {
+    const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + i);
+    float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    uint4 a = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(base) + i);
+    uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = __uint_as_float(w[j] << 16);
+      v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    }
+  }
+}
+
+__device__ __forceinline__ int32_t to_code(double x) {
+  double v = rint(x * kCodeScale);  // scaling by 2^29 is exact
+  v = fmin(fmax(v, -(double)kCodeMax), (double)kCodeMax);
+  return (int32_t)v;
+}
+
+__device__ __forceinline__ uint32_t absdiff(int32_t a, int32_t b) {
+  int64_t d = (int64_t)a - (int64_t)b;
+  return (uint32_t)(d < 0 ? -d : d);
+}
+
+// Rank key of a reranked candidate: ascending key == descending score.
+__device__ __forceinline__ unsigned long long score_rank_key(double s) {
+  if (s == 0.0) s = 0.0;  // one zero
+  unsigned long long b = (unsigned long long)__double_as_longlong(s);
+  unsigned long long ord = (b >> 63) ? ~b : (b | 0x8000000000000000ull);  // ascending
+  return ~ord;
+}
+
+__device__ __forceinline__ unsigned long long lanemask_lt() {
+  const int lane = __lane_id();
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+__device__ __forceinline__ int popc64(unsigned long long x) { return __popcll(x); }
+
+// Index of the n-th (0-based) set bit of m; m must have more than n bits set.
+__device__ __forceinline__ int nth_set_bit(unsigned long long m, int n) {
+  int pos = 0;
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    unsigned long long low = m & ((1ull << w) - 1ull);
+    int c = popc64(low);
+    if (n >= c) {
+      n -= c;
+      m >>= w;
+      pos += w;
+    } else {
+      m = low;
+    }
+  }
+  return pos;
+}
+
+// Lanes of the wave whose `key` (restricted to `bits` low bits) equals this
+// lane's, among the lanes in `active`.
+__device__ __forceinline__ unsigned long long match_bits(uint32_t key, int bits,
+                                                         unsigned long long active) {
+  unsigned long long m = active;
+  for (int b = 0; b < bits; ++b) {
+    unsigned long long bal = __ballot((key >> b) & 1u);
+    m &= ((key >> b) & 1u) ? bal : ~bal;
+  }
+  return m;
+}
+
+}  // namespace ice

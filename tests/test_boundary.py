@@ -1,0 +1,138 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+include/ice.h declares, and rejects bad arguments before any HIP call (the
+fake pointers below are never dereferenced because each call fails its
+checks first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_dci_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x100000)   # aligned, never dereferenced
+ODD = ctypes.c_void_p(0x100001)    # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from sparse_attention_dci_amd import build_lib
+        build_lib.build()
+    return B.lib()
+
+
+def good(**kw):
+    base = dict(d=128, page_size=16, budget_k=256, m=8, L=4, gqa_group=4)
+    base.update(kw)
+    return B.make_params(**base)
+
+
+def test_exports_every_declared_symbol(L):
+    header = open(os.path.join(ROOT, "include", "ice.h")).read()
+    names = set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(ice_\w+)\s*\(", header, re.M))
+    assert {"ice_workspace_bytes", "ice_build_scratch_bytes", "ice_build_index", "ice_insert",
+            "ice_query_pages", "ice_sparse_attn", "ice_destroy_index", "ice_status_string",
+            "ice_index_layout"} <= names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for s in (0, -1, -2, -3, -4, -5):
+        assert L.ice_status_string(s)
+    assert L.ice_status_string(-99) == b"unknown status"
+
+
+def test_workspace_size_rules(L):
+    p = good()
+    a = L.ice_workspace_bytes(ctypes.byref(p), 8, 36864, 36864)
+    b = L.ice_workspace_bytes(ctypes.byref(p), 8, 36864, 36864 + 128)
+    assert 0 < a < b
+    assert L.ice_build_scratch_bytes(ctypes.byref(p), 8, 36864) >= 8 * 32 * 36864 * 12
+    assert L.ice_workspace_bytes(ctypes.byref(p), 8, 0, 16) > 0
+
+
+@pytest.mark.parametrize("bad", [
+    dict(d=96), dict(page_size=12), dict(page_size=128), dict(budget_k=250), dict(budget_k=0),
+    dict(m=0), dict(L=0), dict(m=16, L=9), dict(gqa_group=0), dict(gqa_group=17),
+    dict(tree_depth=14), dict(tree_depth=-1), dict(m=2, L=2, tree_depth=5), dict(c=-1.0),
+    dict(c=float("inf")), dict(c=float("nan")), dict(k0=-1), dict(k1=-5),
+])
+def test_bad_params_rejected(L, bad):
+    p = good(**bad)
+    assert L.ice_workspace_bytes(ctypes.byref(p), 8, 1000, 1000) == 0
+    h = ctypes.c_void_p()
+    st = L.ice_build_index(ctypes.byref(p), 8, 1000, 1000, FAKE, FAKE, FAKE, FAKE, 1 << 40, FAKE,
+                           1 << 40, None, ctypes.byref(h))
+    assert st == B.ICE_ERR_INVALID_ARG and not h.value
+
+
+def test_bad_dtype_rejected(L):
+    p = good()
+    p.dtype = 7
+    assert L.ice_workspace_bytes(ctypes.byref(p), 8, 1000, 1000) == 0
+
+
+@pytest.mark.parametrize("S,n,cap", [(0, 10, 10), (1, 20, 10), (1, -1, 10), (1, 0, 0),
+                                     (1, 10, 1 << 31)])
+def test_bad_sizes_rejected(L, S, n, cap):
+    p = good()
+    assert L.ice_workspace_bytes(ctypes.byref(p), S, n, cap) == 0
+
+
+def test_unsupported_settings(L):
+    h = ctypes.c_void_p()
+    for p in (good(k1=1000), good(budget_k=2048, page_size=32, m=12, L=6)):
+        assert L.ice_workspace_bytes(ctypes.byref(p), 1, 1000, 1000) == 0
+        st = L.ice_build_index(ctypes.byref(p), 1, 1000, 1000, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                               FAKE, 1 << 40, None, ctypes.byref(h))
+        assert st == B.ICE_ERR_UNSUPPORTED
+
+
+def test_build_argument_checks(L):
+    p = good()
+    ws = L.ice_workspace_bytes(ctypes.byref(p), 2, 1000, 1000)
+    sb = L.ice_build_scratch_bytes(ctypes.byref(p), 2, 1000)
+    h = ctypes.c_void_p()
+    call = lambda **a: L.ice_build_index(
+        ctypes.byref(p), 2, 1000, 1000, a.get("K", FAKE), a.get("V", FAKE), a.get("U", FAKE),
+        a.get("ws", FAKE), a.get("wsb", ws), a.get("sc", FAKE), a.get("scb", sb), None,
+        a.get("out", ctypes.byref(h)))
+    assert call(out=None) == B.ICE_ERR_INVALID_ARG
+    assert call(U=None) == B.ICE_ERR_INVALID_ARG
+    assert call(K=None) == B.ICE_ERR_INVALID_ARG
+    assert call(K=ODD) == B.ICE_ERR_INVALID_ARG
+    assert call(ws=None) == B.ICE_ERR_WORKSPACE
+    assert call(ws=ODD) == B.ICE_ERR_WORKSPACE
+    assert call(wsb=ws - 1) == B.ICE_ERR_WORKSPACE
+    assert call(sc=None) == B.ICE_ERR_WORKSPACE
+    assert call(scb=sb - 1) == B.ICE_ERR_WORKSPACE
+    assert not h.value
+
+
+def test_null_handles(L):
+    assert L.ice_insert(None, FAKE, FAKE, None) == B.ICE_ERR_INVALID_ARG
+    assert L.ice_query_pages(None, FAKE, FAKE, FAKE, None, None) == B.ICE_ERR_INVALID_ARG
+    assert L.ice_sparse_attn(None, FAKE, FAKE, FAKE, FAKE, None) == B.ICE_ERR_INVALID_ARG
+    y = B.IceLayout()
+    assert L.ice_index_layout(None, ctypes.byref(y)) == B.ICE_ERR_INVALID_ARG
+    L.ice_destroy_index(None)
+
+
+def test_tree_depth_matches_oracle_reading(L, ora):
+    """The derived depth is visible through the workspace size: the cell tables
+    grow with 2^D.  Compare the sizes with D given explicitly."""
+    for n, pg, m, Lc in [(4096, 16, 4, 2), (36864, 16, 8, 4), (131072, 16, 10, 4), (3000, 8, 4, 2),
+                         (100, 16, 2, 2), (0, 16, 4, 2)]:
+        D = ora.tree_depth(n, pg, m * Lc)
+        auto = good(page_size=pg, budget_k=4 * pg, m=m, L=Lc)
+        fixed = good(page_size=pg, budget_k=4 * pg, m=m, L=Lc, tree_depth=D)
+        cap = max(n, 1)
+        assert (L.ice_workspace_bytes(ctypes.byref(auto), 1, n, cap)
+                == L.ice_workspace_bytes(ctypes.byref(fixed), 1, n, cap)), (n, pg, D)
+        if D < min(m * Lc, 13):
+            other = good(page_size=pg, budget_k=4 * pg, m=m, L=Lc, tree_depth=D + 1)
+            assert (L.ice_workspace_bytes(ctypes.byref(auto), 1, n, cap)
+                    != L.ice_workspace_bytes(ctypes.byref(other), 1, n, cap))
