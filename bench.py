@@ -45,18 +45,29 @@ def kernel_source_hash() -> str:
 
 def algorithmic_bytes(w, kernel: str, ntok: int, n_cand: float, attended: float) -> float:
     """Bytes the decode path has to move per launch of `kernel` for the whole layer
-    (S streams): the per-unit figures times the units one launch processes."""
+    (S streams): the per-unit figures times the units one launch processes.
+
+    insert    new k, v in; pool rows, codes and list entries out: 4d*elem + 12*mL
+    qprep     query heads and the fp64 directions: g*d*elem + (d+1)*mL*8
+    qscan     every token's m*L projection codes: 4*mL per token
+    qcollect  every token's L completion distances written by the scan: 4*L per token
+    qfinal    the key row of every reranked candidate: d*elem per candidate
+    attn      K and V rows of every attended token, the queries and the outputs
+    """
     S, d, mL, L, g = w.streams, w.d, w.mL, w.L, w.g
     elem = 2 if w.dtype == "bf16" else 4
-    if kernel == "qscan":      # every token's m*L projection codes, 4 B each
-        return S * ntok * mL * 4.0
-    if kernel == "qcollect":   # every token's L composite distances + candidate key rows
-        return S * (ntok * L * 4.0 + n_cand * d * elem)
-    if kernel == "attn_part":  # K and V rows of every attended token + queries
-        return S * (attended * 2 * d * elem + g * d * elem)
-    if kernel == "insert":     # new k, v in; pool rows, codes and list entries out
-        return S * (4.0 * d * elem + mL * 12.0)
-    return 0.0
+    per_stream = {
+        "insert": 4.0 * d * elem + 12.0 * mL,
+        "qprep": g * d * elem + (d + 1) * mL * 8.0,
+        "qscan": ntok * mL * 4.0,
+        "qcollect": ntok * L * 4.0,
+        "qfinal": n_cand * d * elem,
+        "attn": attended * 2 * d * elem + g * d * (elem + 4),
+    }
+    return S * per_stream.get(kernel, 0.0)
+
+
+STEP_KERNELS = ("insert", "qprep", "qscan", "qfinal", "attn")  # excludes the scan's own scratch
 
 
 def cpu_baseline(w, K, V, q, U, k_new, v_new, reps: int):
@@ -200,8 +211,7 @@ def main():
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": traffic, "avg_us": round(avg_us[dominant], 3),
                 "alg_bytes": int(alg)}
-    step_alg = sum(algorithmic_bytes(w, k, ntok, n_cand, attended)
-                   for k in ("insert", "qscan", "qcollect", "attn_part"))
+    step_alg = sum(algorithmic_bytes(w, k, ntok, n_cand, attended) for k in STEP_KERNELS)
 
     cpu = None
     if not args.no_cpu:

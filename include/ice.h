@@ -156,7 +156,8 @@ const char *ice_status_string(ice_status s);
  * tests.  Element types and shapes (S streams, Ncap = capacity_tokens,
  * Pcap = page_capacity, mL = m*L):
  *   norm_c        float   [S]            the key-norm bound c
- *   codes         int32   [S][Ncap][mL]  projection codes, token-major
+ *   codes         int32   [S][ceil(Ncap/64)][mL][64]  projection codes in tiles
+ *                 of 64 tokens: code t of token i at [i/64][t][i%64]
  *   list_code/id  int32   [S][mL][Ncap]  per-direction lists: entries
  *                 [0, n_build) sorted by (code, token); entries inserted later
  *                 follow in insertion order (the logical list merges both)
@@ -187,7 +188,7 @@ ice_status ice_index_layout(const ice_index *idx, ice_layout *out);
  * kernel (arrays of ICE_TIMED_KERNELS, in the order of ice_timing_name) and
  * clears the record.  The event records add a little time between kernels;
  * leave timing off for end-to-end latency. */
-#define ICE_TIMED_KERNELS 6
+#define ICE_TIMED_KERNELS 6 /* insert, qprep, qscan, qcollect, qfinal, attn */
 ice_status ice_timing_enable(ice_index *idx, int enable);
 ice_status ice_timing_read(ice_index *idx, double *total_ms, int64_t *launches);
 const char *ice_timing_name(int kernel);

@@ -236,7 +236,7 @@ class Index:
         L = self.prm.L
         shapes = {
             "norm_c": (torch.float32, (S,)),
-            "codes": (torch.int32, (S, ncap, mL)),
+            "codes": (torch.int32, (S, (ncap + 63) // 64, mL, 64)),
             "list_code": (torch.int32, (S, mL, ncap)),
             "list_id": (torch.int32, (S, mL, ncap)),
             "loc": (torch.int32, (S, ncap)),
@@ -258,4 +258,7 @@ class Index:
         for s_ in shape:
             count *= s_
         raw = self.workspace[off:off + count * nbytes]
-        return raw.view(dt).view(shape)
+        t = raw.view(dt).view(shape)
+        if name == "codes":  # tiles of 64 tokens -> [S][ncap][mL] (a copy)
+            t = t.permute(0, 1, 3, 2).reshape(S, -1, mL)[:, :ncap]
+        return t

@@ -59,7 +59,7 @@ void timer_mark(Timer *tm, int kid, hipStream_t st) {
 namespace {
 
 constexpr int64_t kAlign = 256;
-constexpr int kAttnTps = 32;
+constexpr int kAttnTps = 32;  // tokens per attention block (kTps in ice_attn.hip)
 constexpr int64_t kMaxPages = 65536;
 
 int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -85,8 +85,9 @@ struct Layout {
   int D, nchunk, k0, elem, attn_nsplit;
   int64_t ncell, pcap;
   int64_t dirs, norm_c, inv_c, inv_c2, maxnsq, codes, list_code, list_id, loc, page_tokens,
-      page_len, page_cell, npages, cell_count, cell_last, pool_k, pool_v, mark, qkv, qcode, mbuf,
-      hist, cand, cand_count, bnd, bnd_count, cs_key, cs_id, c_count, attn_part;
+      page_len, page_cell, npages, cell_count, cell_last, pool_k, pool_v, qkv, qcode, mbuf,
+      hist, cand, cand_count, bnd, bnd_count, rr_key, rr_id, rr_pg, rr_count, cmark,
+      attn_part, attn_done;
   int64_t total;
 };
 
@@ -111,6 +112,7 @@ ice_status check_params(const ice_params *prm, int32_t S, int64_t n, int64_t nca
   if (S < 1 || n < 0 || ncap < n || ncap < 1 || ncap > 0x7fffffffLL - 1)
     return ICE_ERR_INVALID_ARG;
   if (prm->k1 != 0) return ICE_ERR_UNSUPPORTED;
+  if (prm->L > 32) return ICE_ERR_UNSUPPORTED;
   const int64_t k0 = prm->k0 > 0 ? prm->k0 : prm->budget_k;
   if (k0 * prm->L > ice::kMaxCand) return ICE_ERR_UNSUPPORTED;
   return ICE_OK;
@@ -142,7 +144,7 @@ ice_status make_layout(const ice_params *prm, int32_t S, int64_t n, int64_t ncap
   y.inv_c = seg(Sl * 8);
   y.inv_c2 = seg(Sl * 8);
   y.maxnsq = seg(Sl * 8);
-  y.codes = seg(Sl * ncap * mL * 4);
+  y.codes = seg(Sl * ((ncap + ice::kCodeTile - 1) / ice::kCodeTile) * ice::kCodeTile * mL * 4);
   y.list_code = seg(Sl * mL * ncap * 4);
   y.list_id = seg(Sl * mL * ncap * 4);
   y.loc = seg(Sl * ncap * 4);
@@ -154,7 +156,6 @@ ice_status make_layout(const ice_params *prm, int32_t S, int64_t n, int64_t ncap
   y.cell_last = seg(Sl * y.ncell * 4);
   y.pool_k = seg(Sl * y.pcap * p * d * y.elem);
   y.pool_v = seg(Sl * y.pcap * p * d * y.elem);
-  y.mark = seg(Sl * ncap * 4);
   y.qkv = seg(Sl * d * 4);
   y.qcode = seg(Sl * mL * 4);
   y.mbuf = seg(Sl * Ll * ncap * 4);
@@ -163,10 +164,13 @@ ice_status make_layout(const ice_params *prm, int32_t S, int64_t n, int64_t ncap
   y.cand_count = seg(Sl * Ll * 4);
   y.bnd = seg(Sl * Ll * ncap * 8);
   y.bnd_count = seg(Sl * Ll * 4);
-  y.cs_key = seg(Sl * Ll * y.k0 * 8);
-  y.cs_id = seg(Sl * Ll * y.k0 * 4);
-  y.c_count = seg(Sl * 4);
+  y.rr_key = seg(Sl * Ll * y.k0 * 8);
+  y.rr_id = seg(Sl * Ll * y.k0 * 4);
+  y.rr_pg = seg(Sl * Ll * y.k0 * 4);
+  y.rr_count = seg(Sl * 4);
+  y.cmark = seg(Sl * ((ncap + 31) / 32) * 4);
   y.attn_part = seg(Sl * y.attn_nsplit * g * (d + 2) * 4);
+  y.attn_done = seg(Sl * 4);
   y.total = o;
   *L = y;
   return ICE_OK;
@@ -193,7 +197,6 @@ struct ice_index {
   Layout lay;
   char *ws;
   Dev dv;
-  uint32_t epoch;
   ice::Timer *timer;
 };
 
@@ -240,7 +243,6 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
   idx->ncap = capacity_tokens;
   idx->lay = y;
   idx->ws = (char *)workspace;
-  idx->epoch = 0;
   idx->timer = nullptr;
   Dev &dv = idx->dv;
   std::memset(&dv, 0, sizeof(dv));
@@ -263,7 +265,6 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
   dv.ncell = y.ncell;
   dv.nbuild = n_tokens;
   dv.nchunk = y.nchunk;
-  dv.attn_tps = kAttnTps;
   dv.attn_nsplit = y.attn_nsplit;
   dv.dirs = (double *)(w + y.dirs);
   dv.norm_c = (float *)(w + y.norm_c);
@@ -271,6 +272,7 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
   dv.inv_c2 = (double *)(w + y.inv_c2);
   dv.maxnsq = (unsigned long long *)(w + y.maxnsq);
   dv.codes = (int32_t *)(w + y.codes);
+  dv.ntile = (capacity_tokens + ice::kCodeTile - 1) / ice::kCodeTile;
   dv.list_code = (int32_t *)(w + y.list_code);
   dv.list_id = (int32_t *)(w + y.list_id);
   dv.loc = (int32_t *)(w + y.loc);
@@ -282,7 +284,6 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
   dv.cell_last = (int32_t *)(w + y.cell_last);
   dv.pool_k = w + y.pool_k;
   dv.pool_v = w + y.pool_v;
-  dv.mark = (uint32_t *)(w + y.mark);
   dv.qkv = (float *)(w + y.qkv);
   dv.qcode = (int32_t *)(w + y.qcode);
   dv.mbuf = (uint32_t *)(w + y.mbuf);
@@ -291,10 +292,14 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
   dv.cand_count = (uint32_t *)(w + y.cand_count);
   dv.bnd = (unsigned long long *)(w + y.bnd);
   dv.bnd_count = (uint32_t *)(w + y.bnd_count);
-  dv.cs_key = (unsigned long long *)(w + y.cs_key);
-  dv.cs_id = (int32_t *)(w + y.cs_id);
-  dv.c_count = (uint32_t *)(w + y.c_count);
+  dv.rr_key = (unsigned long long *)(w + y.rr_key);
+  dv.rr_id = (int32_t *)(w + y.rr_id);
+  dv.rr_pg = (int32_t *)(w + y.rr_pg);
+  dv.rr_count = (uint32_t *)(w + y.rr_count);
+  dv.cmark = (uint32_t *)(w + y.cmark);
+  dv.mwords = (capacity_tokens + 31) / 32;
   dv.attn_part = (float *)(w + y.attn_part);
+  dv.attn_done = (uint32_t *)(w + y.attn_done);
 
   ice::BuildScratch bs;
   std::memset(&bs, 0, sizeof(bs));
@@ -335,15 +340,7 @@ ice_status ice_query_pages(ice_index *idx, const void *q, int32_t *page_ids, int
   if (!idx || !q || !page_ids || !n_pages || !aligned(q, 4) || !aligned(page_ids, 4) ||
       !aligned(n_pages, 4) || (topk_ids && !aligned(topk_ids, 4)))
     return ICE_ERR_INVALID_ARG;
-  // Epochs tag the tokens a query has already scored; restart them before
-  // they wrap.
-  if (idx->epoch == 0xffffffffu) {
-    hipError_t e = ice::launch_build_reset_marks(idx->dv, (hipStream_t)stream);
-    if (e != hipSuccess) return ICE_ERR_HIP;
-    idx->epoch = 0;
-  }
-  idx->epoch += 1;
-  hipError_t e = ice::launch_query(idx->dv, idx->n, q, idx->epoch, page_ids, n_pages, topk_ids,
+  hipError_t e = ice::launch_query(idx->dv, idx->n, q, page_ids, n_pages, topk_ids,
                                    (hipStream_t)stream, idx->timer);
   return e == hipSuccess ? ICE_OK : ICE_ERR_HIP;
 }
@@ -399,8 +396,8 @@ ice_status ice_timing_read(ice_index *idx, double *total_ms, int64_t *launches) 
 }
 
 const char *ice_timing_name(int kernel) {
-  static const char *names[ICE_TIMED_KERNELS] = {"insert",   "qscan",     "qcollect",
-                                                 "qfinal",   "attn_part", "attn_combine"};
+  static const char *names[ICE_TIMED_KERNELS] = {"insert", "qprep",  "qscan",
+                                                 "qcollect", "qfinal", "attn"};
   return (kernel >= 0 && kernel < ICE_TIMED_KERNELS) ? names[kernel] : "";
 }
 

@@ -104,8 +104,10 @@ __device__ __forceinline__ float stream_bound(const Dev &dv, int s, float c_fixe
 //   x_t = r_t * (1/c) + sqrt(max(0, 1 - |k|^2 (1/c)^2)) * u_td
 //   code_t = round(x_t * 2^29), saturated; cell = sign bits of r_t, t < D.
 template <int DT>
-__global__ __launch_bounds__(256) void k_project(Dev dv, BuildScratch bs, const void *K,
-                                                 int64_t n, float c_fixed) {
+__global__ __launch_bounds__(256) void k_project(Dev dv, BuildScratch bs,
+                                                 const void *__restrict__ K,
+                                                 const double *__restrict__ dirs, int64_t n,
+                                                 float c_fixed) {
   const int s = blockIdx.z, ch = blockIdx.y;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int d = dv.d, mL = dv.mL;
@@ -118,7 +120,8 @@ __global__ __launch_bounds__(256) void k_project(Dev dv, BuildScratch bs, const 
     dv.inv_c2[s] = inv_c2;
   }
   if (i >= n) return;
-  const double *__restrict__ dir = dv.dirs + (size_t)ch * (d + 1) * kDirChunk;
+  // wave-uniform addresses into a read-only argument: scalar loads
+  const double *__restrict__ dir = dirs + (size_t)ch * (d + 1) * kDirChunk;
   double r[kDirChunk];
 #pragma unroll
   for (int t = 0; t < kDirChunk; ++t) r[t] = 0.0;
@@ -141,14 +144,13 @@ __global__ __launch_bounds__(256) void k_project(Dev dv, BuildScratch bs, const 
   const double sv = __dsqrt_rn(b);
   const int t0 = ch * kDirChunk;
   const int nt = min(kDirChunk, mL - t0);
-  int32_t *crow = dv.codes + ((int64_t)s * dv.ncap + i) * mL + t0;
   const double *ud = dir + (size_t)d * kDirChunk;
 #pragma unroll
   for (int t = 0; t < kDirChunk; ++t) {
     if (t < nt) {
       const double x = __dadd_rn(__dmul_rn(r[t], inv_c), __dmul_rn(sv, ud[t]));
       const int32_t code = to_code(x);
-      crow[t] = code;
+      dv.codes[code_index(dv.ntile, mL, s, i, t0 + t)] = code;
       bs.codes_dm[((int64_t)s * mL + t0 + t) * n + i] = code;
     }
   }
@@ -183,9 +185,13 @@ __device__ __forceinline__ uint32_t block_excl_scan256(uint32_t v, uint32_t *wsu
 // four stable LSD passes of 8 bits over the order-preserving unsigned image
 // of the code.  Pass 0 reads the direction-major codes with implicit tokens;
 // passes alternate between the scratch pair and the index lists, ending in
-// the index lists.  Inside a pass, tiles of 256 entries are ranked in entry
-// order: lanes with the same digit are matched with ballots, waves are
-// ordered through per-wave digit counts.
+// the index lists.  The four digit histograms come from one initial pass (a
+// pass never changes the multiset of keys).  Inside a pass, tiles of 256
+// entries are ranked in entry order: lanes with the same digit are matched
+// with ballots, waves are ordered through per-wave digit counts; the loads of
+// kSortGroup tiles are issued together.
+constexpr int kSortGroup = 16;
+
 __global__ __launch_bounds__(256) void k_sort_lists(Dev dv, BuildScratch bs, int64_t n) {
   const int lst = blockIdx.x;  // s * mL + t
   const int s = lst / dv.mL, t = lst % dv.mL;
@@ -196,11 +202,25 @@ __global__ __launch_bounds__(256) void k_sort_lists(Dev dv, BuildScratch bs, int
   int32_t *oc = dv.list_code + ((int64_t)s * dv.mL + t) * dv.ncap;
   int32_t *oi = dv.list_id + ((int64_t)s * dv.mL + t) * dv.ncap;
 
-  __shared__ uint32_t cnt[256];
+  __shared__ uint32_t cnt[4][256];
   __shared__ uint32_t base[256];
   __shared__ uint32_t wcnt[4][256];
   __shared__ uint32_t woff[4][256];
   __shared__ uint32_t wsum[4];
+
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    cnt[k][tid] = 0;
+    wcnt[k][tid] = 0;
+  }
+  __syncthreads();
+  for (int64_t x = tid; x < n; x += 256) {
+    const uint32_t key = (uint32_t)in0[x] ^ 0x80000000u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) atomicAdd(&cnt[k][(key >> (8 * k)) & 255u], 1u);
+  }
+  __syncthreads();
+  const unsigned long long lt = lanemask_lt();
 
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 8 * pass;
@@ -208,50 +228,45 @@ __global__ __launch_bounds__(256) void k_sort_lists(Dev dv, BuildScratch bs, int
     const int32_t *si = pass == 0 ? nullptr : ((pass & 1) ? ti : oi);
     int32_t *dc = (pass & 1) ? oc : tc;
     int32_t *di = (pass & 1) ? oi : ti;
+    base[tid] = block_excl_scan256(cnt[pass][tid], wsum);
+    __syncthreads();
 
-    cnt[tid] = 0;
+    for (int64_t g0 = 0; g0 < n; g0 += 256 * kSortGroup) {
+      int32_t gc[kSortGroup], gi[kSortGroup];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) wcnt[k][tid] = 0;
-    __syncthreads();
-    for (int64_t x = tid; x < n; x += 256) {
-      const uint32_t key = (uint32_t)sc[x] ^ 0x80000000u;
-      atomicAdd(&cnt[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    base[tid] = block_excl_scan256(cnt[tid], wsum);
-    __syncthreads();
-
-    for (int64_t t0 = 0; t0 < n; t0 += 256) {
-      const int64_t x = t0 + tid;
-      const bool valid = x < n;
-      int32_t code = 0, id = 0;
-      uint32_t dig = 0;
-      if (valid) {
-        code = sc[x];
-        id = si ? si[x] : (int32_t)x;
-        dig = (((uint32_t)code ^ 0x80000000u) >> shift) & 255u;
+      for (int k = 0; k < kSortGroup; ++k) {  // clamped, unconditional loads
+        const int64_t x = g0 + 256 * k + tid;
+        const int64_t xc = x < n ? x : 0;
+        gc[k] = sc[xc];
+        gi[k] = si ? si[xc] : (int32_t)x;
       }
-      const unsigned long long act = __ballot(valid);
-      const unsigned long long mt = match_bits(dig, 8, act);
-      const int lrank = popc64(mt & lanemask_lt());
-      const bool leader = valid && ((mt >> lane) >> 1) == 0ull;
-      if (leader) wcnt[w][dig] = (uint32_t)popc64(mt);
-      __syncthreads();
-      {
-        uint32_t o = base[tid];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          woff[k][tid] = o;
-          o += wcnt[k][tid];
-          wcnt[k][tid] = 0;
+      for (int k = 0; k < kSortGroup; ++k) {
+        const int64_t x = g0 + 256 * k + tid;
+        const bool valid = x < n;
+        const uint32_t dig = valid ? ((((uint32_t)gc[k] ^ 0x80000000u) >> shift) & 255u) : 0u;
+        const unsigned long long act = __ballot(valid);
+        const unsigned long long mt = match_bits(dig, 8, act);
+        const int lrank = popc64(mt & lt);
+        const bool leader = valid && ((mt >> lane) >> 1) == 0ull;
+        if (leader) wcnt[w][dig] = (uint32_t)popc64(mt);
+        __syncthreads();
+        {
+          uint32_t o = base[tid];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            woff[q][tid] = o;
+            o += wcnt[q][tid];
+            wcnt[q][tid] = 0;
+          }
+          base[tid] = o;
         }
-        base[tid] = o;
-      }
-      __syncthreads();
-      if (valid) {
-        const uint32_t pos = woff[w][dig] + (uint32_t)lrank;
-        dc[pos] = code;
-        di[pos] = id;
+        __syncthreads();
+        if (valid) {
+          const uint32_t pos = woff[w][dig] + (uint32_t)lrank;
+          dc[pos] = gc[k];
+          di[pos] = gi[k];
+        }
       }
     }
     __syncthreads();
@@ -271,6 +286,7 @@ __global__ __launch_bounds__(64) void k_pages(Dev dv, BuildScratch bs, int64_t n
   extern __shared__ int32_t lds[];
   int32_t *cnt = lds;
   int32_t *open = lds + dv.ncell;
+  constexpr int kAhead = 16;  // tiles of cells loaded per batch
   const int s = blockIdx.x;
   const int lane = threadIdx.x;
   const int p = dv.p;
@@ -281,40 +297,57 @@ __global__ __launch_bounds__(64) void k_pages(Dev dv, BuildScratch bs, int64_t n
   __syncthreads();
   int32_t npg = 0;
   const unsigned long long lt = lanemask_lt();
-  for (int64_t t0 = 0; t0 < n; t0 += 64) {
-    const int64_t i = t0 + lane;
-    const bool valid = i < n;
-    const uint32_t c = valid ? bs.cell[(int64_t)s * n + i] : 0u;
-    const unsigned long long act = __ballot(valid);
-    const unsigned long long mt = match_bits(c, dv.D, act);
-    const int base = valid ? cnt[c] : 0;
-    const int prev_open = valid ? open[c] : -1;
-    const int rank = base + popc64(mt & lt);
-    const int slot = rank & (p - 1);
-    const bool first = valid && slot == 0;
-    const unsigned long long fm = __ballot(first);
-    const int cs = rank - slot;
-    int pid;
-    if (cs >= base) {
-      const int fl = valid ? nth_set_bit(mt, cs - base) : 0;
-      pid = npg + popc64(fm & ((1ull << fl) - 1ull));
-    } else {
-      pid = prev_open;
+  const uint32_t *cells = bs.cell + (int64_t)s * n;
+  uint32_t cur[kAhead], nxt[kAhead];
+#pragma unroll
+  for (int k = 0; k < kAhead; ++k) {  // clamped, unconditional loads
+    const int64_t i = 64 * k + lane;
+    cur[k] = cells[i < n ? i : 0];
+  }
+  for (int64_t b0 = 0; b0 < n; b0 += 64 * kAhead) {
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) {
+      const int64_t i = b0 + 64 * (kAhead + k) + lane;
+      nxt[k] = cells[i < n ? i : 0];
     }
-    const bool leader = valid && ((mt >> lane) >> 1) == 0ull;
-    __builtin_amdgcn_wave_barrier();
-    if (leader) {
-      cnt[c] = rank + 1;
-      open[c] = pid;
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) {
+      const int64_t i = b0 + 64 * k + lane;
+      const bool valid = i < n;
+      const uint32_t c = valid ? cur[k] : 0u;
+      const unsigned long long act = __ballot(valid);
+      const unsigned long long mt = match_bits(c, dv.D, act);
+      const int base = valid ? cnt[c] : 0;
+      const int prev_open = valid ? open[c] : -1;
+      const int rank = base + popc64(mt & lt);
+      const int slot = rank & (p - 1);
+      const bool first = valid && slot == 0;
+      const unsigned long long fm = __ballot(first);
+      const int cs = rank - slot;
+      int pid;
+      if (cs >= base) {
+        const int fl = valid ? nth_set_bit(mt, cs - base) : 0;
+        pid = npg + popc64(fm & ((1ull << fl) - 1ull));
+      } else {
+        pid = prev_open;
+      }
+      const bool leader = valid && ((mt >> lane) >> 1) == 0ull;
+      __builtin_amdgcn_wave_barrier();
+      if (leader) {
+        cnt[c] = rank + 1;
+        open[c] = pid;
+      }
+      npg += popc64(fm);
+      if (valid) {
+        dv.loc[(int64_t)s * dv.ncap + i] = pid * p + slot;
+        dv.page_tokens[((int64_t)s * dv.pcap + pid) * p + slot] = (int32_t)i;
+        if (first) dv.page_cell[(int64_t)s * dv.pcap + pid] = (int32_t)c;
+        if (slot == p - 1 || leader) dv.page_len[(int64_t)s * dv.pcap + pid] = slot + 1;
+      }
+      __builtin_amdgcn_wave_barrier();
     }
-    npg += popc64(fm);
-    if (valid) {
-      dv.loc[(int64_t)s * dv.ncap + i] = pid * p + slot;
-      dv.page_tokens[((int64_t)s * dv.pcap + pid) * p + slot] = (int32_t)i;
-      if (first) dv.page_cell[(int64_t)s * dv.pcap + pid] = (int32_t)c;
-      if (slot == p - 1 || leader) dv.page_len[(int64_t)s * dv.pcap + pid] = slot + 1;
-    }
-    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) cur[k] = nxt[k];
   }
   __syncthreads();
   if (lane == 0) dv.npages[s] = npg;
@@ -347,46 +380,74 @@ __global__ __launch_bounds__(256) void k_scatter(Dev dv, const void *K, const vo
 
 // ---------------------------------------------------------------- insert
 
-// One block per stream appends token n: projection with the stored bound,
-// list entries at position n of each direction's insert region, the page
-// rule, and the pool rows.  Lane t < mL forms r_t; lane 255 forms |k|^2.
+// One block per stream appends token n: projection with the stored bound
+// (directions staged in LDS, 32 per round; lane t forms r_t, lane 255 forms
+// |k|^2), list entries at position n of each direction's insert region, the
+// page rule, and the pool rows.
 template <int DT>
 __global__ __launch_bounds__(256) void k_insert(Dev dv, int64_t n, const void *k_new,
                                                 const void *v_new) {
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
-  const int d = dv.d, mL = dv.mL, p = dv.p;
+  const int d = dv.d, mL = dv.mL, p = dv.p, d1 = dv.d + 1;
   __shared__ float kv[128];
+  __shared__ double dl[129 * 32];
+  __shared__ double rs[kMaxMl];
+  __shared__ double ud[kMaxMl];
   __shared__ double nsq_s;
   __shared__ uint32_t cell_s;
   __shared__ int32_t loc_s;
   if (tid < d) kv[tid] = load_elem<DT>(k_new, (int64_t)s * d + tid);
   __syncthreads();
-  double r = 0.0;
-  const double *dir = dv.dirs + (size_t)(tid / kDirChunk) * (d + 1) * kDirChunk + (tid % kDirChunk);
-  if (tid < mL) {
-    for (int e = 0; e < d; ++e) r = fma((double)kv[e], dir[(size_t)e * kDirChunk], r);
-  } else if (tid == 255) {
+  if (tid == 255) {
     double a = 0.0;
+#pragma unroll 16
     for (int e = 0; e < d; ++e) a = fma((double)kv[e], (double)kv[e], a);
     nsq_s = a;
   }
-  // cell = sign bits of r on the first D directions (all in wave 0)
+  for (int t0 = 0; t0 < mL; t0 += 32) {
+    {  // every load of this thread issued before its stores
+      constexpr int kIter = (129 * 32 + 255) / 256;
+      double v[kIter];
+#pragma unroll
+      for (int k = 0; k < kIter; ++k) {  // clamped, unconditional loads
+        const int x = min(tid + 256 * k, d1 * 32 - 1);
+        const int e = x >> 5, j = x & 31, t = t0 + j;
+        const int ch = min(t / kDirChunk, dv.nchunk - 1);
+        v[k] = dv.dirs[((size_t)ch * d1 + e) * kDirChunk + (t % kDirChunk)];
+      }
+#pragma unroll
+      for (int k = 0; k < kIter; ++k) {
+        const int x = tid + 256 * k;
+        if (x < d1 * 32) dl[x] = (t0 + (x & 31)) < dv.nchunk * kDirChunk ? v[k] : 0.0;
+      }
+    }
+    __syncthreads();
+    if (tid < 32 && t0 + tid < mL) {
+      double r = 0.0;
+#pragma unroll 16
+      for (int e = 0; e < d; ++e) r = fma((double)kv[e], dl[e * 32 + tid], r);
+      rs[t0 + tid] = r;
+      ud[t0 + tid] = dl[d * 32 + tid];
+    }
+    __syncthreads();
+  }
+  // cell = sign bits of r on the first D directions (D <= 13)
   if (tid < 64) {
-    const unsigned long long bal = __ballot(tid < dv.D && r >= 0.0);
+    const unsigned long long bal = __ballot(tid < dv.D && rs[tid < mL ? tid : 0] >= 0.0);
     if (tid == 0) cell_s = (uint32_t)bal & ((1u << dv.D) - 1u);
   }
-  __syncthreads();
   if (tid < mL) {
     double b = __dsub_rn(1.0, __dmul_rn(nsq_s, dv.inv_c2[s]));
     if (b < 0.0) b = 0.0;
     const double sv = __dsqrt_rn(b);
-    const double x = __dadd_rn(__dmul_rn(r, dv.inv_c[s]), __dmul_rn(sv, dir[(size_t)d * kDirChunk]));
+    const double x = __dadd_rn(__dmul_rn(rs[tid], dv.inv_c[s]), __dmul_rn(sv, ud[tid]));
     const int32_t code = to_code(x);
-    dv.codes[((int64_t)s * dv.ncap + n) * mL + tid] = code;
+    dv.codes[code_index(dv.ntile, mL, s, n, tid)] = code;
     dv.list_code[((int64_t)s * mL + tid) * dv.ncap + n] = code;
     dv.list_id[((int64_t)s * mL + tid) * dv.ncap + n] = (int32_t)n;
   }
+  __syncthreads();
   if (tid == 0) {
     const uint32_t c = cell_s;
     const int64_t ci = (int64_t)s * dv.ncell + c;
@@ -431,7 +492,7 @@ static hipError_t build_impl(const Dev &dv, const BuildScratch &bs, int64_t n, c
   if ((e = fill_i32(dv.page_tokens, (int64_t)dv.S * dv.pcap * dv.p, -1, st))) return e;
   if ((e = fill_i32(dv.page_len, (int64_t)dv.S * dv.pcap, 0, st))) return e;
   if ((e = fill_i32(dv.page_cell, (int64_t)dv.S * dv.pcap, -1, st))) return e;
-  if ((e = fill_i32((int32_t *)dv.mark, (int64_t)dv.S * dv.ncap, 0, st))) return e;
+  if ((e = fill_i32((int32_t *)dv.attn_done, (int64_t)dv.S, 0, st))) return e;
   if ((e = fill_i32((int32_t *)dv.hist, (int64_t)dv.S * dv.L * kHistBins, 0, st))) return e;
   if ((e = fill_i32((int32_t *)dv.cand_count, (int64_t)dv.S * dv.L, 0, st))) return e;
   hipLaunchKernelGGL(k_fill_u64, dim3(1), dim3(256), 0, st, dv.maxnsq, (int64_t)dv.S, 0ull);
@@ -445,12 +506,12 @@ static hipError_t build_impl(const Dev &dv, const BuildScratch &bs, int64_t n, c
     if (c_fixed <= 0.0f)
       hipLaunchKernelGGL(k_norms<DT>, dim3(nb, dv.S), dim3(256), 0, st, dv, K, n);
     hipLaunchKernelGGL(k_project<DT>, dim3(nb, dv.nchunk, dv.S), dim3(256), 0, st, dv, bs, K,
-                       n, c_fixed);
+                       (const double *)dv.dirs, n, c_fixed);
     hipLaunchKernelGGL(k_sort_lists, dim3(dv.S * dv.mL), dim3(256), 0, st, dv, bs, n);
   } else {
     // an empty build still fixes c, 1/c and 1/c^2
-    hipLaunchKernelGGL(k_project<DT>, dim3(1, 1, dv.S), dim3(256), 0, st, dv, bs, K, n,
-                       c_fixed);
+    hipLaunchKernelGGL(k_project<DT>, dim3(1, 1, dv.S), dim3(256), 0, st, dv, bs, K,
+                       (const double *)dv.dirs, n, c_fixed);
   }
   hipLaunchKernelGGL(k_pages, dim3(dv.S), dim3(64), (size_t)dv.ncell * 2 * sizeof(int32_t), st,
                      dv, bs, n);
@@ -467,10 +528,6 @@ hipError_t launch_build(const Dev &dv, const BuildScratch &bs, int64_t n, const 
                         const void *V, const void *dirs, float c_fixed, hipStream_t st) {
   return dv.dtype == 0 ? build_impl<0>(dv, bs, n, K, V, dirs, c_fixed, st)
                        : build_impl<1>(dv, bs, n, K, V, dirs, c_fixed, st);
-}
-
-hipError_t launch_build_reset_marks(const Dev &dv, hipStream_t st) {
-  return fill_i32((int32_t *)dv.mark, (int64_t)dv.S * dv.ncap, 0, st);
 }
 
 hipError_t launch_insert(const Dev &dv, int64_t n, const void *k_new, const void *v_new,

@@ -23,6 +23,9 @@ constexpr int kHistShift = 31 - kHistBits;
 constexpr int kMaxCand = 4096;
 // Directions are stored in fp64, 16 per chunk, [chunk][d+1][16].
 constexpr int kDirChunk = 16;
+// Projection codes are stored in tiles of 64 tokens, [S][tile][mL][64]: a
+// wave reads code t of its 64 tokens as one contiguous 256-byte load.
+constexpr int kCodeTile = 64;
 
 // Every device array of one index, resolved from the caller's workspace.
 struct Dev {
@@ -30,7 +33,6 @@ struct Dev {
   int d, p, m, L, mL, g, D, k, P, k0, dtype, elem;  // elem = bytes per element
   int64_t ncap, pcap, ncell, nbuild;
   int nchunk;          // direction chunks of kDirChunk
-  int attn_tps;        // attention tokens per split
   int attn_nsplit;     // attention splits per stream
 
   double *dirs;        // [nchunk][d+1][16]
@@ -38,7 +40,8 @@ struct Dev {
   double *inv_c;       // [S]
   double *inv_c2;      // [S]
   unsigned long long *maxnsq;  // [S] bit pattern of the largest |k|^2
-  int32_t *codes;      // [S][ncap][mL]
+  int32_t *codes;      // [S][ntile][mL][64], ntile = ceil(ncap / 64)
+  int64_t ntile;
   int32_t *list_code;  // [S][mL][ncap]
   int32_t *list_id;    // [S][mL][ncap]
   int32_t *loc;        // [S][ncap]
@@ -50,7 +53,6 @@ struct Dev {
   int32_t *cell_last;    // [S][ncell]
   void *pool_k;          // [S][pcap][p][d]
   void *pool_v;
-  uint32_t *mark;        // [S][ncap] query epoch that claimed the token
 
   // per-query state
   float *qkv;            // [S][d]
@@ -61,13 +63,22 @@ struct Dev {
   uint32_t *cand_count;  // [S][L]
   unsigned long long *bnd;  // [S][L][ncap]
   uint32_t *bnd_count;      // [S][L]
-  unsigned long long *cs_key;  // [S][L*k0]
-  int32_t *cs_id;              // [S][L*k0]
-  uint32_t *c_count;           // [S]
-  float *attn_part;            // [S][nsplit][g][d+2]
+  unsigned long long *rr_key;  // [S][L*k0] rank key of each scored candidate
+  int32_t *rr_id;              // [S][L*k0]
+  int32_t *rr_pg;              // [S][L*k0] its page
+  uint32_t *rr_count;          // [S]
+  uint32_t *cmark;             // [S][mwords] tokens already in the query's rerank list
+  int64_t mwords;              // ceil(ncap / 32)
+  float *attn_part;         // [S][nsplit][g][d+2]
+  uint32_t *attn_done;      // [S] splits finished (the last one merges and resets it)
 };
 
 // Build scratch (caller-owned, only used while the build runs).
+// Address of code t of token i of stream s.
+__host__ __device__ inline int64_t code_index(int64_t ntile, int mL, int s, int64_t i, int t) {
+  return (((int64_t)s * ntile + (i >> 6)) * mL + t) * kCodeTile + (i & 63);
+}
+
 struct BuildScratch {
   int32_t *codes_dm;  // [S][mL][n]
   int32_t *tmp_code;  // [S][mL][n]
@@ -76,8 +87,8 @@ struct BuildScratch {
 };
 
 // Decode-time kernels that the optional event timer reports separately.
-enum KernelId { KID_INSERT = 0, KID_QSCAN, KID_QCOLLECT, KID_QFINAL, KID_ATTN_PART,
-                KID_ATTN_COMBINE, KID_COUNT };
+enum KernelId { KID_INSERT = 0, KID_QPREP, KID_QSCAN, KID_QCOLLECT, KID_QFINAL, KID_ATTN,
+                KID_COUNT };
 
 // Optional host-side event timer (owned by an index); null when timing is off.
 struct Timer;
@@ -87,12 +98,10 @@ void timer_mark(Timer *tm, int kid, hipStream_t st);    // after each launch
 // Host launchers (each returns the hipGetLastError of its launches).
 hipError_t launch_build(const Dev &dv, const BuildScratch &bs, int64_t n, const void *K,
                         const void *V, const void *dirs, float c_fixed, hipStream_t st);
-hipError_t launch_build_reset_marks(const Dev &dv, hipStream_t st);
 hipError_t launch_insert(const Dev &dv, int64_t n, const void *k_new, const void *v_new,
                          hipStream_t st, Timer *tm);
-hipError_t launch_query(const Dev &dv, int64_t n, const void *q, uint32_t epoch,
-                        int32_t *page_ids, int32_t *n_pages, int32_t *topk_ids,
-                        hipStream_t st, Timer *tm);
+hipError_t launch_query(const Dev &dv, int64_t n, const void *q, int32_t *page_ids,
+                        int32_t *n_pages, int32_t *topk_ids, hipStream_t st, Timer *tm);
 hipError_t launch_attn(const Dev &dv, const void *q, const int32_t *page_ids,
                        const int32_t *n_pages, float *out, hipStream_t st, Timer *tm);
 

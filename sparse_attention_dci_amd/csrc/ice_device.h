@@ -43,6 +43,14 @@ __device__ __forceinline__ void load8(const void *base, int64_t i, float (&v)[8]
   }
 }
 
+// Workgroup barrier that orders LDS only: global loads and stores stay in
+// flight across it (__syncthreads would wait for every outstanding one).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ int32_t to_code(double x) {
   double v = rint(x * kCodeScale);  // scaling by 2^29 is exact
   v = fmin(fmax(v, -(double)kCodeMax), (double)kCodeMax);
