@@ -48,26 +48,25 @@ def algorithmic_bytes(w, kernel: str, ntok: int, n_cand: float, attended: float)
     (S streams): the per-unit figures times the units one launch processes.
 
     insert    new k, v in; pool rows, codes and list entries out: 4d*elem + 12*mL
-    qprep     query heads and the fp64 directions: g*d*elem + (d+1)*mL*8
-    qscan     every token's m*L projection codes: 4*mL per token
-    qcollect  every token's L completion distances written by the scan: 4*L per token
-    qfinal    the key row of every reranked candidate: d*elem per candidate
+    qscan     every token's m*L projection codes (4*mL per token), the query heads
+              and the fp64 directions (g*d*elem + (d+1)*mL*8)
+    qcollect  the key row of every reranked candidate: d*elem per candidate
+    qfinal    the rerank list (rank key, token, page): 16 bytes per candidate
     attn      K and V rows of every attended token, the queries and the outputs
     """
-    S, d, mL, L, g = w.streams, w.d, w.mL, w.L, w.g
+    S, d, mL, g = w.streams, w.d, w.mL, w.g
     elem = 2 if w.dtype == "bf16" else 4
     per_stream = {
         "insert": 4.0 * d * elem + 12.0 * mL,
-        "qprep": g * d * elem + (d + 1) * mL * 8.0,
-        "qscan": ntok * mL * 4.0,
-        "qcollect": ntok * L * 4.0,
-        "qfinal": n_cand * d * elem,
+        "qscan": ntok * mL * 4.0 + g * d * elem + (d + 1) * mL * 8.0,
+        "qcollect": n_cand * d * elem,
+        "qfinal": n_cand * 16.0,
         "attn": attended * 2 * d * elem + g * d * (elem + 4),
     }
     return S * per_stream.get(kernel, 0.0)
 
 
-STEP_KERNELS = ("insert", "qprep", "qscan", "qfinal", "attn")  # excludes the scan's own scratch
+STEP_KERNELS = ("insert", "qscan", "qcollect", "qfinal", "attn")
 
 
 def cpu_baseline(w, K, V, q, U, k_new, v_new, reps: int):

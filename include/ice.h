@@ -167,7 +167,9 @@ const char *ice_status_string(ice_status s);
  *   page_cell     int32   [S][Pcap]      -1 for unused pages
  *   npages        int32   [S]
  *   cell_count    int32   [S][n_cells]   tokens per cell
- *   pool_k/v      dtype   [S][Pcap][p][d]
+ *   pool_k        dtype   [S][Pcap][p][d]  key of each page slot
+ *   pool_v        dtype   [S][Pcap][d][p]  values, element-major inside a
+ *                 page (value element e of slot j at [e][j])
  *   qcode         int32   [S][mL]        last query's projection codes
  *   cand          int32   [S][L][k0]     last query's candidates per composite,
  *                 cand_count int32 [S][L] of them valid, in no fixed order */
@@ -188,7 +190,7 @@ ice_status ice_index_layout(const ice_index *idx, ice_layout *out);
  * kernel (arrays of ICE_TIMED_KERNELS, in the order of ice_timing_name) and
  * clears the record.  The event records add a little time between kernels;
  * leave timing off for end-to-end latency. */
-#define ICE_TIMED_KERNELS 6 /* insert, qprep, qscan, qcollect, qfinal, attn */
+#define ICE_TIMED_KERNELS 6 /* insert, qscan, qcollect, qfinal, attn, amerge */
 ice_status ice_timing_enable(ice_index *idx, int enable);
 ice_status ice_timing_read(ice_index *idx, double *total_ms, int64_t *launches);
 const char *ice_timing_name(int kernel);

@@ -246,7 +246,7 @@ class Index:
             "npages": (torch.int32, (S,)),
             "cell_count": (torch.int32, (S, y["n_cells"])),
             "pool_k": (self.dtype, (S, pcap, p, d)),
-            "pool_v": (self.dtype, (S, pcap, p, d)),
+            "pool_v": (self.dtype, (S, pcap, d, p)),
             "qcode": (torch.int32, (S, mL)),
             "cand": (torch.int32, (S, L, y["k0"])),
             "cand_count": (torch.int32, (S, L)),
@@ -261,4 +261,6 @@ class Index:
         t = raw.view(dt).view(shape)
         if name == "codes":  # tiles of 64 tokens -> [S][ncap][mL] (a copy)
             t = t.permute(0, 1, 3, 2).reshape(S, -1, mL)[:, :ncap]
+        if name == "pool_v":  # element-major pages -> [S][pcap][p][d] (a view)
+            t = t.permute(0, 1, 3, 2)
         return t

@@ -59,7 +59,6 @@ void timer_mark(Timer *tm, int kid, hipStream_t st) {
 namespace {
 
 constexpr int64_t kAlign = 256;
-constexpr int kAttnTps = 32;  // tokens per attention block (kTps in ice_attn.hip)
 constexpr int64_t kMaxPages = 65536;
 
 int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -84,10 +83,10 @@ int derive_depth(int64_t n, int p, int mL) {
 struct Layout {
   int D, nchunk, k0, elem, attn_nsplit;
   int64_t ncell, pcap;
-  int64_t dirs, norm_c, inv_c, inv_c2, maxnsq, codes, list_code, list_id, loc, page_tokens,
+  int64_t dirs, dirs32, norm_c, inv_c, inv_c2, maxnsq, codes, list_code, list_id, loc, page_tokens,
       page_len, page_cell, npages, cell_count, cell_last, pool_k, pool_v, qkv, qcode, mbuf,
-      hist, cand, cand_count, bnd, bnd_count, rr_key, rr_id, rr_pg, rr_count, cmark,
-      attn_part, attn_done;
+      hist, cand, cand_count, bnd, bnd_rk, bnd_pg, bnd_count, rr_key, rr_id, rr_pg, rr_count,
+      attn_part;
   int64_t total;
 };
 
@@ -131,7 +130,7 @@ ice_status make_layout(const ice_params *prm, int32_t S, int64_t n, int64_t ncap
   y.nchunk = (mL + ice::kDirChunk - 1) / ice::kDirChunk;
   y.k0 = prm->k0 > 0 ? prm->k0 : prm->budget_k;
   y.elem = prm->dtype == ICE_F32 ? 4 : 2;
-  y.attn_nsplit = (prm->budget_k + kAttnTps - 1) / kAttnTps;
+  y.attn_nsplit = (prm->budget_k + ice::kAttnTpb - 1) / ice::kAttnTpb;
   const int64_t Sl = S, Ll = prm->L, g = prm->gqa_group;
   int64_t o = 0;
   auto seg = [&](int64_t bytes) {
@@ -140,6 +139,7 @@ ice_status make_layout(const ice_params *prm, int32_t S, int64_t n, int64_t ncap
     return at;
   };
   y.dirs = seg((int64_t)y.nchunk * (d + 1) * ice::kDirChunk * 8);
+  y.dirs32 = seg((int64_t)d * ((mL + 31) / 32 * 32) * 4);
   y.norm_c = seg(Sl * 4);
   y.inv_c = seg(Sl * 8);
   y.inv_c2 = seg(Sl * 8);
@@ -163,14 +163,14 @@ ice_status make_layout(const ice_params *prm, int32_t S, int64_t n, int64_t ncap
   y.cand = seg(Sl * Ll * y.k0 * 4);
   y.cand_count = seg(Sl * Ll * 4);
   y.bnd = seg(Sl * Ll * ncap * 8);
+  y.bnd_rk = seg(Sl * Ll * ncap * 8);
+  y.bnd_pg = seg(Sl * Ll * ncap * 4);
   y.bnd_count = seg(Sl * Ll * 4);
   y.rr_key = seg(Sl * Ll * y.k0 * 8);
   y.rr_id = seg(Sl * Ll * y.k0 * 4);
   y.rr_pg = seg(Sl * Ll * y.k0 * 4);
   y.rr_count = seg(Sl * 4);
-  y.cmark = seg(Sl * ((ncap + 31) / 32) * 4);
   y.attn_part = seg(Sl * y.attn_nsplit * g * (d + 2) * 4);
-  y.attn_done = seg(Sl * 4);
   y.total = o;
   *L = y;
   return ICE_OK;
@@ -267,6 +267,8 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
   dv.nchunk = y.nchunk;
   dv.attn_nsplit = y.attn_nsplit;
   dv.dirs = (double *)(w + y.dirs);
+  dv.dirs32 = (float *)(w + y.dirs32);
+  dv.mLp = (dv.mL + 31) / 32 * 32;
   dv.norm_c = (float *)(w + y.norm_c);
   dv.inv_c = (double *)(w + y.inv_c);
   dv.inv_c2 = (double *)(w + y.inv_c2);
@@ -291,15 +293,14 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
   dv.cand = (int32_t *)(w + y.cand);
   dv.cand_count = (uint32_t *)(w + y.cand_count);
   dv.bnd = (unsigned long long *)(w + y.bnd);
+  dv.bnd_rk = (unsigned long long *)(w + y.bnd_rk);
+  dv.bnd_pg = (int32_t *)(w + y.bnd_pg);
   dv.bnd_count = (uint32_t *)(w + y.bnd_count);
   dv.rr_key = (unsigned long long *)(w + y.rr_key);
   dv.rr_id = (int32_t *)(w + y.rr_id);
   dv.rr_pg = (int32_t *)(w + y.rr_pg);
   dv.rr_count = (uint32_t *)(w + y.rr_count);
-  dv.cmark = (uint32_t *)(w + y.cmark);
-  dv.mwords = (capacity_tokens + 31) / 32;
   dv.attn_part = (float *)(w + y.attn_part);
-  dv.attn_done = (uint32_t *)(w + y.attn_done);
 
   ice::BuildScratch bs;
   std::memset(&bs, 0, sizeof(bs));
@@ -396,8 +397,8 @@ ice_status ice_timing_read(ice_index *idx, double *total_ms, int64_t *launches) 
 }
 
 const char *ice_timing_name(int kernel) {
-  static const char *names[ICE_TIMED_KERNELS] = {"insert", "qprep",  "qscan",
-                                                 "qcollect", "qfinal", "attn"};
+  static const char *names[ICE_TIMED_KERNELS] = {"insert", "qscan", "qcollect",
+                                                 "qfinal", "attn",  "amerge"};
   return (kernel >= 0 && kernel < ICE_TIMED_KERNELS) ? names[kernel] : "";
 }
 

@@ -1,162 +1,337 @@
 // Sparse attention over every token of the selected pages (IceCache paper
 // page, Figure 2 step (3)).
 //
-// The tokens of a stream's selected pages, taken page after page, are split
-// into chunks of kTps tokens; one block per (chunk, stream) stages the
-// chunk's K and V rows in LDS (each page is p contiguous rows, so the copy is
-// a run of 16-byte loads), forms the logits of all g query heads of the
-// stream (each dot product split over up to 8 lanes), takes a half-wave
-// softmax per head, and writes an fp32 partial (max, sum, weighted values).
-// The last block of a stream to finish (a device-scope ticket taken after a
-// release fence) merges the partials.
+// The tokens of a stream's selected pages, taken page after page, are cut
+// into blocks of kAttnTpb = 256; a block is 8 waves of 32 tokens.  Both
+// products run on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16, fp32
+// accumulation), 16 query heads wide (heads past g are zero):
+//   logits  S^T[token][head] = K rows x q^T: a lane feeds 8 consecutive key
+//           elements of one token, read straight from the key pool;
+//   values  O[head][e] = P x V: a lane feeds the probabilities of 8 tokens
+//           for one head and the values of the same 8 tokens for one
+//           element.  Those 8 tokens are two runs of 4 consecutive page
+//           slots, which is why values are stored element-major inside a
+//           page: each run is one 8-byte (bf16) or 16-byte (fp32) load.
+// fp32 keys, values and queries enter as a bf16 pair hi + lo and take three
+// products (hi*hi, hi*lo, lo*hi); probabilities always do, so the only
+// precision loss against fp32 arithmetic is the dropped lo*lo term (relative
+// 2^-16).  The softmax is exact per block (block-wide max); blocks of one
+// stream are merged by a second kernel when the budget spans several.
 #include "ice_device.h"
 
 namespace ice {
 
-constexpr int kTps = 32;  // tokens per block
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <int DT>
-__global__ __launch_bounds__(256) void k_attn(Dev dv, const void *q, const int32_t *page_ids,
-                                              const int32_t *n_pages, float *out) {
-  const int s = blockIdx.y, sp = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int d = dv.d, g = dv.g, p = dv.p;
-  __shared__ float qs[kMaxGroup * 128];
-  __shared__ float kt[kTps * 129];
-  __shared__ float vt[kTps * 128];
-  __shared__ float z[kMaxGroup * kTps];
-  __shared__ float hm[kMaxGroup], hl[kMaxGroup];
-  __shared__ int32_t rowpage[kTps];
-  __shared__ int32_t rowok[kTps];
-  __shared__ uint32_t ticket;
+constexpr int kAttnWaves = kAttnTpb / 32;
+constexpr int kAttnThreads = kAttnWaves * 64;
 
-  if (tid < kTps) {
-    const int gt = sp * kTps + tid;  // token of the concatenated selected pages
-    const int pi = gt / p;
-    // the page id and the page count are loaded together
-    const int32_t pg = page_ids[(int64_t)s * dv.P + min(pi, dv.P - 1)];
-    const int np = min(n_pages[s], dv.P);
-    rowpage[tid] = (pi < np && pg >= 0 && pg < dv.pcap) ? pg : -1;
-  }
-  for (int x = tid; x < g * d; x += 256) qs[x] = load_elem<DT>(q, (int64_t)s * g * d + x);
-  __syncthreads();
-  // stage rows (fp32 in LDS; K rows padded to 129 floats against bank conflicts);
-  // the page length is loaded together with the row chunks
-  for (int x = tid; x < kTps * (d / 8); x += 256) {
-    const int r = x / (d / 8), c8 = (x % (d / 8)) * 8;
-    const int pg = rowpage[r];
-    const int pgc = pg >= 0 ? pg : 0;  // clamped: the loads are unconditional
-    const int slot = (sp * kTps + r) % p;
-    float kx[8], vx[8];
-    const int64_t row = ((int64_t)s * dv.pcap + pgc) * p + slot;
-    load8<DT>(dv.pool_k, row * d + c8, kx);
-    load8<DT>(dv.pool_v, row * d + c8, vx);
-    const bool ok = pg >= 0 && slot < dv.page_len[(int64_t)s * dv.pcap + pgc];
-    if (!ok) {  // empty slots hold no token (and arbitrary bytes): zero them
-#pragma unroll
-      for (int j = 0; j < 8; ++j) kx[j] = vx[j] = 0.0f;
-    }
-    if (c8 == 0) rowok[r] = ok;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      kt[r * 129 + c8 + j] = kx[j];
-      vt[r * 128 + c8 + j] = vx[j];
-    }
-  }
-  __syncthreads();
-  // logits: tp lanes per (head, token) pair
-  const float scale = 1.0f / sqrtf((float)d);
-  const int npair = g * kTps;
-  int tp = 1;
-  while (tp < 8 && tp * 2 * npair <= 256) tp *= 2;
-  for (int x = tid; x < npair * tp; x += 256) {
-    const int pair = x / tp, part = x % tp;
-    const int h = pair / kTps, r = pair % kTps;
-    const int chunk = d / tp, e0 = part * chunk;
-    const float *qh = qs + h * d + e0;
-    const float *kr = kt + r * 129 + e0;
-    float acc = 0.0f;
-#pragma unroll 16
-    for (int e = 0; e < chunk; ++e) acc = fmaf(qh[e], kr[e], acc);
-    for (int o = tp >> 1; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-    if (part == 0) z[h * kTps + r] = rowok[r] ? acc * scale : -INFINITY;
-  }
-  __syncthreads();
-  // softmax pieces per head, one half-wave per head
-  for (int h0 = 0; h0 < g; h0 += 8) {
-    const int h = h0 + (tid >> 5), r = tid & 31;
-    if (h < g) {
-      const float v = z[h * kTps + r];
-      float mx = v;
-      for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 32));
-      const float e = mx == -INFINITY ? 0.0f : __expf(v - mx);
-      float sum = e;
-      for (int o = 16; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 32);
-      z[h * kTps + r] = e;
-      if (r == 0) {
-        hm[h] = mx;
-        hl[h] = sum;
-      }
-    }
-  }
-  __syncthreads();
-  float *part = dv.attn_part + ((int64_t)s * dv.attn_nsplit + sp) * g * (d + 2);
-  for (int x = tid; x < g * d; x += 256) {
-    const int h = x / d, e = x % d;
-    float acc = 0.0f;
-#pragma unroll
-    for (int r = 0; r < kTps; ++r) acc = fmaf(z[h * kTps + r], vt[r * 128 + e], acc);
-    part[h * (d + 2) + e] = acc;
-  }
-  if (tid < g) {
-    part[tid * (d + 2) + d] = hm[tid];
-    part[tid * (d + 2) + d + 1] = hl[tid];
-  }
-
-  // The last split of the stream to finish merges every split's partial.
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) ticket = atomicAdd(&dv.attn_done[s], 1u);
-  __syncthreads();
-  if (ticket != (uint32_t)dv.attn_nsplit - 1u) return;
-  __threadfence();
-  const float *base = dv.attn_part + (int64_t)s * dv.attn_nsplit * g * (d + 2);
-  const int ns = dv.attn_nsplit;
-  for (int x = tid; x < g * d; x += 256) {
-    const int h = x / d, e = x % d;
-    float M = -INFINITY;
-#pragma unroll 8
-    for (int k = 0; k < ns; ++k) M = fmaxf(M, base[((int64_t)k * g + h) * (d + 2) + d]);
-    float num = 0.0f, den = 0.0f;
-    if (M != -INFINITY) {
-#pragma unroll 8
-      for (int k = 0; k < ns; ++k) {
-        const float *pp = base + ((int64_t)k * g + h) * (d + 2);
-        const float mk = pp[d];
-        const float wgt = mk == -INFINITY ? 0.0f : __expf(mk - M);
-        num = fmaf(wgt, pp[e], num);
-        den = fmaf(wgt, pp[d + 1], den);
-      }
-    }
-    out[((int64_t)s * g + h) * d + e] = den > 0.0f ? num / den : 0.0f;
-  }
-  if (tid == 0) dv.attn_done[s] = 0;
+__device__ __forceinline__ floatx4 mfma(u32x4 a, u32x4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-template <int DT>
+// Round to nearest even bf16 (finite inputs), as the high 16 bits.
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Two floats -> packed bf16 pairs hi (x ~ hi) and lo (x - hi ~ lo).
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t &hi, uint32_t &lo) {
+  const uint32_t h0 = bf16_rne(x0), h1 = bf16_rne(x1);
+  const uint32_t l0 = bf16_rne(x0 - __uint_as_float(h0 << 16));
+  const uint32_t l1 = bf16_rne(x1 - __uint_as_float(h1 << 16));
+  hi = h0 | (h1 << 16);
+  lo = l0 | (l1 << 16);
+}
+
+// Eight fp32 values -> bf16x8 hi and lo operands.
+__device__ __forceinline__ void split8(const float (&x)[8], u32x4 &hi, u32x4 &lo) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t h, l;
+    split2(x[2 * j], x[2 * j + 1], h, l);
+    hi[j] = h;
+    lo[j] = l;
+  }
+}
+
+__device__ __forceinline__ u32x4 ld16(const void *p) {
+  const uint4 v = *reinterpret_cast<const uint4 *>(p);
+  return u32x4{v.x, v.y, v.z, v.w};
+}
+
+// Grid (attn_nsplit, S), 512 threads.  Wave w of block b takes tokens
+// b*256 + w*32 .. +31 of the stream's selection.  Lane (G, c) = (lane / 16,
+// lane % 16).
+template <int DT, int D>
+__global__ __launch_bounds__(kAttnThreads) void k_attn(Dev dv, const void *q,
+                                                       const int32_t *page_ids,
+                                                       const int32_t *n_pages, float *out) {
+  constexpr int KK = D / 32;  // 32-element chunks of a key row
+  constexpr int EB = D / 16;  // 16-element blocks of the output
+  const int s = blockIdx.y, sp = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int G = lane >> 4, c = lane & 15;
+  const int g = dv.g, p = dv.p, P = dv.P;
+  const int64_t pcap = dv.pcap;
+  __shared__ float smax[kAttnWaves][16], ssum[kAttnWaves][16];
+  __shared__ float red[kAttnWaves][kMaxGroup * D];
+
+  // 1. pages: the token this lane feeds to the logits (T0 + 16a + c) and the
+  // slot runs it feeds to the values (T0 + 16a + 4G .. +3), a = 0, 1.  All
+  // loads are unconditional; invalid pages read page 0 and are masked.
+  const int T0 = sp * kAttnTpb + w * 32;
+  const int np = min(n_pages[s], P);
+  int32_t pgk[2], pgv[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    pgk[a] = page_ids[(int64_t)s * P + min((T0 + 16 * a + c) / p, P - 1)];
+    pgv[a] = page_ids[(int64_t)s * P + min((T0 + 16 * a + 4 * G) / p, P - 1)];
+  }
+  bool okv[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const bool okk = (T0 + 16 * a + c) / p < np && pgk[a] >= 0 && pgk[a] < pcap;
+    okv[a] = (T0 + 16 * a + 4 * G) / p < np && pgv[a] >= 0 && pgv[a] < pcap;
+    pgk[a] = okk ? pgk[a] : 0;
+    pgv[a] = okv[a] ? pgv[a] : 0;
+  }
+  int32_t plen[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) plen[a] = dv.page_len[(int64_t)s * pcap + pgv[a]];
+
+  // 2. loads: key chunks, value runs, the query heads (zero past g)
+  u32x4 kr[2][KK][DT == 0 ? 2 : 1];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int64_t row = ((int64_t)s * pcap + pgk[a]) * p + (T0 + 16 * a + c) % p;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int e0 = 32 * kk + 8 * G;
+      if constexpr (DT == 0) {
+        const float *kp = reinterpret_cast<const float *>(dv.pool_k) + row * D + e0;
+        kr[a][kk][0] = ld16(kp);
+        kr[a][kk][1] = ld16(kp + 4);
+      } else {
+        kr[a][kk][0] = ld16(reinterpret_cast<const uint16_t *>(dv.pool_k) + row * D + e0);
+      }
+    }
+  }
+  // value run of group a, output block eb: elements (16eb + c) of slots
+  // (T0 + 16a + 4G) % p .. +3
+  u32x4 vr[EB][DT == 0 ? 2 : 1];
+#pragma unroll
+  for (int eb = 0; eb < EB; ++eb) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int64_t col = (((int64_t)s * pcap + pgv[a]) * D + 16 * eb + c) * p +
+                          (T0 + 16 * a + 4 * G) % p;
+      if constexpr (DT == 0) {
+        vr[eb][a] = ld16(reinterpret_cast<const float *>(dv.pool_v) + col);
+      } else {
+        const uint2 v2 = *reinterpret_cast<const uint2 *>(
+            reinterpret_cast<const uint16_t *>(dv.pool_v) + col);
+        vr[eb][0][2 * a] = v2.x;
+        vr[eb][0][2 * a + 1] = v2.y;
+      }
+    }
+  }
+  const int hq = c < g ? c : 0;
+  u32x4 qh[KK], ql[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const int64_t o = ((int64_t)s * g + hq) * D + 32 * kk + 8 * G;
+    if constexpr (DT == 0) {
+      const float *qp = reinterpret_cast<const float *>(q) + o;
+      const u32x4 x0 = ld16(qp), x1 = ld16(qp + 4);
+      float f[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f[j] = __uint_as_float(x0[j]);
+        f[4 + j] = __uint_as_float(x1[j]);
+      }
+      split8(f, qh[kk], ql[kk]);
+    } else {
+      qh[kk] = ld16(reinterpret_cast<const uint16_t *>(q) + o);
+      ql[kk] = u32x4{0u, 0u, 0u, 0u};
+    }
+    if (c >= g) qh[kk] = ql[kk] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // 3. logits: lane (G, c) gets token T0 + 16a + 4G + i, head c, in z[a][i]
+  const float scale = 1.0f / sqrtf((float)D);
+  float z[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      if constexpr (DT == 0) {
+        float f[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f[j] = __uint_as_float(kr[a][kk][0][j]);
+          f[4 + j] = __uint_as_float(kr[a][kk][1][j]);
+        }
+        u32x4 kh, kl;
+        split8(f, kh, kl);
+        acc = mfma(kh, qh[kk], acc);
+        acc = mfma(kh, ql[kk], acc);
+        acc = mfma(kl, qh[kk], acc);
+      } else {
+        acc = mfma(kr[a][kk][0], qh[kk], acc);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int slot = (T0 + 16 * a + 4 * G + i) % p;
+      z[a][i] = (okv[a] && slot < plen[a]) ? acc[i] * scale : -INFINITY;
+    }
+  }
+
+  // 4. block-wide softmax pieces per head
+  float mx = -INFINITY;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, z[a][i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  if (lane < 16) smax[w][lane] = mx;
+  lds_barrier();
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kAttnWaves; ++k) M = fmaxf(M, smax[k][c]);
+  float pr[2][4], lsum = 0.0f;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pr[a][i] = z[a][i] == -INFINITY ? 0.0f : __expf(z[a][i] - M);
+      lsum += pr[a][i];
+    }
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (lane < 16) ssum[w][lane] = lsum;
+
+  // 5. values: A = probabilities (head c; tokens of run 0 then run 1), B =
+  // value runs (element 16eb + c; same tokens), output lane (G, c) holds
+  // head 4G + i, element 16eb + c
+  u32x4 ph, pl;
+  {
+    const float f[8] = {pr[0][0], pr[0][1], pr[0][2], pr[0][3],
+                        pr[1][0], pr[1][1], pr[1][2], pr[1][3]};
+    split8(f, ph, pl);
+  }
+  floatx4 o[EB];
+#pragma unroll
+  for (int eb = 0; eb < EB; ++eb) {
+    floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    float f[8];
+    if constexpr (DT == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f[j] = __uint_as_float(vr[eb][0][j]);
+        f[4 + j] = __uint_as_float(vr[eb][1][j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f[2 * j] = __uint_as_float(vr[eb][0][j] << 16);
+        f[2 * j + 1] = __uint_as_float(vr[eb][0][j] & 0xffff0000u);
+      }
+    }
+    // slots holding no token may hold any bytes (zero times NaN is NaN):
+    // the token's logit is -inf exactly there, for every head
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (z[j >> 2][j & 3] == -INFINITY) f[j] = 0.0f;
+    u32x4 vh, vl;
+    split8(f, vh, vl);
+    acc = mfma(ph, vh, acc);
+    acc = mfma(pl, vh, acc);
+    if constexpr (DT == 0) acc = mfma(ph, vl, acc);
+    o[eb] = acc;
+  }
+
+  // 6. sum the waves (in wave order), normalise or leave a partial
+#pragma unroll
+  for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * G + i < g) red[w][(4 * G + i) * D + 16 * eb + c] = o[eb][i];
+  lds_barrier();
+  const int ns = dv.attn_nsplit;
+  for (int x = tid; x < g * D; x += kAttnThreads) {
+    const int h = x / D, e = x % D;
+    float num = 0.0f, den = 0.0f, bm = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kAttnWaves; ++k) {
+      num += red[k][x];
+      den += ssum[k][h];
+      bm = fmaxf(bm, smax[k][h]);
+    }
+    if (ns == 1) {
+      out[((int64_t)s * g + h) * D + e] = den > 0.0f ? num / den : 0.0f;
+    } else {
+      float *pp = dv.attn_part + (((int64_t)s * ns + sp) * g + h) * (D + 2);
+      pp[e] = num;
+      if (e == 0) {
+        pp[D] = bm;
+        pp[D + 1] = den;
+      }
+    }
+  }
+}
+
+// Merges the blocks of each stream: one block per stream.
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_merge(Dev dv, float *out) {
+  const int s = blockIdx.x, g = dv.g, ns = dv.attn_nsplit;
+  const float *base = dv.attn_part + (int64_t)s * ns * g * (D + 2);
+  for (int x = threadIdx.x; x < g * D; x += 256) {
+    const int h = x / D, e = x % D;
+    float M = -INFINITY;
+    for (int k = 0; k < ns; ++k) M = fmaxf(M, base[((int64_t)k * g + h) * (D + 2) + D]);
+    float num = 0.0f, den = 0.0f;
+    if (M != -INFINITY) {
+      for (int k = 0; k < ns; ++k) {
+        const float *pp = base + ((int64_t)k * g + h) * (D + 2);
+        const float mk = pp[D];
+        const float wgt = mk == -INFINITY ? 0.0f : __expf(mk - M);
+        num = fmaf(wgt, pp[e], num);
+        den = fmaf(wgt, pp[D + 1], den);
+      }
+    }
+    out[((int64_t)s * g + h) * D + e] = den > 0.0f ? num / den : 0.0f;
+  }
+}
+
+template <int DT, int D>
 static hipError_t attn_impl(const Dev &dv, const void *q, const int32_t *page_ids,
                             const int32_t *n_pages, float *out, hipStream_t st, Timer *tm) {
   timer_begin(tm, st);
-  hipLaunchKernelGGL(k_attn<DT>, dim3(dv.attn_nsplit, dv.S), dim3(256), 0, st, dv, q, page_ids,
-                     n_pages, out);
+  hipLaunchKernelGGL((k_attn<DT, D>), dim3(dv.attn_nsplit, dv.S), dim3(kAttnThreads), 0, st, dv,
+                     q, page_ids, n_pages, out);
   timer_mark(tm, KID_ATTN, st);
+  if (dv.attn_nsplit > 1) {
+    hipLaunchKernelGGL(k_attn_merge<D>, dim3(dv.S), dim3(256), 0, st, dv, out);
+    timer_mark(tm, KID_AMERGE, st);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_attn(const Dev &dv, const void *q, const int32_t *page_ids,
                        const int32_t *n_pages, float *out, hipStream_t st, Timer *tm) {
-  return dv.dtype == 0 ? attn_impl<0>(dv, q, page_ids, n_pages, out, st, tm)
-                       : attn_impl<1>(dv, q, page_ids, n_pages, out, st, tm);
+  if (dv.dtype == 0)
+    return dv.d == 128 ? attn_impl<0, 128>(dv, q, page_ids, n_pages, out, st, tm)
+                       : attn_impl<0, 64>(dv, q, page_ids, n_pages, out, st, tm);
+  return dv.d == 128 ? attn_impl<1, 128>(dv, q, page_ids, n_pages, out, st, tm)
+                     : attn_impl<1, 64>(dv, q, page_ids, n_pages, out, st, tm);
 }
 
 }  // namespace ice

@@ -49,6 +49,13 @@ __global__ void k_dirs(Dev dv, const void *dirs) {
     const int t = ch * kDirChunk + j;
     dv.dirs[x] = t < dv.mL ? (double)load_elem<DT>(dirs, (int64_t)t * (dv.d + 1) + e) : 0.0;
   }
+  // fp32 copy of the first d coordinates, element-major (every value is exact in fp32)
+  const int64_t total32 = (int64_t)dv.d * dv.mLp;
+  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < total32;
+       x += (int64_t)gridDim.x * blockDim.x) {
+    const int e = (int)(x / dv.mLp), t = (int)(x % dv.mLp);
+    dv.dirs32[x] = t < dv.mL ? load_elem<DT>(dirs, (int64_t)t * (dv.d + 1) + e) : 0.0f;
+  }
 }
 
 // ---------------------------------------------------------------- norms
@@ -357,9 +364,8 @@ __global__ __launch_bounds__(64) void k_pages(Dev dv, BuildScratch bs, int64_t n
   }
 }
 
-// Copy every key and value row to its page slot (16 bytes per thread).
-__global__ __launch_bounds__(256) void k_scatter(Dev dv, const void *K, const void *V,
-                                                 int64_t n) {
+// Copy every key row to its page slot (16 bytes per thread).
+__global__ __launch_bounds__(256) void k_scatter(Dev dv, const void *K, int64_t n) {
   const int64_t row_bytes = (int64_t)dv.d * dv.elem;
   const int64_t cpr = row_bytes / 16;
   const int64_t total = (int64_t)dv.S * n * cpr;
@@ -373,8 +379,56 @@ __global__ __launch_bounds__(256) void k_scatter(Dev dv, const void *K, const vo
     const int64_t src = row * row_bytes + cc * 16;
     *reinterpret_cast<uint4 *>((char *)dv.pool_k + dst) =
         *reinterpret_cast<const uint4 *>((const char *)K + src);
-    *reinterpret_cast<uint4 *>((char *)dv.pool_v + dst) =
-        *reinterpret_cast<const uint4 *>((const char *)V + src);
+  }
+}
+
+// Values into the element-major page layout ([e][slot] inside a page): a block
+// transposes whole pages through LDS, rows in and element columns out, both
+// as 16-byte accesses.  Empty slots are written as zeros.
+constexpr int kScatterTile = 32 * 1024;
+
+__global__ __launch_bounds__(256) void k_scatter_v(Dev dv, const void *V, int64_t n) {
+  const int s = blockIdx.y;
+  const int p = dv.p, d = dv.d, elem = dv.elem;
+  const int row_bytes = d * elem;
+  const int pb = max(1, kScatterTile / (p * row_bytes));  // pages per round
+  const int cpr = row_bytes / 16;                          // 16-byte chunks per row
+  const int epc = 16 / elem;                               // elements per 16 bytes
+  const int cpe = p / epc;                                 // 16-byte chunks per column
+  __shared__ uint4 tile[kScatterTile / 16];
+  const int64_t npg = dv.npages[s];
+  for (int64_t pg0 = (int64_t)blockIdx.x * pb; pg0 < npg; pg0 += (int64_t)gridDim.x * pb) {
+    const int np = (int)min((int64_t)pb, npg - pg0);
+    for (int x = threadIdx.x; x < np * p * cpr; x += 256) {
+      const int j = x / (p * cpr), slot = (x / cpr) % p, ch = x % cpr;
+      const int32_t tok = dv.page_tokens[((int64_t)s * dv.pcap + pg0 + j) * p + slot];
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (tok >= 0 && tok < n)
+        v = reinterpret_cast<const uint4 *>(V)[((int64_t)s * n + tok) * cpr + ch];
+      tile[(j * p + slot) * cpr + ch] = v;
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < np * d * cpe; x += 256) {
+      const int j = x / (d * cpe), e = (x / cpe) % d, c = x % cpe;
+      uint32_t wds[4];
+      if (elem == 2) {
+        const uint16_t *t16 = reinterpret_cast<const uint16_t *>(tile);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int s0 = c * 8 + 2 * u;
+          wds[u] = (uint32_t)t16[(j * p + s0) * d + e] |
+                   ((uint32_t)t16[(j * p + s0 + 1) * d + e] << 16);
+        }
+      } else {
+        const uint32_t *t32 = reinterpret_cast<const uint32_t *>(tile);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) wds[u] = t32[(j * p + c * 4 + u) * d + e];
+      }
+      const int64_t dst = (((int64_t)s * dv.pcap + pg0 + j) * d + e) * p + c * epc;
+      *reinterpret_cast<uint4 *>((char *)dv.pool_v + dst * elem) =
+          make_uint4(wds[0], wds[1], wds[2], wds[3]);
+    }
+    __syncthreads();
   }
 }
 
@@ -470,14 +524,16 @@ __global__ __launch_bounds__(256) void k_insert(Dev dv, int64_t n, const void *k
     loc_s = lc;
   }
   __syncthreads();
+  // key row at its slot; value element e at [page][e][slot]
   const int64_t row = ((int64_t)s * dv.pcap * p + loc_s) * d;
+  const int64_t vcol = ((int64_t)s * dv.pcap + loc_s / p) * d * p + (loc_s % p);
   if (tid < d) {
     if constexpr (DT == 0) {
       reinterpret_cast<float *>(dv.pool_k)[row + tid] = reinterpret_cast<const float *>(k_new)[(int64_t)s * d + tid];
-      reinterpret_cast<float *>(dv.pool_v)[row + tid] = reinterpret_cast<const float *>(v_new)[(int64_t)s * d + tid];
+      reinterpret_cast<float *>(dv.pool_v)[vcol + (int64_t)tid * p] = reinterpret_cast<const float *>(v_new)[(int64_t)s * d + tid];
     } else {
       reinterpret_cast<uint16_t *>(dv.pool_k)[row + tid] = reinterpret_cast<const uint16_t *>(k_new)[(int64_t)s * d + tid];
-      reinterpret_cast<uint16_t *>(dv.pool_v)[row + tid] = reinterpret_cast<const uint16_t *>(v_new)[(int64_t)s * d + tid];
+      reinterpret_cast<uint16_t *>(dv.pool_v)[vcol + (int64_t)tid * p] = reinterpret_cast<const uint16_t *>(v_new)[(int64_t)s * d + tid];
     }
   }
 }
@@ -492,7 +548,6 @@ static hipError_t build_impl(const Dev &dv, const BuildScratch &bs, int64_t n, c
   if ((e = fill_i32(dv.page_tokens, (int64_t)dv.S * dv.pcap * dv.p, -1, st))) return e;
   if ((e = fill_i32(dv.page_len, (int64_t)dv.S * dv.pcap, 0, st))) return e;
   if ((e = fill_i32(dv.page_cell, (int64_t)dv.S * dv.pcap, -1, st))) return e;
-  if ((e = fill_i32((int32_t *)dv.attn_done, (int64_t)dv.S, 0, st))) return e;
   if ((e = fill_i32((int32_t *)dv.hist, (int64_t)dv.S * dv.L * kHistBins, 0, st))) return e;
   if ((e = fill_i32((int32_t *)dv.cand_count, (int64_t)dv.S * dv.L, 0, st))) return e;
   hipLaunchKernelGGL(k_fill_u64, dim3(1), dim3(256), 0, st, dv.maxnsq, (int64_t)dv.S, 0ull);
@@ -519,7 +574,11 @@ static hipError_t build_impl(const Dev &dv, const BuildScratch &bs, int64_t n, c
     const int64_t total = (int64_t)dv.S * n * ((int64_t)dv.d * dv.elem / 16);
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(k_scatter, dim3((unsigned)blocks), dim3(256), 0, st, dv, K, V, n);
+    hipLaunchKernelGGL(k_scatter, dim3((unsigned)blocks), dim3(256), 0, st, dv, K, n);
+    const int pb = (kScatterTile / (dv.p * dv.d * dv.elem)) > 0 ? kScatterTile / (dv.p * dv.d * dv.elem) : 1;
+    int64_t vb = (dv.pcap + pb - 1) / pb;
+    if (vb > 256) vb = 256;
+    hipLaunchKernelGGL(k_scatter_v, dim3((unsigned)vb, dv.S), dim3(256), 0, st, dv, V, n);
   }
   return hipGetLastError();
 }

@@ -26,6 +26,8 @@ constexpr int kDirChunk = 16;
 // Projection codes are stored in tiles of 64 tokens, [S][tile][mL][64]: a
 // wave reads code t of its 64 tokens as one contiguous 256-byte load.
 constexpr int kCodeTile = 64;
+// Sparse attention: tokens of the selected pages per block (8 waves of 32).
+constexpr int kAttnTpb = 256;
 
 // Every device array of one index, resolved from the caller's workspace.
 struct Dev {
@@ -33,9 +35,11 @@ struct Dev {
   int d, p, m, L, mL, g, D, k, P, k0, dtype, elem;  // elem = bytes per element
   int64_t ncap, pcap, ncell, nbuild;
   int nchunk;          // direction chunks of kDirChunk
-  int attn_nsplit;     // attention splits per stream
+  int attn_nsplit;     // attention blocks per stream, ceil(k / kAttnTpb)
 
   double *dirs;        // [nchunk][d+1][16]
+  float *dirs32;       // [d][mLp] the first d coordinates, mLp = mL rounded up to 32, zero past mL
+  int mLp;
   float *norm_c;       // [S]
   double *inv_c;       // [S]
   double *inv_c2;      // [S]
@@ -51,8 +55,8 @@ struct Dev {
   int32_t *npages;       // [S]
   int32_t *cell_count;   // [S][ncell]
   int32_t *cell_last;    // [S][ncell]
-  void *pool_k;          // [S][pcap][p][d]
-  void *pool_v;
+  void *pool_k;          // [S][pcap][p][d]  key rows, slot-major
+  void *pool_v;          // [S][pcap][d][p]  value columns, element-major within a page
 
   // per-query state
   float *qkv;            // [S][d]
@@ -61,16 +65,15 @@ struct Dev {
   uint32_t *hist;        // [S][L][kHistBins]
   int32_t *cand;         // [S][L][k0]
   uint32_t *cand_count;  // [S][L]
-  unsigned long long *bnd;  // [S][L][ncap]
+  unsigned long long *bnd;  // [S][L][ncap] boundary-bin entries (M << 32 | token)
+  unsigned long long *bnd_rk;  // [S][L][ncap] their rank keys
+  int32_t *bnd_pg;          // [S][L][ncap] their pages
   uint32_t *bnd_count;      // [S][L]
   unsigned long long *rr_key;  // [S][L*k0] rank key of each scored candidate
   int32_t *rr_id;              // [S][L*k0]
   int32_t *rr_pg;              // [S][L*k0] its page
   uint32_t *rr_count;          // [S]
-  uint32_t *cmark;             // [S][mwords] tokens already in the query's rerank list
-  int64_t mwords;              // ceil(ncap / 32)
-  float *attn_part;         // [S][nsplit][g][d+2]
-  uint32_t *attn_done;      // [S] splits finished (the last one merges and resets it)
+  float *attn_part;         // [S][nsplit][g][d+2] (values, max logit, softmax sum)
 };
 
 // Build scratch (caller-owned, only used while the build runs).
@@ -87,7 +90,7 @@ struct BuildScratch {
 };
 
 // Decode-time kernels that the optional event timer reports separately.
-enum KernelId { KID_INSERT = 0, KID_QPREP, KID_QSCAN, KID_QCOLLECT, KID_QFINAL, KID_ATTN,
+enum KernelId { KID_INSERT = 0, KID_QSCAN, KID_QCOLLECT, KID_QFINAL, KID_ATTN, KID_AMERGE,
                 KID_COUNT };
 
 // Optional host-side event timer (owned by an index); null when timing is off.

@@ -10,24 +10,27 @@
 // visits 60-85% of all list entries before k0 tokens complete, so it would
 // touch most of them anyway) followed by an exact selection:
 //
-//   k_qprep     one block per stream: fp32 GQA mean, fp64 projection of the
-//               normalised query to codes (directions staged in LDS), and the
-//               per-query counters and histogram cleared;
-//   k_qscan     M_i for every token and composite, a histogram of its top 11
-//               bits;
-//   k_qcollect  tokens in bins below the k0-th smallest bin are candidates;
-//               boundary-bin tokens are parked with their (M_i, i) key;
+//   k_qscan     derives the query codes (fp32 GQA mean, fp64 projection) while
+//               its first code loads are in flight, then M_i for every token
+//               and composite and a histogram of the top 11 bits of M_i;
+//   k_qcollect  tokens in bins below the k0-th smallest bin b* are
+//               candidates, tokens in bin b* are parked with their (M_i, i)
+//               key; both kinds are scored exactly (fp64, ascending element
+//               order) here, many blocks in parallel;
 //   k_qfinal    one 1024-thread block per stream: exact selection inside the
-//               boundary bins, union of the composites (a per-query token bitmap), exact fp64
-//               rerank, bitonic sort by (score desc, token asc), top-k and the
-//               page walk.
+//               boundary bins, the union of the composites (LDS hash), a
+//               bucket sort by (score desc, token asc), top-k and the page
+//               walk; it leaves a clean histogram for the next query.
 #include "ice_device.h"
 
 namespace ice {
 
+constexpr int kScanThreads = 512;
+constexpr int kScanTpb = 1024;      // tokens per scan range / collect block
 constexpr int kFinalThreads = 1024;
-constexpr int kHashSlots = 8192;  // 2 * kMaxCand
-constexpr int kBndLds = 4096;      // boundary keys ranked in LDS
+constexpr int kHashSlots = 8192;    // 2 * kMaxCand
+constexpr int kBndLds = 2048;       // boundary entries ranked in LDS
+constexpr int kBuckets = 2048;
 
 // ---------------------------------------------------------------- helpers
 
@@ -79,73 +82,10 @@ __device__ void wave_find_bin(const uint32_t *h, uint32_t target, uint32_t &bin,
   below = __shfl(bl, src);
 }
 
-// Directions t0 .. t0+31 into LDS as dl[e * 32 + j] (fp64, zero past mL).
-// For 256-thread blocks: each thread issues all of its loads before storing.
-__device__ void stage_dirs32(const Dev &dv, int t0, double *dl) {
-  constexpr int kIter = (129 * 32 + 255) / 256;
-  const int d1 = dv.d + 1, tot = d1 * 32;
-  double v[kIter];
-#pragma unroll
-  for (int k = 0; k < kIter; ++k) {
-    // clamped addresses keep every load unconditional (a predicated load
-    // would wait for its result at the branch join)
-    const int x = min(threadIdx.x + 256 * k, tot - 1);
-    const int e = x >> 5, j = x & 31, t = t0 + j;
-    const int ch = min(t / kDirChunk, dv.nchunk - 1);
-    v[k] = dv.dirs[((size_t)ch * d1 + e) * kDirChunk + (t % kDirChunk)];
-  }
-#pragma unroll
-  for (int k = 0; k < kIter; ++k) {
-    const int x = threadIdx.x + 256 * k;
-    if (x < tot) dl[x] = (t0 + (x & 31)) < dv.nchunk * kDirChunk ? v[k] : 0.0;
-  }
-}
-
-// Exact fp64 score <q_kv, k> in ascending element order (every product of an
-// fp32 and a key element is exact in fp64).  Up to sixteen 16-byte loads of
-// the row are in flight ahead of their part of the chain.
-template <int DT, int D, int G>
-__device__ __forceinline__ double exact_score_row(const float *qkv, const void *pool, int64_t row) {
-  constexpr int kEpl = DT == 0 ? 4 : 8;   // elements per 16-byte load
-  constexpr int kLoads = D / kEpl;        // loads per row
-  constexpr int kGroup = kLoads < G ? kLoads : G;  // loads in flight: 4*G VGPRs
-  const uint4 *src = reinterpret_cast<const uint4 *>(
-      reinterpret_cast<const char *>(pool) + row * (DT == 0 ? 4 : 2));
-  double acc = 0.0;
-#pragma unroll 1
-  for (int g0 = 0; g0 < kLoads; g0 += kGroup) {
-    uint4 raw[kGroup];
-#pragma unroll
-    for (int k = 0; k < kGroup; ++k) raw[k] = src[g0 + k];
-#pragma unroll
-    for (int k = 0; k < kGroup; ++k) {
-      const uint32_t wv[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
-      const int e0 = (g0 + k) * kEpl;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if constexpr (DT == 0) {
-          acc = fma((double)qkv[e0 + j], (double)__uint_as_float(wv[j]), acc);
-        } else {
-          acc = fma((double)qkv[e0 + 2 * j], (double)__uint_as_float(wv[j] << 16), acc);
-          acc = fma((double)qkv[e0 + 2 * j + 1], (double)__uint_as_float(wv[j] & 0xffff0000u), acc);
-        }
-      }
-    }
-  }
-  return acc;
-}
-
-template <int DT, int G>
-__device__ __forceinline__ double exact_score(const Dev &dv, const float *qkv, int s, int32_t lc) {
-  const int64_t row = ((int64_t)s * dv.pcap * dv.p + lc) * dv.d;
-  return dv.d == 128 ? exact_score_row<DT, 128, G>(qkv, dv.pool_k, row)
-                     : exact_score_row<DT, 64, G>(qkv, dv.pool_k, row);
-}
-
-// Exact fp64 scores of ids[0..cnt) by a block of NT threads: per round of
-// as many tokens as ROWBYTES of LDS holds, one round trip gathers their page
+// Exact fp64 scores of ids[0..cnt) by a block of NT threads: per round of as
+// many tokens as ROWBYTES of LDS holds, one round trip gathers their page
 // slots, one stages their key rows in LDS, then one thread per row runs the
-// ordered chain.  emit(x, id, slot, score) receives each result.  lcs needs
+// ordered chain.  emit(x, slot, score) receives each result.  lcs needs
 // ROWBYTES / 128 entries.
 template <int DT, int NT, int ROWBYTES, typename Emit>
 __device__ void block_score(const Dev &dv, int s, const int32_t *ids, uint32_t cnt,
@@ -160,7 +100,7 @@ __device__ void block_score(const Dev &dv, int s, const int32_t *ids, uint32_t c
   for (uint32_t b0 = 0; b0 < cnt; b0 += cap) {
     const uint32_t nr = min(cap, cnt - b0);
     if ((uint32_t)tid < nr) lcs[tid] = dv.loc[(int64_t)s * dv.ncap + ids[b0 + tid]];
-    __syncthreads();
+    lds_barrier();
     uint4 v[kIter];
 #pragma unroll
     for (int k = 0; k < kIter; ++k) {  // unconditional loads (row 0 stands in past nr)
@@ -176,7 +116,7 @@ __device__ void block_score(const Dev &dv, int s, const int32_t *ids, uint32_t c
       const int r = x / cpr, c = x % cpr;
       if ((uint32_t)r < nr) reinterpret_cast<uint4 *>(rows + r * row_words)[c] = v[k];
     }
-    __syncthreads();
+    lds_barrier();
     if ((uint32_t)tid < nr) {
       const uint32_t *rw = rows + tid * row_words;
       double acc = 0.0;
@@ -191,147 +131,206 @@ __device__ void block_score(const Dev &dv, int s, const int32_t *ids, uint32_t c
           acc = fma((double)qkv[2 * e2 + 1], (double)__uint_as_float(wv & 0xffff0000u), acc);
         }
       }
-      emit(b0 + tid, ids[b0 + tid], lcs[tid], acc);
+      emit(b0 + tid, lcs[tid], acc);
     }
-    __syncthreads();
+    lds_barrier();
   }
-}
-
-// ---------------------------------------------------------------- prep
-
-// q_kv = fp32 mean of the g heads (left fold, then times fp32(1/g));
-// qcode_t = code(<q_kv, u_t[:d]> / |q_kv|) with the dot products and the norm
-// in fp64, ascending element order.  Also clears the query's counters and
-// histogram.
-template <int DT>
-__global__ __launch_bounds__(256) void k_qprep(Dev dv, const void *q) {
-  const int s = blockIdx.x;
-  const int tid = threadIdx.x, d = dv.d, mL = dv.mL, g = dv.g, L = dv.L;
-  __shared__ float qkv[128];
-  __shared__ double dl[129 * 32];
-  __shared__ double zs[kMaxMl];
-  __shared__ double qsq;
-  if (tid < d) {
-    const float inv_g = (float)__ddiv_rn(1.0, (double)g);
-    float acc = load_elem<DT>(q, (int64_t)s * g * d + tid);
-    for (int h = 1; h < g; ++h)
-      acc = __fadd_rn(acc, load_elem<DT>(q, ((int64_t)s * g + h) * d + tid));
-    qkv[tid] = __fmul_rn(acc, inv_g);
-  }
-  if (tid < L) {
-    dv.cand_count[s * L + tid] = 0;
-    dv.bnd_count[s * L + tid] = 0;
-  }
-  if (tid == 0) dv.rr_count[s] = 0;
-  for (int64_t x = tid; x < dv.mwords; x += 256) dv.cmark[(int64_t)s * dv.mwords + x] = 0;
-  uint32_t *hist = dv.hist + (int64_t)s * L * kHistBins;
-  for (int x = tid; x < L * kHistBins; x += 256) hist[x] = 0;
-  __syncthreads();
-  if (tid == 255) {
-    double a = 0.0;
-#pragma unroll 16
-    for (int e = 0; e < d; ++e) a = fma((double)qkv[e], (double)qkv[e], a);
-    qsq = a;
-  }
-  for (int t0 = 0; t0 < mL; t0 += 32) {
-    stage_dirs32(dv, t0, dl);
-    __syncthreads();
-    if (tid < 32 && t0 + tid < mL) {
-      double z = 0.0;
-#pragma unroll 16
-      for (int e = 0; e < d; ++e) z = fma((double)qkv[e], dl[e * 32 + tid], z);
-      zs[t0 + tid] = z;
-    }
-    __syncthreads();
-  }
-  if (tid < mL) {
-    const double qn = __dsqrt_rn(qsq);
-    const double qb = qn > 0.0 ? __ddiv_rn(zs[tid], qn) : 0.0;
-    dv.qcode[(int64_t)s * mL + tid] = to_code(qb);
-  }
-  if (tid < d) dv.qkv[(int64_t)s * d + tid] = qkv[tid];
 }
 
 // ---------------------------------------------------------------- scan
 
-// Grid (blocks, S); each 512-thread block covers kScanTpb = 1024 tokens:
-// wave w takes tiles 2w and 2w+1 of the block, lane j token j of a tile, and
-// reads code t of its 64 tokens as one contiguous 256-byte load (32 codes of
-// both tiles in flight at a time).  Histogram in LDS when L <= 6, else
-// straight to global.
-constexpr int kScanTpb = 1024;
+// Buffer resource over a byte range: loads past its end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
 
-template <bool LDS_HIST>
-__global__ __launch_bounds__(512) void k_qscan(Dev dv, int64_t n) {
-  const int s = blockIdx.y;
+__device__ __forceinline__ int32_t ld_code(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// 1-D grid of S * ceil(n / kScanTpb) blocks, 512 threads.  Block b serves
+// stream b % S (consecutive blocks take different streams, so with S a
+// multiple of 8 all blocks of a stream land on one XCD and share its L2) and
+// the b / S-th range of kScanTpb = 1024 tokens: wave w takes tiles 2w and
+// 2w+1 of the range, lane j token j of a tile, and reads code t of its 64
+// tokens as one contiguous 256-byte load.
+// The block first derives the query codes: q_kv = fp32 mean of the g heads
+// (left fold, then times fp32(1/g)), qcode_t = code(<q_kv, u_t[:d]> / |q_kv|)
+// with the dot products and the norm in fp64, ascending element order (the
+// directions are staged as fp32, which holds every stored value exactly).
+// The heads and directions are loaded first; then kPipe codes of each tile
+// go in flight, and every code slot is refilled with the code kPipe places
+// later right after it is used, so loads stay in flight across the fp64
+// chains and the composites.  R = ceil(mL / kPipe) is a template parameter:
+// the walk over code positions is straight-line code, which lets every wait
+// cover exactly the loads it needs.
+// The histogram lives in LDS when L <= 6 (over the staged directions), and
+// only the bins at or below the block's own k0-th bin are added to the global
+// one; with L > 6 every count goes straight to global.
+constexpr int kPipe = 16;
+
+template <int DT, bool LDS_HIST, int R>
+__global__ __launch_bounds__(kScanThreads) void k_qscan(Dev dv, int64_t n, const void *q) {
+  constexpr int NT = kScanThreads;
+  const int S = dv.S, s = blockIdx.x % S;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int mL = dv.mL, m = dv.m, L = dv.L;
+  const int mL = dv.mL, m = dv.m, L = dv.L, d = dv.d, g = dv.g;
+  __shared__ float qkv[128];
   __shared__ int32_t qc[kMaxMl];
-  __shared__ uint32_t hist[LDS_HIST ? 6 * kHistBins : 1];
-  if (LDS_HIST)
-    for (int x = tid; x < L * kHistBins; x += 512) hist[x] = 0;
-  if (tid < mL) qc[tid] = dv.qcode[(int64_t)s * mL + tid];
-  __syncthreads();
+  __shared__ double zs[kMaxMl];
+  __shared__ double qsq;
+  __shared__ uint32_t blim[6];
+  constexpr int kDirWords = 128 * 32;           // [e][32] fp32
+  constexpr int kHeadWords = kMaxGroup * 128;   // [g][d] fp32
+  constexpr int kBufWords = LDS_HIST ? 6 * kHistBins : kDirWords + kHeadWords;
+  static_assert(kBufWords >= kDirWords + kHeadWords, "directions and heads must fit");
+  __shared__ float lbuf[kBufWords];
+  float *dl = lbuf;
+  float *qs = lbuf + kDirWords;
+  uint32_t *hist = reinterpret_cast<uint32_t *>(lbuf);
   uint32_t *ghist = dv.hist + (int64_t)s * L * kHistBins;
-  const int64_t i0 = (int64_t)blockIdx.x * kScanTpb;
-  const int64_t i1 = min(i0 + kScanTpb, n);
-  const int64_t tile0 = (i0 >> 6) + 2 * w;  // this wave's first tile
-  const int64_t ia = tile0 * 64 + lane, ib = ia + 64;
-  const bool va = ia < i1, vb = ib < i1;
-  // tiles past the array read tile 0 instead: every load is unconditional
-  const int64_t tla = tile0 < dv.ntile ? tile0 : 0, tlb = tile0 + 1 < dv.ntile ? tile0 + 1 : 0;
-  const int32_t *pa = dv.codes + ((int64_t)s * dv.ntile + tla) * mL * kCodeTile + lane;
-  const int32_t *pb = dv.codes + ((int64_t)s * dv.ntile + tlb) * mL * kCodeTile + lane;
-  struct Run {
-    int l, j;
-    uint32_t M;
-  } ra{0, 0, 0u}, rb{0, 0, 0u};
-  auto take = [&](Run &r, int64_t i, int32_t code, int t) {
-    const uint32_t dd = absdiff(code, qc[t]);
-    r.M = dd > r.M ? dd : r.M;
-    if (++r.j == m) {
-      dv.mbuf[((int64_t)s * L + r.l) * dv.ncap + i] = r.M;
-      if (LDS_HIST)
-        atomicAdd(&hist[r.l * kHistBins + (r.M >> kHistShift)], 1u);
-      else
-        atomicAdd(&ghist[r.l * kHistBins + (r.M >> kHistShift)], 1u);
-      ++r.l;
-      r.j = 0;
-      r.M = 0;
-    }
-  };
+
+  // 1. the query heads and directions 0..31 into LDS
+  for (int x = tid; x < g * d; x += NT) qs[x] = load_elem<DT>(q, (int64_t)s * g * d + x);
+  for (int x = tid; x < d * 8; x += NT) {
+    const int e = x >> 3, c4 = (x & 7) * 4;
+    *reinterpret_cast<float4 *>(dl + e * 32 + c4) =
+        *reinterpret_cast<const float4 *>(dv.dirs32 + (int64_t)e * dv.mLp + c4);
+  }
+  lds_barrier();
+
+  // 2. the first kPipe codes of both tiles of the first range
+  const uint32_t tile_bytes = (uint32_t)mL * kCodeTile * 4;
+  const __amdgpu_buffer_rsrc_t rc =
+      byte_range(dv.codes + (int64_t)s * dv.ntile * mL * kCodeTile, (uint32_t)dv.ntile * tile_bytes);
+  const int64_t r = blockIdx.x / S;
+  const uint32_t oa = (uint32_t)(r * (kScanTpb / 64) + 2 * w) * tile_bytes + lane * 4;
+  int32_t a[kPipe], b[kPipe];
+#pragma unroll
+  for (int x = 0; x < kPipe; ++x) {
+    a[x] = ld_code(rc, oa + x * 256);
+    b[x] = ld_code(rc, oa + tile_bytes + x * 256);
+  }
+
+  // 3. query codes
+  if (tid < d) {
+    const float inv_g = (float)__ddiv_rn(1.0, (double)g);
+    float acc = qs[tid];
+    for (int h = 1; h < g; ++h) acc = __fadd_rn(acc, qs[h * d + tid]);
+    qkv[tid] = __fmul_rn(acc, inv_g);
+  }
+  lds_barrier();
+  if (tid == NT - 1) {
+    double x = 0.0;
+#pragma unroll 8
+    for (int e = 0; e < d; ++e) x = fma((double)qkv[e], (double)qkv[e], x);
+    qsq = x;
+  }
   for (int t0 = 0; t0 < mL; t0 += 32) {
-    int32_t a[32], b[32];
-#pragma unroll
-    for (int x = 0; x < 32; ++x) {
-      const int t = min(t0 + x, mL - 1);
-      a[x] = pa[(int64_t)t * kCodeTile];
-      b[x] = pb[(int64_t)t * kCodeTile];
-    }
-#pragma unroll
-    for (int x = 0; x < 32; ++x) {
-      if (t0 + x < mL) {
-        if (va) take(ra, ia, a[x], t0 + x);
-        if (vb) take(rb, ib, b[x], t0 + x);
+    if (t0 > 0) {
+      lds_barrier();
+      for (int x = tid; x < d * 8; x += NT) {
+        const int e = x >> 3, c4 = (x & 7) * 4;
+        *reinterpret_cast<float4 *>(dl + e * 32 + c4) =
+            *reinterpret_cast<const float4 *>(dv.dirs32 + (int64_t)e * dv.mLp + t0 + c4);
       }
+      lds_barrier();
+    }
+    if (tid < 32 && t0 + tid < mL) {
+      double z = 0.0;
+#pragma unroll 8
+      for (int e = 0; e < d; ++e) z = fma((double)qkv[e], (double)dl[e * 32 + tid], z);
+      zs[t0 + tid] = z;
     }
   }
+  lds_barrier();
+  if (tid < mL) {
+    const double qn = __dsqrt_rn(qsq);
+    const double qb = qn > 0.0 ? __ddiv_rn(zs[tid], qn) : 0.0;
+    qc[tid] = to_code(qb);
+  }
+  lds_barrier();
   if (LDS_HIST) {
-    __syncthreads();
-    // Flush only the bins at or below this block's own k0-th smallest bin.
-    // The k0-th smallest M of the whole stream is never in a higher bin of a
-    // block that holds at least k0 tokens, so every bin up to the global
-    // threshold bin still receives every block's count.
-    __shared__ uint32_t blim[6];
-    const int lane = tid & 63, w = tid >> 6;
-    const uint32_t ntok = (uint32_t)(i1 > i0 ? i1 - i0 : 0);
-    for (int l = w; l < L; l += 8) {
-      uint32_t b = kHistBins - 1, bl;
-      if (ntok >= (uint32_t)dv.k0 && dv.k0 > 0) wave_find_bin(hist + l * kHistBins, dv.k0, b, bl);
-      if (lane == 0) blim[l] = b;
+    for (int x = tid; x < L * kHistBins; x += NT) hist[x] = 0;
+    lds_barrier();
+  }
+
+  // 4. M per token and composite.  Composite boundaries depend on the code
+  // position only, so every branch but the ragged tail's is uniform.
+  const int64_t i0 = r * kScanTpb, i1 = min(i0 + kScanTpb, n);
+  const uint32_t ntok = (uint32_t)(i1 > i0 ? i1 - i0 : 0);
+  const int64_t ia = i0 + 128 * w + lane, ib = ia + 64;
+  const bool va = ia < i1, vb = ib < i1;
+  int32_t Ma = 0, Mb = 0;
+  int l = 0, tend = m - 1;
+  int32_t qround[kPipe];  // this round's query codes, uniform (scalar registers)
+#pragma unroll
+  for (int t = 0; t < R * kPipe; ++t) {
+    const int x = t % kPipe;
+    if (x == 0) {
+#pragma unroll
+      for (int y = 0; y < kPipe; ++y)
+        qround[y] = __builtin_amdgcn_readfirstlane(qc[min(t + y, kMaxMl - 1)]);
     }
-    __syncthreads();
-    for (int x = tid; x < L * kHistBins; x += 512) {
+    if (t < mL) {
+      const int32_t qv = qround[x];
+      const int32_t da = a[x] - qv, db = b[x] - qv;  // |da| < 2^31: no overflow
+      Ma = max(Ma, max(da, -da));
+      Mb = max(Mb, max(db, -db));
+    }
+    if (t + kPipe < R * kPipe) {
+      a[x] = ld_code(rc, oa + (t + kPipe) * 256);
+      b[x] = ld_code(rc, oa + tile_bytes + (t + kPipe) * 256);
+    }
+    if (t < mL && t == tend) {  // composite l complete (placeholders never are)
+      uint32_t *mrow = dv.mbuf + ((int64_t)s * L + l) * dv.ncap;
+      if (va) {
+        mrow[ia] = (uint32_t)Ma;
+        if (LDS_HIST)
+          atomicAdd(&hist[l * kHistBins + (Ma >> kHistShift)], 1u);
+        else
+          atomicAdd(&ghist[l * kHistBins + (Ma >> kHistShift)], 1u);
+      }
+      if (vb) {
+        mrow[ib] = (uint32_t)Mb;
+        if (LDS_HIST)
+          atomicAdd(&hist[l * kHistBins + (Mb >> kHistShift)], 1u);
+        else
+          atomicAdd(&ghist[l * kHistBins + (Mb >> kHistShift)], 1u);
+      }
+      Ma = 0;
+      Mb = 0;
+      ++l;
+      tend += m;
+    }
+  }
+
+  // the query's own outputs and counters (after the loop, so that no global
+  // store precedes a barrier while the code loads are in flight)
+  if (blockIdx.x < (unsigned)S) {
+    if (tid < d) dv.qkv[(int64_t)s * d + tid] = qkv[tid];
+    if (tid < mL) dv.qcode[(int64_t)s * mL + tid] = qc[tid];
+    if (tid < L) {  // this query's counters, used by the collect kernel
+      dv.cand_count[s * L + tid] = 0;
+      dv.bnd_count[s * L + tid] = 0;
+    }
+    if (tid == 0) dv.rr_count[s] = 0;
+  }
+
+  // 5. flush the block's histogram.  The k0-th smallest M of the stream is
+  // never in a higher bin than the k0-th smallest of a block holding at least
+  // k0 tokens, so every bin up to the global threshold bin still receives
+  // every block's count.
+  if (LDS_HIST) {
+    lds_barrier();
+    for (int l = w; l < L; l += NT / 64) {
+      uint32_t bb = kHistBins - 1, bl;
+      if (ntok >= (uint32_t)dv.k0 && dv.k0 > 0) wave_find_bin(hist + l * kHistBins, dv.k0, bb, bl);
+      if (lane == 0) blim[l] = bb;
+    }
+    lds_barrier();
+    for (int x = tid; x < L * kHistBins; x += NT) {
       const uint32_t h = hist[x];
       if (h && (uint32_t)(x % kHistBins) <= blim[x / kHistBins]) atomicAdd(&ghist[x], h);
     }
@@ -340,114 +339,143 @@ __global__ __launch_bounds__(512) void k_qscan(Dev dv, int64_t n) {
 
 // ---------------------------------------------------------------- collect
 
-// Token i is a candidate of composite l when its bin is below the k0-th
-// smallest bin b*, and its key (M << 32 | i) goes to the boundary list when
-// the bin is b*.  Candidates are gathered per block (one device atomic per
-// block and composite), each distinct candidate token is scored exactly here,
-// in parallel, and its (rank key, token, page) appended to the rerank list.
+// Blocks of kScanTpb tokens.  Token i is a candidate of composite l when its
+// bin is below the k0-th smallest bin b*, a boundary entry when its bin is b*.
+// Every candidate or boundary token of the block is scored once; the
+// below-bin ones go to the stream's rerank list, the boundary entries carry
+// their score and page to the final selection.  Appends take one device
+// atomic per block and list.
+constexpr int kCollectRowBytes = 32 * 1024;
+
 template <int DT>
-__global__ __launch_bounds__(512) void k_qcollect(Dev dv, int64_t n) {
-  const int s = blockIdx.y;
+__global__ __launch_bounds__(kScanThreads) void k_qcollect(Dev dv, int64_t n) {
+  const int s = blockIdx.x % dv.S;  // the scan's block-to-stream mapping
+  const int64_t rng = blockIdx.x / dv.S;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int L = dv.L;
   __shared__ uint32_t bstar[32];
-  __shared__ uint32_t ccount[32], cbase[32];
+  __shared__ uint32_t ccount[32], bcount[32], cbase[32], bbase[32];
+  __shared__ uint32_t nc, nrl, rbase;
   __shared__ float qkv[128];
   __shared__ int32_t cid[kScanTpb];
-  constexpr int kCollectRowBytes = 32 * 1024;
+  __shared__ unsigned long long skb[kScanTpb];
+  __shared__ int32_t spb[kScanTpb];
   __shared__ int32_t lcs[kCollectRowBytes / 128];
   __shared__ uint32_t rows[kCollectRowBytes / 4];
-  __shared__ uint32_t nc, rbase;
   const uint32_t k0e = (uint32_t)min((int64_t)dv.k0, n);
   if (k0e == 0) return;
-  const int64_t i0 = (int64_t)blockIdx.x * kScanTpb;
+  const int64_t i0 = rng * kScanTpb;
   const int64_t i1 = min(i0 + kScanTpb, n);
-  const int64_t ii[2] = {i0 + tid, i0 + 512 + tid};
+  const int64_t ii[2] = {i0 + tid, i0 + kScanThreads + tid};
   const bool vv[2] = {ii[0] < i1, ii[1] < i1};
-  // every composite distance of both tokens for the first 8 composites
+  // distances of both tokens for the first 8 composites (unconditional loads)
   uint32_t Mv[2][8];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int l = 0; l < 8; ++l) {  // unconditional loads at clamped addresses
+    for (int l = 0; l < 8; ++l) {
       const int lc = l < L ? l : 0;
       const int64_t ic = vv[u] ? ii[u] : 0;
       Mv[u][l] = dv.mbuf[((int64_t)s * L + lc) * dv.ncap + ic];
     }
+  auto Mof = [&](int u, int l) -> uint32_t {
+    uint32_t M = 0;
+    if (l < 8) {
+#pragma unroll
+      for (int x = 0; x < 8; ++x)
+        if (x == l) M = Mv[u][x];
+    } else {
+      M = dv.mbuf[((int64_t)s * L + l) * dv.ncap + (vv[u] ? ii[u] : 0)];
+    }
+    return M;
+  };
   if (tid < dv.d) qkv[tid] = dv.qkv[(int64_t)s * dv.d + tid];
-  if (tid < L) ccount[tid] = 0;
-  if (tid == 0) nc = 0;
-  for (int l = w; l < L; l += 8) {
-    uint32_t b, bl;
-    wave_find_bin(dv.hist + ((int64_t)s * L + l) * kHistBins, k0e, b, bl);
-    if (lane == 0) bstar[l] = b;
+  if (tid < L) {
+    ccount[tid] = 0;
+    bcount[tid] = 0;
+  }
+  if (tid == 0) {
+    nc = 0;
+    nrl = 0;
+  }
+  for (int l = w; l < L; l += kScanThreads / 64) {
+    uint32_t bb, bl;
+    wave_find_bin(dv.hist + ((int64_t)s * L + l) * kHistBins, k0e, bb, bl);
+    if (lane == 0) bstar[l] = bb;
   }
   __syncthreads();
-  const unsigned long long lt = lanemask_lt();
-  uint32_t masks[2];
+  // classify
+  uint32_t below[2], bnd[2];
+  int slot[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int64_t i = ii[u];
-    const bool valid = vv[u];
-    uint32_t mask = 0;
-    for (int l = 0; l < L; ++l) {
-      uint32_t M = 0xffffffffu;
-      if (l < 8) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (q == l) M = Mv[u][q];
-      } else {
-        M = dv.mbuf[((int64_t)s * L + l) * dv.ncap + (valid ? i : 0)];
-      }
-      const uint32_t b = M >> kHistShift;
-      if (valid && b < bstar[l]) mask |= 1u << l;
-      const bool is_b = valid && b == bstar[l];
-      const unsigned long long mb = __ballot(is_b);
-      if (mb) {  // rare: wave-aggregated append of boundary keys
-        const int first = __ffsll((long long)mb) - 1;
-        uint32_t base = 0;
-        if (lane == first) base = atomicAdd(&dv.bnd_count[s * L + l], (uint32_t)popc64(mb));
-        base = __shfl(base, first);
-        if (is_b)
-          dv.bnd[((int64_t)s * L + l) * dv.ncap + base + popc64(mb & lt)] =
-              ((unsigned long long)M << 32) | (uint32_t)i;
+    below[u] = 0;
+    bnd[u] = 0;
+    slot[u] = -1;
+    if (vv[u]) {
+      for (int l = 0; l < L; ++l) {
+        const uint32_t bb = Mof(u, l) >> kHistShift;
+        if (bb < bstar[l]) below[u] |= 1u << l;
+        if (bb == bstar[l]) bnd[u] |= 1u << l;
       }
     }
-    masks[u] = mask;
-    if (mask) {
-      cid[atomicAdd(&nc, 1u)] = (int32_t)i;
-      for (int l = 0; l < L; ++l)
-        if ((mask >> l) & 1u) atomicAdd(&ccount[l], 1u);
+    if (below[u] | bnd[u]) {
+      slot[u] = (int)atomicAdd(&nc, 1u);
+      cid[slot[u]] = (int32_t)ii[u];
+      if (below[u]) atomicAdd(&nrl, 1u);
+      for (int l = 0; l < L; ++l) {
+        if ((below[u] >> l) & 1u) atomicAdd(&ccount[l], 1u);
+        if ((bnd[u] >> l) & 1u) atomicAdd(&bcount[l], 1u);
+      }
     }
   }
-  __syncthreads();
+  lds_barrier();
+  // one device atomic per list for the block
   if (tid < L) {
     cbase[tid] = ccount[tid] ? atomicAdd(&dv.cand_count[s * L + tid], ccount[tid]) : 0u;
+    bbase[tid] = bcount[tid] ? atomicAdd(&dv.bnd_count[s * L + tid], bcount[tid]) : 0u;
     ccount[tid] = 0;
+    bcount[tid] = 0;
   }
-  if (tid == 64 && nc) rbase = atomicAdd(&dv.rr_count[s], nc);
-  __syncthreads();
+  if (tid == 64) {
+    rbase = nrl ? atomicAdd(&dv.rr_count[s], nrl) : 0u;
+    nrl = 0;
+  }
+  lds_barrier();
+  // exact scores of the block's candidate and boundary tokens
+  const int p = dv.p;
+  unsigned long long *skbp = skb;
+  int32_t *spbp = spb;
+  block_score<DT, kScanThreads, kCollectRowBytes>(
+      dv, s, cid, nc, qkv, lcs, rows, [skbp, spbp, p](uint32_t x, int32_t lc, double sc) {
+        skbp[x] = score_rank_key(sc);
+        spbp[x] = lc / p;
+      });
+  // the appends
+  const int64_t rr0 = (int64_t)s * L * dv.k0;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const uint32_t mask = masks[u];
-    for (int l = 0; l < L; ++l)
-      if ((mask >> l) & 1u)
-        dv.cand[((int64_t)s * L + l) * dv.k0 + cbase[l] + atomicAdd(&ccount[l], 1u)] =
-            (int32_t)ii[u];
+    if (slot[u] < 0) continue;
+    const int32_t i = (int32_t)ii[u];
+    const unsigned long long rk = skb[slot[u]];
+    const int32_t pg = spb[slot[u]];
+    if (below[u]) {
+      const int64_t o = rr0 + rbase + atomicAdd(&nrl, 1u);
+      dv.rr_key[o] = rk;
+      dv.rr_id[o] = i;
+      dv.rr_pg[o] = pg;
+    }
+    for (int l = 0; l < L; ++l) {
+      if ((below[u] >> l) & 1u)
+        dv.cand[((int64_t)s * L + l) * dv.k0 + cbase[l] + atomicAdd(&ccount[l], 1u)] = i;
+      if ((bnd[u] >> l) & 1u) {
+        const int64_t o = ((int64_t)s * L + l) * dv.ncap + bbase[l] + atomicAdd(&bcount[l], 1u);
+        dv.bnd[o] = ((unsigned long long)Mof(u, l) << 32) | (uint32_t)i;
+        dv.bnd_rk[o] = rk;
+        dv.bnd_pg[o] = pg;
+      }
+    }
   }
-  const int64_t obase = (int64_t)s * L * dv.k0 + rbase;
-  unsigned long long *rk = dv.rr_key + obase;
-  int32_t *ri = dv.rr_id + obase;
-  int32_t *rp = dv.rr_pg + obase;
-  uint32_t *mk = dv.cmark + (int64_t)s * dv.mwords;
-  const int p = dv.p;
-  block_score<DT, 512, kCollectRowBytes>(dv, s, cid, nc, qkv, lcs, rows,
-                       [rk, ri, rp, mk, p](uint32_t x, int32_t id, int32_t lc, double sc) {
-                         rk[x] = score_rank_key(sc);
-                         ri[x] = id;
-                         rp[x] = lc / p;
-                         atomicOr(&mk[id >> 5], 1u << (id & 31));
-                       });
 }
 
 // ---------------------------------------------------------------- final
@@ -496,130 +524,6 @@ __device__ unsigned long long block_select(const unsigned long long *keys, uint3
   return prefix;
 }
 
-// Element of the rerank order: rank key, token, page.
-struct RankEl {
-  unsigned long long k;
-  int32_t id, pg;
-};
-
-__device__ __forceinline__ bool rank_less(const RankEl &a, const RankEl &b) {
-  return a.k < b.k || (a.k == b.k && a.id < b.id);
-}
-
-__device__ __forceinline__ RankEl shfl_xor_el(const RankEl &e, int m) {
-  RankEl o;
-  o.k = ((unsigned long long)(uint32_t)__shfl_xor((int)(uint32_t)(e.k >> 32), m) << 32) |
-        (uint32_t)__shfl_xor((int)(uint32_t)e.k, m);
-  o.id = __shfl_xor(e.id, m);
-  o.pg = __shfl_xor(e.pg, m);
-  return o;
-}
-
-// Bitonic step for element x against its partner's value o (partner index
-// x ^ jj): in an ascending run the lower index keeps the smaller element.
-__device__ __forceinline__ void bitonic_keep(RankEl &e, const RankEl &o, uint32_t x, uint32_t jj,
-                                             uint32_t kk) {
-  const bool asc = (x & kk) == 0;
-  const bool lower = (x & jj) == 0;
-  if ((lower == asc) == rank_less(o, e)) e = o;
-}
-
-// a holds element xa, b its partner (a higher index) in the same thread.
-__device__ __forceinline__ void reg_pair(RankEl &a, RankEl &b, uint32_t xa, uint32_t kk) {
-  const bool asc = (xa & kk) == 0;
-  if (rank_less(b, a) == asc) {
-    const RankEl t = a;
-    a = b;
-    b = t;
-  }
-}
-
-// Sorts npad (a power of two <= NT*R) elements ascending by (key, token)
-// across a block of NT threads.  Element x = r*NT + tid lives in registers;
-// partner distances below 64 are wave shuffles, distances of NT and more are
-// register swaps inside a thread, the rest go through the LDS arrays xk/xi/xg.
-template <int NT, int R>
-__device__ void block_bitonic(RankEl (&el)[R], uint32_t npad, unsigned long long *xk, int32_t *xi,
-                              int32_t *xg) {
-  const int tid = threadIdx.x;
-  for (uint32_t kk = 2; kk <= npad; kk <<= 1) {
-    for (uint32_t jj = kk >> 1; jj > 0; jj >>= 1) {
-      if (jj >= (uint32_t)NT) {
-        if constexpr (R >= 2) {
-          if (jj == (uint32_t)NT) {
-#pragma unroll
-            for (int r = 0; r < R; r += 2) reg_pair(el[r], el[r + 1], r * NT + tid, kk);
-          }
-        }
-        if constexpr (R >= 4) {
-          if (jj == 2u * NT) {
-            reg_pair(el[0], el[2], tid, kk);
-            reg_pair(el[1], el[3], NT + tid, kk);
-          }
-        }
-      } else if (jj >= 64) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const uint32_t x = r * NT + tid;
-          xk[x] = el[r].k;
-          xi[x] = el[r].id;
-          xg[x] = el[r].pg;
-        }
-        __syncthreads();
-        RankEl o[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const uint32_t y = (r * NT + tid) ^ jj;
-          o[r].k = xk[y];
-          o[r].id = xi[y];
-          o[r].pg = xg[y];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < R; ++r) bitonic_keep(el[r], o[r], r * NT + tid, jj, kk);
-      } else {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const RankEl o = shfl_xor_el(el[r], (int)jj);
-          bitonic_keep(el[r], o, r * NT + tid, jj, kk);
-        }
-      }
-    }
-  }
-}
-
-// Sorts the LDS arrays (sk, si, sp)[0..npad) in place through registers.
-template <int NT, int R>
-__device__ void sort_rank_arrays(unsigned long long *sk, int32_t *si, int32_t *sp, uint32_t npad) {
-  RankEl el[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const uint32_t x = r * NT + threadIdx.x;
-    if (x < npad) {
-      el[r].k = sk[x];
-      el[r].id = si[x];
-      el[r].pg = sp[x];
-    } else {
-      el[r].k = ~0ull;
-      el[r].id = 0x7fffffff;
-      el[r].pg = 0;
-    }
-  }
-  __syncthreads();
-  block_bitonic<NT, R>(el, npad, sk, si, sp);
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const uint32_t x = r * NT + threadIdx.x;
-    if (x < npad) {
-      sk[x] = el[r].k;
-      si[x] = el[r].id;
-      sp[x] = el[r].pg;
-    }
-  }
-  __syncthreads();
-}
-
 // Inserts id into the LDS hash set; true when it was not there yet.
 __device__ __forceinline__ bool hash_insert(uint32_t *tab, int32_t id) {
   const uint32_t key = (uint32_t)id + 1u;
@@ -632,34 +536,50 @@ __device__ __forceinline__ bool hash_insert(uint32_t *tab, int32_t id) {
   }
 }
 
-constexpr int kFinalRowBytes = 48 * 1024;  // key rows staged for scoring
+__device__ __forceinline__ bool key_less(unsigned long long ka, int32_t ia, unsigned long long kb,
+                                         int32_t ib) {
+  return ka < kb || (ka == kb && ia < ib);
+}
+
+// Score back from its rank key (the inverse of score_rank_key).
+__device__ __forceinline__ double rank_key_score(unsigned long long key) {
+  const unsigned long long ord = ~key;
+  const unsigned long long b = (ord >> 63) ? (ord & 0x7fffffffffffffffull) : ~ord;
+  return __longlong_as_double((long long)b);
+}
 
 struct FinalShared {
+  unsigned long long skey[kMaxCand];  // the rerank list: rank key, token, page
+  int32_t sid[kMaxCand];
+  int32_t spg[kMaxCand];
   union {
-    unsigned long long bk[kBndLds];  // boundary keys (selection phase)
-    uint32_t rows[kFinalRowBytes / 4];  // key rows (scoring phase)
+    struct {  // boundary entries (selection phase)
+      unsigned long long bk[kBndLds];
+      unsigned long long brk[kBndLds];
+      int32_t bpg[kBndLds];
+    };
+    struct {  // bucket sort (sort phase)
+      int32_t tmp[kMaxCand];
+      int32_t inv[kMaxCand];  // rank -> position in the rerank list
+    };
   };
   union {
     uint32_t hash[kHashSlots];  // rerank-list membership (selection phase)
-    uint32_t seen[2048];        // selected pages (page walk)
+    struct {
+      uint32_t bcnt[kBuckets];
+      uint32_t bstart[kBuckets];
+      uint32_t bfill[kBuckets];
+      uint32_t seen[2048];  // selected pages (page walk)
+    };
   };
-  unsigned long long skey[kMaxCand];  // rank keys
-  int32_t sid[kMaxCand];
-  int32_t spg[kMaxCand];
   uint32_t cnt[256];
-  float qkv[128];
-  int32_t lcs[512];
   uint32_t cc[32], nb[32], need[32], boff[33], extra[32];
   uint32_t nu;
   uint32_t rr;
   unsigned long long res;
+  unsigned long long wlo[16], whi[16];
+  uint32_t wsum[16];
 };
-
-template <int DT>
-__device__ void final_add(FinalShared &sh, const Dev &dv, int s, int l, int32_t id) {
-  dv.cand[((int64_t)s * dv.L + l) * dv.k0 + sh.cc[l] + atomicAdd(&sh.extra[l], 1u)] = id;
-  if (hash_insert(sh.hash, id)) sh.sid[atomicAdd(&sh.nu, 1u)] = id;  // scored in phase C
-}
 
 template <int DT>
 __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int32_t *page_ids,
@@ -670,16 +590,14 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
   const int L = dv.L, k0 = dv.k0;
   const uint32_t k0e = (uint32_t)min((int64_t)k0, n);
 
-  // A. counts, thresholds, the query
+  // A. counts and thresholds
   for (int x = tid; x < kHashSlots; x += kFinalThreads) sh.hash[x] = 0;
-  if (tid < dv.d) sh.qkv[tid] = dv.qkv[(int64_t)s * dv.d + tid];
   if (tid < L) {
     sh.cc[tid] = dv.cand_count[s * L + tid];
     sh.nb[tid] = dv.bnd_count[s * L + tid];
     sh.extra[tid] = 0;
     sh.need[tid] = 0;
   }
-  if (tid == 0) sh.nu = 0;
   if (k0e > 0) {
     for (int l = w; l < L; l += kFinalThreads / 64) {
       uint32_t b, bl;
@@ -698,7 +616,11 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
     sh.boff[L] = o;
     sh.nu = nrr;
   }
-  // B1. the scored candidates below the boundary bins
+  __syncthreads();
+  const uint32_t nbt = sh.boff[L];
+  const bool bnd_lds = nbt <= (uint32_t)kBndLds;
+
+  // B. the scored below-bin candidates and, when they fit, the boundary entries
   for (uint32_t x = tid; x < nrr; x += kFinalThreads) {
     const int64_t o = (int64_t)s * L * k0 + x;
     const int32_t id = dv.rr_id[o];
@@ -707,78 +629,134 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
     sh.skey[x] = dv.rr_key[o];
     sh.spg[x] = dv.rr_pg[o];
   }
+  if (bnd_lds) {
+    for (uint32_t x = tid; x < nbt; x += kFinalThreads) {
+      int l = 0;
+      while (x >= sh.boff[l + 1]) ++l;
+      const int64_t o = ((int64_t)s * L + l) * dv.ncap + (x - sh.boff[l]);
+      sh.bk[x] = dv.bnd[o];
+      sh.brk[x] = dv.bnd_rk[o];
+      sh.bpg[x] = dv.bnd_pg[o];
+    }
+  }
   __syncthreads();
-  // B2. the need_l smallest (M, i) of each composite's boundary bin
-  const uint32_t nbt = sh.boff[L];
+
+  // C. the need_l smallest (M, i) of each composite's boundary bin join the
+  // composite's candidates, and the union when not in it yet
+  auto add_pick = [&](int l, unsigned long long key, unsigned long long rk, int32_t pg) {
+    const int32_t id = (int32_t)(key & 0xffffffffull);
+    dv.cand[((int64_t)s * L + l) * k0 + sh.cc[l] + atomicAdd(&sh.extra[l], 1u)] = id;
+    if (hash_insert(sh.hash, id)) {
+      const uint32_t pos = atomicAdd(&sh.nu, 1u);
+      sh.sid[pos] = id;
+      sh.skey[pos] = rk;
+      sh.spg[pos] = pg;
+    }
+  };
   if (nbt > 0) {
-    if (nbt <= (uint32_t)kBndLds) {
-      for (uint32_t x = tid; x < nbt; x += kFinalThreads) {
-        int l = 0;
-        while (x >= sh.boff[l + 1]) ++l;
-        sh.bk[x] = dv.bnd[((int64_t)s * L + l) * dv.ncap + (x - sh.boff[l])];
-      }
-      __syncthreads();
+    if (bnd_lds) {
       for (uint32_t x = tid; x < nbt; x += kFinalThreads) {
         int l = 0;
         while (x >= sh.boff[l + 1]) ++l;
         const unsigned long long key = sh.bk[x];
         uint32_t rank = 0;
         for (uint32_t y = sh.boff[l]; y < sh.boff[l + 1]; ++y) rank += sh.bk[y] < key;
-        if (rank < sh.need[l]) final_add<DT>(sh, dv, s, l, (int32_t)(key & 0xffffffffull));
+        if (rank < sh.need[l]) add_pick(l, key, sh.brk[x], sh.bpg[x]);
       }
     } else {
       for (int l = 0; l < L; ++l) {
-        const unsigned long long *bk = dv.bnd + ((int64_t)s * L + l) * dv.ncap;
+        const int64_t o0 = ((int64_t)s * L + l) * dv.ncap;
+        const unsigned long long *bk = dv.bnd + o0;
         const uint32_t nbl = sh.nb[l], nd = sh.need[l];
         const unsigned long long thr =
             nd >= nbl ? ~0ull : block_select(bk, nbl, nd, sh.cnt, &sh.res, &sh.rr);
         for (uint32_t x = tid; x < nbl; x += kFinalThreads) {
           const unsigned long long key = bk[x];
-          if (key <= thr) final_add<DT>(sh, dv, s, l, (int32_t)(key & 0xffffffffull));
+          if (key <= thr) add_pick(l, key, dv.bnd_rk[o0 + x], dv.bnd_pg[o0 + x]);
         }
         __syncthreads();
       }
     }
   }
   __syncthreads();
-  if (tid < L && k0e > 0) dv.cand_count[s * L + tid] = sh.cc[tid] + sh.extra[tid];
-
-  // C. score the boundary picks (positions nrr .. nu-1); pad for the sort
   const uint32_t nu = sh.nu;
-  uint32_t npad = 1;
-  while (npad < nu) npad <<= 1;
-  {
-    unsigned long long *sk = sh.skey + nrr;
-    int32_t *sp = sh.spg + nrr;
-    const int p = dv.p;
-    block_score<DT, kFinalThreads, kFinalRowBytes>(dv, s, sh.sid + nrr, nu - nrr, sh.qkv, sh.lcs,
-                                                   sh.rows,
-                                   [sk, sp, p](uint32_t x, int32_t, int32_t lc, double sc) {
-                                     sk[x] = score_rank_key(sc);
-                                     sp[x] = lc / p;
-                                   });
-  }
-  for (uint32_t x = nu + tid; x < npad; x += kFinalThreads) {
-    sh.skey[x] = ~0ull;
-    sh.sid[x] = 0x7fffffff;
-    sh.spg[x] = 0;
-  }
-  __syncthreads();
 
-  // D. sort by (rank key, token): register bitonic, npad <= 4096
-  if (npad <= (uint32_t)kFinalThreads)
-    sort_rank_arrays<kFinalThreads, 1>(sh.skey, sh.sid, sh.spg, npad);
-  else if (npad <= 2u * kFinalThreads)
-    sort_rank_arrays<kFinalThreads, 2>(sh.skey, sh.sid, sh.spg, npad);
-  else
-    sort_rank_arrays<kFinalThreads, 4>(sh.skey, sh.sid, sh.spg, npad);
-  for (int x = tid; x < 2048; x += kFinalThreads) sh.seen[x] = 0;  // the hash is done
-  __syncthreads();
+  // D. bucket sort by (rank key, token).  Bucket = floor((s_max - score) *
+  // (kBuckets-1) / (s_max - s_min)) never decreases along ascending keys, so
+  // an element's rank is its bucket's start plus the number of smaller
+  // elements inside its bucket.
+  {
+    unsigned long long lo = ~0ull, hi = 0;
+    for (uint32_t x = tid; x < nu; x += kFinalThreads) {
+      lo = min(lo, sh.skey[x]);
+      hi = max(hi, sh.skey[x]);
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      lo = min(lo, (unsigned long long)__shfl_xor((long long)lo, off));
+      hi = max(hi, (unsigned long long)__shfl_xor((long long)hi, off));
+    }
+    if (lane == 0) {
+      sh.wlo[w] = lo;
+      sh.whi[w] = hi;
+    }
+    for (int x = tid; x < kBuckets; x += kFinalThreads) {
+      sh.bcnt[x] = 0;
+      sh.bfill[x] = 0;
+    }
+    lds_barrier();
+    lo = ~0ull;
+    hi = 0;
+#pragma unroll
+    for (int k = 0; k < kFinalThreads / 64; ++k) {
+      lo = min(lo, sh.wlo[k]);
+      hi = max(hi, sh.whi[k]);
+    }
+    const double smax = nu ? rank_key_score(lo) : 0.0;
+    const double smin = nu ? rank_key_score(hi) : 0.0;
+    const double scale = smax > smin ? (double)(kBuckets - 1) / (smax - smin) : 0.0;
+    auto bucket_of = [smax, scale](unsigned long long key) -> uint32_t {
+      const double t = (smax - rank_key_score(key)) * scale;
+      return (uint32_t)min((double)(kBuckets - 1), t);
+    };
+    for (uint32_t x = tid; x < nu; x += kFinalThreads) atomicAdd(&sh.bcnt[bucket_of(sh.skey[x])], 1u);
+    lds_barrier();
+    {  // exclusive scan of the bucket counts, two per thread
+      const uint32_t c0 = sh.bcnt[2 * tid], c1 = sh.bcnt[2 * tid + 1];
+      const uint32_t incl = wave_incl_scan(c0 + c1);
+      if (lane == 63) sh.wsum[w] = incl;
+      lds_barrier();
+      uint32_t pre = 0;
+      for (int k = 0; k < w; ++k) pre += sh.wsum[k];
+      const uint32_t excl = pre + incl - (c0 + c1);
+      sh.bstart[2 * tid] = excl;
+      sh.bstart[2 * tid + 1] = excl + c0;
+    }
+    lds_barrier();
+    for (uint32_t x = tid; x < nu; x += kFinalThreads) {
+      const uint32_t bk = bucket_of(sh.skey[x]);
+      sh.tmp[sh.bstart[bk] + atomicAdd(&sh.bfill[bk], 1u)] = (int32_t)x;
+    }
+    lds_barrier();
+    for (uint32_t x = tid; x < nu; x += kFinalThreads) {
+      const unsigned long long kx = sh.skey[x];
+      const int32_t ix = sh.sid[x];
+      const uint32_t bk = bucket_of(kx);
+      const uint32_t b0 = sh.bstart[bk], b1 = b0 + sh.bcnt[bk];
+      uint32_t rk = b0;
+      for (uint32_t y = b0; y < b1; ++y) {
+        const int32_t j = sh.tmp[y];
+        rk += key_less(sh.skey[j], sh.sid[j], kx, ix);
+      }
+      sh.inv[rk] = (int32_t)x;
+    }
+    for (int x = tid; x < 2048; x += kFinalThreads) sh.seen[x] = 0;
+    lds_barrier();
+  }
 
   // E. top-k tokens, then pages in rank order
   if (topk_ids)
     for (int x = tid; x < dv.k; x += kFinalThreads)
-      topk_ids[(int64_t)s * dv.k + x] = (uint32_t)x < nu ? sh.sid[x] : -1;
+      topk_ids[(int64_t)s * dv.k + x] = (uint32_t)x < nu ? sh.sid[sh.inv[x]] : -1;
   if (w == 0) {
     int pbits = 1;
     while ((1ll << pbits) < dv.pcap) ++pbits;
@@ -787,7 +765,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
     for (uint32_t x0 = 0; x0 < nu && nsel < dv.P; x0 += 64) {
       const uint32_t x = x0 + lane;
       const bool valid = x < nu;
-      const int32_t pg = valid ? sh.spg[x] : 0;
+      const int32_t pg = valid ? sh.spg[sh.inv[x]] : 0;
       const bool fresh = valid && ((sh.seen[pg >> 5] >> (pg & 31)) & 1u) == 0u;
       const unsigned long long act = __ballot(fresh);
       const unsigned long long mt = match_bits((uint32_t)pg, pbits, act);
@@ -804,24 +782,50 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
     for (int x = nsel + lane; x < dv.P; x += 64) page_ids[(int64_t)s * dv.P + x] = -1;
     if (lane == 0) n_pages[s] = nsel;
   }
+  // F. the candidate counts for inspection, a clean histogram for the next
+  // query
+  if (tid < L && k0e > 0) dv.cand_count[s * L + tid] = sh.cc[tid] + sh.extra[tid];
+  uint32_t *hist = dv.hist + (int64_t)s * L * kHistBins;
+  for (int x = tid; x < L * kHistBins; x += kFinalThreads) hist[x] = 0;
 }
 
 // ---------------------------------------------------------------- launcher
 
+template <int DT, bool LH, int R>
+static void launch_scan(const Dev &dv, int64_t n, const void *q, unsigned grid, hipStream_t st) {
+  hipLaunchKernelGGL((k_qscan<DT, LH, R>), dim3(grid), dim3(kScanThreads), 0, st, dv, n, q);
+}
+
+template <int DT, bool LH>
+static void launch_scan_r(const Dev &dv, int64_t n, const void *q, unsigned grid, hipStream_t st) {
+  switch ((dv.mL + kPipe - 1) / kPipe) {
+    case 1: launch_scan<DT, LH, 1>(dv, n, q, grid, st); break;
+    case 2: launch_scan<DT, LH, 2>(dv, n, q, grid, st); break;
+    case 3: launch_scan<DT, LH, 3>(dv, n, q, grid, st); break;
+    case 4: launch_scan<DT, LH, 4>(dv, n, q, grid, st); break;
+    case 5: launch_scan<DT, LH, 5>(dv, n, q, grid, st); break;
+    case 6: launch_scan<DT, LH, 6>(dv, n, q, grid, st); break;
+    case 7: launch_scan<DT, LH, 7>(dv, n, q, grid, st); break;
+    default: launch_scan<DT, LH, 8>(dv, n, q, grid, st); break;  // mL <= 128
+  }
+}
+
 template <int DT>
 static hipError_t query_impl(const Dev &dv, int64_t n, const void *q, int32_t *page_ids,
                              int32_t *n_pages, int32_t *topk_ids, hipStream_t st, Timer *tm) {
-  const unsigned nblk = (unsigned)((n + kScanTpb - 1) / kScanTpb);  // scan and collect blocks match
+  const int64_t nrange = (n + kScanTpb - 1) / kScanTpb;
+  // the scan also derives the query codes, so it runs (over no tokens) on an
+  // empty index too
+  const unsigned sgrid = (unsigned)((nrange > 0 ? nrange : 1) * dv.S);
   timer_begin(tm, st);
-  hipLaunchKernelGGL(k_qprep<DT>, dim3(dv.S), dim3(256), 0, st, dv, q);
-  timer_mark(tm, KID_QPREP, st);
+  if (dv.L <= 6)
+    launch_scan_r<DT, true>(dv, n, q, sgrid, st);
+  else
+    launch_scan_r<DT, false>(dv, n, q, sgrid, st);
+  timer_mark(tm, KID_QSCAN, st);
   if (n > 0) {
-    if (dv.L <= 6)
-      hipLaunchKernelGGL((k_qscan<true>), dim3(nblk, dv.S), dim3(512), 0, st, dv, n);
-    else
-      hipLaunchKernelGGL((k_qscan<false>), dim3(nblk, dv.S), dim3(512), 0, st, dv, n);
-    timer_mark(tm, KID_QSCAN, st);
-    hipLaunchKernelGGL(k_qcollect<DT>, dim3(nblk, dv.S), dim3(512), 0, st, dv, n);
+    hipLaunchKernelGGL(k_qcollect<DT>, dim3((unsigned)(nrange * dv.S)), dim3(kScanThreads), 0, st,
+                       dv, n);
     timer_mark(tm, KID_QCOLLECT, st);
   }
   hipLaunchKernelGGL(k_qfinal<DT>, dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n, page_ids,
