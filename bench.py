@@ -47,9 +47,10 @@ def algorithmic_bytes(w, kernel: str, ntok: int, n_cand: float, attended: float)
     """Bytes the decode path has to move per launch of `kernel` for the whole layer
     (S streams): the per-unit figures times the units one launch processes.
 
-    insert    new k, v in; pool rows, codes and list entries out: 4d*elem + 12*mL
-    qscan     every token's m*L projection codes (4*mL per token), the query heads
-              and the fp64 directions (g*d*elem + (d+1)*mL*8)
+    prep      the insert (new k, v in; pool rows, codes and list entries out:
+              4d*elem + 12*mL) and the query's projection (the heads and the fp32
+              directions: g*d*elem + (d+1)*mL*4)
+    qscan     every token's m*L projection codes: 4*mL per token
     qcollect  the key row of every reranked candidate: d*elem per candidate
     qfinal    the rerank list (rank key, token, page): 16 bytes per candidate
     attn      K and V rows of every attended token, the queries and the outputs
@@ -57,8 +58,8 @@ def algorithmic_bytes(w, kernel: str, ntok: int, n_cand: float, attended: float)
     S, d, mL, g = w.streams, w.d, w.mL, w.g
     elem = 2 if w.dtype == "bf16" else 4
     per_stream = {
-        "insert": 4.0 * d * elem + 12.0 * mL,
-        "qscan": ntok * mL * 4.0 + g * d * elem + (d + 1) * mL * 8.0,
+        "prep": 4.0 * d * elem + 12.0 * mL + g * d * elem + (d + 1) * mL * 4.0,
+        "qscan": ntok * mL * 4.0,
         "qcollect": n_cand * d * elem,
         "qfinal": n_cand * 16.0,
         "attn": attended * 2 * d * elem + g * d * (elem + 4),
@@ -66,7 +67,7 @@ def algorithmic_bytes(w, kernel: str, ntok: int, n_cand: float, attended: float)
     return S * per_stream.get(kernel, 0.0)
 
 
-STEP_KERNELS = ("insert", "qscan", "qcollect", "qfinal", "attn")
+STEP_KERNELS = ("prep", "qscan", "qcollect", "qfinal", "attn")
 
 
 def cpu_baseline(w, K, V, q, U, k_new, v_new, reps: int):
@@ -163,9 +164,7 @@ def main():
         idx, _ = layers[r]
         k_new, v_new, q = steps_in[t]
         pg, npg, out = outs[r]
-        idx.insert(k_new, v_new)
-        idx.query_pages(q, page_ids=pg, n_pages=npg)
-        idx.sparse_attn(q, pg, npg, out=out)
+        idx.decode_step(k_new, v_new, q, page_ids=pg, n_pages=npg, out=out)
 
     for t in range(args.warmup):
         step(t)
@@ -239,7 +238,7 @@ def main():
         "config": {"workload": WORKLOAD, "kv_heads": w.streams, "query_heads": w.streams * w.g,
                    "context": w.n, "head_dim": w.d, "page_size": w.p, "budget_k": w.k,
                    "m": w.m, "L": w.L, "layers_rotated": R,
-                   "step": "insert + query_pages + sparse_attn"},
+                   "step": "ice_decode_step = insert + query_pages + sparse_attn"},
         "build_ms": round(sorted(build_ms)[len(build_ms) // 2], 3),
         "step_alg_gbs": round(step_alg / (ms_per_step * 1e-3) / 1e9, 1),
         "kernel_avg_us": {k: round(v, 3) for k, v in avg_us.items()},

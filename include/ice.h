@@ -147,6 +147,17 @@ ice_status ice_query_pages(ice_index *idx, const void *q, int32_t *page_ids, int
 ice_status ice_sparse_attn(const ice_index *idx, const void *q, const int32_t *page_ids,
                            const int32_t *n_pages, float *out, void *stream);
 
+/* One decode step: ice_insert(k_new, v_new), then ice_query_pages(q, ...)
+ * over the n+1 tokens, then ice_sparse_attn(q, page_ids, n_pages, out), with
+ * results identical to those three calls (IceCache paper page, Figure 2 steps
+ * (2)-(3); blog page: new tokens join the tree with no rebuild).  The insert
+ * and the query's projection share one kernel, so the step takes fewer
+ * launches.  Arguments as for those calls; q must be 16-byte aligned.
+ * ICE_ERR_CAPACITY (nothing enqueued) when the index is full. */
+ice_status ice_decode_step(ice_index *idx, const void *k_new, const void *v_new, const void *q,
+                           int32_t *page_ids, int32_t *n_pages, int32_t *topk_ids, float *out,
+                           void *stream);
+
 /* Frees the handle (not the workspace). NULL is allowed. */
 void ice_destroy_index(ice_index *idx);
 
@@ -190,7 +201,7 @@ ice_status ice_index_layout(const ice_index *idx, ice_layout *out);
  * kernel (arrays of ICE_TIMED_KERNELS, in the order of ice_timing_name) and
  * clears the record.  The event records add a little time between kernels;
  * leave timing off for end-to-end latency. */
-#define ICE_TIMED_KERNELS 6 /* insert, qscan, qcollect, qfinal, attn, amerge */
+#define ICE_TIMED_KERNELS 6 /* prep, qscan, qcollect, qfinal, attn, amerge */
 ice_status ice_timing_enable(ice_index *idx, int enable);
 ice_status ice_timing_read(ice_index *idx, double *total_ms, int64_t *launches);
 const char *ice_timing_name(int kernel);

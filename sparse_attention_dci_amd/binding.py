@@ -74,6 +74,8 @@ def lib():
         L.ice_query_pages.restype = ctypes.c_int
         L.ice_sparse_attn.argtypes = [P, P, P, P, P, P]
         L.ice_sparse_attn.restype = ctypes.c_int
+        L.ice_decode_step.argtypes = [P, P, P, P, P, P, P, P, P]
+        L.ice_decode_step.restype = ctypes.c_int
         L.ice_destroy_index.argtypes = [P]
         L.ice_destroy_index.restype = None
         L.ice_status_string.argtypes = [ctypes.c_int]
@@ -209,6 +211,29 @@ class Index:
         _check(lib().ice_sparse_attn(self._h, _ptr(q), _ptr(page_ids), _ptr(n_pages), _ptr(out),
                                      _stream(stream)), "ice_sparse_attn")
         return out
+
+    def decode_step(self, k_new, v_new, q, page_ids=None, n_pages=None, out=None,
+                    with_topk=False, topk=None, stream=None):
+        """insert(k_new, v_new); query_pages(q); sparse_attn(q, ...) in one call."""
+        for t, nm in ((k_new, "k_new"), (v_new, "v_new"), (q, "q")):
+            _dev_tensor(t, nm, self.dtype, 2)
+        if k_new.shape != (self.S, self.d) or v_new.shape != (self.S, self.d):
+            raise ValueError("k_new, v_new must be [S][d]")
+        if q.shape != (self.S * self.g, self.d):
+            raise ValueError("q must be [S*g][d]")
+        dev = self.device
+        page_ids = page_ids if page_ids is not None else torch.empty(
+            self.S, self.P, dtype=torch.int32, device=dev)
+        n_pages = n_pages if n_pages is not None else torch.empty(self.S, dtype=torch.int32,
+                                                                  device=dev)
+        out = out if out is not None else torch.empty(self.S * self.g, self.d,
+                                                      dtype=torch.float32, device=dev)
+        if with_topk and topk is None:
+            topk = torch.empty(self.S, self.k, dtype=torch.int32, device=dev)
+        _check(lib().ice_decode_step(self._h, _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(page_ids),
+                                     _ptr(n_pages), _ptr(topk) if with_topk else None, _ptr(out),
+                                     _stream(stream)), "ice_decode_step")
+        return page_ids, n_pages, out, (topk if with_topk else None)
 
     # ------------------------------------------------------------ timing
     def timing(self, enable: bool):

@@ -139,7 +139,7 @@ ice_status make_layout(const ice_params *prm, int32_t S, int64_t n, int64_t ncap
     return at;
   };
   y.dirs = seg((int64_t)y.nchunk * (d + 1) * ice::kDirChunk * 8);
-  y.dirs32 = seg((int64_t)d * ((mL + 31) / 32 * 32) * 4);
+  y.dirs32 = seg((int64_t)(d + 1) * ((mL + 31) / 32 * 32) * 4);
   y.norm_c = seg(Sl * 4);
   y.inv_c = seg(Sl * 8);
   y.inv_c2 = seg(Sl * 8);
@@ -348,12 +348,27 @@ ice_status ice_query_pages(ice_index *idx, const void *q, int32_t *page_ids, int
 
 ice_status ice_sparse_attn(const ice_index *idx, const void *q, const int32_t *page_ids,
                            const int32_t *n_pages, float *out, void *stream) {
-  if (!idx || !q || !page_ids || !n_pages || !out || !aligned(q, 4) || !aligned(page_ids, 4) ||
+  if (!idx || !q || !page_ids || !n_pages || !out || !aligned(q, 16) || !aligned(page_ids, 4) ||
       !aligned(n_pages, 4) || !aligned(out, 4))
     return ICE_ERR_INVALID_ARG;
   hipError_t e = ice::launch_attn(idx->dv, q, page_ids, n_pages, out, (hipStream_t)stream,
                                   idx->timer);
   return e == hipSuccess ? ICE_OK : ICE_ERR_HIP;
+}
+
+ice_status ice_decode_step(ice_index *idx, const void *k_new, const void *v_new, const void *q,
+                           int32_t *page_ids, int32_t *n_pages, int32_t *topk_ids, float *out,
+                           void *stream) {
+  if (!idx || !k_new || !v_new || !q || !page_ids || !n_pages || !out || !aligned(k_new, 4) ||
+      !aligned(v_new, 4) || !aligned(q, 16) || !aligned(page_ids, 4) || !aligned(n_pages, 4) ||
+      !aligned(out, 4) || (topk_ids && !aligned(topk_ids, 4)))
+    return ICE_ERR_INVALID_ARG;
+  if (idx->n >= idx->ncap) return ICE_ERR_CAPACITY;
+  hipError_t e = ice::launch_decode(idx->dv, idx->n, k_new, v_new, q, page_ids, n_pages, topk_ids,
+                                    out, (hipStream_t)stream, idx->timer);
+  if (e != hipSuccess) return ICE_ERR_HIP;
+  idx->n += 1;
+  return ICE_OK;
 }
 
 void ice_destroy_index(ice_index *idx) {
@@ -397,8 +412,8 @@ ice_status ice_timing_read(ice_index *idx, double *total_ms, int64_t *launches) 
 }
 
 const char *ice_timing_name(int kernel) {
-  static const char *names[ICE_TIMED_KERNELS] = {"insert", "qscan", "qcollect",
-                                                 "qfinal", "attn",  "amerge"};
+  static const char *names[ICE_TIMED_KERNELS] = {"prep", "qscan", "qcollect",
+                                                 "qfinal", "attn", "amerge"};
   return (kernel >= 0 && kernel < ICE_TIMED_KERNELS) ? names[kernel] : "";
 }
 

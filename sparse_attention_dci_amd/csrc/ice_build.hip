@@ -49,8 +49,8 @@ __global__ void k_dirs(Dev dv, const void *dirs) {
     const int t = ch * kDirChunk + j;
     dv.dirs[x] = t < dv.mL ? (double)load_elem<DT>(dirs, (int64_t)t * (dv.d + 1) + e) : 0.0;
   }
-  // fp32 copy of the first d coordinates, element-major (every value is exact in fp32)
-  const int64_t total32 = (int64_t)dv.d * dv.mLp;
+  // fp32 copy, element-major (every value is exact in fp32)
+  const int64_t total32 = (int64_t)(dv.d + 1) * dv.mLp;
   for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < total32;
        x += (int64_t)gridDim.x * blockDim.x) {
     const int e = (int)(x / dv.mLp), t = (int)(x % dv.mLp);
@@ -432,112 +432,6 @@ __global__ __launch_bounds__(256) void k_scatter_v(Dev dv, const void *V, int64_
   }
 }
 
-// ---------------------------------------------------------------- insert
-
-// One block per stream appends token n: projection with the stored bound
-// (directions staged in LDS, 32 per round; lane t forms r_t, lane 255 forms
-// |k|^2), list entries at position n of each direction's insert region, the
-// page rule, and the pool rows.
-template <int DT>
-__global__ __launch_bounds__(256) void k_insert(Dev dv, int64_t n, const void *k_new,
-                                                const void *v_new) {
-  const int s = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int d = dv.d, mL = dv.mL, p = dv.p, d1 = dv.d + 1;
-  __shared__ float kv[128];
-  __shared__ double dl[129 * 32];
-  __shared__ double rs[kMaxMl];
-  __shared__ double ud[kMaxMl];
-  __shared__ double nsq_s;
-  __shared__ uint32_t cell_s;
-  __shared__ int32_t loc_s;
-  if (tid < d) kv[tid] = load_elem<DT>(k_new, (int64_t)s * d + tid);
-  __syncthreads();
-  if (tid == 255) {
-    double a = 0.0;
-#pragma unroll 16
-    for (int e = 0; e < d; ++e) a = fma((double)kv[e], (double)kv[e], a);
-    nsq_s = a;
-  }
-  for (int t0 = 0; t0 < mL; t0 += 32) {
-    {  // every load of this thread issued before its stores
-      constexpr int kIter = (129 * 32 + 255) / 256;
-      double v[kIter];
-#pragma unroll
-      for (int k = 0; k < kIter; ++k) {  // clamped, unconditional loads
-        const int x = min(tid + 256 * k, d1 * 32 - 1);
-        const int e = x >> 5, j = x & 31, t = t0 + j;
-        const int ch = min(t / kDirChunk, dv.nchunk - 1);
-        v[k] = dv.dirs[((size_t)ch * d1 + e) * kDirChunk + (t % kDirChunk)];
-      }
-#pragma unroll
-      for (int k = 0; k < kIter; ++k) {
-        const int x = tid + 256 * k;
-        if (x < d1 * 32) dl[x] = (t0 + (x & 31)) < dv.nchunk * kDirChunk ? v[k] : 0.0;
-      }
-    }
-    __syncthreads();
-    if (tid < 32 && t0 + tid < mL) {
-      double r = 0.0;
-#pragma unroll 16
-      for (int e = 0; e < d; ++e) r = fma((double)kv[e], dl[e * 32 + tid], r);
-      rs[t0 + tid] = r;
-      ud[t0 + tid] = dl[d * 32 + tid];
-    }
-    __syncthreads();
-  }
-  // cell = sign bits of r on the first D directions (D <= 13)
-  if (tid < 64) {
-    const unsigned long long bal = __ballot(tid < dv.D && rs[tid < mL ? tid : 0] >= 0.0);
-    if (tid == 0) cell_s = (uint32_t)bal & ((1u << dv.D) - 1u);
-  }
-  if (tid < mL) {
-    double b = __dsub_rn(1.0, __dmul_rn(nsq_s, dv.inv_c2[s]));
-    if (b < 0.0) b = 0.0;
-    const double sv = __dsqrt_rn(b);
-    const double x = __dadd_rn(__dmul_rn(rs[tid], dv.inv_c[s]), __dmul_rn(sv, ud[tid]));
-    const int32_t code = to_code(x);
-    dv.codes[code_index(dv.ntile, mL, s, n, tid)] = code;
-    dv.list_code[((int64_t)s * mL + tid) * dv.ncap + n] = code;
-    dv.list_id[((int64_t)s * mL + tid) * dv.ncap + n] = (int32_t)n;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t c = cell_s;
-    const int64_t ci = (int64_t)s * dv.ncell + c;
-    const int32_t cntc = dv.cell_count[ci];
-    const int32_t slot = cntc & (p - 1);
-    int32_t pid;
-    if (slot == 0) {
-      pid = dv.npages[s];
-      dv.npages[s] = pid + 1;
-      dv.cell_last[ci] = pid;
-      dv.page_cell[(int64_t)s * dv.pcap + pid] = (int32_t)c;
-    } else {
-      pid = dv.cell_last[ci];
-    }
-    dv.cell_count[ci] = cntc + 1;
-    dv.page_tokens[((int64_t)s * dv.pcap + pid) * p + slot] = (int32_t)n;
-    dv.page_len[(int64_t)s * dv.pcap + pid] = slot + 1;
-    const int32_t lc = pid * p + slot;
-    dv.loc[(int64_t)s * dv.ncap + n] = lc;
-    loc_s = lc;
-  }
-  __syncthreads();
-  // key row at its slot; value element e at [page][e][slot]
-  const int64_t row = ((int64_t)s * dv.pcap * p + loc_s) * d;
-  const int64_t vcol = ((int64_t)s * dv.pcap + loc_s / p) * d * p + (loc_s % p);
-  if (tid < d) {
-    if constexpr (DT == 0) {
-      reinterpret_cast<float *>(dv.pool_k)[row + tid] = reinterpret_cast<const float *>(k_new)[(int64_t)s * d + tid];
-      reinterpret_cast<float *>(dv.pool_v)[vcol + (int64_t)tid * p] = reinterpret_cast<const float *>(v_new)[(int64_t)s * d + tid];
-    } else {
-      reinterpret_cast<uint16_t *>(dv.pool_k)[row + tid] = reinterpret_cast<const uint16_t *>(k_new)[(int64_t)s * d + tid];
-      reinterpret_cast<uint16_t *>(dv.pool_v)[vcol + (int64_t)tid * p] = reinterpret_cast<const uint16_t *>(v_new)[(int64_t)s * d + tid];
-    }
-  }
-}
-
 // ---------------------------------------------------------------- launchers
 
 template <int DT>
@@ -587,17 +481,6 @@ hipError_t launch_build(const Dev &dv, const BuildScratch &bs, int64_t n, const 
                         const void *V, const void *dirs, float c_fixed, hipStream_t st) {
   return dv.dtype == 0 ? build_impl<0>(dv, bs, n, K, V, dirs, c_fixed, st)
                        : build_impl<1>(dv, bs, n, K, V, dirs, c_fixed, st);
-}
-
-hipError_t launch_insert(const Dev &dv, int64_t n, const void *k_new, const void *v_new,
-                         hipStream_t st, Timer *tm) {
-  timer_begin(tm, st);
-  if (dv.dtype == 0)
-    hipLaunchKernelGGL(k_insert<0>, dim3(dv.S), dim3(256), 0, st, dv, n, k_new, v_new);
-  else
-    hipLaunchKernelGGL(k_insert<1>, dim3(dv.S), dim3(256), 0, st, dv, n, k_new, v_new);
-  timer_mark(tm, KID_INSERT, st);
-  return hipGetLastError();
 }
 
 }  // namespace ice

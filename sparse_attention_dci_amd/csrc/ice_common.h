@@ -38,7 +38,7 @@ struct Dev {
   int attn_nsplit;     // attention blocks per stream, ceil(k / kAttnTpb)
 
   double *dirs;        // [nchunk][d+1][16]
-  float *dirs32;       // [d][mLp] the first d coordinates, mLp = mL rounded up to 32, zero past mL
+  float *dirs32;       // [d+1][mLp] element-major, mLp = mL rounded up to 32, zero past mL
   int mLp;
   float *norm_c;       // [S]
   double *inv_c;       // [S]
@@ -90,7 +90,7 @@ struct BuildScratch {
 };
 
 // Decode-time kernels that the optional event timer reports separately.
-enum KernelId { KID_INSERT = 0, KID_QSCAN, KID_QCOLLECT, KID_QFINAL, KID_ATTN, KID_AMERGE,
+enum KernelId { KID_PREP = 0, KID_QSCAN, KID_QCOLLECT, KID_QFINAL, KID_ATTN, KID_AMERGE,
                 KID_COUNT };
 
 // Optional host-side event timer (owned by an index); null when timing is off.
@@ -101,11 +101,17 @@ void timer_mark(Timer *tm, int kid, hipStream_t st);    // after each launch
 // Host launchers (each returns the hipGetLastError of its launches).
 hipError_t launch_build(const Dev &dv, const BuildScratch &bs, int64_t n, const void *K,
                         const void *V, const void *dirs, float c_fixed, hipStream_t st);
+hipError_t launch_prep(const Dev &dv, int64_t n, const void *k_new, const void *v_new,
+                       const void *q, int mode, hipStream_t st);  // mode: 1 insert, 2 query, 3 both
 hipError_t launch_insert(const Dev &dv, int64_t n, const void *k_new, const void *v_new,
                          hipStream_t st, Timer *tm);
 hipError_t launch_query(const Dev &dv, int64_t n, const void *q, int32_t *page_ids,
                         int32_t *n_pages, int32_t *topk_ids, hipStream_t st, Timer *tm);
 hipError_t launch_attn(const Dev &dv, const void *q, const int32_t *page_ids,
                        const int32_t *n_pages, float *out, hipStream_t st, Timer *tm);
+// insert of token n, then the query over n + 1 tokens and the attention
+hipError_t launch_decode(const Dev &dv, int64_t n, const void *k_new, const void *v_new,
+                         const void *q, int32_t *page_ids, int32_t *n_pages, int32_t *topk_ids,
+                         float *out, hipStream_t st, Timer *tm);
 
 }  // namespace ice

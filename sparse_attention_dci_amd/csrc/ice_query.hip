@@ -10,9 +10,10 @@
 // visits 60-85% of all list entries before k0 tokens complete, so it would
 // touch most of them anyway) followed by an exact selection:
 //
-//   k_qscan     derives the query codes (fp32 GQA mean, fp64 projection) while
-//               its first code loads are in flight, then M_i for every token
-//               and composite and a histogram of the top 11 bits of M_i;
+//   k_prep      (ice_prep.hip) the query codes: fp32 GQA mean, fp64
+//               projection;
+//   k_qscan     M_i for every token and composite and a histogram of the top
+//               11 bits of M_i;
 //   k_qcollect  tokens in bins below the k0-th smallest bin b* are
 //               candidates, tokens in bin b* are parked with their (M_i, i)
 //               key; both kinds are scored exactly (fp64, ascending element
@@ -21,7 +22,7 @@
 //               boundary bins, the union of the composites (LDS hash), a
 //               bucket sort by (score desc, token asc), top-k and the page
 //               walk; it leaves a clean histogram for the next query.
-#include "ice_device.h"
+#include "ice_attn_dev.h"
 
 namespace ice {
 
@@ -31,6 +32,7 @@ constexpr int kFinalThreads = 1024;
 constexpr int kHashSlots = 8192;    // 2 * kMaxCand
 constexpr int kBndLds = 2048;       // boundary entries ranked in LDS
 constexpr int kBuckets = 2048;
+constexpr int kFusedMaxPages = 1024;  // page budgets up to this take the fused attention
 
 // ---------------------------------------------------------------- helpers
 
@@ -154,53 +156,29 @@ __device__ __forceinline__ int32_t ld_code(__amdgpu_buffer_rsrc_t r, uint32_t of
 // multiple of 8 all blocks of a stream land on one XCD and share its L2) and
 // the b / S-th range of kScanTpb = 1024 tokens: wave w takes tiles 2w and
 // 2w+1 of the range, lane j token j of a tile, and reads code t of its 64
-// tokens as one contiguous 256-byte load.
-// The block first derives the query codes: q_kv = fp32 mean of the g heads
-// (left fold, then times fp32(1/g)), qcode_t = code(<q_kv, u_t[:d]> / |q_kv|)
-// with the dot products and the norm in fp64, ascending element order (the
-// directions are staged as fp32, which holds every stored value exactly).
-// The heads and directions are loaded first; then kPipe codes of each tile
-// go in flight, and every code slot is refilled with the code kPipe places
-// later right after it is used, so loads stay in flight across the fp64
-// chains and the composites.  R = ceil(mL / kPipe) is a template parameter:
-// the walk over code positions is straight-line code, which lets every wait
-// cover exactly the loads it needs.
-// The histogram lives in LDS when L <= 6 (over the staged directions), and
-// only the bins at or below the block's own k0-th bin are added to the global
-// one; with L > 6 every count goes straight to global.
+// tokens as one contiguous 256-byte load.  kPipe codes of each tile are in
+// flight at a time: every code slot is refilled with the code kPipe places
+// later right after it is used.  R = ceil(mL / kPipe) is a template
+// parameter, so the walk over code positions is straight-line code and every
+// wait covers exactly the loads it needs.  The query codes come from the prep
+// kernel.  The histogram lives in LDS when L <= 6, and only the bins at or
+// below the block's own k0-th bin are added to the global one; with L > 6
+// every count goes straight to global.
 constexpr int kPipe = 16;
 
-template <int DT, bool LDS_HIST, int R>
-__global__ __launch_bounds__(kScanThreads) void k_qscan(Dev dv, int64_t n, const void *q) {
+template <bool LDS_HIST, int R>
+__global__ __launch_bounds__(kScanThreads) void k_qscan(Dev dv, int64_t n) {
   constexpr int NT = kScanThreads;
   const int S = dv.S, s = blockIdx.x % S;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int mL = dv.mL, m = dv.m, L = dv.L, d = dv.d, g = dv.g;
-  __shared__ float qkv[128];
+  const int mL = dv.mL, m = dv.m, L = dv.L;
   __shared__ int32_t qc[kMaxMl];
-  __shared__ double zs[kMaxMl];
-  __shared__ double qsq;
   __shared__ uint32_t blim[6];
-  constexpr int kDirWords = 128 * 32;           // [e][32] fp32
-  constexpr int kHeadWords = kMaxGroup * 128;   // [g][d] fp32
-  constexpr int kBufWords = LDS_HIST ? 6 * kHistBins : kDirWords + kHeadWords;
-  static_assert(kBufWords >= kDirWords + kHeadWords, "directions and heads must fit");
-  __shared__ float lbuf[kBufWords];
-  float *dl = lbuf;
-  float *qs = lbuf + kDirWords;
-  uint32_t *hist = reinterpret_cast<uint32_t *>(lbuf);
+  __shared__ uint32_t hist[LDS_HIST ? 6 * kHistBins : 1];
   uint32_t *ghist = dv.hist + (int64_t)s * L * kHistBins;
 
-  // 1. the query heads and directions 0..31 into LDS
-  for (int x = tid; x < g * d; x += NT) qs[x] = load_elem<DT>(q, (int64_t)s * g * d + x);
-  for (int x = tid; x < d * 8; x += NT) {
-    const int e = x >> 3, c4 = (x & 7) * 4;
-    *reinterpret_cast<float4 *>(dl + e * 32 + c4) =
-        *reinterpret_cast<const float4 *>(dv.dirs32 + (int64_t)e * dv.mLp + c4);
-  }
-  lds_barrier();
-
-  // 2. the first kPipe codes of both tiles of the first range
+  // 1. the query codes, then the first kPipe codes of both tiles
+  const int32_t qv0 = dv.qcode[(int64_t)s * mL + min(tid, mL - 1)];
   const uint32_t tile_bytes = (uint32_t)mL * kCodeTile * 4;
   const __amdgpu_buffer_rsrc_t rc =
       byte_range(dv.codes + (int64_t)s * dv.ntile * mL * kCodeTile, (uint32_t)dv.ntile * tile_bytes);
@@ -212,51 +190,12 @@ __global__ __launch_bounds__(kScanThreads) void k_qscan(Dev dv, int64_t n, const
     a[x] = ld_code(rc, oa + x * 256);
     b[x] = ld_code(rc, oa + tile_bytes + x * 256);
   }
-
-  // 3. query codes
-  if (tid < d) {
-    const float inv_g = (float)__ddiv_rn(1.0, (double)g);
-    float acc = qs[tid];
-    for (int h = 1; h < g; ++h) acc = __fadd_rn(acc, qs[h * d + tid]);
-    qkv[tid] = __fmul_rn(acc, inv_g);
-  }
-  lds_barrier();
-  if (tid == NT - 1) {
-    double x = 0.0;
-#pragma unroll 8
-    for (int e = 0; e < d; ++e) x = fma((double)qkv[e], (double)qkv[e], x);
-    qsq = x;
-  }
-  for (int t0 = 0; t0 < mL; t0 += 32) {
-    if (t0 > 0) {
-      lds_barrier();
-      for (int x = tid; x < d * 8; x += NT) {
-        const int e = x >> 3, c4 = (x & 7) * 4;
-        *reinterpret_cast<float4 *>(dl + e * 32 + c4) =
-            *reinterpret_cast<const float4 *>(dv.dirs32 + (int64_t)e * dv.mLp + t0 + c4);
-      }
-      lds_barrier();
-    }
-    if (tid < 32 && t0 + tid < mL) {
-      double z = 0.0;
-#pragma unroll 8
-      for (int e = 0; e < d; ++e) z = fma((double)qkv[e], (double)dl[e * 32 + tid], z);
-      zs[t0 + tid] = z;
-    }
-  }
-  lds_barrier();
-  if (tid < mL) {
-    const double qn = __dsqrt_rn(qsq);
-    const double qb = qn > 0.0 ? __ddiv_rn(zs[tid], qn) : 0.0;
-    qc[tid] = to_code(qb);
-  }
-  lds_barrier();
-  if (LDS_HIST) {
+  if (tid < mL) qc[tid] = qv0;
+  if (LDS_HIST)
     for (int x = tid; x < L * kHistBins; x += NT) hist[x] = 0;
-    lds_barrier();
-  }
+  lds_barrier();
 
-  // 4. M per token and composite.  Composite boundaries depend on the code
+  // 2. M per token and composite.  Composite boundaries depend on the code
   // position only, so every branch but the ragged tail's is uniform.
   const int64_t i0 = r * kScanTpb, i1 = min(i0 + kScanTpb, n);
   const uint32_t ntok = (uint32_t)(i1 > i0 ? i1 - i0 : 0);
@@ -306,28 +245,16 @@ __global__ __launch_bounds__(kScanThreads) void k_qscan(Dev dv, int64_t n, const
     }
   }
 
-  // the query's own outputs and counters (after the loop, so that no global
-  // store precedes a barrier while the code loads are in flight)
-  if (blockIdx.x < (unsigned)S) {
-    if (tid < d) dv.qkv[(int64_t)s * d + tid] = qkv[tid];
-    if (tid < mL) dv.qcode[(int64_t)s * mL + tid] = qc[tid];
-    if (tid < L) {  // this query's counters, used by the collect kernel
-      dv.cand_count[s * L + tid] = 0;
-      dv.bnd_count[s * L + tid] = 0;
-    }
-    if (tid == 0) dv.rr_count[s] = 0;
-  }
-
-  // 5. flush the block's histogram.  The k0-th smallest M of the stream is
+  // 3. flush the block's histogram.  The k0-th smallest M of the stream is
   // never in a higher bin than the k0-th smallest of a block holding at least
   // k0 tokens, so every bin up to the global threshold bin still receives
   // every block's count.
   if (LDS_HIST) {
     lds_barrier();
-    for (int l = w; l < L; l += NT / 64) {
+    for (int l2 = w; l2 < L; l2 += NT / 64) {
       uint32_t bb = kHistBins - 1, bl;
-      if (ntok >= (uint32_t)dv.k0 && dv.k0 > 0) wave_find_bin(hist + l * kHistBins, dv.k0, bb, bl);
-      if (lane == 0) blim[l] = bb;
+      if (ntok >= (uint32_t)dv.k0 && dv.k0 > 0) wave_find_bin(hist + l2 * kHistBins, dv.k0, bb, bl);
+      if (lane == 0) blim[l2] = bb;
     }
     lds_barrier();
     for (int x = tid; x < L * kHistBins; x += NT) {
@@ -579,11 +506,15 @@ struct FinalShared {
   unsigned long long res;
   unsigned long long wlo[16], whi[16];
   uint32_t wsum[16];
+  int32_t sel[kFusedMaxPages];  // the selected pages, for the fused attention
+  int32_t nsel;
+  float wm[16 * 16], wl[16 * 16];
 };
 
-template <int DT>
+template <int DT, int D>
 __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int32_t *page_ids,
-                                                          int32_t *n_pages, int32_t *topk_ids) {
+                                                          int32_t *n_pages, int32_t *topk_ids,
+                                                          const void *q, float *out) {
   __shared__ FinalShared sh;
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -774,70 +705,128 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
       const int pos = nsel + popc64(fm & lt);
       if (firstocc && pos < dv.P) {
         page_ids[(int64_t)s * dv.P + pos] = pg;
+        if (pos < kFusedMaxPages) sh.sel[pos] = pg;
         atomicOr(&sh.seen[pg >> 5], 1u << (pg & 31));
       }
       nsel = min(dv.P, nsel + popc64(fm));
       __builtin_amdgcn_wave_barrier();
     }
     for (int x = nsel + lane; x < dv.P; x += 64) page_ids[(int64_t)s * dv.P + x] = -1;
-    if (lane == 0) n_pages[s] = nsel;
+    if (lane == 0) {
+      n_pages[s] = nsel;
+      sh.nsel = nsel;
+    }
   }
   // F. the candidate counts for inspection, a clean histogram for the next
-  // query
-  if (tid < L && k0e > 0) dv.cand_count[s * L + tid] = sh.cc[tid] + sh.extra[tid];
-  uint32_t *hist = dv.hist + (int64_t)s * L * kHistBins;
-  for (int x = tid; x < L * kHistBins; x += kFinalThreads) hist[x] = 0;
+  // query (after the attention: a barrier after global stores waits for them)
+  auto bookkeeping = [&]() {
+    if (tid < L && k0e > 0) dv.cand_count[s * L + tid] = sh.cc[tid] + sh.extra[tid];
+    uint32_t *hist = dv.hist + (int64_t)s * L * kHistBins;
+    for (int x = tid; x < L * kHistBins; x += kFinalThreads) hist[x] = 0;
+  };
+  if (out == nullptr) {
+    bookkeeping();
+    return;
+  }
+
+  // G. the fused sparse attention over the selected pages: 16 waves, one
+  // 32-token chunk at a time each, merged at the end (LDS of the dead
+  // selection arrays holds the wave outputs)
+  constexpr int NW = kFinalThreads / 64;
+  static_assert(sizeof(FinalShared) >= (size_t)NW * kMaxGroup * D * 4 + 0, "wave outputs fit");
+  u32x4 qh[D / 32], ql[D / 32];
+  attn_load_q<DT, D>(dv, s, q, qh, ql);
+  AttnWave<D> st;
+  attn_init(st);
+  __syncthreads();
+  const int np = sh.nsel;
+  for (int T0 = w * 32; T0 < np * dv.p; T0 += NW * 32)
+    attn_chunk<DT, D, true>(dv, s, T0, sh.sel, np, qh, ql, st);
+  float *red = reinterpret_cast<float *>(&sh.skey[0]);
+  attn_publish(st, w, dv.g, sh.wm, sh.wl, red);
+  __syncthreads();
+  for (int x = tid; x < dv.g * D; x += kFinalThreads) {
+    float M, num, den;
+    attn_merge<D>(NW, dv.g, x, sh.wm, sh.wl, red, M, num, den);
+    out[(int64_t)s * dv.g * D + x] = den > 0.0f ? num / den : 0.0f;
+  }
+  bookkeeping();
 }
 
 // ---------------------------------------------------------------- launcher
 
-template <int DT, bool LH, int R>
-static void launch_scan(const Dev &dv, int64_t n, const void *q, unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_qscan<DT, LH, R>), dim3(grid), dim3(kScanThreads), 0, st, dv, n, q);
+template <bool LH, int R>
+static void launch_scan(const Dev &dv, int64_t n, unsigned grid, hipStream_t st) {
+  hipLaunchKernelGGL((k_qscan<LH, R>), dim3(grid), dim3(kScanThreads), 0, st, dv, n);
 }
 
-template <int DT, bool LH>
-static void launch_scan_r(const Dev &dv, int64_t n, const void *q, unsigned grid, hipStream_t st) {
+template <bool LH>
+static void launch_scan_r(const Dev &dv, int64_t n, unsigned grid, hipStream_t st) {
   switch ((dv.mL + kPipe - 1) / kPipe) {
-    case 1: launch_scan<DT, LH, 1>(dv, n, q, grid, st); break;
-    case 2: launch_scan<DT, LH, 2>(dv, n, q, grid, st); break;
-    case 3: launch_scan<DT, LH, 3>(dv, n, q, grid, st); break;
-    case 4: launch_scan<DT, LH, 4>(dv, n, q, grid, st); break;
-    case 5: launch_scan<DT, LH, 5>(dv, n, q, grid, st); break;
-    case 6: launch_scan<DT, LH, 6>(dv, n, q, grid, st); break;
-    case 7: launch_scan<DT, LH, 7>(dv, n, q, grid, st); break;
-    default: launch_scan<DT, LH, 8>(dv, n, q, grid, st); break;  // mL <= 128
+    case 1: launch_scan<LH, 1>(dv, n, grid, st); break;
+    case 2: launch_scan<LH, 2>(dv, n, grid, st); break;
+    case 3: launch_scan<LH, 3>(dv, n, grid, st); break;
+    case 4: launch_scan<LH, 4>(dv, n, grid, st); break;
+    case 5: launch_scan<LH, 5>(dv, n, grid, st); break;
+    case 6: launch_scan<LH, 6>(dv, n, grid, st); break;
+    case 7: launch_scan<LH, 7>(dv, n, grid, st); break;
+    default: launch_scan<LH, 8>(dv, n, grid, st); break;  // mL <= 128
   }
 }
 
+// The query after its prep: scan, collect, final.
 template <int DT>
-static hipError_t query_impl(const Dev &dv, int64_t n, const void *q, int32_t *page_ids,
-                             int32_t *n_pages, int32_t *topk_ids, hipStream_t st, Timer *tm) {
+static void query_tail(const Dev &dv, int64_t n, int32_t *page_ids, int32_t *n_pages,
+                       int32_t *topk_ids, const void *q, float *out, hipStream_t st, Timer *tm) {
   const int64_t nrange = (n + kScanTpb - 1) / kScanTpb;
-  // the scan also derives the query codes, so it runs (over no tokens) on an
-  // empty index too
-  const unsigned sgrid = (unsigned)((nrange > 0 ? nrange : 1) * dv.S);
-  timer_begin(tm, st);
-  if (dv.L <= 6)
-    launch_scan_r<DT, true>(dv, n, q, sgrid, st);
-  else
-    launch_scan_r<DT, false>(dv, n, q, sgrid, st);
-  timer_mark(tm, KID_QSCAN, st);
   if (n > 0) {
-    hipLaunchKernelGGL(k_qcollect<DT>, dim3((unsigned)(nrange * dv.S)), dim3(kScanThreads), 0, st,
-                       dv, n);
+    const unsigned grid = (unsigned)(nrange * dv.S);
+    if (dv.L <= 6)
+      launch_scan_r<true>(dv, n, grid, st);
+    else
+      launch_scan_r<false>(dv, n, grid, st);
+    timer_mark(tm, KID_QSCAN, st);
+    hipLaunchKernelGGL(k_qcollect<DT>, dim3(grid), dim3(kScanThreads), 0, st, dv, n);
     timer_mark(tm, KID_QCOLLECT, st);
   }
-  hipLaunchKernelGGL(k_qfinal<DT>, dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n, page_ids,
-                     n_pages, topk_ids);
+  if (dv.d == 128)
+    hipLaunchKernelGGL((k_qfinal<DT, 128>), dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n,
+                       page_ids, n_pages, topk_ids, q, out);
+  else
+    hipLaunchKernelGGL((k_qfinal<DT, 64>), dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n,
+                       page_ids, n_pages, topk_ids, q, out);
   timer_mark(tm, KID_QFINAL, st);
-  return hipGetLastError();
 }
 
 hipError_t launch_query(const Dev &dv, int64_t n, const void *q, int32_t *page_ids,
                         int32_t *n_pages, int32_t *topk_ids, hipStream_t st, Timer *tm) {
-  return dv.dtype == 0 ? query_impl<0>(dv, n, q, page_ids, n_pages, topk_ids, st, tm)
-                       : query_impl<1>(dv, n, q, page_ids, n_pages, topk_ids, st, tm);
+  timer_begin(tm, st);
+  hipError_t e = launch_prep(dv, n, nullptr, nullptr, q, 2, st);
+  if (e != hipSuccess) return e;
+  timer_mark(tm, KID_PREP, st);
+  if (dv.dtype == 0)
+    query_tail<0>(dv, n, page_ids, n_pages, topk_ids, nullptr, nullptr, st, tm);
+  else
+    query_tail<1>(dv, n, page_ids, n_pages, topk_ids, nullptr, nullptr, st, tm);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const Dev &dv, int64_t n, const void *k_new, const void *v_new,
+                         const void *q, int32_t *page_ids, int32_t *n_pages, int32_t *topk_ids,
+                         float *out, hipStream_t st, Timer *tm) {
+  // the new token is token n; the query sees n + 1 tokens
+  timer_begin(tm, st);
+  hipError_t e = launch_prep(dv, n, k_new, v_new, q, 3, st);
+  if (e != hipSuccess) return e;
+  timer_mark(tm, KID_PREP, st);
+  // pages up to kFusedMaxPages: the finaliser runs the attention itself
+  const bool fused = dv.P <= kFusedMaxPages;
+  if (dv.dtype == 0)
+    query_tail<0>(dv, n + 1, page_ids, n_pages, topk_ids, q, fused ? out : nullptr, st, tm);
+  else
+    query_tail<1>(dv, n + 1, page_ids, n_pages, topk_ids, q, fused ? out : nullptr, st, tm);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return fused ? hipSuccess : launch_attn(dv, q, page_ids, n_pages, out, st, tm);
 }
 
 }  // namespace ice

@@ -33,8 +33,8 @@ def test_exports_every_declared_symbol(L):
     header = open(os.path.join(ROOT, "include", "ice.h")).read()
     names = set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(ice_\w+)\s*\(", header, re.M))
     assert {"ice_workspace_bytes", "ice_build_scratch_bytes", "ice_build_index", "ice_insert",
-            "ice_query_pages", "ice_sparse_attn", "ice_destroy_index", "ice_status_string",
-            "ice_index_layout"} <= names
+            "ice_query_pages", "ice_sparse_attn", "ice_decode_step", "ice_destroy_index",
+            "ice_status_string", "ice_index_layout"} <= names
     for n in names:
         assert hasattr(L, n), n
 
@@ -116,6 +116,8 @@ def test_null_handles(L):
     assert L.ice_insert(None, FAKE, FAKE, None) == B.ICE_ERR_INVALID_ARG
     assert L.ice_query_pages(None, FAKE, FAKE, FAKE, None, None) == B.ICE_ERR_INVALID_ARG
     assert L.ice_sparse_attn(None, FAKE, FAKE, FAKE, FAKE, None) == B.ICE_ERR_INVALID_ARG
+    assert L.ice_decode_step(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                             None) == B.ICE_ERR_INVALID_ARG
     y = B.IceLayout()
     assert L.ice_index_layout(None, ctypes.byref(y)) == B.ICE_ERR_INVALID_ARG
     L.ice_destroy_index(None)

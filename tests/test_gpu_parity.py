@@ -266,6 +266,44 @@ def test_repeated_queries_are_deterministic(B):
                 assert torch.equal(a_, b_)
 
 
+@pytest.mark.parametrize("dtype,S,g,d,p,m,L", [("bf16", 8, 4, 128, 16, 8, 4),
+                                               ("f32", 2, 2, 64, 8, 3, 3)])
+def test_decode_step_equals_separate_calls(B, dtype, S, g, d, p, m, L):
+    """ice_decode_step gives bit-identical pages, top-k and attention to
+    ice_insert + ice_query_pages + ice_sparse_attn, step after step, and its
+    last step matches the oracle."""
+    n, steps, k = 3000, 6, 128
+    dev = torch.device("cuda")
+    K, V, q0, _ = _inputs(S, n + steps, d, g, 24, 31, dtype)
+    U = W.directions(m * L, d, 31, dtype).to(dev)
+    print(f"[case] decode_step {dtype} S={S} g={g} d={d} p={p} m={m} L={L}", flush=True)
+    mk = lambda: B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U,
+                         page_size=p, budget_k=k, m=m, L=L, gqa_group=g, capacity=n + steps)
+    a, b = mk(), mk()
+    gen = torch.Generator().manual_seed(5)
+    for t in range(steps):
+        qt = torch.randn(S * g, d, generator=gen).to(q0.dtype).to(dev)
+        kn, vn = K[:, n + t].contiguous().to(dev), V[:, n + t].contiguous().to(dev)
+        pa, na, oa, ta = a.decode_step(kn, vn, qt, with_topk=True)
+        b.insert(kn, vn)
+        pb, nb, tb = b.query_pages(qt, with_topk=True)
+        ob = b.sparse_attn(qt, pb, nb)
+        torch.cuda.synchronize()
+        assert torch.equal(pa, pb) and torch.equal(na, nb) and torch.equal(ta, tb)
+        assert torch.equal(oa, ob)
+    prm = oracle.Params(d=d, p=p, k=k, m=m, L=L, g=g)
+    st = oracle.OracleStream(prm, _np(K[0, :n]), _np(V[0, :n]), _np(U), n_cap=n + steps)
+    for t in range(steps):
+        st.insert(_np(K[0, n + t]), _np(V[0, n + t]))
+    q_s = _np(qt[:g])
+    r = st.query(q_s, literal=False)
+    _check_index(a, st, 0, n + steps)
+    _check_query(a, st, 0, r, pa, na, ta, oa[:g], q_s)
+    with pytest.raises(B.IceError) as e:
+        a.decode_step(kn, vn, qt)
+    assert e.value.status == B.ICE_ERR_CAPACITY
+
+
 def test_capacity_error(B):
     dev = torch.device("cuda")
     K, V, q, _ = _inputs(1, 40, 128, 1, 4, 13, "bf16")
