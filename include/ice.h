@@ -120,7 +120,8 @@ ice_status ice_insert(ice_index *idx, const void *k_new, const void *v_new, void
 
 /* Query: P-DCI candidates, exact rerank, page selection (IceCache paper page,
  * Figure 2 steps (2)-(3)).
- *   q         device [S*g][d] dtype: query heads, head j uses stream j / g.
+ *   q         device [S*g][d] dtype: query heads, head j uses stream j / g;
+ *             16-byte aligned.
  *   page_ids  device [S][P] int32 out: selected pages in selection order,
  *             -1 after the last.
  *   n_pages   device [S] int32 out.
@@ -139,7 +140,7 @@ ice_status ice_query_pages(ice_index *idx, const void *q, int32_t *page_ids, int
 
 /* Sparse attention over every token of the selected pages (IceCache paper
  * page, Figure 2 step (3)).
- *   q         device [S*g][d] dtype.
+ *   q         device [S*g][d] dtype, 16-byte aligned.
  *   page_ids  device [S][P] int32, n_pages device [S] int32 (as written by
  *             ice_query_pages; any valid page numbers may be passed).
  *   out       device [S*g][d] fp32: softmax(q k^T / sqrt(d)) V per head,

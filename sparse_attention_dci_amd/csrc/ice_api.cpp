@@ -85,7 +85,7 @@ struct Layout {
   int64_t ncell, pcap;
   int64_t dirs, dirs32, norm_c, inv_c, inv_c2, maxnsq, codes, list_code, list_id, loc, page_tokens,
       page_len, page_cell, npages, cell_count, cell_last, pool_k, pool_v, qkv, qcode, mbuf,
-      hist, cand, cand_count, bnd, bnd_rk, bnd_pg, bnd_count, rr_key, rr_id, rr_pg, rr_count,
+      hist, hist2, cand, cand_count, bnd, bnd_rk, bnd_pg, bnd_count, rr_key, rr_id, rr_pg, rr_count,
       attn_part;
   int64_t total;
 };
@@ -160,6 +160,7 @@ ice_status make_layout(const ice_params *prm, int32_t S, int64_t n, int64_t ncap
   y.qcode = seg(Sl * mL * 4);
   y.mbuf = seg(Sl * Ll * ncap * 4);
   y.hist = seg(Sl * Ll * ice::kHistBins * 4);
+  y.hist2 = seg(Sl * Ll * ice::kHistBins * 4);
   y.cand = seg(Sl * Ll * y.k0 * 4);
   y.cand_count = seg(Sl * Ll * 4);
   y.bnd = seg(Sl * Ll * ncap * 8);
@@ -290,6 +291,7 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
   dv.qcode = (int32_t *)(w + y.qcode);
   dv.mbuf = (uint32_t *)(w + y.mbuf);
   dv.hist = (uint32_t *)(w + y.hist);
+  dv.hist2 = (uint32_t *)(w + y.hist2);
   dv.cand = (int32_t *)(w + y.cand);
   dv.cand_count = (uint32_t *)(w + y.cand_count);
   dv.bnd = (unsigned long long *)(w + y.bnd);
@@ -338,7 +340,7 @@ ice_status ice_insert(ice_index *idx, const void *k_new, const void *v_new, void
 
 ice_status ice_query_pages(ice_index *idx, const void *q, int32_t *page_ids, int32_t *n_pages,
                            int32_t *topk_ids, void *stream) {
-  if (!idx || !q || !page_ids || !n_pages || !aligned(q, 4) || !aligned(page_ids, 4) ||
+  if (!idx || !q || !page_ids || !n_pages || !aligned(q, 16) || !aligned(page_ids, 4) ||
       !aligned(n_pages, 4) || (topk_ids && !aligned(topk_ids, 4)))
     return ICE_ERR_INVALID_ARG;
   hipError_t e = ice::launch_query(idx->dv, idx->n, q, page_ids, n_pages, topk_ids,

@@ -63,6 +63,7 @@ struct Dev {
   int32_t *qcode;        // [S][mL]
   uint32_t *mbuf;        // [S][L][ncap]
   uint32_t *hist;        // [S][L][kHistBins]
+  uint32_t *hist2;       // [S][L][kHistBins] second level: the boundary bin's next 11 bits
   int32_t *cand;         // [S][L][k0]
   uint32_t *cand_count;  // [S][L]
   unsigned long long *bnd;  // [S][L][ncap] boundary-bin entries (M << 32 | token)

@@ -32,7 +32,8 @@ constexpr int kFinalThreads = 1024;
 constexpr int kHashSlots = 8192;    // 2 * kMaxCand
 constexpr int kBndLds = 2048;       // boundary entries ranked in LDS
 constexpr int kBuckets = 2048;
-constexpr int kFusedMaxPages = 1024;  // page budgets up to this take the fused attention
+constexpr int kFusedMaxPages = 1024;
+constexpr int kMaxTies = 256;  // page budgets up to this take the fused attention
 
 // ---------------------------------------------------------------- helpers
 
@@ -45,24 +46,31 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
-// One whole wave: smallest bin b of h[0..kHistBins) whose inclusive prefix
-// reaches `target` (1 <= target <= total) and the count below b.
-__device__ void wave_find_bin(const uint32_t *h, uint32_t target, uint32_t &bin,
-                              uint32_t &below) {
-  constexpr int per = kHistBins / 64;
-  const int lane = __lane_id();
-  uint32_t v[per];
-  uint32_t sum = 0;
-  const uint4 *h4 = reinterpret_cast<const uint4 *>(h + lane * per);
+// One whole wave: smallest bin b of a kHistBins histogram whose inclusive
+// prefix reaches `target` (1 <= target <= total) and the count below b.  The
+// histogram is read by wave_hist_load (lane j holds bins 32j .. 32j+31) so
+// that several can be in flight before any is searched.
+constexpr int kBinsPerLane = kHistBins / 64;
+
+__device__ __forceinline__ void wave_hist_load(const uint32_t *h, uint32_t (&v)[kBinsPerLane]) {
+  const uint4 *h4 = reinterpret_cast<const uint4 *>(h + __lane_id() * kBinsPerLane);
 #pragma unroll
-  for (int k = 0; k < per / 4; ++k) {
+  for (int k = 0; k < kBinsPerLane / 4; ++k) {
     const uint4 x = h4[k];
     v[4 * k] = x.x;
     v[4 * k + 1] = x.y;
     v[4 * k + 2] = x.z;
     v[4 * k + 3] = x.w;
-    sum += x.x + x.y + x.z + x.w;
   }
+}
+
+__device__ void wave_find_bin_regs(const uint32_t (&v)[kBinsPerLane], uint32_t target,
+                                   uint32_t &bin, uint32_t &below) {
+  constexpr int per = kBinsPerLane;
+  const int lane = __lane_id();
+  uint32_t sum = 0;
+#pragma unroll
+  for (int k = 0; k < per; ++k) sum += v[k];
   const uint32_t incl = wave_incl_scan(sum);
   const uint32_t excl = incl - sum;
   const bool mine = excl < target && incl >= target;
@@ -84,14 +92,21 @@ __device__ void wave_find_bin(const uint32_t *h, uint32_t target, uint32_t &bin,
   below = __shfl(bl, src);
 }
 
-// Exact fp64 scores of ids[0..cnt) by a block of NT threads: per round of as
-// many tokens as ROWBYTES of LDS holds, one round trip gathers their page
-// slots, one stages their key rows in LDS, then one thread per row runs the
-// ordered chain.  emit(x, slot, score) receives each result.  lcs needs
+__device__ __forceinline__ void wave_find_bin(const uint32_t *h, uint32_t target, uint32_t &bin,
+                                              uint32_t &below) {
+  uint32_t v[kBinsPerLane];
+  wave_hist_load(h, v);
+  wave_find_bin_regs(v, target, bin, below);
+}
+
+// Exact fp64 scores of cnt tokens by a block of NT threads: per round of as
+// many tokens as ROWBYTES of LDS holds, their key rows are staged in LDS
+// (slot_of(j) gives token j's page slot), then one thread per row runs the
+// ordered chain.  emit(j, slot, score) receives each result.  lcs needs
 // ROWBYTES / 128 entries.
-template <int DT, int NT, int ROWBYTES, typename Emit>
-__device__ void block_score(const Dev &dv, int s, const int32_t *ids, uint32_t cnt,
-                            const float *qkv, int32_t *lcs, uint32_t *rows, Emit emit) {
+template <int DT, int NT, int ROWBYTES, typename SlotOf, typename Emit>
+__device__ void block_score(const Dev &dv, int s, uint32_t cnt, SlotOf slot_of, const float *qkv,
+                            int32_t *lcs, uint32_t *rows, Emit emit) {
   const int tid = threadIdx.x;
   const int d = dv.d;
   const int row_bytes = d * dv.elem;
@@ -101,7 +116,7 @@ __device__ void block_score(const Dev &dv, int s, const int32_t *ids, uint32_t c
   constexpr int kIter = (ROWBYTES / 16 + NT - 1) / NT;
   for (uint32_t b0 = 0; b0 < cnt; b0 += cap) {
     const uint32_t nr = min(cap, cnt - b0);
-    if ((uint32_t)tid < nr) lcs[tid] = dv.loc[(int64_t)s * dv.ncap + ids[b0 + tid]];
+    if ((uint32_t)tid < nr) lcs[tid] = slot_of(b0 + tid);
     lds_barrier();
     uint4 v[kIter];
 #pragma unroll
@@ -266,13 +281,17 @@ __global__ __launch_bounds__(kScanThreads) void k_qscan(Dev dv, int64_t n) {
 
 // ---------------------------------------------------------------- collect
 
-// Blocks of kScanTpb tokens.  Token i is a candidate of composite l when its
-// bin is below the k0-th smallest bin b*, a boundary entry when its bin is b*.
-// Every candidate or boundary token of the block is scored once; the
-// below-bin ones go to the stream's rerank list, the boundary entries carry
-// their score and page to the final selection.  Appends take one device
-// atomic per block and list.
+// Blocks of kScanTpb tokens, mapped to streams as in the scan.  Token i is a
+// candidate of composite l when its bin is below the k0-th smallest bin b*,
+// a boundary entry when its bin is b*.  Every candidate or boundary token of
+// the block is scored once; the below-bin ones go to the stream's rerank
+// list, the boundary entries carry their score and page to the final
+// selection and are also counted in a second-level histogram of bin b* (the
+// next 11 bits of M), which lets the finaliser resolve the boundary without
+// ranking it.  Appends take one device atomic per block and list, issued
+// before the scoring and consumed after it.
 constexpr int kCollectRowBytes = 32 * 1024;
+constexpr int kSubShift = kHistShift - kHistBits;  // second-level bins: M >> 9 & 2047
 
 template <int DT>
 __global__ __launch_bounds__(kScanThreads) void k_qcollect(Dev dv, int64_t n) {
@@ -284,7 +303,8 @@ __global__ __launch_bounds__(kScanThreads) void k_qcollect(Dev dv, int64_t n) {
   __shared__ uint32_t ccount[32], bcount[32], cbase[32], bbase[32];
   __shared__ uint32_t nc, nrl, rbase;
   __shared__ float qkv[128];
-  __shared__ int32_t cid[kScanTpb];
+  __shared__ int32_t cid[kScanTpb];      // candidate or boundary tokens, as offsets in the block
+  __shared__ int32_t lloc[kScanTpb];     // page slots of the block's tokens
   __shared__ unsigned long long skb[kScanTpb];
   __shared__ int32_t spb[kScanTpb];
   __shared__ int32_t lcs[kCollectRowBytes / 128];
@@ -295,16 +315,21 @@ __global__ __launch_bounds__(kScanThreads) void k_qcollect(Dev dv, int64_t n) {
   const int64_t i1 = min(i0 + kScanTpb, n);
   const int64_t ii[2] = {i0 + tid, i0 + kScanThreads + tid};
   const bool vv[2] = {ii[0] < i1, ii[1] < i1};
-  // distances of both tokens for the first 8 composites (unconditional loads)
+
+  // 1. loads: M of both tokens for the first 8 composites, their page slots,
+  // the query, the threshold bins (unconditional loads at clamped addresses)
   uint32_t Mv[2][8];
+  int32_t lc[2];
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < 2; ++u) {
+    const int64_t ic = vv[u] ? ii[u] : 0;
 #pragma unroll
     for (int l = 0; l < 8; ++l) {
-      const int lc = l < L ? l : 0;
-      const int64_t ic = vv[u] ? ii[u] : 0;
-      Mv[u][l] = dv.mbuf[((int64_t)s * L + lc) * dv.ncap + ic];
+      const int lcl = l < L ? l : 0;
+      Mv[u][l] = dv.mbuf[((int64_t)s * L + lcl) * dv.ncap + ic];
     }
+    lc[u] = dv.loc[(int64_t)s * dv.ncap + ic];
+  }
   auto Mof = [&](int u, int l) -> uint32_t {
     uint32_t M = 0;
     if (l < 8) {
@@ -316,7 +341,15 @@ __global__ __launch_bounds__(kScanThreads) void k_qcollect(Dev dv, int64_t n) {
     }
     return M;
   };
-  if (tid < dv.d) qkv[tid] = dv.qkv[(int64_t)s * dv.d + tid];
+  const float qk = dv.qkv[(int64_t)s * dv.d + min(tid, dv.d - 1)];
+  for (int l = w; l < L; l += kScanThreads / 64) {
+    uint32_t bb, bl;
+    wave_find_bin(dv.hist + ((int64_t)s * L + l) * kHistBins, k0e, bb, bl);
+    if (lane == 0) bstar[l] = bb;
+  }
+  if (tid < dv.d) qkv[tid] = qk;
+  lloc[tid] = lc[0];
+  lloc[kScanThreads + tid] = lc[1];
   if (tid < L) {
     ccount[tid] = 0;
     bcount[tid] = 0;
@@ -325,13 +358,9 @@ __global__ __launch_bounds__(kScanThreads) void k_qcollect(Dev dv, int64_t n) {
     nc = 0;
     nrl = 0;
   }
-  for (int l = w; l < L; l += kScanThreads / 64) {
-    uint32_t bb, bl;
-    wave_find_bin(dv.hist + ((int64_t)s * L + l) * kHistBins, k0e, bb, bl);
-    if (lane == 0) bstar[l] = bb;
-  }
   __syncthreads();
-  // classify
+
+  // 2. classify
   uint32_t below[2], bnd[2];
   int slot[2];
 #pragma unroll
@@ -341,14 +370,18 @@ __global__ __launch_bounds__(kScanThreads) void k_qcollect(Dev dv, int64_t n) {
     slot[u] = -1;
     if (vv[u]) {
       for (int l = 0; l < L; ++l) {
-        const uint32_t bb = Mof(u, l) >> kHistShift;
+        const uint32_t M = Mof(u, l), bb = M >> kHistShift;
         if (bb < bstar[l]) below[u] |= 1u << l;
-        if (bb == bstar[l]) bnd[u] |= 1u << l;
+        if (bb == bstar[l]) {
+          bnd[u] |= 1u << l;
+          atomicAdd(&dv.hist2[((int64_t)s * L + l) * kHistBins + ((M >> kSubShift) & (kHistBins - 1))],
+                    1u);
+        }
       }
     }
-    if (below[u] | bnd[u]) {
+    if (below[u] | bnd[u]) {  // sparse: a few lanes per block
       slot[u] = (int)atomicAdd(&nc, 1u);
-      cid[slot[u]] = (int32_t)ii[u];
+      cid[slot[u]] = (int32_t)(ii[u] - i0);
       if (below[u]) atomicAdd(&nrl, 1u);
       for (int l = 0; l < L; ++l) {
         if ((below[u] >> l) & 1u) atomicAdd(&ccount[l], 1u);
@@ -357,28 +390,39 @@ __global__ __launch_bounds__(kScanThreads) void k_qcollect(Dev dv, int64_t n) {
     }
   }
   lds_barrier();
-  // one device atomic per list for the block
+
+  // 3. one device atomic per list for the block, consumed after the scoring
+  uint32_t my_c = 0, my_b = 0, my_r = 0;
   if (tid < L) {
-    cbase[tid] = ccount[tid] ? atomicAdd(&dv.cand_count[s * L + tid], ccount[tid]) : 0u;
-    bbase[tid] = bcount[tid] ? atomicAdd(&dv.bnd_count[s * L + tid], bcount[tid]) : 0u;
+    my_c = ccount[tid] ? atomicAdd(&dv.cand_count[s * L + tid], ccount[tid]) : 0u;
+    my_b = bcount[tid] ? atomicAdd(&dv.bnd_count[s * L + tid], bcount[tid]) : 0u;
+  }
+  if (tid == 64) my_r = nrl ? atomicAdd(&dv.rr_count[s], nrl) : 0u;
+
+  // 4. exact scores of the block's candidate and boundary tokens
+  const int p = dv.p;
+  unsigned long long *skbp = skb;
+  int32_t *spbp = spb;
+  const int32_t *cidp = cid, *llocp = lloc;
+  block_score<DT, kScanThreads, kCollectRowBytes>(
+      dv, s, nc, [cidp, llocp](uint32_t j) { return llocp[cidp[j]]; }, qkv, lcs, rows,
+      [skbp, spbp, p](uint32_t x, int32_t slotx, double sc) {
+        skbp[x] = score_rank_key(sc);
+        spbp[x] = slotx / p;
+      });
+
+  // 5. the appends
+  if (tid < L) {
+    cbase[tid] = my_c;
+    bbase[tid] = my_b;
     ccount[tid] = 0;
     bcount[tid] = 0;
   }
   if (tid == 64) {
-    rbase = nrl ? atomicAdd(&dv.rr_count[s], nrl) : 0u;
+    rbase = my_r;
     nrl = 0;
   }
   lds_barrier();
-  // exact scores of the block's candidate and boundary tokens
-  const int p = dv.p;
-  unsigned long long *skbp = skb;
-  int32_t *spbp = spb;
-  block_score<DT, kScanThreads, kCollectRowBytes>(
-      dv, s, cid, nc, qkv, lcs, rows, [skbp, spbp, p](uint32_t x, int32_t lc, double sc) {
-        skbp[x] = score_rank_key(sc);
-        spbp[x] = lc / p;
-      });
-  // the appends
   const int64_t rr0 = (int64_t)s * L * dv.k0;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -500,7 +544,9 @@ struct FinalShared {
     };
   };
   uint32_t cnt[256];
-  uint32_t cc[32], nb[32], need[32], boff[33], extra[32];
+  uint32_t cc[32], nb[32], need[32], boff[33], extra[32], b2[32], need2[32];
+  uint32_t tie[kMaxTies];  // boundary entries in their composite's second-level bin b2
+  uint32_t ntie;
   uint32_t nu;
   uint32_t rr;
   unsigned long long res;
@@ -521,23 +567,37 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
   const int L = dv.L, k0 = dv.k0;
   const uint32_t k0e = (uint32_t)min((int64_t)k0, n);
 
-  // A. counts and thresholds
+  // A. loads, all issued up front: the query operands of the attention, the
+  // counts, the two threshold levels of every composite
+  u32x4 qh[D / 32], ql[D / 32];
+  attn_load_q<DT, D>(dv, s, q, qh, ql);
   for (int x = tid; x < kHashSlots; x += kFinalThreads) sh.hash[x] = 0;
+  const uint32_t nrr_ld = dv.rr_count[s];
   if (tid < L) {
     sh.cc[tid] = dv.cand_count[s * L + tid];
     sh.nb[tid] = dv.bnd_count[s * L + tid];
     sh.extra[tid] = 0;
     sh.need[tid] = 0;
+    sh.b2[tid] = 0;
+    sh.need2[tid] = 0;
   }
   if (k0e > 0) {
     for (int l = w; l < L; l += kFinalThreads / 64) {
-      uint32_t b, bl;
-      wave_find_bin(dv.hist + ((int64_t)s * L + l) * kHistBins, k0e, b, bl);
-      if (lane == 0) sh.need[l] = k0e - bl;
+      uint32_t b, bl, b2, bl2, h1[kBinsPerLane], h2[kBinsPerLane];
+      wave_hist_load(dv.hist + ((int64_t)s * L + l) * kHistBins, h1);  // both levels in flight
+      wave_hist_load(dv.hist2 + ((int64_t)s * L + l) * kHistBins, h2);
+      wave_find_bin_regs(h1, k0e, b, bl);
+      const uint32_t need = k0e - bl;  // picks from the boundary bin, >= 1
+      wave_find_bin_regs(h2, need, b2, bl2);
+      if (lane == 0) {
+        sh.need[l] = need;
+        sh.b2[l] = b2;
+        sh.need2[l] = need - bl2;  // picks from second-level bin b2
+      }
     }
   }
-  const uint32_t nrr = k0e > 0 ? dv.rr_count[s] : 0u;
   __syncthreads();
+  const uint32_t nrr = k0e > 0 ? nrr_ld : 0u;
   if (tid == 0) {
     uint32_t o = 0;
     for (int l = 0; l < L; ++l) {
@@ -546,6 +606,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
     }
     sh.boff[L] = o;
     sh.nu = nrr;
+    sh.ntie = 0;
   }
   __syncthreads();
   const uint32_t nbt = sh.boff[L];
@@ -573,7 +634,8 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
   __syncthreads();
 
   // C. the need_l smallest (M, i) of each composite's boundary bin join the
-  // composite's candidates, and the union when not in it yet
+  // composite's candidates, and the union when not in it yet: every entry in
+  // a second-level bin below b2_l, and the need2_l smallest of bin b2_l
   auto add_pick = [&](int l, unsigned long long key, unsigned long long rk, int32_t pg) {
     const int32_t id = (int32_t)(key & 0xffffffffull);
     dv.cand[((int64_t)s * L + l) * k0 + sh.cc[l] + atomicAdd(&sh.extra[l], 1u)] = id;
@@ -584,15 +646,50 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
       sh.spg[pos] = pg;
     }
   };
+  auto sub_of = [](unsigned long long key) -> uint32_t {
+    return (uint32_t)(key >> (32 + kSubShift)) & (kHistBins - 1);
+  };
   if (nbt > 0) {
     if (bnd_lds) {
+      // entries below second-level bin b2_l are picked outright; the few in
+      // bin b2_l go to a tie list and are ranked among themselves
       for (uint32_t x = tid; x < nbt; x += kFinalThreads) {
         int l = 0;
         while (x >= sh.boff[l + 1]) ++l;
         const unsigned long long key = sh.bk[x];
-        uint32_t rank = 0;
-        for (uint32_t y = sh.boff[l]; y < sh.boff[l + 1]; ++y) rank += sh.bk[y] < key;
-        if (rank < sh.need[l]) add_pick(l, key, sh.brk[x], sh.bpg[x]);
+        const uint32_t sb = sub_of(key);
+        if (sb < sh.b2[l]) add_pick(l, key, sh.brk[x], sh.bpg[x]);
+        if (sb == sh.b2[l]) {
+          const uint32_t t = atomicAdd(&sh.ntie, 1u);
+          if (t < kMaxTies) sh.tie[t] = x;
+        }
+      }
+      __syncthreads();
+      const uint32_t nt = sh.ntie;
+      if (nt <= (uint32_t)kMaxTies) {
+        for (uint32_t t = tid; t < nt; t += kFinalThreads) {
+          const uint32_t x = sh.tie[t];
+          int l = 0;
+          while (x >= sh.boff[l + 1]) ++l;
+          const unsigned long long key = sh.bk[x];
+          uint32_t rank = 0;
+          for (uint32_t u = 0; u < nt; ++u) {
+            const uint32_t y = sh.tie[u];
+            rank += (y >= sh.boff[l]) & (y < sh.boff[l + 1]) & (sh.bk[y] < key);
+          }
+          if (rank < sh.need2[l]) add_pick(l, key, sh.brk[x], sh.bpg[x]);
+        }
+      } else {  // many equal second-level bins: rank tied entries over their composite
+        for (uint32_t x = tid; x < nbt; x += kFinalThreads) {
+          int l = 0;
+          while (x >= sh.boff[l + 1]) ++l;
+          const unsigned long long key = sh.bk[x];
+          if (sub_of(key) != sh.b2[l]) continue;
+          uint32_t rank = 0;
+          for (uint32_t y = sh.boff[l]; y < sh.boff[l + 1]; ++y)
+            rank += (sub_of(sh.bk[y]) == sh.b2[l]) & (sh.bk[y] < key);
+          if (rank < sh.need2[l]) add_pick(l, key, sh.brk[x], sh.bpg[x]);
+        }
       }
     } else {
       for (int l = 0; l < L; ++l) {
@@ -722,7 +819,11 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
   auto bookkeeping = [&]() {
     if (tid < L && k0e > 0) dv.cand_count[s * L + tid] = sh.cc[tid] + sh.extra[tid];
     uint32_t *hist = dv.hist + (int64_t)s * L * kHistBins;
-    for (int x = tid; x < L * kHistBins; x += kFinalThreads) hist[x] = 0;
+    uint32_t *hist2 = dv.hist2 + (int64_t)s * L * kHistBins;
+    for (int x = tid; x < L * kHistBins; x += kFinalThreads) {
+      hist[x] = 0;
+      hist2[x] = 0;
+    }
   };
   if (out == nullptr) {
     bookkeeping();
@@ -734,8 +835,6 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
   // selection arrays holds the wave outputs)
   constexpr int NW = kFinalThreads / 64;
   static_assert(sizeof(FinalShared) >= (size_t)NW * kMaxGroup * D * 4 + 0, "wave outputs fit");
-  u32x4 qh[D / 32], ql[D / 32];
-  attn_load_q<DT, D>(dv, s, q, qh, ql);
   AttnWave<D> st;
   attn_init(st);
   __syncthreads();
@@ -805,9 +904,9 @@ hipError_t launch_query(const Dev &dv, int64_t n, const void *q, int32_t *page_i
   if (e != hipSuccess) return e;
   timer_mark(tm, KID_PREP, st);
   if (dv.dtype == 0)
-    query_tail<0>(dv, n, page_ids, n_pages, topk_ids, nullptr, nullptr, st, tm);
+    query_tail<0>(dv, n, page_ids, n_pages, topk_ids, q, nullptr, st, tm);
   else
-    query_tail<1>(dv, n, page_ids, n_pages, topk_ids, nullptr, nullptr, st, tm);
+    query_tail<1>(dv, n, page_ids, n_pages, topk_ids, q, nullptr, st, tm);
   return hipGetLastError();
 }
 
