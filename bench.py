@@ -1,15 +1,20 @@
 """Decode-step benchmark of the IceCache hot path on one MI355X.
 
-Workload: one Llama-3.1-8B-shaped layer at 36,864 tokens of context (8 KV
-heads, 32 query heads, head_dim 128, bf16 KV, page 16, budget 256 tokens,
-DCI m=8, L=4), synthetic mixture keys.  A decode step is the whole decode-time
-path on that layer: insert the new token's key/value into every head's index,
-query (P-DCI candidates, exact rerank, page selection) and paged sparse
-attention.  The prefill build of the index is timed separately (build_ms).
+Default workload: one Llama-3.1-8B-shaped layer at 36,864 tokens of context
+(8 KV heads, 32 query heads, head_dim 128, bf16 KV, page 16, budget 256
+tokens, DCI m=8, L=4), synthetic mixture keys.  A decode step is the whole
+decode-time path on that layer, one ice_decode_step call: insert the new
+token's key/value into every head's index, query (P-DCI candidates, exact
+rerank, page selection) and paged sparse attention.  The prefill build of the
+index is timed separately (build_ms).
 
-Eight copies of the layer (eight "layers" with their own inputs, ~2.3 GB of
-index) are built and the steps rotate over them, so each step finds its
-index cold in the 256 MB last-level cache, as in a real 32-layer decode.
+Several copies of the layer ("layers" with their own inputs) are built and the
+steps rotate over them, so each step finds its index cold in the 256 MB
+last-level cache, as in a real multi-layer decode.
+
+--workload picks another configuration (the 32-layer decode, the 131k needle
+batch); --copy-calibration times a plain device copy of known size instead
+(the reference for the HBM byte counters).
 
 Prints one JSON line (the last line of stdout).
 """
@@ -26,7 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
-WORKLOAD = "llama8b_layer_36k"
+DEFAULT_WORKLOAD = "llama8b_layer_36k"
 
 
 def log(*a):
@@ -43,35 +48,36 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w, kernel: str, ntok: int, n_cand: float, attended: float) -> float:
-    """Bytes the decode path has to move per launch of `kernel` for the whole layer
+def algorithmic_bytes(w, kernel: str, ntok: float, n_cand: float, attended: float) -> float:
+    """Bytes the decode path has to move per launch of `kernel` for one layer
     (S streams): the per-unit figures times the units one launch processes.
 
-    prep      the insert (new k, v in; pool rows, codes and list entries out:
-              4d*elem + 12*mL) and the query's projection (the heads and the fp32
-              directions: g*d*elem + (d+1)*mL*4)
+    prep      insert: k, v in and their pool rows out (4*d*elem), mL list entries
+              (8 B) and codes (4 B); query: the g heads (g*d*elem), the fp32
+              directions ((d+1)*mL*4), the query codes out (4*mL)
     qscan     every token's m*L projection codes: 4*mL per token
     qcollect  the key row of every reranked candidate: d*elem per candidate
-    qfinal    the rerank list (rank key, token, page): 16 bytes per candidate
-    attn      K and V rows of every attended token, the queries and the outputs
+    qfinal    the rerank list (16 B per candidate), then the attention: K and V
+              rows of every attended token (2*d*elem each), the g heads and
+              their fp32 outputs
+    attn      (only when the finaliser does not run the attention) as above
     """
     S, d, mL, g = w.streams, w.d, w.mL, w.g
     elem = 2 if w.dtype == "bf16" else 4
+    att = attended * 2 * d * elem + g * d * (elem + 4)
     per_stream = {
-        "prep": 4.0 * d * elem + 12.0 * mL + g * d * elem + (d + 1) * mL * 4.0,
+        "prep": 4.0 * d * elem + 12.0 * mL + g * d * elem + (d + 1) * mL * 4.0 + 4.0 * mL,
         "qscan": ntok * mL * 4.0,
         "qcollect": n_cand * d * elem,
-        "qfinal": n_cand * 16.0,
-        "attn": attended * 2 * d * elem + g * d * (elem + 4),
+        "qfinal": n_cand * 16.0 + att,
+        "attn": att,
     }
     return S * per_stream.get(kernel, 0.0)
 
 
-STEP_KERNELS = ("prep", "qscan", "qcollect", "qfinal", "attn")
-
-
 def cpu_baseline(w, K, V, q, U, k_new, v_new, reps: int):
-    """The oracle, as it stands, on one layer's decode step for every stream."""
+    """The oracle, as it stands, on one layer's decode step for every stream.
+    Returns (best microseconds, threads, mean union size |C| per stream)."""
     import concurrent.futures as cf
 
     import numpy as np
@@ -97,13 +103,29 @@ def cpu_baseline(w, K, V, q, U, k_new, v_new, reps: int):
         st.attend(qs, r["page_ids"])
         return r
 
-    times = []
+    times, sizes = [], []
     with cf.ThreadPoolExecutor(threads) as ex:
         for _ in range(reps):
             t0 = time.perf_counter()
-            list(ex.map(step, range(w.streams)))
+            res = list(ex.map(step, range(w.streams)))
             times.append(time.perf_counter() - t0)
-    return min(times) * 1e6, threads
+            sizes = [len(r["C"]) for r in res]
+    return min(times) * 1e6, threads, float(np.mean(sizes))
+
+
+def copy_calibration(args):
+    """A plain device-to-device copy of known size, for scaling the HBM byte
+    counters (FETCH_SIZE / WRITE_SIZE) of the profiled kernels."""
+    import torch
+    n = 256 << 20  # bytes
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": args.steps}), flush=True)
 
 
 def main():
@@ -111,28 +133,36 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--layers", type=int, default=8,
+                    help="index copies rotated (at least the layers of one step)")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the streams of different layers and heads are independent, so a multi-GPU "
               "run would shard whole layers with no exchange)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args)
+        return
 
     import torch
 
     from sparse_attention_dci_amd import binding, workloads as W
 
-    w = W.WORKLOADS[WORKLOAD]
+    w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    R = args.layers
-    total_steps = args.warmup + 2 * args.steps
-    per_layer = (total_steps + R - 1) // R + 1
+    # a decode step of the 32-layer workload runs every layer once
+    layers_per_step = w.layers if args.workload == "llama8b_decode_36k" else 1
+    R = max(args.layers, layers_per_step)
+    total_calls = (args.warmup + 2 * args.steps) * layers_per_step
+    per_layer = (total_calls + R - 1) // R + 1
     cap = w.n + per_layer
 
-    log(f"[bench] building {R} layers of {WORKLOAD}")
+    log(f"[bench] building {R} layers of {args.workload}")
     layers, build_ms = [], []
     keep = None
     for r in range(R):
@@ -146,81 +176,92 @@ def main():
         torch.cuda.synchronize()
         build_ms.append(e0.elapsed_time(e1))
         idx.release_build_buffers()
-        layers.append((idx, q))
-        if r == 0:
+        layers.append(idx)
+        if r == 0 and not args.no_cpu:
             keep = (K, V, q, U)
-        else:
-            del K, V
+        del K, V
     log(f"[bench] build ms per layer: {[round(x, 2) for x in build_ms]}")
 
-    steps_in = [W.step_inputs(w, layer=t % R, step=t, device=dev) for t in range(total_steps)]
+    steps_in = [W.step_inputs(w, layer=t % R, step=t, device=dev) for t in range(4 * R)]
     outs = [(torch.empty(w.streams, w.k // w.p, dtype=torch.int32, device=dev),
              torch.empty(w.streams, dtype=torch.int32, device=dev),
              torch.empty(w.streams * w.g, w.d, dtype=torch.float32, device=dev))
             for _ in range(R)]
+    call = [0]
 
-    def step(t):
-        r = t % R
-        idx, _ = layers[r]
-        k_new, v_new, q = steps_in[t]
-        pg, npg, out = outs[r]
-        idx.decode_step(k_new, v_new, q, page_ids=pg, n_pages=npg, out=out)
+    def step():
+        for _ in range(layers_per_step):
+            t = call[0]
+            call[0] += 1
+            r = t % R
+            k_new, v_new, q = steps_in[t % len(steps_in)]
+            pg, npg, out = outs[r]
+            layers[r].decode_step(k_new, v_new, q, page_ids=pg, n_pages=npg, out=out)
 
-    for t in range(args.warmup):
-        step(t)
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
     log("[bench] timing")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for t in range(args.warmup, args.warmup + args.steps):
-        step(t)
+    for _ in range(args.steps):
+        step()
     e1.record()
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
-    # per-kernel durations, HIP events on the launch stream, a second pass
-    for idx, _ in layers:
+    # per-kernel durations: HIP events the library records on the launch stream
+    for idx in layers:
         idx.timing(True)
-    for t in range(args.warmup + args.steps, total_steps):
-        step(t)
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     per_kernel = {}
-    for idx, _ in layers:
+    for idx in layers:
         for name, (ms, cnt) in idx.timing_read().items():
             a, b = per_kernel.get(name, (0.0, 0))
             per_kernel[name] = (a + ms, b + cnt)
         idx.timing(False)
     avg_us = {k: 1e3 * ms / c for k, (ms, c) in per_kernel.items() if c}
     log(f"[bench] per-kernel average us: { {k: round(v, 2) for k, v in avg_us.items()} }")
-    dominant = max(avg_us, key=avg_us.get)
+
+    cpu, n_cand = None, float(w.L * w.k)
+    if not args.no_cpu:
+        log("[bench] oracle cpu baseline")
+        K, V, q, U = keep
+        k_new, v_new, _ = W.step_inputs(w, layer=0, step=10 ** 6, device=dev)
+        us, threads, n_cand = cpu_baseline(w, K, V, q, U, k_new, v_new, args.cpu_reps)
+        cpu = {"value": round(us * layers_per_step, 1), "unit": "us", "cores": threads,
+               "kind": "oracle",
+               "sample": f"one decode step (insert + literal P-DCI query + rerank + page "
+                         f"selection + fp64 attention) of all {w.streams} KV heads of one "
+                         f"{w.n}-token layer, best of {args.cpu_reps}"
+                         + (f", times {layers_per_step} layers" if layers_per_step > 1 else "")
+                         + "; oracle build untimed"}
+
     ntok = w.n + per_layer // 2
-    n_cand = w.L * w.k * 0.9   # the union of the composites' k0 candidates, about L*k0
     attended = float(w.k)
-    alg = algorithmic_bytes(w, dominant, ntok, n_cand, attended)
-    achieved = alg / (avg_us[dominant] * 1e-6) / 1e9
+    kernels = {}
+    for k, us in avg_us.items():
+        alg = algorithmic_bytes(w, k, ntok, n_cand, attended)
+        kernels[k] = {"avg_us": round(us, 3), "alg_bytes": int(alg),
+                      "gbs": round(alg / (us * 1e-6) / 1e9, 1),
+                      "frac": round(alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    dominant = max(avg_us, key=avg_us.get)
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tfile):
         with open(tfile) as fh:
             tr = json.load(fh)
-        if tr.get("source_hash") == kernel_source_hash() and dominant in tr.get("kernels", {}):
+        if (tr.get("source_hash") == kernel_source_hash() and tr.get("workload") == args.workload
+                and dominant in tr.get("kernels", {})):
             traffic = tr["kernels"][dominant]
-    roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": traffic, "avg_us": round(avg_us[dominant], 3),
-                "alg_bytes": int(alg)}
-    step_alg = sum(algorithmic_bytes(w, k, ntok, n_cand, attended) for k in STEP_KERNELS)
-
-    cpu = None
-    if not args.no_cpu:
-        log("[bench] oracle cpu baseline")
-        K, V, q, U = keep
-        k_new, v_new, _ = W.step_inputs(w, layer=0, step=10 ** 6, device=dev)
-        us, threads = cpu_baseline(w, K, V, q, U, k_new, v_new, args.cpu_reps)
-        cpu = {"value": round(us, 1), "unit": "us", "cores": threads, "kind": "oracle",
-               "sample": f"one decode step (insert + literal P-DCI query + rerank + page "
-                         f"selection + fp64 attention) of all {w.streams} KV heads of one "
-                         f"{w.n}-token layer, best of {args.cpu_reps}; oracle build untimed"}
+    dk = kernels[dominant]
+    roofline = {"bound": "hbm", "kernel": dominant, "achieved": dk["gbs"], "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": dk["frac"], "traffic": traffic, "avg_us": dk["avg_us"],
+                "alg_bytes": dk["alg_bytes"]}
+    step_alg = sum(algorithmic_bytes(w, k, ntok, n_cand, attended)
+                   for k in ("prep", "qscan", "qcollect", "qfinal")) * layers_per_step
 
     res = {
         "metric": "decode-step us (P-DCI query + sparse paged attn) @36k ctx; achieved HBM GB/s",
@@ -235,13 +276,15 @@ def main():
         "vs_baseline": None,
         "dtype": "int32 codes + fp64 rerank + fp32 attention over bf16 KV",
         "data": "synthetic (seeded Gaussian-mixture keys, N(0,1) values)",
-        "config": {"workload": WORKLOAD, "kv_heads": w.streams, "query_heads": w.streams * w.g,
-                   "context": w.n, "head_dim": w.d, "page_size": w.p, "budget_k": w.k,
-                   "m": w.m, "L": w.L, "layers_rotated": R,
+        "config": {"workload": args.workload, "kv_heads": w.streams,
+                   "query_heads": w.streams * w.g, "context": w.n, "head_dim": w.d,
+                   "page_size": w.p, "budget_k": w.k, "m": w.m, "L": w.L,
+                   "layers_per_step": layers_per_step, "layers_rotated": R,
                    "step": "ice_decode_step = insert + query_pages + sparse_attn"},
         "build_ms": round(sorted(build_ms)[len(build_ms) // 2], 3),
         "step_alg_gbs": round(step_alg / (ms_per_step * 1e-3) / 1e9, 1),
-        "kernel_avg_us": {k: round(v, 3) for k, v in avg_us.items()},
+        "union_size": round(n_cand, 1),
+        "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -529,9 +529,9 @@ struct FinalShared {
       unsigned long long brk[kBndLds];
       int32_t bpg[kBndLds];
     };
-    struct {  // bucket sort (sort phase)
-      int32_t tmp[kMaxCand];
-      int32_t inv[kMaxCand];  // rank -> position in the rerank list
+    struct {  // bucket sort (sort phase): keys and list positions in bucket order
+      unsigned long long tk[kMaxCand];
+      int32_t tx[kMaxCand];
     };
   };
   union {
@@ -539,7 +539,6 @@ struct FinalShared {
     struct {
       uint32_t bcnt[kBuckets];
       uint32_t bstart[kBuckets];
-      uint32_t bfill[kBuckets];
       uint32_t seen[2048];  // selected pages (page walk)
     };
   };
@@ -712,12 +711,30 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
   // D. bucket sort by (rank key, token).  Bucket = floor((s_max - score) *
   // (kBuckets-1) / (s_max - s_min)) never decreases along ascending keys, so
   // an element's rank is its bucket's start plus the number of smaller
-  // elements inside its bucket.
+  // elements inside its bucket.  The count's atomic hands every element its
+  // slot inside the bucket; the sorted list ends up rank-ordered (token,
+  // page) over the dead key array.
+  int32_t* const rsid = reinterpret_cast<int32_t *>(&sh.skey[0]);
+  int32_t* const rspg = rsid + kMaxCand;
   {
+    constexpr int kPer = kMaxCand / kFinalThreads;
+    unsigned long long kx[kPer];
+    int32_t ix[kPer], px[kPer];
+    uint32_t bkt[kPer], within[kPer], rnk[kPer];
     unsigned long long lo = ~0ull, hi = 0;
-    for (uint32_t x = tid; x < nu; x += kFinalThreads) {
-      lo = min(lo, sh.skey[x]);
-      hi = max(hi, sh.skey[x]);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t x = tid + kFinalThreads * j;
+      kx[j] = ~0ull;
+      ix[j] = 0;
+      px[j] = 0;
+      if (x < nu) {  // whole waves past nu skip
+        kx[j] = sh.skey[x];
+        ix[j] = sh.sid[x];
+        px[j] = sh.spg[x];
+        lo = min(lo, kx[j]);
+        hi = max(hi, kx[j]);
+      }
     }
     for (int off = 32; off >= 1; off >>= 1) {
       lo = min(lo, (unsigned long long)__shfl_xor((long long)lo, off));
@@ -727,10 +744,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
       sh.wlo[w] = lo;
       sh.whi[w] = hi;
     }
-    for (int x = tid; x < kBuckets; x += kFinalThreads) {
-      sh.bcnt[x] = 0;
-      sh.bfill[x] = 0;
-    }
+    for (int x = tid; x < kBuckets; x += kFinalThreads) sh.bcnt[x] = 0;
     lds_barrier();
     lo = ~0ull;
     hi = 0;
@@ -742,11 +756,16 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
     const double smax = nu ? rank_key_score(lo) : 0.0;
     const double smin = nu ? rank_key_score(hi) : 0.0;
     const double scale = smax > smin ? (double)(kBuckets - 1) / (smax - smin) : 0.0;
-    auto bucket_of = [smax, scale](unsigned long long key) -> uint32_t {
-      const double t = (smax - rank_key_score(key)) * scale;
-      return (uint32_t)min((double)(kBuckets - 1), t);
-    };
-    for (uint32_t x = tid; x < nu; x += kFinalThreads) atomicAdd(&sh.bcnt[bucket_of(sh.skey[x])], 1u);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      bkt[j] = 0;
+      within[j] = 0;
+      if (tid + kFinalThreads * j < nu) {
+        const double t = (smax - rank_key_score(kx[j])) * scale;
+        bkt[j] = (uint32_t)min((double)(kBuckets - 1), t);
+        within[j] = atomicAdd(&sh.bcnt[bkt[j]], 1u);
+      }
+    }
     lds_barrier();
     {  // exclusive scan of the bucket counts, two per thread
       const uint32_t c0 = sh.bcnt[2 * tid], c1 = sh.bcnt[2 * tid + 1];
@@ -760,22 +779,41 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
       sh.bstart[2 * tid + 1] = excl + c0;
     }
     lds_barrier();
-    for (uint32_t x = tid; x < nu; x += kFinalThreads) {
-      const uint32_t bk = bucket_of(sh.skey[x]);
-      sh.tmp[sh.bstart[bk] + atomicAdd(&sh.bfill[bk], 1u)] = (int32_t)x;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t x = tid + kFinalThreads * j;
+      if (x < nu) {
+        const uint32_t pos = sh.bstart[bkt[j]] + within[j];
+        sh.tk[pos] = kx[j];
+        sh.tx[pos] = (int32_t)x;
+      }
     }
     lds_barrier();
-    for (uint32_t x = tid; x < nu; x += kFinalThreads) {
-      const unsigned long long kx = sh.skey[x];
-      const int32_t ix = sh.sid[x];
-      const uint32_t bk = bucket_of(kx);
-      const uint32_t b0 = sh.bstart[bk], b1 = b0 + sh.bcnt[bk];
-      uint32_t rk = b0;
-      for (uint32_t y = b0; y < b1; ++y) {
-        const int32_t j = sh.tmp[y];
-        rk += key_less(sh.skey[j], sh.sid[j], kx, ix);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t x = tid + kFinalThreads * j;
+      rnk[j] = 0;
+      if (x < nu) {
+        const uint32_t b0 = sh.bstart[bkt[j]], b1 = b0 + sh.bcnt[bkt[j]];
+        uint32_t r = b0, eq = 0;
+        for (uint32_t y = b0; y < b1; ++y) {
+          const unsigned long long ky = sh.tk[y];
+          r += ky < kx[j];
+          eq += ky == kx[j];
+        }
+        if (eq > 1)  // equal keys (rare): order them by token
+          for (uint32_t y = b0; y < b1; ++y)
+            r += sh.tk[y] == kx[j] && sh.sid[sh.tx[y]] < ix[j];
+        rnk[j] = r;
       }
-      sh.inv[rk] = (int32_t)x;
+    }
+    lds_barrier();  // every read of the key arrays is done
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (tid + kFinalThreads * j < nu) {
+        rsid[rnk[j]] = ix[j];
+        rspg[rnk[j]] = px[j];
+      }
     }
     for (int x = tid; x < 2048; x += kFinalThreads) sh.seen[x] = 0;
     lds_barrier();
@@ -784,7 +822,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
   // E. top-k tokens, then pages in rank order
   if (topk_ids)
     for (int x = tid; x < dv.k; x += kFinalThreads)
-      topk_ids[(int64_t)s * dv.k + x] = (uint32_t)x < nu ? sh.sid[sh.inv[x]] : -1;
+      topk_ids[(int64_t)s * dv.k + x] = (uint32_t)x < nu ? rsid[x] : -1;
   if (w == 0) {
     int pbits = 1;
     while ((1ll << pbits) < dv.pcap) ++pbits;
@@ -793,7 +831,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
     for (uint32_t x0 = 0; x0 < nu && nsel < dv.P; x0 += 64) {
       const uint32_t x = x0 + lane;
       const bool valid = x < nu;
-      const int32_t pg = valid ? sh.spg[sh.inv[x]] : 0;
+      const int32_t pg = valid ? rspg[x] : 0;
       const bool fresh = valid && ((sh.seen[pg >> 5] >> (pg & 31)) & 1u) == 0u;
       const unsigned long long act = __ballot(fresh);
       const unsigned long long mt = match_bits((uint32_t)pg, pbits, act);
