@@ -48,7 +48,8 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w, kernel: str, ntok: float, n_cand: float, attended: float) -> float:
+def algorithmic_bytes(w, kernel: str, ntok: float, n_cand: float, attended: float,
+                      fused: bool = True) -> float:
     """Bytes the decode path has to move per launch of `kernel` for one layer
     (S streams): the per-unit figures times the units one launch processes.
 
@@ -57,10 +58,10 @@ def algorithmic_bytes(w, kernel: str, ntok: float, n_cand: float, attended: floa
               directions ((d+1)*mL*4), the query codes out (4*mL)
     qscan     every token's m*L projection codes: 4*mL per token
     qcollect  the key row of every reranked candidate: d*elem per candidate
-    qfinal    the rerank list (16 B per candidate), then the attention: K and V
-              rows of every attended token (2*d*elem each), the g heads and
-              their fp32 outputs
-    attn      (only when the finaliser does not run the attention) as above
+    qfinal    the rerank list (16 B per candidate), then (fused) the attention:
+              K and V rows of every attended token (2*d*elem each), the g
+              heads and their fp32 outputs
+    attn      (when the finaliser does not run the attention) as above
     """
     S, d, mL, g = w.streams, w.d, w.mL, w.g
     elem = 2 if w.dtype == "bf16" else 4
@@ -69,7 +70,7 @@ def algorithmic_bytes(w, kernel: str, ntok: float, n_cand: float, attended: floa
         "prep": 4.0 * d * elem + 12.0 * mL + g * d * elem + (d + 1) * mL * 4.0 + 4.0 * mL,
         "qscan": ntok * mL * 4.0,
         "qcollect": n_cand * d * elem,
-        "qfinal": n_cand * 16.0 + att,
+        "qfinal": n_cand * 16.0 + (att if fused else 0.0),
         "attn": att,
     }
     return S * per_stream.get(kernel, 0.0)
@@ -242,8 +243,9 @@ def main():
     ntok = w.n + per_layer // 2
     attended = float(w.k)
     kernels = {}
+    fused = "attn" not in avg_us
     for k, us in avg_us.items():
-        alg = algorithmic_bytes(w, k, ntok, n_cand, attended)
+        alg = algorithmic_bytes(w, k, ntok, n_cand, attended, fused)
         kernels[k] = {"avg_us": round(us, 3), "alg_bytes": int(alg),
                       "gbs": round(alg / (us * 1e-6) / 1e9, 1),
                       "frac": round(alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
@@ -260,8 +262,9 @@ def main():
     roofline = {"bound": "hbm", "kernel": dominant, "achieved": dk["gbs"], "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": dk["frac"], "traffic": traffic, "avg_us": dk["avg_us"],
                 "alg_bytes": dk["alg_bytes"]}
-    step_alg = sum(algorithmic_bytes(w, k, ntok, n_cand, attended)
-                   for k in ("prep", "qscan", "qcollect", "qfinal")) * layers_per_step
+    step_alg = sum(algorithmic_bytes(w, k, ntok, n_cand, attended, fused)
+                   for k in ("prep", "qscan", "qcollect", "qfinal", "attn")
+                   if fused is False or k != "attn") * layers_per_step
 
     res = {
         "metric": "decode-step us (P-DCI query + sparse paged attn) @36k ctx; achieved HBM GB/s",

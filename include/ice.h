@@ -67,7 +67,8 @@ typedef struct {
   int32_t m;          /* simple indices (lists) per composite index, >= 1      */
   int32_t L;          /* composite indices, >= 1; m * L <= 128                 */
   int32_t gqa_group;  /* g: query heads per KV head, 1..16                      */
-  int32_t k0;         /* candidates retrieved per composite; 0 -> budget_k      */
+  int32_t k0;         /* candidates retrieved per composite; 0 -> budget_k;
+                         L * k0 <= 12288 (larger: UNSUPPORTED)                 */
   int64_t k1;         /* visit budget per composite; 0 -> unbounded (the only
                          value this build implements; others: UNSUPPORTED)      */
   int32_t tree_depth; /* D, 1..13 and <= m*L; 0 -> derived from the build size:

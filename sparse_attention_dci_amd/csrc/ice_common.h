@@ -19,8 +19,10 @@ constexpr int kMaxGroup = 16;
 constexpr int kHistBits = 11;
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kHistShift = 31 - kHistBits;
-// Largest reranked candidate set per stream that the finaliser sorts in LDS.
+// Largest candidate union per stream (L*k0) that the finaliser keeps in LDS;
+// up to kMaxCandBig the union stays in global memory and is ranked in windows.
 constexpr int kMaxCand = 4096;
+constexpr int kMaxCandBig = 12288;
 // Directions are stored in fp64, 16 per chunk, [chunk][d+1][16].
 constexpr int kDirChunk = 16;
 // Projection codes are stored in tiles of 64 tokens, [S][tile][mL][64]: a

@@ -495,15 +495,17 @@ __device__ unsigned long long block_select(const unsigned long long *keys, uint3
   return prefix;
 }
 
-// Inserts id into the LDS hash set; true when it was not there yet.
+// Inserts id into an LDS hash set of 2^BITS slots (linear probing); true when
+// it was not there yet.
+template <int BITS = 13>
 __device__ __forceinline__ bool hash_insert(uint32_t *tab, int32_t id) {
   const uint32_t key = (uint32_t)id + 1u;
-  uint32_t h = (key * 2654435761u) >> (32 - 13);
+  uint32_t h = (key * 2654435761u) >> (32 - BITS);
   for (;;) {
     const uint32_t old = atomicCAS(&tab[h], 0u, key);
     if (old == 0u) return true;
     if (old == key) return false;
-    h = (h + 1u) & (kHashSlots - 1u);
+    h = (h + 1u) & ((1u << BITS) - 1u);
   }
 }
 
@@ -890,6 +892,374 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
   bookkeeping();
 }
 
+// ---------------------------------------------------------------- final, large unions
+
+// For L*k0 above kMaxCand (the 262k-token configuration: 6 x 2048): the union
+// of the candidates stays in global memory (the rerank list, followed by the
+// boundary picks that are new to it), duplicates are caught by an LDS hash of
+// 2^14 slots, and the ranking proceeds in windows of consecutive score
+// buckets holding at most kWin elements, each sorted in LDS, until the page
+// walk has P pages and the top-k (when asked for) is written.  The bucket
+// mapping is the small path's.  A bucket of more than kWin elements (near
+// equal scores) is ranked by counting over the union in global memory.  The
+// attention runs in its own kernel.
+constexpr int kBigHashBits = 14;
+constexpr int kWin = 4096;
+
+struct BigShared {
+  union {
+    uint32_t hash[1 << kBigHashBits];  // union membership (selection phase)
+    struct {                           // one window of the ranking
+      unsigned long long wk[kWin];
+      int32_t wx[kWin];
+      int32_t rsid[kWin];
+      int32_t rspg[kWin];
+    };
+  };
+  union {
+    struct {  // boundary entries (selection phase)
+      unsigned long long bk[kBndLds];
+      unsigned long long brk[kBndLds];
+      int32_t bpg[kBndLds];
+    };
+    struct {  // bucket counts (ranking phase)
+      uint32_t bcnt[kBuckets];
+      uint32_t bstart[kBuckets + 1];
+      uint32_t bfill[kBuckets];
+    };
+  };
+  uint32_t seen[2048];
+  uint32_t cnt[256];
+  uint32_t cc[32], nb[32], need[32], boff[33], extra[32], b2[32], need2[32];
+  uint32_t tie[kMaxTies];
+  uint32_t ntie, nux, rr, nsel, win_end;
+  unsigned long long res;
+  unsigned long long wlo[16], whi[16];
+  uint32_t wsum[16];
+};
+
+template <int DT>
+__global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n, int32_t *page_ids,
+                                                              int32_t *n_pages, int32_t *topk_ids) {
+  __shared__ BigShared sh;
+  const int s = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int L = dv.L, k0 = dv.k0;
+  const uint32_t k0e = (uint32_t)min((int64_t)k0, n);
+  const int64_t o0 = (int64_t)s * L * k0;  // the stream's union arrays (rerank list first)
+  unsigned long long *ukey = dv.rr_key + o0;
+  int32_t *uid = dv.rr_id + o0, *upg = dv.rr_pg + o0;
+
+  // A. counts and the two threshold levels of every composite
+  const uint32_t nrr_ld = dv.rr_count[s];
+  for (int x = tid; x < (1 << kBigHashBits); x += kFinalThreads) sh.hash[x] = 0;
+  if (tid < L) {
+    sh.cc[tid] = dv.cand_count[s * L + tid];
+    sh.nb[tid] = dv.bnd_count[s * L + tid];
+    sh.extra[tid] = 0;
+    sh.need[tid] = 0;
+    sh.b2[tid] = 0;
+    sh.need2[tid] = 0;
+  }
+  if (k0e > 0) {
+    for (int l = w; l < L; l += kFinalThreads / 64) {
+      uint32_t b, bl, b2, bl2, h1[kBinsPerLane], h2[kBinsPerLane];
+      wave_hist_load(dv.hist + ((int64_t)s * L + l) * kHistBins, h1);
+      wave_hist_load(dv.hist2 + ((int64_t)s * L + l) * kHistBins, h2);
+      wave_find_bin_regs(h1, k0e, b, bl);
+      const uint32_t need = k0e - bl;
+      wave_find_bin_regs(h2, need, b2, bl2);
+      if (lane == 0) {
+        sh.need[l] = need;
+        sh.b2[l] = b2;
+        sh.need2[l] = need - bl2;
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t nrr = k0e > 0 ? nrr_ld : 0u;
+  if (tid == 0) {
+    uint32_t o = 0;
+    for (int l = 0; l < L; ++l) {
+      sh.boff[l] = o;
+      o += (k0e > 0) ? sh.nb[l] : 0u;
+    }
+    sh.boff[L] = o;
+    sh.ntie = 0;
+    sh.nux = 0;
+    sh.nsel = 0;
+  }
+  __syncthreads();
+  const uint32_t nbt = sh.boff[L];
+  const bool bnd_lds = nbt <= (uint32_t)kBndLds;
+
+  // B. the rerank list's tokens into the hash; the boundary entries into LDS
+  for (uint32_t x = tid; x < nrr; x += kFinalThreads) hash_insert<kBigHashBits>(sh.hash, uid[x]);
+  if (bnd_lds) {
+    for (uint32_t x = tid; x < nbt; x += kFinalThreads) {
+      int l = 0;
+      while (x >= sh.boff[l + 1]) ++l;
+      const int64_t o = ((int64_t)s * L + l) * dv.ncap + (x - sh.boff[l]);
+      sh.bk[x] = dv.bnd[o];
+      sh.brk[x] = dv.bnd_rk[o];
+      sh.bpg[x] = dv.bnd_pg[o];
+    }
+  }
+  __syncthreads();
+
+  // C. boundary picks, as in the small path; new tokens are appended to the
+  // union after the rerank list
+  auto add_pick = [&](int l, unsigned long long key, unsigned long long rk, int32_t pg) {
+    const int32_t id = (int32_t)(key & 0xffffffffull);
+    dv.cand[((int64_t)s * L + l) * k0 + sh.cc[l] + atomicAdd(&sh.extra[l], 1u)] = id;
+    if (hash_insert<kBigHashBits>(sh.hash, id)) {
+      const uint32_t pos = nrr + atomicAdd(&sh.nux, 1u);
+      ukey[pos] = rk;
+      uid[pos] = id;
+      upg[pos] = pg;
+    }
+  };
+  auto sub_of = [](unsigned long long key) -> uint32_t {
+    return (uint32_t)(key >> (32 + kSubShift)) & (kHistBins - 1);
+  };
+  if (nbt > 0) {
+    if (bnd_lds) {
+      for (uint32_t x = tid; x < nbt; x += kFinalThreads) {
+        int l = 0;
+        while (x >= sh.boff[l + 1]) ++l;
+        const unsigned long long key = sh.bk[x];
+        const uint32_t sb = sub_of(key);
+        if (sb < sh.b2[l]) add_pick(l, key, sh.brk[x], sh.bpg[x]);
+        if (sb == sh.b2[l]) {
+          const uint32_t t = atomicAdd(&sh.ntie, 1u);
+          if (t < kMaxTies) sh.tie[t] = x;
+        }
+      }
+      __syncthreads();
+      const uint32_t nt = sh.ntie;
+      if (nt <= (uint32_t)kMaxTies) {
+        for (uint32_t t = tid; t < nt; t += kFinalThreads) {
+          const uint32_t x = sh.tie[t];
+          int l = 0;
+          while (x >= sh.boff[l + 1]) ++l;
+          const unsigned long long key = sh.bk[x];
+          uint32_t rank = 0;
+          for (uint32_t u = 0; u < nt; ++u) {
+            const uint32_t y = sh.tie[u];
+            rank += (y >= sh.boff[l]) & (y < sh.boff[l + 1]) & (sh.bk[y] < key);
+          }
+          if (rank < sh.need2[l]) add_pick(l, key, sh.brk[x], sh.bpg[x]);
+        }
+      } else {
+        for (uint32_t x = tid; x < nbt; x += kFinalThreads) {
+          int l = 0;
+          while (x >= sh.boff[l + 1]) ++l;
+          const unsigned long long key = sh.bk[x];
+          if (sub_of(key) != sh.b2[l]) continue;
+          uint32_t rank = 0;
+          for (uint32_t y = sh.boff[l]; y < sh.boff[l + 1]; ++y)
+            rank += (sub_of(sh.bk[y]) == sh.b2[l]) & (sh.bk[y] < key);
+          if (rank < sh.need2[l]) add_pick(l, key, sh.brk[x], sh.bpg[x]);
+        }
+      }
+    } else {
+      for (int l = 0; l < L; ++l) {
+        const int64_t ob = ((int64_t)s * L + l) * dv.ncap;
+        const unsigned long long *bk = dv.bnd + ob;
+        const uint32_t nbl = sh.nb[l], nd = sh.need[l];
+        const unsigned long long thr =
+            nd >= nbl ? ~0ull : block_select(bk, nbl, nd, sh.cnt, &sh.res, &sh.rr);
+        for (uint32_t x = tid; x < nbl; x += kFinalThreads) {
+          const unsigned long long key = bk[x];
+          if (key <= thr) add_pick(l, key, dv.bnd_rk[ob + x], dv.bnd_pg[ob + x]);
+        }
+        __syncthreads();
+      }
+    }
+  }
+  __syncthreads();  // the union is complete (and its global writes visible to the block)
+  const uint32_t nu = nrr + sh.nux;
+
+  // D. ranking in windows of score buckets
+  unsigned long long lo = ~0ull, hi = 0;
+  for (uint32_t x = tid; x < nu; x += kFinalThreads) {
+    const unsigned long long kx = ukey[x];
+    lo = min(lo, kx);
+    hi = max(hi, kx);
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    lo = min(lo, (unsigned long long)__shfl_xor((long long)lo, off));
+    hi = max(hi, (unsigned long long)__shfl_xor((long long)hi, off));
+  }
+  if (lane == 0) {
+    sh.wlo[w] = lo;
+    sh.whi[w] = hi;
+  }
+  for (int x = tid; x < kBuckets; x += kFinalThreads) {
+    sh.bcnt[x] = 0;
+    sh.bfill[x] = 0;
+  }
+  for (int x = tid; x < 2048; x += kFinalThreads) sh.seen[x] = 0;
+  __syncthreads();
+  lo = ~0ull;
+  hi = 0;
+#pragma unroll
+  for (int k = 0; k < kFinalThreads / 64; ++k) {
+    lo = min(lo, sh.wlo[k]);
+    hi = max(hi, sh.whi[k]);
+  }
+  const double smax = nu ? rank_key_score(lo) : 0.0;
+  const double smin = nu ? rank_key_score(hi) : 0.0;
+  const double scale = smax > smin ? (double)(kBuckets - 1) / (smax - smin) : 0.0;
+  auto bucket_of = [smax, scale](unsigned long long key) -> uint32_t {
+    const double t = (smax - rank_key_score(key)) * scale;
+    return (uint32_t)min((double)(kBuckets - 1), t);
+  };
+  for (uint32_t x = tid; x < nu; x += kFinalThreads) atomicAdd(&sh.bcnt[bucket_of(ukey[x])], 1u);
+  __syncthreads();
+  {  // exclusive scan of the bucket counts, two per thread
+    const uint32_t c0 = sh.bcnt[2 * tid], c1 = sh.bcnt[2 * tid + 1];
+    const uint32_t incl = wave_incl_scan(c0 + c1);
+    if (lane == 63) sh.wsum[w] = incl;
+    __syncthreads();
+    uint32_t pre = 0;
+    for (int k = 0; k < w; ++k) pre += sh.wsum[k];
+    const uint32_t excl = pre + incl - (c0 + c1);
+    sh.bstart[2 * tid] = excl;
+    sh.bstart[2 * tid + 1] = excl + c0;
+    if (tid == 0) sh.bstart[kBuckets] = nu;
+  }
+  __syncthreads();
+
+  const int P = dv.P;
+  const uint32_t want_top = topk_ids ? min((uint32_t)dv.k, nu) : 0u;
+  int pbits = 1;
+  while ((1ll << pbits) < dv.pcap) ++pbits;
+  uint32_t B0 = 0, rank_base = 0;
+  unsigned long long *grank = dv.bnd + (int64_t)s * L * dv.ncap;  // dead boundary keys as scratch
+  while (B0 < (uint32_t)kBuckets && rank_base < nu &&
+         ((int)sh.nsel < P || rank_base < want_top)) {
+    // the window: buckets [B0, B1), at most kWin elements (one bucket at least)
+    if (tid == 0) {
+      uint32_t lo_b = B0 + 1, hi_b = kBuckets;  // largest B1 with count <= kWin
+      while (lo_b < hi_b) {
+        const uint32_t mid = (lo_b + hi_b + 1) / 2;
+        if (sh.bstart[mid] - sh.bstart[B0] <= (uint32_t)kWin)
+          lo_b = mid;
+        else
+          hi_b = mid - 1;
+      }
+      sh.win_end = lo_b;
+    }
+    __syncthreads();
+    const uint32_t B1 = sh.win_end;
+    const uint32_t base = sh.bstart[B0], cntw = sh.bstart[B1] - base;
+    if (cntw <= (uint32_t)kWin) {
+      for (uint32_t x = tid; x < nu; x += kFinalThreads) {
+        const unsigned long long kx = ukey[x];
+        const uint32_t b = bucket_of(kx);
+        if (b >= B0 && b < B1) {
+          const uint32_t pos = sh.bstart[b] - base + atomicAdd(&sh.bfill[b], 1u);
+          sh.wk[pos] = kx;
+          sh.wx[pos] = (int32_t)x;
+        }
+      }
+      __syncthreads();
+      for (uint32_t r = tid; r < cntw; r += kFinalThreads) {
+        const unsigned long long kx = sh.wk[r];
+        const int32_t x = sh.wx[r];
+        const int32_t ix = uid[x];
+        const uint32_t b = bucket_of(kx);
+        const uint32_t b0 = sh.bstart[b] - base, b1 = b0 + sh.bcnt[b];
+        uint32_t rk = b0, eq = 0;
+        for (uint32_t y = b0; y < b1; ++y) {
+          const unsigned long long ky = sh.wk[y];
+          rk += ky < kx;
+          eq += ky == kx;
+        }
+        if (eq > 1)
+          for (uint32_t y = b0; y < b1; ++y) rk += sh.wk[y] == kx && uid[sh.wx[y]] < ix;
+        sh.rsid[rk] = ix;
+        sh.rspg[rk] = upg[x];
+      }
+    } else {
+      // one bucket above the window: rank its elements by counting over the
+      // union (slow; only near-equal scores get here), in chunks of kWin ranks
+      for (uint32_t x = tid; x < nu; x += kFinalThreads) {
+        const unsigned long long kx = ukey[x];
+        if (bucket_of(kx) != B0) continue;
+        const int32_t ix = uid[x];
+        uint32_t rk = 0;
+        for (uint32_t y = 0; y < nu; ++y) {
+          const unsigned long long ky = ukey[y];
+          rk += bucket_of(ky) == B0 && (ky < kx || (ky == kx && uid[y] < ix));
+        }
+        grank[x] = rk;
+      }
+      __syncthreads();
+    }
+    // walk the window's ranks (the big-bucket case in chunks of kWin ranks)
+    for (uint32_t c0 = 0; c0 < cntw; c0 += kWin) {
+      const uint32_t cw = min((uint32_t)kWin, cntw - c0);
+      if (cntw > (uint32_t)kWin) {
+        for (uint32_t x = tid; x < nu; x += kFinalThreads) {
+          if (bucket_of(ukey[x]) != B0) continue;
+          const uint32_t rk = (uint32_t)grank[x];
+          if (rk >= c0 && rk < c0 + cw) {
+            sh.rsid[rk - c0] = uid[x];
+            sh.rspg[rk - c0] = upg[x];
+          }
+        }
+      }
+      __syncthreads();
+      const uint32_t rb = rank_base + c0;
+      if (topk_ids)
+        for (uint32_t r = tid; r < cw; r += kFinalThreads)
+          if (rb + r < want_top) topk_ids[(int64_t)s * dv.k + rb + r] = sh.rsid[r];
+      if (w == 0 && (int)sh.nsel < P) {
+        int nsel = sh.nsel;
+        const unsigned long long lt = lanemask_lt();
+        for (uint32_t x0 = 0; x0 < cw && nsel < P; x0 += 64) {
+          const uint32_t x = x0 + lane;
+          const bool valid = x < cw;
+          const int32_t pg = valid ? sh.rspg[x] : 0;
+          const bool fresh = valid && ((sh.seen[pg >> 5] >> (pg & 31)) & 1u) == 0u;
+          const unsigned long long act = __ballot(fresh);
+          const unsigned long long mt = match_bits((uint32_t)pg, pbits, act);
+          const bool firstocc = fresh && (mt & lt) == 0ull;
+          const unsigned long long fm = __ballot(firstocc);
+          const int pos = nsel + popc64(fm & lt);
+          if (firstocc && pos < P) {
+            page_ids[(int64_t)s * P + pos] = pg;
+            atomicOr(&sh.seen[pg >> 5], 1u << (pg & 31));
+          }
+          nsel = min(P, nsel + popc64(fm));
+          __builtin_amdgcn_wave_barrier();
+        }
+        if (lane == 0) sh.nsel = nsel;
+      }
+      __syncthreads();
+    }
+    rank_base += cntw;
+    B0 = B1;
+  }
+
+  // E. padding and counts
+  const int nsel = sh.nsel;
+  for (int x = nsel + tid; x < P; x += kFinalThreads) page_ids[(int64_t)s * P + x] = -1;
+  if (tid == 0) n_pages[s] = nsel;
+  if (topk_ids)
+    for (uint32_t x = want_top + tid; x < (uint32_t)dv.k; x += kFinalThreads)
+      topk_ids[(int64_t)s * dv.k + x] = -1;
+  if (tid < L && k0e > 0) dv.cand_count[s * L + tid] = sh.cc[tid] + sh.extra[tid];
+  uint32_t *hist = dv.hist + (int64_t)s * L * kHistBins;
+  uint32_t *hist2 = dv.hist2 + (int64_t)s * L * kHistBins;
+  for (int x = tid; x < L * kHistBins; x += kFinalThreads) {
+    hist[x] = 0;
+    hist2[x] = 0;
+  }
+}
+
 // ---------------------------------------------------------------- launcher
 
 template <bool LH, int R>
@@ -926,7 +1296,10 @@ static void query_tail(const Dev &dv, int64_t n, int32_t *page_ids, int32_t *n_p
     hipLaunchKernelGGL(k_qcollect<DT>, dim3(grid), dim3(kScanThreads), 0, st, dv, n);
     timer_mark(tm, KID_QCOLLECT, st);
   }
-  if (dv.d == 128)
+  if (dv.L * dv.k0 > kMaxCand)
+    hipLaunchKernelGGL(k_qfinal_big<DT>, dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n, page_ids,
+                       n_pages, topk_ids);
+  else if (dv.d == 128)
     hipLaunchKernelGGL((k_qfinal<DT, 128>), dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n,
                        page_ids, n_pages, topk_ids, q, out);
   else
@@ -956,8 +1329,9 @@ hipError_t launch_decode(const Dev &dv, int64_t n, const void *k_new, const void
   hipError_t e = launch_prep(dv, n, k_new, v_new, q, 3, st);
   if (e != hipSuccess) return e;
   timer_mark(tm, KID_PREP, st);
-  // pages up to kFusedMaxPages: the finaliser runs the attention itself
-  const bool fused = dv.P <= kFusedMaxPages;
+  // pages up to kFusedMaxPages and unions that fit LDS: the finaliser runs the
+  // attention itself
+  const bool fused = dv.P <= kFusedMaxPages && dv.L * dv.k0 <= kMaxCand;
   if (dv.dtype == 0)
     query_tail<0>(dv, n + 1, page_ids, n_pages, topk_ids, q, fused ? out : nullptr, st, tm);
   else

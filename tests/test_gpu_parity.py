@@ -342,3 +342,48 @@ def test_needle_131k_full_layer_sampled(B):
         q_s = _np(q[s * w.g:(s + 1) * w.g])
         r = st.query(q_s, literal=False)
         _check_query(idx, st, s, r, page_ids, n_pages, topk, out[s * w.g:(s + 1) * w.g], q_s)
+
+
+@pytest.mark.parametrize("S,n,g,p,k,m,L,k0", [
+    (2, 20011, 2, 16, 1024, 6, 6, 0),   # union up to 6,144 tokens per stream
+    (1, 30000, 1, 16, 4800, 4, 2, 0),   # top-k of 4,800 ranks: several rank windows, 300 pages
+    (2, 9000, 4, 32, 256, 4, 4, 1500),  # k0 above the budget: few pages, large union
+])
+def test_large_union(B, S, n, g, p, k, m, L, k0):
+    """L * k0 above 4,096: the union stays in global memory and is ranked in windows."""
+    run_case(B, S=S, n=n, g=g, p=p, k=k, m=m, L=L, k0=k0, seed=40 + L, literal=False)
+
+
+def test_identical_keys_large_union(B):
+    """Every score equal and a union of 4,608 tokens: one score bucket larger
+    than a rank window, ranked by token."""
+    S, n, d, g = 1, 6000, 128, 1
+    K = torch.full((S, n, d), 0.5, dtype=torch.bfloat16)
+    V = torch.randn(S, n, d, generator=torch.Generator().manual_seed(6)).to(torch.bfloat16)
+    q = torch.randn(S * g, d, generator=torch.Generator().manual_seed(7)).to(torch.bfloat16)
+    run_case(B, S=S, n=n, d=d, g=g, p=16, k=4608, m=3, L=2, keys=(K, V, q), seed=41,
+             literal=False)
+
+
+def test_qwen3_4b_262k_full_layer_sampled(B):
+    """Full-size layer of the 262,144-token Qwen3-4B-shaped workload (8 streams,
+    power-law cluster sizes, L * k0 = 12,288): two sampled streams checked
+    stage by stage against the oracle."""
+    w = W.WORKLOADS["qwen3_4b_262k"]
+    dev = torch.device("cuda")
+    print("[case] qwen3_4b_262k full layer", flush=True)
+    K, V, q, U, _ = W.layer_inputs(w, layer=0, device=dev)
+    idx = B.Index(K, V, U, page_size=w.p, budget_k=w.k, m=w.m, L=w.L, gqa_group=w.g,
+                  capacity=w.n + 64)
+    page_ids, n_pages, topk = idx.query_pages(q, with_topk=True)
+    out = idx.sparse_attn(q, page_ids, n_pages)
+    torch.cuda.synchronize()
+    assert torch.all(n_pages == w.k // w.p)
+    prm = oracle.Params(d=w.d, p=w.p, k=w.k, m=w.m, L=w.L, g=w.g)
+    for s in (2, 7):
+        print(f"[case] qwen3_4b_262k stream {s} vs oracle", flush=True)
+        st = oracle.OracleStream(prm, _np(K[s]), _np(V[s]), _np(U), n_cap=w.n + 64)
+        _check_index(idx, st, s, w.n)
+        q_s = _np(q[s * w.g:(s + 1) * w.g])
+        r = st.query(q_s, literal=False)
+        _check_query(idx, st, s, r, page_ids, n_pages, topk, out[s * w.g:(s + 1) * w.g], q_s)
