@@ -896,36 +896,37 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
 
 // For L*k0 above kMaxCand (the 262k-token configuration: 6 x 2048): the union
 // of the candidates stays in global memory (the rerank list, followed by the
-// boundary picks that are new to it), duplicates are caught by an LDS hash of
-// 2^14 slots, and the ranking proceeds in windows of consecutive score
-// buckets holding at most kWin elements, each sorted in LDS, until the page
-// walk has P pages and the top-k (when asked for) is written.  The bucket
-// mapping is the small path's.  A bucket of more than kWin elements (near
-// equal scores) is ranked by counting over the union in global memory.  The
-// attention runs in its own kernel.
+// boundary picks that are new to it) and, for the ranking, in registers
+// (kPerBig elements per thread).  Duplicates are caught by a bitmap over the
+// tokens (one test-and-set per token) when the stream has at most kBitTokens
+// tokens, else by an LDS hash of 2^14 slots.  The ranking uses the small
+// path's score buckets and proceeds in windows of consecutive buckets holding
+// at most kWin elements, each ranked in LDS, until the page walk has P pages
+// and the top-k (when asked for) is written.  A bucket of more than kWin elements (near equal scores) is ranked
+// by counting over the union in global memory.  The attention runs in its own
+// kernel.
 constexpr int kBigHashBits = 14;
+constexpr int64_t kBitTokens = (int64_t)32 << kBigHashBits;  // bitmap of the hash's words
 constexpr int kWin = 4096;
+constexpr int kBndBig = 5120;  // boundary keys held in LDS (their rank keys and pages stay global)
+constexpr int kPerBig = kMaxCandBig / kFinalThreads;
+constexpr int kPerBnd = kBndBig / kFinalThreads;
+static_assert(kPerBig * kFinalThreads == kMaxCandBig && kPerBnd * kFinalThreads == kBndBig, "");
 
 struct BigShared {
   union {
-    uint32_t hash[1 << kBigHashBits];  // union membership (selection phase)
-    struct {                           // one window of the ranking
-      unsigned long long wk[kWin];
-      int32_t wx[kWin];
-      int32_t rsid[kWin];
-      int32_t rspg[kWin];
+    uint32_t hash[1 << kBigHashBits];  // union membership: bitmap or hash (selection phase)
+    struct {                           // one window of the ranking, in bucket order
+      unsigned long long wk[kWin];     // keys; later the rank-ordered tokens and pages
+      int32_t wid[kWin];               // tokens
+      int32_t wpg[kWin];               // pages
     };
   };
   union {
-    struct {  // boundary entries (selection phase)
-      unsigned long long bk[kBndLds];
-      unsigned long long brk[kBndLds];
-      int32_t bpg[kBndLds];
-    };
-    struct {  // bucket counts (ranking phase)
+    unsigned long long bk[kBndBig];  // boundary keys (selection phase)
+    struct {                         // bucket counts (ranking phase)
       uint32_t bcnt[kBuckets];
       uint32_t bstart[kBuckets + 1];
-      uint32_t bfill[kBuckets];
     };
   };
   uint32_t seen[2048];
@@ -942,6 +943,7 @@ template <int DT>
 __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n, int32_t *page_ids,
                                                               int32_t *n_pages, int32_t *topk_ids) {
   __shared__ BigShared sh;
+  constexpr int NT = kFinalThreads;
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int L = dv.L, k0 = dv.k0;
@@ -952,7 +954,17 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
 
   // A. counts and the two threshold levels of every composite
   const uint32_t nrr_ld = dv.rr_count[s];
-  for (int x = tid; x < (1 << kBigHashBits); x += kFinalThreads) sh.hash[x] = 0;
+  const bool bitmap = n <= kBitTokens;
+  const int hwords = bitmap ? (int)((n + 31) >> 5) : (1 << kBigHashBits);
+  for (int x = tid; x < hwords; x += NT) sh.hash[x] = 0;
+  // true when the token was not in the union yet
+  auto mark = [&](int32_t id) -> bool {
+    if (bitmap) {
+      const uint32_t bit = 1u << (id & 31);
+      return (atomicOr(&sh.hash[id >> 5], bit) & bit) == 0u;
+    }
+    return hash_insert<kBigHashBits>(sh.hash, id);
+  };
   if (tid < L) {
     sh.cc[tid] = dv.cand_count[s * L + tid];
     sh.nb[tid] = dv.bnd_count[s * L + tid];
@@ -962,7 +974,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
     sh.need2[tid] = 0;
   }
   if (k0e > 0) {
-    for (int l = w; l < L; l += kFinalThreads / 64) {
+    for (int l = w; l < L; l += NT / 64) {
       uint32_t b, bl, b2, bl2, h1[kBinsPerLane], h2[kBinsPerLane];
       wave_hist_load(dv.hist + ((int64_t)s * L + l) * kHistBins, h1);
       wave_hist_load(dv.hist2 + ((int64_t)s * L + l) * kHistBins, h2);
@@ -991,19 +1003,42 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
   }
   __syncthreads();
   const uint32_t nbt = sh.boff[L];
-  const bool bnd_lds = nbt <= (uint32_t)kBndLds;
+  const bool bnd_lds = nbt <= (uint32_t)kBndBig;
+  auto comp_of = [&](uint32_t x) {
+    int l = 0;
+    while (x >= sh.boff[l + 1]) ++l;
+    return l;
+  };
+  auto bnd_off = [&](int l, uint32_t x) {
+    return ((int64_t)s * L + l) * dv.ncap + (x - sh.boff[l]);
+  };
 
-  // B. the rerank list's tokens into the hash; the boundary entries into LDS
-  for (uint32_t x = tid; x < nrr; x += kFinalThreads) hash_insert<kBigHashBits>(sh.hash, uid[x]);
-  if (bnd_lds) {
-    for (uint32_t x = tid; x < nbt; x += kFinalThreads) {
-      int l = 0;
-      while (x >= sh.boff[l + 1]) ++l;
-      const int64_t o = ((int64_t)s * L + l) * dv.ncap + (x - sh.boff[l]);
-      sh.bk[x] = dv.bnd[o];
-      sh.brk[x] = dv.bnd_rk[o];
-      sh.bpg[x] = dv.bnd_pg[o];
+  // B. the rerank list's tokens into the hash; the boundary keys into LDS
+  // (each thread's loads issued together)
+  {
+    int32_t ids[kPerBig];
+#pragma unroll
+    for (int j = 0; j < kPerBig; ++j) {
+      const uint32_t x = tid + NT * j;
+      ids[j] = x < nrr ? uid[x] : -1;
     }
+    if (bnd_lds) {
+      int64_t bo[kPerBnd];
+#pragma unroll
+      for (int j = 0; j < kPerBnd; ++j) {
+        const uint32_t x = tid + NT * j;
+        bo[j] = x < nbt ? bnd_off(comp_of(x), x) : -1;
+      }
+      unsigned long long bv[kPerBnd];
+#pragma unroll
+      for (int j = 0; j < kPerBnd; ++j) bv[j] = bo[j] >= 0 ? dv.bnd[bo[j]] : 0ull;
+#pragma unroll
+      for (int j = 0; j < kPerBnd; ++j)
+        if (bo[j] >= 0) sh.bk[tid + NT * j] = bv[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kPerBig; ++j)
+      if (ids[j] >= 0) mark(ids[j]);
   }
   __syncthreads();
 
@@ -1012,54 +1047,81 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
   auto add_pick = [&](int l, unsigned long long key, unsigned long long rk, int32_t pg) {
     const int32_t id = (int32_t)(key & 0xffffffffull);
     dv.cand[((int64_t)s * L + l) * k0 + sh.cc[l] + atomicAdd(&sh.extra[l], 1u)] = id;
-    if (hash_insert<kBigHashBits>(sh.hash, id)) {
+    if (mark(id)) {
       const uint32_t pos = nrr + atomicAdd(&sh.nux, 1u);
       ukey[pos] = rk;
       uid[pos] = id;
       upg[pos] = pg;
     }
   };
+  auto add_pick_x = [&](int l, unsigned long long key, uint32_t x) {
+    const int64_t o = bnd_off(l, x);
+    add_pick(l, key, dv.bnd_rk[o], dv.bnd_pg[o]);
+  };
   auto sub_of = [](unsigned long long key) -> uint32_t {
     return (uint32_t)(key >> (32 + kSubShift)) & (kHistBins - 1);
   };
   if (nbt > 0) {
     if (bnd_lds) {
-      for (uint32_t x = tid; x < nbt; x += kFinalThreads) {
-        int l = 0;
-        while (x >= sh.boff[l + 1]) ++l;
-        const unsigned long long key = sh.bk[x];
-        const uint32_t sb = sub_of(key);
-        if (sb < sh.b2[l]) add_pick(l, key, sh.brk[x], sh.bpg[x]);
-        if (sb == sh.b2[l]) {
-          const uint32_t t = atomicAdd(&sh.ntie, 1u);
-          if (t < kMaxTies) sh.tie[t] = x;
+      // entries below second-level bin b2_l: picked outright (their rank
+      // keys and pages loaded together); bin b2_l: the tie list
+      int64_t po[kPerBnd];
+      unsigned long long pk[kPerBnd];
+      int pl[kPerBnd];
+#pragma unroll
+      for (int j = 0; j < kPerBnd; ++j) {
+        const uint32_t x = tid + NT * j;
+        po[j] = -1;
+        pk[j] = 0;
+        pl[j] = 0;
+        if (x < nbt) {
+          const int l = comp_of(x);
+          const unsigned long long key = sh.bk[x];
+          const uint32_t sb = sub_of(key);
+          if (sb < sh.b2[l]) {
+            po[j] = bnd_off(l, x);
+            pk[j] = key;
+            pl[j] = l;
+          }
+          if (sb == sh.b2[l]) {
+            const uint32_t t = atomicAdd(&sh.ntie, 1u);
+            if (t < kMaxTies) sh.tie[t] = x;
+          }
         }
       }
+      unsigned long long prk[kPerBnd];
+      int32_t ppg[kPerBnd];
+#pragma unroll
+      for (int j = 0; j < kPerBnd; ++j) {
+        prk[j] = po[j] >= 0 ? dv.bnd_rk[po[j]] : 0ull;
+        ppg[j] = po[j] >= 0 ? dv.bnd_pg[po[j]] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < kPerBnd; ++j)
+        if (po[j] >= 0) add_pick(pl[j], pk[j], prk[j], ppg[j]);
       __syncthreads();
       const uint32_t nt = sh.ntie;
       if (nt <= (uint32_t)kMaxTies) {
-        for (uint32_t t = tid; t < nt; t += kFinalThreads) {
+        for (uint32_t t = tid; t < nt; t += NT) {
           const uint32_t x = sh.tie[t];
-          int l = 0;
-          while (x >= sh.boff[l + 1]) ++l;
+          const int l = comp_of(x);
           const unsigned long long key = sh.bk[x];
           uint32_t rank = 0;
           for (uint32_t u = 0; u < nt; ++u) {
             const uint32_t y = sh.tie[u];
             rank += (y >= sh.boff[l]) & (y < sh.boff[l + 1]) & (sh.bk[y] < key);
           }
-          if (rank < sh.need2[l]) add_pick(l, key, sh.brk[x], sh.bpg[x]);
+          if (rank < sh.need2[l]) add_pick_x(l, key, x);
         }
       } else {
-        for (uint32_t x = tid; x < nbt; x += kFinalThreads) {
-          int l = 0;
-          while (x >= sh.boff[l + 1]) ++l;
+        for (uint32_t x = tid; x < nbt; x += NT) {
+          const int l = comp_of(x);
           const unsigned long long key = sh.bk[x];
           if (sub_of(key) != sh.b2[l]) continue;
           uint32_t rank = 0;
           for (uint32_t y = sh.boff[l]; y < sh.boff[l + 1]; ++y)
             rank += (sub_of(sh.bk[y]) == sh.b2[l]) & (sh.bk[y] < key);
-          if (rank < sh.need2[l]) add_pick(l, key, sh.brk[x], sh.bpg[x]);
+          if (rank < sh.need2[l]) add_pick_x(l, key, x);
         }
       }
     } else {
@@ -1069,7 +1131,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
         const uint32_t nbl = sh.nb[l], nd = sh.need[l];
         const unsigned long long thr =
             nd >= nbl ? ~0ull : block_select(bk, nbl, nd, sh.cnt, &sh.res, &sh.rr);
-        for (uint32_t x = tid; x < nbl; x += kFinalThreads) {
+        for (uint32_t x = tid; x < nbl; x += NT) {
           const unsigned long long key = bk[x];
           if (key <= thr) add_pick(l, key, dv.bnd_rk[ob + x], dv.bnd_pg[ob + x]);
         }
@@ -1080,13 +1142,26 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
   __syncthreads();  // the union is complete (and its global writes visible to the block)
   const uint32_t nu = nrr + sh.nux;
 
-  // D. ranking in windows of score buckets
-  unsigned long long lo = ~0ull, hi = 0;
-  for (uint32_t x = tid; x < nu; x += kFinalThreads) {
-    const unsigned long long kx = ukey[x];
-    lo = min(lo, kx);
-    hi = max(hi, kx);
+  // D. ranking in windows of score buckets, the union in registers
+  unsigned long long kx[kPerBig];
+  int32_t ix[kPerBig], px[kPerBig];
+  uint32_t bw[kPerBig];  // bucket | slot inside the bucket << 12
+  auto bkt_of = [](uint32_t v) { return v & 0xfffu; };
+  auto within_of = [](uint32_t v) { return v >> 12; };
+#pragma unroll
+  for (int j = 0; j < kPerBig; ++j) {
+    const uint32_t x = tid + NT * j;
+    kx[j] = x < nu ? ukey[x] : ~0ull;
+    ix[j] = x < nu ? uid[x] : 0;
+    px[j] = x < nu ? upg[x] : 0;
   }
+  unsigned long long lo = ~0ull, hi = 0;
+#pragma unroll
+  for (int j = 0; j < kPerBig; ++j)
+    if (tid + NT * j < nu) {
+      lo = min(lo, kx[j]);
+      hi = max(hi, kx[j]);
+    }
   for (int off = 32; off >= 1; off >>= 1) {
     lo = min(lo, (unsigned long long)__shfl_xor((long long)lo, off));
     hi = max(hi, (unsigned long long)__shfl_xor((long long)hi, off));
@@ -1095,27 +1170,28 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
     sh.wlo[w] = lo;
     sh.whi[w] = hi;
   }
-  for (int x = tid; x < kBuckets; x += kFinalThreads) {
-    sh.bcnt[x] = 0;
-    sh.bfill[x] = 0;
-  }
-  for (int x = tid; x < 2048; x += kFinalThreads) sh.seen[x] = 0;
+  for (int x = tid; x < kBuckets; x += NT) sh.bcnt[x] = 0;
+  for (int x = tid; x < 2048; x += NT) sh.seen[x] = 0;
   __syncthreads();
   lo = ~0ull;
   hi = 0;
 #pragma unroll
-  for (int k = 0; k < kFinalThreads / 64; ++k) {
+  for (int k = 0; k < NT / 64; ++k) {
     lo = min(lo, sh.wlo[k]);
     hi = max(hi, sh.whi[k]);
   }
   const double smax = nu ? rank_key_score(lo) : 0.0;
   const double smin = nu ? rank_key_score(hi) : 0.0;
   const double scale = smax > smin ? (double)(kBuckets - 1) / (smax - smin) : 0.0;
-  auto bucket_of = [smax, scale](unsigned long long key) -> uint32_t {
-    const double t = (smax - rank_key_score(key)) * scale;
-    return (uint32_t)min((double)(kBuckets - 1), t);
-  };
-  for (uint32_t x = tid; x < nu; x += kFinalThreads) atomicAdd(&sh.bcnt[bucket_of(ukey[x])], 1u);
+#pragma unroll
+  for (int j = 0; j < kPerBig; ++j) {
+    bw[j] = kBuckets;  // past every window
+    if (tid + NT * j < nu) {
+      const double t = (smax - rank_key_score(kx[j])) * scale;
+      const uint32_t b = (uint32_t)min((double)(kBuckets - 1), t);
+      bw[j] = b | (atomicAdd(&sh.bcnt[b], 1u) << 12);
+    }
+  }
   __syncthreads();
   {  // exclusive scan of the bucket counts, two per thread
     const uint32_t c0 = sh.bcnt[2 * tid], c1 = sh.bcnt[2 * tid + 1];
@@ -1135,8 +1211,9 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
   const uint32_t want_top = topk_ids ? min((uint32_t)dv.k, nu) : 0u;
   int pbits = 1;
   while ((1ll << pbits) < dv.pcap) ++pbits;
+  int32_t *const rsid = reinterpret_cast<int32_t *>(&sh.wk[0]);  // over the dead keys
+  int32_t *const rspg = rsid + kWin;
   uint32_t B0 = 0, rank_base = 0;
-  unsigned long long *grank = dv.bnd + (int64_t)s * L * dv.ncap;  // dead boundary keys as scratch
   while (B0 < (uint32_t)kBuckets && rank_base < nu &&
          ((int)sh.nsel < P || rank_base < want_top)) {
     // the window: buckets [B0, B1), at most kWin elements (one bucket at least)
@@ -1155,74 +1232,96 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
     const uint32_t B1 = sh.win_end;
     const uint32_t base = sh.bstart[B0], cntw = sh.bstart[B1] - base;
     if (cntw <= (uint32_t)kWin) {
-      for (uint32_t x = tid; x < nu; x += kFinalThreads) {
-        const unsigned long long kx = ukey[x];
-        const uint32_t b = bucket_of(kx);
-        if (b >= B0 && b < B1) {
-          const uint32_t pos = sh.bstart[b] - base + atomicAdd(&sh.bfill[b], 1u);
-          sh.wk[pos] = kx;
-          sh.wx[pos] = (int32_t)x;
+      // scatter the window's elements in bucket order, rank each by position
+      // (kWin / NT per thread), then write tokens and pages in rank order
+#pragma unroll
+      for (int j = 0; j < kPerBig; ++j)
+        if (bkt_of(bw[j]) >= B0 && bkt_of(bw[j]) < B1) {
+          const uint32_t pos = sh.bstart[bkt_of(bw[j])] - base + within_of(bw[j]);
+          sh.wk[pos] = kx[j];
+          sh.wid[pos] = ix[j];
+          sh.wpg[pos] = px[j];
         }
-      }
       __syncthreads();
-      for (uint32_t r = tid; r < cntw; r += kFinalThreads) {
-        const unsigned long long kx = sh.wk[r];
-        const int32_t x = sh.wx[r];
-        const int32_t ix = uid[x];
-        const uint32_t b = bucket_of(kx);
-        const uint32_t b0 = sh.bstart[b] - base, b1 = b0 + sh.bcnt[b];
-        uint32_t rk = b0, eq = 0;
-        for (uint32_t y = b0; y < b1; ++y) {
-          const unsigned long long ky = sh.wk[y];
-          rk += ky < kx;
-          eq += ky == kx;
+      constexpr int kPerWin = kWin / NT;
+      uint32_t rr[kPerWin];
+      int32_t ri[kPerWin], rp[kPerWin];
+#pragma unroll
+      for (int j = 0; j < kPerWin; ++j) {
+        const uint32_t x = tid + NT * j;
+        rr[j] = ~0u;
+        ri[j] = 0;
+        rp[j] = 0;
+        if (x < cntw) {
+          const unsigned long long kk = sh.wk[x];
+          const int32_t id = sh.wid[x];
+          const double t = (smax - rank_key_score(kk)) * scale;
+          const uint32_t b = (uint32_t)min((double)(kBuckets - 1), t);
+          const uint32_t b0 = sh.bstart[b] - base, b1 = b0 + sh.bcnt[b];
+          uint32_t r = b0, eq = 0;
+          for (uint32_t y = b0; y < b1; ++y) {
+            const unsigned long long ky = sh.wk[y];
+            r += ky < kk;
+            eq += ky == kk;
+          }
+          if (eq > 1)  // equal keys (rare): order them by token
+            for (uint32_t y = b0; y < b1; ++y) r += sh.wk[y] == kk && sh.wid[y] < id;
+          rr[j] = r;
+          ri[j] = id;
+          rp[j] = sh.wpg[x];
         }
-        if (eq > 1)
-          for (uint32_t y = b0; y < b1; ++y) rk += sh.wk[y] == kx && uid[sh.wx[y]] < ix;
-        sh.rsid[rk] = ix;
-        sh.rspg[rk] = upg[x];
       }
+      __syncthreads();  // every read of the window is done
+#pragma unroll
+      for (int j = 0; j < kPerWin; ++j)
+        if (rr[j] != ~0u) {
+          rsid[rr[j]] = ri[j];
+          rspg[rr[j]] = rp[j];
+        }
     } else {
-      // one bucket above the window: rank its elements by counting over the
-      // union (slow; only near-equal scores get here), in chunks of kWin ranks
-      for (uint32_t x = tid; x < nu; x += kFinalThreads) {
-        const unsigned long long kx = ukey[x];
-        if (bucket_of(kx) != B0) continue;
-        const int32_t ix = uid[x];
-        uint32_t rk = 0;
+      // one bucket above the window size: rank its elements by counting
+      // over the union (slow; only near-equal scores get here), written out
+      // in chunks of kWin ranks below
+#pragma unroll
+      for (int j = 0; j < kPerBig; ++j) {
+        if (bkt_of(bw[j]) != B0) continue;
+        uint32_t r = 0;
         for (uint32_t y = 0; y < nu; ++y) {
           const unsigned long long ky = ukey[y];
-          rk += bucket_of(ky) == B0 && (ky < kx || (ky == kx && uid[y] < ix));
+          if (ky < kx[j] || (ky == kx[j] && uid[y] < ix[j])) {
+            const double t = (smax - rank_key_score(ky)) * scale;
+            r += (uint32_t)min((double)(kBuckets - 1), t) == B0;
+          }
         }
-        grank[x] = rk;
+        bw[j] = (bw[j] & 0xfffu) | (r << 12);  // the rank replaces the slot (bucket B0 is done after)
       }
-      __syncthreads();
     }
-    // walk the window's ranks (the big-bucket case in chunks of kWin ranks)
+    // walk the window's ranks in chunks of kWin (one chunk unless one bucket
+    // holds more)
     for (uint32_t c0 = 0; c0 < cntw; c0 += kWin) {
       const uint32_t cw = min((uint32_t)kWin, cntw - c0);
       if (cntw > (uint32_t)kWin) {
-        for (uint32_t x = tid; x < nu; x += kFinalThreads) {
-          if (bucket_of(ukey[x]) != B0) continue;
-          const uint32_t rk = (uint32_t)grank[x];
-          if (rk >= c0 && rk < c0 + cw) {
-            sh.rsid[rk - c0] = uid[x];
-            sh.rspg[rk - c0] = upg[x];
+#pragma unroll
+        for (int j = 0; j < kPerBig; ++j) {
+          const uint32_t r = within_of(bw[j]);
+          if (bkt_of(bw[j]) == B0 && r >= c0 && r < c0 + cw) {
+            rsid[r - c0] = ix[j];
+            rspg[r - c0] = px[j];
           }
         }
       }
       __syncthreads();
       const uint32_t rb = rank_base + c0;
       if (topk_ids)
-        for (uint32_t r = tid; r < cw; r += kFinalThreads)
-          if (rb + r < want_top) topk_ids[(int64_t)s * dv.k + rb + r] = sh.rsid[r];
+        for (uint32_t r = tid; r < cw; r += NT)
+          if (rb + r < want_top) topk_ids[(int64_t)s * dv.k + rb + r] = rsid[r];
       if (w == 0 && (int)sh.nsel < P) {
         int nsel = sh.nsel;
         const unsigned long long lt = lanemask_lt();
         for (uint32_t x0 = 0; x0 < cw && nsel < P; x0 += 64) {
           const uint32_t x = x0 + lane;
           const bool valid = x < cw;
-          const int32_t pg = valid ? sh.rspg[x] : 0;
+          const int32_t pg = valid ? rspg[x] : 0;
           const bool fresh = valid && ((sh.seen[pg >> 5] >> (pg & 31)) & 1u) == 0u;
           const unsigned long long act = __ballot(fresh);
           const unsigned long long mt = match_bits((uint32_t)pg, pbits, act);
@@ -1246,15 +1345,15 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
 
   // E. padding and counts
   const int nsel = sh.nsel;
-  for (int x = nsel + tid; x < P; x += kFinalThreads) page_ids[(int64_t)s * P + x] = -1;
+  for (int x = nsel + tid; x < P; x += NT) page_ids[(int64_t)s * P + x] = -1;
   if (tid == 0) n_pages[s] = nsel;
   if (topk_ids)
-    for (uint32_t x = want_top + tid; x < (uint32_t)dv.k; x += kFinalThreads)
+    for (uint32_t x = want_top + tid; x < (uint32_t)dv.k; x += NT)
       topk_ids[(int64_t)s * dv.k + x] = -1;
   if (tid < L && k0e > 0) dv.cand_count[s * L + tid] = sh.cc[tid] + sh.extra[tid];
   uint32_t *hist = dv.hist + (int64_t)s * L * kHistBins;
   uint32_t *hist2 = dv.hist2 + (int64_t)s * L * kHistBins;
-  for (int x = tid; x < L * kHistBins; x += kFinalThreads) {
+  for (int x = tid; x < L * kHistBins; x += NT) {
     hist[x] = 0;
     hist2[x] = 0;
   }
