@@ -93,6 +93,8 @@ struct BuildScratch {
 };
 
 // Decode-time kernels that the optional event timer reports separately.
+// KID_PREP is the standalone insert; a decode step's insert and query prep
+// run inside the scan.
 enum KernelId { KID_PREP = 0, KID_QSCAN, KID_QCOLLECT, KID_QFINAL, KID_ATTN, KID_AMERGE,
                 KID_COUNT };
 
@@ -104,8 +106,6 @@ void timer_mark(Timer *tm, int kid, hipStream_t st);    // after each launch
 // Host launchers (each returns the hipGetLastError of its launches).
 hipError_t launch_build(const Dev &dv, const BuildScratch &bs, int64_t n, const void *K,
                         const void *V, const void *dirs, float c_fixed, hipStream_t st);
-hipError_t launch_prep(const Dev &dv, int64_t n, const void *k_new, const void *v_new,
-                       const void *q, int mode, hipStream_t st);  // mode: 1 insert, 2 query, 3 both
 hipError_t launch_insert(const Dev &dv, int64_t n, const void *k_new, const void *v_new,
                          hipStream_t st, Timer *tm);
 hipError_t launch_query(const Dev &dv, int64_t n, const void *q, int32_t *page_ids,

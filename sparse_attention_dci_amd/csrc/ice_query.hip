@@ -10,10 +10,9 @@
 // visits 60-85% of all list entries before k0 tokens complete, so it would
 // touch most of them anyway) followed by an exact selection:
 //
-//   k_prep      (ice_prep.hip) the query codes: fp32 GQA mean, fp64
-//               projection;
-//   k_qscan     M_i for every token and composite and a histogram of the top
-//               11 bits of M_i;
+//   k_qscan     the query codes (fp32 GQA mean, fp64 projection; in a
+//               decode step also the new token's insert), then M_i for every
+//               token and composite and a histogram of the top 11 bits of M_i;
 //   k_qcollect  tokens in bins below the k0-th smallest bin b* are
 //               candidates, tokens in bin b* are parked with their (M_i, i)
 //               key; both kinds are scored exactly (fp64, ascending element
@@ -21,8 +20,10 @@
 //   k_qfinal    one 1024-thread block per stream: exact selection inside the
 //               boundary bins, the union of the composites (LDS hash), a
 //               bucket sort by (score desc, token asc), top-k and the page
-//               walk; it leaves a clean histogram for the next query.
+//               walk; it leaves a clean histogram for the next query (and
+//               k_qfinal_big does the same for unions above kMaxCand).
 #include "ice_attn_dev.h"
+#include "ice_step_dev.h"
 
 namespace ice {
 
@@ -166,8 +167,8 @@ __device__ __forceinline__ int32_t ld_code(__amdgpu_buffer_rsrc_t r, uint32_t of
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
-// 1-D grid of S * ceil(n / kScanTpb) blocks, 512 threads.  Block b serves
-// stream b % S (consecutive blocks take different streams, so with S a
+// 1-D grid of S * max(1, ceil(n / kScanTpb)) blocks, 512 threads.  Block b
+// serves stream b % S (consecutive blocks take different streams, so with S a
 // multiple of 8 all blocks of a stream land on one XCD and share its L2) and
 // the b / S-th range of kScanTpb = 1024 tokens: wave w takes tiles 2w and
 // 2w+1 of the range, lane j token j of a tile, and reads code t of its 64
@@ -175,29 +176,97 @@ __device__ __forceinline__ int32_t ld_code(__amdgpu_buffer_rsrc_t r, uint32_t of
 // flight at a time: every code slot is refilled with the code kPipe places
 // later right after it is used.  R = ceil(mL / kPipe) is a template
 // parameter, so the walk over code positions is straight-line code and every
-// wait covers exactly the loads it needs.  The query codes come from the prep
-// kernel.  The histogram lives in LDS when L <= 6, and only the bins at or
-// below the block's own k0-th bin are added to the global one; with L > 6
-// every count goes straight to global.
+// wait covers exactly the loads it needs.  The histogram lives in LDS when
+// L <= 6, and only the bins at or below the block's own k0-th bin are added to
+// the global one; with L > 6 every count goes straight to global.
+//
+// Every block first derives the query codes itself (the directions staged in
+// LDS, the arithmetic of ice_step_dev.h), so no prep kernel sits on the
+// query's critical path; the blocks of range 0 publish q_kv and the codes for
+// the later kernels and clear the query's counters.  In a decode step (k_new
+// given) token n - 1 is the new token: the block whose range holds it
+// projects it on the same staged directions, leaves it out of the code walk,
+// adds its M values afterwards and writes its codes, list entries, page and
+// pool rows at the end.
 constexpr int kPipe = 16;
 
-template <bool LDS_HIST, int R>
-__global__ __launch_bounds__(kScanThreads) void k_qscan(Dev dv, int64_t n) {
+template <int DT, bool LDS_HIST, int R>
+__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(6))) void k_qscan(Dev dv, int64_t n, const void *q,
+                                                        const void *k_new, const void *v_new) {
   constexpr int NT = kScanThreads;
+  constexpr int W = R * kPipe;  // staged direction columns (>= mL, <= the stored row width)
+  constexpr int W4 = W / 4;
+  constexpr int kStage = (129 * W4 + NT - 1) / NT;
   const int S = dv.S, s = blockIdx.x % S;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int mL = dv.mL, m = dv.m, L = dv.L;
-  __shared__ int32_t qc[kMaxMl];
+  const int mL = dv.mL, m = dv.m, L = dv.L, d = dv.d, g = dv.g;
+  const int64_t r = blockIdx.x / S;
+  const int64_t nold = k_new != nullptr ? n - 1 : n;  // tokens already in the index
+  const bool ins = k_new != nullptr && r == nold / kScanTpb;  // this block inserts token nold
+  union ScanShared {
+    uint32_t hist[LDS_HIST ? 6 * kHistBins : 1];
+    float dl[kStage * NT * 4];  // directions as [e][W] (row d holds u_t[d]), padded
+  };
+  __shared__ ScanShared sm;
+  __shared__ int32_t qc[kMaxMl], nc[kMaxMl];
   __shared__ uint32_t blim[6];
-  __shared__ uint32_t hist[LDS_HIST ? 6 * kHistBins : 1];
+  __shared__ float qkv[128], kv[128];
+  __shared__ double zs[kMaxMl], rs[kMaxMl];
+  __shared__ double qsq_s, ksq_s;
+  __shared__ uint32_t cell_s;
+  __shared__ int32_t loc_s;
   uint32_t *ghist = dv.hist + (int64_t)s * L * kHistBins;
 
-  // 1. the query codes, then the first kPipe codes of both tiles
-  const int32_t qv0 = dv.qcode[(int64_t)s * mL + min(tid, mL - 1)];
+  // 1. the prep's loads, every one issued before any is used (clamped
+  // addresses, no branches): the directions, heads 0..3 of element tid, the
+  // new key (any valid address when there is none), the insert's scalars
+  const int tot4 = (d + 1) * W4;
+  float4 st4[kStage];
+#pragma unroll
+  for (int k = 0; k < kStage; ++k) {
+    const int x = min(tid + NT * k, tot4 - 1);
+    st4[k] = *reinterpret_cast<const float4 *>(dv.dirs32 + (int64_t)(x / W4) * dv.mLp +
+                                               (x % W4) * 4);
+  }
+  const int te = min(tid & 127, d - 1);
+  float hv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) hv[j] = load_elem<DT>(q, ((int64_t)s * g + min(j, g - 1)) * d + te);
+  const float kx = load_elem<DT>(k_new != nullptr ? k_new : q, (int64_t)s * d + te);
+  const int32_t np0 = dv.npages[s];
+  const double ic = dv.inv_c[s], ic2 = dv.inv_c2[s];
+#pragma unroll
+  for (int k = 0; k < kStage; ++k) {
+    const int x = tid + NT * k;  // past tot4: padding
+    *reinterpret_cast<float4 *>(sm.dl + (x / W4) * W + (x % W4) * 4) = st4[k];
+  }
+  float acc = hv[0];  // left fold of the heads
+#pragma unroll
+  for (int j = 1; j < 4; ++j) acc = j < g ? __fadd_rn(acc, hv[j]) : acc;
+  for (int h0 = 4; h0 < g; h0 += 4) {  // groups above 4
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      hv[j] = load_elem<DT>(q, ((int64_t)s * g + min(h0 + j, g - 1)) * d + te);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = h0 + j < g ? __fadd_rn(acc, hv[j]) : acc;
+  }
+  if (tid < d) qkv[tid] = __fmul_rn(acc, group_inv(g));
+  if (ins && tid >= 256 && tid < 256 + d) kv[tid - 256] = kx;
+  lds_barrier();
+
+  // the chains: query on threads < mL and 128, insert on 256 + t and 384
+  if (tid < mL) zs[tid] = dot_chain(qkv, sm.dl + tid, W, d);
+  if (tid == 128) qsq_s = dot_chain(qkv, qkv, 1, d);
+  if (ins) {
+    if (tid >= 256 && tid < 256 + mL) rs[tid - 256] = dot_chain(kv, sm.dl + (tid - 256), W, d);
+    if (tid == 384) ksq_s = dot_chain(kv, kv, 1, d);
+  }
+  lds_barrier();
+  // the first kPipe codes of both tiles (issued after the chains, which
+  // need the registers)
   const uint32_t tile_bytes = (uint32_t)mL * kCodeTile * 4;
   const __amdgpu_buffer_rsrc_t rc =
       byte_range(dv.codes + (int64_t)s * dv.ntile * mL * kCodeTile, (uint32_t)dv.ntile * tile_bytes);
-  const int64_t r = blockIdx.x / S;
   const uint32_t oa = (uint32_t)(r * (kScanTpb / 64) + 2 * w) * tile_bytes + lane * 4;
   int32_t a[kPipe], b[kPipe];
 #pragma unroll
@@ -205,17 +274,41 @@ __global__ __launch_bounds__(kScanThreads) void k_qscan(Dev dv, int64_t n) {
     a[x] = ld_code(rc, oa + x * 256);
     b[x] = ld_code(rc, oa + tile_bytes + x * 256);
   }
-  if (tid < mL) qc[tid] = qv0;
-  if (LDS_HIST)
-    for (int x = tid; x < L * kHistBins; x += NT) hist[x] = 0;
+
+  if (tid < mL) qc[tid] = query_code(zs[tid], qsq_s);
+  if (ins) {
+    if (tid >= 256 && tid < 256 + mL) {
+      const int t = tid - 256;
+      nc[t] = insert_code(rs[t], (double)sm.dl[d * W + t], ksq_s, ic, ic2);
+    }
+    if (w == 4) {  // the new token's cell: sign bits of r on the first D directions
+      const unsigned long long bal = __ballot(lane < dv.D && rs[lane < mL ? lane : 0] >= 0.0);
+      if (lane == 0) cell_s = (uint32_t)bal & ((1u << dv.D) - 1u);
+    }
+  }
   lds_barrier();
+  if (r == 0) {  // publication and the query's counters
+    if (tid < mL) dv.qcode[(int64_t)s * mL + tid] = qc[tid];
+    if (tid < d) dv.qkv[(int64_t)s * d + tid] = qkv[tid];
+    if (tid < L) {
+      dv.cand_count[s * L + tid] = 0;
+      dv.bnd_count[s * L + tid] = 0;
+    }
+    if (tid == 0) dv.rr_count[s] = 0;
+  }
+  if (LDS_HIST) {
+    for (int x = tid; x < L * kHistBins; x += NT) sm.hist[x] = 0;
+    lds_barrier();
+  }
+  uint32_t *hist = sm.hist;
 
   // 2. M per token and composite.  Composite boundaries depend on the code
   // position only, so every branch but the ragged tail's is uniform.
   const int64_t i0 = r * kScanTpb, i1 = min(i0 + kScanTpb, n);
   const uint32_t ntok = (uint32_t)(i1 > i0 ? i1 - i0 : 0);
   const int64_t ia = i0 + 128 * w + lane, ib = ia + 64;
-  const bool va = ia < i1, vb = ib < i1;
+  const int64_t iv = min(i1, nold);  // the new token is added after the walk
+  const bool va = ia < iv, vb = ib < iv;
   int32_t Ma = 0, Mb = 0;
   int l = 0, tend = m - 1;
   int32_t qround[kPipe];  // this round's query codes, uniform (scalar registers)
@@ -260,6 +353,21 @@ __global__ __launch_bounds__(kScanThreads) void k_qscan(Dev dv, int64_t n) {
     }
   }
 
+  if (ins && tid == 0) {  // the new token's M of every composite
+    for (int l2 = 0; l2 < L; ++l2) {
+      int32_t M = 0;
+      for (int j = 0; j < m; ++j) {
+        const int32_t dd = nc[l2 * m + j] - qc[l2 * m + j];
+        M = max(M, max(dd, -dd));
+      }
+      dv.mbuf[((int64_t)s * L + l2) * dv.ncap + nold] = (uint32_t)M;
+      if (LDS_HIST)
+        atomicAdd(&hist[l2 * kHistBins + (M >> kHistShift)], 1u);
+      else
+        atomicAdd(&ghist[l2 * kHistBins + (M >> kHistShift)], 1u);
+    }
+  }
+
   // 3. flush the block's histogram.  The k0-th smallest M of the stream is
   // never in a higher bin than the k0-th smallest of a block holding at least
   // k0 tokens, so every bin up to the global threshold bin still receives
@@ -276,6 +384,14 @@ __global__ __launch_bounds__(kScanThreads) void k_qscan(Dev dv, int64_t n) {
       const uint32_t h = hist[x];
       if (h && (uint32_t)(x % kHistBins) <= blim[x / kHistBins]) atomicAdd(&ghist[x], h);
     }
+  }
+
+  // 4. the insert's stores: codes and list entries, the page rule, the pool
+  if (ins) {
+    if (tid < mL) insert_code_store(dv, s, nold, tid, nc[tid]);
+    if (tid == 0) loc_s = insert_page_rule(dv, s, nold, cell_s, np0);
+    __syncthreads();
+    if (tid < d) insert_pool_store<DT>(dv, s, loc_s, tid, k_new, v_new);
   }
 }
 
@@ -1361,37 +1477,42 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
 
 // ---------------------------------------------------------------- launcher
 
-template <bool LH, int R>
-static void launch_scan(const Dev &dv, int64_t n, unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_qscan<LH, R>), dim3(grid), dim3(kScanThreads), 0, st, dv, n);
+template <int DT, bool LH, int R>
+static void launch_scan(const Dev &dv, int64_t n, unsigned grid, const void *q, const void *k_new,
+                        const void *v_new, hipStream_t st) {
+  hipLaunchKernelGGL((k_qscan<DT, LH, R>), dim3(grid), dim3(kScanThreads), 0, st, dv, n, q, k_new,
+                     v_new);
 }
 
-template <bool LH>
-static void launch_scan_r(const Dev &dv, int64_t n, unsigned grid, hipStream_t st) {
+template <int DT, bool LH>
+static void launch_scan_r(const Dev &dv, int64_t n, unsigned grid, const void *q,
+                          const void *k_new, const void *v_new, hipStream_t st) {
   switch ((dv.mL + kPipe - 1) / kPipe) {
-    case 1: launch_scan<LH, 1>(dv, n, grid, st); break;
-    case 2: launch_scan<LH, 2>(dv, n, grid, st); break;
-    case 3: launch_scan<LH, 3>(dv, n, grid, st); break;
-    case 4: launch_scan<LH, 4>(dv, n, grid, st); break;
-    case 5: launch_scan<LH, 5>(dv, n, grid, st); break;
-    case 6: launch_scan<LH, 6>(dv, n, grid, st); break;
-    case 7: launch_scan<LH, 7>(dv, n, grid, st); break;
-    default: launch_scan<LH, 8>(dv, n, grid, st); break;  // mL <= 128
+    case 1: launch_scan<DT, LH, 1>(dv, n, grid, q, k_new, v_new, st); break;
+    case 2: launch_scan<DT, LH, 2>(dv, n, grid, q, k_new, v_new, st); break;
+    case 3: launch_scan<DT, LH, 3>(dv, n, grid, q, k_new, v_new, st); break;
+    case 4: launch_scan<DT, LH, 4>(dv, n, grid, q, k_new, v_new, st); break;
+    case 5: launch_scan<DT, LH, 5>(dv, n, grid, q, k_new, v_new, st); break;
+    case 6: launch_scan<DT, LH, 6>(dv, n, grid, q, k_new, v_new, st); break;
+    case 7: launch_scan<DT, LH, 7>(dv, n, grid, q, k_new, v_new, st); break;
+    default: launch_scan<DT, LH, 8>(dv, n, grid, q, k_new, v_new, st); break;  // mL <= 128
   }
 }
 
-// The query after its prep: scan, collect, final.
+// The query over n tokens (token n - 1 inserted by the scan when k_new is
+// given): scan, collect, final.
 template <int DT>
 static void query_tail(const Dev &dv, int64_t n, int32_t *page_ids, int32_t *n_pages,
-                       int32_t *topk_ids, const void *q, float *out, hipStream_t st, Timer *tm) {
+                       int32_t *topk_ids, const void *q, const void *k_new, const void *v_new,
+                       float *out, hipStream_t st, Timer *tm) {
   const int64_t nrange = (n + kScanTpb - 1) / kScanTpb;
+  const unsigned grid = (unsigned)(max(nrange, (int64_t)1) * dv.S);
+  if (dv.L <= 6)
+    launch_scan_r<DT, true>(dv, n, grid, q, k_new, v_new, st);
+  else
+    launch_scan_r<DT, false>(dv, n, grid, q, k_new, v_new, st);
+  timer_mark(tm, KID_QSCAN, st);
   if (n > 0) {
-    const unsigned grid = (unsigned)(nrange * dv.S);
-    if (dv.L <= 6)
-      launch_scan_r<true>(dv, n, grid, st);
-    else
-      launch_scan_r<false>(dv, n, grid, st);
-    timer_mark(tm, KID_QSCAN, st);
     hipLaunchKernelGGL(k_qcollect<DT>, dim3(grid), dim3(kScanThreads), 0, st, dv, n);
     timer_mark(tm, KID_QCOLLECT, st);
   }
@@ -1410,32 +1531,28 @@ static void query_tail(const Dev &dv, int64_t n, int32_t *page_ids, int32_t *n_p
 hipError_t launch_query(const Dev &dv, int64_t n, const void *q, int32_t *page_ids,
                         int32_t *n_pages, int32_t *topk_ids, hipStream_t st, Timer *tm) {
   timer_begin(tm, st);
-  hipError_t e = launch_prep(dv, n, nullptr, nullptr, q, 2, st);
-  if (e != hipSuccess) return e;
-  timer_mark(tm, KID_PREP, st);
   if (dv.dtype == 0)
-    query_tail<0>(dv, n, page_ids, n_pages, topk_ids, q, nullptr, st, tm);
+    query_tail<0>(dv, n, page_ids, n_pages, topk_ids, q, nullptr, nullptr, nullptr, st, tm);
   else
-    query_tail<1>(dv, n, page_ids, n_pages, topk_ids, q, nullptr, st, tm);
+    query_tail<1>(dv, n, page_ids, n_pages, topk_ids, q, nullptr, nullptr, nullptr, st, tm);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const Dev &dv, int64_t n, const void *k_new, const void *v_new,
                          const void *q, int32_t *page_ids, int32_t *n_pages, int32_t *topk_ids,
                          float *out, hipStream_t st, Timer *tm) {
-  // the new token is token n; the query sees n + 1 tokens
+  // the new token is token n (inserted by the scan); the query sees n + 1
+  // tokens.  Pages up to kFusedMaxPages and unions that fit LDS: the
+  // finaliser runs the attention itself.
   timer_begin(tm, st);
-  hipError_t e = launch_prep(dv, n, k_new, v_new, q, 3, st);
-  if (e != hipSuccess) return e;
-  timer_mark(tm, KID_PREP, st);
-  // pages up to kFusedMaxPages and unions that fit LDS: the finaliser runs the
-  // attention itself
   const bool fused = dv.P <= kFusedMaxPages && dv.L * dv.k0 <= kMaxCand;
+  float *fo = fused ? out : nullptr;
   if (dv.dtype == 0)
-    query_tail<0>(dv, n + 1, page_ids, n_pages, topk_ids, q, fused ? out : nullptr, st, tm);
+    query_tail<0>(dv, n + 1, page_ids, n_pages, topk_ids, q, k_new, v_new, fo, st, tm);
   else
-    query_tail<1>(dv, n + 1, page_ids, n_pages, topk_ids, q, fused ? out : nullptr, st, tm);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+    query_tail<1>(dv, n + 1, page_ids, n_pages, topk_ids, q, k_new, v_new, fo, st, tm);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   return fused ? hipSuccess : launch_attn(dv, q, page_ids, n_pages, out, st, tm);
 }
 
