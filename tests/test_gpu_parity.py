@@ -304,6 +304,41 @@ def test_decode_step_equals_separate_calls(B, dtype, S, g, d, p, m, L):
     assert e.value.status == B.ICE_ERR_CAPACITY
 
 
+def test_decode_step_many_streams(B):
+    """64 streams of 20,011 tokens (1,280 scan blocks, more than the device
+    holds at once; the new token in the last, ragged range of every stream):
+    decode steps match separate calls bit for bit and the oracle on two
+    streams."""
+    S, n, g, d, p, m, L, k, steps = 64, 20011, 1, 128, 16, 4, 2, 128, 3
+    dev = torch.device("cuda")
+    K, V, q0, _ = _inputs(S, n + steps, d, g, 16, 33, "bf16")
+    U = W.directions(m * L, d, 33, "bf16").to(dev)
+    print("[case] decode_step S=64 n=20011", flush=True)
+    mk = lambda: B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U,
+                         page_size=p, budget_k=k, m=m, L=L, gqa_group=g, capacity=n + steps)
+    a, b = mk(), mk()
+    gen = torch.Generator().manual_seed(9)
+    for t in range(steps):
+        qt = torch.randn(S * g, d, generator=gen).to(torch.bfloat16).to(dev)
+        kn, vn = K[:, n + t].contiguous().to(dev), V[:, n + t].contiguous().to(dev)
+        pa, na, oa, ta = a.decode_step(kn, vn, qt, with_topk=True)
+        b.insert(kn, vn)
+        pb, nb, tb = b.query_pages(qt, with_topk=True)
+        ob = b.sparse_attn(qt, pb, nb)
+        torch.cuda.synchronize()
+        assert torch.equal(pa, pb) and torch.equal(na, nb) and torch.equal(ta, tb)
+        assert torch.equal(oa, ob)
+    prm = oracle.Params(d=d, p=p, k=k, m=m, L=L, g=g)
+    for s_ in (0, 37):
+        st = oracle.OracleStream(prm, _np(K[s_, :n]), _np(V[s_, :n]), _np(U), n_cap=n + steps)
+        for t in range(steps):
+            st.insert(_np(K[s_, n + t]), _np(V[s_, n + t]))
+        q_s = _np(qt[s_ * g:(s_ + 1) * g])
+        r = st.query(q_s, literal=False)
+        _check_index(a, st, s_, n + steps)
+        _check_query(a, st, s_, r, pa, na, ta, oa[s_ * g:(s_ + 1) * g], q_s)
+
+
 def test_capacity_error(B):
     dev = torch.device("cuda")
     K, V, q, _ = _inputs(1, 40, 128, 1, 4, 13, "bf16")
