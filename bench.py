@@ -53,27 +53,33 @@ def algorithmic_bytes(w, kernel: str, ntok: float, n_cand: float, attended: floa
     """Bytes the decode path has to move per launch of `kernel` for one layer
     (S streams): the per-unit figures times the units one launch processes.
 
-    prep      insert: k, v in and their pool rows out (4*d*elem), mL list entries
-              (8 B) and codes (4 B); query: the g heads (g*d*elem), the fp32
-              directions ((d+1)*mL*4), the query codes out (4*mL)
-    qscan     every token's m*L projection codes: 4*mL per token
+    qscan     every token's m*L projection codes (4*mL per token); the query
+              prep: the g heads (g*d*elem), the query codes and q_kv out
+              (4*mL + 4*d), the fp32 directions once per layer
+              ((d+1)*mL*4); the insert of the step's token: k and v in, their
+              pool rows out (4*d*elem), mL codes and list entries out (12*mL)
     qcollect  the key row of every reranked candidate: d*elem per candidate
     qfinal    the rerank list (16 B per candidate), then (fused) the attention:
               K and V rows of every attended token (2*d*elem each), the g
               heads and their fp32 outputs
     attn      (when the finaliser does not run the attention) as above
+    insert    (the standalone ice_insert, not part of a decode step) the
+              insert's bytes as above plus the directions
     """
     S, d, mL, g = w.streams, w.d, w.mL, w.g
     elem = 2 if w.dtype == "bf16" else 4
     att = attended * 2 * d * elem + g * d * (elem + 4)
+    dirs = (d + 1) * mL * 4.0
+    insert = 4.0 * d * elem + 12.0 * mL
     per_stream = {
-        "prep": 4.0 * d * elem + 12.0 * mL + g * d * elem + (d + 1) * mL * 4.0 + 4.0 * mL,
-        "qscan": ntok * mL * 4.0,
+        "insert": insert,
+        "qscan": ntok * mL * 4.0 + g * d * elem + 4.0 * mL + 4.0 * d + insert,
         "qcollect": n_cand * d * elem,
         "qfinal": n_cand * 16.0 + (att if fused else 0.0),
         "attn": att,
     }
-    return S * per_stream.get(kernel, 0.0)
+    per_layer = {"insert": dirs, "qscan": dirs}
+    return S * per_stream.get(kernel, 0.0) + per_layer.get(kernel, 0.0)
 
 
 def cpu_baseline(w, K, V, q, U, k_new, v_new, reps: int):
@@ -255,15 +261,15 @@ def main():
     if os.path.exists(tfile):
         with open(tfile) as fh:
             tr = json.load(fh)
-        if (tr.get("source_hash") == kernel_source_hash() and tr.get("workload") == args.workload
-                and dominant in tr.get("kernels", {})):
-            traffic = tr["kernels"][dominant]
+        per_wl = tr.get("workloads", {}).get(args.workload, {})
+        if tr.get("source_hash") == kernel_source_hash() and dominant in per_wl:
+            traffic = per_wl[dominant]
     dk = kernels[dominant]
     roofline = {"bound": "hbm", "kernel": dominant, "achieved": dk["gbs"], "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": dk["frac"], "traffic": traffic, "avg_us": dk["avg_us"],
                 "alg_bytes": dk["alg_bytes"]}
     step_alg = sum(algorithmic_bytes(w, k, ntok, n_cand, attended, fused)
-                   for k in ("prep", "qscan", "qcollect", "qfinal", "attn")
+                   for k in ("qscan", "qcollect", "qfinal", "attn")
                    if fused is False or k != "attn") * layers_per_step
 
     res = {

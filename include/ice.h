@@ -197,13 +197,13 @@ typedef struct {
 ice_status ice_index_layout(const ice_index *idx, ice_layout *out);
 
 /* Per-kernel timing for benchmarks.  When enabled, every decode-time call
- * (ice_insert, ice_query_pages, ice_sparse_attn) records HIP events on its
+ * (ice_insert, ice_query_pages, ice_sparse_attn, ice_decode_step) records HIP events on its
  * stream around each kernel it launches; ice_timing_read waits for the
  * recorded events, writes the summed milliseconds and launch counts per
  * kernel (arrays of ICE_TIMED_KERNELS, in the order of ice_timing_name) and
  * clears the record.  The event records add a little time between kernels;
  * leave timing off for end-to-end latency. */
-#define ICE_TIMED_KERNELS 6 /* prep, qscan, qcollect, qfinal, attn, amerge */
+#define ICE_TIMED_KERNELS 6 /* insert, qscan, qcollect, qfinal, attn, amerge */
 ice_status ice_timing_enable(ice_index *idx, int enable);
 ice_status ice_timing_read(ice_index *idx, double *total_ms, int64_t *launches);
 const char *ice_timing_name(int kernel);

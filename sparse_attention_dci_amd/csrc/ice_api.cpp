@@ -414,7 +414,7 @@ ice_status ice_timing_read(ice_index *idx, double *total_ms, int64_t *launches) 
 }
 
 const char *ice_timing_name(int kernel) {
-  static const char *names[ICE_TIMED_KERNELS] = {"prep", "qscan", "qcollect",
+  static const char *names[ICE_TIMED_KERNELS] = {"insert", "qscan", "qcollect",
                                                  "qfinal", "attn", "amerge"};
   return (kernel >= 0 && kernel < ICE_TIMED_KERNELS) ? names[kernel] : "";
 }

@@ -93,9 +93,9 @@ struct BuildScratch {
 };
 
 // Decode-time kernels that the optional event timer reports separately.
-// KID_PREP is the standalone insert; a decode step's insert and query prep
-// run inside the scan.
-enum KernelId { KID_PREP = 0, KID_QSCAN, KID_QCOLLECT, KID_QFINAL, KID_ATTN, KID_AMERGE,
+// KID_INSERT is the standalone insert; a decode step's insert and query prep
+// run inside the scan and are timed with it.
+enum KernelId { KID_INSERT = 0, KID_QSCAN, KID_QCOLLECT, KID_QFINAL, KID_ATTN, KID_AMERGE,
                 KID_COUNT };
 
 // Optional host-side event timer (owned by an index); null when timing is off.

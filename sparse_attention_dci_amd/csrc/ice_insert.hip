@@ -79,7 +79,7 @@ hipError_t launch_insert(const Dev &dv, int64_t n, const void *k_new, const void
     hipLaunchKernelGGL(k_insert<0>, dim3(dv.S), dim3(kInsThreads), 0, st, dv, n, k_new, v_new);
   else
     hipLaunchKernelGGL(k_insert<1>, dim3(dv.S), dim3(kInsThreads), 0, st, dv, n, k_new, v_new);
-  timer_mark(tm, KID_PREP, st);
+  timer_mark(tm, KID_INSERT, st);
   return hipGetLastError();
 }
 
