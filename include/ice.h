@@ -101,6 +101,8 @@ size_t ice_build_scratch_bytes(const ice_params *prm, int32_t n_streams, int64_t
  * pool holding a copy of every key and value at its page slot.
  * K, V and dirs are read only by work enqueued here; once it has finished the
  * caller may free them.  The workspace must outlive the index.
+ * n_tokens above 2^24 per stream: ICE_ERR_UNSUPPORTED (later inserts may grow
+ * the index to capacity_tokens).
  * On success *out receives a new handle. */
 ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_tokens,
                            int64_t capacity_tokens, const void *K, const void *V,

@@ -114,6 +114,7 @@ ice_status check_params(const ice_params *prm, int32_t S, int64_t n, int64_t nca
   if (prm->L > 32) return ICE_ERR_UNSUPPORTED;
   const int64_t k0 = prm->k0 > 0 ? prm->k0 : prm->budget_k;
   if (k0 * prm->L > ice::kMaxCandBig) return ICE_ERR_UNSUPPORTED;
+  if (n > (int64_t)ice::kPageChunk * 16384) return ICE_ERR_UNSUPPORTED;  // build's chunk counters
   return ICE_OK;
 }
 
@@ -177,14 +178,25 @@ ice_status make_layout(const ice_params *prm, int32_t S, int64_t n, int64_t ncap
   return ICE_OK;
 }
 
-int64_t scratch_size(const ice_params *prm, int32_t S, int64_t n) {
+// Offsets of the build scratch arrays (ice::BuildScratch order); returns the total.
+int64_t scratch_offsets(const ice_params *prm, int32_t S, int64_t n, int64_t off[9]) {
   const int64_t mL = (int64_t)prm->m * prm->L;
+  const int64_t cmax = (int64_t)1 << (mL < ice::kMaxTreeDepth ? mL : ice::kMaxTreeDepth);
+  const int64_t nchunk = (n + ice::kPageChunk - 1) / ice::kPageChunk;
+  const int64_t sz[9] = {S * mL * n * 4,         S * mL * n * 4,          S * mL * n * 4,
+                         S * n * 4,              S * nchunk * cmax * 4,   S * n * 4,
+                         S * (nchunk + 1) * 4,   S * (cmax + 1) * 4,      S * (n / 8 + cmax + 1) * 4};
   int64_t o = 0;
-  o = align_up(o + (int64_t)S * mL * n * 4);  // codes_dm
-  o = align_up(o + (int64_t)S * mL * n * 4);  // tmp_code
-  o = align_up(o + (int64_t)S * mL * n * 4);  // tmp_id
-  o = align_up(o + (int64_t)S * n * 4);       // cell
+  for (int i = 0; i < 9; ++i) {
+    off[i] = o;
+    o = align_up(o + sz[i]);
+  }
   return o;
+}
+
+int64_t scratch_size(const ice_params *prm, int32_t S, int64_t n) {
+  int64_t off[9];
+  return scratch_offsets(prm, S, n, off);
 }
 
 bool aligned(const void *ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
@@ -308,15 +320,17 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
   std::memset(&bs, 0, sizeof(bs));
   if (n_tokens > 0) {
     char *sc = (char *)scratch;
-    const int64_t mL = dv.mL;
-    int64_t o = 0;
-    bs.codes_dm = (int32_t *)(sc + o);
-    o = align_up(o + (int64_t)n_streams * mL * n_tokens * 4);
-    bs.tmp_code = (int32_t *)(sc + o);
-    o = align_up(o + (int64_t)n_streams * mL * n_tokens * 4);
-    bs.tmp_id = (int32_t *)(sc + o);
-    o = align_up(o + (int64_t)n_streams * mL * n_tokens * 4);
-    bs.cell = (uint32_t *)(sc + o);
+    int64_t off[9];
+    scratch_offsets(prm, n_streams, n_tokens, off);
+    bs.codes_dm = (int32_t *)(sc + off[0]);
+    bs.tmp_code = (int32_t *)(sc + off[1]);
+    bs.tmp_id = (int32_t *)(sc + off[2]);
+    bs.cell = (uint32_t *)(sc + off[3]);
+    bs.chunk_cnt = (int32_t *)(sc + off[4]);
+    bs.rank = (int32_t *)(sc + off[5]);
+    bs.chunk_pg = (int32_t *)(sc + off[6]);
+    bs.cell_pg = (int32_t *)(sc + off[7]);
+    bs.page_of = (int32_t *)(sc + off[8]);
   }
   hipError_t e = ice::launch_build(dv, bs, n_tokens, K, V, dirs, prm->c, (hipStream_t)stream);
   if (e != hipSuccess) {

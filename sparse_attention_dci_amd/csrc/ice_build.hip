@@ -282,85 +282,200 @@ __global__ __launch_bounds__(256) void k_sort_lists(Dev dv, BuildScratch bs, int
 
 // ---------------------------------------------------------------- pages
 
-// One wave per stream walks the tokens in order, 64 at a time, and applies
-// the insert rule to each: a token takes the next slot of its cell's open
-// page, and a token whose in-cell rank is a multiple of p opens the next page
-// number.  Tokens of the same cell inside one step are ranked with ballots,
-// and a token whose page opens in the same step finds the opener's lane.
-// The result is the cells' tokens, in token order, cut into pages of p and
-// numbered by first token.
-__global__ __launch_bounds__(64) void k_pages(Dev dv, BuildScratch bs, int64_t n) {
-  extern __shared__ int32_t lds[];
-  int32_t *cnt = lds;
-  int32_t *open = lds + dv.ncell;
-  constexpr int kAhead = 16;  // tiles of cells loaded per batch
-  const int s = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int p = dv.p;
-  for (int64_t c = lane; c < dv.ncell; c += 64) {
-    cnt[c] = 0;
-    open[c] = -1;
-  }
+// The tree's leaves as pages: each cell's tokens, in token order, cut into
+// pages of p, pages numbered by their first token (which is what inserting
+// the tokens one by one gives).  In parallel over chunks of kPageChunk tokens:
+//   k_cell_count   per chunk, the tokens of each cell (LDS histogram);
+//   k_cell_scan    per cell (a lane) and stream, the count of the cell in all
+//                  earlier chunks (four waves split the chunks, then pass the
+//                  carry), the cell totals and page counts, and per chunk the
+//                  pages its tokens open (the ranks that are multiples of p);
+//   k_page_prefix  per stream, the prefix sums of those: every chunk's first
+//                  page id, every cell's first entry in the page_of table;
+//   k_cell_rank    one wave per chunk walks it 64 tokens at a time: a token's
+//                  rank in its cell = its cell's count before the chunk + the
+//                  same-cell tokens before it in the chunk (ballots); openers
+//                  (rank a multiple of p) number their pages;
+//   k_page_fill    every token's page and slot from its rank.
+
+__global__ __launch_bounds__(256) void k_cell_count(Dev dv, BuildScratch bs, int64_t n, int cmax) {
+  extern __shared__ int32_t hc[];
+  const int s = blockIdx.y;
+  const int64_t k = blockIdx.x, nchunk = gridDim.x;
+  const int ncell = (int)dv.ncell;
+  for (int c = threadIdx.x; c < ncell; c += 256) hc[c] = 0;
   __syncthreads();
-  int32_t npg = 0;
-  const unsigned long long lt = lanemask_lt();
   const uint32_t *cells = bs.cell + (int64_t)s * n;
-  uint32_t cur[kAhead], nxt[kAhead];
+  const int64_t i0 = k * kPageChunk;
+  for (int64_t i = i0 + threadIdx.x; i < min(i0 + kPageChunk, n); i += 256)
+    atomicAdd(&hc[cells[i]], 1);
+  __syncthreads();
+  int32_t *out = bs.chunk_cnt + ((int64_t)s * nchunk + k) * cmax;
+  for (int c = threadIdx.x; c < ncell; c += 256) out[c] = hc[c];
+}
+
+// grid (ceil(ncell / 64), S), 256 threads; LDS: nchunk counters
+__global__ __launch_bounds__(256) void k_cell_scan(Dev dv, BuildScratch bs, int64_t nchunk,
+                                                   int cmax) {
+  extern __shared__ int32_t opk[];
+  __shared__ int32_t qsum[4][64];
+  constexpr int B = 16;
+  const int s = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int ncell = (int)dv.ncell, p = dv.p;
+  const int c = blockIdx.x * 64 + lane;
+  const bool cv = c < ncell;
+  const int cl = cv ? c : 0;
+  int32_t *cc = bs.chunk_cnt + (int64_t)s * nchunk * cmax;
+  for (int64_t k = tid; k < nchunk; k += 256) opk[k] = 0;
+  const int64_t q0 = nchunk * w / 4, q1 = nchunk * (w + 1) / 4;
+  int32_t sum = 0;
+  for (int64_t k0 = q0; k0 < q1; k0 += B) {  // this wave's quarter: its sum
+    int32_t x[B];
 #pragma unroll
-  for (int k = 0; k < kAhead; ++k) {  // clamped, unconditional loads
-    const int64_t i = 64 * k + lane;
-    cur[k] = cells[i < n ? i : 0];
+    for (int j = 0; j < B; ++j) x[j] = cc[min(k0 + j, q1 - 1) * cmax + cl];
+#pragma unroll
+    for (int j = 0; j < B; ++j) sum += k0 + j < q1 ? x[j] : 0;
   }
-  for (int64_t b0 = 0; b0 < n; b0 += 64 * kAhead) {
+  qsum[w][lane] = sum;
+  __syncthreads();
+  int32_t tot = 0;
+  for (int u = 0; u < w; ++u) tot += qsum[u][lane];
+  for (int64_t k0 = q0; k0 < q1; k0 += B) {  // counts before each chunk; pages opened
+    int32_t x[B];
 #pragma unroll
-    for (int k = 0; k < kAhead; ++k) {
-      const int64_t i = b0 + 64 * (kAhead + k) + lane;
-      nxt[k] = cells[i < n ? i : 0];
+    for (int j = 0; j < B; ++j) x[j] = cc[min(k0 + j, q1 - 1) * cmax + cl];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      if (k0 + j < q1 && cv) {
+        cc[(k0 + j) * cmax + c] = tot;
+        const int32_t opened = (tot + x[j] + p - 1) / p - (tot + p - 1) / p;
+        if (opened) atomicAdd(&opk[k0 + j], opened);
+        tot += x[j];
+      }
     }
-#pragma unroll
-    for (int k = 0; k < kAhead; ++k) {
-      const int64_t i = b0 + 64 * k + lane;
-      const bool valid = i < n;
-      const uint32_t c = valid ? cur[k] : 0u;
-      const unsigned long long act = __ballot(valid);
-      const unsigned long long mt = match_bits(c, dv.D, act);
-      const int base = valid ? cnt[c] : 0;
-      const int prev_open = valid ? open[c] : -1;
-      const int rank = base + popc64(mt & lt);
-      const int slot = rank & (p - 1);
-      const bool first = valid && slot == 0;
-      const unsigned long long fm = __ballot(first);
-      const int cs = rank - slot;
-      int pid;
-      if (cs >= base) {
-        const int fl = valid ? nth_set_bit(mt, cs - base) : 0;
-        pid = npg + popc64(fm & ((1ull << fl) - 1ull));
-      } else {
-        pid = prev_open;
-      }
-      const bool leader = valid && ((mt >> lane) >> 1) == 0ull;
-      __builtin_amdgcn_wave_barrier();
-      if (leader) {
-        cnt[c] = rank + 1;
-        open[c] = pid;
-      }
-      npg += popc64(fm);
-      if (valid) {
-        dv.loc[(int64_t)s * dv.ncap + i] = pid * p + slot;
-        dv.page_tokens[((int64_t)s * dv.pcap + pid) * p + slot] = (int32_t)i;
-        if (first) dv.page_cell[(int64_t)s * dv.pcap + pid] = (int32_t)c;
-        if (slot == p - 1 || leader) dv.page_len[(int64_t)s * dv.pcap + pid] = slot + 1;
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-#pragma unroll
-    for (int k = 0; k < kAhead; ++k) cur[k] = nxt[k];
   }
   __syncthreads();
-  if (lane == 0) dv.npages[s] = npg;
-  for (int64_t c = lane; c < dv.ncell; c += 64) {
-    dv.cell_count[(int64_t)s * dv.ncell + c] = cnt[c];
-    dv.cell_last[(int64_t)s * dv.ncell + c] = open[c];
+  for (int64_t k = tid; k < nchunk; k += 256)
+    if (opk[k]) atomicAdd(&bs.chunk_pg[(int64_t)s * (nchunk + 1) + k], opk[k]);
+  if (w == 0 && cv) {
+    const int32_t total = qsum[0][lane] + qsum[1][lane] + qsum[2][lane] + qsum[3][lane];
+    dv.cell_count[(int64_t)s * ncell + c] = total;
+    if (total == 0) dv.cell_last[(int64_t)s * ncell + c] = -1;
+    bs.cell_pg[(int64_t)s * (cmax + 1) + c] = (total + p - 1) / p;
+  }
+}
+
+// Exclusive prefix of x[0..m) in place (one 1024-thread block); returns the total.
+__device__ int32_t block_prefix_1024(int32_t *x, int64_t m, int32_t *wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t per = (m + 1023) / 1024;
+  const int64_t b = tid * per, e = min(b + per, m);
+  int32_t loc = 0;
+  for (int64_t i = b; i < e; ++i) loc += x[i];
+  int32_t incl = loc;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int32_t pre = 0, tot = 0;
+  for (int u = 0; u < 16; ++u) {
+    if (u < w) pre += wsum[u];
+    tot += wsum[u];
+  }
+  int32_t run = pre + incl - loc;
+  for (int64_t i = b; i < e; ++i) {
+    const int32_t v = x[i];
+    x[i] = run;
+    run += v;
+  }
+  __syncthreads();
+  return tot;
+}
+
+__global__ __launch_bounds__(1024) void k_page_prefix(Dev dv, BuildScratch bs, int64_t nchunk,
+                                                      int cmax) {
+  __shared__ int32_t wsum[16];
+  const int s = blockIdx.x;
+  int32_t *cpg = bs.cell_pg + (int64_t)s * (cmax + 1);
+  const int32_t tc = block_prefix_1024(cpg, dv.ncell, wsum);
+  if (threadIdx.x == 0) cpg[dv.ncell] = tc;
+  int32_t *kpg = bs.chunk_pg + (int64_t)s * (nchunk + 1);
+  const int32_t tk = block_prefix_1024(kpg, nchunk, wsum);
+  if (threadIdx.x == 0) {
+    kpg[nchunk] = tk;
+    dv.npages[s] = tk;
+  }
+}
+
+// grid (nchunk, S), one wave; LDS: ncell counters
+__global__ __launch_bounds__(64) void k_cell_rank(Dev dv, BuildScratch bs, int64_t n, int cmax) {
+  extern __shared__ int32_t cnt[];
+  constexpr int kSteps = kPageChunk / 64;
+  const int s = blockIdx.y;
+  const int64_t k = blockIdx.x, nchunk = gridDim.x;
+  const int lane = threadIdx.x;
+  const int ncell = (int)dv.ncell, p = dv.p;
+  const int32_t *cpg = bs.cell_pg + (int64_t)s * (cmax + 1);
+  const uint32_t *cells = bs.cell + (int64_t)s * n;
+  const int64_t i0 = k * kPageChunk, i1 = min(i0 + kPageChunk, n);
+  // loads first: the chunk's cells, their page_of offsets, the counts before the chunk
+  uint32_t cv[kSteps];
+  int32_t po[kSteps];
+#pragma unroll
+  for (int j = 0; j < kSteps; ++j) cv[j] = cells[min(i0 + 64 * j + lane, n - 1)];
+#pragma unroll
+  for (int j = 0; j < kSteps; ++j) po[j] = cpg[cv[j]];
+  const int32_t *base = bs.chunk_cnt + ((int64_t)s * nchunk + k) * cmax;
+  for (int c = lane; c < ncell; c += 64) cnt[c] = base[c];
+  const int32_t pg0 = bs.chunk_pg[(int64_t)s * (nchunk + 1) + k];
+  int32_t *pof = bs.page_of + (int64_t)s * (n / 8 + cmax + 1);
+  __syncthreads();
+  const unsigned long long lt = lanemask_lt();
+  int32_t opened = 0;
+#pragma unroll
+  for (int j = 0; j < kSteps; ++j) {
+    const int64_t i = i0 + 64 * j + lane;
+    const bool valid = i < i1;
+    const uint32_t c = cv[j];
+    const unsigned long long mt = match_bits(c, dv.D, __ballot(valid));
+    const int32_t rank = valid ? cnt[c] + popc64(mt & lt) : 0;
+    const bool first = valid && rank % p == 0;
+    const unsigned long long fm = __ballot(first);
+    if (first) {
+      const int32_t pid = pg0 + opened + popc64(fm & lt);
+      pof[po[j] + rank / p] = pid;
+      dv.page_cell[(int64_t)s * dv.pcap + pid] = (int32_t)c;
+    }
+    if (valid) bs.rank[(int64_t)s * n + i] = rank;
+    __builtin_amdgcn_wave_barrier();
+    if (valid && ((mt >> lane) >> 1) == 0ull) cnt[c] = rank + 1;  // the cell's last lane
+    opened += popc64(fm);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+__global__ __launch_bounds__(256) void k_page_fill(Dev dv, BuildScratch bs, int64_t n, int cmax) {
+  const int s = blockIdx.y;
+  const int p = dv.p, ncell = (int)dv.ncell;
+  const int32_t *cpg = bs.cell_pg + (int64_t)s * (cmax + 1);
+  const int32_t *pof = bs.page_of + (int64_t)s * (n / 8 + cmax + 1);
+  const int32_t *ccount = dv.cell_count + (int64_t)s * ncell;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const uint32_t c = bs.cell[(int64_t)s * n + i];
+    const int32_t rank = bs.rank[(int64_t)s * n + i];
+    const int32_t pid = pof[cpg[c] + rank / p], slot = rank % p;
+    dv.loc[(int64_t)s * dv.ncap + i] = pid * p + slot;
+    dv.page_tokens[((int64_t)s * dv.pcap + pid) * p + slot] = (int32_t)i;
+    if (slot == 0) dv.page_len[(int64_t)s * dv.pcap + pid] = min(p, ccount[c] - rank);
+  }
+  // each non-empty cell's last page
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < ncell;
+       c += (int64_t)gridDim.x * 256) {
+    const int32_t cnt = ccount[c];
+    if (cnt > 0) dv.cell_last[(int64_t)s * ncell + c] = pof[cpg[c] + (cnt - 1) / p];
   }
 }
 
@@ -463,8 +578,26 @@ static hipError_t build_impl(const Dev &dv, const BuildScratch &bs, int64_t n, c
     hipLaunchKernelGGL(k_project<DT>, dim3(1, 1, dv.S), dim3(256), 0, st, dv, bs, K,
                        (const double *)dv.dirs, n, c_fixed);
   }
-  hipLaunchKernelGGL(k_pages, dim3(dv.S), dim3(64), (size_t)dv.ncell * 2 * sizeof(int32_t), st,
-                     dv, bs, n);
+  if (n > 0) {
+    const int64_t nchunk = (n + kPageChunk - 1) / kPageChunk;
+    const int cmax = 1 << min(dv.mL, kMaxTreeDepth);
+    const size_t lds = (size_t)dv.ncell * sizeof(int32_t);
+    hipLaunchKernelGGL(k_cell_count, dim3((unsigned)nchunk, dv.S), dim3(256), lds, st, dv, bs, n,
+                       cmax);
+    if ((e = fill_i32(bs.chunk_pg, (int64_t)dv.S * (nchunk + 1), 0, st))) return e;
+    hipLaunchKernelGGL(k_cell_scan, dim3((unsigned)((dv.ncell + 63) / 64), dv.S), dim3(256),
+                       (size_t)nchunk * sizeof(int32_t), st, dv, bs, nchunk, cmax);
+    hipLaunchKernelGGL(k_page_prefix, dim3(dv.S), dim3(1024), 0, st, dv, bs, nchunk, cmax);
+    hipLaunchKernelGGL(k_cell_rank, dim3((unsigned)nchunk, dv.S), dim3(64), lds, st, dv, bs, n,
+                       cmax);
+    int64_t fb = (n + 255) / 256;
+    if (fb > 4096) fb = 4096;
+    hipLaunchKernelGGL(k_page_fill, dim3((unsigned)fb, dv.S), dim3(256), 0, st, dv, bs, n, cmax);
+  } else {  // no tokens: no pages, empty cells
+    if ((e = fill_i32(dv.npages, dv.S, 0, st))) return e;
+    if ((e = fill_i32(dv.cell_count, (int64_t)dv.S * dv.ncell, 0, st))) return e;
+    if ((e = fill_i32(dv.cell_last, (int64_t)dv.S * dv.ncell, -1, st))) return e;
+  }
   if (n > 0) {
     const int64_t total = (int64_t)dv.S * n * ((int64_t)dv.d * dv.elem / 16);
     int64_t blocks = (total + 255) / 256;

@@ -90,7 +90,16 @@ struct BuildScratch {
   int32_t *tmp_code;  // [S][mL][n]
   int32_t *tmp_id;    // [S][mL][n]
   uint32_t *cell;     // [S][n]
+  // page assignment (chunks of kPageChunk tokens, cmax = 2^min(mL, 13) cells)
+  int32_t *chunk_cnt;   // [S][nchunk][cmax] tokens of each cell per chunk, then their prefix
+  int32_t *rank;        // [S][n] a token's rank among its cell's tokens
+  int32_t *chunk_pg;    // [S][nchunk + 1] pages opened per chunk, then their prefix
+  int32_t *cell_pg;     // [S][cmax + 1] prefix of the cells' page counts
+  int32_t *page_of;     // [S][n / 8 + cmax + 1] page id by (cell_pg[c] + ordinal in the cell)
 };
+
+// Tokens per chunk of the build's page assignment.
+constexpr int kPageChunk = 1024;
 
 // Decode-time kernels that the optional event timer reports separately.
 // KID_INSERT is the standalone insert; a decode step's insert and query prep

@@ -91,6 +91,16 @@ def test_unsupported_settings(L):
         assert st == B.ICE_ERR_UNSUPPORTED
 
 
+def test_build_size_limit(L):
+    """Builds of more than 2^24 tokens per stream are refused before any launch."""
+    p = good()
+    big = (1 << 24) + 1
+    assert L.ice_workspace_bytes(ctypes.byref(p), 1, big, big) == 0
+    assert L.ice_build_scratch_bytes(ctypes.byref(p), 1, big) == 0
+    p64 = good(page_size=64, budget_k=256)
+    assert L.ice_workspace_bytes(ctypes.byref(p64), 1, 1 << 20, 1 << 20) > 0
+
+
 def test_build_argument_checks(L):
     p = good()
     ws = L.ice_workspace_bytes(ctypes.byref(p), 2, 1000, 1000)
