@@ -193,13 +193,24 @@ __device__ __forceinline__ uint32_t block_excl_scan256(uint32_t v, uint32_t *wsu
 // of the code.  Pass 0 reads the direction-major codes with implicit tokens;
 // passes alternate between the scratch pair and the index lists, ending in
 // the index lists.  The four digit histograms come from one initial pass (a
-// pass never changes the multiset of keys).  Inside a pass, tiles of 256
-// entries are ranked in entry order: lanes with the same digit are matched
-// with ballots, waves are ordered through per-wave digit counts; the loads of
-// kSortGroup tiles are issued together.
-constexpr int kSortGroup = 16;
+// pass never changes the multiset of keys).  A pass walks the list in tiles
+// of 256 x ITEMS entries; wave w owns the tile's w-th quarter, row j of it
+// being 64 consecutive entries:
+//   ranks  row by row, lanes with equal digits are matched with ballots and
+//          ranked after the wave's running count of that digit (LDS, updated
+//          by each digit's last lane); the four waves' counts, prefix-summed
+//          per digit, and the digits' starts in the tile complete every
+//          entry's stable rank within the tile;
+//   stage  the tile is written to LDS in digit order;
+//   write  consecutive threads copy consecutive staged entries to their
+//          digit's running position in the output, so each digit's run goes
+//          out as one coalesced stretch instead of one scattered word per
+//          entry.
+constexpr int kSortItems = 16;
 
+template <int ITEMS>
 __global__ __launch_bounds__(256) void k_sort_lists(Dev dv, BuildScratch bs, int64_t n) {
+  constexpr int NT = 256, TILE = NT * ITEMS, QUARTER = TILE / 4;
   const int lst = blockIdx.x;  // s * mL + t
   const int s = lst / dv.mL, t = lst % dv.mL;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -209,22 +220,20 @@ __global__ __launch_bounds__(256) void k_sort_lists(Dev dv, BuildScratch bs, int
   int32_t *oc = dv.list_code + ((int64_t)s * dv.mL + t) * dv.ncap;
   int32_t *oi = dv.list_id + ((int64_t)s * dv.mL + t) * dv.ncap;
 
-  __shared__ uint32_t cnt[4][256];
-  __shared__ uint32_t base[256];
-  __shared__ uint32_t wcnt[4][256];
-  __shared__ uint32_t woff[4][256];
+  __shared__ uint32_t ghist[4][256];
+  __shared__ uint32_t gbase[256], ls[256];
+  __shared__ uint32_t cntw[4][256];
+  __shared__ uint32_t skey[TILE];
+  __shared__ int32_t sval[TILE];
   __shared__ uint32_t wsum[4];
 
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    cnt[k][tid] = 0;
-    wcnt[k][tid] = 0;
-  }
+  for (int k = 0; k < 4; ++k) ghist[k][tid] = 0;
   __syncthreads();
-  for (int64_t x = tid; x < n; x += 256) {
+  for (int64_t x = tid; x < n; x += NT) {
     const uint32_t key = (uint32_t)in0[x] ^ 0x80000000u;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) atomicAdd(&cnt[k][(key >> (8 * k)) & 255u], 1u);
+    for (int k = 0; k < 4; ++k) atomicAdd(&ghist[k][(key >> (8 * k)) & 255u], 1u);
   }
   __syncthreads();
   const unsigned long long lt = lanemask_lt();
@@ -235,46 +244,70 @@ __global__ __launch_bounds__(256) void k_sort_lists(Dev dv, BuildScratch bs, int
     const int32_t *si = pass == 0 ? nullptr : ((pass & 1) ? ti : oi);
     int32_t *dc = (pass & 1) ? oc : tc;
     int32_t *di = (pass & 1) ? oi : ti;
-    base[tid] = block_excl_scan256(cnt[pass][tid], wsum);
-    __syncthreads();
+    gbase[tid] = block_excl_scan256(ghist[pass][tid], wsum);
 
-    for (int64_t g0 = 0; g0 < n; g0 += 256 * kSortGroup) {
-      int32_t gc[kSortGroup], gi[kSortGroup];
+    for (int64_t t0 = 0; t0 < n; t0 += TILE) {
+      const int nv = (int)min((int64_t)TILE, n - t0);
+      uint32_t key[ITEMS];
+      int32_t val[ITEMS];
 #pragma unroll
-      for (int k = 0; k < kSortGroup; ++k) {  // clamped, unconditional loads
-        const int64_t x = g0 + 256 * k + tid;
-        const int64_t xc = x < n ? x : 0;
-        gc[k] = sc[xc];
-        gi[k] = si ? si[xc] : (int32_t)x;
+      for (int j = 0; j < ITEMS; ++j) {  // clamped, unconditional loads
+        const int64_t x = t0 + w * QUARTER + j * 64 + lane;
+        const int64_t xc = x < n ? x : n - 1;
+        key[j] = (uint32_t)sc[xc] ^ 0x80000000u;
+        val[j] = si ? si[xc] : (int32_t)x;
       }
 #pragma unroll
-      for (int k = 0; k < kSortGroup; ++k) {
-        const int64_t x = g0 + 256 * k + tid;
-        const bool valid = x < n;
-        const uint32_t dig = valid ? ((((uint32_t)gc[k] ^ 0x80000000u) >> shift) & 255u) : 0u;
-        const unsigned long long act = __ballot(valid);
-        const unsigned long long mt = match_bits(dig, 8, act);
-        const int lrank = popc64(mt & lt);
-        const bool leader = valid && ((mt >> lane) >> 1) == 0ull;
-        if (leader) wcnt[w][dig] = (uint32_t)popc64(mt);
-        __syncthreads();
-        {
-          uint32_t o = base[tid];
+      for (int q = 0; q < 4; ++q) cntw[w][q * 64 + lane] = 0;
+      __builtin_amdgcn_wave_barrier();
+      // ranks inside the wave's quarter, row by row
+      uint32_t rank[ITEMS];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            woff[q][tid] = o;
-            o += wcnt[q][tid];
-            wcnt[q][tid] = 0;
-          }
-          base[tid] = o;
-        }
-        __syncthreads();
-        if (valid) {
-          const uint32_t pos = woff[w][dig] + (uint32_t)lrank;
-          dc[pos] = gc[k];
-          di[pos] = gi[k];
+      for (int j = 0; j < ITEMS; ++j) {
+        const bool valid = w * QUARTER + j * 64 + lane < nv;
+        const uint32_t dig = (key[j] >> shift) & 255u;
+        const unsigned long long mt = match_bits(dig, 8, __ballot(valid));
+        const uint32_t before = valid ? cntw[w][dig] : 0u;
+        rank[j] = before + (uint32_t)popc64(mt & lt);
+        __builtin_amdgcn_wave_barrier();
+        if (valid && ((mt >> lane) >> 1) == 0ull) cntw[w][dig] = before + (uint32_t)popc64(mt);
+        __builtin_amdgcn_wave_barrier();
+      }
+      __syncthreads();
+      // per digit: the waves' offsets, the tile count and the digit's start
+      const uint32_t c0 = cntw[0][tid], c1 = cntw[1][tid], c2 = cntw[2][tid], c3 = cntw[3][tid];
+      const uint32_t run = c0 + c1 + c2 + c3;
+      cntw[0][tid] = 0;
+      cntw[1][tid] = c0;
+      cntw[2][tid] = c0 + c1;
+      cntw[3][tid] = c0 + c1 + c2;
+      ls[tid] = block_excl_scan256(run, wsum);  // (barriers inside)
+      __syncthreads();
+      // stage in digit order
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j) {
+        if (w * QUARTER + j * 64 + lane < nv) {
+          const uint32_t dig = (key[j] >> shift) & 255u;
+          const uint32_t pos = ls[dig] + cntw[w][dig] + rank[j];
+          skey[pos] = key[j];
+          sval[pos] = val[j];
         }
       }
+      __syncthreads();
+      // write each digit's run out contiguously
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j) {
+        const int x = j * NT + tid;
+        if (x < nv) {
+          const uint32_t k2 = skey[x];
+          const uint32_t dig = (k2 >> shift) & 255u;
+          const uint32_t gpos = gbase[dig] + (uint32_t)x - ls[dig];
+          dc[gpos] = (int32_t)(k2 ^ 0x80000000u);
+          di[gpos] = sval[x];
+        }
+      }
+      __syncthreads();
+      gbase[tid] += run;
     }
     __syncthreads();
   }
@@ -572,7 +605,7 @@ static hipError_t build_impl(const Dev &dv, const BuildScratch &bs, int64_t n, c
       hipLaunchKernelGGL(k_norms<DT>, dim3(nb, dv.S), dim3(256), 0, st, dv, K, n);
     hipLaunchKernelGGL(k_project<DT>, dim3(nb, dv.nchunk, dv.S), dim3(256), 0, st, dv, bs, K,
                        (const double *)dv.dirs, n, c_fixed);
-    hipLaunchKernelGGL(k_sort_lists, dim3(dv.S * dv.mL), dim3(256), 0, st, dv, bs, n);
+    hipLaunchKernelGGL(k_sort_lists<kSortItems>, dim3(dv.S * dv.mL), dim3(256), 0, st, dv, bs, n);
   } else {
     // an empty build still fixes c, 1/c and 1/c^2
     hipLaunchKernelGGL(k_project<DT>, dim3(1, 1, dv.S), dim3(256), 0, st, dv, bs, K,
