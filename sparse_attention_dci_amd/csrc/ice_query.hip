@@ -104,7 +104,46 @@ __device__ __forceinline__ void wave_find_bin(const uint32_t *h, uint32_t target
 // many tokens as ROWBYTES of LDS holds, their key rows are staged in LDS
 // (slot_of(j) gives token j's page slot), then one thread per row runs the
 // ordered chain.  emit(j, slot, score) receives each result.  lcs needs
-// ROWBYTES / 128 entries.
+// ROWBYTES / 128 entries.  Rows are stored word-major with an odd stride
+// (word w of row r at w * (cap + 1) + r), so the chain's reads, one row per
+// lane, fall in distinct banks; the reads run a batch of 8 words ahead of the
+// dependent fma chain (two register sets, as in dot_chain).
+template <int DT>
+__device__ __forceinline__ double row_chain(const float *qkv, const uint32_t *rw, int stride,
+                                            int words) {
+  constexpr int B = 8;
+  uint32_t r0[B], r1[B];
+  float q0[2 * B], q1[2 * B];
+  auto rd = [&](uint32_t (&r)[B], float (&qq)[2 * B], int w0) {
+#pragma unroll
+    for (int j = 0; j < B; ++j) r[j] = rw[(w0 + j) * stride];
+#pragma unroll
+    for (int j = 0; j < (DT == 0 ? B : 2 * B); ++j) qq[j] = qkv[(DT == 0 ? w0 : 2 * w0) + j];
+  };
+  auto sum = [](double acc, const uint32_t (&r)[B], const float (&qq)[2 * B]) {
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      if constexpr (DT == 0) {
+        acc = fma((double)qq[j], (double)__uint_as_float(r[j]), acc);
+      } else {
+        acc = fma((double)qq[2 * j], (double)__uint_as_float(r[j] << 16), acc);
+        acc = fma((double)qq[2 * j + 1], (double)__uint_as_float(r[j] & 0xffff0000u), acc);
+      }
+    }
+    return acc;
+  };
+  rd(r0, q0, 0);
+  double acc = 0.0;
+#pragma unroll 1
+  for (int w0 = 0; w0 < words; w0 += 2 * B) {
+    rd(r1, q1, w0 + B);
+    acc = sum(acc, r0, q0);
+    rd(r0, q0, min(w0 + 2 * B, words - B));
+    acc = sum(acc, r1, q1);
+  }
+  return acc;
+}
+
 template <int DT, int NT, int ROWBYTES, typename SlotOf, typename Emit>
 __device__ void block_score(const Dev &dv, int s, uint32_t cnt, SlotOf slot_of, const float *qkv,
                             int32_t *lcs, uint32_t *rows, Emit emit) {
@@ -112,7 +151,9 @@ __device__ void block_score(const Dev &dv, int s, uint32_t cnt, SlotOf slot_of, 
   const int d = dv.d;
   const int row_bytes = d * dv.elem;
   const int row_words = row_bytes / 4;
-  const uint32_t cap = ROWBYTES / row_bytes;  // rows per round (<= NT)
+  const uint32_t fit = (ROWBYTES / (row_bytes + 4)) & ~1u;
+  const uint32_t cap = fit < (uint32_t)NT ? fit : NT;  // rows per round, even
+  const int stride = (int)cap + 1;                      // odd
   const int cpr = row_bytes / 16;             // 16-byte chunks per row
   constexpr int kIter = (ROWBYTES / 16 + NT - 1) / NT;
   for (uint32_t b0 = 0; b0 < cnt; b0 += cap) {
@@ -132,25 +173,16 @@ __device__ void block_score(const Dev &dv, int s, uint32_t cnt, SlotOf slot_of, 
     for (int k = 0; k < kIter; ++k) {
       const int x = tid + NT * k;
       const int r = x / cpr, c = x % cpr;
-      if ((uint32_t)r < nr) reinterpret_cast<uint4 *>(rows + r * row_words)[c] = v[k];
+      if ((uint32_t)r < nr) {
+        uint32_t *dst = rows + (4 * c) * stride + r;
+        dst[0] = v[k].x;
+        dst[stride] = v[k].y;
+        dst[2 * stride] = v[k].z;
+        dst[3 * stride] = v[k].w;
+      }
     }
     lds_barrier();
-    if ((uint32_t)tid < nr) {
-      const uint32_t *rw = rows + tid * row_words;
-      double acc = 0.0;
-      if constexpr (DT == 0) {
-#pragma unroll 16
-        for (int e = 0; e < d; ++e) acc = fma((double)qkv[e], (double)__uint_as_float(rw[e]), acc);
-      } else {
-#pragma unroll 8
-        for (int e2 = 0; e2 < d / 2; ++e2) {
-          const uint32_t wv = rw[e2];
-          acc = fma((double)qkv[2 * e2], (double)__uint_as_float(wv << 16), acc);
-          acc = fma((double)qkv[2 * e2 + 1], (double)__uint_as_float(wv & 0xffff0000u), acc);
-        }
-      }
-      emit(b0 + tid, lcs[tid], acc);
-    }
+    if ((uint32_t)tid < nr) emit(b0 + tid, lcs[tid], row_chain<DT>(qkv, rows + tid, stride, row_words));
     lds_barrier();
   }
 }
@@ -410,7 +442,8 @@ constexpr int kCollectRowBytes = 32 * 1024;
 constexpr int kSubShift = kHistShift - kHistBits;  // second-level bins: M >> 9 & 2047
 
 template <int DT>
-__global__ __launch_bounds__(kScanThreads) void k_qcollect(Dev dv, int64_t n) {
+__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_qcollect(
+    Dev dv, int64_t n) {
   const int s = blockIdx.x % dv.S;  // the scan's block-to-stream mapping
   const int64_t rng = blockIdx.x / dv.S;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
