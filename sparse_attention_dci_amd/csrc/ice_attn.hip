@@ -4,18 +4,20 @@
 // the query finaliser instead.
 //
 // The tokens of a stream's selected pages, taken page after page, are cut
-// into blocks of kAttnTpb = 256; a block is 8 waves of one 32-token chunk
-// each, merged in LDS by their softmax maxima.  Blocks of one stream are
-// merged by a second kernel when the budget spans several.
+// into blocks of kAttnTpb = 256; a block is 16 waves of one 16-token chunk
+// each (keys and values requested together), merged in LDS by their softmax
+// maxima.  Blocks of one stream are merged by a second kernel when the
+// budget spans several.  With one block per stream the arithmetic is the
+// fused finaliser's, so both give identical outputs.
 #include "ice_attn_dev.h"
 
 namespace ice {
 
-constexpr int kAttnWaves = kAttnTpb / 32;
+constexpr int kAttnWaves = kAttnTpb / 16;
 constexpr int kAttnThreads = kAttnWaves * 64;
 
-// Grid (attn_nsplit, S), 512 threads.  Block b covers tokens b*256 .. +255 of
-// the stream's selection, one 32-token chunk per wave; its page numbers are
+// Grid (attn_nsplit, S), 1024 threads.  Block b covers tokens b*256 .. +255 of
+// the stream's selection, one 16-token chunk per wave; its page numbers are
 // staged in LDS first.  With one block per stream the block writes the
 // output, else a partial (max, sum, values) per head for k_attn_merge.
 template <int DT, int D>
@@ -37,7 +39,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(Dev dv, const void *q,
   AttnWave<D> st;
   attn_init(st);
   __syncthreads();
-  if (w * 32 < np * p) attn_chunk<DT, D>(dv, s, w * 32, sel, np, qh, ql, st);
+  if (w * 16 < np * p) attn_chunk<DT, D, false, 1>(dv, s, w * 16, sel, np, qh, ql, st);
   attn_publish(st, w, g, wm, wl, red);
   __syncthreads();
   const int ns = dv.attn_nsplit;

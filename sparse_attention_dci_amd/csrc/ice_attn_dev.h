@@ -100,13 +100,15 @@ __device__ __forceinline__ void attn_init(AttnWave<D> &st) {
   for (int eb = 0; eb < D / 16; ++eb) st.o[eb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
-// Tokens T0 .. T0+31 of the stream's selection (pages sel[0..np), p tokens
-// each, page after page).  Every load is unconditional: tokens past the
-// selection, on invalid page numbers or in empty slots read page 0 and are
-// masked (their logit is -inf and their values are zeroed, since empty
-// slots may hold any bytes).  LATE_V issues the value loads after the logits
-// (one more round trip, about 30 fewer registers).
-template <int DT, int D, bool LATE_V = false>
+// Tokens T0 .. T0+16*NA-1 of the stream's selection (pages sel[0..np), p
+// tokens each, page after page): NA = 2 for 32-token chunks, 1 for 16-token
+// chunks (the second half of the values product is then zero).  Every load is
+// unconditional: tokens past the selection, on invalid page numbers or in
+// empty slots read page 0 and are masked (their logit is -inf and their
+// values are zeroed, since empty slots may hold any bytes).  LATE_V issues
+// the value loads after the logits (one more round trip, about 30 fewer
+// registers).
+template <int DT, int D, bool LATE_V = false, int NA = 2>
 __device__ __forceinline__ void attn_chunk(const Dev &dv, int s, int T0, const int32_t *sel,
                                            int np, const u32x4 (&qh)[D / 32],
                                            const u32x4 (&ql)[D / 32], AttnWave<D> &st) {
@@ -115,9 +117,9 @@ __device__ __forceinline__ void attn_chunk(const Dev &dv, int s, int T0, const i
   const int p = dv.p;
   const int64_t pcap = dv.pcap;
   int32_t pgk[2], pgv[2];
-  bool okv[2];
+  bool okv[2] = {false, false};
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
+  for (int a = 0; a < NA; ++a) {
     const int pik = (T0 + 16 * a + c) / p, piv = (T0 + 16 * a + 4 * G) / p;
     const int32_t pk = sel[min(pik, np - 1)], pv = sel[min(piv, np - 1)];
     const bool okk = pik < np && pk >= 0 && pk < pcap;
@@ -125,13 +127,17 @@ __device__ __forceinline__ void attn_chunk(const Dev &dv, int s, int T0, const i
     pgk[a] = okk ? pk : 0;
     pgv[a] = okv[a] ? pv : 0;
   }
-  int32_t plen[2];
-  u32x4 kr[2][KK][DT == 0 ? 2 : 1];
+  int32_t plen[2] = {0, 0};
+  u32x4 kr[NA][KK][DT == 0 ? 2 : 1];
   u32x4 vr[EB][DT == 0 ? 2 : 1];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) plen[a] = dv.page_len[(int64_t)s * pcap + pgv[a]];
+  for (int eb = 0; eb < EB; ++eb)
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
+    for (int x = 0; x < (DT == 0 ? 2 : 1); ++x) vr[eb][x] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int a = 0; a < NA; ++a) plen[a] = dv.page_len[(int64_t)s * pcap + pgv[a]];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
     const int64_t row = ((int64_t)s * pcap + pgk[a]) * p + (T0 + 16 * a + c) % p;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
@@ -149,7 +155,7 @@ __device__ __forceinline__ void attn_chunk(const Dev &dv, int s, int T0, const i
 #pragma unroll
     for (int eb = 0; eb < EB; ++eb) {
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
+      for (int a = 0; a < NA; ++a) {
         const int64_t col =
             (((int64_t)s * pcap + pgv[a]) * D + 16 * eb + c) * p + (T0 + 16 * a + 4 * G) % p;
         if constexpr (DT == 0) {
@@ -169,7 +175,9 @@ __device__ __forceinline__ void attn_chunk(const Dev &dv, int s, int T0, const i
   const float scale = 1.0f / sqrtf((float)D);
   float z[2][4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
+  for (int i = 0; i < 4; ++i) z[1][i] = -INFINITY;
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
     floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {

@@ -28,7 +28,7 @@ constexpr int kDirChunk = 16;
 // Projection codes are stored in tiles of 64 tokens, [S][tile][mL][64]: a
 // wave reads code t of its 64 tokens as one contiguous 256-byte load.
 constexpr int kCodeTile = 64;
-// Sparse attention: tokens of the selected pages per block (8 waves of 32).
+// Sparse attention: tokens of the selected pages per block (16 waves of 16).
 constexpr int kAttnTpb = 256;
 
 // Every device array of one index, resolved from the caller's workspace.

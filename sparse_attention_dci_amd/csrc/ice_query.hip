@@ -1020,16 +1020,17 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
   }
 
   // G. the fused sparse attention over the selected pages: 16 waves, one
-  // 32-token chunk at a time each, merged at the end (LDS of the dead
-  // selection arrays holds the wave outputs)
+  // 16-token chunk at a time each (keys and values requested together),
+  // merged at the end (LDS of the dead selection arrays holds the wave
+  // outputs)
   constexpr int NW = kFinalThreads / 64;
   static_assert(sizeof(FinalShared) >= (size_t)NW * kMaxGroup * D * 4 + 0, "wave outputs fit");
   AttnWave<D> st;
   attn_init(st);
   __syncthreads();
   const int np = sh.nsel;
-  for (int T0 = w * 32; T0 < np * dv.p; T0 += NW * 32)
-    attn_chunk<DT, D, true>(dv, s, T0, sh.sel, np, qh, ql, st);
+  for (int T0 = w * 16; T0 < np * dv.p; T0 += NW * 16)
+    attn_chunk<DT, D, false, 1>(dv, s, T0, sh.sel, np, qh, ql, st);
   float *red = reinterpret_cast<float *>(&sh.skey[0]);
   attn_publish(st, w, dv.g, sh.wm, sh.wl, red);
   __syncthreads();
