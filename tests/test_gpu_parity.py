@@ -266,13 +266,15 @@ def test_repeated_queries_are_deterministic(B):
                 assert torch.equal(a_, b_)
 
 
-@pytest.mark.parametrize("dtype,S,g,d,p,m,L", [("bf16", 8, 4, 128, 16, 8, 4),
-                                               ("f32", 2, 2, 64, 8, 3, 3)])
-def test_decode_step_equals_separate_calls(B, dtype, S, g, d, p, m, L):
+@pytest.mark.parametrize("dtype,S,g,d,p,m,L,k", [("bf16", 8, 4, 128, 16, 8, 4, 128),
+                                                 ("f32", 2, 2, 64, 8, 3, 3, 128),
+                                                 ("bf16", 2, 2, 128, 16, 4, 6, 1024)])
+def test_decode_step_equals_separate_calls(B, dtype, S, g, d, p, m, L, k):
     """ice_decode_step gives bit-identical pages, top-k and attention to
     ice_insert + ice_query_pages + ice_sparse_attn, step after step, and its
-    last step matches the oracle."""
-    n, steps, k = 3000, 6, 128
+    last step matches the oracle (the last case takes the large-union path:
+    L * k0 = 6,144)."""
+    n, steps = 3000, 6
     dev = torch.device("cuda")
     K, V, q0, _ = _inputs(S, n + steps, d, g, 24, 31, dtype)
     U = W.directions(m * L, d, 31, dtype).to(dev)
@@ -387,6 +389,12 @@ def test_needle_131k_full_layer_sampled(B):
 def test_large_union(B, S, n, g, p, k, m, L, k0):
     """L * k0 above 4,096: the union stays in global memory and is ranked in windows."""
     run_case(B, S=S, n=n, g=g, p=p, k=k, m=m, L=L, k0=k0, seed=40 + L, literal=False)
+
+
+def test_large_union_fewer_tokens_than_k0(B):
+    """L * k0 above 4,096 with fewer tokens than k0: every composite returns
+    all tokens and the union is the whole stream; then inserts grow it."""
+    run_case(B, S=2, n=700, inserts=30, g=2, p=16, k=1024, m=3, L=6, seed=42, literal=False)
 
 
 def test_identical_keys_large_union(B):
