@@ -412,9 +412,12 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(6)
       if (lane == 0) blim[l2] = bb;
     }
     lds_barrier();
-    for (int x = tid; x < L * kHistBins; x += NT) {
-      const uint32_t h = hist[x];
-      if (h && (uint32_t)(x % kHistBins) <= blim[x / kHistBins]) atomicAdd(&ghist[x], h);
+    for (int l2 = 0; l2 < L; ++l2) {
+      const int lim = (int)blim[l2];
+      for (int b = tid; b <= lim; b += NT) {
+        const uint32_t h = hist[l2 * kHistBins + b];
+        if (h) atomicAdd(&ghist[l2 * kHistBins + b], h);
+      }
     }
   }
 
