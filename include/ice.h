@@ -63,7 +63,8 @@ typedef enum { ICE_F32 = 0, ICE_BF16 = 1 } ice_dtype;
 typedef struct {
   int32_t head_dim;   /* d: 64 or 128                                          */
   int32_t page_size;  /* p: 8, 16, 32 or 64 tokens per page                    */
-  int32_t budget_k;   /* k: tokens; a multiple of p; P = k / p pages per query */
+  int32_t budget_k;   /* k: tokens; a multiple of p; P = k / p pages per query;
+                         above 65536: UNSUPPORTED                              */
   int32_t m;          /* simple indices (lists) per composite index, >= 1      */
   int32_t L;          /* composite indices, >= 1; m * L <= 128                 */
   int32_t gqa_group;  /* g: query heads per KV head, 1..16                      */

@@ -114,6 +114,7 @@ ice_status check_params(const ice_params *prm, int32_t S, int64_t n, int64_t nca
   if (prm->L > 32) return ICE_ERR_UNSUPPORTED;
   const int64_t k0 = prm->k0 > 0 ? prm->k0 : prm->budget_k;
   if (k0 * prm->L > ice::kMaxCandBig) return ICE_ERR_UNSUPPORTED;
+  if (prm->budget_k > ice::kMaxBudget) return ICE_ERR_UNSUPPORTED;
   if (n > (int64_t)ice::kPageChunk * 16384) return ICE_ERR_UNSUPPORTED;  // build's chunk counters
   return ICE_OK;
 }

@@ -60,25 +60,61 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(Dev dv, const void *q,
   }
 }
 
-// Merges the blocks of each stream: one block per stream.
+// Merges the blocks of each stream: one block per stream.  The blocks'
+// maxima and sums go to LDS first (one load per pair, all in flight), each
+// head's weights are computed once, and the value loads of eight blocks are
+// issued together; the sums run over the blocks in order.
+constexpr int kMergeMaxSplit = kMaxBudget / kAttnTpb;
+
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_merge(Dev dv, float *out) {
   const int s = blockIdx.x, g = dv.g, ns = dv.attn_nsplit;
+  __shared__ float wgt[kMergeMaxSplit * kMaxGroup];  // the blocks' maxima, then weights
+  __shared__ float sum[kMergeMaxSplit * kMaxGroup];  // the blocks' softmax sums
+  __shared__ float den_s[kMaxGroup];
   const float *base = dv.attn_part + (int64_t)s * ns * g * (D + 2);
+  for (int x = threadIdx.x; x < ns * g; x += 256) {  // x = k * g + h
+    wgt[x] = base[(int64_t)x * (D + 2) + D];
+    sum[x] = base[(int64_t)x * (D + 2) + D + 1];
+  }
+  __syncthreads();
+  // per head: the common max, the weights exp(m_k - M), the weighted sum
+  float mk_h = 0.0f;
+  if (threadIdx.x < g) {
+    const int h = threadIdx.x;
+    float M = -INFINITY;
+    for (int k = 0; k < ns; ++k) M = fmaxf(M, wgt[k * g + h]);
+    float den = 0.0f;
+    for (int k = 0; k < ns; ++k) {
+      const float mk = wgt[k * g + h];
+      const float wk = (M == -INFINITY || mk == -INFINITY) ? 0.0f : __expf(mk - M);
+      den = fmaf(wk, sum[k * g + h], den);
+    }
+    den_s[h] = den;
+    mk_h = M;
+  }
+  __syncthreads();
+  if (threadIdx.x < g) {  // weights replace the maxima (every read of the maxima is done)
+    const int h = threadIdx.x;
+    for (int k = 0; k < ns; ++k) {
+      const float mk = wgt[k * g + h];
+      wgt[k * g + h] = (mk_h == -INFINITY || mk == -INFINITY) ? 0.0f : __expf(mk - mk_h);
+    }
+  }
+  __syncthreads();
   for (int x = threadIdx.x; x < g * D; x += 256) {
     const int h = x / D, e = x % D;
-    float M = -INFINITY;
-    for (int k = 0; k < ns; ++k) M = fmaxf(M, base[((int64_t)k * g + h) * (D + 2) + D]);
-    float num = 0.0f, den = 0.0f;
-    if (M != -INFINITY) {
-      for (int k = 0; k < ns; ++k) {
-        const float *pp = base + ((int64_t)k * g + h) * (D + 2);
-        const float mk = pp[D];
-        const float wgt = mk == -INFINITY ? 0.0f : __expf(mk - M);
-        num = fmaf(wgt, pp[e], num);
-        den = fmaf(wgt, pp[D + 1], den);
-      }
+    float num = 0.0f;
+    for (int k0 = 0; k0 < ns; k0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v[j] = base[((int64_t)min(k0 + j, ns - 1) * g + h) * (D + 2) + e];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (k0 + j < ns) num = fmaf(wgt[(k0 + j) * g + h], v[j], num);
     }
+    const float den = den_s[h];
     out[((int64_t)s * g + h) * D + e] = den > 0.0f ? num / den : 0.0f;
   }
 }

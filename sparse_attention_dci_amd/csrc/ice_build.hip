@@ -61,22 +61,81 @@ __global__ void k_dirs(Dev dv, const void *dirs) {
 // ---------------------------------------------------------------- norms
 
 // Largest |k|^2 per stream (fp64, ascending element order), as the bit
-// pattern of a non-negative double (order-preserving as an integer).
+// pattern of a non-negative double (order-preserving as an integer).  A block
+// stages kNormRows consecutive key rows in LDS with coalesced 16-byte loads
+// (word-major, odd stride: the chain reads of one row per lane fall in
+// distinct banks), then one thread per row runs the chain, its reads a batch
+// ahead of the dependent fma.
+template <int DT>
+struct NormRows {
+  static constexpr int kRows = DT == 0 ? 128 : 256;
+};
+
 template <int DT>
 __global__ __launch_bounds__(256) void k_norms(Dev dv, const void *K, int64_t n) {
+  constexpr int R = NormRows<DT>::kRows, ST = R + 1;
+  constexpr int kMaxWords = 128 * (DT == 0 ? 4 : 2) / 4;  // words of a d = 128 row
+  __shared__ uint32_t rows[kMaxWords * ST];
+  __shared__ unsigned long long wmax[4];
   const int s = blockIdx.y;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  double nsq = 0.0;
-  if (i < n) {
-    const int64_t base = ((int64_t)s * n + i) * dv.d;
-    for (int e0 = 0; e0 < dv.d; e0 += 8) {
-      float x[8];
-      load8<DT>(K, base + e0, x);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t r0 = (int64_t)blockIdx.x * R;
+  const int words = dv.d * (DT == 0 ? 4 : 2) / 4;  // words per row
+  const int cpr = words / 4;                        // 16-byte chunks per row
+  const char *kb = reinterpret_cast<const char *>(K) + (int64_t)s * n * words * 4;
+  constexpr int kIter = R * kMaxWords / 4 / 256;
+  uint4 v[kIter];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const double v = (double)x[j];
-        nsq = fma(v, v, nsq);  // v*v is exact
+  for (int k = 0; k < kIter; ++k) {  // clamped, unconditional loads
+    const int x = tid + 256 * k;
+    const int r = x / cpr, c = x % cpr;
+    const int64_t row = min(r0 + (r < R ? r : R - 1), n - 1);
+    v[k] = reinterpret_cast<const uint4 *>(kb + row * words * 4)[c];
+  }
+#pragma unroll
+  for (int k = 0; k < kIter; ++k) {
+    const int x = tid + 256 * k;
+    const int r = x / cpr, c = x % cpr;
+    if (r < R) {
+      uint32_t *dst = rows + (4 * c) * ST + r;
+      dst[0] = v[k].x;
+      dst[ST] = v[k].y;
+      dst[2 * ST] = v[k].z;
+      dst[3 * ST] = v[k].w;
+    }
+  }
+  __syncthreads();
+  double nsq = 0.0;
+  if (tid < R && r0 + tid < n) {
+    const uint32_t *rw = rows + tid;
+    constexpr int B = 8;
+    uint32_t a0[B], a1[B];
+    auto rd = [&](uint32_t (&x)[B], int w0) {
+#pragma unroll
+      for (int j = 0; j < B; ++j) x[j] = rw[(w0 + j) * ST];
+    };
+    auto sum = [](double acc, const uint32_t (&x)[B]) {
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        if constexpr (DT == 0) {
+          const double f = (double)__uint_as_float(x[j]);
+          acc = fma(f, f, acc);  // f*f is exact
+        } else {
+          const double lo = (double)__uint_as_float(x[j] << 16);
+          const double hi = (double)__uint_as_float(x[j] & 0xffff0000u);
+          acc = fma(lo, lo, acc);
+          acc = fma(hi, hi, acc);
+        }
       }
+      return acc;
+    };
+    rd(a0, 0);
+#pragma unroll 1
+    for (int w0 = 0; w0 < words; w0 += 2 * B) {
+      rd(a1, w0 + B);
+      nsq = sum(nsq, a0);
+      rd(a0, min(w0 + 2 * B, words - B));
+      nsq = sum(nsq, a1);
     }
   }
   unsigned long long b = (unsigned long long)__double_as_longlong(nsq);
@@ -84,11 +143,9 @@ __global__ __launch_bounds__(256) void k_norms(Dev dv, const void *K, int64_t n)
     unsigned long long o = __shfl_xor(b, off);
     b = o > b ? o : b;
   }
-  __shared__ unsigned long long wmax[4];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (lane == 0) wmax[w] = b;
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     unsigned long long m = wmax[0];
     for (int k = 1; k < 4; ++k) m = wmax[k] > m ? wmax[k] : m;
     atomicMax(&dv.maxnsq[s], m);
@@ -602,7 +659,9 @@ static hipError_t build_impl(const Dev &dv, const BuildScratch &bs, int64_t n, c
   const unsigned nb = (unsigned)((n + 255) / 256);
   if (n > 0) {
     if (c_fixed <= 0.0f)
-      hipLaunchKernelGGL(k_norms<DT>, dim3(nb, dv.S), dim3(256), 0, st, dv, K, n);
+      hipLaunchKernelGGL(k_norms<DT>,
+                         dim3((unsigned)((n + NormRows<DT>::kRows - 1) / NormRows<DT>::kRows), dv.S),
+                         dim3(256), 0, st, dv, K, n);
     hipLaunchKernelGGL(k_project<DT>, dim3(nb, dv.nchunk, dv.S), dim3(256), 0, st, dv, bs, K,
                        (const double *)dv.dirs, n, c_fixed);
     hipLaunchKernelGGL(k_sort_lists<kSortItems>, dim3(dv.S * dv.mL), dim3(256), 0, st, dv, bs, n);

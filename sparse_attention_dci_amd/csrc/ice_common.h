@@ -30,6 +30,8 @@ constexpr int kDirChunk = 16;
 constexpr int kCodeTile = 64;
 // Sparse attention: tokens of the selected pages per block (16 waves of 16).
 constexpr int kAttnTpb = 256;
+// Largest budget the standalone attention merges (blocks of kAttnTpb tokens).
+constexpr int kMaxBudget = 65536;
 
 // Every device array of one index, resolved from the caller's workspace.
 struct Dev {

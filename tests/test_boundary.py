@@ -84,7 +84,8 @@ def test_bad_sizes_rejected(L, S, n, cap):
 
 def test_unsupported_settings(L):
     h = ctypes.c_void_p()
-    for p in (good(k1=1000), good(budget_k=4096, page_size=32, m=8, L=4)):
+    for p in (good(k1=1000), good(budget_k=4096, page_size=32, m=8, L=4),
+              good(budget_k=65536 + 16, k0=64)):
         assert L.ice_workspace_bytes(ctypes.byref(p), 1, 1000, 1000) == 0
         st = L.ice_build_index(ctypes.byref(p), 1, 1000, 1000, FAKE, FAKE, FAKE, FAKE, 1 << 40,
                                FAKE, 1 << 40, None, ctypes.byref(h))
