@@ -68,22 +68,22 @@ __global__ void k_dirs(Dev dv, const void *dirs) {
 // ahead of the dependent fma.
 template <int DT>
 struct NormRows {
-  static constexpr int kRows = DT == 0 ? 128 : 256;
+  static constexpr int kRows = DT == 0 ? 128 : 256;  // rows staged per block
+  static constexpr int kMaxWords = DT == 0 ? 128 : 64;  // words of a d = 128 row
+  static constexpr int kStride = kRows + 1;            // odd
 };
 
+// Stages key rows r0 .. r0 + kRows - 1 of stream s (clamped to n - 1) in LDS,
+// word w of row r at w * kStride + r, with coalesced 16-byte loads.
 template <int DT>
-__global__ __launch_bounds__(256) void k_norms(Dev dv, const void *K, int64_t n) {
-  constexpr int R = NormRows<DT>::kRows, ST = R + 1;
-  constexpr int kMaxWords = 128 * (DT == 0 ? 4 : 2) / 4;  // words of a d = 128 row
-  __shared__ uint32_t rows[kMaxWords * ST];
-  __shared__ unsigned long long wmax[4];
-  const int s = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t r0 = (int64_t)blockIdx.x * R;
-  const int words = dv.d * (DT == 0 ? 4 : 2) / 4;  // words per row
-  const int cpr = words / 4;                        // 16-byte chunks per row
+__device__ __forceinline__ void stage_rows(const Dev &dv, const void *K, int s, int64_t n,
+                                           int64_t r0, uint32_t *rows) {
+  constexpr int R = NormRows<DT>::kRows, ST = NormRows<DT>::kStride;
+  const int tid = threadIdx.x;
+  const int words = dv.d * (DT == 0 ? 4 : 2) / 4;
+  const int cpr = words / 4;  // 16-byte chunks per row
   const char *kb = reinterpret_cast<const char *>(K) + (int64_t)s * n * words * 4;
-  constexpr int kIter = R * kMaxWords / 4 / 256;
+  constexpr int kIter = R * NormRows<DT>::kMaxWords / 4 / 256;
   uint4 v[kIter];
 #pragma unroll
   for (int k = 0; k < kIter; ++k) {  // clamped, unconditional loads
@@ -104,40 +104,57 @@ __global__ __launch_bounds__(256) void k_norms(Dev dv, const void *K, int64_t n)
       dst[3 * ST] = v[k].w;
     }
   }
+}
+
+// fp64 sum of squares of a staged row (ascending element order), the reads
+// a batch ahead of the dependent fma.
+template <int DT>
+__device__ __forceinline__ double row_norm2(const uint32_t *rw, int words) {
+  constexpr int B = 8, ST = NormRows<DT>::kStride;
+  uint32_t a0[B], a1[B];
+  auto rd = [&](uint32_t (&x)[B], int w0) {
+#pragma unroll
+    for (int j = 0; j < B; ++j) x[j] = rw[(w0 + j) * ST];
+  };
+  auto sum = [](double acc, const uint32_t (&x)[B]) {
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      if constexpr (DT == 0) {
+        const double f = (double)__uint_as_float(x[j]);
+        acc = fma(f, f, acc);  // f*f is exact
+      } else {
+        const double lo = (double)__uint_as_float(x[j] << 16);
+        const double hi = (double)__uint_as_float(x[j] & 0xffff0000u);
+        acc = fma(lo, lo, acc);
+        acc = fma(hi, hi, acc);
+      }
+    }
+    return acc;
+  };
+  double nsq = 0.0;
+  rd(a0, 0);
+#pragma unroll 1
+  for (int w0 = 0; w0 < words; w0 += 2 * B) {
+    rd(a1, w0 + B);
+    nsq = sum(nsq, a0);
+    rd(a0, min(w0 + 2 * B, words - B));
+    nsq = sum(nsq, a1);
+  }
+  return nsq;
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_norms(Dev dv, const void *K, int64_t n) {
+  constexpr int R = NormRows<DT>::kRows;
+  __shared__ uint32_t rows[NormRows<DT>::kMaxWords * NormRows<DT>::kStride];
+  __shared__ unsigned long long wmax[4];
+  const int s = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t r0 = (int64_t)blockIdx.x * R;
+  stage_rows<DT>(dv, K, s, n, r0, rows);
   __syncthreads();
   double nsq = 0.0;
-  if (tid < R && r0 + tid < n) {
-    const uint32_t *rw = rows + tid;
-    constexpr int B = 8;
-    uint32_t a0[B], a1[B];
-    auto rd = [&](uint32_t (&x)[B], int w0) {
-#pragma unroll
-      for (int j = 0; j < B; ++j) x[j] = rw[(w0 + j) * ST];
-    };
-    auto sum = [](double acc, const uint32_t (&x)[B]) {
-#pragma unroll
-      for (int j = 0; j < B; ++j) {
-        if constexpr (DT == 0) {
-          const double f = (double)__uint_as_float(x[j]);
-          acc = fma(f, f, acc);  // f*f is exact
-        } else {
-          const double lo = (double)__uint_as_float(x[j] << 16);
-          const double hi = (double)__uint_as_float(x[j] & 0xffff0000u);
-          acc = fma(lo, lo, acc);
-          acc = fma(hi, hi, acc);
-        }
-      }
-      return acc;
-    };
-    rd(a0, 0);
-#pragma unroll 1
-    for (int w0 = 0; w0 < words; w0 += 2 * B) {
-      rd(a1, w0 + B);
-      nsq = sum(nsq, a0);
-      rd(a0, min(w0 + 2 * B, words - B));
-      nsq = sum(nsq, a1);
-    }
-  }
+  if (tid < R && r0 + tid < n) nsq = row_norm2<DT>(rows + tid, dv.d * (DT == 0 ? 4 : 2) / 4);
   unsigned long long b = (unsigned long long)__double_as_longlong(nsq);
   for (int off = 32; off >= 1; off >>= 1) {
     unsigned long long o = __shfl_xor(b, off);
@@ -656,14 +673,13 @@ static hipError_t build_impl(const Dev &dv, const BuildScratch &bs, int64_t n, c
     hipLaunchKernelGGL(k_dirs<DT>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, dv,
                        dirs);
   }
-  const unsigned nb = (unsigned)((n + 255) / 256);
   if (n > 0) {
     if (c_fixed <= 0.0f)
       hipLaunchKernelGGL(k_norms<DT>,
                          dim3((unsigned)((n + NormRows<DT>::kRows - 1) / NormRows<DT>::kRows), dv.S),
                          dim3(256), 0, st, dv, K, n);
-    hipLaunchKernelGGL(k_project<DT>, dim3(nb, dv.nchunk, dv.S), dim3(256), 0, st, dv, bs, K,
-                       (const double *)dv.dirs, n, c_fixed);
+    hipLaunchKernelGGL(k_project<DT>, dim3((unsigned)((n + 255) / 256), dv.nchunk, dv.S),
+                       dim3(256), 0, st, dv, bs, K, (const double *)dv.dirs, n, c_fixed);
     hipLaunchKernelGGL(k_sort_lists<kSortItems>, dim3(dv.S * dv.mL), dim3(256), 0, st, dv, bs, n);
   } else {
     // an empty build still fixes c, 1/c and 1/c^2
