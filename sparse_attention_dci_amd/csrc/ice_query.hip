@@ -286,6 +286,19 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(6)
   if (ins && tid >= 256 && tid < 256 + d) kv[tid - 256] = kx;
   lds_barrier();
 
+  // the first kEarly codes of both tiles go out before the chains
+  constexpr int kEarly = 8;
+  const uint32_t tile_bytes = (uint32_t)mL * kCodeTile * 4;
+  const __amdgpu_buffer_rsrc_t rc =
+      byte_range(dv.codes + (int64_t)s * dv.ntile * mL * kCodeTile, (uint32_t)dv.ntile * tile_bytes);
+  const uint32_t oa = (uint32_t)(r * (kScanTpb / 64) + 2 * w) * tile_bytes + lane * 4;
+  int32_t a[kPipe], b[kPipe];
+#pragma unroll
+  for (int x = 0; x < kEarly; ++x) {
+    a[x] = ld_code(rc, oa + x * 256);
+    b[x] = ld_code(rc, oa + tile_bytes + x * 256);
+  }
+
   // the chains: query on threads < mL and 128, insert on 256 + t and 384
   if (tid < mL) zs[tid] = dot_chain(qkv, sm.dl + tid, W, d);
   if (tid == 128) qsq_s = dot_chain(qkv, qkv, 1, d);
@@ -294,15 +307,10 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(6)
     if (tid == 384) ksq_s = dot_chain(kv, kv, 1, d);
   }
   lds_barrier();
-  // the first kPipe codes of both tiles (issued after the chains, which
-  // need the registers)
-  const uint32_t tile_bytes = (uint32_t)mL * kCodeTile * 4;
-  const __amdgpu_buffer_rsrc_t rc =
-      byte_range(dv.codes + (int64_t)s * dv.ntile * mL * kCodeTile, (uint32_t)dv.ntile * tile_bytes);
-  const uint32_t oa = (uint32_t)(r * (kScanTpb / 64) + 2 * w) * tile_bytes + lane * 4;
-  int32_t a[kPipe], b[kPipe];
+  // the rest of the first kPipe codes of both tiles (the chains needed the
+  // registers)
 #pragma unroll
-  for (int x = 0; x < kPipe; ++x) {
+  for (int x = kEarly; x < kPipe; ++x) {
     a[x] = ld_code(rc, oa + x * 256);
     b[x] = ld_code(rc, oa + tile_bytes + x * 256);
   }
