@@ -728,25 +728,33 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
   const int L = dv.L, k0 = dv.k0;
   const uint32_t k0e = (uint32_t)min((int64_t)k0, n);
 
-  // A. loads, all issued up front: the query operands of the attention, the
-  // counts, the two threshold levels of every composite
-  u32x4 qh[D / 32], ql[D / 32];
-  attn_load_q<DT, D>(dv, s, q, qh, ql);
-  for (int x = tid; x < kHashSlots; x += kFinalThreads) sh.hash[x] = 0;
-  const uint32_t nrr_ld = dv.rr_count[s];
-  if (tid < L) {
-    sh.cc[tid] = dv.cand_count[s * L + tid];
-    sh.nb[tid] = dv.bnd_count[s * L + tid];
-    sh.extra[tid] = 0;
-    sh.need[tid] = 0;
-    sh.b2[tid] = 0;
-    sh.need2[tid] = 0;
+  // A. loads, all issued before any is used (one round trip): the two
+  // threshold levels of wave w's composite, the counts, the query operands
+  // of the attention
+  uint32_t h1[kBinsPerLane], h2[kBinsPerLane];
+  if (w < L) {  // wave w's composite
+    wave_hist_load(dv.hist + ((int64_t)s * L + w) * kHistBins, h1);
+    wave_hist_load(dv.hist2 + ((int64_t)s * L + w) * kHistBins, h2);
   }
-  if (k0e > 0) {
+  const uint32_t nrr_ld = dv.rr_count[s];
+  uint32_t cc_ld = 0, nb_ld = 0;
+  if (tid < L) {
+    cc_ld = dv.cand_count[s * L + tid];
+    nb_ld = dv.bnd_count[s * L + tid];
+  }
+  for (int x = tid; x < kHashSlots; x += kFinalThreads) sh.hash[x] = 0;
+  if (tid < L) {
+    sh.cc[tid] = cc_ld;
+    sh.nb[tid] = nb_ld;
+    sh.extra[tid] = 0;
+  }
+  {  // need, b2, need2 of composite l come from wave l alone (all zero when k0e = 0)
     for (int l = w; l < L; l += kFinalThreads / 64) {
-      uint32_t b, bl, b2, bl2, h1[kBinsPerLane], h2[kBinsPerLane];
-      wave_hist_load(dv.hist + ((int64_t)s * L + l) * kHistBins, h1);  // both levels in flight
-      wave_hist_load(dv.hist2 + ((int64_t)s * L + l) * kHistBins, h2);
+      uint32_t b, bl, b2, bl2;
+      if (l != w) {  // more composites than waves
+        wave_hist_load(dv.hist + ((int64_t)s * L + l) * kHistBins, h1);
+        wave_hist_load(dv.hist2 + ((int64_t)s * L + l) * kHistBins, h2);
+      }
       wave_find_bin_regs(h1, k0e, b, bl);
       const uint32_t need = k0e - bl;  // picks from the boundary bin, >= 1
       wave_find_bin_regs(h2, need, b2, bl2);
@@ -758,6 +766,8 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
     }
   }
   __syncthreads();
+  u32x4 qh[D / 32], ql[D / 32];  // needed by the attention only: in flight meanwhile
+  attn_load_q<DT, D>(dv, s, q, qh, ql);
   const uint32_t nrr = k0e > 0 ? nrr_ld : 0u;
   if (tid == 0) {
     uint32_t o = 0;
@@ -1113,8 +1123,19 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
   unsigned long long *ukey = dv.rr_key + o0;
   int32_t *uid = dv.rr_id + o0, *upg = dv.rr_pg + o0;
 
-  // A. counts and the two threshold levels of every composite
+  // A. counts and the two threshold levels of every composite, all loads
+  // issued before any is used
+  uint32_t h1[kBinsPerLane], h2[kBinsPerLane];
+  if (w < L) {  // wave w's composite
+    wave_hist_load(dv.hist + ((int64_t)s * L + w) * kHistBins, h1);
+    wave_hist_load(dv.hist2 + ((int64_t)s * L + w) * kHistBins, h2);
+  }
   const uint32_t nrr_ld = dv.rr_count[s];
+  uint32_t cc_ld = 0, nb_ld = 0;
+  if (tid < L) {
+    cc_ld = dv.cand_count[s * L + tid];
+    nb_ld = dv.bnd_count[s * L + tid];
+  }
   const bool bitmap = n <= kBitTokens;
   const int hwords = bitmap ? (int)((n + 31) >> 5) : (1 << kBigHashBits);
   for (int x = tid; x < hwords; x += NT) sh.hash[x] = 0;
@@ -1127,18 +1148,17 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
     return hash_insert<kBigHashBits>(sh.hash, id);
   };
   if (tid < L) {
-    sh.cc[tid] = dv.cand_count[s * L + tid];
-    sh.nb[tid] = dv.bnd_count[s * L + tid];
+    sh.cc[tid] = cc_ld;
+    sh.nb[tid] = nb_ld;
     sh.extra[tid] = 0;
-    sh.need[tid] = 0;
-    sh.b2[tid] = 0;
-    sh.need2[tid] = 0;
   }
-  if (k0e > 0) {
+  {  // need, b2, need2 of composite l come from wave l alone (all zero when k0e = 0)
     for (int l = w; l < L; l += NT / 64) {
-      uint32_t b, bl, b2, bl2, h1[kBinsPerLane], h2[kBinsPerLane];
-      wave_hist_load(dv.hist + ((int64_t)s * L + l) * kHistBins, h1);
-      wave_hist_load(dv.hist2 + ((int64_t)s * L + l) * kHistBins, h2);
+      uint32_t b, bl, b2, bl2;
+      if (l != w) {  // more composites than waves
+        wave_hist_load(dv.hist + ((int64_t)s * L + l) * kHistBins, h1);
+        wave_hist_load(dv.hist2 + ((int64_t)s * L + l) * kHistBins, h2);
+      }
       wave_find_bin_regs(h1, k0e, b, bl);
       const uint32_t need = k0e - bl;
       wave_find_bin_regs(h2, need, b2, bl2);
