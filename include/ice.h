@@ -70,8 +70,8 @@ typedef struct {
   int32_t gqa_group;  /* g: query heads per KV head, 1..16                      */
   int32_t k0;         /* candidates retrieved per composite; 0 -> budget_k;
                          L * k0 <= 12288 (larger: UNSUPPORTED)                 */
-  int64_t k1;         /* visit budget per composite; 0 -> unbounded (the only
-                         value this build implements; others: UNSUPPORTED)      */
+  int64_t k1;         /* visit budget per composite: the walk stops after k1
+                         list entries (see ice_query_pages); 0 -> unbounded    */
   int32_t tree_depth; /* D, 1..13 and <= m*L; 0 -> derived from the build size:
                          D = round(log2(n_tokens / (4p))) clamped to [1, min(mL,13)] */
   float c;            /* key-norm bound of the transform; 0 -> the largest key
@@ -134,7 +134,11 @@ ice_status ice_insert(ice_index *idx, const void *k_new, const void *v_new, void
  * Per stream: the g query heads are averaged in fp32 (q_kv) and normalised;
  * composite l's candidates are the k0 tokens with the smallest
  * max_j |code_j - qcode_j| over its m directions (ties by token), which is
- * the set a prioritized-DCI walk over the sorted lists retrieves; the union
+ * the set a prioritized-DCI walk over the sorted lists retrieves.  With a
+ * visit budget k1 < m * n the walk visits only the first k1 of the
+ * composite's m * n list entries in ascending (|code - qcode|, token, list)
+ * order, and the candidates are the first min(k0, n_l) tokens of that order,
+ * n_l being the tokens whose every entry is among those k1.  The union
  * of all composites is scored exactly, <q_kv, k> in fp64, and ranked by
  * (score desc, token asc); pages are taken in rank order, each the first time
  * one of its tokens appears, up to P = k/p pages.  Outputs are bit-exact and
@@ -206,7 +210,7 @@ ice_status ice_index_layout(const ice_index *idx, ice_layout *out);
  * kernel (arrays of ICE_TIMED_KERNELS, in the order of ice_timing_name) and
  * clears the record.  The event records add a little time between kernels;
  * leave timing off for end-to-end latency. */
-#define ICE_TIMED_KERNELS 6 /* insert, qscan, qcollect, qfinal, attn, amerge */
+#define ICE_TIMED_KERNELS 7 /* insert, qscan, qcollect, qfinal, attn, amerge, visit */
 ice_status ice_timing_enable(ice_index *idx, int enable);
 ice_status ice_timing_read(ice_index *idx, double *total_ms, int64_t *launches);
 const char *ice_timing_name(int kernel);

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libice.so")
 ICE_OK, ICE_ERR_INVALID_ARG, ICE_ERR_CAPACITY, ICE_ERR_UNSUPPORTED, ICE_ERR_WORKSPACE, \
     ICE_ERR_HIP = 0, -1, -2, -3, -4, -5
 ICE_F32, ICE_BF16 = 0, 1
-TIMED_KERNELS = 6
+TIMED_KERNELS = 7
 
 
 class IceParams(ctypes.Structure):

@@ -86,7 +86,8 @@ struct Layout {
   int64_t dirs, dirs32, norm_c, inv_c, inv_c2, maxnsq, codes, list_code, list_id, loc, page_tokens,
       page_len, page_cell, npages, cell_count, cell_last, pool_k, pool_v, qkv, qcode, mbuf,
       hist, hist2, cand, cand_count, bnd, bnd_rk, bnd_pg, bnd_count, rr_key, rr_id, rr_pg, rr_count,
-      attn_part;
+      attn_part, vhist, vstate, vtie, vcount;
+  int64_t nvrange;
   int64_t total;
 };
 
@@ -110,7 +111,6 @@ ice_status check_params(const ice_params *prm, int32_t S, int64_t n, int64_t nca
   if (prm->dtype != ICE_F32 && prm->dtype != ICE_BF16) return ICE_ERR_INVALID_ARG;
   if (S < 1 || n < 0 || ncap < n || ncap < 1 || ncap > 0x7fffffffLL - 1)
     return ICE_ERR_INVALID_ARG;
-  if (prm->k1 != 0) return ICE_ERR_UNSUPPORTED;
   if (prm->L > 32) return ICE_ERR_UNSUPPORTED;
   const int64_t k0 = prm->k0 > 0 ? prm->k0 : prm->budget_k;
   if (k0 * prm->L > ice::kMaxCandBig) return ICE_ERR_UNSUPPORTED;
@@ -128,6 +128,8 @@ ice_status make_layout(const ice_params *prm, int32_t S, int64_t n, int64_t ncap
   y.D = prm->tree_depth > 0 ? prm->tree_depth : derive_depth(n, p, mL);
   y.ncell = (int64_t)1 << y.D;
   y.pcap = (ncap + p - 1) / p + y.ncell;
+  // this limit also keeps m * ncap below 2^29, so a bounded walk's entry
+  // counts fit in 32 bits
   if (y.pcap > kMaxPages) return ICE_ERR_UNSUPPORTED;
   y.nchunk = (mL + ice::kDirChunk - 1) / ice::kDirChunk;
   y.k0 = prm->k0 > 0 ? prm->k0 : prm->budget_k;
@@ -174,6 +176,11 @@ ice_status make_layout(const ice_params *prm, int32_t S, int64_t n, int64_t ncap
   y.rr_pg = seg(Sl * Ll * y.k0 * 4);
   y.rr_count = seg(Sl * 4);
   y.attn_part = seg(Sl * y.attn_nsplit * g * (d + 2) * 4);
+  y.nvrange = (ncap + ice::kVisitRange - 1) / ice::kVisitRange;
+  y.vhist = seg(Sl * Ll * ice::kHistBins * 4);
+  y.vstate = seg(Sl * Ll * 4 * 4);
+  y.vtie = seg(Sl * Ll * y.nvrange * 4);
+  y.vcount = seg(Sl * Ll * 4);
   y.total = o;
   *L = y;
   return ICE_OK;
@@ -316,6 +323,11 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
   dv.rr_pg = (int32_t *)(w + y.rr_pg);
   dv.rr_count = (uint32_t *)(w + y.rr_count);
   dv.attn_part = (float *)(w + y.attn_part);
+  dv.nvrange = y.nvrange;
+  dv.vhist = (uint32_t *)(w + y.vhist);
+  dv.vstate = (uint32_t *)(w + y.vstate);
+  dv.vtie = (uint32_t *)(w + y.vtie);
+  dv.vcount = (uint32_t *)(w + y.vcount);
 
   ice::BuildScratch bs;
   std::memset(&bs, 0, sizeof(bs));
@@ -358,7 +370,7 @@ ice_status ice_query_pages(ice_index *idx, const void *q, int32_t *page_ids, int
   if (!idx || !q || !page_ids || !n_pages || !aligned(q, 16) || !aligned(page_ids, 4) ||
       !aligned(n_pages, 4) || (topk_ids && !aligned(topk_ids, 4)))
     return ICE_ERR_INVALID_ARG;
-  hipError_t e = ice::launch_query(idx->dv, idx->n, q, page_ids, n_pages, topk_ids,
+  hipError_t e = ice::launch_query(idx->dv, idx->n, idx->prm.k1, q, page_ids, n_pages, topk_ids,
                                    (hipStream_t)stream, idx->timer);
   return e == hipSuccess ? ICE_OK : ICE_ERR_HIP;
 }
@@ -381,8 +393,8 @@ ice_status ice_decode_step(ice_index *idx, const void *k_new, const void *v_new,
       !aligned(out, 4) || (topk_ids && !aligned(topk_ids, 4)))
     return ICE_ERR_INVALID_ARG;
   if (idx->n >= idx->ncap) return ICE_ERR_CAPACITY;
-  hipError_t e = ice::launch_decode(idx->dv, idx->n, k_new, v_new, q, page_ids, n_pages, topk_ids,
-                                    out, (hipStream_t)stream, idx->timer);
+  hipError_t e = ice::launch_decode(idx->dv, idx->n, idx->prm.k1, k_new, v_new, q, page_ids,
+                                    n_pages, topk_ids, out, (hipStream_t)stream, idx->timer);
   if (e != hipSuccess) return ICE_ERR_HIP;
   idx->n += 1;
   return ICE_OK;
@@ -429,8 +441,8 @@ ice_status ice_timing_read(ice_index *idx, double *total_ms, int64_t *launches) 
 }
 
 const char *ice_timing_name(int kernel) {
-  static const char *names[ICE_TIMED_KERNELS] = {"insert", "qscan", "qcollect",
-                                                 "qfinal", "attn", "amerge"};
+  static const char *names[ICE_TIMED_KERNELS] = {"insert", "qscan", "qcollect", "qfinal",
+                                                 "attn",   "amerge", "visit"};
   return (kernel >= 0 && kernel < ICE_TIMED_KERNELS) ? names[kernel] : "";
 }
 

@@ -32,6 +32,8 @@ constexpr int kCodeTile = 64;
 constexpr int kAttnTpb = 256;
 // Largest budget the standalone attention merges (blocks of kAttnTpb tokens).
 constexpr int kMaxBudget = 65536;
+// Token ranges of the visit-budget passes (one block per range and stream).
+constexpr int kVisitRange = 1024;
 
 // Every device array of one index, resolved from the caller's workspace.
 struct Dev {
@@ -79,6 +81,13 @@ struct Dev {
   int32_t *rr_pg;              // [S][L*k0] its page
   uint32_t *rr_count;          // [S]
   float *attn_part;         // [S][nsplit][g][d+2] (values, max logit, softmax sum)
+
+  // visit budget k1 (bounded walks only)
+  int64_t nvrange;          // ceil(ncap / kVisitRange)
+  uint32_t *vhist;          // [S][L][kHistBins] selection histogram, left cleared
+  uint32_t *vstate;         // [S][L][4] prefix / d*, remaining rank, t*, t* completes
+  uint32_t *vtie;           // [S][L][nvrange] entries at distance d* per token range
+  uint32_t *vcount;         // [S][L] n_l, the tokens the bounded walk completes
 };
 
 // Build scratch (caller-owned, only used while the build runs).
@@ -107,7 +116,7 @@ constexpr int kPageChunk = 1024;
 // KID_INSERT is the standalone insert; a decode step's insert and query prep
 // run inside the scan and are timed with it.
 enum KernelId { KID_INSERT = 0, KID_QSCAN, KID_QCOLLECT, KID_QFINAL, KID_ATTN, KID_AMERGE,
-                KID_COUNT };
+                KID_VISIT, KID_COUNT };
 
 // Optional host-side event timer (owned by an index); null when timing is off.
 struct Timer;
@@ -119,13 +128,16 @@ hipError_t launch_build(const Dev &dv, const BuildScratch &bs, int64_t n, const 
                         const void *V, const void *dirs, float c_fixed, hipStream_t st);
 hipError_t launch_insert(const Dev &dv, int64_t n, const void *k_new, const void *v_new,
                          hipStream_t st, Timer *tm);
-hipError_t launch_query(const Dev &dv, int64_t n, const void *q, int32_t *page_ids,
+// k1: the visit budget per composite, 0 = unbounded
+hipError_t launch_query(const Dev &dv, int64_t n, int64_t k1, const void *q, int32_t *page_ids,
                         int32_t *n_pages, int32_t *topk_ids, hipStream_t st, Timer *tm);
 hipError_t launch_attn(const Dev &dv, const void *q, const int32_t *page_ids,
                        const int32_t *n_pages, float *out, hipStream_t st, Timer *tm);
+// n_l of every composite for a walk bounded at k1 visits (1 <= k1 < m * n)
+hipError_t launch_visit_budget(const Dev &dv, int64_t n, uint32_t k1, hipStream_t st);
 // insert of token n, then the query over n + 1 tokens and the attention
-hipError_t launch_decode(const Dev &dv, int64_t n, const void *k_new, const void *v_new,
-                         const void *q, int32_t *page_ids, int32_t *n_pages, int32_t *topk_ids,
-                         float *out, hipStream_t st, Timer *tm);
+hipError_t launch_decode(const Dev &dv, int64_t n, int64_t k1, const void *k_new,
+                         const void *v_new, const void *q, int32_t *page_ids, int32_t *n_pages,
+                         int32_t *topk_ids, float *out, hipStream_t st, Timer *tm);
 
 }  // namespace ice

@@ -107,4 +107,67 @@ __device__ __forceinline__ unsigned long long match_bits(uint32_t key, int bits,
   return m;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const int lane = __lane_id();
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(v, off);
+    if (lane >= off) v += y;
+  }
+  return v;
+}
+
+// One whole wave: smallest bin b of a kHistBins histogram whose inclusive
+// prefix reaches `target` (1 <= target <= total) and the count below b.  The
+// histogram is read by wave_hist_load (lane j holds bins 32j .. 32j+31) so
+// that several can be in flight before any is searched.
+constexpr int kBinsPerLane = kHistBins / 64;
+
+__device__ __forceinline__ void wave_hist_load(const uint32_t *h, uint32_t (&v)[kBinsPerLane]) {
+  const uint4 *h4 = reinterpret_cast<const uint4 *>(h + __lane_id() * kBinsPerLane);
+#pragma unroll
+  for (int k = 0; k < kBinsPerLane / 4; ++k) {
+    const uint4 x = h4[k];
+    v[4 * k] = x.x;
+    v[4 * k + 1] = x.y;
+    v[4 * k + 2] = x.z;
+    v[4 * k + 3] = x.w;
+  }
+}
+
+__device__ void wave_find_bin_regs(const uint32_t (&v)[kBinsPerLane], uint32_t target,
+                                   uint32_t &bin, uint32_t &below) {
+  constexpr int per = kBinsPerLane;
+  const int lane = __lane_id();
+  uint32_t sum = 0;
+#pragma unroll
+  for (int k = 0; k < per; ++k) sum += v[k];
+  const uint32_t incl = wave_incl_scan(sum);
+  const uint32_t excl = incl - sum;
+  const bool mine = excl < target && incl >= target;
+  const unsigned long long bal = __ballot(mine);
+  const int src = bal ? __ffsll((long long)bal) - 1 : 0;
+  uint32_t b = 0, bl = 0;
+  if (mine) {
+    uint32_t run = excl;
+#pragma unroll
+    for (int k = 0; k < per; ++k) {
+      if (run < target && run + v[k] >= target) {
+        b = lane * per + k;
+        bl = run;
+      }
+      run += v[k];
+    }
+  }
+  bin = __shfl(b, src);
+  below = __shfl(bl, src);
+}
+
+__device__ __forceinline__ void wave_find_bin(const uint32_t *h, uint32_t target, uint32_t &bin,
+                                              uint32_t &below) {
+  uint32_t v[kBinsPerLane];
+  wave_hist_load(h, v);
+  wave_find_bin_regs(v, target, bin, below);
+}
+
 }  // namespace ice

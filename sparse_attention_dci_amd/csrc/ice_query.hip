@@ -38,68 +38,6 @@ constexpr int kMaxTies = 256;  // page budgets up to this take the fused attenti
 
 // ---------------------------------------------------------------- helpers
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = __lane_id();
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(v, off);
-    if (lane >= off) v += y;
-  }
-  return v;
-}
-
-// One whole wave: smallest bin b of a kHistBins histogram whose inclusive
-// prefix reaches `target` (1 <= target <= total) and the count below b.  The
-// histogram is read by wave_hist_load (lane j holds bins 32j .. 32j+31) so
-// that several can be in flight before any is searched.
-constexpr int kBinsPerLane = kHistBins / 64;
-
-__device__ __forceinline__ void wave_hist_load(const uint32_t *h, uint32_t (&v)[kBinsPerLane]) {
-  const uint4 *h4 = reinterpret_cast<const uint4 *>(h + __lane_id() * kBinsPerLane);
-#pragma unroll
-  for (int k = 0; k < kBinsPerLane / 4; ++k) {
-    const uint4 x = h4[k];
-    v[4 * k] = x.x;
-    v[4 * k + 1] = x.y;
-    v[4 * k + 2] = x.z;
-    v[4 * k + 3] = x.w;
-  }
-}
-
-__device__ void wave_find_bin_regs(const uint32_t (&v)[kBinsPerLane], uint32_t target,
-                                   uint32_t &bin, uint32_t &below) {
-  constexpr int per = kBinsPerLane;
-  const int lane = __lane_id();
-  uint32_t sum = 0;
-#pragma unroll
-  for (int k = 0; k < per; ++k) sum += v[k];
-  const uint32_t incl = wave_incl_scan(sum);
-  const uint32_t excl = incl - sum;
-  const bool mine = excl < target && incl >= target;
-  const unsigned long long bal = __ballot(mine);
-  const int src = bal ? __ffsll((long long)bal) - 1 : 0;
-  uint32_t b = 0, bl = 0;
-  if (mine) {
-    uint32_t run = excl;
-#pragma unroll
-    for (int k = 0; k < per; ++k) {
-      if (run < target && run + v[k] >= target) {
-        b = lane * per + k;
-        bl = run;
-      }
-      run += v[k];
-    }
-  }
-  bin = __shfl(b, src);
-  below = __shfl(bl, src);
-}
-
-__device__ __forceinline__ void wave_find_bin(const uint32_t *h, uint32_t target, uint32_t &bin,
-                                              uint32_t &below) {
-  uint32_t v[kBinsPerLane];
-  wave_hist_load(h, v);
-  wave_find_bin_regs(v, target, bin, below);
-}
-
 // Exact fp64 scores of cnt tokens by a block of NT threads: per round of as
 // many tokens as ROWBYTES of LDS holds, their key rows are staged in LDS
 // (slot_of(j) gives token j's page slot), then one thread per row runs the
@@ -454,12 +392,12 @@ constexpr int kSubShift = kHistShift - kHistBits;  // second-level bins: M >> 9 
 
 template <int DT>
 __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_qcollect(
-    Dev dv, int64_t n) {
+    Dev dv, int64_t n, bool bounded) {
   const int s = blockIdx.x % dv.S;  // the scan's block-to-stream mapping
   const int64_t rng = blockIdx.x / dv.S;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int L = dv.L;
-  __shared__ uint32_t bstar[32];
+  __shared__ int32_t bstar[32];  // -1: the composite takes no candidates
   __shared__ uint32_t ccount[32], bcount[32], cbase[32], bbase[32];
   __shared__ uint32_t nc, nrl, rbase;
   __shared__ float qkv[128];
@@ -503,9 +441,10 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(4)
   };
   const float qk = dv.qkv[(int64_t)s * dv.d + min(tid, dv.d - 1)];
   for (int l = w; l < L; l += kScanThreads / 64) {
-    uint32_t bb, bl;
-    wave_find_bin(dv.hist + ((int64_t)s * L + l) * kHistBins, k0e, bb, bl);
-    if (lane == 0) bstar[l] = bb;
+    const uint32_t kl = bounded ? min(k0e, dv.vcount[s * L + l]) : k0e;
+    uint32_t bb = 0, bl;
+    if (kl > 0) wave_find_bin(dv.hist + ((int64_t)s * L + l) * kHistBins, kl, bb, bl);
+    if (lane == 0) bstar[l] = kl > 0 ? (int32_t)bb : -1;
   }
   if (tid < dv.d) qkv[tid] = qk;
   lloc[tid] = lc[0];
@@ -530,7 +469,8 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(4)
     slot[u] = -1;
     if (vv[u]) {
       for (int l = 0; l < L; ++l) {
-        const uint32_t M = Mof(u, l), bb = M >> kHistShift;
+        const uint32_t M = Mof(u, l);
+        const int32_t bb = (int32_t)(M >> kHistShift);
         if (bb < bstar[l]) below[u] |= 1u << l;
         if (bb == bstar[l]) {
           bnd[u] |= 1u << l;
@@ -719,9 +659,10 @@ struct FinalShared {
 };
 
 template <int DT, int D>
-__global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int32_t *page_ids,
-                                                          int32_t *n_pages, int32_t *topk_ids,
-                                                          const void *q, float *out) {
+__global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, bool bounded,
+                                                          int32_t *page_ids, int32_t *n_pages,
+                                                          int32_t *topk_ids, const void *q,
+                                                          float *out) {
   __shared__ FinalShared sh;
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -736,6 +677,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
     wave_hist_load(dv.hist + ((int64_t)s * L + w) * kHistBins, h1);
     wave_hist_load(dv.hist2 + ((int64_t)s * L + w) * kHistBins, h2);
   }
+  const uint32_t kl_ld = bounded && w < L ? dv.vcount[s * L + w] : k0e;
   const uint32_t nrr_ld = dv.rr_count[s];
   uint32_t cc_ld = 0, nb_ld = 0;
   if (tid < L) {
@@ -748,20 +690,27 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, int
     sh.nb[tid] = nb_ld;
     sh.extra[tid] = 0;
   }
-  {  // need, b2, need2 of composite l come from wave l alone (all zero when k0e = 0)
+  {  // need, b2, need2 of composite l come from wave l alone (all zero when it takes no
+     // candidates: k0e = 0, or a bounded walk that completes no token)
     for (int l = w; l < L; l += kFinalThreads / 64) {
       uint32_t b, bl, b2, bl2;
       if (l != w) {  // more composites than waves
         wave_hist_load(dv.hist + ((int64_t)s * L + l) * kHistBins, h1);
         wave_hist_load(dv.hist2 + ((int64_t)s * L + l) * kHistBins, h2);
       }
-      wave_find_bin_regs(h1, k0e, b, bl);
-      const uint32_t need = k0e - bl;  // picks from the boundary bin, >= 1
-      wave_find_bin_regs(h2, need, b2, bl2);
+      const uint32_t kl = min(k0e, l == w ? kl_ld : (bounded ? dv.vcount[s * L + l] : k0e));
+      uint32_t need = 0, need2 = 0;  // picks from the boundary bin (>= 1 when kl > 0) and
+      b2 = 0;                        // from its second-level bin b2
+      if (kl > 0) {
+        wave_find_bin_regs(h1, kl, b, bl);
+        need = kl - bl;
+        wave_find_bin_regs(h2, need, b2, bl2);
+        need2 = need - bl2;
+      }
       if (lane == 0) {
         sh.need[l] = need;
         sh.b2[l] = b2;
-        sh.need2[l] = need - bl2;  // picks from second-level bin b2
+        sh.need2[l] = need2;
       }
     }
   }
@@ -1111,8 +1060,9 @@ struct BigShared {
 };
 
 template <int DT>
-__global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n, int32_t *page_ids,
-                                                              int32_t *n_pages, int32_t *topk_ids) {
+__global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n, bool bounded,
+                                                              int32_t *page_ids, int32_t *n_pages,
+                                                              int32_t *topk_ids) {
   __shared__ BigShared sh;
   constexpr int NT = kFinalThreads;
   const int s = blockIdx.x;
@@ -1130,6 +1080,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
     wave_hist_load(dv.hist + ((int64_t)s * L + w) * kHistBins, h1);
     wave_hist_load(dv.hist2 + ((int64_t)s * L + w) * kHistBins, h2);
   }
+  const uint32_t kl_ld = bounded && w < L ? dv.vcount[s * L + w] : k0e;
   const uint32_t nrr_ld = dv.rr_count[s];
   uint32_t cc_ld = 0, nb_ld = 0;
   if (tid < L) {
@@ -1152,20 +1103,27 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
     sh.nb[tid] = nb_ld;
     sh.extra[tid] = 0;
   }
-  {  // need, b2, need2 of composite l come from wave l alone (all zero when k0e = 0)
+  {  // need, b2, need2 of composite l come from wave l alone (all zero when it takes no
+     // candidates: k0e = 0, or a bounded walk that completes no token)
     for (int l = w; l < L; l += NT / 64) {
       uint32_t b, bl, b2, bl2;
       if (l != w) {  // more composites than waves
         wave_hist_load(dv.hist + ((int64_t)s * L + l) * kHistBins, h1);
         wave_hist_load(dv.hist2 + ((int64_t)s * L + l) * kHistBins, h2);
       }
-      wave_find_bin_regs(h1, k0e, b, bl);
-      const uint32_t need = k0e - bl;
-      wave_find_bin_regs(h2, need, b2, bl2);
+      const uint32_t kl = min(k0e, l == w ? kl_ld : (bounded ? dv.vcount[s * L + l] : k0e));
+      uint32_t need = 0, need2 = 0;  // picks from the boundary bin (>= 1 when kl > 0) and
+      b2 = 0;                        // from its second-level bin b2
+      if (kl > 0) {
+        wave_find_bin_regs(h1, kl, b, bl);
+        need = kl - bl;
+        wave_find_bin_regs(h2, need, b2, bl2);
+        need2 = need - bl2;
+      }
       if (lane == 0) {
         sh.need[l] = need;
         sh.b2[l] = b2;
-        sh.need2[l] = need - bl2;
+        sh.need2[l] = need2;
       }
     }
   }
@@ -1565,11 +1523,12 @@ static void launch_scan_r(const Dev &dv, int64_t n, unsigned grid, const void *q
 }
 
 // The query over n tokens (token n - 1 inserted by the scan when k_new is
-// given): scan, collect, final.
+// given): scan, the visit-budget passes when the walk is bounded (k1 < m * n),
+// collect, final.
 template <int DT>
-static void query_tail(const Dev &dv, int64_t n, int32_t *page_ids, int32_t *n_pages,
-                       int32_t *topk_ids, const void *q, const void *k_new, const void *v_new,
-                       float *out, hipStream_t st, Timer *tm) {
+static void query_tail(const Dev &dv, int64_t n, int64_t k1, int32_t *page_ids,
+                       int32_t *n_pages, int32_t *topk_ids, const void *q, const void *k_new,
+                       const void *v_new, float *out, hipStream_t st, Timer *tm) {
   const int64_t nrange = (n + kScanTpb - 1) / kScanTpb;
   const unsigned grid = (unsigned)(max(nrange, (int64_t)1) * dv.S);
   if (dv.L <= 6)
@@ -1577,35 +1536,40 @@ static void query_tail(const Dev &dv, int64_t n, int32_t *page_ids, int32_t *n_p
   else
     launch_scan_r<DT, false>(dv, n, grid, q, k_new, v_new, st);
   timer_mark(tm, KID_QSCAN, st);
+  const bool bounded = n > 0 && k1 > 0 && k1 < (int64_t)dv.m * n;
+  if (bounded) {
+    launch_visit_budget(dv, n, (uint32_t)k1, st);
+    timer_mark(tm, KID_VISIT, st);
+  }
   if (n > 0) {
-    hipLaunchKernelGGL(k_qcollect<DT>, dim3(grid), dim3(kScanThreads), 0, st, dv, n);
+    hipLaunchKernelGGL(k_qcollect<DT>, dim3(grid), dim3(kScanThreads), 0, st, dv, n, bounded);
     timer_mark(tm, KID_QCOLLECT, st);
   }
   if (dv.L * dv.k0 > kMaxCand)
-    hipLaunchKernelGGL(k_qfinal_big<DT>, dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n, page_ids,
-                       n_pages, topk_ids);
+    hipLaunchKernelGGL(k_qfinal_big<DT>, dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n, bounded,
+                       page_ids, n_pages, topk_ids);
   else if (dv.d == 128)
     hipLaunchKernelGGL((k_qfinal<DT, 128>), dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n,
-                       page_ids, n_pages, topk_ids, q, out);
+                       bounded, page_ids, n_pages, topk_ids, q, out);
   else
     hipLaunchKernelGGL((k_qfinal<DT, 64>), dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n,
-                       page_ids, n_pages, topk_ids, q, out);
+                       bounded, page_ids, n_pages, topk_ids, q, out);
   timer_mark(tm, KID_QFINAL, st);
 }
 
-hipError_t launch_query(const Dev &dv, int64_t n, const void *q, int32_t *page_ids,
+hipError_t launch_query(const Dev &dv, int64_t n, int64_t k1, const void *q, int32_t *page_ids,
                         int32_t *n_pages, int32_t *topk_ids, hipStream_t st, Timer *tm) {
   timer_begin(tm, st);
   if (dv.dtype == 0)
-    query_tail<0>(dv, n, page_ids, n_pages, topk_ids, q, nullptr, nullptr, nullptr, st, tm);
+    query_tail<0>(dv, n, k1, page_ids, n_pages, topk_ids, q, nullptr, nullptr, nullptr, st, tm);
   else
-    query_tail<1>(dv, n, page_ids, n_pages, topk_ids, q, nullptr, nullptr, nullptr, st, tm);
+    query_tail<1>(dv, n, k1, page_ids, n_pages, topk_ids, q, nullptr, nullptr, nullptr, st, tm);
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const Dev &dv, int64_t n, const void *k_new, const void *v_new,
-                         const void *q, int32_t *page_ids, int32_t *n_pages, int32_t *topk_ids,
-                         float *out, hipStream_t st, Timer *tm) {
+hipError_t launch_decode(const Dev &dv, int64_t n, int64_t k1, const void *k_new,
+                         const void *v_new, const void *q, int32_t *page_ids, int32_t *n_pages,
+                         int32_t *topk_ids, float *out, hipStream_t st, Timer *tm) {
   // the new token is token n (inserted by the scan); the query sees n + 1
   // tokens.  Pages up to kFusedMaxPages and unions that fit LDS: the
   // finaliser runs the attention itself.
@@ -1613,9 +1577,9 @@ hipError_t launch_decode(const Dev &dv, int64_t n, const void *k_new, const void
   const bool fused = dv.P <= kFusedMaxPages && dv.L * dv.k0 <= kMaxCand;
   float *fo = fused ? out : nullptr;
   if (dv.dtype == 0)
-    query_tail<0>(dv, n + 1, page_ids, n_pages, topk_ids, q, k_new, v_new, fo, st, tm);
+    query_tail<0>(dv, n + 1, k1, page_ids, n_pages, topk_ids, q, k_new, v_new, fo, st, tm);
   else
-    query_tail<1>(dv, n + 1, page_ids, n_pages, topk_ids, q, k_new, v_new, fo, st, tm);
+    query_tail<1>(dv, n + 1, k1, page_ids, n_pages, topk_ids, q, k_new, v_new, fo, st, tm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return fused ? hipSuccess : launch_attn(dv, q, page_ids, n_pages, out, st, tm);

@@ -84,12 +84,24 @@ def test_bad_sizes_rejected(L, S, n, cap):
 
 def test_unsupported_settings(L):
     h = ctypes.c_void_p()
-    for p in (good(k1=1000), good(budget_k=4096, page_size=32, m=8, L=4),
+    for p in (good(budget_k=4096, page_size=32, m=8, L=4),
               good(budget_k=65536 + 16, k0=64)):
         assert L.ice_workspace_bytes(ctypes.byref(p), 1, 1000, 1000) == 0
         st = L.ice_build_index(ctypes.byref(p), 1, 1000, 1000, FAKE, FAKE, FAKE, FAKE, 1 << 40,
                                FAKE, 1 << 40, None, ctypes.byref(h))
         assert st == B.ICE_ERR_UNSUPPORTED
+
+
+def test_visit_budget_accepted(L):
+    """Bounded walks are accepted; the page-capacity limit keeps m * capacity
+    (the list entries a composite's selection counts) below 2^29."""
+    p = good(k1=1000)
+    assert L.ice_workspace_bytes(ctypes.byref(p), 1, 1000, 1000) > 0
+    wide = good(k1=1 << 40, m=128, L=1, page_size=64, tree_depth=8)
+    cap = (65536 - 256) * 64
+    assert L.ice_workspace_bytes(ctypes.byref(wide), 1, 1000, cap) > 0
+    assert 128 * cap < 1 << 29
+    assert L.ice_workspace_bytes(ctypes.byref(wide), 1, 1000, cap + 64) == 0
 
 
 def test_build_size_limit(L):

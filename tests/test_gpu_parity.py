@@ -104,7 +104,7 @@ def _check_query(idx, st, s, r, page_ids, n_pages, topk, out, q_s):
 
 
 def run_case(B, *, S, n, d=128, g=1, p=16, k=256, m=4, L=2, dtype="bf16", clusters=32,
-             seed=1, inserts=0, k0=0, check=None, keys=None, literal=True):
+             seed=1, inserts=0, k0=0, k1=0, check=None, keys=None, literal=True):
     dev = torch.device("cuda")
     cap = n + inserts
     if keys is None:
@@ -112,17 +112,18 @@ def run_case(B, *, S, n, d=128, g=1, p=16, k=256, m=4, L=2, dtype="bf16", cluste
     else:
         K, V, q = keys
     U = W.directions(m * L, d, seed, dtype)
-    print(f"[case] S={S} n={n} inserts={inserts} d={d} g={g} p={p} k={k} m={m} L={L} {dtype}",
-          flush=True)
+    print(f"[case] S={S} n={n} inserts={inserts} d={d} g={g} p={p} k={k} m={m} L={L} {dtype} "
+          f"k0={k0} k1={k1}", flush=True)
     idx = B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U.to(dev),
-                  page_size=p, budget_k=k, m=m, L=L, gqa_group=g, k0=k0, capacity=max(cap, 1))
+                  page_size=p, budget_k=k, m=m, L=L, gqa_group=g, k0=k0, k1=k1,
+                  capacity=max(cap, 1))
     for t in range(inserts):
         idx.insert(K[:, n + t].contiguous().to(dev), V[:, n + t].contiguous().to(dev))
     qd = q.to(dev)
     page_ids, n_pages, topk = idx.query_pages(qd, with_topk=True)
     out = idx.sparse_attn(qd, page_ids, n_pages)
     torch.cuda.synchronize()
-    prm = oracle.Params(d=d, p=p, k=k, m=m, L=L, g=g, k0=k0)
+    prm = oracle.Params(d=d, p=p, k=k, m=m, L=L, g=g, k0=k0, k1=k1)
     Un = _np(U)
     for s in (check if check is not None else range(S)):
         st = oracle.OracleStream(prm, _np(K[s, :n]), _np(V[s, :n]), Un, n_cap=max(cap, 1))
@@ -430,3 +431,79 @@ def test_qwen3_4b_262k_full_layer_sampled(B):
         q_s = _np(q[s * w.g:(s + 1) * w.g])
         r = st.query(q_s, literal=False)
         _check_query(idx, st, s, r, page_ids, n_pages, topk, out[s * w.g:(s + 1) * w.g], q_s)
+
+
+# ---------------------------------------------------------------- visit budget k1
+
+@pytest.mark.parametrize("k1", [1, 7, 500, 3001, 9000, 15999, 16000, 1 << 40])
+def test_visit_budget(B, k1):
+    """Walks bounded at k1 list entries per composite (m * n = 16,000 here):
+    from no completed token (k1 = 1) to the unbounded result (k1 >= m * n)."""
+    idx = run_case(B, S=2, n=4000, g=2, p=16, k=256, m=4, L=2, k1=k1, seed=41)
+    cc = idx.view("cand_count").cpu().numpy()
+    if k1 <= 500:  # the budget, not k0 = 256, ends every walk
+        assert cc.max() < 256
+    if k1 == 1:  # a token needs all m = 4 of its entries visited
+        assert cc.max() == 0
+
+
+def test_visit_budget_ragged_fp32_inserts(B):
+    run_case(B, S=3, n=2333, g=1, p=8, k=128, m=3, L=3, dtype="f32", inserts=4, k1=2500,
+             seed=42)
+
+
+def test_visit_budget_identical_keys(B):
+    """Every key equal: every entry of a composite ties at one distance, so the
+    k1-th entry is found by token and list order alone."""
+    S, n, d, g = 2, 700, 128, 2
+    K = torch.full((S, n, d), 0.5, dtype=torch.bfloat16)
+    V = torch.randn(S, n, d, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    q = torch.randn(S * g, d, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16)
+    for k1 in (1, 4, 5, 999, 1001, 2799):
+        run_case(B, S=S, n=n, d=d, g=g, p=16, k=64, m=4, L=2, keys=(K, V, q), k1=k1, seed=10)
+
+
+def test_visit_budget_few_distinct_keys(B):
+    """Keys drawn from four points: long runs of equal distances around the
+    k1-th entry in every composite."""
+    S, n, d, g = 2, 3000, 64, 1
+    gen = torch.Generator().manual_seed(8)
+    pts = torch.randn(4, d, generator=gen)
+    K = pts[torch.randint(0, 4, (S, n), generator=gen)].to(torch.bfloat16)
+    V = torch.randn(S, n, d, generator=gen).to(torch.bfloat16)
+    q = torch.randn(S * g, d, generator=gen).to(torch.bfloat16)
+    for k1 in (2000, 6001, 11999):
+        run_case(B, S=S, n=n, d=d, g=g, p=16, k=128, m=4, L=2, keys=(K, V, q), k1=k1, seed=11)
+
+
+def test_visit_budget_large_union(B):
+    """L * k0 = 6,000 takes the large-union finaliser."""
+    for k1 in (20000, 45000):
+        run_case(B, S=1, n=12000, g=2, p=16, k=1024, m=4, L=2, k0=3000, k1=k1, seed=43,
+                 literal=False)
+
+
+def test_visit_budget_decode_step(B):
+    """ice_decode_step with a bounded walk equals the oracle after every step."""
+    S, n, steps, g, d, p, m, L, k, k1 = 2, 2500, 3, 2, 128, 16, 4, 2, 128, 3000
+    dev = torch.device("cuda")
+    K, V, _, _ = _inputs(S, n + steps, d, g, 24, 44, "bf16")
+    U = W.directions(m * L, d, 44, "bf16")
+    print(f"[case] decode_step k1={k1}", flush=True)
+    a = B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U.to(dev),
+                page_size=p, budget_k=k, m=m, L=L, gqa_group=g, k1=k1, capacity=n + steps)
+    prm = oracle.Params(d=d, p=p, k=k, m=m, L=L, g=g, k1=k1)
+    sts = [oracle.OracleStream(prm, _np(K[s, :n]), _np(V[s, :n]), _np(U), n_cap=n + steps)
+           for s in range(S)]
+    gen = torch.Generator().manual_seed(6)
+    for t in range(steps):
+        qt = torch.randn(S * g, d, generator=gen).to(torch.bfloat16)
+        pa, na, oa, ta = a.decode_step(K[:, n + t].contiguous().to(dev),
+                                       V[:, n + t].contiguous().to(dev), qt.to(dev),
+                                       with_topk=True)
+        torch.cuda.synchronize()
+        for s in range(S):
+            sts[s].insert(_np(K[s, n + t]), _np(V[s, n + t]))
+            q_s = _np(qt[s * g:(s + 1) * g])
+            r = sts[s].query(q_s, literal=True)
+            _check_query(a, sts[s], s, r, pa, na, ta, oa[s * g:(s + 1) * g], q_s)
