@@ -670,8 +670,8 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
   const uint32_t k0e = (uint32_t)min((int64_t)k0, n);
 
   // A. loads, all issued before any is used (one round trip): the two
-  // threshold levels of wave w's composite, the counts, the query operands
-  // of the attention
+  // threshold levels of wave w's composite, the counts; thread tid also owns
+  // boundary entry ep of composite lp (for the prefetch below)
   uint32_t h1[kBinsPerLane], h2[kBinsPerLane];
   if (w < L) {  // wave w's composite
     wave_hist_load(dv.hist + ((int64_t)s * L + w) * kHistBins, h1);
@@ -679,6 +679,10 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
   }
   const uint32_t kl_ld = bounded && w < L ? dv.vcount[s * L + w] : k0e;
   const uint32_t nrr_ld = dv.rr_count[s];
+  const int per = kFinalThreads / L;  // boundary entries prefetched per composite
+  const int lp = min(tid / per, L - 1);
+  const uint32_t ep = (uint32_t)(tid - lp * per);
+  const uint32_t nbp = dv.bnd_count[s * L + lp];
   uint32_t cc_ld = 0, nb_ld = 0;
   if (tid < L) {
     cc_ld = dv.cand_count[s * L + tid];
@@ -714,10 +718,28 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
       }
     }
   }
-  __syncthreads();
+  // the rerank list and this thread's boundary entry, requested before the
+  // first barrier (the barriers up to the attention order LDS only, so these
+  // and the query loads stay in flight across them)
+  constexpr int kPer = kMaxCand / kFinalThreads;
+  const uint32_t nrr = k0e > 0 ? nrr_ld : 0u;
+  int32_t pid[kPer], ppg[kPer];
+  unsigned long long pkey[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const uint32_t x = tid + kFinalThreads * j;
+    const int64_t o = (int64_t)s * L * k0 + min(x, (uint32_t)(L * k0 - 1));
+    pid[j] = dv.rr_id[o];
+    pkey[j] = dv.rr_key[o];
+    ppg[j] = dv.rr_pg[o];
+  }
+  const bool pv = tid < L * per && ep < nbp && k0e > 0;
+  const int64_t po = ((int64_t)s * L + lp) * dv.ncap + (pv ? ep : 0u);
+  const unsigned long long pbk = dv.bnd[po], pbrk = dv.bnd_rk[po];
+  const int32_t pbpg = dv.bnd_pg[po];
+  lds_barrier();
   u32x4 qh[D / 32], ql[D / 32];  // needed by the attention only: in flight meanwhile
   attn_load_q<DT, D>(dv, s, q, qh, ql);
-  const uint32_t nrr = k0e > 0 ? nrr_ld : 0u;
   if (tid == 0) {
     uint32_t o = 0;
     for (int l = 0; l < L; ++l) {
@@ -728,30 +750,49 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
     sh.nu = nrr;
     sh.ntie = 0;
   }
-  __syncthreads();
+  lds_barrier();
   const uint32_t nbt = sh.boff[L];
   const bool bnd_lds = nbt <= (uint32_t)kBndLds;
 
-  // B. the scored below-bin candidates and, when they fit, the boundary entries
-  for (uint32_t x = tid; x < nrr; x += kFinalThreads) {
-    const int64_t o = (int64_t)s * L * k0 + x;
-    const int32_t id = dv.rr_id[o];
-    hash_insert(sh.hash, id);
-    sh.sid[x] = id;
-    sh.skey[x] = dv.rr_key[o];
-    sh.spg[x] = dv.rr_pg[o];
+  // B. the scored below-bin candidates and, when they fit, the boundary
+  // entries (a composite's entries past the prefetched ones are loaded here)
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const uint32_t x = tid + kFinalThreads * j;
+    if (x < nrr) {
+      hash_insert(sh.hash, pid[j]);
+      sh.sid[x] = pid[j];
+      sh.skey[x] = pkey[j];
+      sh.spg[x] = ppg[j];
+    }
   }
   if (bnd_lds) {
+    if (pv) {
+      const uint32_t x = sh.boff[lp] + ep;
+      sh.bk[x] = pbk;
+      sh.brk[x] = pbrk;
+      sh.bpg[x] = pbpg;
+    }
     for (uint32_t x = tid; x < nbt; x += kFinalThreads) {
       int l = 0;
       while (x >= sh.boff[l + 1]) ++l;
+      if (x - sh.boff[l] < (uint32_t)per) continue;
       const int64_t o = ((int64_t)s * L + l) * dv.ncap + (x - sh.boff[l]);
       sh.bk[x] = dv.bnd[o];
       sh.brk[x] = dv.bnd_rk[o];
       sh.bpg[x] = dv.bnd_pg[o];
     }
   }
-  __syncthreads();
+  {  // a clean histogram for the next query: every read of it is done, and
+     // the stores drain while the rest runs (no later barrier waits for them)
+    uint32_t *hist = dv.hist + (int64_t)s * L * kHistBins;
+    uint32_t *hist2 = dv.hist2 + (int64_t)s * L * kHistBins;
+    for (int x = tid; x < L * kHistBins; x += kFinalThreads) {
+      hist[x] = 0;
+      hist2[x] = 0;
+    }
+  }
+  lds_barrier();
 
   // C. the need_l smallest (M, i) of each composite's boundary bin join the
   // composite's candidates, and the union when not in it yet: every entry in
@@ -784,7 +825,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
           if (t < kMaxTies) sh.tie[t] = x;
         }
       }
-      __syncthreads();
+      lds_barrier();
       const uint32_t nt = sh.ntie;
       if (nt <= (uint32_t)kMaxTies) {
         for (uint32_t t = tid; t < nt; t += kFinalThreads) {
@@ -826,7 +867,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   const uint32_t nu = sh.nu;
 
   // D. bucket sort by (rank key, token).  Bucket = floor((s_max - score) *
@@ -973,21 +1014,9 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
       sh.nsel = nsel;
     }
   }
-  // F. the candidate counts for inspection, a clean histogram for the next
-  // query (after the attention: a barrier after global stores waits for them)
-  auto bookkeeping = [&]() {
-    if (tid < L && k0e > 0) dv.cand_count[s * L + tid] = sh.cc[tid] + sh.extra[tid];
-    uint32_t *hist = dv.hist + (int64_t)s * L * kHistBins;
-    uint32_t *hist2 = dv.hist2 + (int64_t)s * L * kHistBins;
-    for (int x = tid; x < L * kHistBins; x += kFinalThreads) {
-      hist[x] = 0;
-      hist2[x] = 0;
-    }
-  };
-  if (out == nullptr) {
-    bookkeeping();
-    return;
-  }
+  // F. the candidate counts, for inspection
+  if (tid < L && k0e > 0) dv.cand_count[s * L + tid] = sh.cc[tid] + sh.extra[tid];
+  if (out == nullptr) return;
 
   // G. the fused sparse attention over the selected pages: 16 waves, one
   // 16-token chunk at a time each (keys and values requested together),
@@ -997,19 +1026,18 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
   static_assert(sizeof(FinalShared) >= (size_t)NW * kMaxGroup * D * 4 + 0, "wave outputs fit");
   AttnWave<D> st;
   attn_init(st);
-  __syncthreads();
+  lds_barrier();
   const int np = sh.nsel;
   for (int T0 = w * 16; T0 < np * dv.p; T0 += NW * 16)
     attn_chunk<DT, D, false, 1>(dv, s, T0, sh.sel, np, qh, ql, st);
   float *red = reinterpret_cast<float *>(&sh.skey[0]);
   attn_publish(st, w, dv.g, sh.wm, sh.wl, red);
-  __syncthreads();
+  lds_barrier();
   for (int x = tid; x < dv.g * D; x += kFinalThreads) {
     float M, num, den;
     attn_merge<D>(NW, dv.g, x, sh.wm, sh.wl, red, M, num, den);
     out[(int64_t)s * dv.g * D + x] = den > 0.0f ? num / den : 0.0f;
   }
-  bookkeeping();
 }
 
 // ---------------------------------------------------------------- final, large unions
