@@ -14,7 +14,9 @@ last-level cache, as in a real multi-layer decode.
 
 --workload picks another configuration (the 32-layer decode, the 131k needle
 batch); --copy-calibration times a plain device copy of known size instead
-(the reference for the HBM byte counters).
+(the reference for the HBM byte counters); --write-traffic turns four
+rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE of the decode kernels, the
+same two of the copy) into profiles/traffic.json (no GPU needed).
 
 Prints one JSON line (the last line of stdout).
 """
@@ -135,6 +137,71 @@ def copy_calibration(args):
     print(json.dumps({"copy_bytes_per_launch": n, "launches": args.steps}), flush=True)
 
 
+# decode kernels reported by the benchmark -> their names in rocprofv3 output
+# (the library's own timing names both finalisers "qfinal")
+PROFILED = {"qscan": ("k_qscan<",), "qcollect": ("k_qcollect<",),
+            "qfinal": ("k_qfinal<", "k_qfinal_big<"), "attn": ("k_attn<",),
+            "amerge": ("k_attn_merge",)}
+
+
+def _counter_means(directory: str, counter: str) -> dict:
+    """Mean value of `counter` per dispatch, per kernel name, over every
+    rocprofv3 counter_collection.csv under `directory`."""
+    import csv
+    sums = {}
+    for root, _, files in os.walk(directory):
+        for f in files:
+            if not f.endswith("counter_collection.csv"):
+                continue
+            with open(os.path.join(root, f), newline="") as fh:
+                for row in csv.DictReader(fh):
+                    if row.get("Counter_Name") != counter:
+                        continue
+                    name = row["Kernel_Name"]
+                    a, c = sums.get(name, (0.0, 0))
+                    sums[name] = (a + float(row["Counter_Value"]), c + 1)
+    if not sums:
+        raise SystemExit(f"no {counter} rows under {directory}")
+    return {k: a / c for k, (a, c) in sums.items()}
+
+
+def write_traffic(args):
+    """HBM bytes per launch of each decode kernel: FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch), each scaled so that a plain device copy of known size
+    reads and writes exactly its size."""
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.write_traffic
+    copy_bytes = 256 << 20  # the --copy-calibration copy
+
+    def copy_kib(d, counter):
+        means = _counter_means(d, counter)
+        return max(v for k, v in means.items() if "copy" in k.lower())
+
+    fscale = copy_bytes / 1024.0 / copy_kib(cfetch_dir, "FETCH_SIZE")
+    wscale = copy_bytes / 1024.0 / copy_kib(cwrite_dir, "WRITE_SIZE")
+    fm = _counter_means(fetch_dir, "FETCH_SIZE")
+    wm = _counter_means(write_dir, "WRITE_SIZE")
+    per = {}
+    for short, pats in PROFILED.items():
+        fk = [v for k, v in fm.items() if any(p in k for p in pats)]
+        wk = [v for k, v in wm.items() if any(p in k for p in pats)]
+        if fk and wk:
+            per[short] = int(round(1024.0 * (fk[0] * fscale + wk[0] * wscale)))
+    tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    tr = {}
+    if os.path.exists(tfile):
+        with open(tfile) as fh:
+            tr = json.load(fh)
+    h = kernel_source_hash()
+    if tr.get("source_hash") != h or abs(tr.get("fetch_scale", 0) - fscale) > 0.05:
+        tr = {"workloads": {}}
+    tr.update({"source_hash": h, "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4),
+               "unit": "HBM bytes per launch (fetch + write)"})
+    tr["workloads"][args.workload] = per
+    with open(tfile, "w") as fh:
+        json.dump(tr, fh, indent=1)
+    print(json.dumps(tr), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,7 +213,12 @@ def main():
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--write-traffic", nargs=4,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the streams of different layers and heads are independent, so a multi-GPU "

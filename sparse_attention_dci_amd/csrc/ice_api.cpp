@@ -187,15 +187,16 @@ ice_status make_layout(const ice_params *prm, int32_t S, int64_t n, int64_t ncap
 }
 
 // Offsets of the build scratch arrays (ice::BuildScratch order); returns the total.
-int64_t scratch_offsets(const ice_params *prm, int32_t S, int64_t n, int64_t off[9]) {
+int64_t scratch_offsets(const ice_params *prm, int32_t S, int64_t n, int64_t off[10]) {
   const int64_t mL = (int64_t)prm->m * prm->L;
   const int64_t cmax = (int64_t)1 << (mL < ice::kMaxTreeDepth ? mL : ice::kMaxTreeDepth);
   const int64_t nchunk = (n + ice::kPageChunk - 1) / ice::kPageChunk;
-  const int64_t sz[9] = {S * mL * n * 4,         S * mL * n * 4,          S * mL * n * 4,
-                         S * n * 4,              S * nchunk * cmax * 4,   S * n * 4,
-                         S * (nchunk + 1) * 4,   S * (cmax + 1) * 4,      S * (n / 8 + cmax + 1) * 4};
+  const int64_t sz[10] = {S * mL * n * 4,         S * mL * n * 4,          S * mL * n * 4,
+                          S * n * 4,              S * nchunk * cmax * 4,   S * n * 4,
+                          S * (nchunk + 1) * 4,   S * (cmax + 1) * 4,      S * (n / 8 + cmax + 1) * 4,
+                          S * n * 8};
   int64_t o = 0;
-  for (int i = 0; i < 9; ++i) {
+  for (int i = 0; i < 10; ++i) {
     off[i] = o;
     o = align_up(o + sz[i]);
   }
@@ -203,7 +204,7 @@ int64_t scratch_offsets(const ice_params *prm, int32_t S, int64_t n, int64_t off
 }
 
 int64_t scratch_size(const ice_params *prm, int32_t S, int64_t n) {
-  int64_t off[9];
+  int64_t off[10];
   return scratch_offsets(prm, S, n, off);
 }
 
@@ -333,7 +334,7 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
   std::memset(&bs, 0, sizeof(bs));
   if (n_tokens > 0) {
     char *sc = (char *)scratch;
-    int64_t off[9];
+    int64_t off[10];
     scratch_offsets(prm, n_streams, n_tokens, off);
     bs.codes_dm = (int32_t *)(sc + off[0]);
     bs.tmp_code = (int32_t *)(sc + off[1]);
@@ -344,6 +345,7 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
     bs.chunk_pg = (int32_t *)(sc + off[6]);
     bs.cell_pg = (int32_t *)(sc + off[7]);
     bs.page_of = (int32_t *)(sc + off[8]);
+    bs.nsq = (double *)(sc + off[9]);
   }
   hipError_t e = ice::launch_build(dv, bs, n_tokens, K, V, dirs, prm->c, (hipStream_t)stream);
   if (e != hipSuccess) {

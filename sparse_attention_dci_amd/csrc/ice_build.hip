@@ -60,8 +60,9 @@ __global__ void k_dirs(Dev dv, const void *dirs) {
 
 // ---------------------------------------------------------------- norms
 
-// Largest |k|^2 per stream (fp64, ascending element order), as the bit
-// pattern of a non-negative double (order-preserving as an integer).  A block
+// |k|^2 of every key row (fp64, ascending element order), kept for the
+// projection, and the largest per stream, as the bit pattern of a
+// non-negative double (order-preserving as an integer).  A block
 // stages kNormRows consecutive key rows in LDS with coalesced 16-byte loads
 // (word-major, odd stride: the chain reads of one row per lane fall in
 // distinct banks), then one thread per row runs the chain, its reads a batch
@@ -144,7 +145,7 @@ __device__ __forceinline__ double row_norm2(const uint32_t *rw, int words) {
 }
 
 template <int DT>
-__global__ __launch_bounds__(256) void k_norms(Dev dv, const void *K, int64_t n) {
+__global__ __launch_bounds__(256) void k_norms(Dev dv, BuildScratch bs, const void *K, int64_t n) {
   constexpr int R = NormRows<DT>::kRows;
   __shared__ uint32_t rows[NormRows<DT>::kMaxWords * NormRows<DT>::kStride];
   __shared__ unsigned long long wmax[4];
@@ -154,7 +155,10 @@ __global__ __launch_bounds__(256) void k_norms(Dev dv, const void *K, int64_t n)
   stage_rows<DT>(dv, K, s, n, r0, rows);
   __syncthreads();
   double nsq = 0.0;
-  if (tid < R && r0 + tid < n) nsq = row_norm2<DT>(rows + tid, dv.d * (DT == 0 ? 4 : 2) / 4);
+  if (tid < R && r0 + tid < n) {
+    nsq = row_norm2<DT>(rows + tid, dv.d * (DT == 0 ? 4 : 2) / 4);
+    bs.nsq[(int64_t)s * n + r0 + tid] = nsq;
+  }
   unsigned long long b = (unsigned long long)__double_as_longlong(nsq);
   for (int off = 32; off >= 1; off >>= 1) {
     unsigned long long o = __shfl_xor(b, off);
@@ -180,67 +184,128 @@ __device__ __forceinline__ float stream_bound(const Dev &dv, int s, float c_fixe
   return c > 0.0f ? c : 1.0f;
 }
 
-// One thread = one token x one chunk of 16 directions (blockIdx.y).
-//   r_t = sum_e k_e u_te (fp64, ascending e, exact products)
+// Projection on the fp64 matrix cores.  v_mfma_f64_16x16x4f64 adds the four
+// products of its k-slice to the accumulator one after another, in k order,
+// each addition rounded (checked on gfx950 against sequential fma chains, also
+// with operands spread over 2^-40 .. 2^12), so a chain of HD/4 of them over
+// k = 0 .. HD-1 is the chain r_t = fma(k_e, u_te, r_t), ascending e, bit for
+// bit.  Every product of a key element and a direction element is exact in
+// fp64.  Then
 //   x_t = r_t * (1/c) + sqrt(max(0, 1 - |k|^2 (1/c)^2)) * u_td
 //   code_t = round(x_t * 2^29), saturated; cell = sign bits of r_t, t < D.
-template <int DT>
+//
+// A wave takes 16 tokens and every one of the NC chunks of 16 directions
+// (the keys are read once).  Lane (q, j) = (lane / 16, lane % 16):
+//   A  keys: lane (q, j) supplies element 4kk + q of token t0 + j; it loads
+//      the whole row in 16-byte pieces (the four lanes of a token share the
+//      addresses) and picks the elements of its residue q;
+//   B  directions, staged in LDS once per block as [NC][HD][16]: lane (q, j)
+//      supplies u_{16ct + j, 4kk + q}, 512 contiguous bytes per wave;
+//   D  lane (q, j), register r: token t0 + q + 4r, direction 16ct + j.
+// The waves of a block take consecutive tiles, so a block writes 64
+// consecutive tokens of every direction.  |k|^2 comes from k_norms.  (More
+// tiles per wave, for more independent chains, measured slower.)
+template <int DT, int HD>
+struct ProjRow {
+  static constexpr int kChunks = HD * (DT == 0 ? 4 : 2) / 16;  // 16-byte pieces per key row
+};
+
+template <int DT, int HD>
+__device__ __forceinline__ void proj_load_row(const char *kb, int64_t row, uint4 (&v)[ProjRow<DT, HD>::kChunks]) {
+  constexpr int CH = ProjRow<DT, HD>::kChunks;
+  const uint4 *rp = reinterpret_cast<const uint4 *>(kb + row * (int64_t)CH * 16);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) v[c] = rp[c];
+}
+
+// Element 4kk + q of the row held in v, as a double (q = lane / 16).
+template <int DT, int HD>
+__device__ __forceinline__ double proj_elem(const uint4 (&v)[ProjRow<DT, HD>::kChunks], int kk,
+                                            int q) {
+  if constexpr (DT == 0) {  // piece kk holds elements 4kk .. 4kk+3
+    const uint4 x = v[kk];
+    const uint32_t lo = (q & 1) ? x.y : x.x, hi = (q & 1) ? x.w : x.z;
+    return (double)__uint_as_float((q & 2) ? hi : lo);
+  } else {  // piece kk/2 holds elements 8(kk/2) .. +7; ours is 4(kk&1) + q in it
+    const uint4 x = v[kk >> 1];
+    const uint32_t wd = (kk & 1) ? ((q & 2) ? x.w : x.z) : ((q & 2) ? x.y : x.x);
+    return (double)__uint_as_float((q & 1) ? (wd & 0xffff0000u) : (wd << 16));
+  }
+}
+
+typedef double doublex4 __attribute__((ext_vector_type(4)));
+
+template <int DT, int HD, int NC>
 __global__ __launch_bounds__(256) void k_project(Dev dv, BuildScratch bs,
-                                                 const void *__restrict__ K,
-                                                 const double *__restrict__ dirs, int64_t n,
+                                                 const void *__restrict__ K, int64_t n,
                                                  float c_fixed) {
-  const int s = blockIdx.z, ch = blockIdx.y;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int d = dv.d, mL = dv.mL;
+  constexpr int CH = ProjRow<DT, HD>::kChunks;
+  __shared__ double su[NC * HD * kDirChunk];
+  const int s = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int q = lane >> 4, j = lane & 15;
+  const int mL = dv.mL;
   const float c = stream_bound(dv, s, c_fixed);
   const double inv_c = __ddiv_rn(1.0, (double)c);
   const double inv_c2 = __dmul_rn(inv_c, inv_c);
-  if (blockIdx.x == 0 && ch == 0 && threadIdx.x == 0) {
+  if (blockIdx.x == 0 && tid == 0) {
     dv.norm_c[s] = c;
     dv.inv_c[s] = inv_c;
     dv.inv_c2[s] = inv_c2;
   }
-  if (i >= n) return;
-  // wave-uniform addresses into a read-only argument: scalar loads
-  const double *__restrict__ dir = dirs + (size_t)ch * (d + 1) * kDirChunk;
-  double r[kDirChunk];
-#pragma unroll
-  for (int t = 0; t < kDirChunk; ++t) r[t] = 0.0;
-  double nsq = 0.0;
-  const int64_t base = ((int64_t)s * n + i) * d;
-  for (int e0 = 0; e0 < d; e0 += 8) {
-    float x[8];
-    load8<DT>(K, base + e0, x);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const double v = (double)x[j];
-      nsq = fma(v, v, nsq);
-      const double *u = dir + (e0 + j) * kDirChunk;
-#pragma unroll
-      for (int t = 0; t < kDirChunk; ++t) r[t] = fma(v, u[t], r[t]);
-    }
+  if (n == 0) return;
+  for (int x = tid; x < NC * HD * kDirChunk; x += 256) {  // rows e < HD of every chunk
+    const int ct = x / (HD * kDirChunk), r = x % (HD * kDirChunk);
+    su[x] = dv.dirs[(int64_t)ct * (HD + 1) * kDirChunk + r];
   }
-  double b = __dsub_rn(1.0, __dmul_rn(nsq, inv_c2));
-  if (b < 0.0) b = 0.0;
-  const double sv = __dsqrt_rn(b);
-  const int t0 = ch * kDirChunk;
-  const int nt = min(kDirChunk, mL - t0);
-  const double *ud = dir + (size_t)d * kDirChunk;
+  double ud[NC];  // u_{16ct + j, HD}
 #pragma unroll
-  for (int t = 0; t < kDirChunk; ++t) {
-    if (t < nt) {
-      const double x = __dadd_rn(__dmul_rn(r[t], inv_c), __dmul_rn(sv, ud[t]));
-      const int32_t code = to_code(x);
-      dv.codes[code_index(dv.ntile, mL, s, i, t0 + t)] = code;
-      bs.codes_dm[((int64_t)s * mL + t0 + t) * n + i] = code;
+  for (int ct = 0; ct < NC; ++ct) ud[ct] = dv.dirs[((int64_t)ct * (HD + 1) + HD) * kDirChunk + j];
+  __syncthreads();
+
+  const char *kb = reinterpret_cast<const char *>(K) + (int64_t)s * n * CH * 16;
+  const int64_t ntiles = (n + 15) / 16, stride = (int64_t)gridDim.x * 4;
+  for (int64_t tile = (int64_t)blockIdx.x * 4 + w; tile < ntiles; tile += stride) {
+    const int64_t t0 = tile * 16;
+    uint4 cur[CH];
+    proj_load_row<DT, HD>(kb, min(t0 + j, n - 1), cur);
+    double nsq[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) nsq[r] = bs.nsq[(int64_t)s * n + min(t0 + q + 4 * r, n - 1)];
+    doublex4 acc[NC];
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) acc[ct] = doublex4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int kk = 0; kk < HD / 4; ++kk) {
+      const double a = proj_elem<DT, HD>(cur, kk, q);
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct)
+        acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+            a, su[(ct * HD + 4 * kk + q) * kDirChunk + j], acc[ct], 0, 0, 0);
+      // keeps the direction reads from being hoisted all at once (registers)
+      if ((kk & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
-  }
-  if (ch == 0) {
-    uint32_t cl = 0;
 #pragma unroll
-    for (int t = 0; t < kDirChunk; ++t)
-      if (t < dv.D && r[t] >= 0.0) cl |= (1u << t);
-    bs.cell[(int64_t)s * n + i] = cl;
+    for (int r = 0; r < 4; ++r) {
+      const int64_t tok = t0 + q + 4 * r;
+      double bb = __dsub_rn(1.0, __dmul_rn(nsq[r], inv_c2));
+      if (bb < 0.0) bb = 0.0;
+      const double sv = __dsqrt_rn(bb);
+      // cell: sign bits of the first D directions (D <= 16: chunk 0)
+      const unsigned long long nonneg = __ballot(j < dv.D && acc[0][r] >= 0.0);
+      if (j == 0 && tok < n)
+        bs.cell[(int64_t)s * n + tok] = (uint32_t)(nonneg >> (16 * q)) & 0xffffu;
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) {
+        const int t = ct * kDirChunk + j;
+        const double x = __dadd_rn(__dmul_rn(acc[ct][r], inv_c), __dmul_rn(sv, ud[ct]));
+        if (t < mL && tok < n) {
+          const int32_t code = to_code(x);
+          dv.codes[code_index(dv.ntile, mL, s, tok, t)] = code;
+          bs.codes_dm[((int64_t)s * mL + t) * n + tok] = code;
+        }
+      }
+    }
   }
 }
 
@@ -656,6 +721,46 @@ __global__ __launch_bounds__(256) void k_scatter_v(Dev dv, const void *V, int64_
 
 // ---------------------------------------------------------------- launchers
 
+// Blocks per stream: enough tiles per block to amortise its direction
+// staging, about eight blocks per CU over all streams (a sweep of 512 to 4096
+// blocks put the best at 2048 for both the 36k and the 262k layers).
+template <int DT, int HD, int NC>
+static hipError_t launch_project_nc(const Dev &dv, const BuildScratch &bs, const void *K,
+                                    int64_t n, float c_fixed, hipStream_t st) {
+  const int64_t ntiles = (n + 15) / 16;
+  int64_t nb = (ntiles + 3) / 4;
+  const int64_t cap = 2048 / dv.S > 0 ? 2048 / dv.S : 1;
+  if (nb > cap) nb = cap;
+  if (nb < 1) nb = 1;
+  hipLaunchKernelGGL((k_project<DT, HD, NC>), dim3((unsigned)nb, dv.S), dim3(256), 0, st, dv, bs,
+                     K, n, c_fixed);
+  return hipGetLastError();
+}
+
+template <int DT, int HD>
+static hipError_t launch_project_hd(const Dev &dv, const BuildScratch &bs, const void *K,
+                                    int64_t n, float c_fixed, hipStream_t st) {
+  switch (dv.nchunk) {
+    case 1: return launch_project_nc<DT, HD, 1>(dv, bs, K, n, c_fixed, st);
+    case 2: return launch_project_nc<DT, HD, 2>(dv, bs, K, n, c_fixed, st);
+    case 3: return launch_project_nc<DT, HD, 3>(dv, bs, K, n, c_fixed, st);
+    case 4: return launch_project_nc<DT, HD, 4>(dv, bs, K, n, c_fixed, st);
+    case 5: return launch_project_nc<DT, HD, 5>(dv, bs, K, n, c_fixed, st);
+    case 6: return launch_project_nc<DT, HD, 6>(dv, bs, K, n, c_fixed, st);
+    case 7: return launch_project_nc<DT, HD, 7>(dv, bs, K, n, c_fixed, st);
+    case 8: return launch_project_nc<DT, HD, 8>(dv, bs, K, n, c_fixed, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DT>
+static hipError_t launch_project(const Dev &dv, const BuildScratch &bs, const void *K, int64_t n,
+                                 float c_fixed, hipStream_t st) {
+  static_assert(kMaxMl <= 8 * kDirChunk && kMaxTreeDepth <= kDirChunk, "chunks");
+  return dv.d == 64 ? launch_project_hd<DT, 64>(dv, bs, K, n, c_fixed, st)
+                    : launch_project_hd<DT, 128>(dv, bs, K, n, c_fixed, st);
+}
+
 template <int DT>
 static hipError_t build_impl(const Dev &dv, const BuildScratch &bs, int64_t n, const void *K,
                              const void *V, const void *dirs, float c_fixed, hipStream_t st) {
@@ -674,19 +779,14 @@ static hipError_t build_impl(const Dev &dv, const BuildScratch &bs, int64_t n, c
     hipLaunchKernelGGL(k_dirs<DT>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, dv,
                        dirs);
   }
-  if (n > 0) {
-    if (c_fixed <= 0.0f)
-      hipLaunchKernelGGL(k_norms<DT>,
-                         dim3((unsigned)((n + NormRows<DT>::kRows - 1) / NormRows<DT>::kRows), dv.S),
-                         dim3(256), 0, st, dv, K, n);
-    hipLaunchKernelGGL(k_project<DT>, dim3((unsigned)((n + 255) / 256), dv.nchunk, dv.S),
-                       dim3(256), 0, st, dv, bs, K, (const double *)dv.dirs, n, c_fixed);
+  if (n > 0)  // every row's |k|^2 (the projection needs them), and c when not fixed
+    hipLaunchKernelGGL(k_norms<DT>,
+                       dim3((unsigned)((n + NormRows<DT>::kRows - 1) / NormRows<DT>::kRows), dv.S),
+                       dim3(256), 0, st, dv, bs, K, n);
+  // (an empty build still fixes c, 1/c and 1/c^2)
+  if ((e = launch_project<DT>(dv, bs, K, n, c_fixed, st))) return e;
+  if (n > 0)
     hipLaunchKernelGGL(k_sort_lists<kSortItems>, dim3(dv.S * dv.mL), dim3(256), 0, st, dv, bs, n);
-  } else {
-    // an empty build still fixes c, 1/c and 1/c^2
-    hipLaunchKernelGGL(k_project<DT>, dim3(1, 1, dv.S), dim3(256), 0, st, dv, bs, K,
-                       (const double *)dv.dirs, n, c_fixed);
-  }
   if (n > 0) {
     const int64_t nchunk = (n + kPageChunk - 1) / kPageChunk;
     const int cmax = 1 << min(dv.mL, kMaxTreeDepth);

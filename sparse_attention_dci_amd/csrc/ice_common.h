@@ -107,6 +107,7 @@ struct BuildScratch {
   int32_t *chunk_pg;    // [S][nchunk + 1] pages opened per chunk, then their prefix
   int32_t *cell_pg;     // [S][cmax + 1] prefix of the cells' page counts
   int32_t *page_of;     // [S][n / 8 + cmax + 1] page id by (cell_pg[c] + ordinal in the cell)
+  double *nsq;          // [S][n] |k|^2 of every key row (fp64, ascending element order)
 };
 
 // Tokens per chunk of the build's page assignment.

@@ -205,6 +205,23 @@ def test_llama8b_layer_36k_workload(B):
         _check_query(idx, st, s, r, page_ids, n_pages, topk, out[s * w.g:(s + 1) * w.g], q_s)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_projection_wide_exponents(B, dtype):
+    """Key elements spread over 2^-30 .. 2^10: every fp64 partial sum of the
+    projection rounds differently under any reordering, so the codes (and
+    everything after them) match the oracle's sequential chain only if the
+    matrix-core projection accumulates in ascending element order."""
+    S, n, d, g = 2, 2100, 128, 2
+    gen = torch.Generator().manual_seed(71)
+    K = torch.randn(S, n, d, generator=gen) * torch.exp2(
+        torch.randint(-30, 11, (S, n, d), generator=gen).float())
+    V = torch.randn(S, n, d, generator=gen)
+    q = torch.randn(S * g, d, generator=gen) * 4.0
+    td = W.torch_dtype(dtype)
+    run_case(B, S=S, n=n, d=d, g=g, p=16, k=128, m=4, L=3, dtype=dtype, seed=71,
+             keys=(K.to(td), V.to(td), q.to(td)))
+
+
 def test_insert_equals_rebuild_on_gpu(B):
     """ice_insert x t, then query == rebuild over n+t tokens with the stored c
     and D, then the same query (every array and every output)."""
@@ -340,6 +357,51 @@ def test_decode_step_many_streams(B):
         r = st.query(q_s, literal=False)
         _check_index(a, st, s_, n + steps)
         _check_query(a, st, s_, r, pa, na, ta, oa[s_ * g:(s_ + 1) * g], q_s)
+
+
+def test_llama8b_decode_loop_36k_128_steps(B):
+    """The 32-layer decode loop's per-layer work at full size: one
+    36,864-token layer of 8 KV heads (32 query heads), 128 consecutive
+    ice_decode_step calls, each appending one fresh (k, v) per head and
+    querying with a fresh query cluster.  Two heads are followed by the oracle
+    (insert, literal P-DCI walk, rerank, page walk, fp64 attention) and must
+    match at every step; all 8 heads' index arrays are checked after the last
+    step for those two heads."""
+    w = W.WORKLOADS["llama8b_decode_36k"]
+    layer, steps, follow = 31, 128, (0, 5)
+    K, V, q0, U, _ = W.layer_inputs(w, layer=layer)
+    dev = torch.device("cuda")
+    print(f"[case] llama8b_decode_36k layer={layer} steps={steps}", flush=True)
+    idx = B.Index(K.to(dev), V.to(dev), U.to(dev), page_size=w.p, budget_k=w.k, m=w.m, L=w.L,
+                  gqa_group=w.g, capacity=w.n + steps)
+    res = []
+    ins = []
+    for t in range(steps):
+        kn, vn, qt = W.step_inputs(w, layer, t)
+        pg, npg, out, tk = idx.decode_step(kn.to(dev), vn.to(dev), qt.to(dev), with_topk=True)
+        res.append((pg.cpu(), npg.cpu(), out.cpu(), tk.cpu()))
+        ins.append((kn, vn, qt))
+    torch.cuda.synchronize()
+    prm = oracle.Params(d=w.d, p=w.p, k=w.k, m=w.m, L=w.L, g=w.g)
+    g = w.g
+    for s in follow:
+        st = oracle.OracleStream(prm, _np(K[s]), _np(V[s]), _np(U), n_cap=w.n + steps)
+        for t in range(steps):
+            kn, vn, qt = ins[t]
+            st.insert(_np(kn[s]), _np(vn[s]))
+            q_s = _np(qt[s * g:(s + 1) * g])
+            r = st.query(q_s)
+            pg, npg, out, tk = res[t]
+            nsel = int(npg[s])
+            np.testing.assert_array_equal(pg[s, :nsel].numpy(), r["page_ids"],
+                                          err_msg=f"pages, head {s} step {t}")
+            kk = len(r["topk"])
+            np.testing.assert_array_equal(tk[s, :kk].numpy(), r["topk"],
+                                          err_msg=f"top-k, head {s} step {t}")
+            ref = st.attend(q_s, r["page_ids"])
+            err = float(np.max(np.abs(out[s * g:(s + 1) * g].numpy() - ref)))
+            assert err <= ATTN_TOL, (s, t, err)
+        _check_index(idx, st, s, w.n + steps)
 
 
 def test_capacity_error(B):
