@@ -658,7 +658,11 @@ struct FinalShared {
   float wm[16 * 16], wl[16 * 16];
 };
 
-template <int DT, int D>
+// PER = union elements per thread (L * k0 <= PER * kFinalThreads): 1 when the
+// union holds at most 1,024 tokens, which keeps the per-element loops (and the
+// code the block has to fetch: most of this kernel's time is instruction
+// fetch on a cold cache) a quarter of the size.
+template <int DT, int D, int PER>
 __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, bool bounded,
                                                           int32_t *page_ids, int32_t *n_pages,
                                                           int32_t *topk_ids, const void *q,
@@ -721,7 +725,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
   // the rerank list and this thread's boundary entry, requested before the
   // first barrier (the barriers up to the attention order LDS only, so these
   // and the query loads stay in flight across them)
-  constexpr int kPer = kMaxCand / kFinalThreads;
+  constexpr int kPer = PER;
   const uint32_t nrr = k0e > 0 ? nrr_ld : 0u;
   int32_t pid[kPer], ppg[kPer];
   unsigned long long pkey[kPer];
@@ -879,7 +883,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
   int32_t* const rsid = reinterpret_cast<int32_t *>(&sh.skey[0]);
   int32_t* const rspg = rsid + kMaxCand;
   {
-    constexpr int kPer = kMaxCand / kFinalThreads;
+    constexpr int kPer = PER;
     unsigned long long kx[kPer];
     int32_t ix[kPer], px[kPer];
     uint32_t bkt[kPer], within[kPer], rnk[kPer];
@@ -1553,6 +1557,19 @@ static void launch_scan_r(const Dev &dv, int64_t n, unsigned grid, const void *q
 // The query over n tokens (token n - 1 inserted by the scan when k_new is
 // given): scan, the visit-budget passes when the walk is bounded (k1 < m * n),
 // collect, final.
+template <int DT, int PER>
+static void launch_final(const Dev &dv, int64_t n, bool bounded, int32_t *page_ids,
+                         int32_t *n_pages, int32_t *topk_ids, const void *q, float *out,
+                         hipStream_t st) {
+  static_assert(PER * kFinalThreads <= kMaxCand, "union arrays");
+  if (dv.d == 128)
+    hipLaunchKernelGGL((k_qfinal<DT, 128, PER>), dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n,
+                       bounded, page_ids, n_pages, topk_ids, q, out);
+  else
+    hipLaunchKernelGGL((k_qfinal<DT, 64, PER>), dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n,
+                       bounded, page_ids, n_pages, topk_ids, q, out);
+}
+
 template <int DT>
 static void query_tail(const Dev &dv, int64_t n, int64_t k1, int32_t *page_ids,
                        int32_t *n_pages, int32_t *topk_ids, const void *q, const void *k_new,
@@ -1576,12 +1593,11 @@ static void query_tail(const Dev &dv, int64_t n, int64_t k1, int32_t *page_ids,
   if (dv.L * dv.k0 > kMaxCand)
     hipLaunchKernelGGL(k_qfinal_big<DT>, dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n, bounded,
                        page_ids, n_pages, topk_ids);
-  else if (dv.d == 128)
-    hipLaunchKernelGGL((k_qfinal<DT, 128>), dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n,
-                       bounded, page_ids, n_pages, topk_ids, q, out);
+  else if (dv.L * dv.k0 <= kFinalThreads)
+    launch_final<DT, 1>(dv, n, bounded, page_ids, n_pages, topk_ids, q, out, st);
   else
-    hipLaunchKernelGGL((k_qfinal<DT, 64>), dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n,
-                       bounded, page_ids, n_pages, topk_ids, q, out);
+    launch_final<DT, kMaxCand / kFinalThreads>(dv, n, bounded, page_ids, n_pages, topk_ids, q,
+                                               out, st);
   timer_mark(tm, KID_QFINAL, st);
 }
 
