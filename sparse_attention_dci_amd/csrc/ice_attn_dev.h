@@ -239,28 +239,31 @@ __device__ __forceinline__ void attn_chunk(const Dev &dv, int s, int T0, const i
                         pr[1][0], pr[1][1], pr[1][2], pr[1][3]};
     split8(f, ph, pl);
   }
+  // a token's logit is -inf exactly where it is masked, for every head; bf16
+  // values are already the operand, so masking their packed words is all
+  uint32_t vmask[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    vmask[j] = (z[(2 * j) >> 2][(2 * j) & 3] == -INFINITY ? 0u : 0x0000ffffu) |
+               (z[(2 * j + 1) >> 2][(2 * j + 1) & 3] == -INFINITY ? 0u : 0xffff0000u);
 #pragma unroll
   for (int eb = 0; eb < EB; ++eb) {
-    float f[8];
+    u32x4 vh, vl;
     if constexpr (DT == 0) {
+      float f[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         f[j] = __uint_as_float(vr[eb][0][j]);
         f[4 + j] = __uint_as_float(vr[eb][1][j]);
       }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (z[j >> 2][j & 3] == -INFINITY) f[j] = 0.0f;
+      split8(f, vh, vl);
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f[2 * j] = __uint_as_float(vr[eb][0][j] << 16);
-        f[2 * j + 1] = __uint_as_float(vr[eb][0][j] & 0xffff0000u);
-      }
+      for (int j = 0; j < 4; ++j) vh[j] = vr[eb][0][j] & vmask[j];
     }
-    // a token's logit is -inf exactly where it is masked, for every head
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (z[j >> 2][j & 3] == -INFINITY) f[j] = 0.0f;
-    u32x4 vh, vl;
-    split8(f, vh, vl);
     floatx4 acc = st.o[eb];
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] *= rs_row[i];
