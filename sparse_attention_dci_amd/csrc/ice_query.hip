@@ -27,8 +27,12 @@
 
 namespace ice {
 
-constexpr int kScanThreads = 512;
-constexpr int kScanTpb = 1024;      // tokens per scan range / collect block
+// Scan and collect blocks: NT threads, 2 * NT tokens (two 64-token tiles per
+// wave).  512 by default; 640 when that puts every block of the launch on a
+// CU of its own and 512 would not (the 36,864-token layer: 232 blocks instead
+// of 296, 52.8 instead of 55.5 us per step), since a CU holding two blocks
+// finishes last.
+constexpr int kScanThreadsLo = 512, kScanThreadsHi = 640;
 constexpr int kFinalThreads = 1024;
 constexpr int kHashSlots = 8192;    // 2 * kMaxCand
 constexpr int kBndLds = 2048;       // boundary entries ranked in LDS
@@ -137,10 +141,10 @@ __device__ __forceinline__ int32_t ld_code(__amdgpu_buffer_rsrc_t r, uint32_t of
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
-// 1-D grid of S * max(1, ceil(n / kScanTpb)) blocks, 512 threads.  Block b
+// 1-D grid of S * max(1, ceil(n / kScanTpb)) blocks of NT threads.  Block b
 // serves stream b % S (consecutive blocks take different streams, so with S a
 // multiple of 8 all blocks of a stream land on one XCD and share its L2) and
-// the b / S-th range of kScanTpb = 1024 tokens: wave w takes tiles 2w and
+// the b / S-th range of kScanTpb = 2 * NT tokens: wave w takes tiles 2w and
 // 2w+1 of the range, lane j token j of a tile, and reads code t of its 64
 // tokens as one contiguous 256-byte load.  kPipe codes of each tile are in
 // flight at a time: every code slot is refilled with the code kPipe places
@@ -160,10 +164,10 @@ __device__ __forceinline__ int32_t ld_code(__amdgpu_buffer_rsrc_t r, uint32_t of
 // pool rows at the end.
 constexpr int kPipe = 16;
 
-template <int DT, bool LDS_HIST, int R>
-__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(6))) void k_qscan(Dev dv, int64_t n, const void *q,
+template <int DT, bool LDS_HIST, int R, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_qscan(Dev dv, int64_t n, const void *q,
                                                         const void *k_new, const void *v_new) {
-  constexpr int NT = kScanThreads;
+  constexpr int kScanTpb = 2 * NT;
   constexpr int W = R * kPipe;  // staged direction columns (>= mL, <= the stored row width)
   constexpr int W4 = W / 4;
   constexpr int kStage = (129 * W4 + NT - 1) / NT;
@@ -390,9 +394,10 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(6)
 constexpr int kCollectRowBytes = 32 * 1024;
 constexpr int kSubShift = kHistShift - kHistBits;  // second-level bins: M >> 9 & 2047
 
-template <int DT>
-__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_qcollect(
+template <int DT, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_qcollect(
     Dev dv, int64_t n, bool bounded) {
+  constexpr int kScanThreads = NT, kScanTpb = 2 * NT;
   const int s = blockIdx.x % dv.S;  // the scan's block-to-stream mapping
   const int64_t rng = blockIdx.x / dv.S;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1532,25 +1537,46 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
 
 // ---------------------------------------------------------------- launcher
 
-template <int DT, bool LH, int R>
+template <int DT, bool LH, int R, int NT>
 static void launch_scan(const Dev &dv, int64_t n, unsigned grid, const void *q, const void *k_new,
                         const void *v_new, hipStream_t st) {
-  hipLaunchKernelGGL((k_qscan<DT, LH, R>), dim3(grid), dim3(kScanThreads), 0, st, dv, n, q, k_new,
+  hipLaunchKernelGGL((k_qscan<DT, LH, R, NT>), dim3(grid), dim3(NT), 0, st, dv, n, q, k_new,
                      v_new);
 }
 
-template <int DT, bool LH>
+template <int DT, bool LH, int NT>
 static void launch_scan_r(const Dev &dv, int64_t n, unsigned grid, const void *q,
                           const void *k_new, const void *v_new, hipStream_t st) {
   switch ((dv.mL + kPipe - 1) / kPipe) {
-    case 1: launch_scan<DT, LH, 1>(dv, n, grid, q, k_new, v_new, st); break;
-    case 2: launch_scan<DT, LH, 2>(dv, n, grid, q, k_new, v_new, st); break;
-    case 3: launch_scan<DT, LH, 3>(dv, n, grid, q, k_new, v_new, st); break;
-    case 4: launch_scan<DT, LH, 4>(dv, n, grid, q, k_new, v_new, st); break;
-    case 5: launch_scan<DT, LH, 5>(dv, n, grid, q, k_new, v_new, st); break;
-    case 6: launch_scan<DT, LH, 6>(dv, n, grid, q, k_new, v_new, st); break;
-    case 7: launch_scan<DT, LH, 7>(dv, n, grid, q, k_new, v_new, st); break;
-    default: launch_scan<DT, LH, 8>(dv, n, grid, q, k_new, v_new, st); break;  // mL <= 128
+    case 1: launch_scan<DT, LH, 1, NT>(dv, n, grid, q, k_new, v_new, st); break;
+    case 2: launch_scan<DT, LH, 2, NT>(dv, n, grid, q, k_new, v_new, st); break;
+    case 3: launch_scan<DT, LH, 3, NT>(dv, n, grid, q, k_new, v_new, st); break;
+    case 4: launch_scan<DT, LH, 4, NT>(dv, n, grid, q, k_new, v_new, st); break;
+    case 5: launch_scan<DT, LH, 5, NT>(dv, n, grid, q, k_new, v_new, st); break;
+    case 6: launch_scan<DT, LH, 6, NT>(dv, n, grid, q, k_new, v_new, st); break;
+    case 7: launch_scan<DT, LH, 7, NT>(dv, n, grid, q, k_new, v_new, st); break;
+    default: launch_scan<DT, LH, 8, NT>(dv, n, grid, q, k_new, v_new, st); break;  // mL <= 128
+  }
+}
+
+// Scan and collect over n tokens with NT-thread blocks of 2 * NT tokens.
+template <int DT, int NT>
+static void scan_collect(const Dev &dv, int64_t n, bool bounded, uint32_t k1, const void *q,
+                         const void *k_new, const void *v_new, hipStream_t st, Timer *tm) {
+  const int64_t nrange = (n + 2 * NT - 1) / (2 * NT);
+  const unsigned grid = (unsigned)(max(nrange, (int64_t)1) * dv.S);
+  if (dv.L <= 6)
+    launch_scan_r<DT, true, NT>(dv, n, grid, q, k_new, v_new, st);
+  else
+    launch_scan_r<DT, false, NT>(dv, n, grid, q, k_new, v_new, st);
+  timer_mark(tm, KID_QSCAN, st);
+  if (bounded) {
+    launch_visit_budget(dv, n, k1, st);
+    timer_mark(tm, KID_VISIT, st);
+  }
+  if (n > 0) {
+    hipLaunchKernelGGL((k_qcollect<DT, NT>), dim3(grid), dim3(NT), 0, st, dv, n, bounded);
+    timer_mark(tm, KID_QCOLLECT, st);
   }
 }
 
@@ -1574,22 +1600,14 @@ template <int DT>
 static void query_tail(const Dev &dv, int64_t n, int64_t k1, int32_t *page_ids,
                        int32_t *n_pages, int32_t *topk_ids, const void *q, const void *k_new,
                        const void *v_new, float *out, hipStream_t st, Timer *tm) {
-  const int64_t nrange = (n + kScanTpb - 1) / kScanTpb;
-  const unsigned grid = (unsigned)(max(nrange, (int64_t)1) * dv.S);
-  if (dv.L <= 6)
-    launch_scan_r<DT, true>(dv, n, grid, q, k_new, v_new, st);
-  else
-    launch_scan_r<DT, false>(dv, n, grid, q, k_new, v_new, st);
-  timer_mark(tm, KID_QSCAN, st);
   const bool bounded = n > 0 && k1 > 0 && k1 < (int64_t)dv.m * n;
-  if (bounded) {
-    launch_visit_budget(dv, n, (uint32_t)k1, st);
-    timer_mark(tm, KID_VISIT, st);
-  }
-  if (n > 0) {
-    hipLaunchKernelGGL(k_qcollect<DT>, dim3(grid), dim3(kScanThreads), 0, st, dv, n, bounded);
-    timer_mark(tm, KID_QCOLLECT, st);
-  }
+  const int64_t cus = 256;  // MI355X compute units
+  const int64_t blo = dv.S * ((n + 2 * kScanThreadsLo - 1) / (2 * kScanThreadsLo));
+  const int64_t bhi = dv.S * ((n + 2 * kScanThreadsHi - 1) / (2 * kScanThreadsHi));
+  if (blo > cus && bhi <= cus)
+    scan_collect<DT, kScanThreadsHi>(dv, n, bounded, (uint32_t)k1, q, k_new, v_new, st, tm);
+  else
+    scan_collect<DT, kScanThreadsLo>(dv, n, bounded, (uint32_t)k1, q, k_new, v_new, st, tm);
   if (dv.L * dv.k0 > kMaxCand)
     hipLaunchKernelGGL(k_qfinal_big<DT>, dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n, bounded,
                        page_ids, n_pages, topk_ids);
