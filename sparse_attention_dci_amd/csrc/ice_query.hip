@@ -137,8 +137,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void *base, u
                                            0x00020000);
 }
 
+// Codes are read once per query: non-temporal (nt), so the stream does not
+// push the rest of the step's working set (and the kernels' code) out of L2.
 __device__ __forceinline__ int32_t ld_code(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, /*nt*/ 2);
 }
 
 // 1-D grid of S * max(1, ceil(n / kScanTpb)) blocks of NT threads.  Block b
