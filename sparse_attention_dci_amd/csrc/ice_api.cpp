@@ -86,7 +86,7 @@ struct Layout {
   int64_t dirs, dirs32, norm_c, inv_c, inv_c2, maxnsq, codes, list_code, list_id, loc, page_tokens,
       page_len, page_cell, npages, cell_count, cell_last, pool_k, pool_v, qkv, qcode, mbuf,
       hist, hist2, cand, cand_count, bnd, bnd_rk, bnd_pg, bnd_count, rr_key, rr_id, rr_pg, rr_count,
-      attn_part, vhist, vstate, vtie, vcount;
+      attn_part, vhist, vstate, vtie, vcount, bsel;
   int64_t nvrange;
   int64_t total;
 };
@@ -181,6 +181,7 @@ ice_status make_layout(const ice_params *prm, int32_t S, int64_t n, int64_t ncap
   y.vstate = seg(Sl * Ll * 4 * 4);
   y.vtie = seg(Sl * Ll * y.nvrange * 4);
   y.vcount = seg(Sl * Ll * 4);
+  y.bsel = seg(Sl * Ll * 2 * 4);
   y.total = o;
   *L = y;
   return ICE_OK;
@@ -329,6 +330,7 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
   dv.vstate = (uint32_t *)(w + y.vstate);
   dv.vtie = (uint32_t *)(w + y.vtie);
   dv.vcount = (uint32_t *)(w + y.vcount);
+  dv.bsel = (uint32_t *)(w + y.bsel);
 
   ice::BuildScratch bs;
   std::memset(&bs, 0, sizeof(bs));

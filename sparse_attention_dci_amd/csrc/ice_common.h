@@ -88,6 +88,8 @@ struct Dev {
   uint32_t *vstate;         // [S][L][4] prefix / d*, remaining rank, t*, t* completes
   uint32_t *vtie;           // [S][L][nvrange] entries at distance d* per token range
   uint32_t *vcount;         // [S][L] n_l, the tokens the bounded walk completes
+  uint32_t *bsel;           // [S][L][2] the collect pass's threshold bin b* of each composite and
+                            // the count of tokens below it (for the finaliser)
 };
 
 // Build scratch (caller-owned, only used while the build runs).

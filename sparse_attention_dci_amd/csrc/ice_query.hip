@@ -16,7 +16,8 @@
 //   k_qcollect  tokens in bins below the k0-th smallest bin b* are
 //               candidates, tokens in bin b* are parked with their (M_i, i)
 //               key; both kinds are scored exactly (fp64, ascending element
-//               order) here, many blocks in parallel;
+//               order) here, many blocks in parallel; the first block of
+//               each stream publishes b* and the count below it;
 //   k_qfinal    one 1024-thread block per stream: exact selection inside the
 //               boundary bins, the union of the composites (LDS hash), a
 //               bucket sort by (score desc, token asc), top-k and the page
@@ -449,9 +450,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
   const float qk = dv.qkv[(int64_t)s * dv.d + min(tid, dv.d - 1)];
   for (int l = w; l < L; l += kScanThreads / 64) {
     const uint32_t kl = bounded ? min(k0e, dv.vcount[s * L + l]) : k0e;
-    uint32_t bb = 0, bl;
+    uint32_t bb = 0, bl = 0;
     if (kl > 0) wave_find_bin(dv.hist + ((int64_t)s * L + l) * kHistBins, kl, bb, bl);
-    if (lane == 0) bstar[l] = kl > 0 ? (int32_t)bb : -1;
+    if (lane == 0) {
+      bstar[l] = kl > 0 ? (int32_t)bb : -1;
+      if (rng == 0) {  // for the finaliser: b* and the count below it
+        dv.bsel[((int64_t)s * L + l) * 2] = bb;
+        dv.bsel[((int64_t)s * L + l) * 2 + 1] = bl;
+      }
+    }
   }
   if (tid < dv.d) qkv[tid] = qk;
   lloc[tid] = lc[0];
@@ -680,13 +687,14 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
   const int L = dv.L, k0 = dv.k0;
   const uint32_t k0e = (uint32_t)min((int64_t)k0, n);
 
-  // A. loads, all issued before any is used (one round trip): the two
-  // threshold levels of wave w's composite, the counts; thread tid also owns
-  // boundary entry ep of composite lp (for the prefetch below)
-  uint32_t h1[kBinsPerLane], h2[kBinsPerLane];
+  // A. loads, all issued before any is used (one round trip): the
+  // second-level histogram of wave w's composite and the count below its
+  // threshold bin b* (the collect pass found b*), the counts; thread tid also
+  // owns boundary entry ep of composite lp (for the prefetch below)
+  uint32_t h2[kBinsPerLane], bl_ld = 0;  // second-level histogram; count below b*
   if (w < L) {  // wave w's composite
-    wave_hist_load(dv.hist + ((int64_t)s * L + w) * kHistBins, h1);
     wave_hist_load(dv.hist2 + ((int64_t)s * L + w) * kHistBins, h2);
+    bl_ld = dv.bsel[((int64_t)s * L + w) * 2 + 1];
   }
   const uint32_t kl_ld = bounded && w < L ? dv.vcount[s * L + w] : k0e;
   const uint32_t nrr_ld = dv.rr_count[s];
@@ -708,16 +716,14 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
   {  // need, b2, need2 of composite l come from wave l alone (all zero when it takes no
      // candidates: k0e = 0, or a bounded walk that completes no token)
     for (int l = w; l < L; l += kFinalThreads / 64) {
-      uint32_t b, bl, b2, bl2;
-      if (l != w) {  // more composites than waves
-        wave_hist_load(dv.hist + ((int64_t)s * L + l) * kHistBins, h1);
+      uint32_t b2, bl2;
+      if (l != w)  // more composites than waves
         wave_hist_load(dv.hist2 + ((int64_t)s * L + l) * kHistBins, h2);
-      }
       const uint32_t kl = min(k0e, l == w ? kl_ld : (bounded ? dv.vcount[s * L + l] : k0e));
       uint32_t need = 0, need2 = 0;  // picks from the boundary bin (>= 1 when kl > 0) and
       b2 = 0;                        // from its second-level bin b2
-      if (kl > 0) {
-        wave_find_bin_regs(h1, kl, b, bl);
+      if (kl > 0) {  // the first-level bin b* and the count below it come from the collect pass
+        const uint32_t bl = l == w ? bl_ld : dv.bsel[((int64_t)s * L + l) * 2 + 1];
         need = kl - bl;
         wave_find_bin_regs(h2, need, b2, bl2);
         need2 = need - bl2;
@@ -1114,10 +1120,10 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
 
   // A. counts and the two threshold levels of every composite, all loads
   // issued before any is used
-  uint32_t h1[kBinsPerLane], h2[kBinsPerLane];
+  uint32_t h2[kBinsPerLane], bl_ld = 0;  // second-level histogram; count below b*
   if (w < L) {  // wave w's composite
-    wave_hist_load(dv.hist + ((int64_t)s * L + w) * kHistBins, h1);
     wave_hist_load(dv.hist2 + ((int64_t)s * L + w) * kHistBins, h2);
+    bl_ld = dv.bsel[((int64_t)s * L + w) * 2 + 1];
   }
   const uint32_t kl_ld = bounded && w < L ? dv.vcount[s * L + w] : k0e;
   const uint32_t nrr_ld = dv.rr_count[s];
@@ -1145,16 +1151,14 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
   {  // need, b2, need2 of composite l come from wave l alone (all zero when it takes no
      // candidates: k0e = 0, or a bounded walk that completes no token)
     for (int l = w; l < L; l += NT / 64) {
-      uint32_t b, bl, b2, bl2;
-      if (l != w) {  // more composites than waves
-        wave_hist_load(dv.hist + ((int64_t)s * L + l) * kHistBins, h1);
+      uint32_t b2, bl2;
+      if (l != w)  // more composites than waves
         wave_hist_load(dv.hist2 + ((int64_t)s * L + l) * kHistBins, h2);
-      }
       const uint32_t kl = min(k0e, l == w ? kl_ld : (bounded ? dv.vcount[s * L + l] : k0e));
       uint32_t need = 0, need2 = 0;  // picks from the boundary bin (>= 1 when kl > 0) and
       b2 = 0;                        // from its second-level bin b2
-      if (kl > 0) {
-        wave_find_bin_regs(h1, kl, b, bl);
+      if (kl > 0) {  // the first-level bin b* and the count below it come from the collect pass
+        const uint32_t bl = l == w ? bl_ld : dv.bsel[((int64_t)s * L + l) * 2 + 1];
         need = kl - bl;
         wave_find_bin_regs(h2, need, b2, bl2);
         need2 = need - bl2;
