@@ -108,13 +108,19 @@ __device__ __forceinline__ unsigned long long match_bits(uint32_t key, int bits,
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes with DPP moves (no LDS round trips):
+// row_shr 1, 2, 4, 8 scan each row of 16 lanes, row_bcast 15 and 31 carry
+// the row totals into the rows above.  Lanes whose DPP source is outside the
+// row, or rows the row mask excludes, add 0.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = __lane_id();
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(v, off);
-    if (lane >= off) v += y;
-  }
-  return v;
+  int x = (int)v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return (uint32_t)x;
 }
 
 // One whole wave: smallest bin b of a kHistBins histogram whose inclusive
@@ -159,8 +165,8 @@ __device__ void wave_find_bin_regs(const uint32_t (&v)[kBinsPerLane], uint32_t t
       run += v[k];
     }
   }
-  bin = __shfl(b, src);
-  below = __shfl(bl, src);
+  bin = (uint32_t)__builtin_amdgcn_readlane((int)b, src);  // src is wave-uniform
+  below = (uint32_t)__builtin_amdgcn_readlane((int)bl, src);
 }
 
 __device__ __forceinline__ void wave_find_bin(const uint32_t *h, uint32_t target, uint32_t &bin,
