@@ -13,7 +13,7 @@
 
 namespace ice {
 
-constexpr int kAttnWaves = kAttnTpb / 16;
+constexpr int kAttnWaves = kAttnTpb / kAttnChunk;
 constexpr int kAttnThreads = kAttnWaves * 64;
 
 // Grid (attn_nsplit, S), 1024 threads.  Block b covers tokens b*256 .. +255 of
@@ -39,7 +39,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(Dev dv, const void *q,
   AttnWave<D> st;
   attn_init(st);
   __syncthreads();
-  if (w * 16 < np * p) attn_chunk<DT, D, false, 1>(dv, s, w * 16, sel, np, qh, ql, st);
+  if (w * kAttnChunk < np * p)
+    attn_chunk<DT, D, false, kAttnChunk / 16>(dv, s, w * kAttnChunk, sel, np, qh, ql, st);
   attn_publish(st, w, g, wm, wl, red);
   __syncthreads();
   const int ns = dv.attn_nsplit;

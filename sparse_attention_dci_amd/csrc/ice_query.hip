@@ -1045,8 +1045,8 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
   attn_init(st);
   lds_barrier();
   const int np = sh.nsel;
-  for (int T0 = w * 16; T0 < np * dv.p; T0 += NW * 16)
-    attn_chunk<DT, D, false, 1>(dv, s, T0, sh.sel, np, qh, ql, st);
+  for (int T0 = w * kAttnChunk; T0 < np * dv.p; T0 += NW * kAttnChunk)
+    attn_chunk<DT, D, false, kAttnChunk / 16>(dv, s, T0, sh.sel, np, qh, ql, st);
   float *red = reinterpret_cast<float *>(&sh.skey[0]);
   attn_publish(st, w, dv.g, sh.wm, sh.wl, red);
   lds_barrier();
