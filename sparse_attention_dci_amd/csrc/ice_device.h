@@ -123,6 +123,34 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return (uint32_t)x;
 }
 
+// Smallest / largest 64-bit value over the 64 lanes (whole wave), by the
+// same DPP sequence as wave_incl_scan on both halves (lane 63 ends with the
+// result), broadcast.  Lanes without a DPP source take the identity.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long id,
+                                                      unsigned long long v) {
+  const int lo = __builtin_amdgcn_update_dpp((int)(uint32_t)id, (int)(uint32_t)v, CTRL, ROWMASK,
+                                             0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp((int)(uint32_t)(id >> 32), (int)(uint32_t)(v >> 32),
+                                             CTRL, ROWMASK, 0xf, false);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+template <bool MAX>
+__device__ __forceinline__ unsigned long long wave_minmax_u64(unsigned long long x) {
+  constexpr unsigned long long id = MAX ? 0ull : ~0ull;
+  auto op = [](unsigned long long a, unsigned long long b) { return MAX ? max(a, b) : min(a, b); };
+  x = op(x, dpp_u64<0x111, 0xf>(id, x));  // row_shr:1
+  x = op(x, dpp_u64<0x112, 0xf>(id, x));  // row_shr:2
+  x = op(x, dpp_u64<0x114, 0xf>(id, x));  // row_shr:4
+  x = op(x, dpp_u64<0x118, 0xf>(id, x));  // row_shr:8
+  x = op(x, dpp_u64<0x142, 0xa>(id, x));  // row_bcast:15
+  x = op(x, dpp_u64<0x143, 0xc>(id, x));  // row_bcast:31
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
 // One whole wave: smallest bin b of a kHistBins histogram whose inclusive
 // prefix reaches `target` (1 <= target <= total) and the count below b.  The
 // histogram is read by wave_hist_load (lane j holds bins 32j .. 32j+31) so

@@ -915,10 +915,8 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
         hi = max(hi, kx[j]);
       }
     }
-    for (int off = 32; off >= 1; off >>= 1) {
-      lo = min(lo, (unsigned long long)__shfl_xor((long long)lo, off));
-      hi = max(hi, (unsigned long long)__shfl_xor((long long)hi, off));
-    }
+    lo = wave_minmax_u64<false>(lo);
+    hi = wave_minmax_u64<true>(hi);
     if (lane == 0) {
       sh.wlo[w] = lo;
       sh.whi[w] = hi;
@@ -1344,10 +1342,8 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
       lo = min(lo, kx[j]);
       hi = max(hi, kx[j]);
     }
-  for (int off = 32; off >= 1; off >>= 1) {
-    lo = min(lo, (unsigned long long)__shfl_xor((long long)lo, off));
-    hi = max(hi, (unsigned long long)__shfl_xor((long long)hi, off));
-  }
+  lo = wave_minmax_u64<false>(lo);
+  hi = wave_minmax_u64<true>(hi);
   if (lane == 0) {
     sh.wlo[w] = lo;
     sh.whi[w] = hi;
