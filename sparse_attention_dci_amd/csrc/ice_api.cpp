@@ -27,7 +27,9 @@ struct Timer {
   std::vector<hipEvent_t> events;
   hipEvent_t make() {
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    // timestamps only: no system-scope release/acquire around each record,
+    // which would add its cache work to every timed kernel
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     events.push_back(e);
     return e;
   }
