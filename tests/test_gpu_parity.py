@@ -509,6 +509,29 @@ def test_visit_budget(B, k1):
         assert cc.max() == 0
 
 
+def test_visit_budget_llama8b_layer_36k(B):
+    """A bounded walk (k1 = m*n/3 visits per composite) on the full 36,864-token
+    layer: the visit-budget passes with the scan and collect grids of that size
+    (1,280-token blocks), two heads against the oracle's literal walk."""
+    w = W.WORKLOADS["llama8b_layer_36k"]
+    K, V, q, U, _ = W.layer_inputs(w, layer=3)
+    k1 = w.m * w.n // 3
+    dev = torch.device("cuda")
+    print(f"[case] llama8b_layer_36k k1={k1}", flush=True)
+    idx = B.Index(K.to(dev), V.to(dev), U.to(dev), page_size=w.p, budget_k=w.k, m=w.m, L=w.L,
+                  gqa_group=w.g, k1=k1, capacity=w.n + 8)
+    qd = q.to(dev)
+    page_ids, n_pages, topk = idx.query_pages(qd, with_topk=True)
+    out = idx.sparse_attn(qd, page_ids, n_pages)
+    torch.cuda.synchronize()
+    prm = oracle.Params(d=w.d, p=w.p, k=w.k, m=w.m, L=w.L, g=w.g, k1=k1)
+    for s in (1, 6):
+        st = oracle.OracleStream(prm, _np(K[s]), _np(V[s]), _np(U), n_cap=w.n + 8)
+        q_s = _np(q[s * w.g:(s + 1) * w.g])
+        r = st.query(q_s)
+        _check_query(idx, st, s, r, page_ids, n_pages, topk, out[s * w.g:(s + 1) * w.g], q_s)
+
+
 def test_visit_budget_ragged_fp32_inserts(B):
     run_case(B, S=3, n=2333, g=1, p=8, k=128, m=3, L=3, dtype="f32", inserts=4, k1=2500,
              seed=42)
