@@ -291,6 +291,14 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
   dv.nbuild = n_tokens;
   dv.nchunk = y.nchunk;
   dv.attn_nsplit = y.attn_nsplit;
+  {  // sizes the scan's blocks (256 on a whole MI355X; fewer on a partition)
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        ncu <= 0)
+      ncu = 256;
+    dv.ncu = ncu;
+  }
   dv.dirs = (double *)(w + y.dirs);
   dv.dirs32 = (float *)(w + y.dirs32);
   dv.mLp = (dv.mL + 31) / 32 * 32;

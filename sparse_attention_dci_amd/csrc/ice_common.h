@@ -47,6 +47,7 @@ struct Dev {
   int64_t ncap, pcap, ncell, nbuild;
   int nchunk;          // direction chunks of kDirChunk
   int attn_nsplit;     // attention blocks per stream, ceil(k / kAttnTpb)
+  int ncu;             // compute units of the device the index was built on
 
   double *dirs;        // [nchunk][d+1][16]
   float *dirs32;       // [d+1][mLp] element-major, mLp = mL rounded up to 32, zero past mL

@@ -1603,7 +1603,7 @@ static void query_tail(const Dev &dv, int64_t n, int64_t k1, int32_t *page_ids,
                        int32_t *n_pages, int32_t *topk_ids, const void *q, const void *k_new,
                        const void *v_new, float *out, hipStream_t st, Timer *tm) {
   const bool bounded = n > 0 && k1 > 0 && k1 < (int64_t)dv.m * n;
-  const int64_t cus = 256;  // MI355X compute units
+  const int64_t cus = dv.ncu;
   const int64_t blo = dv.S * ((n + 2 * kScanThreadsLo - 1) / (2 * kScanThreadsLo));
   const int64_t bhi = dv.S * ((n + 2 * kScanThreadsHi - 1) / (2 * kScanThreadsHi));
   if (blo > cus && bhi <= cus)
