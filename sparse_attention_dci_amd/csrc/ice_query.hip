@@ -51,10 +51,9 @@ constexpr int kMaxTies = 256;  // page budgets up to this take the fused attenti
 // (word w of row r at w * (cap + 1) + r), so the chain's reads, one row per
 // lane, fall in distinct banks; the reads run a batch of 8 words ahead of the
 // dependent fma chain (two register sets, as in dot_chain).
-template <int DT>
+template <int DT, int B = 8>
 __device__ __forceinline__ double row_chain(const float *qkv, const uint32_t *rw, int stride,
                                             int words) {
-  constexpr int B = 8;
   uint32_t r0[B], r1[B];
   float q0[2 * B], q1[2 * B];
   auto rd = [&](uint32_t (&r)[B], float (&qq)[2 * B], int w0) {
@@ -87,7 +86,7 @@ __device__ __forceinline__ double row_chain(const float *qkv, const uint32_t *rw
   return acc;
 }
 
-template <int DT, int NT, int ROWBYTES, typename SlotOf, typename Emit>
+template <int DT, int NT, int ROWBYTES, int B, typename SlotOf, typename Emit>
 __device__ void block_score(const Dev &dv, int s, uint32_t cnt, SlotOf slot_of, const float *qkv,
                             int32_t *lcs, uint32_t *rows, Emit emit) {
   const int tid = threadIdx.x;
@@ -125,7 +124,7 @@ __device__ void block_score(const Dev &dv, int s, uint32_t cnt, SlotOf slot_of, 
       }
     }
     lds_barrier();
-    if ((uint32_t)tid < nr) emit(b0 + tid, lcs[tid], row_chain<DT>(qkv, rows + tid, stride, row_words));
+    if ((uint32_t)tid < nr) emit(b0 + tid, lcs[tid], row_chain<DT, B>(qkv, rows + tid, stride, row_words));
     lds_barrier();
   }
 }
@@ -394,13 +393,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_
 // next 11 bits of M), which lets the finaliser resolve the boundary without
 // ranking it.  Appends take one device atomic per block and list, issued
 // before the scoring and consumed after it.
-constexpr int kCollectRowBytes = 32 * 1024;
 constexpr int kSubShift = kHistShift - kHistBits;  // second-level bins: M >> 9 & 2047
 
+// Two shapes: 640-thread blocks (one per CU) stage 32 KB of candidate rows and
+// read the scoring chains 8 words ahead; 512-thread blocks (many per CU, the
+// long contexts) stage 16 KB and read 4 ahead, so three blocks fit a CU (LDS
+// and registers) and more of their latency chains overlap.
+template <int NT>
+struct CollectShape {
+  static constexpr int kRowBytes = NT == 512 ? 16 * 1024 : 32 * 1024;
+  static constexpr int kAhead = NT == 512 ? 4 : 8;
+  static constexpr int kWavesPerEu = NT == 512 ? 6 : 4;
+};
+
 template <int DT, int NT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_qcollect(
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape<NT>::kWavesPerEu))) void k_qcollect(
     Dev dv, int64_t n, bool bounded) {
   constexpr int kScanThreads = NT, kScanTpb = 2 * NT;
+  constexpr int kCollectRowBytes = CollectShape<NT>::kRowBytes;
   const int s = blockIdx.x % dv.S;  // the scan's block-to-stream mapping
   const int64_t rng = blockIdx.x / dv.S;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -518,7 +528,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
   unsigned long long *skbp = skb;
   int32_t *spbp = spb;
   const int32_t *cidp = cid, *llocp = lloc;
-  block_score<DT, kScanThreads, kCollectRowBytes>(
+  block_score<DT, kScanThreads, kCollectRowBytes, CollectShape<NT>::kAhead>(
       dv, s, nc, [cidp, llocp](uint32_t j) { return llocp[cidp[j]]; }, qkv, lcs, rows,
       [skbp, spbp, p](uint32_t x, int32_t slotx, double sc) {
         skbp[x] = score_rank_key(sc);
