@@ -311,18 +311,17 @@ __global__ __launch_bounds__(256) void k_project(Dev dv, BuildScratch bs,
 
 // ---------------------------------------------------------------- list sort
 
-// Block-wide exclusive scan of one value per thread (256 threads).
-__device__ __forceinline__ uint32_t block_excl_scan256(uint32_t v, uint32_t *wsum) {
+// Exclusive scan over the 256 digits: thread tid < 256 holds digit tid's
+// value (the rest pass 0 and ignore the result).  Every thread of the block
+// calls it (two barriers inside).
+template <int NT>
+__device__ __forceinline__ uint32_t digit_excl_scan(uint32_t v, uint32_t *wsum) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  uint32_t incl = v;
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) wsum[w] = incl;
+  const uint32_t incl = wave_incl_scan(v);
+  if (lane == 63 && w < 4) wsum[w] = incl;
   __syncthreads();
   uint32_t pre = 0;
-  for (int k = 0; k < w; ++k) pre += wsum[k];
+  for (int k = 0; k < w && k < 4; ++k) pre += wsum[k];
   __syncthreads();
   return pre + incl - v;
 }
@@ -333,26 +332,32 @@ __device__ __forceinline__ uint32_t block_excl_scan256(uint32_t v, uint32_t *wsu
 // passes alternate between the scratch pair and the index lists, ending in
 // the index lists.  The four digit histograms come from one initial pass (a
 // pass never changes the multiset of keys).  A pass walks the list in tiles
-// of 256 x ITEMS entries; wave w owns the tile's w-th quarter, row j of it
-// being 64 consecutive entries:
+// of NT x ITEMS entries; wave w owns the tile's w-th part (64 x ITEMS
+// consecutive entries), row j of it being 64 consecutive entries:
 //   ranks  row by row, lanes with equal digits are matched with ballots and
 //          ranked after the wave's running count of that digit (LDS, updated
-//          by each digit's last lane); the four waves' counts, prefix-summed
-//          per digit, and the digits' starts in the tile complete every
-//          entry's stable rank within the tile;
+//          by each digit's last lane); per digit (one thread each) the waves'
+//          counts, prefix-summed over the waves, and the digits' starts in
+//          the tile complete every entry's stable rank within the tile;
 //   stage  the tile is written to LDS in digit order;
 //   write  consecutive threads copy consecutive staged entries to their
 //          digit's running position in the output, so each digit's run goes
 //          out as one coalesced stretch instead of one scattered word per
 //          entry.
-constexpr int kSortItems = 16;
+// Larger blocks mean fewer tiles per pass, and each tile pays the same chain
+// of round trips and barriers: 1024 x 12 sorts the 36k layer's lists in
+// 188 us and the 262k layer's in 4.2 ms (256 x 16: 310 us and 5.1 ms; a sweep
+// of 512-1024 threads x 8-24 items put 1024 x 12 first for both).
+constexpr int kSortThreads = 1024, kSortItems = 12;
 
-template <int ITEMS>
-__global__ __launch_bounds__(256) void k_sort_lists(Dev dv, BuildScratch bs, int64_t n) {
-  constexpr int NT = 256, TILE = NT * ITEMS, QUARTER = TILE / 4;
+template <int NT, int ITEMS>
+__global__ __launch_bounds__(NT) void k_sort_lists(Dev dv, BuildScratch bs, int64_t n) {
+  constexpr int NW = NT / 64, TILE = NT * ITEMS, PART = TILE / NW;
+  static_assert(NT >= 256, "one thread per digit");
   const int lst = blockIdx.x;  // s * mL + t
   const int s = lst / dv.mL, t = lst % dv.mL;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const bool digit = tid < 256;  // this thread owns digit tid
   const int32_t *in0 = bs.codes_dm + (int64_t)lst * n;
   int32_t *tc = bs.tmp_code + (int64_t)lst * n;
   int32_t *ti = bs.tmp_id + (int64_t)lst * n;
@@ -361,13 +366,12 @@ __global__ __launch_bounds__(256) void k_sort_lists(Dev dv, BuildScratch bs, int
 
   __shared__ uint32_t ghist[4][256];
   __shared__ uint32_t gbase[256], ls[256];
-  __shared__ uint32_t cntw[4][256];
+  __shared__ uint32_t cntw[NW][256];
   __shared__ uint32_t skey[TILE];
   __shared__ int32_t sval[TILE];
   __shared__ uint32_t wsum[4];
 
-#pragma unroll
-  for (int k = 0; k < 4; ++k) ghist[k][tid] = 0;
+  for (int x = tid; x < 4 * 256; x += NT) ghist[x >> 8][x & 255] = 0;
   __syncthreads();
   for (int64_t x = tid; x < n; x += NT) {
     const uint32_t key = (uint32_t)in0[x] ^ 0x80000000u;
@@ -383,7 +387,10 @@ __global__ __launch_bounds__(256) void k_sort_lists(Dev dv, BuildScratch bs, int
     const int32_t *si = pass == 0 ? nullptr : ((pass & 1) ? ti : oi);
     int32_t *dc = (pass & 1) ? oc : tc;
     int32_t *di = (pass & 1) ? oi : ti;
-    gbase[tid] = block_excl_scan256(ghist[pass][tid], wsum);
+    {
+      const uint32_t gb = digit_excl_scan<NT>(digit ? ghist[pass][tid] : 0u, wsum);
+      if (digit) gbase[tid] = gb;
+    }
 
     for (int64_t t0 = 0; t0 < n; t0 += TILE) {
       const int nv = (int)min((int64_t)TILE, n - t0);
@@ -391,7 +398,7 @@ __global__ __launch_bounds__(256) void k_sort_lists(Dev dv, BuildScratch bs, int
       int32_t val[ITEMS];
 #pragma unroll
       for (int j = 0; j < ITEMS; ++j) {  // clamped, unconditional loads
-        const int64_t x = t0 + w * QUARTER + j * 64 + lane;
+        const int64_t x = t0 + w * PART + j * 64 + lane;
         const int64_t xc = x < n ? x : n - 1;
         key[j] = (uint32_t)sc[xc] ^ 0x80000000u;
         val[j] = si ? si[xc] : (int32_t)x;
@@ -399,11 +406,11 @@ __global__ __launch_bounds__(256) void k_sort_lists(Dev dv, BuildScratch bs, int
 #pragma unroll
       for (int q = 0; q < 4; ++q) cntw[w][q * 64 + lane] = 0;
       __builtin_amdgcn_wave_barrier();
-      // ranks inside the wave's quarter, row by row
+      // ranks inside the wave's part, row by row
       uint32_t rank[ITEMS];
 #pragma unroll
       for (int j = 0; j < ITEMS; ++j) {
-        const bool valid = w * QUARTER + j * 64 + lane < nv;
+        const bool valid = w * PART + j * 64 + lane < nv;
         const uint32_t dig = (key[j] >> shift) & 255u;
         const unsigned long long mt = match_bits(dig, 8, __ballot(valid));
         const uint32_t before = valid ? cntw[w][dig] : 0u;
@@ -414,18 +421,24 @@ __global__ __launch_bounds__(256) void k_sort_lists(Dev dv, BuildScratch bs, int
       }
       __syncthreads();
       // per digit: the waves' offsets, the tile count and the digit's start
-      const uint32_t c0 = cntw[0][tid], c1 = cntw[1][tid], c2 = cntw[2][tid], c3 = cntw[3][tid];
-      const uint32_t run = c0 + c1 + c2 + c3;
-      cntw[0][tid] = 0;
-      cntw[1][tid] = c0;
-      cntw[2][tid] = c0 + c1;
-      cntw[3][tid] = c0 + c1 + c2;
-      ls[tid] = block_excl_scan256(run, wsum);  // (barriers inside)
+      uint32_t run = 0;
+      if (digit) {
+#pragma unroll
+        for (int k = 0; k < NW; ++k) {
+          const uint32_t c = cntw[k][tid];
+          cntw[k][tid] = run;
+          run += c;
+        }
+      }
+      {
+        const uint32_t st = digit_excl_scan<NT>(run, wsum);  // (barriers inside)
+        if (digit) ls[tid] = st;
+      }
       __syncthreads();
       // stage in digit order
 #pragma unroll
       for (int j = 0; j < ITEMS; ++j) {
-        if (w * QUARTER + j * 64 + lane < nv) {
+        if (w * PART + j * 64 + lane < nv) {
           const uint32_t dig = (key[j] >> shift) & 255u;
           const uint32_t pos = ls[dig] + cntw[w][dig] + rank[j];
           skey[pos] = key[j];
@@ -446,7 +459,7 @@ __global__ __launch_bounds__(256) void k_sort_lists(Dev dv, BuildScratch bs, int
         }
       }
       __syncthreads();
-      gbase[tid] += run;
+      if (digit) gbase[tid] += run;
     }
     __syncthreads();
   }
@@ -786,7 +799,8 @@ static hipError_t build_impl(const Dev &dv, const BuildScratch &bs, int64_t n, c
   // (an empty build still fixes c, 1/c and 1/c^2)
   if ((e = launch_project<DT>(dv, bs, K, n, c_fixed, st))) return e;
   if (n > 0)
-    hipLaunchKernelGGL(k_sort_lists<kSortItems>, dim3(dv.S * dv.mL), dim3(256), 0, st, dv, bs, n);
+    hipLaunchKernelGGL((k_sort_lists<kSortThreads, kSortItems>), dim3(dv.S * dv.mL),
+                       dim3(kSortThreads), 0, st, dv, bs, n);
   if (n > 0) {
     const int64_t nchunk = (n + kPageChunk - 1) / kPageChunk;
     const int cmax = 1 << min(dv.mL, kMaxTreeDepth);
