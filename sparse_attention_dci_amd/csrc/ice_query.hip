@@ -717,7 +717,18 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
     cc_ld = dv.cand_count[s * L + tid];
     nb_ld = dv.bnd_count[s * L + tid];
   }
-  for (int x = tid; x < kHashSlots; x += kFinalThreads) sh.hash[x] = 0;
+  // union membership: a bitmap over the tokens when they fit the table (one
+  // atomic test-and-set per token), else the LDS hash
+  const bool bitmap = n <= (int64_t)32 * kHashSlots;
+  const int hwords = bitmap ? (int)((n + 31) >> 5) : kHashSlots;
+  for (int x = tid; x < hwords; x += kFinalThreads) sh.hash[x] = 0;
+  auto mark = [&](int32_t id) -> bool {  // true when id was not in the union yet
+    if (bitmap) {
+      const uint32_t bit = 1u << (id & 31);
+      return (atomicOr(&sh.hash[id >> 5], bit) & bit) == 0u;
+    }
+    return hash_insert(sh.hash, id);
+  };
   if (tid < L) {
     sh.cc[tid] = cc_ld;
     sh.nb[tid] = nb_ld;
@@ -764,20 +775,18 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
   const int64_t po = ((int64_t)s * L + lp) * dv.ncap + (pv ? ep : 0u);
   const unsigned long long pbk = dv.bnd[po], pbrk = dv.bnd_rk[po];
   const int32_t pbpg = dv.bnd_pg[po];
+  if (w == 0) {  // the composites' boundary offsets: a prefix of the counts (lanes < L hold them)
+    const uint32_t v = k0e > 0 ? nb_ld : 0u;
+    const uint32_t incl = wave_incl_scan(v);
+    if (lane <= L) sh.boff[lane] = incl - v;
+    if (lane == 0) {
+      sh.nu = nrr;
+      sh.ntie = 0;
+    }
+  }
   lds_barrier();
   u32x4 qh[D / 32], ql[D / 32];  // needed by the attention only: in flight meanwhile
   attn_load_q<DT, D>(dv, s, q, qh, ql);
-  if (tid == 0) {
-    uint32_t o = 0;
-    for (int l = 0; l < L; ++l) {
-      sh.boff[l] = o;
-      o += (k0e > 0) ? sh.nb[l] : 0u;
-    }
-    sh.boff[L] = o;
-    sh.nu = nrr;
-    sh.ntie = 0;
-  }
-  lds_barrier();
   const uint32_t nbt = sh.boff[L];
   const bool bnd_lds = nbt <= (uint32_t)kBndLds;
 
@@ -787,7 +796,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
   for (int j = 0; j < kPer; ++j) {
     const uint32_t x = tid + kFinalThreads * j;
     if (x < nrr) {
-      hash_insert(sh.hash, pid[j]);
+      mark(pid[j]);
       sh.sid[x] = pid[j];
       sh.skey[x] = pkey[j];
       sh.spg[x] = ppg[j];
@@ -827,7 +836,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
   auto add_pick = [&](int l, unsigned long long key, unsigned long long rk, int32_t pg) {
     const int32_t id = (int32_t)(key & 0xffffffffull);
     dv.cand[((int64_t)s * L + l) * k0 + sh.cc[l] + atomicAdd(&sh.extra[l], 1u)] = id;
-    if (hash_insert(sh.hash, id)) {
+    if (mark(id)) {
       const uint32_t pos = atomicAdd(&sh.nu, 1u);
       sh.sid[pos] = id;
       sh.skey[pos] = rk;
