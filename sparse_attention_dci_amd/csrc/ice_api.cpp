@@ -291,6 +291,8 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
   dv.nbuild = n_tokens;
   dv.nchunk = y.nchunk;
   dv.attn_nsplit = y.attn_nsplit;
+  dv.lp = 0;
+  while ((1 << dv.lp) < dv.p) ++dv.lp;
   {  // sizes the scan's blocks (256 on a whole MI355X; fewer on a partition)
     int dev = 0, ncu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||

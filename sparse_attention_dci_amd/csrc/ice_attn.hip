@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(Dev dv, const void *q,
   __syncthreads();
   if (w * kAttnChunk < np * p)
     attn_chunk<DT, D, false, kAttnChunk / 16>(dv, s, w * kAttnChunk, sel, np, qh, ql, st);
-  attn_publish(st, w, g, wm, wl, red);
+  attn_publish(st, w, kAttnWaves, g, wm, wl, red);
   __syncthreads();
   const int ns = dv.attn_nsplit;
   for (int x = tid; x < g * D; x += kAttnThreads) {

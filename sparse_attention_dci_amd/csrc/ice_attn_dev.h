@@ -114,13 +114,13 @@ __device__ __forceinline__ void attn_chunk(const Dev &dv, int s, int T0, const i
                                            const u32x4 (&ql)[D / 32], AttnWave<D> &st) {
   constexpr int KK = D / 32, EB = D / 16;
   const int lane = __lane_id(), G = lane >> 4, c = lane & 15;
-  const int p = dv.p;
+  const int p = dv.p, lp = dv.lp, pm = dv.p - 1;  // p is a power of two
   const int64_t pcap = dv.pcap;
   int32_t pgk[2], pgv[2];
   bool okv[2] = {false, false};
 #pragma unroll
   for (int a = 0; a < NA; ++a) {
-    const int pik = (T0 + 16 * a + c) / p, piv = (T0 + 16 * a + 4 * G) / p;
+    const int pik = (T0 + 16 * a + c) >> lp, piv = (T0 + 16 * a + 4 * G) >> lp;
     const int32_t pk = sel[min(pik, np - 1)], pv = sel[min(piv, np - 1)];
     const bool okk = pik < np && pk >= 0 && pk < pcap;
     okv[a] = piv < np && pv >= 0 && pv < pcap;
@@ -138,7 +138,7 @@ __device__ __forceinline__ void attn_chunk(const Dev &dv, int s, int T0, const i
   for (int a = 0; a < NA; ++a) plen[a] = dv.page_len[(int64_t)s * pcap + pgv[a]];
 #pragma unroll
   for (int a = 0; a < NA; ++a) {
-    const int64_t row = ((int64_t)s * pcap + pgk[a]) * p + (T0 + 16 * a + c) % p;
+    const int64_t row = ((int64_t)s * pcap + pgk[a]) * p + ((T0 + 16 * a + c) & pm);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const int e0 = 32 * kk + 8 * G;
@@ -157,7 +157,7 @@ __device__ __forceinline__ void attn_chunk(const Dev &dv, int s, int T0, const i
 #pragma unroll
       for (int a = 0; a < NA; ++a) {
         const int64_t col =
-            (((int64_t)s * pcap + pgv[a]) * D + 16 * eb + c) * p + (T0 + 16 * a + 4 * G) % p;
+            (((int64_t)s * pcap + pgv[a]) * D + 16 * eb + c) * p + ((T0 + 16 * a + 4 * G) & pm);
         if constexpr (DT == 0) {
           vr[eb][a] = ld16(reinterpret_cast<const float *>(dv.pool_v) + col);
         } else {
@@ -199,7 +199,7 @@ __device__ __forceinline__ void attn_chunk(const Dev &dv, int s, int T0, const i
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int slot = (T0 + 16 * a + 4 * G + i) % p;
+      const int slot = (T0 + 16 * a + 4 * G + i) & pm;
       z[a][i] = (okv[a] && slot < plen[a]) ? acc[i] * scale : -INFINITY;
     }
   }
@@ -274,9 +274,11 @@ __device__ __forceinline__ void attn_chunk(const Dev &dv, int s, int T0, const i
   }
 }
 
-// Publishes a wave's state to LDS: wm/wl [nw][16], red [nw][g][D].
+// Publishes a wave's state to LDS: wm/wl [nw][16], red [nw][g][D] (then the
+// rows of heads g..15 of every wave, which nothing reads: red holds
+// nw * 16 * D floats, and the stores need no per-head branch).
 template <int D>
-__device__ __forceinline__ void attn_publish(const AttnWave<D> &st, int w, int g, float *wm,
+__device__ __forceinline__ void attn_publish(const AttnWave<D> &st, int w, int nw, int g, float *wm,
                                              float *wl, float *red) {
   const int lane = __lane_id(), G = lane >> 4, c = lane & 15;
   if (lane < 16) {
@@ -284,10 +286,12 @@ __device__ __forceinline__ void attn_publish(const AttnWave<D> &st, int w, int g
     wl[w * 16 + lane] = st.l;
   }
 #pragma unroll
-  for (int eb = 0; eb < D / 16; ++eb)
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * G + i;
+    const int64_t row = r < g ? (int64_t)w * g + r : (int64_t)nw * g + (int64_t)w * (16 - g) + (r - g);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (4 * G + i < g) red[((int64_t)w * g + 4 * G + i) * D + 16 * eb + c] = st.o[eb][i];
+    for (int eb = 0; eb < D / 16; ++eb) red[row * D + 16 * eb + c] = st.o[eb][i];
+  }
 }
 
 // Merge of nw published waves for output element x = h * D + e: the common

@@ -48,6 +48,7 @@ struct Dev {
   int nchunk;          // direction chunks of kDirChunk
   int attn_nsplit;     // attention blocks per stream, ceil(k / kAttnTpb)
   int ncu;             // compute units of the device the index was built on
+  int lp;              // log2 of the page size (a power of two)
 
   double *dirs;        // [nchunk][d+1][16]
   float *dirs32;       // [d+1][mLp] element-major, mLp = mL rounded up to 32, zero past mL

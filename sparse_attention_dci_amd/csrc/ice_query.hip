@@ -1065,7 +1065,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
   for (int T0 = w * kAttnChunk; T0 < np * dv.p; T0 += NW * kAttnChunk)
     attn_chunk<DT, D, false, kAttnChunk / 16>(dv, s, T0, sh.sel, np, qh, ql, st);
   float *red = reinterpret_cast<float *>(&sh.skey[0]);
-  attn_publish(st, w, dv.g, sh.wm, sh.wl, red);
+  attn_publish(st, w, NW, dv.g, sh.wm, sh.wl, red);
   lds_barrier();
   for (int x = tid; x < dv.g * D; x += kFinalThreads) {
     float M, num, den;
