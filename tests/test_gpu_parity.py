@@ -222,6 +222,13 @@ def test_projection_wide_exponents(B, dtype):
              keys=(K.to(td), V.to(td), q.to(td)))
 
 
+def test_small_union_hash_membership(B):
+    """More tokens than the finaliser's membership bitmap covers (262,144):
+    the small-union finaliser (L*k0 = 512) tracks the union in its LDS hash
+    instead; every stage against the oracle."""
+    run_case(B, S=1, n=263144, g=2, p=16, k=256, m=4, L=2, dtype="bf16", clusters=64, seed=81)
+
+
 def test_insert_equals_rebuild_on_gpu(B):
     """ice_insert x t, then query == rebuild over n+t tokens with the stored c
     and D, then the same query (every array and every output)."""
