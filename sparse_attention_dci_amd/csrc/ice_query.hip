@@ -821,11 +821,11 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
   }
   {  // a clean histogram for the next query: every read of it is done, and
      // the stores drain while the rest runs (no later barrier waits for them)
-    uint32_t *hist = dv.hist + (int64_t)s * L * kHistBins;
-    uint32_t *hist2 = dv.hist2 + (int64_t)s * L * kHistBins;
-    for (int x = tid; x < L * kHistBins; x += kFinalThreads) {
-      hist[x] = 0;
-      hist2[x] = 0;
+    uint4 *hist = reinterpret_cast<uint4 *>(dv.hist + (int64_t)s * L * kHistBins);
+    uint4 *hist2 = reinterpret_cast<uint4 *>(dv.hist2 + (int64_t)s * L * kHistBins);
+    for (int x = tid; x < L * kHistBins / 4; x += kFinalThreads) {  // 16-byte stores
+      hist[x] = make_uint4(0u, 0u, 0u, 0u);
+      hist2[x] = make_uint4(0u, 0u, 0u, 0u);
     }
   }
   lds_barrier();
@@ -1548,11 +1548,11 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
     for (uint32_t x = want_top + tid; x < (uint32_t)dv.k; x += NT)
       topk_ids[(int64_t)s * dv.k + x] = -1;
   if (tid < L && k0e > 0) dv.cand_count[s * L + tid] = sh.cc[tid] + sh.extra[tid];
-  uint32_t *hist = dv.hist + (int64_t)s * L * kHistBins;
-  uint32_t *hist2 = dv.hist2 + (int64_t)s * L * kHistBins;
-  for (int x = tid; x < L * kHistBins; x += NT) {
-    hist[x] = 0;
-    hist2[x] = 0;
+  uint4 *hist = reinterpret_cast<uint4 *>(dv.hist + (int64_t)s * L * kHistBins);
+  uint4 *hist2 = reinterpret_cast<uint4 *>(dv.hist2 + (int64_t)s * L * kHistBins);
+  for (int x = tid; x < L * kHistBins / 4; x += NT) {  // 16-byte stores
+    hist[x] = make_uint4(0u, 0u, 0u, 0u);
+    hist2[x] = make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
