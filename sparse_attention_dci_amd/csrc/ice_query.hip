@@ -179,7 +179,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_
   const int64_t r = blockIdx.x / S;
   const int64_t nold = k_new != nullptr ? n - 1 : n;  // tokens already in the index
   const bool ins = k_new != nullptr && r == nold / kScanTpb;  // this block inserts token nold
-  union ScanShared {
+  union __attribute__((aligned(16))) ScanShared {
     uint32_t hist[LDS_HIST ? 6 * kHistBins : 1];
     float dl[kStage * NT * 4];  // directions as [e][W] (row d holds u_t[d]), padded
   };
@@ -280,8 +280,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_
     }
     if (tid == 0) dv.rr_count[s] = 0;
   }
-  if (LDS_HIST) {
-    for (int x = tid; x < L * kHistBins; x += NT) sm.hist[x] = 0;
+  if (LDS_HIST) {  // 16-byte stores (the union is 16-byte aligned: float4 staging)
+    uint4 *h4 = reinterpret_cast<uint4 *>(sm.hist);
+    for (int x = tid; x < L * kHistBins / 4; x += NT) h4[x] = make_uint4(0u, 0u, 0u, 0u);
     lds_barrier();
   }
   uint32_t *hist = sm.hist;
