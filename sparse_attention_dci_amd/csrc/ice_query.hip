@@ -96,7 +96,8 @@ __device__ void block_score(const Dev &dv, int s, uint32_t cnt, SlotOf slot_of, 
   const uint32_t fit = (ROWBYTES / (row_bytes + 4)) & ~1u;
   const uint32_t cap = fit < (uint32_t)NT ? fit : NT;  // rows per round, even
   const int stride = (int)cap + 1;                      // odd
-  const int cpr = row_bytes / 16;             // 16-byte chunks per row
+  const int cpr = row_bytes / 16;             // 16-byte chunks per row (8, 16 or 32)
+  const int lcpr = __builtin_ctz((unsigned)cpr);
   constexpr int kIter = (ROWBYTES / 16 + NT - 1) / NT;
   for (uint32_t b0 = 0; b0 < cnt; b0 += cap) {
     const uint32_t nr = min(cap, cnt - b0);
@@ -106,7 +107,7 @@ __device__ void block_score(const Dev &dv, int s, uint32_t cnt, SlotOf slot_of, 
 #pragma unroll
     for (int k = 0; k < kIter; ++k) {  // unconditional loads (row 0 stands in past nr)
       const int x = tid + NT * k;
-      const int r = x / cpr, c = x % cpr;
+      const int r = x >> lcpr, c = x & (cpr - 1);
       const int rr = (uint32_t)r < nr ? r : 0;
       const int64_t row = ((int64_t)s * dv.pcap * dv.p + lcs[rr]) * row_bytes;
       v[k] = reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(dv.pool_k) + row)[c];
@@ -114,7 +115,7 @@ __device__ void block_score(const Dev &dv, int s, uint32_t cnt, SlotOf slot_of, 
 #pragma unroll
     for (int k = 0; k < kIter; ++k) {
       const int x = tid + NT * k;
-      const int r = x / cpr, c = x % cpr;
+      const int r = x >> lcpr, c = x & (cpr - 1);
       if ((uint32_t)r < nr) {
         uint32_t *dst = rows + (4 * c) * stride + r;
         dst[0] = v[k].x;
@@ -525,15 +526,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
   if (tid == 64) my_r = nrl ? atomicAdd(&dv.rr_count[s], nrl) : 0u;
 
   // 4. exact scores of the block's candidate and boundary tokens
-  const int p = dv.p;
+  const int lp = dv.lp;  // pages are 2^lp slots
   unsigned long long *skbp = skb;
   int32_t *spbp = spb;
   const int32_t *cidp = cid, *llocp = lloc;
   block_score<DT, kScanThreads, kCollectRowBytes, CollectShape<NT>::kAhead>(
       dv, s, nc, [cidp, llocp](uint32_t j) { return llocp[cidp[j]]; }, qkv, lcs, rows,
-      [skbp, spbp, p](uint32_t x, int32_t slotx, double sc) {
+      [skbp, spbp, lp](uint32_t x, int32_t slotx, double sc) {
         skbp[x] = score_rank_key(sc);
-        spbp[x] = slotx / p;
+        spbp[x] = slotx >> lp;
       });
 
   // 5. the appends
