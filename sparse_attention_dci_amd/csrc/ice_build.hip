@@ -695,12 +695,15 @@ __global__ __launch_bounds__(256) void k_scatter_v(Dev dv, const void *V, int64_
   const int cpr = row_bytes / 16;                          // 16-byte chunks per row
   const int epc = 16 / elem;                               // elements per 16 bytes
   const int cpe = p / epc;                                 // 16-byte chunks per column
+  // every size above is a power of two: index arithmetic by shifts
+  const int lp = dv.lp, lcpr = __builtin_ctz((unsigned)cpr), lcpe = __builtin_ctz((unsigned)cpe),
+            ld = __builtin_ctz((unsigned)d);
   __shared__ uint4 tile[kScatterTile / 16];
   const int64_t npg = dv.npages[s];
   for (int64_t pg0 = (int64_t)blockIdx.x * pb; pg0 < npg; pg0 += (int64_t)gridDim.x * pb) {
     const int np = (int)min((int64_t)pb, npg - pg0);
     for (int x = threadIdx.x; x < np * p * cpr; x += 256) {
-      const int j = x / (p * cpr), slot = (x / cpr) % p, ch = x % cpr;
+      const int j = x >> (lp + lcpr), slot = (x >> lcpr) & (p - 1), ch = x & (cpr - 1);
       const int32_t tok = dv.page_tokens[((int64_t)s * dv.pcap + pg0 + j) * p + slot];
       uint4 v = {0u, 0u, 0u, 0u};
       if (tok >= 0 && tok < n)
@@ -709,7 +712,7 @@ __global__ __launch_bounds__(256) void k_scatter_v(Dev dv, const void *V, int64_
     }
     __syncthreads();
     for (int x = threadIdx.x; x < np * d * cpe; x += 256) {
-      const int j = x / (d * cpe), e = (x / cpe) % d, c = x % cpe;
+      const int j = x >> (ld + lcpe), e = (x >> lcpe) & (d - 1), c = x & (cpe - 1);
       uint32_t wds[4];
       if (elem == 2) {
         const uint16_t *t16 = reinterpret_cast<const uint16_t *>(tile);
