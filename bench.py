@@ -212,6 +212,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--pregen", type=int, default=0,
+                    help="decode steps run on every layer copy before timing (a long generation)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--write-traffic", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
@@ -239,7 +241,7 @@ def main():
     R = max(args.layers, layers_per_step)
     total_calls = (args.warmup + 2 * args.steps) * layers_per_step
     per_layer = (total_calls + R - 1) // R + 1
-    cap = w.n + per_layer
+    cap = w.n + per_layer + args.pregen
 
     log(f"[bench] building {R} layers of {args.workload}")
     layers, build_ms = [], []
@@ -260,6 +262,13 @@ def main():
             keep = (K, V, q, U)
         del K, V
     log(f"[bench] build ms per layer: {[round(x, 2) for x in build_ms]}")
+    if args.pregen:  # a long generation on every copy before anything is timed
+        for r, idx in enumerate(layers):
+            for t in range(args.pregen):
+                k_new, v_new, q = W.step_inputs(w, layer=r, step=10 ** 6 + t, device=dev)
+                idx.decode_step(k_new, v_new, q)
+        torch.cuda.synchronize()
+        log(f"[bench] {args.pregen} tokens generated on every layer copy")
 
     steps_in = [W.step_inputs(w, layer=t % R, step=t, device=dev) for t in range(4 * R)]
     outs = [(torch.empty(w.streams, w.k // w.p, dtype=torch.int32, device=dev),
@@ -305,7 +314,9 @@ def main():
     log(f"[bench] per-kernel average us: { {k: round(v, 2) for k, v in avg_us.items()} }")
 
     cpu, n_cand = None, float(w.L * w.k)
-    if not args.no_cpu:
+    if not args.no_cpu and args.pregen:
+        log("[bench] no oracle baseline after a long generation (the oracle holds the built layer)")
+    if not args.no_cpu and not args.pregen:
         log("[bench] oracle cpu baseline")
         K, V, q, U = keep
         k_new, v_new, _ = W.step_inputs(w, layer=0, step=10 ** 6, device=dev)
@@ -318,7 +329,7 @@ def main():
                          + (f", times {layers_per_step} layers" if layers_per_step > 1 else "")
                          + "; oracle build untimed"}
 
-    ntok = w.n + per_layer // 2
+    ntok = w.n + args.pregen + per_layer // 2
     attended = float(w.k)
     kernels = {}
     fused = "attn" not in avg_us
@@ -361,6 +372,7 @@ def main():
                    "query_heads": w.streams * w.g, "context": w.n, "head_dim": w.d,
                    "page_size": w.p, "budget_k": w.k, "m": w.m, "L": w.L,
                    "layers_per_step": layers_per_step, "layers_rotated": R,
+                   "generated_before_timing": args.pregen,
                    "step": "ice_decode_step = insert + query_pages + sparse_attn"},
         "build_ms": round(sorted(build_ms)[len(build_ms) // 2], 3),
         "step_alg_gbs": round(step_alg / (ms_per_step * 1e-3) / 1e9, 1),

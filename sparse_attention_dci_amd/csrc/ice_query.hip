@@ -29,11 +29,10 @@
 namespace ice {
 
 // Scan and collect blocks: NT threads, 2 * NT tokens (two 64-token tiles per
-// wave).  512 by default; 640 when that puts every block of the launch on a
-// CU of its own and 512 would not (the 36,864-token layer: 232 blocks instead
-// of 296, 52.8 instead of 55.5 us per step), since a CU holding two blocks
-// finishes last.
-constexpr int kScanThreadsLo = 512, kScanThreadsHi = 640;
+// wave).  512 by default; when 512-thread blocks would not all get a CU of
+// their own, the smallest of 640, 768 and 1024 that does (the 36,864-token
+// layer: 232 blocks of 640 instead of 296 of 512, 52.8 instead of 55.5 us
+// per step), since a CU holding two blocks finishes last.
 constexpr int kFinalThreads = 1024;
 constexpr int kHashSlots = 8192;    // 2 * kMaxCand
 constexpr int kBndLds = 2048;       // boundary entries ranked in LDS
@@ -1625,12 +1624,15 @@ static void query_tail(const Dev &dv, int64_t n, int64_t k1, int32_t *page_ids,
                        const void *v_new, float *out, hipStream_t st, Timer *tm) {
   const bool bounded = n > 0 && k1 > 0 && k1 < (int64_t)dv.m * n;
   const int64_t cus = dv.ncu;
-  const int64_t blo = dv.S * ((n + 2 * kScanThreadsLo - 1) / (2 * kScanThreadsLo));
-  const int64_t bhi = dv.S * ((n + 2 * kScanThreadsHi - 1) / (2 * kScanThreadsHi));
-  if (blo > cus && bhi <= cus)
-    scan_collect<DT, kScanThreadsHi>(dv, n, bounded, (uint32_t)k1, q, k_new, v_new, st, tm);
+  auto fits = [&](int nt) { return dv.S * ((n + 2 * nt - 1) / (2 * nt)) <= cus; };
+  if (fits(512) || !fits(1024))
+    scan_collect<DT, 512>(dv, n, bounded, (uint32_t)k1, q, k_new, v_new, st, tm);
+  else if (fits(640))
+    scan_collect<DT, 640>(dv, n, bounded, (uint32_t)k1, q, k_new, v_new, st, tm);
+  else if (fits(768))
+    scan_collect<DT, 768>(dv, n, bounded, (uint32_t)k1, q, k_new, v_new, st, tm);
   else
-    scan_collect<DT, kScanThreadsLo>(dv, n, bounded, (uint32_t)k1, q, k_new, v_new, st, tm);
+    scan_collect<DT, 1024>(dv, n, bounded, (uint32_t)k1, q, k_new, v_new, st, tm);
   if (dv.L * dv.k0 > kMaxCand)
     hipLaunchKernelGGL(k_qfinal_big<DT>, dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n, bounded,
                        page_ids, n_pages, topk_ids);

@@ -411,6 +411,89 @@ def test_llama8b_decode_loop_36k_128_steps(B):
         _check_index(idx, st, s, w.n + steps)
 
 
+def test_long_generation_equals_rebuild(B):
+    """A long generation on the full 36,864-token layer: 2,048 consecutive
+    ice_decode_step calls (one generated token per head per step), then a
+    rebuild over all 38,912 tokens with the stored c and tree depth.  Every
+    index array and the next query's pages, top-k and attention are identical
+    (inserts never drift from a rebuild); one head also against the oracle."""
+    w = W.WORKLOADS["llama8b_decode_36k"]
+    layer, steps = 7, 2048
+    K, V, q0, U, _ = W.layer_inputs(w, layer=layer)
+    dev = torch.device("cuda")
+    print(f"[case] long generation layer={layer} steps={steps}", flush=True)
+    cap = w.n + steps
+    a = B.Index(K.to(dev), V.to(dev), U.to(dev), page_size=w.p, budget_k=w.k, m=w.m, L=w.L,
+                gqa_group=w.g, capacity=cap)
+    ks, vs = [], []
+    for t in range(steps):
+        kn, vn, qt = W.step_inputs(w, layer, t, device=dev)
+        a.decode_step(kn, vn, qt)
+        ks.append(kn)
+        vs.append(vn)
+    torch.cuda.synchronize()
+    Kall = torch.cat([K.to(dev), torch.stack(ks, 1)], 1).contiguous()
+    Vall = torch.cat([V.to(dev), torch.stack(vs, 1)], 1).contiguous()
+    c = a.view("norm_c").cpu()
+    D = a.layout()["tree_depth"]
+    _, _, qn = W.step_inputs(w, layer, steps, device=dev)
+    pa, na, ta = a.query_pages(qn, with_topk=True)
+    oa = a.sparse_attn(qn, pa, na)
+    n = w.n + steps
+    for s in range(w.streams):
+        b = B.Index(Kall[s:s + 1], Vall[s:s + 1], U.to(dev), page_size=w.p, budget_k=w.k, m=w.m,
+                    L=w.L, gqa_group=w.g, capacity=cap, c=float(c[s]), tree_depth=D)
+        qs = qn[s * w.g:(s + 1) * w.g].contiguous()
+        pb, nb, tb = b.query_pages(qs, with_topk=True)
+        ob = b.sparse_attn(qs, pb, nb)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view("codes")[s, :n], b.view("codes")[0, :n])
+        la, lb = _logical_lists(a, s), _logical_lists(b, 0)
+        assert np.array_equal(la[0], lb[0]) and np.array_equal(la[1], lb[1])
+        assert torch.equal(a.view("loc")[s, :n], b.view("loc")[0, :n])
+        npg = int(a.view("npages")[s])
+        assert npg == int(b.view("npages")[0])
+        for f in ("page_tokens", "page_len", "page_cell"):
+            assert torch.equal(a.view(f)[s, :npg], b.view(f)[0, :npg]), f
+        assert torch.equal(pa[s], pb[0]) and torch.equal(na[s], nb[0]) and torch.equal(ta[s], tb[0])
+        assert torch.equal(oa[s * w.g:(s + 1) * w.g], ob)
+        del b
+    prm = oracle.Params(d=w.d, p=w.p, k=w.k, m=w.m, L=w.L, g=w.g)
+    s = 3
+    st = oracle.OracleStream(prm, _np(Kall[s, :w.n]), _np(Vall[s, :w.n]), _np(U), n_cap=cap)
+    for t in range(steps):
+        st.insert(_np(Kall[s, w.n + t]), _np(Vall[s, w.n + t]))
+    q_s = _np(qn[s * w.g:(s + 1) * w.g])
+    r = st.query(q_s)
+    _check_query(a, st, s, r, pa, na, ta, oa[s * w.g:(s + 1) * w.g], q_s)
+
+
+@pytest.mark.parametrize("n", [45000, 60000])
+def test_scan_block_shapes(B, n):
+    """8 streams of 45,000 and 60,000 tokens: scan and collect blocks of 768 and
+    1,024 threads (the smallest shape that gives every block its own CU), with
+    a decode step; two streams against the oracle."""
+    S, g, d, p, m, L, k = 8, 4, 128, 16, 8, 4, 256
+    dev = torch.device("cuda")
+    K, V, q, _ = _inputs(S, n + 1, d, g, 64, 91, "bf16")
+    U = W.directions(m * L, d, 91, "bf16").to(dev)
+    print(f"[case] block shapes n={n}", flush=True)
+    idx = B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U, page_size=p,
+                  budget_k=k, m=m, L=L, gqa_group=g, capacity=n + 1)
+    qd = q.to(dev)
+    pg, npg, out, tk = idx.decode_step(K[:, n].contiguous().to(dev), V[:, n].contiguous().to(dev),
+                                        qd, with_topk=True)
+    torch.cuda.synchronize()
+    prm = oracle.Params(d=d, p=p, k=k, m=m, L=L, g=g)
+    for s in (0, 5):
+        st = oracle.OracleStream(prm, _np(K[s, :n]), _np(V[s, :n]), _np(U), n_cap=n + 1)
+        st.insert(_np(K[s, n]), _np(V[s, n]))
+        q_s = _np(q[s * g:(s + 1) * g])
+        r = st.query(q_s)
+        _check_index(idx, st, s, n + 1)
+        _check_query(idx, st, s, r, pg, npg, tk, out[s * g:(s + 1) * g], q_s)
+
+
 def test_capacity_error(B):
     dev = torch.device("cuda")
     K, V, q, _ = _inputs(1, 40, 128, 1, 4, 13, "bf16")
