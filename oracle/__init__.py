@@ -276,6 +276,11 @@ class OracleStream:
         self.lid = np.zeros((prm.mL, self.n_cap), np.int32)
         for t in range(prm.mL):
             self.lcode[t, :n], self.lid[t, :n] = sort_list(codes, t)
+        # the lists as the build sorted them (before any insert), for tests that
+        # check a stored build order without re-sorting it
+        self.n_build = n
+        self.lcode_build = self.lcode[:, :n].copy()
+        self.lid_build = self.lid[:, :n].copy()
         # DCI-tree leaves as pages
         p = prm.p
         self.page_of = np.full(self.n_cap, -1, np.int32)

@@ -1658,10 +1658,13 @@ hipError_t launch_decode(const Dev &dv, int64_t n, int64_t k1, const void *k_new
                          const void *v_new, const void *q, int32_t *page_ids, int32_t *n_pages,
                          int32_t *topk_ids, float *out, hipStream_t st, Timer *tm) {
   // the new token is token n (inserted by the scan); the query sees n + 1
-  // tokens.  Pages up to kFusedMaxPages and unions that fit LDS: the
-  // finaliser runs the attention itself.
+  // tokens.  Budgets of one attention split (kAttnTpb tokens) and unions that
+  // fit LDS: the finaliser runs the attention itself, with the standalone
+  // kernel's arithmetic (16 waves of one chunk, merged by their maxima).
+  // Larger budgets take the standalone kernels, whose per-split partials and
+  // merge fix the summation order, so the step equals the separate calls.
   timer_begin(tm, st);
-  const bool fused = dv.P <= kFusedMaxPages && dv.L * dv.k0 <= kMaxCand;
+  const bool fused = dv.attn_nsplit == 1 && dv.L * dv.k0 <= kMaxCand;
   float *fo = fused ? out : nullptr;
   if (dv.dtype == 0)
     query_tail<0>(dv, n + 1, k1, page_ids, n_pages, topk_ids, q, k_new, v_new, fo, st, tm);

@@ -41,17 +41,38 @@ def _np(t):
     return t.float().cpu().numpy() if t.dtype in (torch.bfloat16, torch.float32) else t.cpu().numpy()
 
 
-def _logical_lists(idx, s):
-    """Per-direction lists: sorted build entries merged with inserted entries."""
-    lc = idx.view("list_code")[s].cpu().numpy()
-    li = idx.view("list_id")[s].cpu().numpy()
+def _stored_lists(idx, s):
+    """The per-direction lists of stream s as stored: [mL][n] codes and ids."""
     n = idx.layout()["n_tokens"]
+    lc = idx.view("list_code")[s, :, :n].cpu().numpy()
+    li = idx.view("list_id")[s, :, :n].cpu().numpy()
+    return lc, li
+
+
+def _check_list_storage(idx, s, codes):
+    """The stored lists keep the documented order: entries [0, n_build) sorted
+    by (code, token), then the inserted tokens n_build .. n-1 in insertion
+    order with their codes.  `codes` is the expected [n][mL] code table."""
+    lay = idx.layout()
+    nb, n = lay["n_build"], lay["n_tokens"]
+    lc, li = _stored_lists(idx, s)
+    for t in range(lc.shape[0]):
+        c, i = lc[t, :nb].astype(np.int64), li[t, :nb].astype(np.int64)
+        assert np.all((c[1:] > c[:-1]) | ((c[1:] == c[:-1]) & (i[1:] > i[:-1]))), t
+    np.testing.assert_array_equal(li[:, nb:], np.broadcast_to(np.arange(nb, n), (lc.shape[0], n - nb)))
+    np.testing.assert_array_equal(lc[:, nb:], codes[nb:n].T)
+
+
+def _logical_lists(idx, s):
+    """Per-direction lists in logical order: the sorted build prefix merged
+    with the inserted entries (checked to be stored in the documented order
+    before they are merged)."""
+    lc, li = _stored_lists(idx, s)
     out_c, out_i = [], []
     for t in range(lc.shape[0]):
-        c, i = lc[t, :n], li[t, :n]
-        o = np.lexsort((i, c))
-        out_c.append(c[o])
-        out_i.append(i[o])
+        o = np.lexsort((li[t], lc[t]))
+        out_c.append(lc[t][o])
+        out_i.append(li[t][o])
     return np.stack(out_c), np.stack(out_i)
 
 
@@ -61,6 +82,14 @@ def _check_index(idx, st, s, n):
     assert lay["tree_depth"] == st.D
     assert idx.view("norm_c")[s].item() == np.float32(st.c)
     np.testing.assert_array_equal(idx.view("codes")[s, :n].cpu().numpy(), st.codes[:n])
+    # the build prefix as stored (no re-sort) equals the oracle's build-time
+    # lists; the inserted tail is in insertion order; then the merge
+    nb = lay["n_build"]
+    assert nb == st.n_build
+    lc, li = _stored_lists(idx, s)
+    np.testing.assert_array_equal(lc[:, :nb], st.lcode_build)
+    np.testing.assert_array_equal(li[:, :nb], st.lid_build)
+    _check_list_storage(idx, s, st.codes)
     lc, li = _logical_lists(idx, s)
     np.testing.assert_array_equal(lc, st.lcode[:, :n])
     np.testing.assert_array_equal(li, st.lid[:, :n])
@@ -255,6 +284,8 @@ def test_insert_equals_rebuild_on_gpu(B):
         ob = b.sparse_attn(qd[s * g:(s + 1) * g].contiguous(), pb, nb)
         torch.cuda.synchronize()
         assert torch.equal(a.view("codes")[s, :n + t], b.view("codes")[0, :n + t])
+        _check_list_storage(a, s, a.view("codes")[s].cpu().numpy())
+        _check_list_storage(b, 0, b.view("codes")[0].cpu().numpy())
         la = _logical_lists(a, s)
         lb = _logical_lists(b, 0)
         assert np.array_equal(la[0], lb[0]) and np.array_equal(la[1], lb[1])
@@ -291,19 +322,30 @@ def test_repeated_queries_are_deterministic(B):
                 assert torch.equal(a_, b_)
 
 
-@pytest.mark.parametrize("dtype,S,g,d,p,m,L,k", [("bf16", 8, 4, 128, 16, 8, 4, 128),
-                                                 ("f32", 2, 2, 64, 8, 3, 3, 128),
-                                                 ("bf16", 2, 2, 128, 16, 4, 6, 1024)])
-def test_decode_step_equals_separate_calls(B, dtype, S, g, d, p, m, L, k):
+@pytest.mark.parametrize("dtype,S,g,d,p,m,L,k,n", [
+    ("bf16", 8, 4, 128, 16, 8, 4, 128, 3000),
+    ("f32", 2, 2, 64, 8, 3, 3, 128, 3000),
+    ("bf16", 2, 2, 128, 16, 4, 6, 1024, 3000),
+    # the 131k batch-4 workload's index shape (m 10, L 4: 40 directions, three
+    # 16-code rounds in the scan; L*k0 = 4,096, the largest union the fused
+    # finaliser holds, 64 pages)
+    ("bf16", 2, 4, 128, 16, 10, 4, 1024, 14000),
+    # the 262k workload's index shape (m 12, L 6: 72 directions, five rounds;
+    # L*k0 = 12,288: the large-union finaliser, then the attention in eight
+    # 256-token splits and their merge)
+    ("bf16", 2, 4, 128, 32, 12, 6, 2048, 17000),
+])
+def test_decode_step_equals_separate_calls(B, dtype, S, g, d, p, m, L, k, n):
     """ice_decode_step gives bit-identical pages, top-k and attention to
     ice_insert + ice_query_pages + ice_sparse_attn, step after step, and its
-    last step matches the oracle (the last case takes the large-union path:
-    L * k0 = 6,144)."""
-    n, steps = 3000, 6
+    last step matches the oracle (every index array, candidates, pages,
+    top-k, attention)."""
+    steps = 6
     dev = torch.device("cuda")
     K, V, q0, _ = _inputs(S, n + steps, d, g, 24, 31, dtype)
     U = W.directions(m * L, d, 31, dtype).to(dev)
-    print(f"[case] decode_step {dtype} S={S} g={g} d={d} p={p} m={m} L={L}", flush=True)
+    print(f"[case] decode_step {dtype} S={S} g={g} d={d} p={p} m={m} L={L} k={k} n={n}",
+          flush=True)
     mk = lambda: B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U,
                          page_size=p, budget_k=k, m=m, L=L, gqa_group=g, capacity=n + steps)
     a, b = mk(), mk()
@@ -448,6 +490,8 @@ def test_long_generation_equals_rebuild(B):
         ob = b.sparse_attn(qs, pb, nb)
         torch.cuda.synchronize()
         assert torch.equal(a.view("codes")[s, :n], b.view("codes")[0, :n])
+        _check_list_storage(a, s, a.view("codes")[s].cpu().numpy())
+        _check_list_storage(b, 0, b.view("codes")[0].cpu().numpy())
         la, lb = _logical_lists(a, s), _logical_lists(b, 0)
         assert np.array_equal(la[0], lb[0]) and np.array_equal(la[1], lb[1])
         assert torch.equal(a.view("loc")[s, :n], b.view("loc")[0, :n])
@@ -682,3 +726,64 @@ def test_visit_budget_decode_step(B):
             q_s = _np(qt[s * g:(s + 1) * g])
             r = sts[s].query(q_s, literal=True)
             _check_query(a, sts[s], s, r, pa, na, ta, oa[s * g:(s + 1) * g], q_s)
+
+
+# ---------------------------------------------------------------- parameter ranges
+
+@pytest.mark.parametrize("m,L,k", [(10, 4, 256), (12, 6, 256), (4, 32, 128)])
+def test_inserts_many_directions(B, m, L, k):
+    """Standalone inserts with more than 32 directions (the insert stages the
+    directions 32 at a time: 40, 72 and 128 directions take two, three and
+    four chunks), then the query; every array against the oracle."""
+    run_case(B, S=2, n=2500, inserts=37, g=2, p=16, k=k, m=m, L=L, seed=50 + m)
+
+
+@pytest.mark.parametrize("m,L", [(2, 8), (3, 8), (2, 20), (1, 32), (4, 32)])
+def test_many_composites(B, m, L):
+    """More than six composites: the scan's histogram goes straight to global
+    memory, the collect reads M of composites 8 and up from memory, and above
+    16 composites a finaliser wave serves several (L = 32, m = 4: the largest
+    index, 128 directions)."""
+    run_case(B, S=2, n=4100, g=2, p=16, k=128, m=m, L=L, seed=60 + L, inserts=5)
+
+
+@pytest.mark.parametrize("g,d,dtype", [(8, 128, "bf16"), (16, 128, "bf16"), (16, 64, "f32"),
+                                       (5, 128, "bf16")])
+def test_wide_gqa_groups(B, g, d, dtype):
+    """GQA groups above 4: the scan folds the heads four at a time, and the
+    attention's matrix-core tiles carry up to 16 heads."""
+    run_case(B, S=2, n=3300, g=g, d=d, p=16, k=256, m=4, L=3, dtype=dtype, seed=70 + g)
+
+
+@pytest.mark.parametrize("g,L", [(16, 4), (8, 20)])
+def test_decode_step_wide_groups_many_composites(B, g, L):
+    """ice_decode_step (in-scan insert, fused attention) with 16 query heads
+    and with 20 composites: identical to the separate calls, and the oracle."""
+    S, n, d, p, m, k, steps = 2, 5000, 128, 16, 2, 128, 3
+    dev = torch.device("cuda")
+    K, V, _, _ = _inputs(S, n + steps, d, g, 24, 90 + g, "bf16")
+    U = W.directions(m * L, d, 90 + g, "bf16").to(dev)
+    print(f"[case] decode_step g={g} L={L}", flush=True)
+    mk = lambda: B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U,
+                         page_size=p, budget_k=k, m=m, L=L, gqa_group=g, capacity=n + steps)
+    a, b = mk(), mk()
+    gen = torch.Generator().manual_seed(17)
+    for t in range(steps):
+        qt = torch.randn(S * g, d, generator=gen).to(torch.bfloat16).to(dev)
+        kn, vn = K[:, n + t].contiguous().to(dev), V[:, n + t].contiguous().to(dev)
+        pa, na, oa, ta = a.decode_step(kn, vn, qt, with_topk=True)
+        b.insert(kn, vn)
+        pb, nb, tb = b.query_pages(qt, with_topk=True)
+        ob = b.sparse_attn(qt, pb, nb)
+        torch.cuda.synchronize()
+        assert torch.equal(pa, pb) and torch.equal(na, nb) and torch.equal(ta, tb)
+        assert torch.equal(oa, ob)
+    prm = oracle.Params(d=d, p=p, k=k, m=m, L=L, g=g)
+    for s in range(S):
+        st = oracle.OracleStream(prm, _np(K[s, :n]), _np(V[s, :n]), _np(U), n_cap=n + steps)
+        for t in range(steps):
+            st.insert(_np(K[s, n + t]), _np(V[s, n + t]))
+        q_s = _np(qt[s * g:(s + 1) * g])
+        r = st.query(q_s)
+        _check_index(a, st, s, n + steps)
+        _check_query(a, st, s, r, pa, na, ta, oa[s * g:(s + 1) * g], q_s)
