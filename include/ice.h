@@ -51,7 +51,9 @@ typedef enum {
   ICE_ERR_CAPACITY = -2,    /* an insert past capacity_tokens */
   ICE_ERR_UNSUPPORTED = -3, /* a valid setting this build does not implement */
   ICE_ERR_WORKSPACE = -4,   /* workspace or scratch too small or misaligned */
-  ICE_ERR_HIP = -5          /* a HIP launch error */
+  ICE_ERR_HIP = -5,         /* a HIP launch error */
+  ICE_ERR_SCRATCH_LIMIT = -6 /* ice_build_index_noalloc: the build needs more
+                                scratch than the library's fixed array */
 } ice_status;
 
 typedef enum { ICE_F32 = 0, ICE_BF16 = 1 } ice_dtype;
@@ -110,6 +112,25 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
                            const void *dirs, void *workspace, size_t workspace_bytes,
                            void *scratch, size_t scratch_bytes, void *stream,
                            ice_index **out);
+
+/* ice_build_index for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same build with the same results, except that the build scratch is a
+ * fixed array inside the library (ICE_NOALLOC_SCRATCH_BYTES of device memory
+ * on each GPU the library runs on, held until the process ends) instead of a
+ * caller buffer; the caller still passes the inputs and the workspace.  It
+ * calls no allocator.  ICE_ERR_SCRATCH_LIMIT (nothing enqueued) when
+ * ice_build_scratch_bytes for these arguments exceeds
+ * ICE_NOALLOC_SCRATCH_BYTES (an 8-head layer of 36,864 tokens with 32
+ * directions needs about 122 MiB).  Every call on one GPU uses the same
+ * array, which keeps the last build's contents (the build clears what it
+ * needs itself): builds that may overlap in time on one GPU (several streams
+ * or host threads) race, and the caller must serialise them. */
+#define ICE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+ice_status ice_build_index_noalloc(const ice_params *prm, int32_t n_streams, int64_t n_tokens,
+                                   int64_t capacity_tokens, const void *K, const void *V,
+                                   const void *dirs, void *workspace, size_t workspace_bytes,
+                                   void *stream, ice_index **out);
 
 /* Dynamic update (IceCache blog page: the tree takes new tokens with no
  * rebuild).  Appends one token to every stream.

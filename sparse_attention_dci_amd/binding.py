@@ -14,7 +14,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libice.so")
 
 ICE_OK, ICE_ERR_INVALID_ARG, ICE_ERR_CAPACITY, ICE_ERR_UNSUPPORTED, ICE_ERR_WORKSPACE, \
-    ICE_ERR_HIP = 0, -1, -2, -3, -4, -5
+    ICE_ERR_HIP, ICE_ERR_SCRATCH_LIMIT = 0, -1, -2, -3, -4, -5, -6
+NOALLOC_SCRATCH_BYTES = 128 << 20  # ICE_NOALLOC_SCRATCH_BYTES
 ICE_F32, ICE_BF16 = 0, 1
 TIMED_KERNELS = 7
 
@@ -68,6 +69,9 @@ def lib():
         L.ice_build_index.argtypes = [PP, i32, i64, i64, P, P, P, P, ctypes.c_size_t, P,
                                       ctypes.c_size_t, P, ctypes.POINTER(P)]
         L.ice_build_index.restype = ctypes.c_int
+        L.ice_build_index_noalloc.argtypes = [PP, i32, i64, i64, P, P, P, P, ctypes.c_size_t,
+                                              P, ctypes.POINTER(P)]
+        L.ice_build_index_noalloc.restype = ctypes.c_int
         L.ice_insert.argtypes = [P, P, P, P]
         L.ice_insert.restype = ctypes.c_int
         L.ice_query_pages.argtypes = [P, P, P, P, P, P]
@@ -134,7 +138,7 @@ class Index:
     """
 
     def __init__(self, K, V, dirs, *, page_size, budget_k, m, L, gqa_group=1, k0=0, k1=0,
-                 tree_depth=0, c=0.0, capacity=None, stream=None):
+                 tree_depth=0, c=0.0, capacity=None, stream=None, noalloc=False):
         _dev_tensor(K, "K", ndim=3)
         _dev_tensor(V, "V", K.dtype, 3)
         _dev_tensor(dirs, "dirs", K.dtype, 2)
@@ -153,13 +157,20 @@ class Index:
             # let the build report which argument is wrong
             ws = 256
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=K.device)
-        sb = L_.ice_build_scratch_bytes(ctypes.byref(self.prm), S, n) or 256
-        scratch = torch.empty(sb, dtype=torch.uint8, device=K.device)
         h = ctypes.c_void_p()
         st = _stream(stream)
-        _check(L_.ice_build_index(ctypes.byref(self.prm), S, n, self.capacity, _ptr(K), _ptr(V),
-                                  _ptr(dirs), _ptr(self.workspace), ws, _ptr(scratch), sb, st,
-                                  ctypes.byref(h)), "ice_build_index")
+        if noalloc:  # the library's fixed build scratch (ice_build_index_noalloc)
+            scratch = None
+            _check(L_.ice_build_index_noalloc(ctypes.byref(self.prm), S, n, self.capacity,
+                                              _ptr(K), _ptr(V), _ptr(dirs), _ptr(self.workspace),
+                                              ws, st, ctypes.byref(h)),
+                   "ice_build_index_noalloc")
+        else:
+            sb = L_.ice_build_scratch_bytes(ctypes.byref(self.prm), S, n) or 256
+            scratch = torch.empty(sb, dtype=torch.uint8, device=K.device)
+            _check(L_.ice_build_index(ctypes.byref(self.prm), S, n, self.capacity, _ptr(K),
+                                      _ptr(V), _ptr(dirs), _ptr(self.workspace), ws,
+                                      _ptr(scratch), sb, st, ctypes.byref(h)), "ice_build_index")
         self._h = h
         # keep the scratch (and the build inputs) alive until the build has run
         self._pending = (scratch, K, V, dirs)

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -13,6 +14,11 @@
 #include "ice_common.h"
 
 using ice::Dev;
+
+// Build scratch of ice_build_index_noalloc: one fixed array per GPU.  In host
+// code its name stands for a host-side shadow, never a device address: only
+// the address hipGetSymbolAddress returns for the current device is used.
+static __device__ __align__(256) unsigned char scratch[ICE_NOALLOC_SCRATCH_BYTES];
 
 namespace ice {
 
@@ -213,6 +219,24 @@ int64_t scratch_size(const ice_params *prm, int32_t S, int64_t n) {
 
 bool aligned(const void *ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
 
+// Device address of the fixed build scratch on the current device, resolved
+// once per device (nullptr when HIP cannot resolve it).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices];
+
+void *noalloc_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_dev[dev] = ptr;
+  }
+  return g_scratch_dev[dev];
+}
+
 }  // namespace
 
 struct ice_index {
@@ -243,7 +267,7 @@ size_t ice_build_scratch_bytes(const ice_params *prm, int32_t n_streams, int64_t
 ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_tokens,
                            int64_t capacity_tokens, const void *K, const void *V,
                            const void *dirs, void *workspace, size_t workspace_bytes,
-                           void *scratch, size_t scratch_bytes, void *stream,
+                           void *build_scratch, size_t scratch_bytes, void *stream,
                            ice_index **out) {
   if (!out) return ICE_ERR_INVALID_ARG;
   *out = nullptr;
@@ -256,7 +280,8 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
   if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < (size_t)y.total)
     return ICE_ERR_WORKSPACE;
   const int64_t need_scratch = scratch_size(prm, n_streams, n_tokens);
-  if (n_tokens > 0 && (!scratch || !aligned(scratch, kAlign) || scratch_bytes < (size_t)need_scratch))
+  if (n_tokens > 0 &&
+      (!build_scratch || !aligned(build_scratch, kAlign) || scratch_bytes < (size_t)need_scratch))
     return ICE_ERR_WORKSPACE;
 
   ice_index *idx = new (std::nothrow) ice_index;
@@ -347,7 +372,7 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
   ice::BuildScratch bs;
   std::memset(&bs, 0, sizeof(bs));
   if (n_tokens > 0) {
-    char *sc = (char *)scratch;
+    char *sc = (char *)build_scratch;
     int64_t off[10];
     scratch_offsets(prm, n_streams, n_tokens, off);
     bs.codes_dm = (int32_t *)(sc + off[0]);
@@ -368,6 +393,23 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
   }
   *out = idx;
   return ICE_OK;
+}
+
+ice_status ice_build_index_noalloc(const ice_params *prm, int32_t n_streams, int64_t n_tokens,
+                                   int64_t capacity_tokens, const void *K, const void *V,
+                                   const void *dirs, void *workspace, size_t workspace_bytes,
+                                   void *stream, ice_index **out) {
+  if (!out) return ICE_ERR_INVALID_ARG;
+  *out = nullptr;
+  Layout y;
+  ice_status st = make_layout(prm, n_streams, n_tokens, capacity_tokens, &y);
+  if (st != ICE_OK) return st;
+  if (scratch_size(prm, n_streams, n_tokens) > (int64_t)ICE_NOALLOC_SCRATCH_BYTES)
+    return ICE_ERR_SCRATCH_LIMIT;
+  void *dev_scratch = noalloc_scratch();
+  if (!dev_scratch) return ICE_ERR_HIP;
+  return ice_build_index(prm, n_streams, n_tokens, capacity_tokens, K, V, dirs, workspace,
+                         workspace_bytes, dev_scratch, ICE_NOALLOC_SCRATCH_BYTES, stream, out);
 }
 
 ice_status ice_insert(ice_index *idx, const void *k_new, const void *v_new, void *stream) {
@@ -470,6 +512,8 @@ const char *ice_status_string(ice_status s) {
     case ICE_ERR_UNSUPPORTED: return "unsupported setting";
     case ICE_ERR_WORKSPACE: return "workspace or scratch too small or misaligned";
     case ICE_ERR_HIP: return "HIP launch error";
+    case ICE_ERR_SCRATCH_LIMIT:
+      return "the build needs more scratch than the no-allocation build's fixed array";
   }
   return "unknown status";
 }

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in (0, -1, -2, -3, -4, -5):
+    for s in (0, -1, -2, -3, -4, -5, -6):
         assert L.ice_status_string(s)
     assert L.ice_status_string(-99) == b"unknown status"
 
@@ -161,3 +161,24 @@ def test_tree_depth_matches_oracle_reading(L, ora):
             other = good(page_size=pg, budget_k=4 * pg, m=m, L=Lc, tree_depth=D + 1)
             assert (L.ice_workspace_bytes(ctypes.byref(auto), 1, n, cap)
                     != L.ice_workspace_bytes(ctypes.byref(other), 1, n, cap))
+
+
+def test_noalloc_build_limits(L):
+    """The no-allocation build refuses, before any HIP call, a build whose
+    scratch exceeds its fixed array, and bad arguments as the plain build does."""
+    p = good()
+    h = ctypes.c_void_p()
+    # 8 heads x 40,000 tokens x 32 directions needs more than 128 MiB of scratch
+    assert L.ice_build_scratch_bytes(ctypes.byref(p), 8, 40000) > B.NOALLOC_SCRATCH_BYTES
+    st = L.ice_build_index_noalloc(ctypes.byref(p), 8, 40000, 40000, FAKE, FAKE, FAKE, FAKE,
+                                  1 << 40, None, ctypes.byref(h))
+    assert st == B.ICE_ERR_SCRATCH_LIMIT and not h.value
+    # the 36,864-token Llama-3.1-8B layer fits
+    assert L.ice_build_scratch_bytes(ctypes.byref(p), 8, 36864) <= B.NOALLOC_SCRATCH_BYTES
+    bad = good(page_size=12)
+    st = L.ice_build_index_noalloc(ctypes.byref(bad), 8, 1000, 1000, FAKE, FAKE, FAKE, FAKE,
+                                  1 << 40, None, ctypes.byref(h))
+    assert st == B.ICE_ERR_INVALID_ARG and not h.value
+    st = L.ice_build_index_noalloc(ctypes.byref(p), 8, 1000, 1000, FAKE, FAKE, FAKE, FAKE,
+                                  1 << 40, None, None)
+    assert st == B.ICE_ERR_INVALID_ARG
