@@ -50,20 +50,23 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w, kernel: str, ntok: float, n_cand: float, attended: float,
+def algorithmic_bytes(w, kernel: str, visits: float, n_cand: float, attended: float,
                       fused: bool = True) -> float:
     """Bytes the decode path has to move per launch of `kernel` for one layer
     (S streams): the per-unit figures times the units one launch processes.
+    `visits` is the mean sum over composites of the list entries a stream's
+    P-DCI walk visits (sum_l V_l), `n_cand` the mean union size |C|,
+    `attended` the mean tokens attended per stream, all measured (the query
+    statistics of a decode step on the timed layers).
 
-    qscan     every token's m*L projection codes (4*mL per token); the query
-              prep: the g heads (g*d*elem), the query codes and q_kv out
-              (4*mL + 4*d), the fp32 directions once per layer
+    qscan     the walk: 4 bytes per visited list entry (4 * sum_l V_l); the
+              query prep: the g heads in (g*d*elem), the query codes and q_kv
+              out (4*mL + 4*d), the fp32 directions once per layer
               ((d+1)*mL*4); the insert of the step's token: k and v in, their
               pool rows out (4*d*elem), mL codes and list entries out (12*mL)
-    qcollect  the key row of every reranked candidate: d*elem per candidate
-    qfinal    the rerank list (16 B per candidate), then (fused) the attention:
-              K and V rows of every attended token (2*d*elem each), the g
-              heads and their fp32 outputs
+    qcollect  the exact rerank: the key row of every candidate (d*elem * |C|)
+    qfinal    (fused) the attention: K and V rows of every attended token
+              (2*d*elem each), the g heads in and their fp32 outputs
     attn      (when the finaliser does not run the attention) as above
     insert    (the standalone ice_insert, not part of a decode step) the
               insert's bytes as above plus the directions
@@ -75,18 +78,25 @@ def algorithmic_bytes(w, kernel: str, ntok: float, n_cand: float, attended: floa
     insert = 4.0 * d * elem + 12.0 * mL
     per_stream = {
         "insert": insert,
-        "qscan": ntok * mL * 4.0 + g * d * elem + 4.0 * mL + 4.0 * d + insert,
+        "qscan": 4.0 * visits + g * d * elem + 4.0 * mL + 4.0 * d + insert,
         "qcollect": n_cand * d * elem,
-        "qfinal": n_cand * 16.0 + (att if fused else 0.0),
+        "qfinal": att if fused else 0.0,
         "attn": att,
     }
     per_layer = {"insert": dirs, "qscan": dirs}
     return S * per_stream.get(kernel, 0.0) + per_layer.get(kernel, 0.0)
 
 
+def scan_code_bytes(w, ntok: float) -> float:
+    """What the scan actually reads of the index: every token's m*L codes (it
+    computes the walk's closed form in one pass instead of visiting entries)."""
+    return w.streams * ntok * w.mL * 4.0
+
+
 def cpu_baseline(w, K, V, q, U, k_new, v_new, reps: int):
-    """The oracle, as it stands, on one layer's decode step for every stream.
-    Returns (best microseconds, threads, mean union size |C| per stream)."""
+    """The oracle, as it stands, on one layer's decode step for every stream,
+    one stream per thread.  Returns (best step microseconds, build seconds,
+    threads, mean union size |C|, mean sum_l V_l per stream)."""
     import concurrent.futures as cf
 
     import numpy as np
@@ -101,8 +111,10 @@ def cpu_baseline(w, K, V, q, U, k_new, v_new, reps: int):
     def build(s):
         return oracle.OracleStream(prm, Kn[s], Vn[s], Un, n_cap=w.n + reps)
 
+    t0 = time.perf_counter()
     with cf.ThreadPoolExecutor(threads) as ex:
         streams = list(ex.map(build, range(w.streams)))
+    build_s = time.perf_counter() - t0
 
     def step(s):
         st = streams[s]
@@ -112,14 +124,15 @@ def cpu_baseline(w, K, V, q, U, k_new, v_new, reps: int):
         st.attend(qs, r["page_ids"])
         return r
 
-    times, sizes = [], []
+    times, res = [], []
     with cf.ThreadPoolExecutor(threads) as ex:
         for _ in range(reps):
             t0 = time.perf_counter()
             res = list(ex.map(step, range(w.streams)))
             times.append(time.perf_counter() - t0)
-            sizes = [len(r["C"]) for r in res]
-    return min(times) * 1e6, threads, float(np.mean(sizes))
+    sizes = [len(r["C"]) for r in res]
+    visits = [float(sum(r["visits"])) for r in res]
+    return min(times) * 1e6, build_s, threads, float(np.mean(sizes)), float(np.mean(visits))
 
 
 def copy_calibration(args):
@@ -313,31 +326,51 @@ def main():
     avg_us = {k: 1e3 * ms / c for k, (ms, c) in per_kernel.items() if c}
     log(f"[bench] per-kernel average us: { {k: round(v, 2) for k, v in avg_us.items()} }")
 
-    cpu, n_cand = None, float(w.L * w.k)
+    # the work each stream's query did: the query statistics of one more decode
+    # step on every layer copy (after everything timed)
+    stats = binding.stats_tensor(w.streams, dev)
+    vis, cands, toks = [], [], []
+    for r in range(R):
+        k_new, v_new, q = steps_in[r]
+        pg, npg, out = outs[r]
+        layers[r].decode_step(k_new, v_new, q, page_ids=pg, n_pages=npg, out=out, stats=stats)
+        for rec in binding.parse_stats(stats, w.L):
+            vis.append(float(sum(rec["visits"])))
+            cands.append(float(rec["n_cand"]))
+            toks.append(float(rec["n_tokens"]))
+    visits, n_cand, attended = (sum(x) / len(x) for x in (vis, cands, toks))
+    ntok = w.n + args.pregen + per_layer // 2  # mean tokens per stream over the timed steps
+    log(f"[bench] per stream: sum_l V_l {visits:.0f} of {w.m * w.L * ntok:.0f} entries, "
+        f"|C| {n_cand:.1f}, attended {attended:.1f}")
+
+    cpu = None
     if not args.no_cpu and args.pregen:
         log("[bench] no oracle baseline after a long generation (the oracle holds the built layer)")
     if not args.no_cpu and not args.pregen:
         log("[bench] oracle cpu baseline")
         K, V, q, U = keep
         k_new, v_new, _ = W.step_inputs(w, layer=0, step=10 ** 6, device=dev)
-        us, threads, n_cand = cpu_baseline(w, K, V, q, U, k_new, v_new, args.cpu_reps)
-        cpu = {"value": round(us * layers_per_step, 1), "unit": "us", "cores": threads,
-               "kind": "oracle",
+        us, build_s, threads, o_cand, o_visits = cpu_baseline(w, K, V, q, U, k_new, v_new,
+                                                              args.cpu_reps)
+        cpu = {"value": round(us * layers_per_step, 1), "unit": "us",
+               "cores": os.cpu_count(), "threads": threads, "kind": "oracle",
+               "build_s": round(build_s, 2),
                "sample": f"one decode step (insert + literal P-DCI query + rerank + page "
                          f"selection + fp64 attention) of all {w.streams} KV heads of one "
-                         f"{w.n}-token layer, best of {args.cpu_reps}"
+                         f"{w.n}-token layer, one head per thread, best of {args.cpu_reps}"
                          + (f", times {layers_per_step} layers" if layers_per_step > 1 else "")
-                         + "; oracle build untimed"}
+                         + f"; build_s: the oracle's index build of that layer",
+               "oracle_visits": round(o_visits, 1), "oracle_union": round(o_cand, 1)}
 
-    ntok = w.n + args.pregen + per_layer // 2
-    attended = float(w.k)
     kernels = {}
     fused = "attn" not in avg_us
     for k, us in avg_us.items():
-        alg = algorithmic_bytes(w, k, ntok, n_cand, attended, fused)
+        alg = algorithmic_bytes(w, k, visits, n_cand, attended, fused)
         kernels[k] = {"avg_us": round(us, 3), "alg_bytes": int(alg),
                       "gbs": round(alg / (us * 1e-6) / 1e9, 1),
                       "frac": round(alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    if "qscan" in kernels:  # what the scan reads beyond the walk's entries
+        kernels["qscan"]["code_bytes"] = int(scan_code_bytes(w, ntok))
     dominant = max(avg_us, key=avg_us.get)
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
@@ -351,9 +384,10 @@ def main():
     roofline = {"bound": "hbm", "kernel": dominant, "achieved": dk["gbs"], "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": dk["frac"], "traffic": traffic, "avg_us": dk["avg_us"],
                 "alg_bytes": dk["alg_bytes"]}
-    step_alg = sum(algorithmic_bytes(w, k, ntok, n_cand, attended, fused)
+    step_alg = sum(algorithmic_bytes(w, k, visits, n_cand, attended, fused)
                    for k in ("qscan", "qcollect", "qfinal", "attn")
                    if fused is False or k != "attn") * layers_per_step
+    step_gbs = step_alg / (ms_per_step * 1e-3) / 1e9
 
     res = {
         "metric": "decode-step us (P-DCI query + sparse paged attn) @36k ctx; achieved HBM GB/s",
@@ -366,7 +400,8 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int32 codes + fp64 rerank + fp32 attention over bf16 KV",
+        "dtype": "i32 codes, f64 rerank; attention on bf16 MFMA (fp32 accumulate, fp32 "
+                 "probabilities as bf16 hi+lo pairs), fp32 softmax; bf16 KV",
         "data": "synthetic (seeded Gaussian-mixture keys, N(0,1) values)",
         "config": {"workload": args.workload, "kv_heads": w.streams,
                    "query_heads": w.streams * w.g, "context": w.n, "head_dim": w.d,
@@ -375,8 +410,11 @@ def main():
                    "generated_before_timing": args.pregen,
                    "step": "ice_decode_step = insert + query_pages + sparse_attn"},
         "build_ms": round(sorted(build_ms)[len(build_ms) // 2], 3),
-        "step_alg_gbs": round(step_alg / (ms_per_step * 1e-3) / 1e9, 1),
-        "union_size": round(n_cand, 1),
+        "step_alg_bytes": int(step_alg),
+        "step_alg_gbs": round(step_gbs, 1),
+        "step_frac": round(step_gbs / PEAK_HBM_GBS, 4),
+        "query_stats": {"visits": round(visits, 1), "union_size": round(n_cand, 1),
+                        "attended": round(attended, 1), "tokens": ntok},
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,

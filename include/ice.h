@@ -143,6 +143,24 @@ ice_status ice_build_index_noalloc(const ice_params *prm, int32_t n_streams, int
  * ICE_ERR_CAPACITY when the index already holds capacity_tokens tokens. */
 ice_status ice_insert(ice_index *idx, const void *k_new, const void *v_new, void *stream);
 
+/* Per-stream statistics of one query (the work the prioritized-DCI walk and
+ * the attention do), written when a query or decode step is given a non-NULL
+ * `stats` (device memory, one entry per stream; 8-byte aligned).
+ *   visits[l]  V_l, the list entries composite l's walk visits (l < L): the
+ *              visit rank of the entry that completes its k0-th candidate,
+ *              or every entry it may visit (m * n, or k1 when the visit budget
+ *              is smaller) when it completes fewer than k0 tokens
+ *   n_cand     |C|, the tokens in the union of the composites' candidates
+ *   n_pages    pages selected
+ *   n_tokens   tokens attended: the valid slots of the selected pages
+ * Entries l >= L are left untouched.  Collecting visits takes one extra pass
+ * over the projection codes; with stats == NULL nothing extra runs. */
+#define ICE_STATS_MAX_L 32
+typedef struct {
+  int64_t visits[ICE_STATS_MAX_L];
+  int32_t n_cand, n_pages, n_tokens, reserved;
+} ice_query_stats;
+
 /* Query: P-DCI candidates, exact rerank, page selection (IceCache paper page,
  * Figure 2 steps (2)-(3)).
  *   q         device [S*g][d] dtype: query heads, head j uses stream j / g;
@@ -152,6 +170,7 @@ ice_status ice_insert(ice_index *idx, const void *k_new, const void *v_new, void
  *   n_pages   device [S] int32 out.
  *   topk_ids  device [S][k] int32 out or NULL: the reranked top-k tokens,
  *             -1 after the last.
+ *   stats     device [S] out or NULL: see ice_query_stats.
  * Per stream: the g query heads are averaged in fp32 (q_kv) and normalised;
  * composite l's candidates are the k0 tokens with the smallest
  * max_j |code_j - qcode_j| over its m directions (ties by token), which is
@@ -165,7 +184,7 @@ ice_status ice_insert(ice_index *idx, const void *k_new, const void *v_new, void
  * one of its tokens appears, up to P = k/p pages.  Outputs are bit-exact and
  * deterministic. */
 ice_status ice_query_pages(ice_index *idx, const void *q, int32_t *page_ids, int32_t *n_pages,
-                           int32_t *topk_ids, void *stream);
+                           int32_t *topk_ids, ice_query_stats *stats, void *stream);
 
 /* Sparse attention over every token of the selected pages (IceCache paper
  * page, Figure 2 step (3)).
@@ -186,7 +205,7 @@ ice_status ice_sparse_attn(const ice_index *idx, const void *q, const int32_t *p
  * ICE_ERR_CAPACITY (nothing enqueued) when the index is full. */
 ice_status ice_decode_step(ice_index *idx, const void *k_new, const void *v_new, const void *q,
                            int32_t *page_ids, int32_t *n_pages, int32_t *topk_ids, float *out,
-                           void *stream);
+                           ice_query_stats *stats, void *stream);
 
 /* Frees the handle (not the workspace). NULL is allowed. */
 void ice_destroy_index(ice_index *idx);

@@ -74,11 +74,11 @@ def lib():
         L.ice_build_index_noalloc.restype = ctypes.c_int
         L.ice_insert.argtypes = [P, P, P, P]
         L.ice_insert.restype = ctypes.c_int
-        L.ice_query_pages.argtypes = [P, P, P, P, P, P]
+        L.ice_query_pages.argtypes = [P, P, P, P, P, P, P]
         L.ice_query_pages.restype = ctypes.c_int
         L.ice_sparse_attn.argtypes = [P, P, P, P, P, P]
         L.ice_sparse_attn.restype = ctypes.c_int
-        L.ice_decode_step.argtypes = [P, P, P, P, P, P, P, P, P]
+        L.ice_decode_step.argtypes = [P, P, P, P, P, P, P, P, P, P]
         L.ice_decode_step.restype = ctypes.c_int
         L.ice_destroy_index.argtypes = [P]
         L.ice_destroy_index.restype = None
@@ -101,6 +101,26 @@ def make_params(d, page_size, budget_k, m, L, gqa_group=1, k0=0, k1=0, tree_dept
                 dtype=torch.bfloat16) -> IceParams:
     dt = {torch.float32: ICE_F32, torch.bfloat16: ICE_BF16}[dtype]
     return IceParams(d, page_size, budget_k, m, L, gqa_group, k0, k1, tree_depth, c, dt)
+
+
+STATS_MAX_L = 32
+STATS_WORDS = STATS_MAX_L + 2  # int64 words of one ice_query_stats
+
+
+def stats_tensor(S: int, device) -> torch.Tensor:
+    """Device buffer for S ice_query_stats records ([S][34] int64)."""
+    return torch.zeros(S, STATS_WORDS, dtype=torch.int64, device=device)
+
+
+def parse_stats(t: torch.Tensor, L: int) -> list:
+    """ice_query_stats records ([S][34] int64) as dicts."""
+    a = t.cpu()
+    out = []
+    for s in range(a.shape[0]):
+        tail = a[s, STATS_MAX_L:].contiguous().view(torch.int32).tolist()
+        out.append({"visits": a[s, :L].tolist(), "n_cand": tail[0], "n_pages": tail[1],
+                    "n_tokens": tail[2]})
+    return out
 
 
 def _ptr(t):
@@ -197,7 +217,8 @@ class Index:
         _check(lib().ice_insert(self._h, _ptr(k_new), _ptr(v_new), _stream(stream)), "ice_insert")
 
     def query_pages(self, q, with_topk=False, page_ids=None, n_pages=None, topk=None,
-                    stream=None):
+                    stats=None, stream=None):
+        """stats: an optional stats_tensor(S) that receives the query statistics."""
         _dev_tensor(q, "q", self.dtype, 2)
         if q.shape != (self.S * self.g, self.d):
             raise ValueError("q must be [S*g][d]")
@@ -208,8 +229,13 @@ class Index:
                                                                   device=dev)
         if with_topk and topk is None:
             topk = torch.empty(self.S, self.k, dtype=torch.int32, device=dev)
+        if stats is not None:
+            _dev_tensor(stats, "stats", torch.int64, 2)
+            if stats.shape != (self.S, STATS_WORDS):
+                raise ValueError("stats must be stats_tensor(S)")
         _check(lib().ice_query_pages(self._h, _ptr(q), _ptr(page_ids), _ptr(n_pages),
-                                     _ptr(topk) if with_topk else None, _stream(stream)),
+                                     _ptr(topk) if with_topk else None, _ptr(stats),
+                                     _stream(stream)),
                "ice_query_pages")
         return page_ids, n_pages, (topk if with_topk else None)
 
@@ -224,7 +250,7 @@ class Index:
         return out
 
     def decode_step(self, k_new, v_new, q, page_ids=None, n_pages=None, out=None,
-                    with_topk=False, topk=None, stream=None):
+                    with_topk=False, topk=None, stats=None, stream=None):
         """insert(k_new, v_new); query_pages(q); sparse_attn(q, ...) in one call."""
         for t, nm in ((k_new, "k_new"), (v_new, "v_new"), (q, "q")):
             _dev_tensor(t, nm, self.dtype, 2)
@@ -241,9 +267,13 @@ class Index:
                                                       dtype=torch.float32, device=dev)
         if with_topk and topk is None:
             topk = torch.empty(self.S, self.k, dtype=torch.int32, device=dev)
+        if stats is not None:
+            _dev_tensor(stats, "stats", torch.int64, 2)
+            if stats.shape != (self.S, STATS_WORDS):
+                raise ValueError("stats must be stats_tensor(S)")
         _check(lib().ice_decode_step(self._h, _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(page_ids),
                                      _ptr(n_pages), _ptr(topk) if with_topk else None, _ptr(out),
-                                     _stream(stream)), "ice_decode_step")
+                                     _ptr(stats), _stream(stream)), "ice_decode_step")
         return page_ids, n_pages, out, (topk if with_topk else None)
 
     # ------------------------------------------------------------ timing

@@ -94,7 +94,7 @@ struct Layout {
   int64_t dirs, dirs32, norm_c, inv_c, inv_c2, maxnsq, codes, list_code, list_id, loc, page_tokens,
       page_len, page_cell, npages, cell_count, cell_last, pool_k, pool_v, qkv, qcode, mbuf,
       hist, hist2, cand, cand_count, bnd, bnd_rk, bnd_pg, bnd_count, rr_key, rr_id, rr_pg, rr_count,
-      attn_part, vhist, vstate, vtie, vcount, bsel;
+      attn_part, vhist, vstate, vtie, vcount, bsel, vlast;
   int64_t nvrange;
   int64_t total;
 };
@@ -190,6 +190,7 @@ ice_status make_layout(const ice_params *prm, int32_t S, int64_t n, int64_t ncap
   y.vtie = seg(Sl * Ll * y.nvrange * 4);
   y.vcount = seg(Sl * Ll * 4);
   y.bsel = seg(Sl * Ll * 2 * 4);
+  y.vlast = seg(Sl * Ll * 8);
   y.total = o;
   *L = y;
   return ICE_OK;
@@ -368,6 +369,7 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
   dv.vtie = (uint32_t *)(w + y.vtie);
   dv.vcount = (uint32_t *)(w + y.vcount);
   dv.bsel = (uint32_t *)(w + y.bsel);
+  dv.vlast = (unsigned long long *)(w + y.vlast);
 
   ice::BuildScratch bs;
   std::memset(&bs, 0, sizeof(bs));
@@ -424,12 +426,12 @@ ice_status ice_insert(ice_index *idx, const void *k_new, const void *v_new, void
 }
 
 ice_status ice_query_pages(ice_index *idx, const void *q, int32_t *page_ids, int32_t *n_pages,
-                           int32_t *topk_ids, void *stream) {
+                           int32_t *topk_ids, ice_query_stats *stats, void *stream) {
   if (!idx || !q || !page_ids || !n_pages || !aligned(q, 16) || !aligned(page_ids, 4) ||
-      !aligned(n_pages, 4) || (topk_ids && !aligned(topk_ids, 4)))
+      !aligned(n_pages, 4) || (topk_ids && !aligned(topk_ids, 4)) || (stats && !aligned(stats, 8)))
     return ICE_ERR_INVALID_ARG;
   hipError_t e = ice::launch_query(idx->dv, idx->n, idx->prm.k1, q, page_ids, n_pages, topk_ids,
-                                   (hipStream_t)stream, idx->timer);
+                                   stats, (hipStream_t)stream, idx->timer);
   return e == hipSuccess ? ICE_OK : ICE_ERR_HIP;
 }
 
@@ -445,14 +447,15 @@ ice_status ice_sparse_attn(const ice_index *idx, const void *q, const int32_t *p
 
 ice_status ice_decode_step(ice_index *idx, const void *k_new, const void *v_new, const void *q,
                            int32_t *page_ids, int32_t *n_pages, int32_t *topk_ids, float *out,
-                           void *stream) {
+                           ice_query_stats *stats, void *stream) {
   if (!idx || !k_new || !v_new || !q || !page_ids || !n_pages || !out || !aligned(k_new, 4) ||
       !aligned(v_new, 4) || !aligned(q, 16) || !aligned(page_ids, 4) || !aligned(n_pages, 4) ||
-      !aligned(out, 4) || (topk_ids && !aligned(topk_ids, 4)))
+      !aligned(out, 4) || (topk_ids && !aligned(topk_ids, 4)) || (stats && !aligned(stats, 8)))
     return ICE_ERR_INVALID_ARG;
   if (idx->n >= idx->ncap) return ICE_ERR_CAPACITY;
   hipError_t e = ice::launch_decode(idx->dv, idx->n, idx->prm.k1, k_new, v_new, q, page_ids,
-                                    n_pages, topk_ids, out, (hipStream_t)stream, idx->timer);
+                                    n_pages, topk_ids, out, stats, (hipStream_t)stream,
+                                    idx->timer);
   if (e != hipSuccess) return ICE_ERR_HIP;
   idx->n += 1;
   return ICE_OK;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ice.h"
+
 namespace ice {
 
 // Projection codes are fixed point with 29 fractional bits, saturated at
@@ -97,6 +99,8 @@ struct Dev {
   uint32_t *vcount;         // [S][L] n_l, the tokens the bounded walk completes
   uint32_t *bsel;           // [S][L][2] the collect pass's threshold bin b* of each composite and
                             // the count of tokens below it (for the finaliser)
+  unsigned long long *vlast;  // [S][L] query statistics: the (M, token) key of each composite's
+                              // k0-th candidate, ~0 when it completed fewer
 };
 
 // Build scratch (caller-owned, only used while the build runs).
@@ -140,7 +144,11 @@ hipError_t launch_insert(const Dev &dv, int64_t n, const void *k_new, const void
                          hipStream_t st, Timer *tm);
 // k1: the visit budget per composite, 0 = unbounded
 hipError_t launch_query(const Dev &dv, int64_t n, int64_t k1, const void *q, int32_t *page_ids,
-                        int32_t *n_pages, int32_t *topk_ids, hipStream_t st, Timer *tm);
+                        int32_t *n_pages, int32_t *topk_ids, ice_query_stats *stats,
+                        hipStream_t st, Timer *tm);
+// the visit counts and attended tokens of the query just enqueued (stats non-null)
+hipError_t launch_stats(const Dev &dv, int64_t n, ice_query_stats *stats, const int32_t *page_ids,
+                        const int32_t *n_pages, hipStream_t st);
 hipError_t launch_attn(const Dev &dv, const void *q, const int32_t *page_ids,
                        const int32_t *n_pages, float *out, hipStream_t st, Timer *tm);
 // n_l of every composite for a walk bounded at k1 visits (1 <= k1 < m * n)
@@ -148,6 +156,7 @@ hipError_t launch_visit_budget(const Dev &dv, int64_t n, uint32_t k1, hipStream_
 // insert of token n, then the query over n + 1 tokens and the attention
 hipError_t launch_decode(const Dev &dv, int64_t n, int64_t k1, const void *k_new,
                          const void *v_new, const void *q, int32_t *page_ids, int32_t *n_pages,
-                         int32_t *topk_ids, float *out, hipStream_t st, Timer *tm);
+                         int32_t *topk_ids, float *out, ice_query_stats *stats, hipStream_t st,
+                         Timer *tm);
 
 }  // namespace ice

@@ -646,6 +646,30 @@ __device__ __forceinline__ double rank_key_score(unsigned long long key) {
   return __longlong_as_double((long long)b);
 }
 
+// The finaliser's part of the query statistics: per composite, the visit
+// count's start (0 when the walk completed its k0-th candidate, whose key the
+// count pass then ranks among all entries; else every entry the walk may
+// visit, vlimit) and that key; the union size and the pages selected.
+__device__ __forceinline__ void final_stats(const Dev &dv, int s, int64_t n, uint32_t k0e,
+                                            const uint32_t *cc, const uint32_t *extra,
+                                            const unsigned long long *klast, uint32_t nu,
+                                            uint32_t nsel, ice_query_stats *stats,
+                                            unsigned long long vlimit) {
+  const int tid = threadIdx.x, L = dv.L;
+  if (tid < L) {
+    const uint32_t kl = k0e > 0 ? cc[tid] + extra[tid] : 0u;
+    const bool full = n > 0 && kl == (uint32_t)dv.k0;
+    stats[s].visits[tid] = full ? 0 : (n > 0 ? (long long)vlimit : 0);
+    dv.vlast[(int64_t)s * L + tid] = full ? klast[tid] : ~0ull;
+  }
+  if (tid == 0) {
+    stats[s].n_cand = (int32_t)nu;
+    stats[s].n_pages = (int32_t)nsel;
+    stats[s].n_tokens = 0;
+    stats[s].reserved = 0;
+  }
+}
+
 struct FinalShared {
   unsigned long long skey[kMaxCand];  // the rerank list: rank key, token, page
   int32_t sid[kMaxCand];
@@ -671,6 +695,7 @@ struct FinalShared {
   };
   uint32_t cnt[256];
   uint32_t cc[32], nb[32], need[32], boff[33], extra[32], b2[32], need2[32];
+  unsigned long long klast[32];  // largest (M, token) key picked per composite (statistics)
   uint32_t tie[kMaxTies];  // boundary entries in their composite's second-level bin b2
   uint32_t ntie;
   uint32_t nu;
@@ -691,7 +716,8 @@ template <int DT, int D, int PER>
 __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, bool bounded,
                                                           int32_t *page_ids, int32_t *n_pages,
                                                           int32_t *topk_ids, const void *q,
-                                                          float *out) {
+                                                          float *out, ice_query_stats *stats,
+                                                          unsigned long long vlimit) {
   __shared__ FinalShared sh;
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -734,6 +760,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
     sh.cc[tid] = cc_ld;
     sh.nb[tid] = nb_ld;
     sh.extra[tid] = 0;
+    sh.klast[tid] = 0;
   }
   {  // need, b2, need2 of composite l come from wave l alone (all zero when it takes no
      // candidates: k0e = 0, or a bounded walk that completes no token)
@@ -837,6 +864,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
   auto add_pick = [&](int l, unsigned long long key, unsigned long long rk, int32_t pg) {
     const int32_t id = (int32_t)(key & 0xffffffffull);
     dv.cand[((int64_t)s * L + l) * k0 + sh.cc[l] + atomicAdd(&sh.extra[l], 1u)] = id;
+    if (stats != nullptr) atomicMax(&sh.klast[l], key);
     if (mark(id)) {
       const uint32_t pos = atomicAdd(&sh.nu, 1u);
       sh.sid[pos] = id;
@@ -1049,8 +1077,12 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
       sh.nsel = nsel;
     }
   }
-  // F. the candidate counts, for inspection
+  // F. the candidate counts, for inspection, and the statistics
   if (tid < L && k0e > 0) dv.cand_count[s * L + tid] = sh.cc[tid] + sh.extra[tid];
+  if (stats != nullptr) {
+    lds_barrier();  // the page walk's count
+    final_stats(dv, s, n, k0e, sh.cc, sh.extra, sh.klast, nu, sh.nsel, stats, vlimit);
+  }
   if (out == nullptr) return;
 
   // G. the fused sparse attention over the selected pages: 16 waves, one
@@ -1115,6 +1147,7 @@ struct BigShared {
   uint32_t seen[2048];
   uint32_t cnt[256];
   uint32_t cc[32], nb[32], need[32], boff[33], extra[32], b2[32], need2[32];
+  unsigned long long klast[32];
   uint32_t tie[kMaxTies];
   uint32_t ntie, nux, rr, nsel, win_end;
   unsigned long long res;
@@ -1125,7 +1158,9 @@ struct BigShared {
 template <int DT>
 __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n, bool bounded,
                                                               int32_t *page_ids, int32_t *n_pages,
-                                                              int32_t *topk_ids) {
+                                                              int32_t *topk_ids,
+                                                              ice_query_stats *stats,
+                                                              unsigned long long vlimit) {
   __shared__ BigShared sh;
   constexpr int NT = kFinalThreads;
   const int s = blockIdx.x;
@@ -1165,6 +1200,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
     sh.cc[tid] = cc_ld;
     sh.nb[tid] = nb_ld;
     sh.extra[tid] = 0;
+    sh.klast[tid] = 0;
   }
   {  // need, b2, need2 of composite l come from wave l alone (all zero when it takes no
      // candidates: k0e = 0, or a bounded walk that completes no token)
@@ -1247,6 +1283,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
   auto add_pick = [&](int l, unsigned long long key, unsigned long long rk, int32_t pg) {
     const int32_t id = (int32_t)(key & 0xffffffffull);
     dv.cand[((int64_t)s * L + l) * k0 + sh.cc[l] + atomicAdd(&sh.extra[l], 1u)] = id;
+    if (stats != nullptr) atomicMax(&sh.klast[l], key);
     if (mark(id)) {
       const uint32_t pos = nrr + atomicAdd(&sh.nux, 1u);
       ukey[pos] = rk;
@@ -1549,6 +1586,8 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
     for (uint32_t x = want_top + tid; x < (uint32_t)dv.k; x += NT)
       topk_ids[(int64_t)s * dv.k + x] = -1;
   if (tid < L && k0e > 0) dv.cand_count[s * L + tid] = sh.cc[tid] + sh.extra[tid];
+  if (stats != nullptr)
+    final_stats(dv, s, n, k0e, sh.cc, sh.extra, sh.klast, nu, (uint32_t)nsel, stats, vlimit);
   uint4 *hist = reinterpret_cast<uint4 *>(dv.hist + (int64_t)s * L * kHistBins);
   uint4 *hist2 = reinterpret_cast<uint4 *>(dv.hist2 + (int64_t)s * L * kHistBins);
   for (int x = tid; x < L * kHistBins / 4; x += NT) {  // 16-byte stores
@@ -1608,21 +1647,24 @@ static void scan_collect(const Dev &dv, int64_t n, bool bounded, uint32_t k1, co
 template <int DT, int PER>
 static void launch_final(const Dev &dv, int64_t n, bool bounded, int32_t *page_ids,
                          int32_t *n_pages, int32_t *topk_ids, const void *q, float *out,
-                         hipStream_t st) {
+                         ice_query_stats *stats, unsigned long long vlimit, hipStream_t st) {
   static_assert(PER * kFinalThreads <= kMaxCand, "union arrays");
   if (dv.d == 128)
     hipLaunchKernelGGL((k_qfinal<DT, 128, PER>), dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n,
-                       bounded, page_ids, n_pages, topk_ids, q, out);
+                       bounded, page_ids, n_pages, topk_ids, q, out, stats, vlimit);
   else
     hipLaunchKernelGGL((k_qfinal<DT, 64, PER>), dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n,
-                       bounded, page_ids, n_pages, topk_ids, q, out);
+                       bounded, page_ids, n_pages, topk_ids, q, out, stats, vlimit);
 }
 
 template <int DT>
 static void query_tail(const Dev &dv, int64_t n, int64_t k1, int32_t *page_ids,
                        int32_t *n_pages, int32_t *topk_ids, const void *q, const void *k_new,
-                       const void *v_new, float *out, hipStream_t st, Timer *tm) {
+                       const void *v_new, float *out, ice_query_stats *stats, hipStream_t st,
+                       Timer *tm) {
   const bool bounded = n > 0 && k1 > 0 && k1 < (int64_t)dv.m * n;
+  // the entries a walk may visit: its budget, else all m * n
+  const unsigned long long vlimit = bounded ? (unsigned long long)k1 : (unsigned long long)dv.m * n;
   const int64_t cus = dv.ncu;
   auto fits = [&](int nt) { return dv.S * ((n + 2 * nt - 1) / (2 * nt)) <= cus; };
   if (fits(512) || !fits(1024))
@@ -1635,28 +1677,34 @@ static void query_tail(const Dev &dv, int64_t n, int64_t k1, int32_t *page_ids,
     scan_collect<DT, 1024>(dv, n, bounded, (uint32_t)k1, q, k_new, v_new, st, tm);
   if (dv.L * dv.k0 > kMaxCand)
     hipLaunchKernelGGL(k_qfinal_big<DT>, dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n, bounded,
-                       page_ids, n_pages, topk_ids);
+                       page_ids, n_pages, topk_ids, stats, vlimit);
   else if (dv.L * dv.k0 <= kFinalThreads)
-    launch_final<DT, 1>(dv, n, bounded, page_ids, n_pages, topk_ids, q, out, st);
+    launch_final<DT, 1>(dv, n, bounded, page_ids, n_pages, topk_ids, q, out, stats, vlimit, st);
   else
     launch_final<DT, kMaxCand / kFinalThreads>(dv, n, bounded, page_ids, n_pages, topk_ids, q,
-                                               out, st);
+                                               out, stats, vlimit, st);
   timer_mark(tm, KID_QFINAL, st);
 }
 
 hipError_t launch_query(const Dev &dv, int64_t n, int64_t k1, const void *q, int32_t *page_ids,
-                        int32_t *n_pages, int32_t *topk_ids, hipStream_t st, Timer *tm) {
+                        int32_t *n_pages, int32_t *topk_ids, ice_query_stats *stats,
+                        hipStream_t st, Timer *tm) {
   timer_begin(tm, st);
   if (dv.dtype == 0)
-    query_tail<0>(dv, n, k1, page_ids, n_pages, topk_ids, q, nullptr, nullptr, nullptr, st, tm);
+    query_tail<0>(dv, n, k1, page_ids, n_pages, topk_ids, q, nullptr, nullptr, nullptr, stats, st,
+                  tm);
   else
-    query_tail<1>(dv, n, k1, page_ids, n_pages, topk_ids, q, nullptr, nullptr, nullptr, st, tm);
-  return hipGetLastError();
+    query_tail<1>(dv, n, k1, page_ids, n_pages, topk_ids, q, nullptr, nullptr, nullptr, stats, st,
+                  tm);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || stats == nullptr) return e;
+  return launch_stats(dv, n, stats, page_ids, n_pages, st);
 }
 
 hipError_t launch_decode(const Dev &dv, int64_t n, int64_t k1, const void *k_new,
                          const void *v_new, const void *q, int32_t *page_ids, int32_t *n_pages,
-                         int32_t *topk_ids, float *out, hipStream_t st, Timer *tm) {
+                         int32_t *topk_ids, float *out, ice_query_stats *stats, hipStream_t st,
+                         Timer *tm) {
   // the new token is token n (inserted by the scan); the query sees n + 1
   // tokens.  Budgets of one attention split (kAttnTpb tokens) and unions that
   // fit LDS: the finaliser runs the attention itself, with the standalone
@@ -1667,12 +1715,13 @@ hipError_t launch_decode(const Dev &dv, int64_t n, int64_t k1, const void *k_new
   const bool fused = dv.attn_nsplit == 1 && dv.L * dv.k0 <= kMaxCand;
   float *fo = fused ? out : nullptr;
   if (dv.dtype == 0)
-    query_tail<0>(dv, n + 1, k1, page_ids, n_pages, topk_ids, q, k_new, v_new, fo, st, tm);
+    query_tail<0>(dv, n + 1, k1, page_ids, n_pages, topk_ids, q, k_new, v_new, fo, stats, st, tm);
   else
-    query_tail<1>(dv, n + 1, k1, page_ids, n_pages, topk_ids, q, k_new, v_new, fo, st, tm);
+    query_tail<1>(dv, n + 1, k1, page_ids, n_pages, topk_ids, q, k_new, v_new, fo, stats, st, tm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return fused ? hipSuccess : launch_attn(dv, q, page_ids, n_pages, out, st, tm);
+  if (!fused && (e = launch_attn(dv, q, page_ids, n_pages, out, st, tm)) != hipSuccess) return e;
+  return stats != nullptr ? launch_stats(dv, n + 1, stats, page_ids, n_pages, st) : hipSuccess;
 }
 
 }  // namespace ice

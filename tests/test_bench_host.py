@@ -79,12 +79,24 @@ def test_write_traffic_scales_by_the_copy(tmp_path, monkeypatch):
     assert "qcollect" not in per
 
 
-def test_algorithmic_bytes_of_the_scan():
-    """The scan moves every token's m*L codes, plus per stream the query
-    heads, the codes and q_kv out, the insert, and the directions once."""
+def test_algorithmic_bytes_follow_the_walk():
+    """The query's bytes are what the method moves: 4 bytes per list entry the
+    P-DCI walk visits (not every code the scan happens to read), one key row
+    per candidate for the exact rerank, and K and V rows of the attended
+    tokens; per stream, times the layer's streams."""
     w = W.WORKLOADS["llama8b_layer_36k"]
-    ntok = 36865
-    got = bench.algorithmic_bytes(w, "qscan", ntok, 1000.0, 256.0)
-    codes = 4 * w.mL * ntok * w.streams
-    assert got >= codes
-    assert got - codes < 0.01 * codes
+    S, d, mL, g, elem = w.streams, w.d, w.mL, w.g, 2
+    visits, cand, att = 819_000.0, 880.0, 256.0  # per stream
+    scan = bench.algorithmic_bytes(w, "qscan", visits, cand, att)
+    prep_insert = g * d * elem + 4 * mL + 4 * d + 4 * d * elem + 12 * mL
+    assert scan == S * (4 * visits + prep_insert) + (d + 1) * mL * 4
+    assert bench.algorithmic_bytes(w, "qcollect", visits, cand, att) == S * cand * d * elem
+    fin = bench.algorithmic_bytes(w, "qfinal", visits, cand, att)
+    assert fin == S * (att * 2 * d * elem + g * d * (elem + 4))
+    # the attention is counted once: in the finaliser when it is fused, else
+    # in the standalone kernel
+    assert bench.algorithmic_bytes(w, "qfinal", visits, cand, att, fused=False) == 0.0
+    assert bench.algorithmic_bytes(w, "attn", visits, cand, att, fused=False) == fin
+    # the walk's bytes scale with the visits; the scan's code read does not
+    assert bench.scan_code_bytes(w, 36865) == S * 36865 * mL * 4
+    assert bench.algorithmic_bytes(w, "qscan", 2 * visits, cand, att) - scan == S * 4 * visits

@@ -137,13 +137,25 @@ def test_build_argument_checks(L):
 
 def test_null_handles(L):
     assert L.ice_insert(None, FAKE, FAKE, None) == B.ICE_ERR_INVALID_ARG
-    assert L.ice_query_pages(None, FAKE, FAKE, FAKE, None, None) == B.ICE_ERR_INVALID_ARG
+    assert L.ice_query_pages(None, FAKE, FAKE, FAKE, None, None, None) == B.ICE_ERR_INVALID_ARG
     assert L.ice_sparse_attn(None, FAKE, FAKE, FAKE, FAKE, None) == B.ICE_ERR_INVALID_ARG
-    assert L.ice_decode_step(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+    assert L.ice_decode_step(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
                              None) == B.ICE_ERR_INVALID_ARG
     y = B.IceLayout()
     assert L.ice_index_layout(None, ctypes.byref(y)) == B.ICE_ERR_INVALID_ARG
     L.ice_destroy_index(None)
+
+
+def test_stats_record_layout():
+    """ice_query_stats: 32 int64 visit counts, then four int32 (272 bytes), as
+    the binding reads it."""
+    import torch
+    assert B.STATS_WORDS * 8 == 32 * 8 + 4 * 4
+    t = torch.zeros(2, B.STATS_WORDS, dtype=torch.int64)
+    t[1, :3] = torch.tensor([5, 6, 7])
+    t[1, 32:].view(torch.int32)[:3] = torch.tensor([11, 12, 13], dtype=torch.int32)
+    r = B.parse_stats(t, 3)
+    assert r[1] == {"visits": [5, 6, 7], "n_cand": 11, "n_pages": 12, "n_tokens": 13}
 
 
 def test_tree_depth_matches_oracle_reading(L, ora):

@@ -787,3 +787,81 @@ def test_decode_step_wide_groups_many_composites(B, g, L):
         r = st.query(q_s)
         _check_index(a, st, s, n + steps)
         _check_query(a, st, s, r, pa, na, ta, oa[s * g:(s + 1) * g], q_s)
+
+
+# ---------------------------------------------------------------- query statistics
+
+def _check_stats(rec, st, r):
+    """One stream's ice_query_stats against the oracle's walk: the visits of
+    every composite, the union size, pages and attended tokens."""
+    assert rec["visits"] == [int(v) for v in r["visits"]], (rec["visits"], r["visits"])
+    assert rec["n_cand"] == len(r["C"])
+    assert rec["n_pages"] == len(r["page_ids"])
+    assert rec["n_tokens"] == int(st.page_len[r["page_ids"]].sum()) if len(r["page_ids"]) else \
+        rec["n_tokens"] == 0
+
+
+@pytest.mark.parametrize("case", [
+    dict(S=2, n=4100, g=2, p=16, k=128, m=4, L=3, seed=101),
+    dict(S=2, n=3000, g=1, p=16, k=128, m=4, L=2, k1=2500, seed=102),          # budget ends walks
+    dict(S=2, n=3000, g=1, p=16, k=128, m=4, L=2, k1=9000, seed=103),          # mixed
+    dict(S=1, n=100, g=2, p=16, k=256, m=4, L=2, seed=104),                    # n < k0
+    dict(S=1, n=9000, g=2, p=16, k=1024, m=3, L=6, seed=105),                  # large union
+    dict(S=2, n=2500, g=2, p=16, k=128, m=2, L=20, inserts=7, seed=106),       # 20 composites
+    dict(S=1, n=0, g=1, p=16, k=32, m=2, L=2, inserts=3, seed=107),            # tiny
+])
+def test_query_stats(B, case):
+    """ice_query_pages with the statistics output: every composite's visit
+    count equals the oracle's literal walk, and |C|, pages and attended tokens
+    equal the oracle's."""
+    c = dict(d=128, k0=0, k1=0, inserts=0)
+    c.update(case)
+    dev = torch.device("cuda")
+    S, n, ins = c["S"], c["n"], c["inserts"]
+    K, V, q, _ = _inputs(S, n + ins, c["d"], c["g"], 24, c["seed"], "bf16")
+    U = W.directions(c["m"] * c["L"], c["d"], c["seed"], "bf16")
+    print(f"[case] stats {case}", flush=True)
+    idx = B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U.to(dev),
+                  page_size=c["p"], budget_k=c["k"], m=c["m"], L=c["L"], gqa_group=c["g"],
+                  k0=c["k0"], k1=c["k1"], capacity=max(n + ins, 1))
+    for t in range(ins):
+        idx.insert(K[:, n + t].contiguous().to(dev), V[:, n + t].contiguous().to(dev))
+    stats = B.stats_tensor(S, dev)
+    qd = q.to(dev)
+    pg, npg, tk = idx.query_pages(qd, with_topk=True, stats=stats)
+    pg2, npg2, tk2 = idx.query_pages(qd, with_topk=True)  # statistics change nothing
+    torch.cuda.synchronize()
+    assert torch.equal(pg, pg2) and torch.equal(npg, npg2) and torch.equal(tk, tk2)
+    recs = B.parse_stats(stats, c["L"])
+    prm = oracle.Params(d=c["d"], p=c["p"], k=c["k"], m=c["m"], L=c["L"], g=c["g"], k0=c["k0"],
+                        k1=c["k1"])
+    for s in range(S):
+        st = oracle.OracleStream(prm, _np(K[s, :n]), _np(V[s, :n]), _np(U), n_cap=max(n + ins, 1))
+        for t in range(ins):
+            st.insert(_np(K[s, n + t]), _np(V[s, n + t]))
+        r = st.query(_np(q[s * c["g"]:(s + 1) * c["g"]]), literal=True)
+        _check_stats(recs[s], st, r)
+
+
+def test_decode_step_stats_llama8b_layer_36k(B):
+    """ice_decode_step with statistics on the full 36,864-token layer (the
+    benchmark's workload): visits, union, pages and tokens of all eight heads
+    against the oracle's literal walk."""
+    w = W.WORKLOADS["llama8b_layer_36k"]
+    K, V, q, U, _ = W.layer_inputs(w, layer=2)
+    kn, vn, qn = W.step_inputs(w, layer=2, step=0)
+    dev = torch.device("cuda")
+    print("[case] decode stats llama8b_layer_36k", flush=True)
+    idx = B.Index(K.to(dev), V.to(dev), U.to(dev), page_size=w.p, budget_k=w.k, m=w.m, L=w.L,
+                  gqa_group=w.g, capacity=w.n + 4)
+    stats = B.stats_tensor(w.streams, dev)
+    pg, npg, out, _ = idx.decode_step(kn.to(dev), vn.to(dev), qn.to(dev), stats=stats)
+    torch.cuda.synchronize()
+    recs = B.parse_stats(stats, w.L)
+    prm = oracle.Params(d=w.d, p=w.p, k=w.k, m=w.m, L=w.L, g=w.g)
+    for s in range(w.streams):
+        st = oracle.OracleStream(prm, _np(K[s]), _np(V[s]), _np(U), n_cap=w.n + 4)
+        st.insert(_np(kn[s]), _np(vn[s]))
+        r = st.query(_np(qn[s * w.g:(s + 1) * w.g]))
+        _check_stats(recs[s], st, r)
+        np.testing.assert_array_equal(pg[s, :int(npg[s])].cpu().numpy(), r["page_ids"])
