@@ -71,6 +71,8 @@ def lib():
         L.ora_pdci_literal.restype = i64
         L.ora_pdci_closed.argtypes = [P, i64, i32, i32, i32, P, i64, i64, P, P]
         L.ora_pdci_closed.restype = i64
+        L.ora_dot_blocked.argtypes = [P, P, i32]
+        L.ora_dot_blocked.restype = ctypes.c_double
         L.ora_score.argtypes = [P, i32, P, i64]
         L.ora_score.restype = ctypes.c_double
         L.ora_rerank.argtypes = [P, i32, P, P, i64, P, P]
@@ -165,6 +167,13 @@ def pdci_closed(codes, m: int, l: int, qcode, k0: int, k1: int = 0):
     ns = lib().ora_pdci_closed(_p(codes), n, mL, m, l, _p(qcode), k0, k1, _p(S),
                                ctypes.byref(v))
     return S[:ns].copy(), int(v.value)
+
+
+def dot_blocked(a, b) -> float:
+    """The query side's fp64 dot product in its fixed blocked order."""
+    a, b = _f32(a), _f32(b)
+    assert a.shape == b.shape and a.ndim == 1
+    return float(lib().ora_dot_blocked(_p(a), _p(b), a.shape[0]))
 
 
 def score(K, qkv, tok: int) -> float:

@@ -267,9 +267,33 @@ int64_t ora_tree_append(int64_t tok, uint32_t cl, int p, int64_t npages, int32_t
 }
 
 /* ------------------------------------------------------------------ */
+/* Dot products of the query side (the query's projections and norm and */
+/* the rerank scores).  READING (the pages fix no evaluation order): a   */
+/* fixed blocked order in fp64.  The elements are cut into blocks of 16; */
+/* each block's products are added in ascending element order (every     */
+/* product of two floats is exact in fp64, so each addition rounds once);*/
+/* then the block sums are added pairwise, neighbours first:             */
+/* ((b0 + b1) + (b2 + b3)) + ((b4 + b5) + (b6 + b7)) for d = 128.        */
+/* d must be 16 times a power of two.                                    */
+/* ------------------------------------------------------------------ */
+double ora_dot_blocked(const float *a, const float *b, int d) {
+  double part[64];
+  int nb = d / 16;
+  for (int j = 0; j < nb; ++j) {
+    double acc = 0.0;
+    for (int e = 16 * j; e < 16 * j + 16; ++e) acc = acc + (double)a[e] * (double)b[e];
+    part[j] = acc;
+  }
+  for (int w = 1; w < nb; w *= 2) /* tree level: neighbours w apart */
+    for (int j = 0; j + w < nb; j += 2 * w) part[j] = part[j] + part[j + w];
+  return part[0];
+}
+
+/* ------------------------------------------------------------------ */
 /* Query preparation.  READING (GQA is only cited by title): the g      */
 /* query heads that share a KV head are averaged in fp32 (left fold,    */
-/* then times fp32(1/g)); T_Q normalises; q̄_t = <q, u_t[:d]> / |q|.    */
+/* then times fp32(1/g)); T_Q normalises; q̄_t = <q, u_t[:d]> / |q|,    */
+/* the dot products and |q|^2 in the blocked order above.               */
 /* q is [g][d]; outputs qkv[d] (fp32) and qcode[mL].                    */
 /* ------------------------------------------------------------------ */
 void ora_query_prep(const float *q, int g, int d, const float *U, int mL, float *qkv,
@@ -280,13 +304,11 @@ void ora_query_prep(const float *q, int g, int d, const float *U, int mL, float 
     for (int h = 1; h < g; ++h) acc = acc + q[h * d + e];
     qkv[e] = acc * inv_g;
   }
-  double qsq = 0.0;
-  for (int e = 0; e < d; ++e) qsq = qsq + (double)qkv[e] * (double)qkv[e];
+  double qsq = ora_dot_blocked(qkv, qkv, d);
   double qn = sqrt(qsq);
   for (int t = 0; t < mL; ++t) {
     const float *u = U + (int64_t)t * (d + 1);
-    double z = 0.0;
-    for (int e = 0; e < d; ++e) z = z + (double)qkv[e] * (double)u[e];
+    double z = ora_dot_blocked(qkv, u, d);
     double qb = qn > 0.0 ? z / qn : 0.0;
     qcode[t] = ora_to_code(qb);
   }
@@ -477,7 +499,7 @@ int64_t ora_pdci_closed(const int32_t *codes, int64_t n, int mL, int m, int l,
 /* ------------------------------------------------------------------ */
 /* Exact rerank (IceCache paper page, Figure 2 step (2): the top-k      */
 /* tokens most relevant to q).  READING: score_i = <qkv, k_i> in fp64,  */
-/* ascending element order (each product of an fp32 and a key element   */
+/* in the blocked order above (each product of an fp32 and a key element */
 /* is exact in fp64); rank by score descending, then token ascending.   */
 /* ------------------------------------------------------------------ */
 typedef struct {
@@ -492,9 +514,7 @@ static int ora_scored_cmp(const void *a, const void *b) {
 }
 
 double ora_score(const float *K, int d, const float *qkv, int64_t tok) {
-  double acc = 0.0;
-  for (int e = 0; e < d; ++e) acc = acc + (double)qkv[e] * (double)K[tok * d + e];
-  return acc;
+  return ora_dot_blocked(qkv, K + tok * d, d);
 }
 
 void ora_rerank(const float *K, int d, const float *qkv, const int32_t *C, int64_t nC,

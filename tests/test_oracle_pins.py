@@ -103,6 +103,93 @@ def test_projection_saturates(ora):
 
 # ------------------------------------------------------------------ query prep
 
+# ------------------------------------------------------------------ query-side dot products
+
+def _dot_case(d, entries):
+    a = np.ones(d, np.float32)
+    b = np.zeros(d, np.float32)
+    for e, v in entries:
+        b[e] = v
+    return a, b
+
+
+def test_dot_blocked_closed_forms(ora):
+    """The blocked order, worked by hand on sums where the order decides the
+    result (2^53 + 1 rounds to 2^53, ties to even): inside a block of 16 the
+    products are added in element order; the block sums are added pairwise,
+    neighbours first."""
+    B = 2.0 ** 53
+    cases = [
+        (128, [(0, B), (1, 1.0), (2, 1.0)], B),            # one block: each +1 is lost
+        (128, [(0, B), (32, 1.0), (48, 1.0)], B + 2),      # (b0 + b1) + (b2 + b3): the ones meet first
+        (128, [(16, 1.0), (32, 1.0), (48, B)], B),         # (0 + 1) + (1 + 2^53)
+        (128, [(64, B), (96, 1.0), (112, 1.0)], B + 2),    # the upper half, likewise
+        (128, [(0, 1.0), (64, 1.0), (127, B)], B),         # 1 + (1 + 2^53)
+        (64, [(0, B), (32, 1.0), (48, 1.0)], B + 2),
+        (64, [(0, 1.0), (16, 1.0), (32, B)], B + 2),       # (1 + 1) + 2^53
+        (16, [(0, B), (15, 1.0), (14, 1.0)], B),
+    ]
+    for d, ent, want in cases:
+        a, b = _dot_case(d, ent)
+        assert ora.dot_blocked(a, b) == want, (d, ent)
+        assert ora.dot_blocked(b, a) == want  # products commute
+
+
+def test_dot_blocked_error_bound(ora):
+    """Against the exact rational dot product: within the blocked order's
+    rounding bound (16 additions in a block plus log2(d/16) levels, each
+    relative 2^-53 of the absolute sum), and exact when every partial sum is
+    an integer that fits the mantissa."""
+    rng = np.random.default_rng(5)
+    for d in (16, 64, 128):
+        for _ in range(200):
+            a = (rng.standard_normal(d) * np.exp2(rng.integers(-20, 20, d))).astype(np.float32)
+            b = (rng.standard_normal(d) * np.exp2(rng.integers(-20, 20, d))).astype(np.float32)
+            got = ora.dot_blocked(a, b)
+            prods = [Fraction(float(x)) * Fraction(float(y)) for x, y in zip(a, b)]
+            exact = sum(prods)
+            bound = (16 + int(np.log2(d // 16)) + 1) * 2.0 ** -53 * float(sum(abs(x) for x in prods))
+            assert abs(Fraction(got) - exact) <= Fraction(bound)
+        ai = rng.integers(-1000, 1000, d).astype(np.float32)
+        bi = rng.integers(-1000, 1000, d).astype(np.float32)
+        assert ora.dot_blocked(ai, bi) == float(np.dot(ai.astype(np.int64), bi.astype(np.int64)))
+
+
+def test_query_prep_uses_blocked_order(ora):
+    """A query whose code sits on a rounding tie under the sequential order:
+    q = e0 + 2^-40 (e32 + e48) and u0 = 5*2^-30, u32 = u48 = 2^-41 give
+    |q| = 1 and z = 5*2^-30 + 2 * 2^-81.  Element order loses each 2^-81
+    (half an ulp of z, ties to even), giving z * 2^29 = 2.5 and code 2; the
+    blocked order adds the two small products first (2^-80, a whole ulp), so
+    z * 2^29 = 2.5 + 2^-51 and the code is 3."""
+    d = 128
+    q = np.zeros((1, d), np.float32)
+    q[0, 0], q[0, 32], q[0, 48] = 1.0, 2.0 ** -40, 2.0 ** -40
+    U = np.zeros((2, d + 1), np.float32)
+    U[0, 0], U[0, 32], U[0, 48] = 5 * 2.0 ** -30, 2.0 ** -41, 2.0 ** -41
+    U[1, 0] = 3 * 2.0 ** -30  # z * 2^29 = 1.5 exactly in any order: code 2 (ties to even)
+    _, qcode = ora.query_prep(q, U)
+    assert list(qcode) == [3, 2]
+
+
+def test_rerank_uses_blocked_order(ora):
+    """Scores that tie under the blocked order and not under element order:
+    token 0 = e0 + 2^-53 (e32 + e48) scores 1 + 2^-52 (the small products meet
+    first), token 1 = e0 + 2^-52 e1 scores 1 + 2^-52 in either order, token 2 =
+    e0 + 2^-53 (e16 + e32) scores 1 ((1 + 2^-53) rounds to 1 before the second
+    2^-53 joins).  Ranking by (score desc, token asc): 0, 1, 2."""
+    d = 128
+    K = np.zeros((3, d), np.float32)
+    K[:, 0] = 1.0
+    K[0, 32] = K[0, 48] = 2.0 ** -53
+    K[1, 1] = 2.0 ** -52
+    K[2, 16] = K[2, 32] = 2.0 ** -53
+    qkv = np.ones(d, np.float32)
+    ranked, scores = ora.rerank(K, qkv, np.array([2, 1, 0], np.int32))
+    assert list(ranked) == [0, 1, 2]
+    assert list(scores) == [1 + 2.0 ** -52, 1 + 2.0 ** -52, 1.0]
+
+
 def test_query_prep_is_normalised_mean_projection(ora):
     rng = np.random.default_rng(7)
     U = _rand_dirs(rng, 16, 128)
