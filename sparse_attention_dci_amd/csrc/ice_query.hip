@@ -42,62 +42,28 @@ constexpr int kMaxTies = 256;  // page budgets up to this take the fused attenti
 
 // ---------------------------------------------------------------- helpers
 
-// Exact fp64 scores of cnt tokens by a block of NT threads: per round of as
-// many tokens as ROWBYTES of LDS holds, their key rows are staged in LDS
-// (slot_of(j) gives token j's page slot), then one thread per row runs the
-// ordered chain.  emit(j, slot, score) receives each result.  lcs needs
-// ROWBYTES / 128 entries.  Rows are stored word-major with an odd stride
-// (word w of row r at w * (cap + 1) + r), so the chain's reads, one row per
-// lane, fall in distinct banks; the reads run a batch of 8 words ahead of the
-// dependent fma chain (two register sets, as in dot_chain).
-template <int DT, int B = 8>
-__device__ __forceinline__ double row_chain(const float *qkv, const uint32_t *rw, int stride,
-                                            int words) {
-  uint32_t r0[B], r1[B];
-  float q0[2 * B], q1[2 * B];
-  auto rd = [&](uint32_t (&r)[B], float (&qq)[2 * B], int w0) {
-#pragma unroll
-    for (int j = 0; j < B; ++j) r[j] = rw[(w0 + j) * stride];
-#pragma unroll
-    for (int j = 0; j < (DT == 0 ? B : 2 * B); ++j) qq[j] = qkv[(DT == 0 ? w0 : 2 * w0) + j];
-  };
-  auto sum = [](double acc, const uint32_t (&r)[B], const float (&qq)[2 * B]) {
-#pragma unroll
-    for (int j = 0; j < B; ++j) {
-      if constexpr (DT == 0) {
-        acc = fma((double)qq[j], (double)__uint_as_float(r[j]), acc);
-      } else {
-        acc = fma((double)qq[2 * j], (double)__uint_as_float(r[j] << 16), acc);
-        acc = fma((double)qq[2 * j + 1], (double)__uint_as_float(r[j] & 0xffff0000u), acc);
-      }
-    }
-    return acc;
-  };
-  rd(r0, q0, 0);
-  double acc = 0.0;
-#pragma unroll 1
-  for (int w0 = 0; w0 < words; w0 += 2 * B) {
-    rd(r1, q1, w0 + B);
-    acc = sum(acc, r0, q0);
-    rd(r0, q0, min(w0 + 2 * B, words - B));
-    acc = sum(acc, r1, q1);
-  }
-  return acc;
-}
-
-template <int DT, int NT, int ROWBYTES, int B, typename SlotOf, typename Emit>
+// Exact fp64 scores of cnt tokens by a block of NT threads, in the blocked
+// order (ice_step_dev.h): per round of as many rows as ROWBYTES of LDS holds,
+// the key rows are staged in LDS row-major with 16 bytes of padding
+// (slot_of(j) gives token j's page slot); then d/16 lanes score each row,
+// lane j summing elements 16j .. 16j+15 in order (two or four 16-byte LDS
+// reads), and the lanes' sums are added pairwise.  emit(j, slot, score)
+// receives each result.  lcs needs min(NT, ROWBYTES / (d*elem + 16)) entries;
+// rows and qkv are 16-byte aligned.
+template <int DT, int NT, int ROWBYTES, typename SlotOf, typename Emit>
 __device__ void block_score(const Dev &dv, int s, uint32_t cnt, SlotOf slot_of, const float *qkv,
                             int32_t *lcs, uint32_t *rows, Emit emit) {
   const int tid = threadIdx.x;
   const int d = dv.d;
   const int row_bytes = d * dv.elem;
-  const int row_words = row_bytes / 4;
-  const uint32_t fit = (ROWBYTES / (row_bytes + 4)) & ~1u;
-  const uint32_t cap = fit < (uint32_t)NT ? fit : NT;  // rows per round, even
-  const int stride = (int)cap + 1;                      // odd
-  const int cpr = row_bytes / 16;             // 16-byte chunks per row (8, 16 or 32)
+  const int rstride = row_bytes + 16;
+  const uint32_t fit = (uint32_t)(ROWBYTES / rstride);
+  const uint32_t cap = fit < (uint32_t)NT ? fit : (uint32_t)NT;  // rows per round
+  const int cpr = row_bytes / 16;  // 16-byte chunks per row (8, 16 or 32)
   const int lcpr = __builtin_ctz((unsigned)cpr);
+  const int nbk = d >> 4, lnb = d == 128 ? 3 : 2;
   constexpr int kIter = (ROWBYTES / 16 + NT - 1) / NT;
+  char *rb = reinterpret_cast<char *>(rows);
   for (uint32_t b0 = 0; b0 < cnt; b0 += cap) {
     const uint32_t nr = min(cap, cnt - b0);
     if ((uint32_t)tid < nr) lcs[tid] = slot_of(b0 + tid);
@@ -115,16 +81,50 @@ __device__ void block_score(const Dev &dv, int s, uint32_t cnt, SlotOf slot_of, 
     for (int k = 0; k < kIter; ++k) {
       const int x = tid + NT * k;
       const int r = x >> lcpr, c = x & (cpr - 1);
-      if ((uint32_t)r < nr) {
-        uint32_t *dst = rows + (4 * c) * stride + r;
-        dst[0] = v[k].x;
-        dst[stride] = v[k].y;
-        dst[2 * stride] = v[k].z;
-        dst[3 * stride] = v[k].w;
-      }
+      if ((uint32_t)r < nr) *reinterpret_cast<uint4 *>(rb + r * rstride + 16 * c) = v[k];
     }
     lds_barrier();
-    if ((uint32_t)tid < nr) emit(b0 + tid, lcs[tid], row_chain<DT, B>(qkv, rows + tid, stride, row_words));
+    for (uint32_t x = tid; x < nr * nbk; x += NT) {  // whole lane groups
+      const uint32_t r = x >> lnb;
+      const int j = x & (nbk - 1);
+      const char *rp = rb + r * rstride + j * 16 * dv.elem;
+      const float4 *qp = reinterpret_cast<const float4 *>(qkv + 16 * j);
+      float qv[16], kv[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 f = qp[i];
+        qv[4 * i] = f.x;
+        qv[4 * i + 1] = f.y;
+        qv[4 * i + 2] = f.z;
+        qv[4 * i + 3] = f.w;
+      }
+      if constexpr (DT == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 u = reinterpret_cast<const uint4 *>(rp)[i];
+          kv[4 * i] = __uint_as_float(u.x);
+          kv[4 * i + 1] = __uint_as_float(u.y);
+          kv[4 * i + 2] = __uint_as_float(u.z);
+          kv[4 * i + 3] = __uint_as_float(u.w);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint4 u = reinterpret_cast<const uint4 *>(rp)[i];
+          const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            kv[8 * i + 2 * k] = __uint_as_float(wd[k] << 16);
+            kv[8 * i + 2 * k + 1] = __uint_as_float(wd[k] & 0xffff0000u);
+          }
+        }
+      }
+      double z = 0.0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) z = fma((double)qv[i], (double)kv[i], z);
+      z = tree_sum(z, nbk);
+      if (j == 0) emit(b0 + r, lcs[r], z);
+    }
     lds_barrier();
   }
 }
@@ -179,14 +179,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_
   const int64_t r = blockIdx.x / S;
   const int64_t nold = k_new != nullptr ? n - 1 : n;  // tokens already in the index
   const bool ins = k_new != nullptr && r == nold / kScanTpb;  // this block inserts token nold
+  // directions: element e < d of direction t at dl[((e / 16) * W + t) * 16 + e % 16]
+  // (each lane of a query lane group reads its 16 elements as four 16-byte
+  // runs), u_t[d] at ud[t]
   union __attribute__((aligned(16))) ScanShared {
     uint32_t hist[LDS_HIST ? 6 * kHistBins : 1];
-    float dl[kStage * NT * 4];  // directions as [e][W] (row d holds u_t[d]), padded
+    float dl[128 * W];
   };
   __shared__ ScanShared sm;
+  __shared__ float ud[W];
   __shared__ int32_t qc[kMaxMl], nc[kMaxMl];
   __shared__ uint32_t blim[6];
-  __shared__ float qkv[128], kv[128];
+  __shared__ __attribute__((aligned(16))) float qkv[128], kv[128];
   __shared__ double zs[kMaxMl], rs[kMaxMl];
   __shared__ double qsq_s, ksq_s;
   __shared__ uint32_t cell_s;
@@ -213,8 +217,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_
   const double ic = dv.inv_c[s], ic2 = dv.inv_c2[s];
 #pragma unroll
   for (int k = 0; k < kStage; ++k) {
-    const int x = tid + NT * k;  // past tot4: padding
-    *reinterpret_cast<float4 *>(sm.dl + (x / W4) * W + (x % W4) * 4) = st4[k];
+    const int x = tid + NT * k;
+    const int e = x / W4, t0 = (x % W4) * 4;
+    const float c4[4] = {st4[k].x, st4[k].y, st4[k].z, st4[k].w};
+    if (e < d) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sm.dl[((((e >> 4) * W) + t0 + c) << 4) + (e & 15)] = c4[c];
+    } else if (e == d) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ud[t0 + c] = c4[c];
+    }
   }
   float acc = hv[0];  // left fold of the heads
 #pragma unroll
@@ -243,12 +255,33 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_
     b[x] = ld_code(rc, oa + tile_bytes + x * 256);
   }
 
-  // the chains: query on threads < mL and 128, insert on 256 + t and 384
-  if (tid < mL) zs[tid] = dot_chain(qkv, sm.dl + tid, W, d);
-  if (tid == 128) qsq_s = dot_chain(qkv, qkv, 1, d);
-  if (ins) {
-    if (tid >= 256 && tid < 256 + mL) rs[tid - 256] = dot_chain(kv, sm.dl + (tid - 256), W, d);
-    if (tid == 384) ksq_s = dot_chain(kv, kv, 1, d);
+  // the query's dot products in the blocked order: lane group t (d/16 lanes)
+  // is direction t, group mL the norm; the insert's element-order chains run
+  // on the top threads, it = NT-1-tid (r_t for it < mL, |k|^2 for it = mL)
+  {
+    const int nbk = d >> 4, lnb = d == 128 ? 3 : 2;
+    for (int x = tid; x < (mL + 1) * nbk; x += NT) {  // whole lane groups
+      const int t = x >> lnb, j = x & (nbk - 1);
+      const float *b = t < mL ? sm.dl + ((j * W + t) << 4) : qkv + 16 * j;
+      double z = fma16(qkv + 16 * j, b, 0.0);
+      z = tree_sum(z, nbk);
+      if (j == 0) {
+        if (t < mL)
+          zs[t] = z;
+        else
+          qsq_s = z;
+      }
+    }
+  }
+  const int it = NT - 1 - tid;
+  if (ins && it <= mL) {  // element order: one chain through the blocks
+    double z = 0.0;
+    for (int j = 0; j < (d >> 4); ++j)
+      z = fma16(kv + 16 * j, it < mL ? sm.dl + ((j * W + it) << 4) : kv + 16 * j, z);
+    if (it < mL)
+      rs[it] = z;
+    else
+      ksq_s = z;
   }
   lds_barrier();
   // the rest of the first kPipe codes of both tiles (the chains needed the
@@ -261,10 +294,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_
 
   if (tid < mL) qc[tid] = query_code(zs[tid], qsq_s);
   if (ins) {
-    if (tid >= 256 && tid < 256 + mL) {
-      const int t = tid - 256;
-      nc[t] = insert_code(rs[t], (double)sm.dl[d * W + t], ksq_s, ic, ic2);
-    }
+    if (it < mL) nc[it] = insert_code(rs[it], (double)ud[it], ksq_s, ic, ic2);
     if (w == 4) {  // the new token's cell: sign bits of r on the first D directions
       const unsigned long long bal = __ballot(lane < dv.D && rs[lane < mL ? lane : 0] >= 0.0);
       if (lane == 0) cell_s = (uint32_t)bal & ((1u << dv.D) - 1u);
@@ -403,7 +433,6 @@ constexpr int kSubShift = kHistShift - kHistBits;  // second-level bins: M >> 9 
 template <int NT>
 struct CollectShape {
   static constexpr int kRowBytes = NT == 512 ? 16 * 1024 : 32 * 1024;
-  static constexpr int kAhead = NT == 512 ? 4 : 8;
   static constexpr int kWavesPerEu = NT == 512 ? 6 : 4;
 };
 
@@ -419,13 +448,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
   __shared__ int32_t bstar[32];  // -1: the composite takes no candidates
   __shared__ uint32_t ccount[32], bcount[32], cbase[32], bbase[32];
   __shared__ uint32_t nc, nrl, rbase;
-  __shared__ float qkv[128];
+  __shared__ __attribute__((aligned(16))) float qkv[128];
   __shared__ int32_t cid[kScanTpb];      // candidate or boundary tokens, as offsets in the block
   __shared__ int32_t lloc[kScanTpb];     // page slots of the block's tokens
   __shared__ unsigned long long skb[kScanTpb];
   __shared__ int32_t spb[kScanTpb];
   __shared__ int32_t lcs[kCollectRowBytes / 128];
-  __shared__ uint32_t rows[kCollectRowBytes / 4];
+  __shared__ __attribute__((aligned(16))) uint32_t rows[kCollectRowBytes / 4];
   const uint32_t k0e = (uint32_t)min((int64_t)dv.k0, n);
   if (k0e == 0) return;
   const int64_t i0 = rng * kScanTpb;
@@ -529,7 +558,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
   unsigned long long *skbp = skb;
   int32_t *spbp = spb;
   const int32_t *cidp = cid, *llocp = lloc;
-  block_score<DT, kScanThreads, kCollectRowBytes, CollectShape<NT>::kAhead>(
+  block_score<DT, kScanThreads, kCollectRowBytes>(
       dv, s, nc, [cidp, llocp](uint32_t j) { return llocp[cidp[j]]; }, qkv, lcs, rows,
       [skbp, spbp, lp](uint32_t x, int32_t slotx, double sc) {
         skbp[x] = score_rank_key(sc);
@@ -1632,7 +1661,7 @@ static void scan_collect(const Dev &dv, int64_t n, bool bounded, uint32_t k1, co
     launch_scan_r<DT, false, NT>(dv, n, grid, q, k_new, v_new, st);
   timer_mark(tm, KID_QSCAN, st);
   if (bounded) {
-    launch_visit_budget(dv, n, k1, st);
+    (void)launch_visit_budget(dv, n, k1, st);  // a launch error stays for the caller's check
     timer_mark(tm, KID_VISIT, st);
   }
   if (n > 0) {

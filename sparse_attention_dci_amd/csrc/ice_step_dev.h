@@ -4,7 +4,8 @@
 // Query prep (IceCache paper page, Figure 2 step (2)): the query direction is
 // q_kv = fp32 mean of the g heads (left fold, then times fp32(1/g)), and
 // qcode_t = code(<q_kv, u_t[:d]> / |q_kv|), the dot product and the norm in
-// fp64 with the products taken in ascending element order.
+// fp64 in the blocked order below.  The new token's projections (key side)
+// take element order, as the build's do.
 //
 // Insert (IceCache blog page, technical details: new tokens enter the tree
 // with no rebuild): r_t = <k, u_t[:d]> in fp64, x_t = r_t / c +
@@ -48,6 +49,44 @@ __device__ __forceinline__ double dot_chain(const float *a, const float *b, int 
     rd(a0, b0, min(e0 + 2 * B, d - B));
     z = sum(z, a1, b1);
   }
+  return z;
+}
+
+// The query side's dot products (its projections and norm, and the rerank
+// scores) take a fixed blocked order: elements in blocks of 16, each block
+// summed in element order, then the block sums added pairwise, neighbours
+// first.  A group of d/16 consecutive lanes computes one: lane j sums block j
+// (the products are exact in fp64, so each fma rounds once, as an addition
+// would), then xor-1, xor-2 and xor-4 exchanges add the pairs level by level.
+// fp64 addition commutes, so every lane of the group ends with the same total.
+__device__ __forceinline__ double tree_sum(double z, int nbk) {
+  z += __shfl_xor(z, 1);
+  if (nbk > 2) z += __shfl_xor(z, 2);
+  if (nbk > 4) z += __shfl_xor(z, 4);
+  return z;
+}
+
+// z + a[0] b[0] + ... + a[15] b[15], added in element order; a and b are
+// 16-byte aligned runs of 16 floats (four vector reads each).  A query lane
+// computes its block with z = 0; element-order chains continue z block by
+// block.
+__device__ __forceinline__ double fma16(const float *a, const float *b, double z) {
+  float x[16], y[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 fa = reinterpret_cast<const float4 *>(a)[i];
+    const float4 fb = reinterpret_cast<const float4 *>(b)[i];
+    x[4 * i] = fa.x;
+    x[4 * i + 1] = fa.y;
+    x[4 * i + 2] = fa.z;
+    x[4 * i + 3] = fa.w;
+    y[4 * i] = fb.x;
+    y[4 * i + 1] = fb.y;
+    y[4 * i + 2] = fb.z;
+    y[4 * i + 3] = fb.w;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z = fma((double)x[i], (double)y[i], z);
   return z;
 }
 

@@ -865,3 +865,37 @@ def test_decode_step_stats_llama8b_layer_36k(B):
         r = st.query(_np(qn[s * w.g:(s + 1) * w.g]))
         _check_stats(recs[s], st, r)
         np.testing.assert_array_equal(pg[s, :int(npg[s])].cpu().numpy(), r["page_ids"])
+
+
+def test_blocked_dot_order_cases(B):
+    """The query side's dot products take the blocked order on the GPU too: a
+    query code that sits on a rounding tie under element order (the oracle
+    pin's query: code 3, not 2) and keys whose scores tie only under the
+    blocked order (ranked 0, 1, 2 by token), then every stage against the
+    oracle."""
+    d, n, m, L = 128, 300, 2, 2
+    gen = torch.Generator().manual_seed(3)
+    K = torch.randn(1, n, d, generator=gen) * 0.01
+    K[0, :3] = 0.0
+    K[0, :3, 0] = 1.0
+    K[0, 0, 32] = K[0, 0, 48] = 2.0 ** -53
+    K[0, 1, 1] = 2.0 ** -52
+    K[0, 2, 16] = K[0, 2, 32] = 2.0 ** -53
+    V = torch.randn(1, n, d, generator=gen)
+    q = torch.ones(1, d)
+    run_case(B, S=1, n=n, d=d, g=1, p=16, k=64, m=m, L=L, dtype="f32", k0=n, seed=5,
+             keys=(K, V, q))
+    # the query code case: q = e0 + 2^-40 (e32 + e48), direction 0 crafted
+    dev = torch.device("cuda")
+    U = W.directions(m * L, d, 6, "f32")
+    U[0] = 0.0
+    U[0, 0], U[0, 32], U[0, 48] = 5 * 2.0 ** -30, 2.0 ** -41, 2.0 ** -41
+    qq = torch.zeros(1, d)
+    qq[0, 0], qq[0, 32], qq[0, 48] = 1.0, 2.0 ** -40, 2.0 ** -40
+    idx = B.Index(K.to(dev), V.to(dev), U.to(dev), page_size=16, budget_k=64, m=m, L=L,
+                  capacity=n)
+    idx.query_pages(qq.to(dev))
+    torch.cuda.synchronize()
+    _, qcode = oracle.query_prep(qq.numpy(), U.numpy())
+    assert int(qcode[0]) == 3
+    np.testing.assert_array_equal(idx.view("qcode")[0].cpu().numpy(), qcode)
