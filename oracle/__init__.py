@@ -76,6 +76,7 @@ def lib():
         L.ora_score.argtypes = [P, i32, P, i64]
         L.ora_score.restype = ctypes.c_double
         L.ora_rerank.argtypes = [P, i32, P, P, i64, P, P]
+        L.ora_rerank_max.argtypes = [P, i32, P, i32, P, i64, P, P]
         L.ora_select_pages.argtypes = [P, i64, P, i64, P]
         L.ora_select_pages.restype = i64
         L.ora_attention.argtypes = [P, i32, i32, P, P, i32, P, i64, P, P]
@@ -190,6 +191,17 @@ def rerank(K, qkv, C):
     return ranked[:len(C)].copy(), scores[:len(C)].copy()
 
 
+def rerank_max(K, Q, C):
+    """GQA max reading: score_i = max over the heads of <q_h, k_i>."""
+    K, Q = _f32(K), _f32(Q)
+    C = np.ascontiguousarray(C, np.int32)
+    ranked = np.empty(max(len(C), 1), np.int32)
+    scores = np.empty(max(len(C), 1), np.float64)
+    lib().ora_rerank_max(_p(K), K.shape[1], _p(Q), Q.shape[0], _p(C), len(C), _p(ranked),
+                         _p(scores))
+    return ranked[:len(C)].copy(), scores[:len(C)].copy()
+
+
 def select_pages(ranked, page_of, P: int):
     ranked = np.ascontiguousarray(ranked, np.int32)
     page_of = np.ascontiguousarray(page_of, np.int32)
@@ -240,6 +252,7 @@ class Params:
     k1: int = 0           # visit budget per composite (0 -> unbounded)
     D: int = 0            # tree depth (0 -> derived at build)
     c: float = 0.0        # key-norm bound (0 -> derived at build)
+    gqa_max: bool = False  # GQA reading: False = the heads' mean, True = per-head walks, max score
 
     @property
     def mL(self):
@@ -336,11 +349,9 @@ class OracleStream:
         return pk, pv
 
     # ---------------------------------------------------------------- query
-    def query(self, q, literal: bool = True):
-        """q: [g][d].  Returns a dict with every intermediate of the query."""
-        prm = self.prm
-        n = self.n
-        qkv, qcode = query_prep(q, self.U)
+    def _walks(self, qcode, literal):
+        """P-DCI over every composite for one set of query codes."""
+        prm, n = self.prm, self.n
         S, visits = [], []
         for l in range(prm.L):
             if literal:
@@ -351,9 +362,34 @@ class OracleStream:
                 s, v = pdci_closed(self.codes[:n], prm.m, l, qcode, prm.k0_eff, prm.k1)
             S.append(s)
             visits.append(v)
+        return S, visits
+
+    def query(self, q, literal: bool = True):
+        """q: [g][d].  Returns a dict with every intermediate of the query.
+        With gqa_max, S / visits / qcode hold one entry per (head, composite),
+        head-major, and qkv is the heads themselves [g][d]."""
+        prm = self.prm
+        n = self.n
+        if prm.gqa_max:
+            q = _f32(q)
+            S, visits, qcs, qks = [], [], [], []
+            for h in range(q.shape[0]):
+                qk, qc = query_prep(q[h:h + 1], self.U)
+                s_h, v_h = self._walks(qc, literal)
+                S += s_h
+                visits += v_h
+                qcs.append(qc)
+                qks.append(qk)
+            qkv, qcode = np.stack(qks), np.concatenate(qcs)
+        else:
+            qkv, qcode = query_prep(q, self.U)
+            S, visits = self._walks(qcode, literal)
         C = np.unique(np.concatenate(S)) if S else np.empty(0, np.int32)
         C = C.astype(np.int32)
-        ranked, scores = rerank(self.K[:n], qkv, C)
+        if prm.gqa_max:
+            ranked, scores = rerank_max(self.K[:n], qkv, C)
+        else:
+            ranked, scores = rerank(self.K[:n], qkv, C)
         topk = ranked[:prm.k]
         page_ids = select_pages(ranked, self.page_of[:n], prm.P)
         return dict(qkv=qkv, qcode=qcode, S=S, visits=visits, C=C, ranked=ranked,

@@ -532,6 +532,33 @@ void ora_rerank(const float *K, int d, const float *qkv, const int32_t *C, int64
   free(a);
 }
 
+/* GQA "max" reading (BASELINE's 36k configuration lets the query heads */
+/* of a KV head be averaged or maxed; GQA itself is cited by title on    */
+/* the citation-map page).  READING: each of the g heads walks every     */
+/* composite with its own query; the pooled candidates are scored by the */
+/* largest of the heads' exact scores, score_i = max_h <q_h, k_i> (each  */
+/* in the blocked order above), and ranked by score descending, then     */
+/* token ascending.  Q is [g][d].                                         */
+void ora_rerank_max(const float *K, int d, const float *Q, int g, const int32_t *C, int64_t nC,
+                    int32_t *ranked, double *scores) {
+  ora_scored *a = (ora_scored *)malloc(sizeof(ora_scored) * (size_t)(nC > 0 ? nC : 1));
+  for (int64_t x = 0; x < nC; ++x) {
+    double best = ora_score(K, d, Q, C[x]);
+    for (int h = 1; h < g; ++h) {
+      double sc = ora_score(K, d, Q + (int64_t)h * d, C[x]);
+      if (sc > best) best = sc;
+    }
+    a[x].tok = C[x];
+    a[x].score = best;
+  }
+  qsort(a, (size_t)nC, sizeof(ora_scored), ora_scored_cmp);
+  for (int64_t x = 0; x < nC; ++x) {
+    ranked[x] = a[x].tok;
+    if (scores) scores[x] = a[x].score;
+  }
+  free(a);
+}
+
 /* ------------------------------------------------------------------ */
 /* Page selection (IceCache paper page, Figure 2 step (3): the pages    */
 /* that contain the relevant tokens are selected).  READING: walk the   */

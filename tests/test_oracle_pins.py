@@ -456,3 +456,60 @@ def test_needle_is_retrieved(ora):
     assert needle == top16
     sel = set(r["page_ids"].tolist())
     assert all(int(st.page_of[i]) in sel for i in needle)
+
+
+# ------------------------------------------------------------------ GQA max reading
+
+def test_gqa_max_unbounded_gives_exact_topk_of_max_score(ora):
+    """Per-head walks with an unbounded budget pool every token, so the ranked
+    candidates are the brute-force ranking by max_h <q_h, k> (exact rational
+    scores), and the pages follow it."""
+    K, V, q = _mixture(300, 16, 6, 71, g=3)
+    U = _rand_dirs(np.random.default_rng(12), 6, 16)
+    prm = ora.Params(d=16, p=8, k=40, m=3, L=2, g=3, k0=10 ** 6, gqa_max=True)
+    st = ora.OracleStream(prm, K, V, U)
+    r = st.query(q)
+    assert np.array_equal(r["C"], np.arange(300))
+    ex = [max(e) for e in zip(*(_exact_scores(K, q[h]) for h in range(3)))]
+    order = sorted(range(300), key=lambda i: (-ex[i], i))
+    assert list(r["ranked"]) == order
+    assert list(r["topk"]) == order[:40]
+    assert list(r["page_ids"]) == list(ora.select_pages(np.array(order, np.int32),
+                                                        st.page_of[:300], prm.P))
+    assert len(r["S"]) == 6 and len(r["visits"]) == 6  # one walk per (head, composite)
+
+
+def test_gqa_max_one_head_and_equal_heads_are_the_mean(ora):
+    """One head, or g identical heads (their fp32 mean is the head itself),
+    give exactly the mean reading's candidates, ranking and pages."""
+    K, V, q = _mixture(900, 128, 10, 72, g=1)
+    U = _rand_dirs(np.random.default_rng(13), 12, 128)
+    for g, qq in ((1, q), (4, np.repeat(q, 4, axis=0))):
+        mean = ora.OracleStream(ora.Params(d=128, p=16, k=64, m=4, L=3, g=g), K, V, U).query(qq)
+        mx = ora.OracleStream(ora.Params(d=128, p=16, k=64, m=4, L=3, g=g, gqa_max=True),
+                              K, V, U).query(qq)
+        assert np.array_equal(mean["C"], mx["C"])
+        assert np.array_equal(mean["ranked"], mx["ranked"])
+        assert np.array_equal(mean["page_ids"], mx["page_ids"])
+        for h in range(g):
+            for l in range(3):
+                assert np.array_equal(mx["S"][h * 3 + l], mean["S"][l])
+
+
+def test_gqa_max_walks_are_per_head(ora):
+    """Heads from different clusters: each head's walks equal a one-head query
+    with that head alone, and the pool is their union."""
+    K, V, _ = _mixture(1200, 128, 12, 73, g=1)
+    rng = np.random.default_rng(14)
+    q = (rng.standard_normal((3, 128)) * 3).astype(np.float32)
+    U = _rand_dirs(np.random.default_rng(15), 8, 128)
+    prm = ora.Params(d=128, p=16, k=64, m=4, L=2, g=3, gqa_max=True)
+    r = ora.OracleStream(prm, K, V, U).query(q)
+    union = set()
+    for h in range(3):
+        one = ora.OracleStream(ora.Params(d=128, p=16, k=64, m=4, L=2, g=1), K, V, U).query(
+            q[h:h + 1])
+        for l in range(2):
+            assert np.array_equal(r["S"][h * 2 + l], one["S"][l])
+            union |= set(one["S"][l].tolist())
+    assert sorted(union) == list(r["C"])
