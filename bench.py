@@ -225,6 +225,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--gqa", choices=("mean", "max"), default="mean",
+                    help="GQA query mode: the heads' mean, or per-head walks ranked by the max score")
     ap.add_argument("--pregen", type=int, default=0,
                     help="decode steps run on every layer copy before timing (a long generation)")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -265,7 +267,7 @@ def main():
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         idx = binding.Index(K, V, U, page_size=w.p, budget_k=w.k, m=w.m, L=w.L, gqa_group=w.g,
-                            capacity=cap)
+                            capacity=cap, gqa_mode=args.gqa)
         e1.record()
         torch.cuda.synchronize()
         build_ms.append(e0.elapsed_time(e1))
@@ -330,21 +332,24 @@ def main():
     # step on every layer copy (after everything timed)
     stats = binding.stats_tensor(w.streams, dev)
     vis, cands, toks = [], [], []
+    walks = w.L * (w.g if args.gqa == "max" else 1)
     for r in range(R):
         k_new, v_new, q = steps_in[r]
         pg, npg, out = outs[r]
         layers[r].decode_step(k_new, v_new, q, page_ids=pg, n_pages=npg, out=out, stats=stats)
-        for rec in binding.parse_stats(stats, w.L):
+        for rec in binding.parse_stats(stats, walks):
             vis.append(float(sum(rec["visits"])))
             cands.append(float(rec["n_cand"]))
             toks.append(float(rec["n_tokens"]))
     visits, n_cand, attended = (sum(x) / len(x) for x in (vis, cands, toks))
     ntok = w.n + args.pregen + per_layer // 2  # mean tokens per stream over the timed steps
-    log(f"[bench] per stream: sum_l V_l {visits:.0f} of {w.m * w.L * ntok:.0f} entries, "
+    log(f"[bench] per stream: sum_l V_l {visits:.0f} of {walks * w.m * ntok:.0f} entries, "
         f"|C| {n_cand:.1f}, attended {attended:.1f}")
 
     cpu = None
-    if not args.no_cpu and args.pregen:
+    if not args.no_cpu and args.gqa == "max":
+        log("[bench] no oracle baseline for the GQA max mode (the baseline times the mean mode)")
+    elif not args.no_cpu and args.pregen:
         log("[bench] no oracle baseline after a long generation (the oracle holds the built layer)")
     if not args.no_cpu and not args.pregen:
         log("[bench] oracle cpu baseline")
@@ -365,7 +370,10 @@ def main():
     kernels = {}
     fused = "attn" not in avg_us
     for k, us in avg_us.items():
-        alg = algorithmic_bytes(w, k, visits, n_cand, attended, fused)
+        # a layer step's bytes over its launches of the kernel (the GQA max mode
+        # runs the scan and the collect once per head)
+        per_step = per_kernel[k][1] / float(args.steps * layers_per_step)
+        alg = algorithmic_bytes(w, k, visits, n_cand, attended, fused) / max(per_step, 1.0)
         kernels[k] = {"avg_us": round(us, 3), "alg_bytes": int(alg),
                       "gbs": round(alg / (us * 1e-6) / 1e9, 1),
                       "frac": round(alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
@@ -386,7 +394,7 @@ def main():
                 "alg_bytes": dk["alg_bytes"]}
     step_alg = sum(algorithmic_bytes(w, k, visits, n_cand, attended, fused)
                    for k in ("qscan", "qcollect", "qfinal", "attn")
-                   if fused is False or k != "attn") * layers_per_step
+                   if k in avg_us) * layers_per_step
     step_gbs = step_alg / (ms_per_step * 1e-3) / 1e9
 
     res = {
@@ -407,7 +415,7 @@ def main():
                    "query_heads": w.streams * w.g, "context": w.n, "head_dim": w.d,
                    "page_size": w.p, "budget_k": w.k, "m": w.m, "L": w.L,
                    "layers_per_step": layers_per_step, "layers_rotated": R,
-                   "generated_before_timing": args.pregen,
+                   "generated_before_timing": args.pregen, "gqa": args.gqa,
                    "step": "ice_decode_step = insert + query_pages + sparse_attn"},
         "build_ms": round(sorted(build_ms)[len(build_ms) // 2], 3),
         "step_alg_bytes": int(step_alg),

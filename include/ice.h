@@ -79,7 +79,19 @@ typedef struct {
   float c;            /* key-norm bound of the transform; 0 -> the largest key
                          norm of each stream at build, rounded to fp32          */
   int32_t dtype;      /* ice_dtype of K, V, q and the directions                */
+  int32_t gqa_mode;   /* ice_gqa_mode: how the g query heads of a KV head query
+                         the index (0 = their mean; 1 = per-head walks, max score) */
 } ice_params;
+
+/* GQA query modes (the query heads sharing a KV head "averaged or maxed"):
+ *   ICE_GQA_MEAN  one walk per composite with the fp32 mean of the g heads;
+ *                 candidates reranked by <q_kv, k>.
+ *   ICE_GQA_MAX   every head walks every composite with its own query (g * L
+ *                 walks, g * L <= 32 and g * L * k0 <= 4096, else
+ *                 ICE_ERR_UNSUPPORTED); the pooled candidates are reranked by
+ *                 max over the heads of <q_h, k>.
+ * Both select P = k / p pages and attend every head over them. */
+typedef enum { ICE_GQA_MEAN = 0, ICE_GQA_MAX = 1 } ice_gqa_mode;
 
 typedef struct ice_index ice_index; /* opaque host handle */
 
@@ -230,12 +242,15 @@ const char *ice_status_string(ice_status s);
  *   pool_k        dtype   [S][Pcap][p][d]  key of each page slot
  *   pool_v        dtype   [S][Pcap][d][p]  values, element-major inside a
  *                 page (value element e of slot j at [e][j])
- *   qcode         int32   [S][mL]        last query's projection codes
- *   cand          int32   [S][L][k0]     last query's candidates per composite,
- *                 cand_count int32 [S][L] of them valid, in no fixed order */
+ *   qcode         int32   [S][G][mL]     last query's projection codes (G = g
+ *                 in the GQA max mode, one set per head; else 1)
+ *   cand          int32   [S][Lq][k0]    last query's candidates per walk (Lq =
+ *                 L, or g * L in the GQA max mode: walk h * L + l is head h on
+ *                 composite l), cand_count int32 [S][Lq] of them valid, in no
+ *                 fixed order */
 typedef struct {
   int64_t n_streams, n_tokens, n_build, capacity_tokens, page_capacity, n_cells;
-  int32_t tree_depth, mL, k0, elem_bytes;
+  int32_t tree_depth, mL, k0, elem_bytes, Lq, Gq;
   int64_t norm_c, codes, list_code, list_id, loc, page_tokens, page_len, page_cell, npages,
       cell_count, pool_k, pool_v, qcode, cand, cand_count;
   int64_t workspace_bytes;

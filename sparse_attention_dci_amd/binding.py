@@ -17,6 +17,7 @@ ICE_OK, ICE_ERR_INVALID_ARG, ICE_ERR_CAPACITY, ICE_ERR_UNSUPPORTED, ICE_ERR_WORK
     ICE_ERR_HIP, ICE_ERR_SCRATCH_LIMIT = 0, -1, -2, -3, -4, -5, -6
 NOALLOC_SCRATCH_BYTES = 128 << 20  # ICE_NOALLOC_SCRATCH_BYTES
 ICE_F32, ICE_BF16 = 0, 1
+ICE_GQA_MEAN, ICE_GQA_MAX = 0, 1
 TIMED_KERNELS = 7
 
 
@@ -25,12 +26,12 @@ class IceParams(ctypes.Structure):
                 ("budget_k", ctypes.c_int32), ("m", ctypes.c_int32), ("L", ctypes.c_int32),
                 ("gqa_group", ctypes.c_int32), ("k0", ctypes.c_int32), ("k1", ctypes.c_int64),
                 ("tree_depth", ctypes.c_int32), ("c", ctypes.c_float),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("gqa_mode", ctypes.c_int32)]
 
 
 _LAYOUT_I64_HEAD = ["n_streams", "n_tokens", "n_build", "capacity_tokens", "page_capacity",
                     "n_cells"]
-_LAYOUT_I32 = ["tree_depth", "mL", "k0", "elem_bytes"]
+_LAYOUT_I32 = ["tree_depth", "mL", "k0", "elem_bytes", "Lq", "Gq"]
 _LAYOUT_OFFS = ["norm_c", "codes", "list_code", "list_id", "loc", "page_tokens", "page_len",
                 "page_cell", "npages", "cell_count", "pool_k", "pool_v", "qcode", "cand",
                 "cand_count"]
@@ -98,9 +99,10 @@ def lib():
 
 
 def make_params(d, page_size, budget_k, m, L, gqa_group=1, k0=0, k1=0, tree_depth=0, c=0.0,
-                dtype=torch.bfloat16) -> IceParams:
+                dtype=torch.bfloat16, gqa_mode="mean") -> IceParams:
     dt = {torch.float32: ICE_F32, torch.bfloat16: ICE_BF16}[dtype]
-    return IceParams(d, page_size, budget_k, m, L, gqa_group, k0, k1, tree_depth, c, dt)
+    gm = {"mean": ICE_GQA_MEAN, "max": ICE_GQA_MAX}[gqa_mode]
+    return IceParams(d, page_size, budget_k, m, L, gqa_group, k0, k1, tree_depth, c, dt, gm)
 
 
 STATS_MAX_L = 32
@@ -158,7 +160,8 @@ class Index:
     """
 
     def __init__(self, K, V, dirs, *, page_size, budget_k, m, L, gqa_group=1, k0=0, k1=0,
-                 tree_depth=0, c=0.0, capacity=None, stream=None, noalloc=False):
+                 tree_depth=0, c=0.0, capacity=None, stream=None, noalloc=False,
+                 gqa_mode="mean"):
         _dev_tensor(K, "K", ndim=3)
         _dev_tensor(V, "V", K.dtype, 3)
         _dev_tensor(dirs, "dirs", K.dtype, 2)
@@ -170,7 +173,7 @@ class Index:
         self.device = K.device
         self.capacity = int(capacity if capacity is not None else n)
         self.prm = make_params(d, page_size, budget_k, m, L, gqa_group, k0, k1, tree_depth, c,
-                               K.dtype)
+                               K.dtype, gqa_mode)
         L_ = lib()
         ws = L_.ice_workspace_bytes(ctypes.byref(self.prm), S, n, self.capacity)
         if ws == 0:
@@ -299,7 +302,7 @@ class Index:
         y = self.layout()
         S, ncap, pcap = y["n_streams"], y["capacity_tokens"], y["page_capacity"]
         mL, p, d = y["mL"], self.prm.page_size, self.d
-        L = self.prm.L
+        Lq, Gq = y["Lq"], y["Gq"]
         shapes = {
             "norm_c": (torch.float32, (S,)),
             "codes": (torch.int32, (S, (ncap + 63) // 64, mL, 64)),
@@ -313,9 +316,9 @@ class Index:
             "cell_count": (torch.int32, (S, y["n_cells"])),
             "pool_k": (self.dtype, (S, pcap, p, d)),
             "pool_v": (self.dtype, (S, pcap, d, p)),
-            "qcode": (torch.int32, (S, mL)),
-            "cand": (torch.int32, (S, L, y["k0"])),
-            "cand_count": (torch.int32, (S, L)),
+            "qcode": (torch.int32, (S, Gq * mL)),
+            "cand": (torch.int32, (S, Lq, y["k0"])),
+            "cand_count": (torch.int32, (S, Lq)),
         }
         dt, shape = shapes[name]
         off = y[name]

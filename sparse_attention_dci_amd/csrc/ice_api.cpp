@@ -117,6 +117,7 @@ ice_status check_params(const ice_params *prm, int32_t S, int64_t n, int64_t nca
     return ICE_ERR_INVALID_ARG;
   if (!(prm->c >= 0.0f) || std::isinf(prm->c)) return ICE_ERR_INVALID_ARG;
   if (prm->dtype != ICE_F32 && prm->dtype != ICE_BF16) return ICE_ERR_INVALID_ARG;
+  if (prm->gqa_mode != ICE_GQA_MEAN && prm->gqa_mode != ICE_GQA_MAX) return ICE_ERR_INVALID_ARG;
   if (S < 1 || n < 0 || ncap < n || ncap < 1 || ncap > 0x7fffffffLL - 1)
     return ICE_ERR_INVALID_ARG;
   if (prm->L > 32) return ICE_ERR_UNSUPPORTED;
@@ -124,6 +125,9 @@ ice_status check_params(const ice_params *prm, int32_t S, int64_t n, int64_t nca
   if (k0 * prm->L > ice::kMaxCandBig) return ICE_ERR_UNSUPPORTED;
   if (prm->budget_k > ice::kMaxBudget) return ICE_ERR_UNSUPPORTED;
   if (n > (int64_t)ice::kPageChunk * 16384) return ICE_ERR_UNSUPPORTED;  // build's chunk counters
+  if (prm->gqa_mode == ICE_GQA_MAX &&
+      ((int64_t)prm->gqa_group * prm->L > 32 || (int64_t)prm->gqa_group * prm->L * k0 > ice::kMaxCand))
+    return ICE_ERR_UNSUPPORTED;  // the pooled walks' candidates stay in the finaliser's LDS
   return ICE_OK;
 }
 
@@ -143,7 +147,9 @@ ice_status make_layout(const ice_params *prm, int32_t S, int64_t n, int64_t ncap
   y.k0 = prm->k0 > 0 ? prm->k0 : prm->budget_k;
   y.elem = prm->dtype == ICE_F32 ? 4 : 2;
   y.attn_nsplit = (prm->budget_k + ice::kAttnTpb - 1) / ice::kAttnTpb;
-  const int64_t Sl = S, Ll = prm->L, g = prm->gqa_group;
+  const int64_t Sl = S, g = prm->gqa_group;
+  const int64_t Gq = prm->gqa_mode == ICE_GQA_MAX ? g : 1;
+  const int64_t Lb = prm->L, Ll = prm->L * Gq;  // a pass's walks; all walks of a query
   int64_t o = 0;
   auto seg = [&](int64_t bytes) {
     int64_t at = o;
@@ -168,9 +174,9 @@ ice_status make_layout(const ice_params *prm, int32_t S, int64_t n, int64_t ncap
   y.cell_last = seg(Sl * y.ncell * 4);
   y.pool_k = seg(Sl * y.pcap * p * d * y.elem);
   y.pool_v = seg(Sl * y.pcap * p * d * y.elem);
-  y.qkv = seg(Sl * d * 4);
-  y.qcode = seg(Sl * mL * 4);
-  y.mbuf = seg(Sl * Ll * ncap * 4);
+  y.qkv = seg(Sl * Gq * d * 4);
+  y.qcode = seg(Sl * Gq * mL * 4);
+  y.mbuf = seg(Sl * Lb * ncap * 4);
   y.hist = seg(Sl * Ll * ice::kHistBins * 4);
   y.hist2 = seg(Sl * Ll * ice::kHistBins * 4);
   y.cand = seg(Sl * Ll * y.k0 * 4);
@@ -305,6 +311,9 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
   dv.L = prm->L;
   dv.mL = prm->m * prm->L;
   dv.g = prm->gqa_group;
+  dv.gmax = prm->gqa_mode == ICE_GQA_MAX ? 1 : 0;
+  dv.Gq = dv.gmax ? dv.g : 1;
+  dv.Lq = dv.L * dv.Gq;
   dv.D = y.D;
   dv.k = prm->budget_k;
   dv.P = prm->budget_k / prm->page_size;
@@ -535,6 +544,8 @@ ice_status ice_index_layout(const ice_index *idx, ice_layout *out) {
   out->mL = idx->prm.m * idx->prm.L;
   out->k0 = y.k0;
   out->elem_bytes = y.elem;
+  out->Lq = idx->prm.L * (idx->prm.gqa_mode == ICE_GQA_MAX ? idx->prm.gqa_group : 1);
+  out->Gq = idx->prm.gqa_mode == ICE_GQA_MAX ? idx->prm.gqa_group : 1;
   out->norm_c = y.norm_c;
   out->codes = y.codes;
   out->list_code = y.list_code;

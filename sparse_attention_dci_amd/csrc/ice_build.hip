@@ -785,10 +785,10 @@ static hipError_t build_impl(const Dev &dv, const BuildScratch &bs, int64_t n, c
   if ((e = fill_i32(dv.page_tokens, (int64_t)dv.S * dv.pcap * dv.p, -1, st))) return e;
   if ((e = fill_i32(dv.page_len, (int64_t)dv.S * dv.pcap, 0, st))) return e;
   if ((e = fill_i32(dv.page_cell, (int64_t)dv.S * dv.pcap, -1, st))) return e;
-  if ((e = fill_i32((int32_t *)dv.hist, (int64_t)dv.S * dv.L * kHistBins, 0, st))) return e;
-  if ((e = fill_i32((int32_t *)dv.hist2, (int64_t)dv.S * dv.L * kHistBins, 0, st))) return e;
-  if ((e = fill_i32((int32_t *)dv.vhist, (int64_t)dv.S * dv.L * kHistBins, 0, st))) return e;
-  if ((e = fill_i32((int32_t *)dv.cand_count, (int64_t)dv.S * dv.L, 0, st))) return e;
+  if ((e = fill_i32((int32_t *)dv.hist, (int64_t)dv.S * dv.Lq * kHistBins, 0, st))) return e;
+  if ((e = fill_i32((int32_t *)dv.hist2, (int64_t)dv.S * dv.Lq * kHistBins, 0, st))) return e;
+  if ((e = fill_i32((int32_t *)dv.vhist, (int64_t)dv.S * dv.Lq * kHistBins, 0, st))) return e;
+  if ((e = fill_i32((int32_t *)dv.cand_count, (int64_t)dv.S * dv.Lq, 0, st))) return e;
   hipLaunchKernelGGL(k_fill_u64, dim3(1), dim3(256), 0, st, dv.maxnsq, (int64_t)dv.S, 0ull);
   {
     const int64_t total = (int64_t)dv.nchunk * (dv.d + 1) * kDirChunk;

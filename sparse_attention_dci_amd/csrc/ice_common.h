@@ -46,6 +46,10 @@ constexpr int kVisitRange = 1024;
 struct Dev {
   int S;
   int d, p, m, L, mL, g, D, k, P, k0, dtype, elem;  // elem = bytes per element
+  // GQA max mode (gmax = 1): every head walks every composite, Lq = g * L
+  // walks, Gq = g query-code sets; the mean mode has Lq = L, Gq = 1.  Every
+  // query-side array indexed by composite uses Lq (walk h * L + l).
+  int gmax, Lq, Gq;
   int64_t ncap, pcap, ncell, nbuild;
   int nchunk;          // direction chunks of kDirChunk
   int attn_nsplit;     // attention blocks per stream, ceil(k / kAttnTpb)
@@ -73,33 +77,33 @@ struct Dev {
   void *pool_k;          // [S][pcap][p][d]  key rows, slot-major
   void *pool_v;          // [S][pcap][d][p]  value columns, element-major within a page
 
-  // per-query state
-  float *qkv;            // [S][d]
-  int32_t *qcode;        // [S][mL]
-  uint32_t *mbuf;        // [S][L][ncap]
-  uint32_t *hist;        // [S][L][kHistBins]
-  uint32_t *hist2;       // [S][L][kHistBins] second level: the boundary bin's next 11 bits
-  int32_t *cand;         // [S][L][k0]
-  uint32_t *cand_count;  // [S][L]
-  unsigned long long *bnd;  // [S][L][ncap] boundary-bin entries (M << 32 | token)
-  unsigned long long *bnd_rk;  // [S][L][ncap] their rank keys
-  int32_t *bnd_pg;          // [S][L][ncap] their pages
-  uint32_t *bnd_count;      // [S][L]
-  unsigned long long *rr_key;  // [S][L*k0] rank key of each scored candidate
-  int32_t *rr_id;              // [S][L*k0]
-  int32_t *rr_pg;              // [S][L*k0] its page
+  // per-query state (walks: Lq per stream)
+  float *qkv;            // [S][Gq][d]
+  int32_t *qcode;        // [S][Gq][mL]
+  uint32_t *mbuf;        // [S][L][ncap] one pass of L walks
+  uint32_t *hist;        // [S][Lq][kHistBins]
+  uint32_t *hist2;       // [S][Lq][kHistBins] second level: the boundary bin's next 11 bits
+  int32_t *cand;         // [S][Lq][k0]
+  uint32_t *cand_count;  // [S][Lq]
+  unsigned long long *bnd;  // [S][Lq][ncap] boundary-bin entries (M << 32 | token)
+  unsigned long long *bnd_rk;  // [S][Lq][ncap] their rank keys
+  int32_t *bnd_pg;          // [S][Lq][ncap] their pages
+  uint32_t *bnd_count;      // [S][Lq]
+  unsigned long long *rr_key;  // [S][Lq*k0] rank key of each scored candidate
+  int32_t *rr_id;              // [S][Lq*k0]
+  int32_t *rr_pg;              // [S][Lq*k0] its page
   uint32_t *rr_count;          // [S]
   float *attn_part;         // [S][nsplit][g][d+2] (values, max logit, softmax sum)
 
   // visit budget k1 (bounded walks only)
   int64_t nvrange;          // ceil(ncap / kVisitRange)
-  uint32_t *vhist;          // [S][L][kHistBins] selection histogram, left cleared
-  uint32_t *vstate;         // [S][L][4] prefix / d*, remaining rank, t*, t* completes
-  uint32_t *vtie;           // [S][L][nvrange] entries at distance d* per token range
-  uint32_t *vcount;         // [S][L] n_l, the tokens the bounded walk completes
-  uint32_t *bsel;           // [S][L][2] the collect pass's threshold bin b* of each composite and
+  uint32_t *vhist;          // [S][Lq][kHistBins] selection histogram, left cleared
+  uint32_t *vstate;         // [S][Lq][4] prefix / d*, remaining rank, t*, t* completes
+  uint32_t *vtie;           // [S][Lq][nvrange] entries at distance d* per token range
+  uint32_t *vcount;         // [S][Lq] n_l, the tokens the bounded walk completes
+  uint32_t *bsel;           // [S][Lq][2] the collect pass's threshold bin b* of each walk and
                             // the count of tokens below it (for the finaliser)
-  unsigned long long *vlast;  // [S][L] query statistics: the (M, token) key of each composite's
+  unsigned long long *vlast;  // [S][Lq] query statistics: the (M, token) key of each walk's
                               // k0-th candidate, ~0 when it completed fewer
 };
 
@@ -152,7 +156,7 @@ hipError_t launch_stats(const Dev &dv, int64_t n, ice_query_stats *stats, const 
 hipError_t launch_attn(const Dev &dv, const void *q, const int32_t *page_ids,
                        const int32_t *n_pages, float *out, hipStream_t st, Timer *tm);
 // n_l of every composite for a walk bounded at k1 visits (1 <= k1 < m * n)
-hipError_t launch_visit_budget(const Dev &dv, int64_t n, uint32_t k1, hipStream_t st);
+hipError_t launch_visit_budget(const Dev &dv, int64_t n, uint32_t k1, int head, hipStream_t st);
 // insert of token n, then the query over n + 1 tokens and the attention
 hipError_t launch_decode(const Dev &dv, int64_t n, int64_t k1, const void *k_new,
                          const void *v_new, const void *q, int32_t *page_ids, int32_t *n_pages,

@@ -48,11 +48,12 @@ constexpr int kMaxTies = 256;  // page budgets up to this take the fused attenti
 // (slot_of(j) gives token j's page slot); then d/16 lanes score each row,
 // lane j summing elements 16j .. 16j+15 in order (two or four 16-byte LDS
 // reads), and the lanes' sums are added pairwise.  emit(j, slot, score)
-// receives each result.  lcs needs min(NT, ROWBYTES / (d*elem + 16)) entries;
-// rows and qkv are 16-byte aligned.
+// receives each result: with nq query vectors (qkv + 128 h, the GQA max
+// mode's heads) the largest of the nq scores.  lcs needs
+// min(NT, ROWBYTES / (d*elem + 16)) entries; rows and qkv are 16-byte aligned.
 template <int DT, int NT, int ROWBYTES, typename SlotOf, typename Emit>
 __device__ void block_score(const Dev &dv, int s, uint32_t cnt, SlotOf slot_of, const float *qkv,
-                            int32_t *lcs, uint32_t *rows, Emit emit) {
+                            int nq, int32_t *lcs, uint32_t *rows, Emit emit) {
   const int tid = threadIdx.x;
   const int d = dv.d;
   const int row_bytes = d * dv.elem;
@@ -88,16 +89,7 @@ __device__ void block_score(const Dev &dv, int s, uint32_t cnt, SlotOf slot_of, 
       const uint32_t r = x >> lnb;
       const int j = x & (nbk - 1);
       const char *rp = rb + r * rstride + j * 16 * dv.elem;
-      const float4 *qp = reinterpret_cast<const float4 *>(qkv + 16 * j);
-      float qv[16], kv[16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 f = qp[i];
-        qv[4 * i] = f.x;
-        qv[4 * i + 1] = f.y;
-        qv[4 * i + 2] = f.z;
-        qv[4 * i + 3] = f.w;
-      }
+      float kv[16];
       if constexpr (DT == 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -119,11 +111,25 @@ __device__ void block_score(const Dev &dv, int s, uint32_t cnt, SlotOf slot_of, 
           }
         }
       }
-      double z = 0.0;
+      double best = 0.0;
+      for (int h = 0; h < nq; ++h) {
+        const float4 *qp = reinterpret_cast<const float4 *>(qkv + 128 * h + 16 * j);
+        float qv[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) z = fma((double)qv[i], (double)kv[i], z);
-      z = tree_sum(z, nbk);
-      if (j == 0) emit(b0 + r, lcs[r], z);
+        for (int i = 0; i < 4; ++i) {
+          const float4 f = qp[i];
+          qv[4 * i] = f.x;
+          qv[4 * i + 1] = f.y;
+          qv[4 * i + 2] = f.z;
+          qv[4 * i + 3] = f.w;
+        }
+        double z = 0.0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) z = fma((double)qv[i], (double)kv[i], z);
+        z = tree_sum(z, nbk);
+        best = h == 0 ? z : fmax(best, z);
+      }
+      if (j == 0) emit(b0 + r, lcs[r], best);
     }
     lds_barrier();
   }
@@ -166,9 +172,14 @@ __device__ __forceinline__ int32_t ld_code(__amdgpu_buffer_rsrc_t r, uint32_t of
 // pool rows at the end.
 constexpr int kPipe = 16;
 
+//
+// GQA max mode: pass `head` walks the L composites with that head's own query
+// (its row of q alone) and fills walks head * L .. head * L + L - 1 of the
+// stream's query arrays; the mean mode has one pass, head 0.
 template <int DT, bool LDS_HIST, int R, int NT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_qscan(Dev dv, int64_t n, const void *q,
-                                                        const void *k_new, const void *v_new) {
+                                                        const void *k_new, const void *v_new,
+                                                        int head) {
   constexpr int kScanTpb = 2 * NT;
   constexpr int W = R * kPipe;  // staged direction columns (>= mL, <= the stored row width)
   constexpr int W4 = W / 4;
@@ -195,7 +206,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_
   __shared__ double qsq_s, ksq_s;
   __shared__ uint32_t cell_s;
   __shared__ int32_t loc_s;
-  uint32_t *ghist = dv.hist + (int64_t)s * L * kHistBins;
+  const int lo = head * L;                          // this pass's first walk
+  const int gq = dv.gmax ? 1 : g;                     // heads folded into this pass's query
+  const int64_t qr0 = (int64_t)s * g + (dv.gmax ? head : 0);  // its first row of q
+  uint32_t *ghist = dv.hist + ((int64_t)s * dv.Lq + lo) * kHistBins;
 
   // 1. the prep's loads, every one issued before any is used (clamped
   // addresses, no branches): the directions, heads 0..3 of element tid, the
@@ -211,7 +225,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_
   const int te = min(tid & 127, d - 1);
   float hv[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) hv[j] = load_elem<DT>(q, ((int64_t)s * g + min(j, g - 1)) * d + te);
+  for (int j = 0; j < 4; ++j) hv[j] = load_elem<DT>(q, (qr0 + min(j, gq - 1)) * d + te);
   const float kx = load_elem<DT>(k_new != nullptr ? k_new : q, (int64_t)s * d + te);
   const int32_t np0 = dv.npages[s];
   const double ic = dv.inv_c[s], ic2 = dv.inv_c2[s];
@@ -230,15 +244,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_
   }
   float acc = hv[0];  // left fold of the heads
 #pragma unroll
-  for (int j = 1; j < 4; ++j) acc = j < g ? __fadd_rn(acc, hv[j]) : acc;
-  for (int h0 = 4; h0 < g; h0 += 4) {  // groups above 4
+  for (int j = 1; j < 4; ++j) acc = j < gq ? __fadd_rn(acc, hv[j]) : acc;
+  for (int h0 = 4; h0 < gq; h0 += 4) {  // groups above 4
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      hv[j] = load_elem<DT>(q, ((int64_t)s * g + min(h0 + j, g - 1)) * d + te);
+    for (int j = 0; j < 4; ++j) hv[j] = load_elem<DT>(q, (qr0 + min(h0 + j, gq - 1)) * d + te);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc = h0 + j < g ? __fadd_rn(acc, hv[j]) : acc;
+    for (int j = 0; j < 4; ++j) acc = h0 + j < gq ? __fadd_rn(acc, hv[j]) : acc;
   }
-  if (tid < d) qkv[tid] = __fmul_rn(acc, group_inv(g));
+  if (tid < d) qkv[tid] = __fmul_rn(acc, group_inv(gq));
   if (ins && tid >= 256 && tid < 256 + d) kv[tid - 256] = kx;
   lds_barrier();
 
@@ -301,14 +314,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_
     }
   }
   lds_barrier();
-  if (r == 0) {  // publication and the query's counters
-    if (tid < mL) dv.qcode[(int64_t)s * mL + tid] = qc[tid];
-    if (tid < d) dv.qkv[(int64_t)s * d + tid] = qkv[tid];
+  if (r == 0) {  // publication and the query's counters (the rerank list's: first pass only)
+    const int64_t hq = (int64_t)s * dv.Gq + (dv.gmax ? head : 0);
+    if (tid < mL) dv.qcode[hq * mL + tid] = qc[tid];
+    if (tid < d) dv.qkv[hq * d + tid] = qkv[tid];
     if (tid < L) {
-      dv.cand_count[s * L + tid] = 0;
-      dv.bnd_count[s * L + tid] = 0;
+      dv.cand_count[s * dv.Lq + lo + tid] = 0;
+      dv.bnd_count[s * dv.Lq + lo + tid] = 0;
     }
-    if (tid == 0) dv.rr_count[s] = 0;
+    if (tid == 0 && head == 0) dv.rr_count[s] = 0;
   }
   if (LDS_HIST) {  // 16-byte stores (the union is 16-byte aligned: float4 staging)
     uint4 *h4 = reinterpret_cast<uint4 *>(sm.hist);
@@ -436,19 +450,23 @@ struct CollectShape {
   static constexpr int kWavesPerEu = NT == 512 ? 6 : 4;
 };
 
+//
+// GQA max mode: pass `head` serves walks head * L + l; every candidate is
+// scored against all g heads (read from q) and ranked by the largest score.
 template <int DT, int NT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape<NT>::kWavesPerEu))) void k_qcollect(
-    Dev dv, int64_t n, bool bounded) {
+    Dev dv, int64_t n, bool bounded, int head, const void *q) {
   constexpr int kScanThreads = NT, kScanTpb = 2 * NT;
   constexpr int kCollectRowBytes = CollectShape<NT>::kRowBytes;
   const int s = blockIdx.x % dv.S;  // the scan's block-to-stream mapping
   const int64_t rng = blockIdx.x / dv.S;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int L = dv.L;
+  const int L = dv.L, Lq = dv.Lq, lo = head * L;
+  const int nq = dv.gmax ? dv.g : 1;  // query vectors a candidate is scored against
   __shared__ int32_t bstar[32];  // -1: the composite takes no candidates
   __shared__ uint32_t ccount[32], bcount[32], cbase[32], bbase[32];
   __shared__ uint32_t nc, nrl, rbase;
-  __shared__ __attribute__((aligned(16))) float qkv[128];
+  __shared__ __attribute__((aligned(16))) float qkv[kMaxGroup * 128];  // [nq][128]
   __shared__ int32_t cid[kScanTpb];      // candidate or boundary tokens, as offsets in the block
   __shared__ int32_t lloc[kScanTpb];     // page slots of the block's tokens
   __shared__ unsigned long long skb[kScanTpb];
@@ -487,20 +505,33 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
     }
     return M;
   };
-  const float qk = dv.qkv[(int64_t)s * dv.d + min(tid, dv.d - 1)];
+  // the query vectors: q_kv (mean mode), or the g heads as fp32 (max mode)
+  float qk[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int x = min(tid + kScanThreads * u, nq * dv.d - 1);
+    qk[u] = dv.gmax ? load_elem<DT>(q, (int64_t)s * dv.g * dv.d + x) : dv.qkv[(int64_t)s * dv.d + x];
+  }
   for (int l = w; l < L; l += kScanThreads / 64) {
-    const uint32_t kl = bounded ? min(k0e, dv.vcount[s * L + l]) : k0e;
+    const uint32_t kl = bounded ? min(k0e, dv.vcount[s * Lq + lo + l]) : k0e;
     uint32_t bb = 0, bl = 0;
-    if (kl > 0) wave_find_bin(dv.hist + ((int64_t)s * L + l) * kHistBins, kl, bb, bl);
+    if (kl > 0) wave_find_bin(dv.hist + ((int64_t)s * Lq + lo + l) * kHistBins, kl, bb, bl);
     if (lane == 0) {
       bstar[l] = kl > 0 ? (int32_t)bb : -1;
       if (rng == 0) {  // for the finaliser: b* and the count below it
-        dv.bsel[((int64_t)s * L + l) * 2] = bb;
-        dv.bsel[((int64_t)s * L + l) * 2 + 1] = bl;
+        dv.bsel[((int64_t)s * Lq + lo + l) * 2] = bb;
+        dv.bsel[((int64_t)s * Lq + lo + l) * 2 + 1] = bl;
       }
     }
   }
-  if (tid < dv.d) qkv[tid] = qk;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int x = tid + kScanThreads * u;
+    if (x < nq * dv.d) qkv[(x / dv.d) * 128 + x % dv.d] = qk[u];
+  }
+  for (int x = tid + 2 * kScanThreads; x < nq * dv.d; x += kScanThreads)  // g * d > 2 * NT
+    qkv[(x / dv.d) * 128 + x % dv.d] =
+        load_elem<DT>(q, (int64_t)s * dv.g * dv.d + x);
   lloc[tid] = lc[0];
   lloc[kScanThreads + tid] = lc[1];
   if (tid < L) {
@@ -528,7 +559,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
         if (bb < bstar[l]) below[u] |= 1u << l;
         if (bb == bstar[l]) {
           bnd[u] |= 1u << l;
-          atomicAdd(&dv.hist2[((int64_t)s * L + l) * kHistBins + ((M >> kSubShift) & (kHistBins - 1))],
+          atomicAdd(&dv.hist2[((int64_t)s * Lq + lo + l) * kHistBins +
+                              ((M >> kSubShift) & (kHistBins - 1))],
                     1u);
         }
       }
@@ -548,8 +580,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
   // 3. one device atomic per list for the block, consumed after the scoring
   uint32_t my_c = 0, my_b = 0, my_r = 0;
   if (tid < L) {
-    my_c = ccount[tid] ? atomicAdd(&dv.cand_count[s * L + tid], ccount[tid]) : 0u;
-    my_b = bcount[tid] ? atomicAdd(&dv.bnd_count[s * L + tid], bcount[tid]) : 0u;
+    my_c = ccount[tid] ? atomicAdd(&dv.cand_count[s * Lq + lo + tid], ccount[tid]) : 0u;
+    my_b = bcount[tid] ? atomicAdd(&dv.bnd_count[s * Lq + lo + tid], bcount[tid]) : 0u;
   }
   if (tid == 64) my_r = nrl ? atomicAdd(&dv.rr_count[s], nrl) : 0u;
 
@@ -559,7 +591,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
   int32_t *spbp = spb;
   const int32_t *cidp = cid, *llocp = lloc;
   block_score<DT, kScanThreads, kCollectRowBytes>(
-      dv, s, nc, [cidp, llocp](uint32_t j) { return llocp[cidp[j]]; }, qkv, lcs, rows,
+      dv, s, nc, [cidp, llocp](uint32_t j) { return llocp[cidp[j]]; }, qkv, nq, lcs, rows,
       [skbp, spbp, lp](uint32_t x, int32_t slotx, double sc) {
         skbp[x] = score_rank_key(sc);
         spbp[x] = slotx >> lp;
@@ -577,7 +609,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
     nrl = 0;
   }
   lds_barrier();
-  const int64_t rr0 = (int64_t)s * L * dv.k0;
+  const int64_t rr0 = (int64_t)s * Lq * dv.k0;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     if (slot[u] < 0) continue;
@@ -592,9 +624,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
     }
     for (int l = 0; l < L; ++l) {
       if ((below[u] >> l) & 1u)
-        dv.cand[((int64_t)s * L + l) * dv.k0 + cbase[l] + atomicAdd(&ccount[l], 1u)] = i;
+        dv.cand[((int64_t)s * Lq + lo + l) * dv.k0 + cbase[l] + atomicAdd(&ccount[l], 1u)] = i;
       if ((bnd[u] >> l) & 1u) {
-        const int64_t o = ((int64_t)s * L + l) * dv.ncap + bbase[l] + atomicAdd(&bcount[l], 1u);
+        const int64_t o = ((int64_t)s * Lq + lo + l) * dv.ncap + bbase[l] + atomicAdd(&bcount[l], 1u);
         dv.bnd[o] = ((unsigned long long)Mof(u, l) << 32) | (uint32_t)i;
         dv.bnd_rk[o] = rk;
         dv.bnd_pg[o] = pg;
@@ -684,7 +716,7 @@ __device__ __forceinline__ void final_stats(const Dev &dv, int s, int64_t n, uin
                                             const unsigned long long *klast, uint32_t nu,
                                             uint32_t nsel, ice_query_stats *stats,
                                             unsigned long long vlimit) {
-  const int tid = threadIdx.x, L = dv.L;
+  const int tid = threadIdx.x, L = dv.Lq;
   if (tid < L) {
     const uint32_t kl = k0e > 0 ? cc[tid] + extra[tid] : 0u;
     const bool full = n > 0 && kl == (uint32_t)dv.k0;
@@ -750,7 +782,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
   __shared__ FinalShared sh;
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int L = dv.L, k0 = dv.k0;
+  const int L = dv.Lq, k0 = dv.k0;  // the query's walks
   const uint32_t k0e = (uint32_t)min((int64_t)k0, n);
 
   // A. loads, all issued before any is used (one round trip): the
@@ -837,7 +869,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
     const uint32_t incl = wave_incl_scan(v);
     if (lane <= L) sh.boff[lane] = incl - v;
     if (lane == 0) {
-      sh.nu = nrr;
+      sh.nu = dv.gmax ? 0u : nrr;  // max mode: counted as the union is deduplicated
       sh.ntie = 0;
     }
   }
@@ -849,14 +881,32 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
 
   // B. the scored below-bin candidates and, when they fit, the boundary
   // entries (a composite's entries past the prefetched ones are loaded here)
+  if (!dv.gmax) {  // one pass: the rerank list holds every token once
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const uint32_t x = tid + kFinalThreads * j;
-    if (x < nrr) {
-      mark(pid[j]);
-      sh.sid[x] = pid[j];
-      sh.skey[x] = pkey[j];
-      sh.spg[x] = ppg[j];
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t x = tid + kFinalThreads * j;
+      if (x < nrr) {
+        mark(pid[j]);
+        sh.sid[x] = pid[j];
+        sh.skey[x] = pkey[j];
+        sh.spg[x] = ppg[j];
+      }
+    }
+  } else {  // the heads' passes repeat tokens: the first of each joins the union
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t x = tid + kFinalThreads * j;
+      const bool fresh = x < nrr && mark(pid[j]);
+      const unsigned long long bal = __ballot(fresh);
+      uint32_t base = 0;
+      if (lane == 0 && bal) base = atomicAdd(&sh.nu, (uint32_t)popc64(bal));
+      base = (uint32_t)__shfl((int)base, 0);
+      if (fresh) {
+        const uint32_t pos = base + (uint32_t)popc64(bal & lanemask_lt());
+        sh.sid[pos] = pid[j];
+        sh.skey[pos] = pkey[j];
+        sh.spg[pos] = ppg[j];
+      }
     }
   }
   if (bnd_lds) {
@@ -1194,7 +1244,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
   constexpr int NT = kFinalThreads;
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int L = dv.L, k0 = dv.k0;
+  const int L = dv.Lq, k0 = dv.k0;  // the query's walks
   const uint32_t k0e = (uint32_t)min((int64_t)k0, n);
   const int64_t o0 = (int64_t)s * L * k0;  // the stream's union arrays (rerank list first)
   unsigned long long *ukey = dv.rr_key + o0;
@@ -1629,44 +1679,49 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
 
 template <int DT, bool LH, int R, int NT>
 static void launch_scan(const Dev &dv, int64_t n, unsigned grid, const void *q, const void *k_new,
-                        const void *v_new, hipStream_t st) {
+                        const void *v_new, int head, hipStream_t st) {
   hipLaunchKernelGGL((k_qscan<DT, LH, R, NT>), dim3(grid), dim3(NT), 0, st, dv, n, q, k_new,
-                     v_new);
+                     v_new, head);
 }
 
 template <int DT, bool LH, int NT>
 static void launch_scan_r(const Dev &dv, int64_t n, unsigned grid, const void *q,
-                          const void *k_new, const void *v_new, hipStream_t st) {
+                          const void *k_new, const void *v_new, int head, hipStream_t st) {
   switch ((dv.mL + kPipe - 1) / kPipe) {
-    case 1: launch_scan<DT, LH, 1, NT>(dv, n, grid, q, k_new, v_new, st); break;
-    case 2: launch_scan<DT, LH, 2, NT>(dv, n, grid, q, k_new, v_new, st); break;
-    case 3: launch_scan<DT, LH, 3, NT>(dv, n, grid, q, k_new, v_new, st); break;
-    case 4: launch_scan<DT, LH, 4, NT>(dv, n, grid, q, k_new, v_new, st); break;
-    case 5: launch_scan<DT, LH, 5, NT>(dv, n, grid, q, k_new, v_new, st); break;
-    case 6: launch_scan<DT, LH, 6, NT>(dv, n, grid, q, k_new, v_new, st); break;
-    case 7: launch_scan<DT, LH, 7, NT>(dv, n, grid, q, k_new, v_new, st); break;
-    default: launch_scan<DT, LH, 8, NT>(dv, n, grid, q, k_new, v_new, st); break;  // mL <= 128
+    case 1: launch_scan<DT, LH, 1, NT>(dv, n, grid, q, k_new, v_new, head, st); break;
+    case 2: launch_scan<DT, LH, 2, NT>(dv, n, grid, q, k_new, v_new, head, st); break;
+    case 3: launch_scan<DT, LH, 3, NT>(dv, n, grid, q, k_new, v_new, head, st); break;
+    case 4: launch_scan<DT, LH, 4, NT>(dv, n, grid, q, k_new, v_new, head, st); break;
+    case 5: launch_scan<DT, LH, 5, NT>(dv, n, grid, q, k_new, v_new, head, st); break;
+    case 6: launch_scan<DT, LH, 6, NT>(dv, n, grid, q, k_new, v_new, head, st); break;
+    case 7: launch_scan<DT, LH, 7, NT>(dv, n, grid, q, k_new, v_new, head, st); break;
+    default: launch_scan<DT, LH, 8, NT>(dv, n, grid, q, k_new, v_new, head, st); break;  // mL <= 128
   }
 }
 
-// Scan and collect over n tokens with NT-thread blocks of 2 * NT tokens.
+// Scan and collect over n tokens with NT-thread blocks of 2 * NT tokens: one
+// pass per head in the GQA max mode (the first one inserts the new token).
 template <int DT, int NT>
 static void scan_collect(const Dev &dv, int64_t n, bool bounded, uint32_t k1, const void *q,
                          const void *k_new, const void *v_new, hipStream_t st, Timer *tm) {
   const int64_t nrange = (n + 2 * NT - 1) / (2 * NT);
   const unsigned grid = (unsigned)(max(nrange, (int64_t)1) * dv.S);
-  if (dv.L <= 6)
-    launch_scan_r<DT, true, NT>(dv, n, grid, q, k_new, v_new, st);
-  else
-    launch_scan_r<DT, false, NT>(dv, n, grid, q, k_new, v_new, st);
-  timer_mark(tm, KID_QSCAN, st);
-  if (bounded) {
-    (void)launch_visit_budget(dv, n, k1, st);  // a launch error stays for the caller's check
-    timer_mark(tm, KID_VISIT, st);
-  }
-  if (n > 0) {
-    hipLaunchKernelGGL((k_qcollect<DT, NT>), dim3(grid), dim3(NT), 0, st, dv, n, bounded);
-    timer_mark(tm, KID_QCOLLECT, st);
+  for (int head = 0; head < dv.Gq; ++head) {
+    const void *kn = head == 0 ? k_new : nullptr, *vn = head == 0 ? v_new : nullptr;
+    if (dv.L <= 6)
+      launch_scan_r<DT, true, NT>(dv, n, grid, q, kn, vn, head, st);
+    else
+      launch_scan_r<DT, false, NT>(dv, n, grid, q, kn, vn, head, st);
+    timer_mark(tm, KID_QSCAN, st);
+    if (bounded) {
+      (void)launch_visit_budget(dv, n, k1, head, st);  // a launch error stays for the caller's check
+      timer_mark(tm, KID_VISIT, st);
+    }
+    if (n > 0) {
+      hipLaunchKernelGGL((k_qcollect<DT, NT>), dim3(grid), dim3(NT), 0, st, dv, n, bounded, head,
+                         q);
+      timer_mark(tm, KID_QCOLLECT, st);
+    }
   }
 }
 
@@ -1704,10 +1759,10 @@ static void query_tail(const Dev &dv, int64_t n, int64_t k1, int32_t *page_ids,
     scan_collect<DT, 768>(dv, n, bounded, (uint32_t)k1, q, k_new, v_new, st, tm);
   else
     scan_collect<DT, 1024>(dv, n, bounded, (uint32_t)k1, q, k_new, v_new, st, tm);
-  if (dv.L * dv.k0 > kMaxCand)
+  if (dv.Lq * dv.k0 > kMaxCand)
     hipLaunchKernelGGL(k_qfinal_big<DT>, dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n, bounded,
                        page_ids, n_pages, topk_ids, stats, vlimit);
-  else if (dv.L * dv.k0 <= kFinalThreads)
+  else if (dv.Lq * dv.k0 <= kFinalThreads)
     launch_final<DT, 1>(dv, n, bounded, page_ids, n_pages, topk_ids, q, out, stats, vlimit, st);
   else
     launch_final<DT, kMaxCand / kFinalThreads>(dv, n, bounded, page_ids, n_pages, topk_ids, q,
@@ -1741,7 +1796,7 @@ hipError_t launch_decode(const Dev &dv, int64_t n, int64_t k1, const void *k_new
   // Larger budgets take the standalone kernels, whose per-split partials and
   // merge fix the summation order, so the step equals the separate calls.
   timer_begin(tm, st);
-  const bool fused = dv.attn_nsplit == 1 && dv.L * dv.k0 <= kMaxCand;
+  const bool fused = dv.attn_nsplit == 1 && dv.Lq * dv.k0 <= kMaxCand;
   float *fo = fused ? out : nullptr;
   if (dv.dtype == 0)
     query_tail<0>(dv, n + 1, k1, page_ids, n_pages, topk_ids, q, k_new, v_new, fo, stats, st, tm);

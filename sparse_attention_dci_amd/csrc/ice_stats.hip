@@ -26,13 +26,15 @@ __global__ __launch_bounds__(kStatsThreads) void k_qstats(Dev dv, int64_t n,
                                                           const int32_t *page_ids,
                                                           const int32_t *n_pages) {
   const int s = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
-  const int m = dv.m, L = dv.L, mL = dv.mL;
+  // walk l = h * L + c: composite c's codes against head h's query codes (one
+  // head, h = 0, in the mean mode)
+  const int m = dv.m, Lc = dv.L, L = dv.Lq, mL = dv.mL;
   const int64_t i0 = (int64_t)blockIdx.x * kStatsTpb;
-  __shared__ int32_t qc[kMaxMl];
+  __shared__ int32_t qc[kMaxGroup * kMaxMl];
   __shared__ uint32_t Ms[32];
   __shared__ int32_t is[32], js[32];
   __shared__ uint32_t cnt[32];
-  if (tid < mL) qc[tid] = dv.qcode[(int64_t)s * mL + tid];
+  for (int x = tid; x < dv.Gq * mL; x += kStatsThreads) qc[x] = dv.qcode[(int64_t)s * dv.Gq * mL + x];
   if (tid < L) {
     const unsigned long long key = dv.vlast[(int64_t)s * L + tid];
     Ms[tid] = (uint32_t)(key >> 32);
@@ -41,10 +43,12 @@ __global__ __launch_bounds__(kStatsThreads) void k_qstats(Dev dv, int64_t n,
   }
   __syncthreads();
   if (tid < L && is[tid] >= 0) {  // j*: the last list at distance M* for token i*
+    const int h = tid / Lc, c = tid % Lc;
     int jl = 0;
     for (int j = 0; j < m; ++j) {
-      const int t = tid * m + j;
-      if (absdiff(dv.codes[code_index(dv.ntile, mL, s, is[tid], t)], qc[t]) == Ms[tid]) jl = j;
+      const int t = c * m + j;
+      if (absdiff(dv.codes[code_index(dv.ntile, mL, s, is[tid], t)], qc[h * mL + t]) == Ms[tid])
+        jl = j;
     }
     js[tid] = jl;
   }
@@ -54,14 +58,15 @@ __global__ __launch_bounds__(kStatsThreads) void k_qstats(Dev dv, int64_t n,
     const uint32_t M = Ms[l];
     const int64_t ist = is[l];
     const int jst = js[l];
+    const int h = l / Lc, cmp = l % Lc;
     uint32_t c = 0;
 #pragma unroll
     for (int u = 0; u < kStatsTpb / kStatsThreads; ++u) {
       const int64_t i = i0 + tid + (int64_t)kStatsThreads * u;
       if (i >= n) break;
       for (int j = 0; j < m; ++j) {
-        const int t = l * m + j;
-        const uint32_t dd = absdiff(dv.codes[code_index(dv.ntile, mL, s, i, t)], qc[t]);
+        const int t = cmp * m + j;
+        const uint32_t dd = absdiff(dv.codes[code_index(dv.ntile, mL, s, i, t)], qc[h * mL + t]);
         c += dd < M || (dd == M && (i < ist || (i == ist && j <= jst)));
       }
     }

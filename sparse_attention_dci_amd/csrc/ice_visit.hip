@@ -22,8 +22,18 @@ namespace ice {
 constexpr int kVisitThreads = 256;
 constexpr uint32_t kLowMask = (1u << (kHistShift - kHistBits)) - 1u;  // the last 9 bits
 
-// The three selection passes; the state of composite (s, l) is
-// vstate[4 * (s * L + l) + {0: selected prefix, 1: remaining rank (1-based),
+// GQA max mode: each kernel serves the walks of one head's pass, walk
+// head * L + l of the stream (composite l, the head's query codes); the mean
+// mode has the one pass, head 0.
+__device__ __forceinline__ int64_t walk_of(const Dev &dv, int s, int head, int l) {
+  return (int64_t)s * dv.Lq + head * dv.L + l;
+}
+__device__ __forceinline__ const int32_t *qcode_of(const Dev &dv, int s, int head) {
+  return dv.qcode + ((int64_t)s * dv.Gq + (dv.gmax ? head : 0)) * dv.mL;
+}
+
+// The three selection passes; the state of walk w = walk_of(s, head, l) is
+// vstate[4 * w + {0: selected prefix, 1: remaining rank (1-based),
 // 2: t*, 3: whether t* completes}].
 template <int LEVEL>
 __device__ __forceinline__ void visit_bin(uint32_t dd, uint32_t pre, uint32_t *h) {
@@ -40,16 +50,16 @@ __device__ __forceinline__ void visit_bin(uint32_t dd, uint32_t pre, uint32_t *h
 // b / S); per composite, an LDS histogram of the range's entries, added to the
 // stream's global one.
 template <int LEVEL>
-__global__ __launch_bounds__(kVisitThreads) void k_visit_hist(Dev dv, int64_t n) {
+__global__ __launch_bounds__(kVisitThreads) void k_visit_hist(Dev dv, int64_t n, int head) {
   const int S = dv.S, s = blockIdx.x % S, tid = threadIdx.x;
   const int m = dv.m, L = dv.L, mL = dv.mL;
   const int64_t r = blockIdx.x / S;
   const int64_t i0 = r * kVisitRange, i1 = min(i0 + kVisitRange, n);
   __shared__ uint32_t h[kHistBins];
   __shared__ int32_t qc[kMaxMl];
-  if (tid < mL) qc[tid] = dv.qcode[(int64_t)s * mL + tid];
+  if (tid < mL) qc[tid] = qcode_of(dv, s, head)[tid];
   for (int l = 0; l < L; ++l) {
-    const uint32_t pre = LEVEL > 0 ? dv.vstate[4 * ((int64_t)s * L + l)] : 0u;
+    const uint32_t pre = LEVEL > 0 ? dv.vstate[4 * walk_of(dv, s, head, l)] : 0u;
     for (int x = tid; x < kHistBins; x += kVisitThreads) h[x] = 0;
     __syncthreads();
     for (int64_t i = i0 + tid; i < i1; i += kVisitThreads)
@@ -58,7 +68,7 @@ __global__ __launch_bounds__(kVisitThreads) void k_visit_hist(Dev dv, int64_t n)
         visit_bin<LEVEL>(absdiff(dv.codes[code_index(dv.ntile, mL, s, i, t)], qc[t]), pre, h);
       }
     __syncthreads();
-    uint32_t *g = dv.vhist + ((int64_t)s * L + l) * kHistBins;
+    uint32_t *g = dv.vhist + walk_of(dv, s, head, l) * kHistBins;
     for (int x = tid; x < kHistBins; x += kVisitThreads) {
       const uint32_t c = h[x];
       if (c) atomicAdd(&g[x], c);
@@ -70,10 +80,11 @@ __global__ __launch_bounds__(kVisitThreads) void k_visit_hist(Dev dv, int64_t n)
 // One wave per composite (block s * L + l): the bin holding the remaining
 // rank, the new prefix and rank; the histogram is left cleared.
 template <int LEVEL>
-__global__ __launch_bounds__(64) void k_visit_pick(Dev dv, uint32_t k1) {
-  const int sl = blockIdx.x, lane = threadIdx.x;
-  uint32_t *g = dv.vhist + (int64_t)sl * kHistBins;
-  uint32_t *st = dv.vstate + 4 * (int64_t)sl;
+__global__ __launch_bounds__(64) void k_visit_pick(Dev dv, uint32_t k1, int head) {
+  const int lane = threadIdx.x;
+  const int64_t wk = walk_of(dv, blockIdx.x / dv.L, head, blockIdx.x % dv.L);
+  uint32_t *g = dv.vhist + wk * kHistBins;
+  uint32_t *st = dv.vstate + 4 * wk;
   const uint32_t target = LEVEL == 0 ? k1 : st[1];
   const uint32_t pre = LEVEL == 0 ? 0u : st[0];
   uint32_t v[kBinsPerLane];
@@ -104,17 +115,17 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t c, uint32_t *red) {
 }
 
 // Per range and composite: the entries at distance exactly d*.
-__global__ __launch_bounds__(kVisitThreads) void k_visit_ties(Dev dv, int64_t n) {
+__global__ __launch_bounds__(kVisitThreads) void k_visit_ties(Dev dv, int64_t n, int head) {
   const int S = dv.S, s = blockIdx.x % S, tid = threadIdx.x;
   const int m = dv.m, L = dv.L, mL = dv.mL;
   const int64_t r = blockIdx.x / S;
   const int64_t i0 = r * kVisitRange, i1 = min(i0 + kVisitRange, n);
   __shared__ int32_t qc[kMaxMl];
   __shared__ uint32_t red[kVisitThreads / 64];
-  if (tid < mL) qc[tid] = dv.qcode[(int64_t)s * mL + tid];
+  if (tid < mL) qc[tid] = qcode_of(dv, s, head)[tid];
   __syncthreads();
   for (int l = 0; l < L; ++l) {
-    const uint32_t ds = dv.vstate[4 * ((int64_t)s * L + l)];
+    const uint32_t ds = dv.vstate[4 * walk_of(dv, s, head, l)];
     uint32_t c = 0;
     for (int64_t i = i0 + tid; i < i1; i += kVisitThreads)
       for (int j = 0; j < m; ++j) {
@@ -122,7 +133,7 @@ __global__ __launch_bounds__(kVisitThreads) void k_visit_ties(Dev dv, int64_t n)
         c += absdiff(dv.codes[code_index(dv.ntile, mL, s, i, t)], qc[t]) == ds;
       }
     c = block_sum(c, red);
-    if (tid == 0) dv.vtie[((int64_t)s * L + l) * dv.nvrange + r] = c;
+    if (tid == 0) dv.vtie[walk_of(dv, s, head, l) * dv.nvrange + r] = c;
   }
 }
 
@@ -130,14 +141,15 @@ __global__ __launch_bounds__(kVisitThreads) void k_visit_ties(Dev dv, int64_t n)
 // remaining-rank-th entry at distance d* (entries in (token, list) order),
 // the list j* of that entry, and whether it is t*'s largest entry (M_t* = d*
 // and no later list of t* at d*).  Also seeds the completed-token count.
-__global__ __launch_bounds__(64) void k_visit_resolve(Dev dv, int64_t n) {
+__global__ __launch_bounds__(64) void k_visit_resolve(Dev dv, int64_t n, int head) {
   const int sl = blockIdx.x, lane = threadIdx.x;
   const int L = dv.L, s = sl / L, l = sl % L, m = dv.m, mL = dv.mL;
-  uint32_t *st = dv.vstate + 4 * (int64_t)sl;
+  const int64_t wk = walk_of(dv, s, head, l);
+  uint32_t *st = dv.vstate + 4 * wk;
   const uint32_t ds = st[0];
   uint32_t rr = st[1];
   const int64_t nr = (n + kVisitRange - 1) / kVisitRange;
-  const uint32_t *tc = dv.vtie + (int64_t)sl * dv.nvrange;
+  const uint32_t *tc = dv.vtie + wk * dv.nvrange;
   int64_t rg = -1;
   for (int64_t b0 = 0; b0 < nr; b0 += 64) {  // uniform loop: rr and the ballot are wave-wide
     const uint32_t c = b0 + lane < nr ? tc[b0 + lane] : 0u;
@@ -151,7 +163,7 @@ __global__ __launch_bounds__(64) void k_visit_resolve(Dev dv, int64_t n) {
     }
     rr -= __shfl(incl, 63);
   }
-  const int32_t *qs = dv.qcode + (int64_t)s * mL + l * m;
+  const int32_t *qs = qcode_of(dv, s, head) + l * m;
   auto dist = [&](int64_t i, int j) {
     return absdiff(dv.codes[code_index(dv.ntile, mL, s, i, l * m + j)], qs[j]);
   };
@@ -193,18 +205,18 @@ __global__ __launch_bounds__(64) void k_visit_resolve(Dev dv, int64_t n) {
     }
     st[2] = ts >= 0 ? (uint32_t)ts : (uint32_t)n;
     st[3] = done;
-    dv.vcount[sl] = done;
+    dv.vcount[wk] = done;
   }
 }
 
 // Per range and composite: tokens with M < d*, or M = d* and token < t*.
-__global__ __launch_bounds__(kVisitThreads) void k_visit_count(Dev dv, int64_t n) {
+__global__ __launch_bounds__(kVisitThreads) void k_visit_count(Dev dv, int64_t n, int head) {
   const int S = dv.S, s = blockIdx.x % S, tid = threadIdx.x, L = dv.L;
   const int64_t r = blockIdx.x / S;
   const int64_t i0 = r * kVisitRange, i1 = min(i0 + kVisitRange, n);
   __shared__ uint32_t red[kVisitThreads / 64];
   for (int l = 0; l < L; ++l) {
-    const uint32_t *st = dv.vstate + 4 * ((int64_t)s * L + l);
+    const uint32_t *st = dv.vstate + 4 * walk_of(dv, s, head, l);
     const uint32_t ds = st[0], ts = st[2];
     const uint32_t *mrow = dv.mbuf + ((int64_t)s * L + l) * dv.ncap;
     uint32_t c = 0;
@@ -213,22 +225,22 @@ __global__ __launch_bounds__(kVisitThreads) void k_visit_count(Dev dv, int64_t n
       c += (M < ds) || (M == ds && (uint32_t)i < ts);
     }
     c = block_sum(c, red);
-    if (tid == 0 && c) atomicAdd(&dv.vcount[(int64_t)s * L + l], c);
+    if (tid == 0 && c) atomicAdd(&dv.vcount[walk_of(dv, s, head, l)], c);
   }
 }
 
-hipError_t launch_visit_budget(const Dev &dv, int64_t n, uint32_t k1, hipStream_t st) {
+hipError_t launch_visit_budget(const Dev &dv, int64_t n, uint32_t k1, int head, hipStream_t st) {
   const int64_t nr = (n + kVisitRange - 1) / kVisitRange;
   const dim3 grid((unsigned)(nr * dv.S)), sl((unsigned)(dv.S * dv.L));
-  hipLaunchKernelGGL(k_visit_hist<0>, grid, dim3(kVisitThreads), 0, st, dv, n);
-  hipLaunchKernelGGL(k_visit_pick<0>, sl, dim3(64), 0, st, dv, k1);
-  hipLaunchKernelGGL(k_visit_hist<1>, grid, dim3(kVisitThreads), 0, st, dv, n);
-  hipLaunchKernelGGL(k_visit_pick<1>, sl, dim3(64), 0, st, dv, k1);
-  hipLaunchKernelGGL(k_visit_hist<2>, grid, dim3(kVisitThreads), 0, st, dv, n);
-  hipLaunchKernelGGL(k_visit_pick<2>, sl, dim3(64), 0, st, dv, k1);
-  hipLaunchKernelGGL(k_visit_ties, grid, dim3(kVisitThreads), 0, st, dv, n);
-  hipLaunchKernelGGL(k_visit_resolve, sl, dim3(64), 0, st, dv, n);
-  hipLaunchKernelGGL(k_visit_count, grid, dim3(kVisitThreads), 0, st, dv, n);
+  hipLaunchKernelGGL(k_visit_hist<0>, grid, dim3(kVisitThreads), 0, st, dv, n, head);
+  hipLaunchKernelGGL(k_visit_pick<0>, sl, dim3(64), 0, st, dv, k1, head);
+  hipLaunchKernelGGL(k_visit_hist<1>, grid, dim3(kVisitThreads), 0, st, dv, n, head);
+  hipLaunchKernelGGL(k_visit_pick<1>, sl, dim3(64), 0, st, dv, k1, head);
+  hipLaunchKernelGGL(k_visit_hist<2>, grid, dim3(kVisitThreads), 0, st, dv, n, head);
+  hipLaunchKernelGGL(k_visit_pick<2>, sl, dim3(64), 0, st, dv, k1, head);
+  hipLaunchKernelGGL(k_visit_ties, grid, dim3(kVisitThreads), 0, st, dv, n, head);
+  hipLaunchKernelGGL(k_visit_resolve, sl, dim3(64), 0, st, dv, n, head);
+  hipLaunchKernelGGL(k_visit_count, grid, dim3(kVisitThreads), 0, st, dv, n, head);
   return hipGetLastError();
 }
 

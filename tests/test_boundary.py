@@ -194,3 +194,21 @@ def test_noalloc_build_limits(L):
     st = L.ice_build_index_noalloc(ctypes.byref(p), 8, 1000, 1000, FAKE, FAKE, FAKE, FAKE,
                                   1 << 40, None, None)
     assert st == B.ICE_ERR_INVALID_ARG
+
+
+def test_gqa_mode_rules(L):
+    """GQA max mode: an unknown mode is refused; g * L walks above 32, or
+    g * L * k0 above 4,096 pooled candidates, are UNSUPPORTED (ice_workspace_bytes
+    reports 0 and the build refuses before any HIP call)."""
+    h = ctypes.c_void_p()
+    bad = good()
+    bad.gqa_mode = 2
+    assert L.ice_workspace_bytes(ctypes.byref(bad), 8, 1000, 1000) == 0
+    ok = good(gqa_mode="max")  # g 4 x L 4 = 16 walks x k0 256 = 4,096
+    assert L.ice_workspace_bytes(ctypes.byref(ok), 8, 36864, 36864) > \
+        L.ice_workspace_bytes(ctypes.byref(good()), 8, 36864, 36864)
+    for kw in (dict(gqa_group=8, L=5, m=2), dict(budget_k=512)):
+        p = good(gqa_mode="max", **kw)
+        st = L.ice_build_index(ctypes.byref(p), 8, 1000, 1000, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                               FAKE, 1 << 40, None, ctypes.byref(h))
+        assert st == B.ICE_ERR_UNSUPPORTED and not h.value, kw

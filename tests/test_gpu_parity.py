@@ -117,7 +117,7 @@ def _check_query(idx, st, s, r, page_ids, n_pages, topk, out, q_s):
     np.testing.assert_array_equal(idx.view("qcode")[s].cpu().numpy(), r["qcode"])
     cand = idx.view("cand")[s].cpu().numpy()
     cc = idx.view("cand_count")[s].cpu().numpy()
-    for l in range(st.prm.L):
+    for l in range(len(r["S"])):  # every walk: L, or g * L in the GQA max mode
         np.testing.assert_array_equal(np.sort(cand[l, :cc[l]]), np.sort(r["S"][l]),
                                       err_msg=f"candidates of composite {l}")
     nsel = int(n_pages[s].item())
@@ -133,7 +133,7 @@ def _check_query(idx, st, s, r, page_ids, n_pages, topk, out, q_s):
 
 
 def run_case(B, *, S, n, d=128, g=1, p=16, k=256, m=4, L=2, dtype="bf16", clusters=32,
-             seed=1, inserts=0, k0=0, k1=0, check=None, keys=None, literal=True):
+             seed=1, inserts=0, k0=0, k1=0, check=None, keys=None, literal=True, gqa="mean"):
     dev = torch.device("cuda")
     cap = n + inserts
     if keys is None:
@@ -145,14 +145,14 @@ def run_case(B, *, S, n, d=128, g=1, p=16, k=256, m=4, L=2, dtype="bf16", cluste
           f"k0={k0} k1={k1}", flush=True)
     idx = B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U.to(dev),
                   page_size=p, budget_k=k, m=m, L=L, gqa_group=g, k0=k0, k1=k1,
-                  capacity=max(cap, 1))
+                  capacity=max(cap, 1), gqa_mode=gqa)
     for t in range(inserts):
         idx.insert(K[:, n + t].contiguous().to(dev), V[:, n + t].contiguous().to(dev))
     qd = q.to(dev)
     page_ids, n_pages, topk = idx.query_pages(qd, with_topk=True)
     out = idx.sparse_attn(qd, page_ids, n_pages)
     torch.cuda.synchronize()
-    prm = oracle.Params(d=d, p=p, k=k, m=m, L=L, g=g, k0=k0, k1=k1)
+    prm = oracle.Params(d=d, p=p, k=k, m=m, L=L, g=g, k0=k0, k1=k1, gqa_max=gqa == "max")
     Un = _np(U)
     for s in (check if check is not None else range(S)):
         st = oracle.OracleStream(prm, _np(K[s, :n]), _np(V[s, :n]), Un, n_cap=max(cap, 1))
@@ -899,3 +899,98 @@ def test_blocked_dot_order_cases(B):
     _, qcode = oracle.query_prep(qq.numpy(), U.numpy())
     assert int(qcode[0]) == 3
     np.testing.assert_array_equal(idx.view("qcode")[0].cpu().numpy(), qcode)
+
+
+
+# ---------------------------------------------------------------- GQA max mode
+
+@pytest.mark.parametrize("case", [
+    dict(S=2, n=5003, g=4, p=16, k=256, m=8, L=4, seed=201),             # 16 walks, 4,096 pooled
+    dict(S=3, n=3001, g=2, p=16, k=128, m=4, L=2, seed=202, inserts=9),  # 4 walks, 512 pooled
+    dict(S=2, n=2600, g=3, p=8, k=64, m=3, L=3, d=64, dtype="f32", seed=203),
+    dict(S=2, n=4000, g=2, p=16, k=128, m=4, L=2, k1=5000, seed=204),     # bounded walks
+    dict(S=1, n=150, g=4, p=16, k=256, m=4, L=2, seed=205),               # fewer tokens than k0
+])
+def test_gqa_max(B, case):
+    """GQA max mode: every head walks every composite with its own query codes,
+    the pooled candidates are ranked by the largest head score; every walk's
+    candidates, the query codes of every head, pages, top-k and attention
+    against the oracle's max reading."""
+    run_case(B, gqa="max", **case)
+
+
+def test_gqa_max_one_head_is_mean(B):
+    """With one head the max mode's pages, top-k and attention equal the mean
+    mode's bit for bit."""
+    S, n, d = 2, 4000, 128
+    dev = torch.device("cuda")
+    K, V, q, _ = _inputs(S, n, d, 1, 20, 206, "bf16")
+    U = W.directions(8, d, 206, "bf16").to(dev)
+    res = []
+    for mode in ("mean", "max"):
+        idx = B.Index(K.to(dev), V.to(dev), U, page_size=16, budget_k=128, m=4, L=2, gqa_group=1,
+                      gqa_mode=mode)
+        pg, npg, tk = idx.query_pages(q.to(dev), with_topk=True)
+        out = idx.sparse_attn(q.to(dev), pg, npg)
+        torch.cuda.synchronize()
+        res.append((pg.cpu(), npg.cpu(), tk.cpu(), out.cpu()))
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
+
+
+def test_gqa_max_decode_step_and_stats(B):
+    """A decode step in the max mode (the first head's pass inserts the token)
+    equals insert + query + attention, and its statistics (visits of all
+    g * L walks, |C|, pages, tokens) equal the oracle's literal walks."""
+    S, n, g, d, p, m, L, k, steps = 2, 3000, 4, 128, 16, 4, 3, 128, 3
+    dev = torch.device("cuda")
+    K, V, _, _ = _inputs(S, n + steps, d, g, 24, 207, "bf16")
+    U = W.directions(m * L, d, 207, "bf16").to(dev)
+    mk = lambda: B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U,
+                         page_size=p, budget_k=k, m=m, L=L, gqa_group=g, capacity=n + steps,
+                         gqa_mode="max")
+    a, b = mk(), mk()
+    gen = torch.Generator().manual_seed(21)
+    stats = B.stats_tensor(S, dev)
+    for t in range(steps):
+        qt = torch.randn(S * g, d, generator=gen).to(torch.bfloat16).to(dev)
+        kn, vn = K[:, n + t].contiguous().to(dev), V[:, n + t].contiguous().to(dev)
+        pa, na, oa, ta = a.decode_step(kn, vn, qt, with_topk=True, stats=stats)
+        b.insert(kn, vn)
+        pb, nb, tb = b.query_pages(qt, with_topk=True)
+        ob = b.sparse_attn(qt, pb, nb)
+        torch.cuda.synchronize()
+        assert torch.equal(pa, pb) and torch.equal(na, nb) and torch.equal(ta, tb)
+        assert torch.equal(oa, ob)
+    recs = B.parse_stats(stats, g * L)
+    prm = oracle.Params(d=d, p=p, k=k, m=m, L=L, g=g, gqa_max=True)
+    for s in range(S):
+        st = oracle.OracleStream(prm, _np(K[s, :n]), _np(V[s, :n]), _np(U), n_cap=n + steps)
+        for t in range(steps):
+            st.insert(_np(K[s, n + t]), _np(V[s, n + t]))
+        q_s = _np(qt[s * g:(s + 1) * g])
+        r = st.query(q_s, literal=True)
+        _check_index(a, st, s, n + steps)
+        _check_query(a, st, s, r, pa, na, ta, oa[s * g:(s + 1) * g], q_s)
+        _check_stats(recs[s], st, r)
+
+
+def test_gqa_max_llama8b_layer_36k(B):
+    """The 36,864-token Llama-3.1-8B layer in the max mode (4 heads x 4
+    composites = 16 walks per KV head): two heads against the oracle."""
+    w = W.WORKLOADS["llama8b_layer_36k"]
+    K, V, q, U, _ = W.layer_inputs(w, layer=5)
+    dev = torch.device("cuda")
+    print("[case] gqa max llama8b_layer_36k", flush=True)
+    idx = B.Index(K.to(dev), V.to(dev), U.to(dev), page_size=w.p, budget_k=w.k, m=w.m, L=w.L,
+                  gqa_group=w.g, capacity=w.n + 8, gqa_mode="max")
+    qd = q.to(dev)
+    page_ids, n_pages, topk = idx.query_pages(qd, with_topk=True)
+    out = idx.sparse_attn(qd, page_ids, n_pages)
+    torch.cuda.synchronize()
+    prm = oracle.Params(d=w.d, p=w.p, k=w.k, m=w.m, L=w.L, g=w.g, gqa_max=True)
+    for s in (2, 6):
+        st = oracle.OracleStream(prm, _np(K[s]), _np(V[s]), _np(U), n_cap=w.n + 8)
+        q_s = _np(q[s * w.g:(s + 1) * w.g])
+        r = st.query(q_s, literal=False)
+        _check_query(idx, st, s, r, page_ids, n_pages, topk, out[s * w.g:(s + 1) * w.g], q_s)
