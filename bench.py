@@ -82,6 +82,9 @@ def algorithmic_bytes(w, kernel: str, visits: float, n_cand: float, attended: fl
         "qcollect": n_cand * d * elem,
         "qfinal": att if fused else 0.0,
         "attn": att,
+        # the offloaded pool's staging copy: K and V rows of every attended token
+        # in (over the host link) and out (to HBM)
+        "fetch": attended * 2 * d * elem * 2,
     }
     per_layer = {"insert": dirs, "qscan": dirs}
     return S * per_stream.get(kernel, 0.0) + per_layer.get(kernel, 0.0)
@@ -154,7 +157,7 @@ def copy_calibration(args):
 # (the library's own timing names both finalisers "qfinal")
 PROFILED = {"qscan": ("k_qscan<",), "qcollect": ("k_qcollect<",),
             "qfinal": ("k_qfinal<", "k_qfinal_big<"), "attn": ("k_attn<",),
-            "amerge": ("k_attn_merge",)}
+            "amerge": ("k_attn_merge",), "fetch": ("k_fetch_pages",)}
 
 
 def _counter_means(directory: str, counter: str) -> dict:
@@ -227,6 +230,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--gqa", choices=("mean", "max"), default="mean",
                     help="GQA query mode: the heads' mean, or per-head walks ranked by the max score")
+    ap.add_argument("--offload", action="store_true",
+                    help="page pool in pinned host memory; the selected pages are staged in HBM")
     ap.add_argument("--pregen", type=int, default=0,
                     help="decode steps run on every layer copy before timing (a long generation)")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -267,7 +272,7 @@ def main():
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         idx = binding.Index(K, V, U, page_size=w.p, budget_k=w.k, m=w.m, L=w.L, gqa_group=w.g,
-                            capacity=cap, gqa_mode=args.gqa)
+                            capacity=cap, gqa_mode=args.gqa, offload=args.offload)
         e1.record()
         torch.cuda.synchronize()
         build_ms.append(e0.elapsed_time(e1))
@@ -416,6 +421,7 @@ def main():
                    "page_size": w.p, "budget_k": w.k, "m": w.m, "L": w.L,
                    "layers_per_step": layers_per_step, "layers_rotated": R,
                    "generated_before_timing": args.pregen, "gqa": args.gqa,
+                   "pool": "host (pinned, staged per step)" if args.offload else "HBM",
                    "step": "ice_decode_step = insert + query_pages + sparse_attn"},
         "build_ms": round(sorted(build_ms)[len(build_ms) // 2], 3),
         "step_alg_bytes": int(step_alg),
@@ -427,6 +433,13 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if args.offload and "fetch" in avg_us:  # what crosses the host link per layer step
+        page_bytes = w.streams * attended * 2 * w.d * (2 if w.dtype == "bf16" else 4)
+        rows = w.streams * n_cand * w.d * (2 if w.dtype == "bf16" else 4)
+        res["offload"] = {"fetch_us": round(avg_us["fetch"], 2), "page_bytes": int(page_bytes),
+                          "fetch_link_gbs": round(page_bytes / (avg_us["fetch"] * 1e-6) / 1e9, 1),
+                          "rerank_row_bytes_over_link": int(rows),
+                          "collect_us": round(avg_us.get("qcollect", 0.0), 2)}
     print(json.dumps(res), flush=True)
 
 

@@ -81,6 +81,8 @@ typedef struct {
   int32_t dtype;      /* ice_dtype of K, V, q and the directions                */
   int32_t gqa_mode;   /* ice_gqa_mode: how the g query heads of a KV head query
                          the index (0 = their mean; 1 = per-head walks, max score) */
+  int32_t offload;    /* 0: the page pool lives in the workspace (HBM); 1: in
+                         caller-owned pinned host memory (ice_build_index_offload) */
 } ice_params;
 
 /* GQA query modes (the query heads sharing a KV head "averaged or maxed"):
@@ -143,6 +145,32 @@ ice_status ice_build_index_noalloc(const ice_params *prm, int32_t n_streams, int
                                    int64_t capacity_tokens, const void *K, const void *V,
                                    const void *dirs, void *workspace, size_t workspace_bytes,
                                    void *stream, ice_index **out);
+
+/* Host-offloaded page pool (IceCache paper page, abstract: most of the KV
+ * cache is offloaded to the CPU; blog page: only the pages selected at a
+ * decode step are brought to the GPU).  With prm->offload = 1 the K and V
+ * pages live in host memory the caller allocated pinned and device-mapped
+ * (hipHostMalloc; the library resolves it with hipHostGetDevicePointer and
+ * never registers memory); the workspace holds the index and a staging area
+ * of P pages per stream instead of the pool.  Per decode step the query's
+ * exact rerank reads its candidates' key rows from host memory, k_fetch_pages
+ * copies the P selected pages (K and V) into the staging area, and the
+ * attention runs on the staging area: results equal the resident pool's bit
+ * for bit.  The build and the inserts write the pool rows to host memory.
+ *   host_pool  pinned host memory, ice_host_pool_bytes of it, 256-byte
+ *              aligned; it must outlive the index.
+ * ice_build_index refuses prm->offload = 1, and this call prm->offload = 0
+ * (ICE_ERR_INVALID_ARG); ICE_ERR_INVALID_ARG also when host_pool is not
+ * device-mapped pinned memory, ICE_ERR_WORKSPACE when it is too small.
+ * The page pool's layout is the resident one (ice_index_layout's pool_k and
+ * pool_v become byte offsets into host_pool). */
+size_t ice_host_pool_bytes(const ice_params *prm, int32_t n_streams, int64_t n_tokens,
+                           int64_t capacity_tokens);
+ice_status ice_build_index_offload(const ice_params *prm, int32_t n_streams, int64_t n_tokens,
+                                   int64_t capacity_tokens, const void *K, const void *V,
+                                   const void *dirs, void *workspace, size_t workspace_bytes,
+                                   void *scratch, size_t scratch_bytes, void *host_pool,
+                                   size_t host_pool_bytes, void *stream, ice_index **out);
 
 /* Dynamic update (IceCache blog page: the tree takes new tokens with no
  * rebuild).  Appends one token to every stream.
@@ -241,7 +269,8 @@ const char *ice_status_string(ice_status s);
  *   cell_count    int32   [S][n_cells]   tokens per cell
  *   pool_k        dtype   [S][Pcap][p][d]  key of each page slot
  *   pool_v        dtype   [S][Pcap][d][p]  values, element-major inside a
- *                 page (value element e of slot j at [e][j])
+ *                 page (value element e of slot j at [e][j]); with offload
+ *                 set, both are offsets into the host pool, not the workspace
  *   qcode         int32   [S][G][mL]     last query's projection codes (G = g
  *                 in the GQA max mode, one set per head; else 1)
  *   cand          int32   [S][Lq][k0]    last query's candidates per walk (Lq =
@@ -250,7 +279,7 @@ const char *ice_status_string(ice_status s);
  *                 fixed order */
 typedef struct {
   int64_t n_streams, n_tokens, n_build, capacity_tokens, page_capacity, n_cells;
-  int32_t tree_depth, mL, k0, elem_bytes, Lq, Gq;
+  int32_t tree_depth, mL, k0, elem_bytes, Lq, Gq, offload;
   int64_t norm_c, codes, list_code, list_id, loc, page_tokens, page_len, page_cell, npages,
       cell_count, pool_k, pool_v, qcode, cand, cand_count;
   int64_t workspace_bytes;
@@ -265,7 +294,8 @@ ice_status ice_index_layout(const ice_index *idx, ice_layout *out);
  * kernel (arrays of ICE_TIMED_KERNELS, in the order of ice_timing_name) and
  * clears the record.  The event records add a little time between kernels;
  * leave timing off for end-to-end latency. */
-#define ICE_TIMED_KERNELS 7 /* insert, qscan, qcollect, qfinal, attn, amerge, visit */
+#define ICE_TIMED_KERNELS 8 /* insert, qscan, qcollect, qfinal, attn, amerge, visit,
+                              fetch (the offloaded pool's page copy) */
 ice_status ice_timing_enable(ice_index *idx, int enable);
 ice_status ice_timing_read(ice_index *idx, double *total_ms, int64_t *launches);
 const char *ice_timing_name(int kernel);

@@ -18,7 +18,7 @@ ICE_OK, ICE_ERR_INVALID_ARG, ICE_ERR_CAPACITY, ICE_ERR_UNSUPPORTED, ICE_ERR_WORK
 NOALLOC_SCRATCH_BYTES = 128 << 20  # ICE_NOALLOC_SCRATCH_BYTES
 ICE_F32, ICE_BF16 = 0, 1
 ICE_GQA_MEAN, ICE_GQA_MAX = 0, 1
-TIMED_KERNELS = 7
+TIMED_KERNELS = 8
 
 
 class IceParams(ctypes.Structure):
@@ -26,12 +26,13 @@ class IceParams(ctypes.Structure):
                 ("budget_k", ctypes.c_int32), ("m", ctypes.c_int32), ("L", ctypes.c_int32),
                 ("gqa_group", ctypes.c_int32), ("k0", ctypes.c_int32), ("k1", ctypes.c_int64),
                 ("tree_depth", ctypes.c_int32), ("c", ctypes.c_float),
-                ("dtype", ctypes.c_int32), ("gqa_mode", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("gqa_mode", ctypes.c_int32),
+                ("offload", ctypes.c_int32)]
 
 
 _LAYOUT_I64_HEAD = ["n_streams", "n_tokens", "n_build", "capacity_tokens", "page_capacity",
                     "n_cells"]
-_LAYOUT_I32 = ["tree_depth", "mL", "k0", "elem_bytes", "Lq", "Gq"]
+_LAYOUT_I32 = ["tree_depth", "mL", "k0", "elem_bytes", "Lq", "Gq", "offload"]
 _LAYOUT_OFFS = ["norm_c", "codes", "list_code", "list_id", "loc", "page_tokens", "page_len",
                 "page_cell", "npages", "cell_count", "pool_k", "pool_v", "qcode", "cand",
                 "cand_count"]
@@ -73,6 +74,12 @@ def lib():
         L.ice_build_index_noalloc.argtypes = [PP, i32, i64, i64, P, P, P, P, ctypes.c_size_t,
                                               P, ctypes.POINTER(P)]
         L.ice_build_index_noalloc.restype = ctypes.c_int
+        L.ice_host_pool_bytes.argtypes = [PP, i32, i64, i64]
+        L.ice_host_pool_bytes.restype = ctypes.c_size_t
+        L.ice_build_index_offload.argtypes = [PP, i32, i64, i64, P, P, P, P, ctypes.c_size_t, P,
+                                              ctypes.c_size_t, P, ctypes.c_size_t, P,
+                                              ctypes.POINTER(P)]
+        L.ice_build_index_offload.restype = ctypes.c_int
         L.ice_insert.argtypes = [P, P, P, P]
         L.ice_insert.restype = ctypes.c_int
         L.ice_query_pages.argtypes = [P, P, P, P, P, P, P]
@@ -99,10 +106,11 @@ def lib():
 
 
 def make_params(d, page_size, budget_k, m, L, gqa_group=1, k0=0, k1=0, tree_depth=0, c=0.0,
-                dtype=torch.bfloat16, gqa_mode="mean") -> IceParams:
+                dtype=torch.bfloat16, gqa_mode="mean", offload=False) -> IceParams:
     dt = {torch.float32: ICE_F32, torch.bfloat16: ICE_BF16}[dtype]
     gm = {"mean": ICE_GQA_MEAN, "max": ICE_GQA_MAX}[gqa_mode]
-    return IceParams(d, page_size, budget_k, m, L, gqa_group, k0, k1, tree_depth, c, dt, gm)
+    return IceParams(d, page_size, budget_k, m, L, gqa_group, k0, k1, tree_depth, c, dt, gm,
+                     1 if offload else 0)
 
 
 STATS_MAX_L = 32
@@ -161,7 +169,9 @@ class Index:
 
     def __init__(self, K, V, dirs, *, page_size, budget_k, m, L, gqa_group=1, k0=0, k1=0,
                  tree_depth=0, c=0.0, capacity=None, stream=None, noalloc=False,
-                 gqa_mode="mean"):
+                 gqa_mode="mean", offload=False):
+        """offload: keep the page pool in a pinned host tensor (self.host_pool)
+        instead of the workspace (ice_build_index_offload)."""
         _dev_tensor(K, "K", ndim=3)
         _dev_tensor(V, "V", K.dtype, 3)
         _dev_tensor(dirs, "dirs", K.dtype, 2)
@@ -173,7 +183,7 @@ class Index:
         self.device = K.device
         self.capacity = int(capacity if capacity is not None else n)
         self.prm = make_params(d, page_size, budget_k, m, L, gqa_group, k0, k1, tree_depth, c,
-                               K.dtype, gqa_mode)
+                               K.dtype, gqa_mode, offload)
         L_ = lib()
         ws = L_.ice_workspace_bytes(ctypes.byref(self.prm), S, n, self.capacity)
         if ws == 0:
@@ -182,7 +192,17 @@ class Index:
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=K.device)
         h = ctypes.c_void_p()
         st = _stream(stream)
-        if noalloc:  # the library's fixed build scratch (ice_build_index_noalloc)
+        self.host_pool = None
+        if offload:  # the page pool in pinned host memory
+            hb = L_.ice_host_pool_bytes(ctypes.byref(self.prm), S, n, self.capacity) or 256
+            self.host_pool = torch.empty(hb, dtype=torch.uint8, pin_memory=True)
+            sb = L_.ice_build_scratch_bytes(ctypes.byref(self.prm), S, n) or 256
+            scratch = torch.empty(sb, dtype=torch.uint8, device=K.device)
+            _check(L_.ice_build_index_offload(ctypes.byref(self.prm), S, n, self.capacity,
+                                              _ptr(K), _ptr(V), _ptr(dirs), _ptr(self.workspace),
+                                              ws, _ptr(scratch), sb, _ptr(self.host_pool), hb, st,
+                                              ctypes.byref(h)), "ice_build_index_offload")
+        elif noalloc:  # the library's fixed build scratch (ice_build_index_noalloc)
             scratch = None
             _check(L_.ice_build_index_noalloc(ctypes.byref(self.prm), S, n, self.capacity,
                                               _ptr(K), _ptr(V), _ptr(dirs), _ptr(self.workspace),
@@ -326,7 +346,10 @@ class Index:
         count = 1
         for s_ in shape:
             count *= s_
-        raw = self.workspace[off:off + count * nbytes]
+        base = self.workspace
+        if name in ("pool_k", "pool_v") and y["offload"]:  # offsets into the host pool
+            base = self.host_pool
+        raw = base[off:off + count * nbytes]
         t = raw.view(dt).view(shape)
         if name == "codes":  # tiles of 64 tokens -> [S][ncap][mL] (a copy)
             t = t.permute(0, 1, 3, 2).reshape(S, -1, mL)[:, :ncap]

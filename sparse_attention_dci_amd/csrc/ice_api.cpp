@@ -94,7 +94,7 @@ struct Layout {
   int64_t dirs, dirs32, norm_c, inv_c, inv_c2, maxnsq, codes, list_code, list_id, loc, page_tokens,
       page_len, page_cell, npages, cell_count, cell_last, pool_k, pool_v, qkv, qcode, mbuf,
       hist, hist2, cand, cand_count, bnd, bnd_rk, bnd_pg, bnd_count, rr_key, rr_id, rr_pg, rr_count,
-      attn_part, vhist, vstate, vtie, vcount, bsel, vlast;
+      attn_part, vhist, vstate, vtie, vcount, bsel, vlast, stage_k, stage_v, stage_len;
   int64_t nvrange;
   int64_t total;
 };
@@ -118,6 +118,7 @@ ice_status check_params(const ice_params *prm, int32_t S, int64_t n, int64_t nca
   if (!(prm->c >= 0.0f) || std::isinf(prm->c)) return ICE_ERR_INVALID_ARG;
   if (prm->dtype != ICE_F32 && prm->dtype != ICE_BF16) return ICE_ERR_INVALID_ARG;
   if (prm->gqa_mode != ICE_GQA_MEAN && prm->gqa_mode != ICE_GQA_MAX) return ICE_ERR_INVALID_ARG;
+  if (prm->offload != 0 && prm->offload != 1) return ICE_ERR_INVALID_ARG;
   if (S < 1 || n < 0 || ncap < n || ncap < 1 || ncap > 0x7fffffffLL - 1)
     return ICE_ERR_INVALID_ARG;
   if (prm->L > 32) return ICE_ERR_UNSUPPORTED;
@@ -172,8 +173,17 @@ ice_status make_layout(const ice_params *prm, int32_t S, int64_t n, int64_t ncap
   y.npages = seg(Sl * 4);
   y.cell_count = seg(Sl * y.ncell * 4);
   y.cell_last = seg(Sl * y.ncell * 4);
-  y.pool_k = seg(Sl * y.pcap * p * d * y.elem);
-  y.pool_v = seg(Sl * y.pcap * p * d * y.elem);
+  if (prm->offload) {  // the pool is in host memory; P staged pages per stream here
+    y.pool_k = y.pool_v = -1;
+    const int64_t P = prm->budget_k / p;
+    y.stage_k = seg(Sl * P * p * d * y.elem);
+    y.stage_v = seg(Sl * P * p * d * y.elem);
+    y.stage_len = seg(Sl * P * 4);
+  } else {
+    y.pool_k = seg(Sl * y.pcap * p * d * y.elem);
+    y.pool_v = seg(Sl * y.pcap * p * d * y.elem);
+    y.stage_k = y.stage_v = y.stage_len = -1;
+  }
   y.qkv = seg(Sl * Gq * d * 4);
   y.qcode = seg(Sl * Gq * mL * 4);
   y.mbuf = seg(Sl * Lb * ncap * 4);
@@ -217,6 +227,13 @@ int64_t scratch_offsets(const ice_params *prm, int32_t S, int64_t n, int64_t off
     o = align_up(o + sz[i]);
   }
   return o;
+}
+
+// The offloaded pool in host memory: pool_k at 0, pool_v at *off_v; returns the total.
+int64_t host_pool_layout(const Layout &y, const ice_params *prm, int32_t S, int64_t *off_v) {
+  const int64_t one = (int64_t)S * y.pcap * prm->page_size * prm->head_dim * y.elem;
+  *off_v = align_up(one);
+  return align_up(*off_v + one);
 }
 
 int64_t scratch_size(const ice_params *prm, int32_t S, int64_t n) {
@@ -271,13 +288,16 @@ size_t ice_build_scratch_bytes(const ice_params *prm, int32_t n_streams, int64_t
   return (size_t)(s > 0 ? s : kAlign);
 }
 
-ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_tokens,
-                           int64_t capacity_tokens, const void *K, const void *V,
-                           const void *dirs, void *workspace, size_t workspace_bytes,
-                           void *build_scratch, size_t scratch_bytes, void *stream,
-                           ice_index **out) {
-  if (!out) return ICE_ERR_INVALID_ARG;
-  *out = nullptr;
+}  // extern "C"
+
+namespace {
+
+// The build behind ice_build_index and ice_build_index_offload; pool_dev is
+// the device address of the host pool (offload), else null.
+ice_status build_common(const ice_params *prm, int32_t n_streams, int64_t n_tokens,
+                        int64_t capacity_tokens, const void *K, const void *V, const void *dirs,
+                        void *workspace, size_t workspace_bytes, void *build_scratch,
+                        size_t scratch_bytes, char *pool_dev, void *stream, ice_index **out) {
   Layout y;
   ice_status st = make_layout(prm, n_streams, n_tokens, capacity_tokens, &y);
   if (st != ICE_OK) return st;
@@ -354,8 +374,19 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
   dv.npages = (int32_t *)(w + y.npages);
   dv.cell_count = (int32_t *)(w + y.cell_count);
   dv.cell_last = (int32_t *)(w + y.cell_last);
-  dv.pool_k = w + y.pool_k;
-  dv.pool_v = w + y.pool_v;
+  dv.offload = prm->offload;
+  if (prm->offload) {
+    int64_t off_v = 0;
+    host_pool_layout(y, prm, n_streams, &off_v);
+    dv.pool_k = pool_dev;
+    dv.pool_v = pool_dev + off_v;
+    dv.stage_k = w + y.stage_k;
+    dv.stage_v = w + y.stage_v;
+    dv.stage_len = (int32_t *)(w + y.stage_len);
+  } else {
+    dv.pool_k = w + y.pool_k;
+    dv.pool_v = w + y.pool_v;
+  }
   dv.qkv = (float *)(w + y.qkv);
   dv.qcode = (int32_t *)(w + y.qcode);
   dv.mbuf = (uint32_t *)(w + y.mbuf);
@@ -404,6 +435,58 @@ ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_t
   }
   *out = idx;
   return ICE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ice_status ice_build_index(const ice_params *prm, int32_t n_streams, int64_t n_tokens,
+                           int64_t capacity_tokens, const void *K, const void *V,
+                           const void *dirs, void *workspace, size_t workspace_bytes,
+                           void *build_scratch, size_t scratch_bytes, void *stream,
+                           ice_index **out) {
+  if (!out) return ICE_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (prm && prm->offload) return ICE_ERR_INVALID_ARG;  // ice_build_index_offload
+  return build_common(prm, n_streams, n_tokens, capacity_tokens, K, V, dirs, workspace,
+                      workspace_bytes, build_scratch, scratch_bytes, nullptr, stream, out);
+}
+
+size_t ice_host_pool_bytes(const ice_params *prm, int32_t n_streams, int64_t n_tokens,
+                           int64_t capacity_tokens) {
+  Layout y;
+  if (!prm || !prm->offload ||
+      make_layout(prm, n_streams, n_tokens, capacity_tokens, &y) != ICE_OK)
+    return 0;
+  int64_t off_v = 0;
+  return (size_t)host_pool_layout(y, prm, n_streams, &off_v);
+}
+
+ice_status ice_build_index_offload(const ice_params *prm, int32_t n_streams, int64_t n_tokens,
+                                   int64_t capacity_tokens, const void *K, const void *V,
+                                   const void *dirs, void *workspace, size_t workspace_bytes,
+                                   void *build_scratch, size_t scratch_bytes, void *host_pool,
+                                   size_t host_pool_bytes, void *stream, ice_index **out) {
+  if (!out) return ICE_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!prm || !prm->offload) return ICE_ERR_INVALID_ARG;  // ice_build_index
+  Layout y;
+  ice_status st = make_layout(prm, n_streams, n_tokens, capacity_tokens, &y);
+  if (st != ICE_OK) return st;
+  int64_t off_v = 0;
+  const int64_t need = host_pool_layout(y, prm, n_streams, &off_v);
+  if (!host_pool || !aligned(host_pool, kAlign) || host_pool_bytes < (size_t)need)
+    return ICE_ERR_WORKSPACE;
+  if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < (size_t)y.total)
+    return ICE_ERR_WORKSPACE;
+  void *dev = nullptr;  // pinned, device-mapped host memory only
+  if (hipHostGetDevicePointer(&dev, host_pool, 0) != hipSuccess || !dev) {
+    (void)hipGetLastError();
+    return ICE_ERR_INVALID_ARG;
+  }
+  return build_common(prm, n_streams, n_tokens, capacity_tokens, K, V, dirs, workspace,
+                      workspace_bytes, build_scratch, scratch_bytes, (char *)dev, stream, out);
 }
 
 ice_status ice_build_index_noalloc(const ice_params *prm, int32_t n_streams, int64_t n_tokens,
@@ -511,8 +594,8 @@ ice_status ice_timing_read(ice_index *idx, double *total_ms, int64_t *launches) 
 }
 
 const char *ice_timing_name(int kernel) {
-  static const char *names[ICE_TIMED_KERNELS] = {"insert", "qscan", "qcollect", "qfinal",
-                                                 "attn",   "amerge", "visit"};
+  static const char *names[ICE_TIMED_KERNELS] = {"insert", "qscan",  "qcollect", "qfinal",
+                                                 "attn",   "amerge", "visit",    "fetch"};
   return (kernel >= 0 && kernel < ICE_TIMED_KERNELS) ? names[kernel] : "";
 }
 
@@ -556,8 +639,16 @@ ice_status ice_index_layout(const ice_index *idx, ice_layout *out) {
   out->page_cell = y.page_cell;
   out->npages = y.npages;
   out->cell_count = y.cell_count;
-  out->pool_k = y.pool_k;
-  out->pool_v = y.pool_v;
+  if (idx->prm.offload) {  // offsets into the host pool
+    int64_t off_v = 0;
+    host_pool_layout(y, &idx->prm, idx->S, &off_v);
+    out->pool_k = 0;
+    out->pool_v = off_v;
+  } else {
+    out->pool_k = y.pool_k;
+    out->pool_v = y.pool_v;
+  }
+  out->offload = idx->prm.offload;
   out->qcode = y.qcode;
   out->cand = y.cand;
   out->cand_count = y.cand_count;

@@ -20,10 +20,14 @@ constexpr int kAttnThreads = kAttnWaves * 64;
 // the stream's selection, one 16-token chunk per wave; its page numbers are
 // staged in LDS first.  With one block per stream the block writes the
 // output, else a partial (max, sum, values) per head for k_attn_merge.
+// With `staged` (a host-offloaded pool) dv describes the staging area, in
+// which the stream's selected pages sit in selection order: page j of the
+// selection is staged page j.
 template <int DT, int D>
 __global__ __launch_bounds__(kAttnThreads) void k_attn(Dev dv, const void *q,
                                                        const int32_t *page_ids,
-                                                       const int32_t *n_pages, float *out) {
+                                                       const int32_t *n_pages, float *out,
+                                                       bool staged) {
   const int s = blockIdx.y, sp = blockIdx.x;
   const int tid = threadIdx.x, w = tid >> 6;
   const int g = dv.g, p = dv.p, P = dv.P;
@@ -33,7 +37,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(Dev dv, const void *q,
   __shared__ float red[kAttnWaves * kMaxGroup * D];
   const int pbase = sp * kAttnTpb / p;  // p divides kAttnTpb
   const int np = min(min(n_pages[s], P) - pbase, kAttnTpb / p);
-  if (tid < kAttnTpb / p) sel[tid] = page_ids[(int64_t)s * P + min(pbase + tid, P - 1)];
+  if (tid < kAttnTpb / p)
+    sel[tid] = staged ? min(pbase + tid, P - 1) : page_ids[(int64_t)s * P + min(pbase + tid, P - 1)];
   u32x4 qh[D / 32], ql[D / 32];
   attn_load_q<DT, D>(dv, s, q, qh, ql);
   AttnWave<D> st;
@@ -120,12 +125,47 @@ __global__ __launch_bounds__(256) void k_attn_merge(Dev dv, float *out) {
   }
 }
 
+// The selected pages of a host-offloaded pool into the staging area: block
+// (j, s) copies page j of stream s's selection (its keys, then its values,
+// each p*d contiguous elements) with 16-byte loads over the host link, and its
+// valid-slot count (0 past the selection or for a page number outside the
+// pool, whose tokens the attention then masks, as it does on the pool).
+__global__ __launch_bounds__(256) void k_fetch_pages(Dev dv, const int32_t *page_ids,
+                                                     const int32_t *n_pages) {
+  const int j = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+  const int64_t P = dv.P;
+  const int np = min(n_pages[s], dv.P);
+  const int32_t pg = page_ids[(int64_t)s * P + j];
+  const bool ok = j < np && pg >= 0 && pg < dv.pcap;
+  if (tid == 0) dv.stage_len[(int64_t)s * P + j] = ok ? dv.page_len[(int64_t)s * dv.pcap + pg] : 0;
+  if (!ok) return;
+  const int64_t chunks = (int64_t)dv.p * dv.d * dv.elem / 16;  // per page, K or V
+  const uint4 *srck = reinterpret_cast<const uint4 *>(dv.pool_k) + ((int64_t)s * dv.pcap + pg) * chunks;
+  const uint4 *srcv = reinterpret_cast<const uint4 *>(dv.pool_v) + ((int64_t)s * dv.pcap + pg) * chunks;
+  uint4 *dk = reinterpret_cast<uint4 *>(dv.stage_k) + ((int64_t)s * P + j) * chunks;
+  uint4 *dvv = reinterpret_cast<uint4 *>(dv.stage_v) + ((int64_t)s * P + j) * chunks;
+  for (int64_t x = tid; x < chunks; x += 256) {
+    const uint4 a = srck[x], b = srcv[x];
+    dk[x] = a;
+    dvv[x] = b;
+  }
+}
+
 template <int DT, int D>
 static hipError_t attn_impl(const Dev &dv, const void *q, const int32_t *page_ids,
                             const int32_t *n_pages, float *out, hipStream_t st, Timer *tm) {
   timer_begin(tm, st);
-  hipLaunchKernelGGL((k_attn<DT, D>), dim3(dv.attn_nsplit, dv.S), dim3(kAttnThreads), 0, st, dv,
-                     q, page_ids, n_pages, out);
+  Dev da = dv;  // the pool the attention reads: the resident one, or the staged pages
+  if (dv.offload) {
+    hipLaunchKernelGGL(k_fetch_pages, dim3(dv.P, dv.S), dim3(256), 0, st, dv, page_ids, n_pages);
+    timer_mark(tm, KID_FETCH, st);
+    da.pool_k = dv.stage_k;
+    da.pool_v = dv.stage_v;
+    da.page_len = dv.stage_len;
+    da.pcap = dv.P;
+  }
+  hipLaunchKernelGGL((k_attn<DT, D>), dim3(dv.attn_nsplit, dv.S), dim3(kAttnThreads), 0, st, da,
+                     q, page_ids, n_pages, out, dv.offload != 0);
   timer_mark(tm, KID_ATTN, st);
   if (dv.attn_nsplit > 1) {
     hipLaunchKernelGGL(k_attn_merge<D>, dim3(dv.S), dim3(256), 0, st, dv, out);

@@ -76,6 +76,12 @@ struct Dev {
   int32_t *cell_last;    // [S][ncell]
   void *pool_k;          // [S][pcap][p][d]  key rows, slot-major
   void *pool_v;          // [S][pcap][d][p]  value columns, element-major within a page
+  // host-offloaded pool (offload = 1: pool_k / pool_v point into pinned host
+  // memory): the selected pages are copied here before the attention
+  int offload;
+  void *stage_k;         // [S][P][p][d]
+  void *stage_v;         // [S][P][d][p]
+  int32_t *stage_len;    // [S][P] valid slots of each staged page (0: none)
 
   // per-query state (walks: Lq per stream)
   float *qkv;            // [S][Gq][d]
@@ -134,7 +140,7 @@ constexpr int kPageChunk = 1024;
 // KID_INSERT is the standalone insert; a decode step's insert and query prep
 // run inside the scan and are timed with it.
 enum KernelId { KID_INSERT = 0, KID_QSCAN, KID_QCOLLECT, KID_QFINAL, KID_ATTN, KID_AMERGE,
-                KID_VISIT, KID_COUNT };
+                KID_VISIT, KID_FETCH, KID_COUNT };
 
 // Optional host-side event timer (owned by an index); null when timing is off.
 struct Timer;

@@ -1794,9 +1794,10 @@ hipError_t launch_decode(const Dev &dv, int64_t n, int64_t k1, const void *k_new
   // fit LDS: the finaliser runs the attention itself, with the standalone
   // kernel's arithmetic (16 waves of one chunk, merged by their maxima).
   // Larger budgets take the standalone kernels, whose per-split partials and
-  // merge fix the summation order, so the step equals the separate calls.
+  // merge fix the summation order, so the step equals the separate calls; so
+  // does a host-offloaded pool (its selected pages are staged first).
   timer_begin(tm, st);
-  const bool fused = dv.attn_nsplit == 1 && dv.Lq * dv.k0 <= kMaxCand;
+  const bool fused = dv.attn_nsplit == 1 && dv.Lq * dv.k0 <= kMaxCand && !dv.offload;
   float *fo = fused ? out : nullptr;
   if (dv.dtype == 0)
     query_tail<0>(dv, n + 1, k1, page_ids, n_pages, topk_ids, q, k_new, v_new, fo, stats, st, tm);

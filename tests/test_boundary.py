@@ -212,3 +212,30 @@ def test_gqa_mode_rules(L):
         st = L.ice_build_index(ctypes.byref(p), 8, 1000, 1000, FAKE, FAKE, FAKE, FAKE, 1 << 40,
                                FAKE, 1 << 40, None, ctypes.byref(h))
         assert st == B.ICE_ERR_UNSUPPORTED and not h.value, kw
+
+
+def test_offload_entry_rules(L):
+    """The offloaded pool: ice_build_index refuses offload = 1 and the offload
+    entry refuses offload = 0; a missing or short host pool is a workspace
+    error, all before any HIP call; the workspace then holds no pool."""
+    h = ctypes.c_void_p()
+    off = good(offload=True)
+    res = good()
+    assert L.ice_host_pool_bytes(ctypes.byref(res), 8, 36864, 36864) == 0
+    hp = L.ice_host_pool_bytes(ctypes.byref(off), 8, 36864, 36864)
+    assert hp >= 2 * 8 * (36864 // 16) * 16 * 128 * 2
+    assert (L.ice_workspace_bytes(ctypes.byref(res), 8, 36864, 36864)
+            - L.ice_workspace_bytes(ctypes.byref(off), 8, 36864, 36864)) > hp // 2
+    st = L.ice_build_index(ctypes.byref(off), 8, 1000, 1000, FAKE, FAKE, FAKE, FAKE, 1 << 40, FAKE,
+                           1 << 40, None, ctypes.byref(h))
+    assert st == B.ICE_ERR_INVALID_ARG and not h.value
+    st = L.ice_build_index_offload(ctypes.byref(res), 8, 1000, 1000, FAKE, FAKE, FAKE, FAKE,
+                                   1 << 40, FAKE, 1 << 40, FAKE, 1 << 40, None, ctypes.byref(h))
+    assert st == B.ICE_ERR_INVALID_ARG and not h.value
+    for pool, nbytes in ((None, 1 << 40), (FAKE, 16)):
+        st = L.ice_build_index_offload(ctypes.byref(off), 8, 1000, 1000, FAKE, FAKE, FAKE, FAKE,
+                                       1 << 40, FAKE, 1 << 40, pool, nbytes, None, ctypes.byref(h))
+        assert st == B.ICE_ERR_WORKSPACE and not h.value
+    bad = good(offload=True)
+    bad.offload = 2
+    assert L.ice_workspace_bytes(ctypes.byref(bad), 8, 1000, 1000) == 0

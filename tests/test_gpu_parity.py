@@ -994,3 +994,67 @@ def test_gqa_max_llama8b_layer_36k(B):
         q_s = _np(q[s * w.g:(s + 1) * w.g])
         r = st.query(q_s, literal=False)
         _check_query(idx, st, s, r, page_ids, n_pages, topk, out[s * w.g:(s + 1) * w.g], q_s)
+
+
+
+# ---------------------------------------------------------------- host-offloaded pool
+
+@pytest.mark.parametrize("case", [
+    dict(S=4, n=6000, g=4, p=16, k=256, m=8, L=4, gqa="mean", dtype="bf16"),
+    dict(S=2, n=9000, g=2, p=16, k=1024, m=4, L=3, gqa="mean", dtype="bf16"),  # four splits
+    dict(S=2, n=5000, g=4, p=16, k=256, m=8, L=4, gqa="max", dtype="bf16"),
+    dict(S=2, n=3000, g=2, p=8, k=128, m=3, L=3, gqa="mean", dtype="f32", d=64),
+])
+def test_offloaded_pool_equals_resident(B, case):
+    """The page pool in pinned host memory: builds, inserts and decode steps
+    write it over the host link, the rerank reads its key rows there, and the
+    selected pages are staged in HBM for the attention.  Every index array,
+    page, top-k and attention output equals the resident pool's bit for bit,
+    step after step; the last step also against the oracle."""
+    c = dict(d=128)
+    c.update(case)
+    S, n, g, d, steps = c["S"], c["n"], c["g"], c["d"], 3
+    dev = torch.device("cuda")
+    K, V, _, _ = _inputs(S, n + steps, d, g, 24, 301, c["dtype"])
+    U = W.directions(c["m"] * c["L"], d, 301, c["dtype"]).to(dev)
+    print(f"[case] offload {case}", flush=True)
+    kw = dict(page_size=c["p"], budget_k=c["k"], m=c["m"], L=c["L"], gqa_group=g,
+              capacity=n + steps + 2, gqa_mode=c["gqa"])
+    a = B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U, offload=True,
+                **kw)
+    b = B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U, **kw)
+    assert a.layout()["offload"] == 1 and b.layout()["offload"] == 0
+    gen = torch.Generator().manual_seed(31)
+    td = W.torch_dtype(c["dtype"])
+    for t in range(steps):
+        qt = torch.randn(S * g, d, generator=gen).to(td).to(dev)
+        kn, vn = K[:, n + t].contiguous().to(dev), V[:, n + t].contiguous().to(dev)
+        pa, na, oa, ta = a.decode_step(kn, vn, qt, with_topk=True)
+        pb, nb, ob, tb = b.decode_step(kn, vn, qt, with_topk=True)
+        torch.cuda.synchronize()
+        assert torch.equal(pa, pb) and torch.equal(na, nb) and torch.equal(ta, tb)
+        assert torch.equal(oa, ob)
+    # the standalone attention over caller page lists, and an insert
+    oa2 = a.sparse_attn(qt, pa, na)
+    ob2 = b.sparse_attn(qt, pb, nb)
+    torch.cuda.synchronize()
+    assert torch.equal(oa2, ob2) and torch.equal(oa2, oa)
+    nt = a.layout()["n_tokens"]
+    npg = int(a.view("npages").max())
+    assert torch.equal(a.view("npages"), b.view("npages"))
+    for name in ("codes", "loc"):
+        assert torch.equal(a.view(name)[:, :nt], b.view(name)[:, :nt]), name
+    for name in ("page_tokens", "page_len"):
+        assert torch.equal(a.view(name)[:, :npg], b.view(name)[:, :npg]), name
+    filled = b.view("page_tokens") >= 0
+    for name in ("pool_k", "pool_v"):
+        assert torch.equal(a.view(name).cpu()[filled.cpu()], b.view(name).cpu()[filled.cpu()]), name
+    prm = oracle.Params(d=d, p=c["p"], k=c["k"], m=c["m"], L=c["L"], g=g,
+                        gqa_max=c["gqa"] == "max")
+    st = oracle.OracleStream(prm, _np(K[0, :n]), _np(V[0, :n]), _np(U), n_cap=n + steps + 2)
+    for t in range(steps):
+        st.insert(_np(K[0, n + t]), _np(V[0, n + t]))
+    q_s = _np(qt[:g])
+    r = st.query(q_s, literal=False)
+    _check_index(a, st, 0, n + steps)
+    _check_query(a, st, 0, r, pa, na, ta, oa[:g], q_s)
