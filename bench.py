@@ -351,6 +351,35 @@ def main():
     log(f"[bench] per stream: sum_l V_l {visits:.0f} of {walks * w.m * ntok:.0f} entries, "
         f"|C| {n_cand:.1f}, attended {attended:.1f}")
 
+    # page fill of the timed layers (fragmentation after a long generation) and,
+    # after one, the list delta-merge of the generated tokens
+    npg = torch.stack([ly.view("npages").cpu() for ly in layers]).float()
+    fills, partial = [], []
+    for ly in layers:
+        nps, pl = ly.view("npages").cpu(), ly.view("page_len").cpu()
+        for st_ in range(w.streams):
+            lens = pl[st_, :int(nps[st_])].float()
+            fills.append(float(lens.mean()))
+            partial.append(float((lens < w.p).sum()))
+    pages = {"tokens_per_stream": layers[0].layout()["n_tokens"],
+             "pages_per_stream": round(float(npg.mean()), 1),
+             "mean_fill": round(sum(fills) / len(fills), 3), "page_size": w.p,
+             "partial_pages_per_stream": round(sum(partial) / len(partial), 1),
+             "cells": layers[0].layout()["n_cells"]}
+    tail = layers[0].layout()["n_tokens"] - layers[0].layout()["n_build"]
+    if args.pregen and tail <= 8192:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nb = binding.lib().ice_merge_scratch_bytes(layers[0]._h)
+        scratch = torch.empty(nb, dtype=torch.uint8, device=dev)
+        e0.record()
+        binding._check(binding.lib().ice_merge_lists(layers[0]._h, binding._ptr(scratch), nb,
+                                                     binding._stream(None)), "ice_merge_lists")
+        e1.record()
+        torch.cuda.synchronize()
+        pages["merge_tail"] = tail
+        pages["merge_ms"] = round(e0.elapsed_time(e1), 3)
+    log(f"[bench] pages: {pages}")
+
     cpu = None
     if not args.no_cpu and args.gqa == "max":
         log("[bench] no oracle baseline for the GQA max mode (the baseline times the mean mode)")
@@ -427,6 +456,7 @@ def main():
         "step_alg_bytes": int(step_alg),
         "step_alg_gbs": round(step_gbs, 1),
         "step_frac": round(step_gbs / PEAK_HBM_GBS, 4),
+        "pages": pages,
         "query_stats": {"visits": round(visits, 1), "union_size": round(n_cand, 1),
                         "attended": round(attended, 1), "tokens": ntok},
         "kernels": kernels,

@@ -201,6 +201,19 @@ typedef struct {
   int32_t n_cand, n_pages, n_tokens, reserved;
 } ice_query_stats;
 
+/* Delta-merge of the per-direction lists (the DCI index; IceCache blog page:
+ * the tree takes new tokens with no rebuild).  Inserts append each list's new
+ * entries after its sorted part in insertion order (see ice_index_layout);
+ * this call folds them in, so that every list [0, n) is sorted by (code,
+ * token) again and n_build becomes n.  Queries do not need it (they read the
+ * projection codes); it keeps the lists a sorted DCI index.
+ *   scratch  device, ice_merge_scratch_bytes(idx) bytes, 256-byte aligned;
+ *            free to reuse once the call's stream work has finished.
+ * Nothing to merge: ICE_OK with nothing enqueued.  More than 8192 entries
+ * inserted since the build or the last merge: ICE_ERR_UNSUPPORTED. */
+size_t ice_merge_scratch_bytes(const ice_index *idx);
+ice_status ice_merge_lists(ice_index *idx, void *scratch, size_t scratch_bytes, void *stream);
+
 /* Query: P-DCI candidates, exact rerank, page selection (IceCache paper page,
  * Figure 2 steps (2)-(3)).
  *   q         device [S*g][d] dtype: query heads, head j uses stream j / g;

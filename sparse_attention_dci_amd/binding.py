@@ -80,6 +80,10 @@ def lib():
                                               ctypes.c_size_t, P, ctypes.c_size_t, P,
                                               ctypes.POINTER(P)]
         L.ice_build_index_offload.restype = ctypes.c_int
+        L.ice_merge_scratch_bytes.argtypes = [P]
+        L.ice_merge_scratch_bytes.restype = ctypes.c_size_t
+        L.ice_merge_lists.argtypes = [P, P, ctypes.c_size_t, P]
+        L.ice_merge_lists.restype = ctypes.c_int
         L.ice_insert.argtypes = [P, P, P, P]
         L.ice_insert.restype = ctypes.c_int
         L.ice_query_pages.argtypes = [P, P, P, P, P, P, P]
@@ -238,6 +242,15 @@ class Index:
         if k_new.shape != (self.S, self.d) or v_new.shape != (self.S, self.d):
             raise ValueError("k_new, v_new must be [S][d]")
         _check(lib().ice_insert(self._h, _ptr(k_new), _ptr(v_new), _stream(stream)), "ice_insert")
+
+    def merge_lists(self, stream=None):
+        """Fold the inserted list entries into the sorted lists (ice_merge_lists);
+        the scratch is freed when the call returns (after a synchronisation)."""
+        nb = lib().ice_merge_scratch_bytes(self._h)
+        scratch = torch.empty(nb, dtype=torch.uint8, device=self.device)
+        _check(lib().ice_merge_lists(self._h, _ptr(scratch), nb, _stream(stream)),
+               "ice_merge_lists")
+        torch.cuda.synchronize(self.device)  # the scratch lives until the merge has run
 
     def query_pages(self, q, with_topk=False, page_ids=None, n_pages=None, topk=None,
                     stats=None, stream=None):

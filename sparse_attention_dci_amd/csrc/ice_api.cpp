@@ -517,6 +517,27 @@ ice_status ice_insert(ice_index *idx, const void *k_new, const void *v_new, void
   return ICE_OK;
 }
 
+size_t ice_merge_scratch_bytes(const ice_index *idx) {
+  if (!idx) return 0;
+  const int64_t b = ice::merge_scratch_bytes(idx->dv, idx->n);
+  return (size_t)(b > 0 ? align_up(b) : kAlign);
+}
+
+ice_status ice_merge_lists(ice_index *idx, void *scratch, size_t scratch_bytes, void *stream) {
+  if (!idx) return ICE_ERR_INVALID_ARG;
+  const int64_t t = idx->n - idx->nbuild;
+  if (t <= 0) return ICE_OK;
+  if (t > ice::kMaxMergeTail) return ICE_ERR_UNSUPPORTED;
+  if (!scratch || !aligned(scratch, kAlign) ||
+      scratch_bytes < (size_t)ice::merge_scratch_bytes(idx->dv, idx->n))
+    return ICE_ERR_WORKSPACE;
+  hipError_t e = ice::launch_merge(idx->dv, idx->nbuild, idx->n, scratch, (hipStream_t)stream);
+  if (e != hipSuccess) return ICE_ERR_HIP;
+  idx->nbuild = idx->n;
+  idx->dv.nbuild = idx->n;
+  return ICE_OK;
+}
+
 ice_status ice_query_pages(ice_index *idx, const void *q, int32_t *page_ids, int32_t *n_pages,
                            int32_t *topk_ids, ice_query_stats *stats, void *stream) {
   if (!idx || !q || !page_ids || !n_pages || !aligned(q, 16) || !aligned(page_ids, 4) ||

@@ -41,6 +41,9 @@ constexpr int kAttnChunk = 16;
 constexpr int kMaxBudget = 65536;
 // Token ranges of the visit-budget passes (one block per range and stream).
 constexpr int kVisitRange = 1024;
+// Largest list tail (entries inserted since the build or the last merge) that
+// ice_merge_lists sorts in one block's LDS.
+constexpr int kMaxMergeTail = 8192;
 
 // Every device array of one index, resolved from the caller's workspace.
 struct Dev {
@@ -161,6 +164,9 @@ hipError_t launch_stats(const Dev &dv, int64_t n, ice_query_stats *stats, const 
                         const int32_t *n_pages, hipStream_t st);
 hipError_t launch_attn(const Dev &dv, const void *q, const int32_t *page_ids,
                        const int32_t *n_pages, float *out, hipStream_t st, Timer *tm);
+// the list merge: scratch bytes for n tokens, and the merge of entries nb .. n-1
+int64_t merge_scratch_bytes(const Dev &dv, int64_t n);
+hipError_t launch_merge(const Dev &dv, int64_t nb, int64_t n, void *scratch, hipStream_t st);
 // n_l of every composite for a walk bounded at k1 visits (1 <= k1 < m * n)
 hipError_t launch_visit_budget(const Dev &dv, int64_t n, uint32_t k1, int head, hipStream_t st);
 // insert of token n, then the query over n + 1 tokens and the attention

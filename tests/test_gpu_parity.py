@@ -494,6 +494,12 @@ def test_long_generation_equals_rebuild(B):
         _check_list_storage(b, 0, b.view("codes")[0].cpu().numpy())
         la, lb = _logical_lists(a, s), _logical_lists(b, 0)
         assert np.array_equal(la[0], lb[0]) and np.array_equal(la[1], lb[1])
+        if s == 0:  # the delta-merge turns the stored lists into the rebuild's, as stored
+            a.merge_lists()
+            assert a.layout()["n_build"] == n
+        if s >= 0 and a.layout()["n_build"] == n:
+            sa, sb = _stored_lists(a, s), _stored_lists(b, 0)
+            assert np.array_equal(sa[0], sb[0]) and np.array_equal(sa[1], sb[1])
         assert torch.equal(a.view("loc")[s, :n], b.view("loc")[0, :n])
         npg = int(a.view("npages")[s])
         assert npg == int(b.view("npages")[0])
@@ -1058,3 +1064,63 @@ def test_offloaded_pool_equals_resident(B, case):
     r = st.query(q_s, literal=False)
     _check_index(a, st, 0, n + steps)
     _check_query(a, st, 0, r, pa, na, ta, oa[:g], q_s)
+
+
+
+# ---------------------------------------------------------------- list delta-merge
+
+def test_merge_lists(B):
+    """ice_merge_lists folds the inserted entries into the sorted lists: the
+    stored lists then equal the oracle's (which inserts in place) with no
+    re-sort, n_build becomes n, and queries are unchanged; a second round of
+    inserts and merge, and a merge with nothing to merge, likewise."""
+    S, n, g, d, p, m, L, k = 2, 3000, 2, 128, 16, 4, 3, 128
+    dev = torch.device("cuda")
+    K, V, q, _ = _inputs(S, n + 120, d, g, 24, 401, "bf16")
+    U = W.directions(m * L, d, 401, "bf16")
+    idx = B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U.to(dev),
+                  page_size=p, budget_k=k, m=m, L=L, gqa_group=g, capacity=n + 120)
+    prm = oracle.Params(d=d, p=p, k=k, m=m, L=L, g=g)
+    sts = [oracle.OracleStream(prm, _np(K[s, :n]), _np(V[s, :n]), _np(U), n_cap=n + 120)
+           for s in range(S)]
+    qd = q.to(dev)
+    nt = n
+    for rnd, cnt in enumerate((77, 43)):
+        for t in range(nt, nt + cnt):
+            idx.insert(K[:, t].contiguous().to(dev), V[:, t].contiguous().to(dev))
+            for s in range(S):
+                sts[s].insert(_np(K[s, t]), _np(V[s, t]))
+        nt += cnt
+        before = idx.query_pages(qd, with_topk=True)
+        torch.cuda.synchronize()
+        assert idx.layout()["n_build"] == nt - cnt
+        idx.merge_lists()
+        assert idx.layout()["n_build"] == nt
+        for s in range(S):
+            lc, li = _stored_lists(idx, s)
+            np.testing.assert_array_equal(lc, sts[s].lcode[:, :nt])
+            np.testing.assert_array_equal(li, sts[s].lid[:, :nt])
+        after = idx.query_pages(qd, with_topk=True)
+        torch.cuda.synchronize()
+        for x, y in zip(before, after):
+            assert torch.equal(x, y)
+    idx.merge_lists()  # nothing to merge
+    assert idx.layout()["n_build"] == nt
+
+
+def test_merge_lists_tail_limit(B):
+    """More than 8,192 entries inserted since the last merge: UNSUPPORTED, and
+    the index is untouched."""
+    S, n, d = 1, 100, 64
+    dev = torch.device("cuda")
+    K, V, _, _ = _inputs(S, n + 8193, d, 1, 8, 402, "bf16")
+    U = W.directions(4, d, 402, "bf16").to(dev)
+    idx = B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U, page_size=16,
+                  budget_k=32, m=2, L=2, capacity=n + 8193)
+    Kd, Vd = K.to(dev), V.to(dev)
+    for t in range(n, n + 8193):
+        idx.insert(Kd[:, t].contiguous(), Vd[:, t].contiguous())
+    with pytest.raises(B.IceError) as e:
+        idx.merge_lists()
+    assert e.value.status == B.ICE_ERR_UNSUPPORTED
+    assert idx.layout()["n_build"] == n
