@@ -234,6 +234,9 @@ def main():
                     help="page pool in pinned host memory; the selected pages are staged in HBM")
     ap.add_argument("--pregen", type=int, default=0,
                     help="decode steps run on every layer copy before timing (a long generation)")
+    ap.add_argument("--reuse", type=int, default=1,
+                    help="query every REUSE decode steps of a layer; the steps between reuse "
+                         "its last page selection (ice_decode_step_reuse)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--write-traffic", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
@@ -249,6 +252,9 @@ def main():
     if args.copy_calibration:
         copy_calibration(args)
         return
+    if args.reuse < 1:
+        print("--reuse must be at least 1", file=sys.stderr)
+        sys.exit(2)
 
     import torch
 
@@ -259,7 +265,8 @@ def main():
     # a decode step of the 32-layer workload runs every layer once
     layers_per_step = w.layers if args.workload == "llama8b_decode_36k" else 1
     R = max(args.layers, layers_per_step)
-    total_calls = (args.warmup + 2 * args.steps) * layers_per_step
+    passes = 2 if args.reuse == 1 else 5  # timed and kernel-timing passes
+    total_calls = (args.warmup + passes * args.steps) * layers_per_step
     per_layer = (total_calls + R - 1) // R + 1
     cap = w.n + per_layer + args.pregen
 
@@ -291,47 +298,73 @@ def main():
         log(f"[bench] {args.pregen} tokens generated on every layer copy")
 
     steps_in = [W.step_inputs(w, layer=t % R, step=t, device=dev) for t in range(4 * R)]
-    outs = [(torch.empty(w.streams, w.k // w.p, dtype=torch.int32, device=dev),
-             torch.empty(w.streams, dtype=torch.int32, device=dev),
+    # no page selected until a layer copy's first query
+    outs = [(torch.zeros(w.streams, w.k // w.p, dtype=torch.int32, device=dev),
+             torch.zeros(w.streams, dtype=torch.int32, device=dev),
              torch.empty(w.streams * w.g, w.d, dtype=torch.float32, device=dev))
             for _ in range(R)]
     call = [0]
+    ncall = [0] * R  # decode steps run on each layer copy
 
-    def step():
+    def step(reuse=args.reuse):
+        """One decode step of every layer of the step.  With reuse r > 1 a layer
+        queries on every r-th of its steps and reuses its last selection on
+        the others (reuse=0: reuse only)."""
         for _ in range(layers_per_step):
             t = call[0]
             call[0] += 1
             r = t % R
             k_new, v_new, q = steps_in[t % len(steps_in)]
             pg, npg, out = outs[r]
-            layers[r].decode_step(k_new, v_new, q, page_ids=pg, n_pages=npg, out=out)
+            if reuse and ncall[r] % reuse == 0:
+                layers[r].decode_step(k_new, v_new, q, page_ids=pg, n_pages=npg, out=out)
+            else:
+                layers[r].decode_step_reuse(k_new, v_new, q, pg, npg, out=out)
+            ncall[r] += 1
+
+    def timed(reuse):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            step(reuse)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
 
     for _ in range(args.warmup):
-        step()
+        step(1)
     torch.cuda.synchronize()
     log("[bench] timing")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+    ms_per_step = timed(args.reuse)
+    reuse_res = None
+    if args.reuse > 1:  # the two kinds of step the schedule mixes, timed alone
+        q_ms, r_ms = timed(1), timed(0)
+        reuse_res = {"r": args.reuse, "query_step_us": round(q_ms * 1e3, 2),
+                     "reuse_step_us": round(r_ms * 1e3, 2)}
+        log(f"[bench] reuse {reuse_res}")
 
     # per-kernel durations: HIP events the library records on the launch stream
-    for idx in layers:
-        idx.timing(True)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    per_kernel = {}
-    for idx in layers:
-        for name, (ms, cnt) in idx.timing_read().items():
-            a, b = per_kernel.get(name, (0.0, 0))
-            per_kernel[name] = (a + ms, b + cnt)
-        idx.timing(False)
-    avg_us = {k: 1e3 * ms / c for k, (ms, c) in per_kernel.items() if c}
+    def kernel_times(reuse):
+        for idx in layers:
+            idx.timing(True)
+        for _ in range(args.steps):
+            step(reuse)
+        torch.cuda.synchronize()
+        tot = {}
+        for idx in layers:
+            for name, (ms, cnt) in idx.timing_read().items():
+                a, b = tot.get(name, (0.0, 0))
+                tot[name] = (a + ms, b + cnt)
+            idx.timing(False)
+        return tot, {k: 1e3 * ms / c for k, (ms, c) in tot.items() if c}
+
+    # the kernel table is that of the query steps (every step queries)
+    per_kernel, avg_us = kernel_times(1)
     log(f"[bench] per-kernel average us: { {k: round(v, 2) for k, v in avg_us.items()} }")
+    if reuse_res is not None:
+        _, r_us = kernel_times(0)
+        reuse_res["reuse_step_kernels_us"] = {k: round(v, 3) for k, v in r_us.items()}
 
     # the work each stream's query did: the query statistics of one more decode
     # step on every layer copy (after everything timed)
@@ -451,7 +484,12 @@ def main():
                    "layers_per_step": layers_per_step, "layers_rotated": R,
                    "generated_before_timing": args.pregen, "gqa": args.gqa,
                    "pool": "host (pinned, staged per step)" if args.offload else "HBM",
-                   "step": "ice_decode_step = insert + query_pages + sparse_attn"},
+                   "reuse": args.reuse,
+                   "step": "ice_decode_step = insert + query_pages + sparse_attn"
+                           + ("" if args.reuse == 1 else
+                              f"; every {args.reuse}th step of a layer, the others "
+                              "ice_decode_step_reuse = insert + sparse_attn over the "
+                              "layer's last selection")},
         "build_ms": round(sorted(build_ms)[len(build_ms) // 2], 3),
         "step_alg_bytes": int(step_alg),
         "step_alg_gbs": round(step_gbs, 1),
@@ -463,6 +501,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if reuse_res is not None:
+        res["reuse"] = reuse_res
     if args.offload and "fetch" in avg_us:  # what crosses the host link per layer step
         page_bytes = w.streams * attended * 2 * w.d * (2 if w.dtype == "bf16" else 4)
         rows = w.streams * n_cand * w.d * (2 if w.dtype == "bf16" else 4)

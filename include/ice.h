@@ -260,6 +260,20 @@ ice_status ice_decode_step(ice_index *idx, const void *k_new, const void *v_new,
                            int32_t *page_ids, int32_t *n_pages, int32_t *topk_ids, float *out,
                            ice_query_stats *stats, void *stream);
 
+/* A decode step that reuses an earlier page selection (the pages name an
+ * "IceCache (reuse)" variant, paper page Table 5 and the blog's comparison,
+ * without its mechanism; reading: the selection of a query step is reused by
+ * the following decode steps, and the caller re-runs the query every r steps,
+ * which saves the P-DCI query the blog puts at about half of a decode step).
+ * The new token is inserted as by ice_insert, then every head attends over
+ * the pages in page_ids / n_pages (as written by an earlier query, or any
+ * valid page numbers), as by ice_sparse_attn: the new token takes part only
+ * when its page is among them.  Same arguments, alignment and errors as
+ * ice_decode_step; page_ids and n_pages are read, not written. */
+ice_status ice_decode_step_reuse(ice_index *idx, const void *k_new, const void *v_new,
+                                 const void *q, const int32_t *page_ids, const int32_t *n_pages,
+                                 float *out, void *stream);
+
 /* Frees the handle (not the workspace). NULL is allowed. */
 void ice_destroy_index(ice_index *idx);
 

@@ -395,6 +395,13 @@ class OracleStream:
         return dict(qkv=qkv, qcode=qcode, S=S, visits=visits, C=C, ranked=ranked,
                     scores=scores, topk=topk, page_ids=page_ids)
 
+    def decode_reuse(self, k, v, q, page_ids):
+        """READING of the pages' "IceCache (reuse)" variant (named with its
+        accuracy only): a decode step that reuses an earlier step's page
+        selection inserts its token, then attends over those pages."""
+        self.insert(k, v)
+        return self.attend(q, page_ids)
+
     def attend(self, q, page_ids):
         pk, pv = self.pool()
         return attention(q, pk, pv, self.prm.p, page_ids, self.page_len)

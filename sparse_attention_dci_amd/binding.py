@@ -92,6 +92,8 @@ def lib():
         L.ice_sparse_attn.restype = ctypes.c_int
         L.ice_decode_step.argtypes = [P, P, P, P, P, P, P, P, P, P]
         L.ice_decode_step.restype = ctypes.c_int
+        L.ice_decode_step_reuse.argtypes = [P, P, P, P, P, P, P, P]
+        L.ice_decode_step_reuse.restype = ctypes.c_int
         L.ice_destroy_index.argtypes = [P]
         L.ice_destroy_index.restype = None
         L.ice_status_string.argtypes = [ctypes.c_int]
@@ -311,6 +313,24 @@ class Index:
                                      _ptr(n_pages), _ptr(topk) if with_topk else None, _ptr(out),
                                      _ptr(stats), _stream(stream)), "ice_decode_step")
         return page_ids, n_pages, out, (topk if with_topk else None)
+
+    def decode_step_reuse(self, k_new, v_new, q, page_ids, n_pages, out=None, stream=None):
+        """insert(k_new, v_new); sparse_attn(q, page_ids, n_pages): a step that
+        reuses an earlier selection (ice_decode_step_reuse)."""
+        for t, nm in ((k_new, "k_new"), (v_new, "v_new"), (q, "q")):
+            _dev_tensor(t, nm, self.dtype, 2)
+        _dev_tensor(page_ids, "page_ids", torch.int32, 2)
+        _dev_tensor(n_pages, "n_pages", torch.int32, 1)
+        if k_new.shape != (self.S, self.d) or v_new.shape != (self.S, self.d):
+            raise ValueError("k_new, v_new must be [S][d]")
+        if q.shape != (self.S * self.g, self.d):
+            raise ValueError("q must be [S*g][d]")
+        out = out if out is not None else torch.empty(self.S * self.g, self.d,
+                                                      dtype=torch.float32, device=self.device)
+        _check(lib().ice_decode_step_reuse(self._h, _ptr(k_new), _ptr(v_new), _ptr(q),
+                                           _ptr(page_ids), _ptr(n_pages), _ptr(out),
+                                           _stream(stream)), "ice_decode_step_reuse")
+        return out
 
     # ------------------------------------------------------------ timing
     def timing(self, enable: bool):

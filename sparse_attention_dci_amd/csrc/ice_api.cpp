@@ -574,6 +574,22 @@ ice_status ice_decode_step(ice_index *idx, const void *k_new, const void *v_new,
   return ICE_OK;
 }
 
+ice_status ice_decode_step_reuse(ice_index *idx, const void *k_new, const void *v_new,
+                                 const void *q, const int32_t *page_ids, const int32_t *n_pages,
+                                 float *out, void *stream) {
+  if (!idx || !k_new || !v_new || !q || !page_ids || !n_pages || !out || !aligned(k_new, 4) ||
+      !aligned(v_new, 4) || !aligned(q, 16) || !aligned(page_ids, 4) || !aligned(n_pages, 4) ||
+      !aligned(out, 4))
+    return ICE_ERR_INVALID_ARG;
+  if (idx->n >= idx->ncap) return ICE_ERR_CAPACITY;
+  hipError_t e = ice::launch_insert(idx->dv, idx->n, k_new, v_new, (hipStream_t)stream,
+                                    idx->timer);
+  if (e != hipSuccess) return ICE_ERR_HIP;
+  idx->n += 1;
+  e = ice::launch_attn(idx->dv, q, page_ids, n_pages, out, (hipStream_t)stream, idx->timer);
+  return e == hipSuccess ? ICE_OK : ICE_ERR_HIP;
+}
+
 void ice_destroy_index(ice_index *idx) {
   if (!idx) return;
   if (idx->timer) {

@@ -141,6 +141,8 @@ def test_null_handles(L):
     assert L.ice_sparse_attn(None, FAKE, FAKE, FAKE, FAKE, None) == B.ICE_ERR_INVALID_ARG
     assert L.ice_decode_step(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
                              None) == B.ICE_ERR_INVALID_ARG
+    assert L.ice_decode_step_reuse(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None) == B.ICE_ERR_INVALID_ARG
     y = B.IceLayout()
     assert L.ice_index_layout(None, ctypes.byref(y)) == B.ICE_ERR_INVALID_ARG
     L.ice_destroy_index(None)

@@ -1124,3 +1124,53 @@ def test_merge_lists_tail_limit(B):
         idx.merge_lists()
     assert e.value.status == B.ICE_ERR_UNSUPPORTED
     assert idx.layout()["n_build"] == n
+
+
+
+# ---------------------------------------------------------------- reuse steps
+
+@pytest.mark.parametrize("r", [1, 3])
+def test_reuse_schedule(B, r):
+    """A decode loop that queries every r steps and reuses the last selection in
+    between (ice_decode_step_reuse): every step's attention equals the oracle
+    attending over the same pages after the same inserts, reuse steps equal
+    ice_insert + ice_sparse_attn bit for bit, and the index after the loop
+    equals the oracle's."""
+    S, n, g, d, p, m, L, k, steps = 2, 3000, 4, 128, 16, 4, 3, 128, 7
+    dev = torch.device("cuda")
+    K, V, _, _ = _inputs(S, n + steps, d, g, 24, 501, "bf16")
+    U = W.directions(m * L, d, 501, "bf16").to(dev)
+    mk = lambda: B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U,
+                         page_size=p, budget_k=k, m=m, L=L, gqa_group=g, capacity=n + steps)
+    a, b = mk(), mk()
+    prm = oracle.Params(d=d, p=p, k=k, m=m, L=L, g=g)
+    sts = [oracle.OracleStream(prm, _np(K[s, :n]), _np(V[s, :n]), _np(U), n_cap=n + steps)
+           for s in range(S)]
+    gen = torch.Generator().manual_seed(41)
+    pg = npg = None
+    for t in range(steps):
+        qt = torch.randn(S * g, d, generator=gen).to(torch.bfloat16).to(dev)
+        kn, vn = K[:, n + t].contiguous().to(dev), V[:, n + t].contiguous().to(dev)
+        if t % r == 0:
+            pg, npg, out, _ = a.decode_step(kn, vn, qt)
+            b.decode_step(kn, vn, qt)
+            torch.cuda.synchronize()
+            for s in range(S):
+                sts[s].insert(_np(K[s, n + t]), _np(V[s, n + t]))
+                r_o = sts[s].query(_np(qt[s * g:(s + 1) * g]))
+                np.testing.assert_array_equal(pg[s, :int(npg[s])].cpu().numpy(), r_o["page_ids"],
+                                              err_msg=f"pages, stream {s} step {t}")
+        else:
+            out = a.decode_step_reuse(kn, vn, qt, pg, npg)
+            b.insert(kn, vn)
+            ob = b.sparse_attn(qt, pg, npg)
+            torch.cuda.synchronize()
+            assert torch.equal(out, ob)
+            for s in range(S):
+                sts[s].insert(_np(K[s, n + t]), _np(V[s, n + t]))
+        for s in range(S):
+            ref = sts[s].attend(_np(qt[s * g:(s + 1) * g]), pg[s, :int(npg[s])].cpu().numpy())
+            err = float(np.max(np.abs(out[s * g:(s + 1) * g].cpu().numpy() - ref)))
+            assert err <= ATTN_TOL, (t, s, err)
+    for s in range(S):
+        _check_index(a, sts[s], s, n + steps)

@@ -513,3 +513,32 @@ def test_gqa_max_walks_are_per_head(ora):
             assert np.array_equal(r["S"][h * 2 + l], one["S"][l])
             union |= set(one["S"][l].tolist())
     assert sorted(union) == list(r["C"])
+
+
+
+# ------------------------------------------------------------------ reuse reading
+
+def test_reuse_step_attends_the_reused_pages_and_the_new_token(ora):
+    """A reuse step inserts its token and attends over the reused pages: equal
+    to softmax attention (numpy, fp64) over exactly the tokens those pages
+    hold, which includes the new token when it joined one of them."""
+    K, V, q = _mixture(500, 64, 6, 81, g=2)
+    U = _rand_dirs(np.random.default_rng(16), 6, 64)
+    prm = ora.Params(d=64, p=8, k=32, m=3, L=2, g=2)
+    st = ora.OracleStream(prm, K[:499], V[:499], U, n_cap=500)
+    r = st.query(q)
+    pages = r["page_ids"]
+    # make the new token a copy of a selected page's first token, so it joins
+    # that token's cell; its page is selected if the cell's last page is
+    cell_last = {}
+    for pg in range(st.npages):
+        cell_last[int(st.page_cell[pg])] = pg
+    out = st.decode_reuse(K[st.page_tokens[pages[0], 0]], V[499], q, pages)
+    toks = [int(t) for pg in pages for t in st.page_tokens[pg][:st.page_len[pg]]]
+    joined = int(st.page_of[499]) in set(int(x) for x in pages)
+    assert (499 in toks) == joined
+    Kt, Vt = st.K[toks].astype(np.float64), st.V[toks].astype(np.float64)
+    for h in range(2):
+        z = Kt @ q[h].astype(np.float64) / np.sqrt(64)
+        w = np.exp(z - z.max())
+        assert np.allclose(out[h], (w / w.sum()) @ Vt, rtol=0, atol=1e-12)
