@@ -123,6 +123,17 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return (uint32_t)x;
 }
 
+// Sum over each row of 16 lanes, held by the row's lane 15 (the first four
+// steps of wave_incl_scan).
+__device__ __forceinline__ uint32_t row_sum16(uint32_t v) {
+  int x = (int)v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  return (uint32_t)x;
+}
+
 // Smallest / largest 64-bit value over the 64 lanes (whole wave), by the
 // same DPP sequence as wave_incl_scan on both halves (lane 63 ends with the
 // result), broadcast.  Lanes without a DPP source take the identity.
@@ -153,30 +164,32 @@ __device__ __forceinline__ unsigned long long wave_minmax_u64(unsigned long long
 
 // One whole wave: smallest bin b of a kHistBins histogram whose inclusive
 // prefix reaches `target` (1 <= target <= total) and the count below b.  The
-// histogram is read by wave_hist_load (lane j holds bins 32j .. 32j+31) so
-// that several can be in flight before any is searched.
+// histogram is read by wave_hist_load in chunks of 256 bins, one contiguous
+// 16-byte read per lane and chunk (lane j holds bins 256c + 4j .. 256c + 4j
+// + 3 of chunk c in v[4c .. 4c + 3]), so that several can be in flight
+// before any is searched, and a wave's read of a chunk is one contiguous
+// kilobyte (no LDS bank conflicts, whole lines from memory).
 constexpr int kBinsPerLane = kHistBins / 64;
+constexpr int kHistChunks = kHistBins / 256;
 
 __device__ __forceinline__ void wave_hist_load(const uint32_t *h, uint32_t (&v)[kBinsPerLane]) {
-  const uint4 *h4 = reinterpret_cast<const uint4 *>(h + __lane_id() * kBinsPerLane);
+  const uint4 *h4 = reinterpret_cast<const uint4 *>(h) + __lane_id();
 #pragma unroll
-  for (int k = 0; k < kBinsPerLane / 4; ++k) {
-    const uint4 x = h4[k];
-    v[4 * k] = x.x;
-    v[4 * k + 1] = x.y;
-    v[4 * k + 2] = x.z;
-    v[4 * k + 3] = x.w;
+  for (int c = 0; c < kHistChunks; ++c) {
+    const uint4 x = h4[64 * c];
+    v[4 * c] = x.x;
+    v[4 * c + 1] = x.y;
+    v[4 * c + 2] = x.z;
+    v[4 * c + 3] = x.w;
   }
 }
 
-__device__ void wave_find_bin_regs(const uint32_t (&v)[kBinsPerLane], uint32_t target,
-                                   uint32_t &bin, uint32_t &below) {
-  constexpr int per = kBinsPerLane;
+// The bin within a 256-bin chunk (lane j holds c[0..3] = bins 4j .. 4j+3)
+// whose inclusive prefix reaches target, given the lane's inclusive prefix
+// incl of the chunk and its sum (the chunk's total reaches target).
+__device__ __forceinline__ void chunk_find(const uint32_t (&c)[4], uint32_t incl, uint32_t sum,
+                                           uint32_t target, uint32_t &bin, uint32_t &below) {
   const int lane = __lane_id();
-  uint32_t sum = 0;
-#pragma unroll
-  for (int k = 0; k < per; ++k) sum += v[k];
-  const uint32_t incl = wave_incl_scan(sum);
   const uint32_t excl = incl - sum;
   const bool mine = excl < target && incl >= target;
   const unsigned long long bal = __ballot(mine);
@@ -185,16 +198,72 @@ __device__ void wave_find_bin_regs(const uint32_t (&v)[kBinsPerLane], uint32_t t
   if (mine) {
     uint32_t run = excl;
 #pragma unroll
-    for (int k = 0; k < per; ++k) {
-      if (run < target && run + v[k] >= target) {
-        b = lane * per + k;
+    for (int k = 0; k < 4; ++k) {
+      if (run < target && run + c[k] >= target) {
+        b = 4 * lane + k;
         bl = run;
       }
-      run += v[k];
+      run += c[k];
     }
   }
   bin = (uint32_t)__builtin_amdgcn_readlane((int)b, src);  // src is wave-uniform
   below = (uint32_t)__builtin_amdgcn_readlane((int)bl, src);
+}
+
+__device__ void wave_find_bin_regs(const uint32_t (&v)[kBinsPerLane], uint32_t target,
+                                   uint32_t &bin, uint32_t &below) {
+  uint32_t sum[kHistChunks], incl[kHistChunks], tot[kHistChunks];
+#pragma unroll
+  for (int c = 0; c < kHistChunks; ++c) {  // independent scans, all in flight
+    sum[c] = v[4 * c] + v[4 * c + 1] + v[4 * c + 2] + v[4 * c + 3];
+    incl[c] = wave_incl_scan(sum[c]);
+    tot[c] = (uint32_t)__builtin_amdgcn_readlane((int)incl[c], 63);
+  }
+  uint32_t base = 0;  // the count below the chunk that holds the target (uniform)
+  int cs = kHistChunks - 1;
+#pragma unroll
+  for (int c = 0; c < kHistChunks - 1; ++c) {
+    if (cs == kHistChunks - 1 && base + tot[c] >= target) cs = c;
+    if (cs == kHistChunks - 1) base += tot[c];
+  }
+  uint32_t cv[4] = {0u, 0u, 0u, 0u}, ci = 0, csum = 0;
+#pragma unroll
+  for (int c = 0; c < kHistChunks; ++c)
+    if (c == cs) {
+      cv[0] = v[4 * c];
+      cv[1] = v[4 * c + 1];
+      cv[2] = v[4 * c + 2];
+      cv[3] = v[4 * c + 3];
+      ci = incl[c];
+      csum = sum[c];
+    }
+  uint32_t b, bl;
+  chunk_find(cv, ci, csum, target - base, b, bl);
+  bin = 256u * (uint32_t)cs + b;
+  below = base + bl;
+}
+
+// The low kLowBins bins of a histogram (its first chunk), four per lane.
+constexpr int kLowBins = 256;
+static_assert(kLowBins == 4 * 64 && kLowBins <= kHistBins, "four low bins per lane");
+
+__device__ __forceinline__ uint4 wave_hist_load_low(const uint32_t *h) {
+  return reinterpret_cast<const uint4 *>(h)[__lane_id()];
+}
+
+// wave_find_bin_regs over the low bins only: found (wave-uniform) when their
+// total reaches `target`, and then bin and below are those of the whole
+// histogram (the smallest bin whose inclusive prefix reaches the target is
+// among them).
+__device__ __forceinline__ bool wave_find_bin_low(uint4 v, uint32_t target, uint32_t &bin,
+                                                  uint32_t &below) {
+  const uint32_t sum = v.x + v.y + v.z + v.w;
+  const uint32_t incl = wave_incl_scan(sum);
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  if (total < target) return false;
+  const uint32_t c[4] = {v.x, v.y, v.z, v.w};
+  chunk_find(c, incl, sum, target, bin, below);
+  return true;
 }
 
 __device__ __forceinline__ void wave_find_bin(const uint32_t *h, uint32_t target, uint32_t &bin,

@@ -37,6 +37,7 @@ constexpr int kFinalThreads = 1024;
 constexpr int kHashSlots = 8192;    // 2 * kMaxCand
 constexpr int kBndLds = 2048;       // boundary entries ranked in LDS
 constexpr int kBuckets = 2048;
+static_assert(kBuckets == kHistBins, "bucket counts are searched as a histogram");
 constexpr int kFusedMaxPages = 1024;
 constexpr int kMaxTies = 256;  // page budgets up to this take the fused attention
 
@@ -480,18 +481,25 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
   const int64_t ii[2] = {i0 + tid, i0 + kScanThreads + tid};
   const bool vv[2] = {ii[0] < i1, ii[1] < i1};
 
-  // 1. loads: M of both tokens for the first 8 composites, their page slots,
-  // the query, the threshold bins (unconditional loads at clamped addresses)
+  // 1. loads: the low bins of wave w's threshold histogram first (distances
+  // are far below the code range, so the threshold bin is almost always among
+  // them; the whole histogram is read when it is not), M of both tokens for
+  // the first 8 composites, their page slots, the query (unconditional loads
+  // at clamped addresses)
+  uint4 hlow = make_uint4(0u, 0u, 0u, 0u);
+  uint32_t klw = k0e;
+  if (w < L) {
+    hlow = wave_hist_load_low(dv.hist + ((int64_t)s * Lq + lo + w) * kHistBins);
+    if (bounded) klw = min(k0e, dv.vcount[s * Lq + lo + w]);
+  }
   uint32_t Mv[2][8];
   int32_t lc[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int64_t ic = vv[u] ? ii[u] : 0;
 #pragma unroll
-    for (int l = 0; l < 8; ++l) {
-      const int lcl = l < L ? l : 0;
-      Mv[u][l] = dv.mbuf[((int64_t)s * L + lcl) * dv.ncap + ic];
-    }
+    for (int l = 0; l < 8; ++l)
+      Mv[u][l] = l < L ? dv.mbuf[((int64_t)s * L + l) * dv.ncap + ic] : 0u;
     lc[u] = dv.loc[(int64_t)s * dv.ncap + ic];
   }
   auto Mof = [&](int u, int l) -> uint32_t {
@@ -513,9 +521,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
     qk[u] = dv.gmax ? load_elem<DT>(q, (int64_t)s * dv.g * dv.d + x) : dv.qkv[(int64_t)s * dv.d + x];
   }
   for (int l = w; l < L; l += kScanThreads / 64) {
-    const uint32_t kl = bounded ? min(k0e, dv.vcount[s * Lq + lo + l]) : k0e;
+    const uint32_t *hl = dv.hist + ((int64_t)s * Lq + lo + l) * kHistBins;
+    uint32_t kl = klw;
+    if (l != w) {  // more composites than waves
+      kl = bounded ? min(k0e, dv.vcount[s * Lq + lo + l]) : k0e;
+      hlow = wave_hist_load_low(hl);
+    }
     uint32_t bb = 0, bl = 0;
-    if (kl > 0) wave_find_bin(dv.hist + ((int64_t)s * Lq + lo + l) * kHistBins, kl, bb, bl);
+    if (kl > 0 && !wave_find_bin_low(hlow, kl, bb, bl)) wave_find_bin(hl, kl, bb, bl);
     if (lane == 0) {
       bstar[l] = kl > 0 ? (int32_t)bb : -1;
       if (rng == 0) {  // for the finaliser: b* and the count below it
@@ -748,7 +761,7 @@ struct FinalShared {
   };
   union {
     uint32_t hash[kHashSlots];  // rerank-list membership (selection phase)
-    struct {
+    struct __attribute__((aligned(16))) {
       uint32_t bcnt[kBuckets];
       uint32_t bstart[kBuckets];
       uint32_t seen[2048];  // selected pages (page walk)
@@ -805,6 +818,24 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
     cc_ld = dv.cand_count[s * L + tid];
     nb_ld = dv.bnd_count[s * L + tid];
   }
+  // the rerank list and this thread's boundary entry: their addresses depend
+  // on nothing loaded (clamped into the arrays; the counts decide later which
+  // values are used), so they are in flight with the histogram, and stay in
+  // flight across the barriers up to the attention (which order LDS only)
+  constexpr int kPer = PER;
+  int32_t pid[kPer], ppg[kPer];
+  unsigned long long pkey[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const uint32_t x = tid + kFinalThreads * j;
+    const int64_t o = (int64_t)s * L * k0 + min(x, (uint32_t)(L * k0 - 1));
+    pid[j] = dv.rr_id[o];
+    pkey[j] = dv.rr_key[o];
+    ppg[j] = dv.rr_pg[o];
+  }
+  const int64_t po = ((int64_t)s * L + lp) * dv.ncap + min((int64_t)ep, dv.ncap - 1);
+  const unsigned long long pbk = dv.bnd[po], pbrk = dv.bnd_rk[po];
+  const int32_t pbpg = dv.bnd_pg[po];
   // union membership: a bitmap over the tokens when they fit the table (one
   // atomic test-and-set per token), else the LDS hash
   const bool bitmap = n <= (int64_t)32 * kHashSlots;
@@ -845,25 +876,8 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
       }
     }
   }
-  // the rerank list and this thread's boundary entry, requested before the
-  // first barrier (the barriers up to the attention order LDS only, so these
-  // and the query loads stay in flight across them)
-  constexpr int kPer = PER;
   const uint32_t nrr = k0e > 0 ? nrr_ld : 0u;
-  int32_t pid[kPer], ppg[kPer];
-  unsigned long long pkey[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const uint32_t x = tid + kFinalThreads * j;
-    const int64_t o = (int64_t)s * L * k0 + min(x, (uint32_t)(L * k0 - 1));
-    pid[j] = dv.rr_id[o];
-    pkey[j] = dv.rr_key[o];
-    ppg[j] = dv.rr_pg[o];
-  }
   const bool pv = tid < L * per && ep < nbp && k0e > 0;
-  const int64_t po = ((int64_t)s * L + lp) * dv.ncap + (pv ? ep : 0u);
-  const unsigned long long pbk = dv.bnd[po], pbrk = dv.bnd_rk[po];
-  const int32_t pbpg = dv.bnd_pg[po];
   if (w == 0) {  // the composites' boundary offsets: a prefix of the counts (lanes < L hold them)
     const uint32_t v = k0e > 0 ? nb_ld : 0u;
     const uint32_t incl = wave_incl_scan(v);

@@ -91,9 +91,9 @@ __global__ __launch_bounds__(64) void k_visit_pick(Dev dv, uint32_t k1, int head
   wave_hist_load(g, v);
   uint32_t bin, below;
   wave_find_bin_regs(v, target, bin, below);
-  uint4 *g4 = reinterpret_cast<uint4 *>(g + lane * kBinsPerLane);  // the bins this lane read
+  uint4 *g4 = reinterpret_cast<uint4 *>(g) + lane;  // the bins this lane read
 #pragma unroll
-  for (int k = 0; k < kBinsPerLane / 4; ++k) g4[k] = make_uint4(0u, 0u, 0u, 0u);
+  for (int c = 0; c < kHistChunks; ++c) g4[64 * c] = make_uint4(0u, 0u, 0u, 0u);
   if (lane == 0) {
     st[0] = LEVEL == 0 ? bin
                        : (LEVEL == 1 ? ((pre << kHistBits) | bin)

@@ -206,6 +206,37 @@ def test_identical_keys(B):
     run_case(B, S=S, n=n, d=d, g=g, p=16, k=64, m=4, L=2, keys=(K, V, q), seed=10)
 
 
+def test_query_along_a_direction(B):
+    """The query is the first direction itself: every key's distance on that
+    composite is near the top of the code range, so its threshold bin lies
+    far above the usual low bins (the collect reads its whole histogram); the
+    other composites stay in the low bins."""
+    S, n, d, g, m, L, seed = 2, 3000, 128, 2, 4, 3, 21
+    K, V, _, _ = _inputs(S, n, d, g, 16, seed, "bf16")
+    U = W.directions(m * L, d, seed, "bf16")
+    q = U[0, :d].float().repeat(S * g, 1).to(torch.bfloat16)
+    run_case(B, S=S, n=n, d=d, g=g, p=16, k=128, m=m, L=L, keys=(K, V, q), seed=seed)
+
+
+def test_many_equal_top_scores(B):
+    """128 copies of one key of four times the usual norm, and the query is
+    that key: the copies lead the ranking with equal scores (token order)
+    across about 5 pages.  Pages and top-k against the oracle; the page walk
+    with and without the top-k asked gives the same pages."""
+    S, n, d, g = 2, 3000, 128, 1
+    K, V, _, _ = _inputs(S, n, d, g, 16, 23, "bf16")
+    K[:, 1000:1128] = (K[:, 1000:1001].float() * 4).to(torch.bfloat16)
+    q = K[:, 1000].clone()
+    for with_topk in (True, False):
+        idx = run_case(B, S=S, n=n, d=d, g=g, p=16, k=256, m=4, L=2, keys=(K, V, q), seed=23)
+        if not with_topk:  # the page walk alone (no top-k asked): same pages
+            qd = q.to(torch.device("cuda"))
+            pg, npg, _ = idx.query_pages(qd, with_topk=True)
+            pg2, npg2, _ = idx.query_pages(qd)
+            torch.cuda.synchronize()
+            assert torch.equal(pg, pg2) and torch.equal(npg, npg2)
+
+
 def test_single_head_4k_workload(B):
     w = W.WORKLOADS["single_head_4k_f32"]
     K, V, q, U, _ = W.layer_inputs(w)
