@@ -181,6 +181,32 @@ def _counter_means(directory: str, counter: str) -> dict:
     return {k: a / c for k, (a, c) in sums.items()}
 
 
+def counter_summary(directory: str) -> dict:
+    """Every counter of every library kernel under `directory` (rocprofv3
+    counter_collection.csv files): the mean over dispatches of the sum of a
+    dispatch's rows, per kernel (its name without the namespace and template
+    arguments) and counter."""
+    import csv
+    import re
+    acc = {}
+    for root, _, files in os.walk(directory):
+        for f in files:
+            if not f.endswith("counter_collection.csv"):
+                continue
+            with open(os.path.join(root, f), newline="") as fh:
+                for row in csv.DictReader(fh):
+                    m = re.search(r"ice::(\w+)", row["Kernel_Name"])
+                    if not m:
+                        continue
+                    d = acc.setdefault((m.group(1), row["Counter_Name"]), {})
+                    k = row["Dispatch_Id"]
+                    d[k] = d.get(k, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for (kern, ctr), d in sorted(acc.items()):
+        out.setdefault(kern, {"dispatches": len(d)})[ctr] = sum(d.values()) / len(d)
+    return out
+
+
 def write_traffic(args):
     """HBM bytes per launch of each decode kernel: FETCH_SIZE and WRITE_SIZE
     (KiB per dispatch), each scaled so that a plain device copy of known size
@@ -238,11 +264,17 @@ def main():
                     help="query every REUSE decode steps of a layer; the steps between reuse "
                          "its last page selection (ice_decode_step_reuse)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--counter-summary", metavar="DIR",
+                    help="print per-kernel means of every counter under a rocprofv3 --pmc "
+                         "output directory (csv) and exit")
     ap.add_argument("--write-traffic", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
     args = ap.parse_args()
     if args.write_traffic:
         write_traffic(args)
+        return
+    if args.counter_summary:
+        print(json.dumps(counter_summary(args.counter_summary), indent=1), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

@@ -190,7 +190,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_
   const int mL = dv.mL, m = dv.m, L = dv.L, d = dv.d, g = dv.g;
   const int64_t r = blockIdx.x / S;
   const int64_t nold = k_new != nullptr ? n - 1 : n;  // tokens already in the index
-  const bool ins = k_new != nullptr && r == nold / kScanTpb;  // this block inserts token nold
+  // this block inserts token nold (no short circuit: no branch before the
+  // kernel arguments are all requested)
+  const bool ins = (k_new != nullptr) & (r == nold / kScanTpb);
   // directions: element e < d of direction t at dl[((e / 16) * W + t) * 16 + e % 16]
   // (each lane of a query lane group reads its 16 elements as four 16-byte
   // runs), u_t[d] at ud[t]
@@ -475,7 +477,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
   __shared__ int32_t lcs[kCollectRowBytes / 128];
   __shared__ __attribute__((aligned(16))) uint32_t rows[kCollectRowBytes / 4];
   const uint32_t k0e = (uint32_t)min((int64_t)dv.k0, n);
-  if (k0e == 0) return;
   const int64_t i0 = rng * kScanTpb;
   const int64_t i1 = min(i0 + kScanTpb, n);
   const int64_t ii[2] = {i0 + tid, i0 + kScanThreads + tid};
@@ -520,6 +521,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
     const int x = min(tid + kScanThreads * u, nq * dv.d - 1);
     qk[u] = dv.gmax ? load_elem<DT>(q, (int64_t)s * dv.g * dv.d + x) : dv.qkv[(int64_t)s * dv.d + x];
   }
+  if (k0e == 0) return;  // after the loads: the kernel arguments arrive in one round
   for (int l = w; l < L; l += kScanThreads / 64) {
     const uint32_t *hl = dv.hist + ((int64_t)s * Lq + lo + l) * kHistBins;
     uint32_t kl = klw;
