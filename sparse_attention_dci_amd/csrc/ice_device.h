@@ -266,6 +266,28 @@ __device__ __forceinline__ bool wave_find_bin_low(uint4 v, uint32_t target, uint
   return true;
 }
 
+// wave_find_bin one chunk at a time (four registers per lane instead of 32;
+// a chunk is read only when the ones below it do not reach the target).
+__device__ __forceinline__ void wave_find_bin_seq(const uint32_t *h, uint32_t target,
+                                                  uint32_t &bin, uint32_t &below) {
+  uint32_t base = 0;
+  for (int c = 0; c < kHistChunks; ++c) {
+    const uint4 v = reinterpret_cast<const uint4 *>(h)[64 * c + __lane_id()];
+    const uint32_t sum = v.x + v.y + v.z + v.w;
+    const uint32_t incl = wave_incl_scan(sum);
+    const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    if (base + tot >= target || c == kHistChunks - 1) {
+      const uint32_t cv[4] = {v.x, v.y, v.z, v.w};
+      uint32_t b, bl;
+      chunk_find(cv, incl, sum, target - base, b, bl);
+      bin = 256u * (uint32_t)c + b;
+      below = base + bl;
+      return;
+    }
+    base += tot;
+  }
+}
+
 __device__ __forceinline__ void wave_find_bin(const uint32_t *h, uint32_t target, uint32_t &bin,
                                               uint32_t &below) {
   uint32_t v[kBinsPerLane];

@@ -90,43 +90,37 @@ __device__ void block_score(const Dev &dv, int s, uint32_t cnt, SlotOf slot_of, 
       const uint32_t r = x >> lnb;
       const int j = x & (nbk - 1);
       const char *rp = rb + r * rstride + j * 16 * dv.elem;
-      float kv[16];
-      if constexpr (DT == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint4 u = reinterpret_cast<const uint4 *>(rp)[i];
-          kv[4 * i] = __uint_as_float(u.x);
-          kv[4 * i + 1] = __uint_as_float(u.y);
-          kv[4 * i + 2] = __uint_as_float(u.z);
-          kv[4 * i + 3] = __uint_as_float(u.w);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const uint4 u = reinterpret_cast<const uint4 *>(rp)[i];
-          const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            kv[8 * i + 2 * k] = __uint_as_float(wd[k] << 16);
-            kv[8 * i + 2 * k + 1] = __uint_as_float(wd[k] & 0xffff0000u);
-          }
-        }
-      }
       double best = 0.0;
       for (int h = 0; h < nq; ++h) {
+        // element order within the block of 16, four (fp32) or eight (bf16)
+        // key elements and their query elements at a time (few live registers)
         const float4 *qp = reinterpret_cast<const float4 *>(qkv + 128 * h + 16 * j);
-        float qv[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4 f = qp[i];
-          qv[4 * i] = f.x;
-          qv[4 * i + 1] = f.y;
-          qv[4 * i + 2] = f.z;
-          qv[4 * i + 3] = f.w;
-        }
         double z = 0.0;
+        if constexpr (DT == 0) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) z = fma((double)qv[i], (double)kv[i], z);
+          for (int i = 0; i < 4; ++i) {
+            const uint4 u = reinterpret_cast<const uint4 *>(rp)[i];
+            const float4 f = qp[i];
+            z = fma((double)f.x, (double)__uint_as_float(u.x), z);
+            z = fma((double)f.y, (double)__uint_as_float(u.y), z);
+            z = fma((double)f.z, (double)__uint_as_float(u.z), z);
+            z = fma((double)f.w, (double)__uint_as_float(u.w), z);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const uint4 u = reinterpret_cast<const uint4 *>(rp)[i];
+            const float4 f0 = qp[2 * i], f1 = qp[2 * i + 1];
+            z = fma((double)f0.x, (double)__uint_as_float(u.x << 16), z);
+            z = fma((double)f0.y, (double)__uint_as_float(u.x & 0xffff0000u), z);
+            z = fma((double)f0.z, (double)__uint_as_float(u.y << 16), z);
+            z = fma((double)f0.w, (double)__uint_as_float(u.y & 0xffff0000u), z);
+            z = fma((double)f1.x, (double)__uint_as_float(u.z << 16), z);
+            z = fma((double)f1.y, (double)__uint_as_float(u.z & 0xffff0000u), z);
+            z = fma((double)f1.z, (double)__uint_as_float(u.w << 16), z);
+            z = fma((double)f1.w, (double)__uint_as_float(u.w & 0xffff0000u), z);
+          }
+        }
         z = tree_sum(z, nbk);
         best = h == 0 ? z : fmax(best, z);
       }
@@ -530,7 +524,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
       hlow = wave_hist_load_low(hl);
     }
     uint32_t bb = 0, bl = 0;
-    if (kl > 0 && !wave_find_bin_low(hlow, kl, bb, bl)) wave_find_bin(hl, kl, bb, bl);
+    if (kl > 0 && !wave_find_bin_low(hlow, kl, bb, bl)) wave_find_bin_seq(hl, kl, bb, bl);
     if (lane == 0) {
       bstar[l] = kl > 0 ? (int32_t)bb : -1;
       if (rng == 0) {  // for the finaliser: b* and the count below it
@@ -628,7 +622,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     if (slot[u] < 0) continue;
-    const int32_t i = (int32_t)ii[u];
+    const int64_t iu = i0 + tid + (int64_t)kScanThreads * u;  // ii[u], recomputed
+    const int32_t i = (int32_t)iu;
     const unsigned long long rk = skb[slot[u]];
     const int32_t pg = spb[slot[u]];
     if (below[u]) {
@@ -642,7 +637,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
         dv.cand[((int64_t)s * Lq + lo + l) * dv.k0 + cbase[l] + atomicAdd(&ccount[l], 1u)] = i;
       if ((bnd[u] >> l) & 1u) {
         const int64_t o = ((int64_t)s * Lq + lo + l) * dv.ncap + bbase[l] + atomicAdd(&bcount[l], 1u);
-        dv.bnd[o] = ((unsigned long long)Mof(u, l) << 32) | (uint32_t)i;
+        // the 512-thread shape (80 registers) reads M again (L2-hot) rather
+        // than keep its registers over the scoring, which would spill them
+        uint32_t Mx;
+        if constexpr (NT == 512)
+          Mx = dv.mbuf[((int64_t)s * L + l) * dv.ncap + iu];
+        else
+          Mx = Mof(u, l);
+        dv.bnd[o] = ((unsigned long long)Mx << 32) | (uint32_t)i;
         dv.bnd_rk[o] = rk;
         dv.bnd_pg[o] = pg;
       }
