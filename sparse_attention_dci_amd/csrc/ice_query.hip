@@ -1193,7 +1193,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
   lds_barrier();
   const int np = sh.nsel;
   for (int T0 = w * kAttnChunk; T0 < np * dv.p; T0 += NW * kAttnChunk)
-    attn_chunk<DT, D, false, kAttnChunk / 16>(dv, s, T0, sh.sel, np, qh, ql, st);
+    attn_chunk<DT, D, DT == 0, kAttnChunk / 16>(dv, s, T0, sh.sel, np, qh, ql, st);
   float *red = reinterpret_cast<float *>(&sh.skey[0]);
   attn_publish(st, w, NW, dv.g, sh.wm, sh.wl, red);
   lds_barrier();
