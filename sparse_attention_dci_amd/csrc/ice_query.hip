@@ -463,7 +463,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
   __shared__ int32_t bstar[32];  // -1: the composite takes no candidates
   __shared__ uint32_t ccount[32], bcount[32], cbase[32], bbase[32];
   __shared__ uint32_t nc, nrl, rbase;
-  __shared__ __attribute__((aligned(16))) float qkv[kMaxGroup * 128];  // [nq][128]
+  // [nq][128] query vectors: dynamic LDS sized at launch (nq * 512 bytes), so
+  // the mean mode does not reserve the max mode's 8 KB
+  extern __shared__ __attribute__((aligned(16))) float qkv[];
+  // the 512-thread shape keeps a token's classification in LDS over the
+  // scoring (its 80 registers would spill it to scratch memory)
+  constexpr int kKeep = NT == 512 ? 2 * NT : 1;
+  __shared__ uint32_t kbelow[kKeep], kbnd[kKeep];
+  __shared__ int16_t kslot[kKeep];
   __shared__ int32_t cid[kScanTpb];      // candidate or boundary tokens, as offsets in the block
   __shared__ int32_t lloc[kScanTpb];     // page slots of the block's tokens
   __shared__ unsigned long long skb[kScanTpb];
@@ -599,12 +606,28 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
   unsigned long long *skbp = skb;
   int32_t *spbp = spb;
   const int32_t *cidp = cid, *llocp = lloc;
+  if constexpr (NT == 512) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      kbelow[tid + NT * u] = below[u];
+      kbnd[tid + NT * u] = bnd[u];
+      kslot[tid + NT * u] = (int16_t)slot[u];
+    }
+  }
   block_score<DT, kScanThreads, kCollectRowBytes>(
       dv, s, nc, [cidp, llocp](uint32_t j) { return llocp[cidp[j]]; }, qkv, nq, lcs, rows,
       [skbp, spbp, lp](uint32_t x, int32_t slotx, double sc) {
         skbp[x] = score_rank_key(sc);
         spbp[x] = slotx >> lp;
       });
+  if constexpr (NT == 512) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      below[u] = kbelow[tid + NT * u];
+      bnd[u] = kbnd[tid + NT * u];
+      slot[u] = kslot[tid + NT * u];
+    }
+  }
 
   // 5. the appends
   if (tid < L) {
@@ -1736,8 +1759,9 @@ static void scan_collect(const Dev &dv, int64_t n, bool bounded, uint32_t k1, co
       timer_mark(tm, KID_VISIT, st);
     }
     if (n > 0) {
-      hipLaunchKernelGGL((k_qcollect<DT, NT>), dim3(grid), dim3(NT), 0, st, dv, n, bounded, head,
-                         q);
+      const size_t qbytes = (size_t)(dv.gmax ? dv.g : 1) * 128 * sizeof(float);
+      hipLaunchKernelGGL((k_qcollect<DT, NT>), dim3(grid), dim3(NT), qbytes, st, dv, n, bounded,
+                         head, q);
       timer_mark(tm, KID_QCOLLECT, st);
     }
   }
