@@ -269,7 +269,11 @@ ice_status ice_decode_step(ice_index *idx, const void *k_new, const void *v_new,
  * the pages in page_ids / n_pages (as written by an earlier query, or any
  * valid page numbers), as by ice_sparse_attn: the new token takes part only
  * when its page is among them.  Same arguments, alignment and errors as
- * ice_decode_step; page_ids and n_pages are read, not written. */
+ * ice_decode_step; page_ids and n_pages are read, not written.  With a budget
+ * of one attention block (k <= 256) and the pool in HBM this is one kernel:
+ * the index ends as ice_insert leaves it, and the attention equals ice_insert
+ * + ice_sparse_attn up to the fp32 rounding of the new token's logit (summed
+ * in element order, then joined to the pages' softmax). */
 ice_status ice_decode_step_reuse(ice_index *idx, const void *k_new, const void *v_new,
                                  const void *q, const int32_t *page_ids, const int32_t *n_pages,
                                  float *out, void *stream);
@@ -321,8 +325,9 @@ ice_status ice_index_layout(const ice_index *idx, ice_layout *out);
  * kernel (arrays of ICE_TIMED_KERNELS, in the order of ice_timing_name) and
  * clears the record.  The event records add a little time between kernels;
  * leave timing off for end-to-end latency. */
-#define ICE_TIMED_KERNELS 8 /* insert, qscan, qcollect, qfinal, attn, amerge, visit,
-                              fetch (the offloaded pool's page copy) */
+#define ICE_TIMED_KERNELS 9 /* insert, qscan, qcollect, qfinal, attn, amerge, visit,
+                              fetch (the offloaded pool's page copy), reuse (the
+                              one-kernel ice_decode_step_reuse) */
 ice_status ice_timing_enable(ice_index *idx, int enable);
 ice_status ice_timing_read(ice_index *idx, double *total_ms, int64_t *launches);
 const char *ice_timing_name(int kernel);

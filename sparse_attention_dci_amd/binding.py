@@ -18,7 +18,7 @@ ICE_OK, ICE_ERR_INVALID_ARG, ICE_ERR_CAPACITY, ICE_ERR_UNSUPPORTED, ICE_ERR_WORK
 NOALLOC_SCRATCH_BYTES = 128 << 20  # ICE_NOALLOC_SCRATCH_BYTES
 ICE_F32, ICE_BF16 = 0, 1
 ICE_GQA_MEAN, ICE_GQA_MAX = 0, 1
-TIMED_KERNELS = 8
+TIMED_KERNELS = 9
 
 
 class IceParams(ctypes.Structure):

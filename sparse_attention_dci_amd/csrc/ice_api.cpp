@@ -582,6 +582,13 @@ ice_status ice_decode_step_reuse(ice_index *idx, const void *k_new, const void *
       !aligned(out, 4))
     return ICE_ERR_INVALID_ARG;
   if (idx->n >= idx->ncap) return ICE_ERR_CAPACITY;
+  if (idx->dv.attn_nsplit == 1 && !idx->dv.offload) {  // one kernel
+    const hipError_t e = ice::launch_reuse(idx->dv, idx->n, k_new, v_new, q, page_ids, n_pages,
+                                           out, (hipStream_t)stream, idx->timer);
+    if (e != hipSuccess) return ICE_ERR_HIP;
+    idx->n += 1;
+    return ICE_OK;
+  }
   hipError_t e = ice::launch_insert(idx->dv, idx->n, k_new, v_new, (hipStream_t)stream,
                                     idx->timer);
   if (e != hipSuccess) return ICE_ERR_HIP;
@@ -631,8 +638,8 @@ ice_status ice_timing_read(ice_index *idx, double *total_ms, int64_t *launches) 
 }
 
 const char *ice_timing_name(int kernel) {
-  static const char *names[ICE_TIMED_KERNELS] = {"insert", "qscan",  "qcollect", "qfinal",
-                                                 "attn",   "amerge", "visit",    "fetch"};
+  static const char *names[ICE_TIMED_KERNELS] = {"insert", "qscan",  "qcollect", "qfinal", "attn",
+                                                 "amerge", "visit",  "fetch",    "reuse"};
   return (kernel >= 0 && kernel < ICE_TIMED_KERNELS) ? names[kernel] : "";
 }
 

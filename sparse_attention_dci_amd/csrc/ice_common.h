@@ -143,7 +143,7 @@ constexpr int kPageChunk = 1024;
 // KID_INSERT is the standalone insert; a decode step's insert and query prep
 // run inside the scan and are timed with it.
 enum KernelId { KID_INSERT = 0, KID_QSCAN, KID_QCOLLECT, KID_QFINAL, KID_ATTN, KID_AMERGE,
-                KID_VISIT, KID_FETCH, KID_COUNT };
+                KID_VISIT, KID_FETCH, KID_REUSE, KID_COUNT };
 
 // Optional host-side event timer (owned by an index); null when timing is off.
 struct Timer;
@@ -162,6 +162,9 @@ hipError_t launch_query(const Dev &dv, int64_t n, int64_t k1, const void *q, int
 // the visit counts and attended tokens of the query just enqueued (stats non-null)
 hipError_t launch_stats(const Dev &dv, int64_t n, ice_query_stats *stats, const int32_t *page_ids,
                         const int32_t *n_pages, hipStream_t st);
+hipError_t launch_reuse(const Dev &dv, int64_t n, const void *k_new, const void *v_new,
+                        const void *q, const int32_t *page_ids, const int32_t *n_pages,
+                        float *out, hipStream_t st, Timer *tm);
 hipError_t launch_attn(const Dev &dv, const void *q, const int32_t *page_ids,
                        const int32_t *n_pages, float *out, hipStream_t st, Timer *tm);
 // the list merge: scratch bytes for n tokens, and the merge of entries nb .. n-1

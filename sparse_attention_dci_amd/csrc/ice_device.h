@@ -123,17 +123,6 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return (uint32_t)x;
 }
 
-// Sum over each row of 16 lanes, held by the row's lane 15 (the first four
-// steps of wave_incl_scan).
-__device__ __forceinline__ uint32_t row_sum16(uint32_t v) {
-  int x = (int)v;
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
-  return (uint32_t)x;
-}
-
 // Smallest / largest 64-bit value over the 64 lanes (whole wave), by the
 // same DPP sequence as wave_incl_scan on both halves (lane 63 ends with the
 // result), broadcast.  Lanes without a DPP source take the identity.

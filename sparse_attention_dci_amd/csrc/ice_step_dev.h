@@ -114,27 +114,42 @@ __device__ __forceinline__ void insert_code_store(const Dev &dv, int s, int64_t 
   dv.list_id[((int64_t)s * dv.mL + t) * dv.ncap + n] = (int32_t)n;
 }
 
-// The page rule for token n in cell c (one thread).  np0 is npages[s] as
-// loaded before.  Returns the token's slot in the pool (page * p + slot).
-__device__ __forceinline__ int32_t insert_page_rule(const Dev &dv, int s, int64_t n, uint32_t c,
-                                                    int32_t np0) {
-  const int p = dv.p;
+// The page rule for token n in cell c, split in two so that a caller can
+// decide first and write later (one thread).  np0 is npages[s] as loaded
+// before.  The token's slot in the pool is pid * p + slot.
+struct PagePick {
+  int32_t cntc, pid, slot;
+};
+
+__device__ __forceinline__ PagePick insert_page_decide(const Dev &dv, int s, uint32_t c,
+                                                       int32_t np0) {
   const int64_t ci = (int64_t)s * dv.ncell + c;
   const int32_t cntc = dv.cell_count[ci], last = dv.cell_last[ci];  // loaded together
-  const int32_t slot = cntc & (p - 1);
-  int32_t pid = last;
-  if (slot == 0) {
-    pid = np0;
-    dv.npages[s] = np0 + 1;
-    dv.cell_last[ci] = pid;
-    dv.page_cell[(int64_t)s * dv.pcap + pid] = (int32_t)c;
+  const int32_t slot = cntc & (dv.p - 1);
+  return PagePick{cntc, slot == 0 ? np0 : last, slot};
+}
+
+__device__ __forceinline__ void insert_page_commit(const Dev &dv, int s, int64_t n, uint32_t c,
+                                                   PagePick pk) {
+  const int p = dv.p;
+  const int64_t ci = (int64_t)s * dv.ncell + c;
+  if (pk.slot == 0) {
+    dv.npages[s] = pk.pid + 1;
+    dv.cell_last[ci] = pk.pid;
+    dv.page_cell[(int64_t)s * dv.pcap + pk.pid] = (int32_t)c;
   }
-  dv.cell_count[ci] = cntc + 1;
-  dv.page_tokens[((int64_t)s * dv.pcap + pid) * p + slot] = (int32_t)n;
-  dv.page_len[(int64_t)s * dv.pcap + pid] = slot + 1;
-  const int32_t lc = pid * p + slot;
-  dv.loc[(int64_t)s * dv.ncap + n] = lc;
-  return lc;
+  dv.cell_count[ci] = pk.cntc + 1;
+  dv.page_tokens[((int64_t)s * dv.pcap + pk.pid) * p + pk.slot] = (int32_t)n;
+  dv.page_len[(int64_t)s * dv.pcap + pk.pid] = pk.slot + 1;
+  dv.loc[(int64_t)s * dv.ncap + n] = pk.pid * p + pk.slot;
+}
+
+// Both at once; returns the token's slot in the pool (page * p + slot).
+__device__ __forceinline__ int32_t insert_page_rule(const Dev &dv, int s, int64_t n, uint32_t c,
+                                                    int32_t np0) {
+  const PagePick pk = insert_page_decide(dv, s, c, np0);
+  insert_page_commit(dv, s, n, c, pk);
+  return pk.pid * dv.p + pk.slot;
 }
 
 // Element e of the new token's key row (at its slot) and value column

@@ -1165,8 +1165,8 @@ def test_reuse_schedule(B, r):
     """A decode loop that queries every r steps and reuses the last selection in
     between (ice_decode_step_reuse): every step's attention equals the oracle
     attending over the same pages after the same inserts, reuse steps equal
-    ice_insert + ice_sparse_attn bit for bit, and the index after the loop
-    equals the oracle's."""
+    ice_insert + ice_sparse_attn up to the fp32 rounding of the new token's
+    logit (one kernel), and the index after the loop equals the oracle's."""
     S, n, g, d, p, m, L, k, steps = 2, 3000, 4, 128, 16, 4, 3, 128, 7
     dev = torch.device("cuda")
     K, V, _, _ = _inputs(S, n + steps, d, g, 24, 501, "bf16")
@@ -1196,12 +1196,81 @@ def test_reuse_schedule(B, r):
             b.insert(kn, vn)
             ob = b.sparse_attn(qt, pg, npg)
             torch.cuda.synchronize()
-            assert torch.equal(out, ob)
+            # one kernel: equal up to the fp32 rounding of the new token's logit
+            assert float((out - ob).abs().max()) <= 1e-5
             for s in range(S):
                 sts[s].insert(_np(K[s, n + t]), _np(V[s, n + t]))
         for s in range(S):
             ref = sts[s].attend(_np(qt[s * g:(s + 1) * g]), pg[s, :int(npg[s])].cpu().numpy())
             err = float(np.max(np.abs(out[s * g:(s + 1) * g].cpu().numpy() - ref)))
             assert err <= ATTN_TOL, (t, s, err)
+    for s in range(S):
+        _check_index(a, sts[s], s, n + steps)
+
+
+@pytest.mark.parametrize("dtype,d,p", [("bf16", 128, 8), ("f32", 64, 16)])
+def test_reuse_step_one_kernel(B, dtype, d, p):
+    """The one-kernel reuse step (a budget of one attention block, pool in
+    HBM) against ice_insert + ice_sparse_attn on a twin index, over 24 steps
+    whose page lists hold the new token's own page (found on the twin), twice
+    on some steps, and a fresh page on the steps where the token opens one:
+    the index arrays equal the twin's bit for bit; the attention equals the
+    twin's up to the fp32 rounding of the new token's logit (1e-5), and the
+    oracle's within the attention tolerance."""
+    S, n, g, m, L, k, steps = 2, 2000, 2, 4, 2, 8 * p, 24
+    dev = torch.device("cuda")
+    K, V, _, _ = _inputs(S, n + steps, d, g, 16, 601, dtype)
+    U = W.directions(m * L, d, 601, dtype).to(dev)
+    mk = lambda: B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U,
+                         page_size=p, budget_k=k, m=m, L=L, gqa_group=g, capacity=n + steps)
+    a, b = mk(), mk()
+    assert a.layout()["n_tokens"] == n
+    prm = oracle.Params(d=d, p=p, k=k, m=m, L=L, g=g)
+    sts = [oracle.OracleStream(prm, _np(K[s, :n]), _np(V[s, :n]), _np(U), n_cap=n + steps)
+           for s in range(S)]
+    gen = torch.Generator().manual_seed(43)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q0 = torch.randn(S * g, d, generator=gen).to(tdt).to(dev)
+    pg, npg, _ = a.query_pages(q0)
+    torch.cuda.synchronize()
+    P = k // p
+    fresh = 0
+    for t in range(steps):
+        qt = torch.randn(S * g, d, generator=gen).to(tdt).to(dev)
+        kn, vn = K[:, n + t].contiguous().to(dev), V[:, n + t].contiguous().to(dev)
+        b.insert(kn, vn)
+        torch.cuda.synchronize()
+        loc = b.view("loc")[:, n + t].cpu()
+        newpg = (loc // p).to(torch.int32)
+        fresh += int(((loc % p) == 0).sum())
+        pl = pg.clone().cpu()
+        for s in range(S):  # the token's page first; twice on odd steps
+            pl[s, 0] = newpg[s]
+            if t % 2:
+                pl[s, P - 1] = newpg[s]
+        pl = pl.to(dev)
+        npl = torch.full((S,), P, dtype=torch.int32, device=dev)
+        out = a.decode_step_reuse(kn, vn, qt, pl, npl)
+        ob = b.sparse_attn(qt, pl, npl)
+        torch.cuda.synchronize()
+        err_twin = float((out - ob).abs().max())
+        assert err_twin <= 1e-5, (t, err_twin)
+        for s in range(S):
+            sts[s].insert(_np(K[s, n + t]), _np(V[s, n + t]))
+            ref = sts[s].attend(_np(qt[s * g:(s + 1) * g]), pl[s].cpu().numpy())
+            err = float(np.max(np.abs(out[s * g:(s + 1) * g].cpu().numpy() - ref)))
+            assert err <= ATTN_TOL, (t, s, err)
+    assert fresh > 0  # some step opened a page that its list held
+    for name in ("codes", "list_code", "list_id", "loc", "page_tokens", "page_len", "page_cell",
+                 "npages", "cell_count"):
+        assert torch.equal(a.view(name), b.view(name)), name
+    for s in range(S):  # the pools on their valid slots (the rest was never written)
+        npg_s = int(a.view("npages")[s])
+        plen = a.view("page_len")[s, :npg_s].cpu()
+        ka, kb = a.view("pool_k")[s, :npg_s].cpu(), b.view("pool_k")[s, :npg_s].cpu()
+        va, vb = a.view("pool_v")[s, :npg_s].cpu(), b.view("pool_v")[s, :npg_s].cpu()
+        for j in range(npg_s):
+            ln = int(plen[j])
+            assert torch.equal(ka[j, :ln], kb[j, :ln]) and torch.equal(va[j, :ln], vb[j, :ln])
     for s in range(S):
         _check_index(a, sts[s], s, n + steps)
