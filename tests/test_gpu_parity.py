@@ -765,6 +765,43 @@ def test_visit_budget_decode_step(B):
             _check_query(a, sts[s], s, r, pa, na, ta, oa[s * g:(s + 1) * g], q_s)
 
 
+@pytest.mark.parametrize("k1", [0, 5000])
+def test_high_threshold_bins_decode_step(B, k1):
+    """Queries along the first direction (plus a little noise): on the first
+    composite every distance lies above bin 255, so its threshold bin is not
+    among the low bins the collect searches first (it reads the whole
+    histogram), and with a visit budget the k1-th entry's distance is that
+    high too; the other composites stay in the low bins.  ice_decode_step
+    against the oracle after every step, unbounded and bounded walks."""
+    S, n, steps, g, d, p, m, L, k = 2, 2500, 3, 2, 128, 16, 4, 3, 128
+    dev = torch.device("cuda")
+    K, V, _, _ = _inputs(S, n + steps, d, g, 24, 45, "bf16")
+    U = W.directions(m * L, d, 45, "bf16")
+    print(f"[case] high threshold bins decode_step k1={k1}", flush=True)
+    a = B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U.to(dev),
+                page_size=p, budget_k=k, m=m, L=L, gqa_group=g, k1=k1, capacity=n + steps)
+    prm = oracle.Params(d=d, p=p, k=k, m=m, L=L, g=g, k1=k1)
+    sts = [oracle.OracleStream(prm, _np(K[s, :n]), _np(V[s, :n]), _np(U), n_cap=n + steps)
+           for s in range(S)]
+    gen = torch.Generator().manual_seed(7)
+    for t in range(steps):
+        qt = (U[0, :d].float().repeat(S * g, 1)
+              + 0.03 * torch.randn(S * g, d, generator=gen)).to(torch.bfloat16)
+        pa, na, oa, ta = a.decode_step(K[:, n + t].contiguous().to(dev),
+                                       V[:, n + t].contiguous().to(dev), qt.to(dev),
+                                       with_topk=True)
+        torch.cuda.synchronize()
+        for s in range(S):
+            sts[s].insert(_np(K[s, n + t]), _np(V[s, n + t]))
+            q_s = _np(qt[s * g:(s + 1) * g])
+            r = sts[s].query(q_s, literal=True)
+            if t == 0 and s == 0:  # the case is what it says: composite 0 above bin 255
+                c0 = sts[s].codes[:n + 1, :m].astype(np.int64)
+                M0 = np.abs(c0 - r["qcode"][:m].astype(np.int64)).max(axis=1)
+                assert (M0 >> 20).min() > 255
+            _check_query(a, sts[s], s, r, pa, na, ta, oa[s * g:(s + 1) * g], q_s)
+
+
 # ---------------------------------------------------------------- parameter ranges
 
 @pytest.mark.parametrize("m,L,k", [(10, 4, 256), (12, 6, 256), (4, 32, 128)])
