@@ -354,12 +354,16 @@ def main():
                 layers[r].decode_step_reuse(k_new, v_new, q, pg, npg, out=out)
             ncall[r] += 1
 
+    host_us = []  # host time to issue one step (argument marshalling and launches)
+
     def timed(reuse):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
+        h0 = time.perf_counter()
         for _ in range(args.steps):
             step(reuse)
+        host_us.append((time.perf_counter() - h0) * 1e6 / args.steps)
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
@@ -523,6 +527,9 @@ def main():
                               "ice_decode_step_reuse = insert + sparse_attn over the "
                               "layer's last selection")},
         "build_ms": round(sorted(build_ms)[len(build_ms) // 2], 3),
+        # host time to issue one step in the timed loop: below `value`, the
+        # device is the bound and the launch queue never runs dry
+        "host_us_per_step": round(host_us[0], 2),
         "step_alg_bytes": int(step_alg),
         "step_alg_gbs": round(step_gbs, 1),
         "step_frac": round(step_gbs / PEAK_HBM_GBS, 4),

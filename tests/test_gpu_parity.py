@@ -575,6 +575,40 @@ def test_scan_block_shapes(B, n):
         _check_query(idx, st, s, r, pg, npg, tk, out[s * g:(s + 1) * g], q_s)
 
 
+@pytest.mark.parametrize("n", [50500, 50000])
+def test_more_scan_blocks_than_the_device_holds(B, n):
+    """16 streams of about 50,000 tokens: 512-thread scan and collect blocks,
+    800 or 784 of them, more than the device holds at once (three per CU), so
+    the blocks run in two waves.  n = 50,500 puts the decode step's new token
+    in an even range, n = 50,000 in an odd one of a ragged last block.  Two
+    decode steps, each against the oracle on the first and the last stream
+    (every index array, candidates, pages, top-k, attention)."""
+    S, g, d, p, m, L, k, steps = 16, 2, 128, 16, 8, 4, 256, 2
+    dev = torch.device("cuda")
+    K, V, q0, _ = _inputs(S, n + steps, d, g, 64, 93, "bf16")
+    U = W.directions(m * L, d, 93, "bf16").to(dev)
+    print(f"[case] more scan blocks than the device holds n={n}", flush=True)
+    idx = B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U, page_size=p,
+                  budget_k=k, m=m, L=L, gqa_group=g, capacity=n + steps)
+    prm = oracle.Params(d=d, p=p, k=k, m=m, L=L, g=g)
+    sts = {s: oracle.OracleStream(prm, _np(K[s, :n]), _np(V[s, :n]), _np(U), n_cap=n + steps)
+           for s in (0, S - 1)}
+    gen = torch.Generator().manual_seed(8)
+    for t in range(steps):
+        qt = torch.randn(S * g, d, generator=gen).to(torch.bfloat16)
+        pg, npg, out, tk = idx.decode_step(K[:, n + t].contiguous().to(dev),
+                                            V[:, n + t].contiguous().to(dev), qt.to(dev),
+                                            with_topk=True)
+        torch.cuda.synchronize()
+        for s, st in sts.items():
+            st.insert(_np(K[s, n + t]), _np(V[s, n + t]))
+            q_s = _np(qt[s * g:(s + 1) * g])
+            r = st.query(q_s)
+            _check_query(idx, st, s, r, pg, npg, tk, out[s * g:(s + 1) * g], q_s)
+    for s, st in sts.items():
+        _check_index(idx, st, s, n + steps)
+
+
 def test_capacity_error(B):
     dev = torch.device("cuda")
     K, V, q, _ = _inputs(1, 40, 128, 1, 4, 13, "bf16")
