@@ -44,89 +44,63 @@ constexpr int kMaxTies = 256;  // page budgets up to this take the fused attenti
 // ---------------------------------------------------------------- helpers
 
 // Exact fp64 scores of cnt tokens by a block of NT threads, in the blocked
-// order (ice_step_dev.h): per round of as many rows as ROWBYTES of LDS holds,
-// the key rows are staged in LDS row-major with 16 bytes of padding
-// (slot_of(j) gives token j's page slot); then d/16 lanes score each row,
-// lane j summing elements 16j .. 16j+15 in order (two or four 16-byte LDS
-// reads), and the lanes' sums are added pairwise.  emit(j, slot, score)
-// receives each result: with nq query vectors (qkv + 128 h, the GQA max
-// mode's heads) the largest of the nq scores.  lcs needs
-// min(NT, ROWBYTES / (d*elem + 16)) entries; rows and qkv are 16-byte aligned.
-template <int DT, int NT, int ROWBYTES, typename SlotOf, typename Emit>
+// order (ice_step_dev.h): d/16 lanes score each key row, lane j reading
+// elements 16j .. 16j+15 straight from the pool (two bf16 or four fp32
+// 16-byte requests, in flight together) and summing them in order; the
+// lanes' sums are added pairwise.  slot_of(j) gives token j's page slot.
+// emit(j, slot, score) receives each result: with nq query vectors (qkv +
+// 128 h, the GQA max mode's heads) the largest of the nq scores.  qkv is
+// 16-byte aligned.
+template <int DT, int NT, typename SlotOf, typename Emit>
 __device__ void block_score(const Dev &dv, int s, uint32_t cnt, SlotOf slot_of, const float *qkv,
-                            int nq, int32_t *lcs, uint32_t *rows, Emit emit) {
+                            int nq, Emit emit) {
   const int tid = threadIdx.x;
   const int d = dv.d;
-  const int row_bytes = d * dv.elem;
-  const int rstride = row_bytes + 16;
-  const uint32_t fit = (uint32_t)(ROWBYTES / rstride);
-  const uint32_t cap = fit < (uint32_t)NT ? fit : (uint32_t)NT;  // rows per round
-  const int cpr = row_bytes / 16;  // 16-byte chunks per row (8, 16 or 32)
-  const int lcpr = __builtin_ctz((unsigned)cpr);
+  const int64_t row_bytes = (int64_t)d * dv.elem;
+  const char *pool =
+      reinterpret_cast<const char *>(dv.pool_k) + (int64_t)s * dv.pcap * dv.p * row_bytes;
   const int nbk = d >> 4, lnb = d == 128 ? 3 : 2;
-  constexpr int kIter = (ROWBYTES / 16 + NT - 1) / NT;
-  char *rb = reinterpret_cast<char *>(rows);
-  for (uint32_t b0 = 0; b0 < cnt; b0 += cap) {
-    const uint32_t nr = min(cap, cnt - b0);
-    if ((uint32_t)tid < nr) lcs[tid] = slot_of(b0 + tid);
-    lds_barrier();
-    uint4 v[kIter];
+  constexpr int kReq = DT == 0 ? 4 : 2;  // 16-byte requests per lane
+  for (uint32_t x = tid; x < cnt * nbk; x += NT) {  // whole lane groups
+    const uint32_t r = x >> lnb;
+    const int j = x & (nbk - 1);
+    const int32_t slot = slot_of(r);
+    const uint4 *rp = reinterpret_cast<const uint4 *>(pool + slot * row_bytes) + j * kReq;
+    uint4 u[kReq];
 #pragma unroll
-    for (int k = 0; k < kIter; ++k) {  // unconditional loads (row 0 stands in past nr)
-      const int x = tid + NT * k;
-      const int r = x >> lcpr, c = x & (cpr - 1);
-      const int rr = (uint32_t)r < nr ? r : 0;
-      const int64_t row = ((int64_t)s * dv.pcap * dv.p + lcs[rr]) * row_bytes;
-      v[k] = reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(dv.pool_k) + row)[c];
-    }
+    for (int i = 0; i < kReq; ++i) u[i] = rp[i];
+    double best = 0.0;
+    for (int h = 0; h < nq; ++h) {
+      // element order within the block of 16
+      const float4 *qp = reinterpret_cast<const float4 *>(qkv + 128 * h + 16 * j);
+      double z = 0.0;
+      if constexpr (DT == 0) {
 #pragma unroll
-    for (int k = 0; k < kIter; ++k) {
-      const int x = tid + NT * k;
-      const int r = x >> lcpr, c = x & (cpr - 1);
-      if ((uint32_t)r < nr) *reinterpret_cast<uint4 *>(rb + r * rstride + 16 * c) = v[k];
-    }
-    lds_barrier();
-    for (uint32_t x = tid; x < nr * nbk; x += NT) {  // whole lane groups
-      const uint32_t r = x >> lnb;
-      const int j = x & (nbk - 1);
-      const char *rp = rb + r * rstride + j * 16 * dv.elem;
-      double best = 0.0;
-      for (int h = 0; h < nq; ++h) {
-        // element order within the block of 16, four (fp32) or eight (bf16)
-        // key elements and their query elements at a time (few live registers)
-        const float4 *qp = reinterpret_cast<const float4 *>(qkv + 128 * h + 16 * j);
-        double z = 0.0;
-        if constexpr (DT == 0) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint4 u = reinterpret_cast<const uint4 *>(rp)[i];
-            const float4 f = qp[i];
-            z = fma((double)f.x, (double)__uint_as_float(u.x), z);
-            z = fma((double)f.y, (double)__uint_as_float(u.y), z);
-            z = fma((double)f.z, (double)__uint_as_float(u.z), z);
-            z = fma((double)f.w, (double)__uint_as_float(u.w), z);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const uint4 u = reinterpret_cast<const uint4 *>(rp)[i];
-            const float4 f0 = qp[2 * i], f1 = qp[2 * i + 1];
-            z = fma((double)f0.x, (double)__uint_as_float(u.x << 16), z);
-            z = fma((double)f0.y, (double)__uint_as_float(u.x & 0xffff0000u), z);
-            z = fma((double)f0.z, (double)__uint_as_float(u.y << 16), z);
-            z = fma((double)f0.w, (double)__uint_as_float(u.y & 0xffff0000u), z);
-            z = fma((double)f1.x, (double)__uint_as_float(u.z << 16), z);
-            z = fma((double)f1.y, (double)__uint_as_float(u.z & 0xffff0000u), z);
-            z = fma((double)f1.z, (double)__uint_as_float(u.w << 16), z);
-            z = fma((double)f1.w, (double)__uint_as_float(u.w & 0xffff0000u), z);
-          }
+        for (int i = 0; i < 4; ++i) {
+          const float4 f = qp[i];
+          z = fma((double)f.x, (double)__uint_as_float(u[i].x), z);
+          z = fma((double)f.y, (double)__uint_as_float(u[i].y), z);
+          z = fma((double)f.z, (double)__uint_as_float(u[i].z), z);
+          z = fma((double)f.w, (double)__uint_as_float(u[i].w), z);
         }
-        z = tree_sum(z, nbk);
-        best = h == 0 ? z : fmax(best, z);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const float4 f0 = qp[2 * i], f1 = qp[2 * i + 1];
+          z = fma((double)f0.x, (double)__uint_as_float(u[i].x << 16), z);
+          z = fma((double)f0.y, (double)__uint_as_float(u[i].x & 0xffff0000u), z);
+          z = fma((double)f0.z, (double)__uint_as_float(u[i].y << 16), z);
+          z = fma((double)f0.w, (double)__uint_as_float(u[i].y & 0xffff0000u), z);
+          z = fma((double)f1.x, (double)__uint_as_float(u[i].z << 16), z);
+          z = fma((double)f1.y, (double)__uint_as_float(u[i].z & 0xffff0000u), z);
+          z = fma((double)f1.z, (double)__uint_as_float(u[i].w << 16), z);
+          z = fma((double)f1.w, (double)__uint_as_float(u[i].w & 0xffff0000u), z);
+        }
       }
-      if (j == 0) emit(b0 + r, lcs[r], best);
+      z = tree_sum(z, nbk);
+      best = h == 0 ? z : fmax(best, z);
     }
-    lds_barrier();
+    if (j == 0) emit(r, slot, best);
   }
 }
 
@@ -437,13 +411,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_
 // before the scoring and consumed after it.
 constexpr int kSubShift = kHistShift - kHistBits;  // second-level bins: M >> 9 & 2047
 
-// Two shapes: 640-thread blocks (one per CU) stage 32 KB of candidate rows and
-// read the scoring chains 8 words ahead; 512-thread blocks (many per CU, the
-// long contexts) stage 16 KB and read 4 ahead, so three blocks fit a CU (LDS
-// and registers) and more of their latency chains overlap.
+// Two shapes: 640-thread blocks (one per CU) have the registers of four
+// waves per SIMD; 512-thread blocks (many per CU, the long contexts) those of
+// six, so three blocks fit a CU and more of their latency chains overlap.
 template <int NT>
 struct CollectShape {
-  static constexpr int kRowBytes = NT == 512 ? 16 * 1024 : 32 * 1024;
   static constexpr int kWavesPerEu = NT == 512 ? 6 : 4;
 };
 
@@ -454,7 +426,6 @@ template <int DT, int NT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape<NT>::kWavesPerEu))) void k_qcollect(
     Dev dv, int64_t n, bool bounded, int head, const void *q) {
   constexpr int kScanThreads = NT, kScanTpb = 2 * NT;
-  constexpr int kCollectRowBytes = CollectShape<NT>::kRowBytes;
   const int s = blockIdx.x % dv.S;  // the scan's block-to-stream mapping
   const int64_t rng = blockIdx.x / dv.S;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -475,8 +446,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
   __shared__ int32_t lloc[kScanTpb];     // page slots of the block's tokens
   __shared__ unsigned long long skb[kScanTpb];
   __shared__ int32_t spb[kScanTpb];
-  __shared__ int32_t lcs[kCollectRowBytes / 128];
-  __shared__ __attribute__((aligned(16))) uint32_t rows[kCollectRowBytes / 4];
   const uint32_t k0e = (uint32_t)min((int64_t)dv.k0, n);
   const int64_t i0 = rng * kScanTpb;
   const int64_t i1 = min(i0 + kScanTpb, n);
@@ -614,8 +583,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
       kslot[tid + NT * u] = (int16_t)slot[u];
     }
   }
-  block_score<DT, kScanThreads, kCollectRowBytes>(
-      dv, s, nc, [cidp, llocp](uint32_t j) { return llocp[cidp[j]]; }, qkv, nq, lcs, rows,
+  block_score<DT, kScanThreads>(
+      dv, s, nc, [cidp, llocp](uint32_t j) { return llocp[cidp[j]]; }, qkv, nq,
       [skbp, spbp, lp](uint32_t x, int32_t slotx, double sc) {
         skbp[x] = score_rank_key(sc);
         spbp[x] = slotx >> lp;
