@@ -135,10 +135,11 @@ __device__ __forceinline__ int32_t ld_code(__amdgpu_buffer_rsrc_t r, uint32_t of
 // LDS, the arithmetic of ice_step_dev.h), so no prep kernel sits on the
 // query's critical path; the blocks of range 0 publish q_kv and the codes for
 // the later kernels and clear the query's counters.  In a decode step (k_new
-// given) token n - 1 is the new token: the block whose range holds it
-// projects it on the same staged directions, leaves it out of the code walk,
-// adds its M values afterwards and writes its codes, list entries, page and
-// pool rows at the end.
+// given) token n - 1 is the new token: the block whose range holds it leaves
+// it out of its code walk, and the block of range 0 (dispatched first, so the
+// insert is off the critical path of the last blocks) projects it on the
+// same staged directions, adds its M values to its own histogram and writes
+// its codes, list entries, page and pool rows at the end.
 constexpr int kPipe = 16;
 
 //
@@ -158,9 +159,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_
   const int mL = dv.mL, m = dv.m, L = dv.L, d = dv.d, g = dv.g;
   const int64_t r = blockIdx.x / S;
   const int64_t nold = k_new != nullptr ? n - 1 : n;  // tokens already in the index
-  // this block inserts token nold (no short circuit: no branch before the
-  // kernel arguments are all requested)
-  const bool ins = (k_new != nullptr) & (r == nold / kScanTpb);
+  // the blocks of range 0, dispatched first, insert token nold, which keeps
+  // the insert off the last blocks' critical path (no short circuit: no
+  // branch before the kernel arguments are all requested)
+  const bool ins = (k_new != nullptr) & (r == 0);
   // directions: element e < d of direction t at dl[((e / 16) * W + t) * 16 + e % 16]
   // (each lane of a query lane group reads its 16 elements as four 16-byte
   // runs), u_t[d] at ud[t]
