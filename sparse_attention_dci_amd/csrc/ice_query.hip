@@ -1214,6 +1214,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
 constexpr int kBigHashBits = 14;
 constexpr int64_t kBitTokens = (int64_t)32 << kBigHashBits;  // bitmap of the hash's words
 constexpr int kWin = 4096;
+constexpr int kWinWalk = 1024;  // window of the page walk alone (no top-k asked)
 constexpr int kBndBig = 5120;  // boundary keys held in LDS (their rank keys and pages stay global)
 constexpr int kPerBig = kMaxCandBig / kFinalThreads;
 constexpr int kPerBnd = kBndBig / kFinalThreads;
@@ -1498,6 +1499,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
   }
   for (int x = tid; x < kBuckets; x += NT) sh.bcnt[x] = 0;
   for (int x = tid; x < 2048; x += NT) sh.seen[x] = 0;
+  if (tid == 0) sh.win_end = 0;
   __syncthreads();
   lo = ~0ull;
   hi = 0;
@@ -1542,21 +1544,26 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
   uint32_t B0 = 0, rank_base = 0;
   while (B0 < (uint32_t)kBuckets && rank_base < nu &&
          ((int)sh.nsel < P || rank_base < want_top)) {
-    // the window: buckets [B0, B1), at most kWin elements (one bucket at least)
-    if (tid == 0) {
-      uint32_t lo_b = B0 + 1, hi_b = kBuckets;  // largest B1 with count <= kWin
-      while (lo_b < hi_b) {
-        const uint32_t mid = (lo_b + hi_b + 1) / 2;
-        if (sh.bstart[mid] - sh.bstart[B0] <= (uint32_t)kWin)
-          lo_b = mid;
-        else
-          hi_b = mid - 1;
-      }
-      sh.win_end = lo_b;
+    // the window: buckets [B0, B1), the largest B1 whose buckets hold at most
+    // lim elements (one bucket at least).  The page walk alone needs the
+    // first ranks only, so its windows hold at most kWinWalk elements, unless
+    // bucket B0 alone holds more (then up to kWin).  Bucket starts grow with
+    // b, so the buckets that fit are a run from B0 + 1: each wave finds its
+    // last one by a ballot and takes the largest with one LDS atomic.
+    const uint32_t base = sh.bstart[B0];
+    const uint32_t lim = want_top == 0u && sh.bstart[B0 + 1] - base <= (uint32_t)kWinWalk
+                             ? (uint32_t)kWinWalk : (uint32_t)kWin;
+    if (tid == 0) atomicMax(&sh.win_end, B0 + 1);
+    for (uint32_t b0 = B0 + 1; b0 <= (uint32_t)kBuckets; b0 += NT) {  // uniform bound
+      const uint32_t b = b0 + tid;
+      const bool fits = b <= (uint32_t)kBuckets && sh.bstart[b] - base <= lim;
+      const unsigned long long bal = __ballot(fits);
+      if (lane == 0 && bal)
+        atomicMax(&sh.win_end, b0 + 64 * w + 63 - (uint32_t)__builtin_clzll(bal));
     }
     __syncthreads();
     const uint32_t B1 = sh.win_end;
-    const uint32_t base = sh.bstart[B0], cntw = sh.bstart[B1] - base;
+    const uint32_t cntw = sh.bstart[B1] - base;
     if (cntw <= (uint32_t)kWin) {
       // scatter the window's elements in bucket order, rank each by position
       // (kWin / NT per thread), then write tokens and pages in rank order

@@ -676,6 +676,33 @@ def test_identical_keys_large_union(B):
              literal=False)
 
 
+def test_large_union_walk_past_the_first_window(B):
+    """1,500 near-copies of 60 times the query direction, far above every other
+    score, fill whole pages of 32: the first 1,024 ranks hold at most 32 distinct
+    pages, fewer than the 64 the budget selects, so the large-union page walk
+    goes on into its next rank window.  Pages, top-k and attention against
+    the oracle, with and without the top-k asked (its windows differ)."""
+    S, n, d, g, p, k, m, L = 2, 20000, 128, 1, 32, 2048, 4, 4
+    K, V, _, _ = _inputs(S, n, d, g, 64, 95, "bf16")
+    gen = torch.Generator().manual_seed(96)
+    u = torch.randn(d, generator=gen)
+    u = u / u.norm()
+    K[:, 5000:6500] = (60.0 * u + 0.5 * torch.randn(S, 1500, d, generator=gen)).to(torch.bfloat16)
+    q = u.repeat(S * g, 1).to(torch.bfloat16)
+    idx = run_case(B, S=S, n=n, d=d, g=g, p=p, k=k, m=m, L=L, keys=(K, V, q), seed=95,
+                   literal=False)
+    prm = oracle.Params(d=d, p=p, k=k, m=m, L=L, g=g)
+    st = oracle.OracleStream(prm, _np(K[0]), _np(V[0]), _np(W.directions(m * L, d, 95, "bf16")),
+                             n_cap=n)
+    r = st.query(_np(q[:g]), literal=False)
+    assert L * k > 4096  # the large-union finaliser (chosen by L * k0)
+    assert len(np.unique(st.page_of[r["ranked"][:1024]])) < k // p  # the case is what it says
+    dev = torch.device("cuda")
+    pg, npg, _ = idx.query_pages(q.to(dev))  # the page walk alone: walk-only windows
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(pg[0, :int(npg[0])].cpu().numpy(), r["page_ids"])
+
+
 def test_qwen3_4b_262k_full_layer_sampled(B):
     """Full-size layer of the 262,144-token Qwen3-4B-shaped workload (8 streams,
     power-law cluster sizes, L * k0 = 12,288): two sampled streams checked
