@@ -165,6 +165,44 @@ def run_case(B, *, S, n, d=128, g=1, p=16, k=256, m=4, L=2, dtype="bf16", cluste
     return idx
 
 
+def test_golden_tiny_worked_example(B):
+    """The HIP path on tests/golden/tiny_worked_example.json, a three-token
+    stream worked through the decode path by hand: the key-norm bound, codes,
+    query codes, candidates, top-k and pages equal the hand-worked values
+    exactly; the attention is within the attention tolerance of them."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "tiny_worked_example.json")) as f:
+        gd = json.load(f)
+    prm, e = gd["params"], gd["expected"]
+    d, n = prm["d"], 3
+    K = torch.zeros(1, n, d)
+    V = torch.zeros(1, n, d)
+    U = torch.zeros(1, d + 1)
+    q = torch.zeros(1, d)
+    for t, key in ((K[0], "keys_nonzero"), (V[0], "values_nonzero"), (U, "direction_nonzero"),
+                   (q, "query_nonzero")):
+        for r, c, v in gd["inputs"][key]:
+            t[r, c] = v
+    dev = torch.device("cuda")
+    idx = B.Index(K.to(dev), V.to(dev), U.to(dev), page_size=prm["p"], budget_k=prm["k"],
+                  m=prm["m"], L=prm["L"], gqa_group=prm["g"], k0=prm["k0"], capacity=n)
+    qd = q.to(dev)
+    pg, npg, tk = idx.query_pages(qd, with_topk=True)
+    out = idx.sparse_attn(qd, pg, npg)
+    torch.cuda.synchronize()
+    assert float(idx.view("norm_c")[0]) == e["norm_bound"]
+    assert idx.view("codes")[0, :n, 0].tolist() == e["codes"]
+    assert idx.view("qcode")[0].tolist() == e["qcode"]
+    cc = int(idx.view("cand_count")[0, 0])
+    assert sorted(idx.view("cand")[0, 0, :cc].tolist()) == e["candidates"]
+    assert tk[0].tolist() == e["topk"]
+    assert int(npg[0]) == e["n_pages"] and pg[0, :e["n_pages"]].tolist() == e["page_ids"]
+    o = out[0].cpu().numpy()
+    assert np.max(np.abs(o[:2] - np.array(e["attention_first_two"]))) <= ATTN_TOL
+    assert np.max(np.abs(o[2:])) <= ATTN_TOL
+
+
 def test_single_stream_fp32_ragged(B):
     run_case(B, S=1, n=3037, g=1, p=16, k=256, m=4, L=2, dtype="f32", seed=2)
 

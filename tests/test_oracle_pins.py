@@ -542,3 +542,51 @@ def test_reuse_step_attends_the_reused_pages_and_the_new_token(ora):
         z = Kt @ q[h].astype(np.float64) / np.sqrt(64)
         w = np.exp(z - z.max())
         assert np.allclose(out[h], (w / w.sum()) @ Vt, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- golden: a case worked by hand
+
+def _golden_tiny():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "tiny_worked_example.json")) as f:
+        g = json.load(f)
+    prm = g["params"]
+    d, n = prm["d"], 3
+    K = np.zeros((n, d), np.float32)
+    V = np.zeros((n, d), np.float32)
+    U = np.zeros((1, d + 1), np.float32)
+    q = np.zeros((1, d), np.float32)
+    for arr, key in ((K, "keys_nonzero"), (V, "values_nonzero"), (U, "direction_nonzero"),
+                     (q, "query_nonzero")):
+        for r, c, v in g["inputs"][key]:
+            arr[r, c] = v
+    return g, K, V, U, q
+
+
+def test_golden_tiny_worked_example(ora):
+    """The oracle on tests/golden/tiny_worked_example.json: every step of the
+    decode path equals the values worked by hand there (integers exactly, the
+    attention to 1e-12), and the stored attention equals its closed form."""
+    g, K, V, U, q = _golden_tiny()
+    prm, e = g["params"], g["expected"]
+    P = ora.Params(d=prm["d"], p=prm["p"], k=prm["k"], m=prm["m"], L=prm["L"], g=prm["g"],
+                   k0=prm["k0"])
+    st = ora.OracleStream(P, K, V, U)
+    assert st.c == e["norm_bound"] and st.D == e["tree_depth"]
+    assert st.codes[:3, 0].tolist() == e["codes"]
+    assert st.page_of[:3].tolist() == e["page_of"]
+    r = st.query(q)
+    assert r["qcode"].tolist() == e["qcode"]
+    assert sorted(r["S"][0].tolist()) == e["candidates"]
+    assert [int(v) for v in r["visits"]] == e["visits"]
+    assert r["ranked"].tolist() == e["ranked"]
+    topk = r["topk"].tolist() + [-1] * (prm["k"] - len(r["topk"]))
+    assert topk == e["topk"]
+    assert r["page_ids"].tolist() == e["page_ids"]
+    out = st.attend(q, np.asarray(r["page_ids"]))
+    s = np.exp(3 / 8) + 1 + np.exp(1 / 8)
+    closed = [(np.exp(3 / 8) + np.exp(1 / 8)) / s, (1 + np.exp(1 / 8)) / s]
+    np.testing.assert_allclose(e["attention_first_two"], closed, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(out[0, :2], e["attention_first_two"], rtol=0, atol=1e-12)
+    assert np.all(out[0, 2:] == 0)
