@@ -203,6 +203,49 @@ def test_golden_tiny_worked_example(B):
     assert np.max(np.abs(o[2:])) <= ATTN_TOL
 
 
+@pytest.mark.parametrize("case", ["unbounded", "bounded"])
+def test_golden_tiny_pdci_two_lists(B, case):
+    """The HIP path on tests/golden/tiny_pdci_two_lists.json (two lists per
+    composite, a score tie, a visit budget of 4 in the bounded case), worked
+    by hand: codes, query codes, candidates, visits (query statistics), top-k
+    and pages exactly; the attention within the attention tolerance."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "tiny_pdci_two_lists.json")) as f:
+        gd = json.load(f)
+    prm, e = gd["params"], gd["expected"]
+    c = e[case]
+    d, n, mL = prm["d"], 4, prm["m"] * prm["L"]
+    K = torch.zeros(1, n, d)
+    V = torch.zeros(1, n, d)
+    U = torch.zeros(mL, d + 1)
+    q = torch.zeros(1, d)
+    for t, key in ((K[0], "keys_nonzero"), (V[0], "values_nonzero"), (U, "directions_nonzero"),
+                   (q, "query_nonzero")):
+        for r, col, v in gd["inputs"][key]:
+            t[r, col] = v
+    dev = torch.device("cuda")
+    idx = B.Index(K.to(dev), V.to(dev), U.to(dev), page_size=prm["p"], budget_k=prm["k"],
+                  m=prm["m"], L=prm["L"], gqa_group=prm["g"], k0=prm["k0"], k1=c["k1"],
+                  capacity=n)
+    qd = q.to(dev)
+    stats = B.stats_tensor(1, dev)
+    pg, npg, tk = idx.query_pages(qd, with_topk=True, stats=stats)
+    out = idx.sparse_attn(qd, pg, npg)
+    torch.cuda.synchronize()
+    assert float(idx.view("norm_c")[0]) == e["norm_bound"]
+    assert idx.view("codes")[0, :n].tolist() == e["codes"]
+    assert idx.view("qcode")[0].tolist() == e["qcode"]
+    cc = int(idx.view("cand_count")[0, 0])
+    assert sorted(idx.view("cand")[0, 0, :cc].tolist()) == sorted(c["candidates_in_order"])
+    assert B.parse_stats(stats, prm["L"])[0]["visits"] == c["visits"]
+    assert tk[0].tolist() == c["topk"]
+    assert int(npg[0]) == len(c["page_ids"]) and pg[0, :int(npg[0])].tolist() == c["page_ids"]
+    o = out[0].cpu().numpy()
+    assert np.max(np.abs(o[:4] - np.array(e["attention_first_four"]))) <= ATTN_TOL
+    assert np.max(np.abs(o[4:])) <= ATTN_TOL
+
+
 def test_single_stream_fp32_ragged(B):
     run_case(B, S=1, n=3037, g=1, p=16, k=256, m=4, L=2, dtype="f32", seed=2)
 

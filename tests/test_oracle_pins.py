@@ -590,3 +590,52 @@ def test_golden_tiny_worked_example(ora):
     np.testing.assert_allclose(e["attention_first_two"], closed, rtol=0, atol=1e-15)
     np.testing.assert_allclose(out[0, :2], e["attention_first_two"], rtol=0, atol=1e-12)
     assert np.all(out[0, 2:] == 0)
+
+
+def _golden_pdci():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "tiny_pdci_two_lists.json")) as f:
+        g = json.load(f)
+    d, n, mL = g["params"]["d"], 4, g["params"]["m"] * g["params"]["L"]
+    K = np.zeros((n, d), np.float32)
+    V = np.zeros((n, d), np.float32)
+    U = np.zeros((mL, d + 1), np.float32)
+    q = np.zeros((1, d), np.float32)
+    for arr, key in ((K, "keys_nonzero"), (V, "values_nonzero"), (U, "directions_nonzero"),
+                     (q, "query_nonzero")):
+        for r, c, v in g["inputs"][key]:
+            arr[r, c] = v
+    return g, K, V, U, q
+
+
+@pytest.mark.parametrize("case", ["unbounded", "bounded"])
+def test_golden_tiny_pdci_two_lists(ora, case):
+    """The oracle on tests/golden/tiny_pdci_two_lists.json (two lists per
+    composite, a score tie, a visit budget), by the literal walk and by the
+    closed form: every value equals the one worked by hand there, the
+    attention to 1e-12 and its stored value to its closed form."""
+    g, K, V, U, q = _golden_pdci()
+    prm, e = g["params"], g["expected"]
+    c = e[case]
+    P = ora.Params(d=prm["d"], p=prm["p"], k=prm["k"], m=prm["m"], L=prm["L"], g=prm["g"],
+                   k0=prm["k0"], k1=c["k1"])
+    st = ora.OracleStream(P, K, V, U)
+    assert st.c == e["norm_bound"] and st.D == e["tree_depth"]
+    assert st.codes[:4].tolist() == e["codes"] and st.page_of[:4].tolist() == e["page_of"]
+    for literal in (True, False):
+        r = st.query(q, literal=literal)
+        assert r["qcode"].tolist() == e["qcode"]
+        if literal:  # the literal walk hands candidates out in completion order
+            assert r["S"][0].tolist() == c["candidates_in_order"]
+        assert sorted(r["S"][0].tolist()) == sorted(c["candidates_in_order"])
+        assert [int(v) for v in r["visits"]] == c["visits"]
+        assert r["ranked"].tolist() == c["ranked"]
+        assert r["topk"].tolist() + [-1] * (prm["k"] - len(r["topk"])) == c["topk"]
+        assert r["page_ids"].tolist() == c["page_ids"]
+    out = st.attend(q, np.asarray(c["page_ids"]))
+    w = np.exp(0.25)
+    closed = [w / (3 * w + 1)] * 3 + [1 / (3 * w + 1)]
+    np.testing.assert_allclose(e["attention_first_four"], closed, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(out[0, :4], e["attention_first_four"], rtol=0, atol=1e-12)
+    assert np.all(out[0, 4:] == 0)
