@@ -39,6 +39,7 @@ constexpr int kBndLds = 2048;       // boundary entries ranked in LDS
 constexpr int kBuckets = 2048;
 static_assert(kBuckets == kHistBins, "bucket counts are searched as a histogram");
 constexpr int kFusedMaxPages = 1024;
+constexpr int kFastPages = 32;  // selections every wave walks for itself, at most
 constexpr int kMaxTies = 256;  // page budgets up to this take the fused attention
 
 // ---------------------------------------------------------------- helpers
@@ -778,6 +779,11 @@ struct FinalShared {
   int32_t sel[kFusedMaxPages];  // the selected pages, for the fused attention
   int32_t nsel;
   float wm[16 * 16], wl[16 * 16];
+  // past the wave outputs of the fused attention (which overwrite the rank
+  // arrays): the pages of the first 64 ranks, and each wave's own copy of the
+  // selection when those ranks hold all of it
+  int32_t top_pg[64];
+  int32_t wsel[16 * kFastPages];
 };
 
 // PER = union elements per thread (L * k0 <= PER * kFinalThreads): 1 when the
@@ -1129,6 +1135,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
       if (tid + kFinalThreads * j < nu) {
         rsid[rnk[j]] = ix[j];
         rspg[rnk[j]] = px[j];
+        if (rnk[j] < 64u) sh.top_pg[rnk[j]] = px[j];
       }
     }
     for (int x = tid; x < 2048; x += kFinalThreads) sh.seen[x] = 0;
@@ -1147,7 +1154,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
     for (uint32_t x0 = 0; x0 < nu && nsel < dv.P; x0 += 64) {
       const uint32_t x = x0 + lane;
       const bool valid = x < nu;
-      const int32_t pg = valid ? rspg[x] : 0;
+      const int32_t pg = valid ? (x0 == 0 ? sh.top_pg[x] : rspg[x]) : 0;
       const bool fresh = valid && ((sh.seen[pg >> 5] >> (pg & 31)) & 1u) == 0u;
       const unsigned long long act = __ballot(fresh);
       const unsigned long long mt = match_bits((uint32_t)pg, pbits, act);
@@ -1182,12 +1189,42 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
   // outputs)
   constexpr int NW = kFinalThreads / 64;
   static_assert(sizeof(FinalShared) >= (size_t)NW * kMaxGroup * D * 4 + 0, "wave outputs fit");
+  static_assert(offsetof(FinalShared, sel) >= (size_t)NW * kMaxGroup * D * 4,
+                "the wave outputs leave the selection, its copies and the top ranks' pages");
   AttnWave<D> st;
   attn_init(st);
-  lds_barrier();
-  const int np = sh.nsel;
+  // When the first 64 ranks hold the whole selection (and no top-k is
+  // written, whose reads of the rank arrays the wave outputs would race),
+  // every wave walks them for itself, as wave 0 did, and starts its chunk at
+  // once; else all wait for wave 0's walk.
+  int np;
+  const int32_t *selp;
+  bool fast = topk_ids == nullptr && dv.P <= kFastPages;
+  {
+    int pbits = 1;
+    while ((1ll << pbits) < dv.pcap) ++pbits;
+    const bool valid = (uint32_t)lane < nu;
+    const int32_t pg = valid ? sh.top_pg[lane] : 0;
+    const unsigned long long act = __ballot(valid);
+    const unsigned long long mt = match_bits((uint32_t)pg, pbits, act);
+    const unsigned long long lt = lanemask_lt();
+    const bool firstocc = valid && (mt & lt) == 0ull;
+    const unsigned long long fm = __ballot(firstocc);
+    const int nf = popc64(fm);
+    fast = fast && (nf >= dv.P || nu <= 64u);
+    np = min(dv.P, nf);
+    selp = sh.wsel + w * kFastPages;
+    const int pos = popc64(fm & lt);
+    if (fast && firstocc && pos < dv.P) sh.wsel[w * kFastPages + pos] = pg;
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (!fast) {  // uniform: every wave decides on the same ranks
+    lds_barrier();
+    np = sh.nsel;
+    selp = sh.sel;
+  }
   for (int T0 = w * kAttnChunk; T0 < np * dv.p; T0 += NW * kAttnChunk)
-    attn_chunk<DT, D, DT == 0, kAttnChunk / 16>(dv, s, T0, sh.sel, np, qh, ql, st);
+    attn_chunk<DT, D, DT == 0, kAttnChunk / 16>(dv, s, T0, selp, np, qh, ql, st);
   float *red = reinterpret_cast<float *>(&sh.skey[0]);
   attn_publish(st, w, NW, dv.g, sh.wm, sh.wl, red);
   lds_barrier();
