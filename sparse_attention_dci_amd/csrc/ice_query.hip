@@ -379,7 +379,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_
     lds_barrier();
     for (int l2 = w; l2 < L; l2 += NT / 64) {
       uint32_t bb = kHistBins - 1, bl;
-      if (ntok >= (uint32_t)dv.k0 && dv.k0 > 0) wave_find_bin(hist + l2 * kHistBins, dv.k0, bb, bl);
+      if (ntok >= (uint32_t)dv.k0 && dv.k0 > 0) {  // the low bins first (almost always there)
+        const uint4 v = reinterpret_cast<const uint4 *>(hist + l2 * kHistBins)[lane];
+        if (!wave_find_bin_low(v, dv.k0, bb, bl)) wave_find_bin(hist + l2 * kHistBins, dv.k0, bb, bl);
+      }
       if (lane == 0) blim[l2] = bb;
     }
     lds_barrier();
