@@ -256,8 +256,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--gqa", choices=("mean", "max"), default="mean",
                     help="GQA query mode: the heads' mean, or per-head walks ranked by the max score")
-    ap.add_argument("--offload", action="store_true",
-                    help="page pool in pinned host memory; the selected pages are staged in HBM")
+    ap.add_argument("--offload", nargs="?", const="all", default=None, choices=("all", "values"),
+                    help="page pool in pinned host memory (all; 'values': only the value pages, "
+                         "the keys stay in HBM); the selected pages are staged in HBM")
     ap.add_argument("--pregen", type=int, default=0,
                     help="decode steps run on every layer copy before timing (a long generation)")
     ap.add_argument("--reuse", type=int, default=1,
@@ -311,7 +312,8 @@ def main():
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         idx = binding.Index(K, V, U, page_size=w.p, budget_k=w.k, m=w.m, L=w.L, gqa_group=w.g,
-                            capacity=cap, gqa_mode=args.gqa, offload=args.offload)
+                            capacity=cap, gqa_mode=args.gqa,
+                            offload={None: False, "all": True, "values": "values"}[args.offload])
         e1.record()
         torch.cuda.synchronize()
         build_ms.append(e0.elapsed_time(e1))
@@ -519,7 +521,9 @@ def main():
                    "page_size": w.p, "budget_k": w.k, "m": w.m, "L": w.L,
                    "layers_per_step": layers_per_step, "layers_rotated": R,
                    "generated_before_timing": args.pregen, "gqa": args.gqa,
-                   "pool": "host (pinned, staged per step)" if args.offload else "HBM",
+                   "pool": {None: "HBM", "all": "host (pinned, staged per step)",
+                            "values": "values in host memory (pinned, staged per step), keys in HBM"}[
+                       args.offload],
                    "reuse": args.reuse,
                    "step": "ice_decode_step = insert + query_pages + sparse_attn"
                            + ("" if args.reuse == 1 else
@@ -543,8 +547,10 @@ def main():
     if reuse_res is not None:
         res["reuse"] = reuse_res
     if args.offload and "fetch" in avg_us:  # what crosses the host link per layer step
-        page_bytes = w.streams * attended * 2 * w.d * (2 if w.dtype == "bf16" else 4)
-        rows = w.streams * n_cand * w.d * (2 if w.dtype == "bf16" else 4)
+        ways = 1 if args.offload == "values" else 2  # the values alone, or keys and values
+        page_bytes = w.streams * attended * ways * w.d * (2 if w.dtype == "bf16" else 4)
+        rows = (0 if args.offload == "values" else 1) * w.streams * n_cand * w.d * (
+            2 if w.dtype == "bf16" else 4)
         res["offload"] = {"fetch_us": round(avg_us["fetch"], 2), "page_bytes": int(page_bytes),
                           "fetch_link_gbs": round(page_bytes / (avg_us["fetch"] * 1e-6) / 1e9, 1),
                           "rerank_row_bytes_over_link": int(rows),

@@ -82,7 +82,8 @@ typedef struct {
   int32_t gqa_mode;   /* ice_gqa_mode: how the g query heads of a KV head query
                          the index (0 = their mean; 1 = per-head walks, max score) */
   int32_t offload;    /* 0: the page pool lives in the workspace (HBM); 1: in
-                         caller-owned pinned host memory (ice_build_index_offload) */
+                         caller-owned pinned host memory (ice_build_index_offload);
+                         2: its values there, its keys in the workspace      */
 } ice_params;
 
 /* GQA query modes (the query heads sharing a KV head "averaged or maxed"):
@@ -157,13 +158,18 @@ ice_status ice_build_index_noalloc(const ice_params *prm, int32_t n_streams, int
  * copies the P selected pages (K and V) into the staging area, and the
  * attention runs on the staging area: results equal the resident pool's bit
  * for bit.  The build and the inserts write the pool rows to host memory.
+ * With prm->offload = 2 only the value pages live in host memory and the key
+ * pages stay in the workspace: the rerank reads its key rows from HBM, the
+ * host link carries the selected pages' values alone (the staging copy of
+ * their keys is an HBM copy), and the host pool is half the size.
  *   host_pool  pinned host memory, ice_host_pool_bytes of it, 256-byte
  *              aligned; it must outlive the index.
- * ice_build_index refuses prm->offload = 1, and this call prm->offload = 0
- * (ICE_ERR_INVALID_ARG); ICE_ERR_INVALID_ARG also when host_pool is not
- * device-mapped pinned memory, ICE_ERR_WORKSPACE when it is too small.
- * The page pool's layout is the resident one (ice_index_layout's pool_k and
- * pool_v become byte offsets into host_pool). */
+ * ice_build_index refuses prm->offload = 1 or 2, and this call
+ * prm->offload = 0 (ICE_ERR_INVALID_ARG); ICE_ERR_INVALID_ARG also when
+ * host_pool is not device-mapped pinned memory, ICE_ERR_WORKSPACE when it is
+ * too small.  The page pool's layout is the resident one (ice_index_layout's
+ * pool_k and pool_v become byte offsets into host_pool; with offload 2
+ * pool_k stays a workspace offset). */
 size_t ice_host_pool_bytes(const ice_params *prm, int32_t n_streams, int64_t n_tokens,
                            int64_t capacity_tokens);
 ice_status ice_build_index_offload(const ice_params *prm, int32_t n_streams, int64_t n_tokens,
@@ -301,7 +307,8 @@ const char *ice_status_string(ice_status s);
  *   pool_k        dtype   [S][Pcap][p][d]  key of each page slot
  *   pool_v        dtype   [S][Pcap][d][p]  values, element-major inside a
  *                 page (value element e of slot j at [e][j]); with offload
- *                 set, both are offsets into the host pool, not the workspace
+ *                 1 both are offsets into the host pool, not the workspace
+ *                 (offload 2: pool_v only)
  *   qcode         int32   [S][G][mL]     last query's projection codes (G = g
  *                 in the GQA max mode, one set per head; else 1)
  *   cand          int32   [S][Lq][k0]    last query's candidates per walk (Lq =

@@ -115,8 +115,8 @@ def make_params(d, page_size, budget_k, m, L, gqa_group=1, k0=0, k1=0, tree_dept
                 dtype=torch.bfloat16, gqa_mode="mean", offload=False) -> IceParams:
     dt = {torch.float32: ICE_F32, torch.bfloat16: ICE_BF16}[dtype]
     gm = {"mean": ICE_GQA_MEAN, "max": ICE_GQA_MAX}[gqa_mode]
-    return IceParams(d, page_size, budget_k, m, L, gqa_group, k0, k1, tree_depth, c, dt, gm,
-                     1 if offload else 0)
+    mode = 2 if offload == "values" else (1 if offload else 0)
+    return IceParams(d, page_size, budget_k, m, L, gqa_group, k0, k1, tree_depth, c, dt, gm, mode)
 
 
 STATS_MAX_L = 32
@@ -177,7 +177,8 @@ class Index:
                  tree_depth=0, c=0.0, capacity=None, stream=None, noalloc=False,
                  gqa_mode="mean", offload=False):
         """offload: keep the page pool in a pinned host tensor (self.host_pool)
-        instead of the workspace (ice_build_index_offload)."""
+        instead of the workspace (ice_build_index_offload); "values": only its
+        value pages there, the key pages in the workspace."""
         _dev_tensor(K, "K", ndim=3)
         _dev_tensor(V, "V", K.dtype, 3)
         _dev_tensor(dirs, "dirs", K.dtype, 2)
@@ -380,8 +381,8 @@ class Index:
         for s_ in shape:
             count *= s_
         base = self.workspace
-        if name in ("pool_k", "pool_v") and y["offload"]:  # offsets into the host pool
-            base = self.host_pool
+        if y["offload"] and (name == "pool_v" or (name == "pool_k" and y["offload"] == 1)):
+            base = self.host_pool  # offsets into the host pool
         raw = base[off:off + count * nbytes]
         t = raw.view(dt).view(shape)
         if name == "codes":  # tiles of 64 tokens -> [S][ncap][mL] (a copy)

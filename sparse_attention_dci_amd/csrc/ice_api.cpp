@@ -118,7 +118,7 @@ ice_status check_params(const ice_params *prm, int32_t S, int64_t n, int64_t nca
   if (!(prm->c >= 0.0f) || std::isinf(prm->c)) return ICE_ERR_INVALID_ARG;
   if (prm->dtype != ICE_F32 && prm->dtype != ICE_BF16) return ICE_ERR_INVALID_ARG;
   if (prm->gqa_mode != ICE_GQA_MEAN && prm->gqa_mode != ICE_GQA_MAX) return ICE_ERR_INVALID_ARG;
-  if (prm->offload != 0 && prm->offload != 1) return ICE_ERR_INVALID_ARG;
+  if (prm->offload < 0 || prm->offload > 2) return ICE_ERR_INVALID_ARG;
   if (S < 1 || n < 0 || ncap < n || ncap < 1 || ncap > 0x7fffffffLL - 1)
     return ICE_ERR_INVALID_ARG;
   if (prm->L > 32) return ICE_ERR_UNSUPPORTED;
@@ -174,7 +174,9 @@ ice_status make_layout(const ice_params *prm, int32_t S, int64_t n, int64_t ncap
   y.cell_count = seg(Sl * y.ncell * 4);
   y.cell_last = seg(Sl * y.ncell * 4);
   if (prm->offload) {  // the pool is in host memory; P staged pages per stream here
-    y.pool_k = y.pool_v = -1;
+    // (offload 2: the keys stay here, only the values are in host memory)
+    y.pool_k = prm->offload == 2 ? seg(Sl * y.pcap * p * d * y.elem) : -1;
+    y.pool_v = -1;
     const int64_t P = prm->budget_k / p;
     y.stage_k = seg(Sl * P * p * d * y.elem);
     y.stage_v = seg(Sl * P * p * d * y.elem);
@@ -229,9 +231,15 @@ int64_t scratch_offsets(const ice_params *prm, int32_t S, int64_t n, int64_t off
   return o;
 }
 
-// The offloaded pool in host memory: pool_k at 0, pool_v at *off_v; returns the total.
+// The offloaded pool in host memory: pool_k at 0, pool_v at *off_v (offload 1),
+// or pool_v alone at 0 (offload 2: the keys stay in the workspace); returns the
+// total.
 int64_t host_pool_layout(const Layout &y, const ice_params *prm, int32_t S, int64_t *off_v) {
   const int64_t one = (int64_t)S * y.pcap * prm->page_size * prm->head_dim * y.elem;
+  if (prm->offload == 2) {
+    *off_v = 0;
+    return align_up(one);
+  }
   *off_v = align_up(one);
   return align_up(*off_v + one);
 }
@@ -378,7 +386,7 @@ ice_status build_common(const ice_params *prm, int32_t n_streams, int64_t n_toke
   if (prm->offload) {
     int64_t off_v = 0;
     host_pool_layout(y, prm, n_streams, &off_v);
-    dv.pool_k = pool_dev;
+    dv.pool_k = prm->offload == 2 ? w + y.pool_k : pool_dev;
     dv.pool_v = pool_dev + off_v;
     dv.stage_k = w + y.stage_k;
     dv.stage_v = w + y.stage_v;
@@ -683,10 +691,10 @@ ice_status ice_index_layout(const ice_index *idx, ice_layout *out) {
   out->page_cell = y.page_cell;
   out->npages = y.npages;
   out->cell_count = y.cell_count;
-  if (idx->prm.offload) {  // offsets into the host pool
+  if (idx->prm.offload) {  // offsets into the host pool (offload 2: pool_k in the workspace)
     int64_t off_v = 0;
     host_pool_layout(y, &idx->prm, idx->S, &off_v);
-    out->pool_k = 0;
+    out->pool_k = idx->prm.offload == 2 ? y.pool_k : 0;
     out->pool_v = off_v;
   } else {
     out->pool_k = y.pool_k;

@@ -217,9 +217,10 @@ def test_gqa_mode_rules(L):
 
 
 def test_offload_entry_rules(L):
-    """The offloaded pool: ice_build_index refuses offload = 1 and the offload
-    entry refuses offload = 0; a missing or short host pool is a workspace
-    error, all before any HIP call; the workspace then holds no pool."""
+    """The offloaded pool: ice_build_index refuses offload = 1 and 2 and the
+    offload entry refuses offload = 0; a missing or short host pool is a
+    workspace error, all before any HIP call; the workspace then holds no pool
+    (offload 1) or the key pages alone (offload 2, half the host pool)."""
     h = ctypes.c_void_p()
     off = good(offload=True)
     res = good()
@@ -238,6 +239,17 @@ def test_offload_entry_rules(L):
         st = L.ice_build_index_offload(ctypes.byref(off), 8, 1000, 1000, FAKE, FAKE, FAKE, FAKE,
                                        1 << 40, FAKE, 1 << 40, pool, nbytes, None, ctypes.byref(h))
         assert st == B.ICE_ERR_WORKSPACE and not h.value
+    # offload 2: the values alone in host memory (half the host pool), the keys
+    # in the workspace; ice_build_index refuses it too
+    vo = good(offload="values")
+    assert vo.offload == 2
+    hv = L.ice_host_pool_bytes(ctypes.byref(vo), 8, 36864, 36864)
+    assert hv * 2 >= hp - 512 and hv * 2 <= hp + 512
+    assert (L.ice_workspace_bytes(ctypes.byref(vo), 8, 36864, 36864)
+            - L.ice_workspace_bytes(ctypes.byref(off), 8, 36864, 36864)) >= hv - 256
+    st = L.ice_build_index(ctypes.byref(vo), 8, 1000, 1000, FAKE, FAKE, FAKE, FAKE, 1 << 40, FAKE,
+                           1 << 40, None, ctypes.byref(h))
+    assert st == B.ICE_ERR_INVALID_ARG and not h.value
     bad = good(offload=True)
-    bad.offload = 2
+    bad.offload = 3
     assert L.ice_workspace_bytes(ctypes.byref(bad), 8, 1000, 1000) == 0

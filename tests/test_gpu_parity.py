@@ -1263,11 +1263,16 @@ def test_gqa_max_llama8b_layer_36k(B):
     dict(S=2, n=9000, g=2, p=16, k=1024, m=4, L=3, gqa="mean", dtype="bf16"),  # four splits
     dict(S=2, n=5000, g=4, p=16, k=256, m=8, L=4, gqa="max", dtype="bf16"),
     dict(S=2, n=3000, g=2, p=8, k=128, m=3, L=3, gqa="mean", dtype="f32", d=64),
+    # the values alone in host memory, the keys resident
+    dict(S=4, n=6000, g=4, p=16, k=256, m=8, L=4, gqa="mean", dtype="bf16", mode="values"),
+    dict(S=2, n=9000, g=2, p=16, k=1024, m=4, L=3, gqa="mean", dtype="bf16", mode="values"),
+    dict(S=2, n=3000, g=2, p=8, k=128, m=3, L=3, gqa="max", dtype="f32", d=64, mode="values"),
 ])
 def test_offloaded_pool_equals_resident(B, case):
-    """The page pool in pinned host memory: builds, inserts and decode steps
-    write it over the host link, the rerank reads its key rows there, and the
-    selected pages are staged in HBM for the attention.  Every index array,
+    """The page pool in pinned host memory (or its values alone, the keys
+    resident): builds, inserts and decode steps write it over the host link,
+    the rerank reads its key rows there (or in HBM), and the selected pages
+    are staged in HBM for the attention.  Every index array,
     page, top-k and attention output equals the resident pool's bit for bit,
     step after step; the last step also against the oracle."""
     c = dict(d=128)
@@ -1279,10 +1284,11 @@ def test_offloaded_pool_equals_resident(B, case):
     print(f"[case] offload {case}", flush=True)
     kw = dict(page_size=c["p"], budget_k=c["k"], m=c["m"], L=c["L"], gqa_group=g,
               capacity=n + steps + 2, gqa_mode=c["gqa"])
-    a = B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U, offload=True,
+    mode = c.get("mode", True)
+    a = B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U, offload=mode,
                 **kw)
     b = B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U, **kw)
-    assert a.layout()["offload"] == 1 and b.layout()["offload"] == 0
+    assert a.layout()["offload"] == (2 if mode == "values" else 1) and b.layout()["offload"] == 0
     gen = torch.Generator().manual_seed(31)
     td = W.torch_dtype(c["dtype"])
     for t in range(steps):
