@@ -150,7 +150,7 @@ ice_status make_layout(const ice_params *prm, int32_t S, int64_t n, int64_t ncap
   y.attn_nsplit = (prm->budget_k + ice::kAttnTpb - 1) / ice::kAttnTpb;
   const int64_t Sl = S, g = prm->gqa_group;
   const int64_t Gq = prm->gqa_mode == ICE_GQA_MAX ? g : 1;
-  const int64_t Lb = prm->L, Ll = prm->L * Gq;  // a pass's walks; all walks of a query
+  const int64_t Ll = prm->L * Gq;  // all walks of a query
   int64_t o = 0;
   auto seg = [&](int64_t bytes) {
     int64_t at = o;
@@ -188,7 +188,7 @@ ice_status make_layout(const ice_params *prm, int32_t S, int64_t n, int64_t ncap
   }
   y.qkv = seg(Sl * Gq * d * 4);
   y.qcode = seg(Sl * Gq * mL * 4);
-  y.mbuf = seg(Sl * Lb * ncap * 4);
+  y.mbuf = seg(Sl * Ll * ncap * 4);
   y.hist = seg(Sl * Ll * ice::kHistBins * 4);
   y.hist2 = seg(Sl * Ll * ice::kHistBins * 4);
   y.cand = seg(Sl * Ll * y.k0 * 4);

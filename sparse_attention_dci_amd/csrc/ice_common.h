@@ -89,7 +89,7 @@ struct Dev {
   // per-query state (walks: Lq per stream)
   float *qkv;            // [S][Gq][d]
   int32_t *qcode;        // [S][Gq][mL]
-  uint32_t *mbuf;        // [S][L][ncap] one pass of L walks
+  uint32_t *mbuf;        // [S][Lq][ncap] every walk of a query (all passes)
   uint32_t *hist;        // [S][Lq][kHistBins]
   uint32_t *hist2;       // [S][Lq][kHistBins] second level: the boundary bin's next 11 bits
   int32_t *cand;         // [S][Lq][k0]

@@ -144,26 +144,36 @@ __device__ __forceinline__ int32_t ld_code(__amdgpu_buffer_rsrc_t r, uint32_t of
 constexpr int kPipe = 16;
 
 //
-// GQA max mode: pass `head` walks the L composites with that head's own query
-// (its row of q alone) and fills walks head * L .. head * L + L - 1 of the
-// stream's query arrays; the mean mode has one pass, head 0.
-template <int DT, bool LDS_HIST, int R, int NT>
+// GQA max mode: the blocks of pass `head` (the grid holds every head's pass)
+// walk the L composites with that head's own query (its row of q alone) and
+// fill walks head * L .. head * L + L - 1 of the stream's query arrays; the
+// mean mode has one pass, head 0.  In a decode step the range-0 block of every
+// pass projects the new token for its M values; pass 0's also stores it.
+template <int DT, bool LDS_HIST, int R, int NT, bool MULTI>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_qscan(Dev dv, int64_t n, const void *q,
                                                         const void *k_new, const void *v_new,
-                                                        int head) {
+                                                        int npass) {
   constexpr int kScanTpb = 2 * NT;
   constexpr int W = R * kPipe;  // staged direction columns (>= mL, <= the stored row width)
   constexpr int W4 = W / 4;
   constexpr int kStage = (129 * W4 + NT - 1) / NT;
-  const int S = dv.S, s = blockIdx.x % S;
+  // the GQA max mode's passes share the launch: blocks [h * per, (h + 1) * per)
+  // are head h's (per = S * ranges); the mean mode has one pass, head 0
+  const int S = dv.S;
+  // (MULTI: several passes; else head 0 at compile time)
+  const uint32_t per = MULTI ? gridDim.x / (uint32_t)npass : gridDim.x;
+  const int head = MULTI ? (int)(blockIdx.x / per) : 0;
+  const uint32_t bb0 = blockIdx.x - (uint32_t)head * per;
+  const int s = (int)(bb0 % (uint32_t)S);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int mL = dv.mL, m = dv.m, L = dv.L, d = dv.d, g = dv.g;
-  const int64_t r = blockIdx.x / S;
+  const int64_t r = bb0 / (uint32_t)S;
   const int64_t nold = k_new != nullptr ? n - 1 : n;  // tokens already in the index
   // the blocks of range 0, dispatched first, insert token nold, which keeps
   // the insert off the last blocks' critical path (no short circuit: no
   // branch before the kernel arguments are all requested)
-  const bool ins = (k_new != nullptr) & (r == 0);
+  const bool proj = (k_new != nullptr) & (r == 0);  // every pass's range-0 block projects it
+  const bool ins = proj & (head == 0);                // pass 0's stores it
   // directions: element e < d of direction t at dl[((e / 16) * W + t) * 16 + e % 16]
   // (each lane of a query lane group reads its 16 elements as four 16-byte
   // runs), u_t[d] at ud[t]
@@ -226,7 +236,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_
     for (int j = 0; j < 4; ++j) acc = h0 + j < gq ? __fadd_rn(acc, hv[j]) : acc;
   }
   if (tid < d) qkv[tid] = __fmul_rn(acc, group_inv(gq));
-  if (ins && tid >= 256 && tid < 256 + d) kv[tid - 256] = kx;
+  if (proj && tid >= 256 && tid < 256 + d) kv[tid - 256] = kx;
   lds_barrier();
 
   // the first kEarly codes of both tiles go out before the chains
@@ -261,7 +271,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_
     }
   }
   const int it = NT - 1 - tid;
-  if (ins && it <= mL) {  // element order: one chain through the blocks
+  if (proj && it <= mL) {  // element order: one chain through the blocks
     double z = 0.0;
     for (int j = 0; j < (d >> 4); ++j)
       z = fma16(kv + 16 * j, it < mL ? sm.dl + ((j * W + it) << 4) : kv + 16 * j, z);
@@ -280,7 +290,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_
   }
 
   if (tid < mL) qc[tid] = query_code(zs[tid], qsq_s);
-  if (ins) {
+  if (proj) {
     if (it < mL) nc[it] = insert_code(rs[it], (double)ud[it], ksq_s, ic, ic2);
     if (w == 4) {  // the new token's cell: sign bits of r on the first D directions
       const unsigned long long bal = __ballot(lane < dv.D && rs[lane < mL ? lane : 0] >= 0.0);
@@ -334,7 +344,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_
       b[x] = ld_code(rc, oa + tile_bytes + (t + kPipe) * 256);
     }
     if (t < mL && t == tend) {  // composite l complete (placeholders never are)
-      uint32_t *mrow = dv.mbuf + ((int64_t)s * L + l) * dv.ncap;
+      uint32_t *mrow = dv.mbuf + ((int64_t)s * dv.Lq + lo + l) * dv.ncap;
       if (va) {
         mrow[ia] = (uint32_t)Ma;
         if (LDS_HIST)
@@ -356,14 +366,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_
     }
   }
 
-  if (ins && tid == 0) {  // the new token's M of every composite
+  if (proj && tid == 0) {  // the new token's M of every composite
     for (int l2 = 0; l2 < L; ++l2) {
       int32_t M = 0;
       for (int j = 0; j < m; ++j) {
         const int32_t dd = nc[l2 * m + j] - qc[l2 * m + j];
         M = max(M, max(dd, -dd));
       }
-      dv.mbuf[((int64_t)s * L + l2) * dv.ncap + nold] = (uint32_t)M;
+      dv.mbuf[((int64_t)s * dv.Lq + lo + l2) * dv.ncap + nold] = (uint32_t)M;
       if (LDS_HIST)
         atomicAdd(&hist[l2 * kHistBins + (M >> kHistShift)], 1u);
       else
@@ -426,14 +436,19 @@ struct CollectShape {
 };
 
 //
-// GQA max mode: pass `head` serves walks head * L + l; every candidate is
-// scored against all g heads (read from q) and ranked by the largest score.
+// GQA max mode: the blocks of pass `head` (the grid holds every head's pass)
+// serve walks head * L + l; every candidate is scored against all g heads
+// (read from q) and ranked by the largest score.
 template <int DT, int NT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape<NT>::kWavesPerEu))) void k_qcollect(
-    Dev dv, int64_t n, bool bounded, int head, const void *q) {
+    Dev dv, int64_t n, bool bounded, const void *q, int npass) {
   constexpr int kScanThreads = NT, kScanTpb = 2 * NT;
-  const int s = blockIdx.x % dv.S;  // the scan's block-to-stream mapping
-  const int64_t rng = blockIdx.x / dv.S;
+  // the scan's block mapping: head h's pass, stream, range
+  const uint32_t per = npass > 1 ? gridDim.x / (uint32_t)npass : gridDim.x;
+  const int head = npass > 1 ? (int)(blockIdx.x / per) : 0;
+  const uint32_t bb0 = blockIdx.x - (uint32_t)head * per;
+  const int s = (int)(bb0 % (uint32_t)dv.S);
+  const int64_t rng = bb0 / (uint32_t)dv.S;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int L = dv.L, Lq = dv.Lq, lo = head * L;
   const int nq = dv.gmax ? dv.g : 1;  // query vectors a candidate is scored against
@@ -476,7 +491,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
     const int64_t ic = vv[u] ? ii[u] : 0;
 #pragma unroll
     for (int l = 0; l < 8; ++l)
-      Mv[u][l] = l < L ? dv.mbuf[((int64_t)s * L + l) * dv.ncap + ic] : 0u;
+      Mv[u][l] = l < L ? dv.mbuf[((int64_t)s * Lq + lo + l) * dv.ncap + ic] : 0u;
     lc[u] = dv.loc[(int64_t)s * dv.ncap + ic];
   }
   auto Mof = [&](int u, int l) -> uint32_t {
@@ -486,7 +501,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
       for (int x = 0; x < 8; ++x)
         if (x == l) M = Mv[u][x];
     } else {
-      M = dv.mbuf[((int64_t)s * L + l) * dv.ncap + (vv[u] ? ii[u] : 0)];
+      M = dv.mbuf[((int64_t)s * Lq + lo + l) * dv.ncap + (vv[u] ? ii[u] : 0)];
     }
     return M;
   };
@@ -639,7 +654,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
         // than keep its registers over the scoring, which would spill them
         uint32_t Mx;
         if constexpr (NT == 512)
-          Mx = dv.mbuf[((int64_t)s * L + l) * dv.ncap + iu];
+          Mx = dv.mbuf[((int64_t)s * Lq + lo + l) * dv.ncap + iu];
         else
           Mx = Mof(u, l);
         dv.bnd[o] = ((unsigned long long)Mx << 32) | (uint32_t)i;
@@ -1738,50 +1753,54 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
 
 template <int DT, bool LH, int R, int NT>
 static void launch_scan(const Dev &dv, int64_t n, unsigned grid, const void *q, const void *k_new,
-                        const void *v_new, int head, hipStream_t st) {
-  hipLaunchKernelGGL((k_qscan<DT, LH, R, NT>), dim3(grid), dim3(NT), 0, st, dv, n, q, k_new,
-                     v_new, head);
+                        const void *v_new, hipStream_t st) {
+  if (dv.Gq > 1)
+    hipLaunchKernelGGL((k_qscan<DT, LH, R, NT, true>), dim3(grid), dim3(NT), 0, st, dv, n, q,
+                       k_new, v_new, dv.Gq);
+  else
+    hipLaunchKernelGGL((k_qscan<DT, LH, R, NT, false>), dim3(grid), dim3(NT), 0, st, dv, n, q,
+                       k_new, v_new, 1);
 }
 
 template <int DT, bool LH, int NT>
 static void launch_scan_r(const Dev &dv, int64_t n, unsigned grid, const void *q,
-                          const void *k_new, const void *v_new, int head, hipStream_t st) {
+                          const void *k_new, const void *v_new, hipStream_t st) {
   switch ((dv.mL + kPipe - 1) / kPipe) {
-    case 1: launch_scan<DT, LH, 1, NT>(dv, n, grid, q, k_new, v_new, head, st); break;
-    case 2: launch_scan<DT, LH, 2, NT>(dv, n, grid, q, k_new, v_new, head, st); break;
-    case 3: launch_scan<DT, LH, 3, NT>(dv, n, grid, q, k_new, v_new, head, st); break;
-    case 4: launch_scan<DT, LH, 4, NT>(dv, n, grid, q, k_new, v_new, head, st); break;
-    case 5: launch_scan<DT, LH, 5, NT>(dv, n, grid, q, k_new, v_new, head, st); break;
-    case 6: launch_scan<DT, LH, 6, NT>(dv, n, grid, q, k_new, v_new, head, st); break;
-    case 7: launch_scan<DT, LH, 7, NT>(dv, n, grid, q, k_new, v_new, head, st); break;
-    default: launch_scan<DT, LH, 8, NT>(dv, n, grid, q, k_new, v_new, head, st); break;  // mL <= 128
+    case 1: launch_scan<DT, LH, 1, NT>(dv, n, grid, q, k_new, v_new, st); break;
+    case 2: launch_scan<DT, LH, 2, NT>(dv, n, grid, q, k_new, v_new, st); break;
+    case 3: launch_scan<DT, LH, 3, NT>(dv, n, grid, q, k_new, v_new, st); break;
+    case 4: launch_scan<DT, LH, 4, NT>(dv, n, grid, q, k_new, v_new, st); break;
+    case 5: launch_scan<DT, LH, 5, NT>(dv, n, grid, q, k_new, v_new, st); break;
+    case 6: launch_scan<DT, LH, 6, NT>(dv, n, grid, q, k_new, v_new, st); break;
+    case 7: launch_scan<DT, LH, 7, NT>(dv, n, grid, q, k_new, v_new, st); break;
+    default: launch_scan<DT, LH, 8, NT>(dv, n, grid, q, k_new, v_new, st); break;  // mL <= 128
   }
 }
 
-// Scan and collect over n tokens with NT-thread blocks of 2 * NT tokens: one
-// pass per head in the GQA max mode (the first one inserts the new token).
+// Scan and collect over n tokens with NT-thread blocks of 2 * NT tokens.  The
+// GQA max mode's passes (one per head) share each launch: the scan's grid
+// holds every head's blocks, then the visit-budget passes run per head, then
+// one collect covers every head's walks.
 template <int DT, int NT>
 static void scan_collect(const Dev &dv, int64_t n, bool bounded, uint32_t k1, const void *q,
                          const void *k_new, const void *v_new, hipStream_t st, Timer *tm) {
   const int64_t nrange = (n + 2 * NT - 1) / (2 * NT);
-  const unsigned grid = (unsigned)(max(nrange, (int64_t)1) * dv.S);
-  for (int head = 0; head < dv.Gq; ++head) {
-    const void *kn = head == 0 ? k_new : nullptr, *vn = head == 0 ? v_new : nullptr;
-    if (dv.L <= 6)
-      launch_scan_r<DT, true, NT>(dv, n, grid, q, kn, vn, head, st);
-    else
-      launch_scan_r<DT, false, NT>(dv, n, grid, q, kn, vn, head, st);
-    timer_mark(tm, KID_QSCAN, st);
-    if (bounded) {
+  const unsigned grid = (unsigned)(max(nrange, (int64_t)1) * dv.S * dv.Gq);
+  if (dv.L <= 6)
+    launch_scan_r<DT, true, NT>(dv, n, grid, q, k_new, v_new, st);
+  else
+    launch_scan_r<DT, false, NT>(dv, n, grid, q, k_new, v_new, st);
+  timer_mark(tm, KID_QSCAN, st);
+  if (bounded) {
+    for (int head = 0; head < dv.Gq; ++head)
       (void)launch_visit_budget(dv, n, k1, head, st);  // a launch error stays for the caller's check
-      timer_mark(tm, KID_VISIT, st);
-    }
-    if (n > 0) {
-      const size_t qbytes = (size_t)(dv.gmax ? dv.g : 1) * 128 * sizeof(float);
-      hipLaunchKernelGGL((k_qcollect<DT, NT>), dim3(grid), dim3(NT), qbytes, st, dv, n, bounded,
-                         head, q);
-      timer_mark(tm, KID_QCOLLECT, st);
-    }
+    timer_mark(tm, KID_VISIT, st);
+  }
+  if (n > 0) {
+    const size_t qbytes = (size_t)(dv.gmax ? dv.g : 1) * 128 * sizeof(float);
+    hipLaunchKernelGGL((k_qcollect<DT, NT>), dim3(grid), dim3(NT), qbytes, st, dv, n, bounded, q,
+                       dv.Gq);
+    timer_mark(tm, KID_QCOLLECT, st);
   }
 }
 
@@ -1810,7 +1829,7 @@ static void query_tail(const Dev &dv, int64_t n, int64_t k1, int32_t *page_ids,
   // the entries a walk may visit: its budget, else all m * n
   const unsigned long long vlimit = bounded ? (unsigned long long)k1 : (unsigned long long)dv.m * n;
   const int64_t cus = dv.ncu;
-  auto fits = [&](int nt) { return dv.S * ((n + 2 * nt - 1) / (2 * nt)) <= cus; };
+  auto fits = [&](int nt) { return dv.S * dv.Gq * ((n + 2 * nt - 1) / (2 * nt)) <= cus; };
   if (fits(512) || !fits(1024))
     scan_collect<DT, 512>(dv, n, bounded, (uint32_t)k1, q, k_new, v_new, st, tm);
   else if (fits(640))

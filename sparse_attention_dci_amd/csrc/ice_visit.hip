@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kVisitThreads) void k_visit_count(Dev dv, int64_t n
   for (int l = 0; l < L; ++l) {
     const uint32_t *st = dv.vstate + 4 * walk_of(dv, s, head, l);
     const uint32_t ds = st[0], ts = st[2];
-    const uint32_t *mrow = dv.mbuf + ((int64_t)s * L + l) * dv.ncap;
+    const uint32_t *mrow = dv.mbuf + walk_of(dv, s, head, l) * dv.ncap;
     uint32_t c = 0;
     for (int64_t i = i0 + tid; i < i1; i += kVisitThreads) {
       const uint32_t M = mrow[i];
