@@ -157,17 +157,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_
   constexpr int W = R * kPipe;  // staged direction columns (>= mL, <= the stored row width)
   constexpr int W4 = W / 4;
   constexpr int kStage = (129 * W4 + NT - 1) / NT;
-  // the GQA max mode's passes share the launch: blocks [h * per, (h + 1) * per)
-  // are head h's (per = S * ranges); the mean mode has one pass, head 0
+  // grid (S, ranges, passes): the GQA max mode's passes share the launch
+  // (MULTI; else one pass, head 0 at compile time)
   const int S = dv.S;
-  // (MULTI: several passes; else head 0 at compile time)
-  const uint32_t per = MULTI ? gridDim.x / (uint32_t)npass : gridDim.x;
-  const int head = MULTI ? (int)(blockIdx.x / per) : 0;
-  const uint32_t bb0 = blockIdx.x - (uint32_t)head * per;
-  const int s = (int)(bb0 % (uint32_t)S);
+  const int head = MULTI ? (int)blockIdx.z : 0;
+  const int s = (int)blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int mL = dv.mL, m = dv.m, L = dv.L, d = dv.d, g = dv.g;
-  const int64_t r = bb0 / (uint32_t)S;
+  const int64_t r = blockIdx.y;
   const int64_t nold = k_new != nullptr ? n - 1 : n;  // tokens already in the index
   // the blocks of range 0, dispatched first, insert token nold, which keeps
   // the insert off the last blocks' critical path (no short circuit: no
@@ -443,12 +440,10 @@ template <int DT, int NT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape<NT>::kWavesPerEu))) void k_qcollect(
     Dev dv, int64_t n, bool bounded, const void *q, int npass) {
   constexpr int kScanThreads = NT, kScanTpb = 2 * NT;
-  // the scan's block mapping: head h's pass, stream, range
-  const uint32_t per = npass > 1 ? gridDim.x / (uint32_t)npass : gridDim.x;
-  const int head = npass > 1 ? (int)(blockIdx.x / per) : 0;
-  const uint32_t bb0 = blockIdx.x - (uint32_t)head * per;
-  const int s = (int)(bb0 % (uint32_t)dv.S);
-  const int64_t rng = bb0 / (uint32_t)dv.S;
+  // the scan's grid (S, ranges, passes)
+  const int head = (int)blockIdx.z;
+  const int s = (int)blockIdx.x;
+  const int64_t rng = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int L = dv.L, Lq = dv.Lq, lo = head * L;
   const int nq = dv.gmax ? dv.g : 1;  // query vectors a candidate is scored against
@@ -1752,18 +1747,18 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal_big(Dev dv, int64_t n,
 // ---------------------------------------------------------------- launcher
 
 template <int DT, bool LH, int R, int NT>
-static void launch_scan(const Dev &dv, int64_t n, unsigned grid, const void *q, const void *k_new,
+static void launch_scan(const Dev &dv, int64_t n, dim3 grid, const void *q, const void *k_new,
                         const void *v_new, hipStream_t st) {
   if (dv.Gq > 1)
-    hipLaunchKernelGGL((k_qscan<DT, LH, R, NT, true>), dim3(grid), dim3(NT), 0, st, dv, n, q,
-                       k_new, v_new, dv.Gq);
+    hipLaunchKernelGGL((k_qscan<DT, LH, R, NT, true>), grid, dim3(NT), 0, st, dv, n, q, k_new,
+                       v_new, dv.Gq);
   else
-    hipLaunchKernelGGL((k_qscan<DT, LH, R, NT, false>), dim3(grid), dim3(NT), 0, st, dv, n, q,
-                       k_new, v_new, 1);
+    hipLaunchKernelGGL((k_qscan<DT, LH, R, NT, false>), grid, dim3(NT), 0, st, dv, n, q, k_new,
+                       v_new, 1);
 }
 
 template <int DT, bool LH, int NT>
-static void launch_scan_r(const Dev &dv, int64_t n, unsigned grid, const void *q,
+static void launch_scan_r(const Dev &dv, int64_t n, dim3 grid, const void *q,
                           const void *k_new, const void *v_new, hipStream_t st) {
   switch ((dv.mL + kPipe - 1) / kPipe) {
     case 1: launch_scan<DT, LH, 1, NT>(dv, n, grid, q, k_new, v_new, st); break;
@@ -1785,7 +1780,11 @@ template <int DT, int NT>
 static void scan_collect(const Dev &dv, int64_t n, bool bounded, uint32_t k1, const void *q,
                          const void *k_new, const void *v_new, hipStream_t st, Timer *tm) {
   const int64_t nrange = (n + 2 * NT - 1) / (2 * NT);
-  const unsigned grid = (unsigned)(max(nrange, (int64_t)1) * dv.S * dv.Gq);
+  // x: streams (consecutive blocks take different streams, so with S a
+  // multiple of 8 a stream's blocks share an XCD), y: token ranges (at most
+  // 2^22 tokens per stream under the page-capacity limit: 4,096 ranges), z:
+  // passes
+  const dim3 grid((unsigned)dv.S, (unsigned)max(nrange, (int64_t)1), (unsigned)dv.Gq);
   if (dv.L <= 6)
     launch_scan_r<DT, true, NT>(dv, n, grid, q, k_new, v_new, st);
   else
