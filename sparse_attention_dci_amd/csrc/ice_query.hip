@@ -119,10 +119,11 @@ __device__ __forceinline__ int32_t ld_code(__amdgpu_buffer_rsrc_t r, uint32_t of
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, /*nt*/ 2);
 }
 
-// 1-D grid of S * max(1, ceil(n / kScanTpb)) blocks of NT threads.  Block b
-// serves stream b % S (consecutive blocks take different streams, so with S a
-// multiple of 8 all blocks of a stream land on one XCD and share its L2) and
-// the b / S-th range of kScanTpb = 2 * NT tokens: wave w takes tiles 2w and
+// Grid (S, max(1, ceil(n / kScanTpb)), passes) of NT-thread blocks.  Block
+// (s, r, h) serves stream s (consecutive blocks take different streams, so
+// with S a multiple of 8 all blocks of a stream land on one XCD and share its
+// L2), the r-th range of kScanTpb = 2 * NT tokens and the GQA max mode's
+// pass h (the mean mode has one): wave w takes tiles 2w and
 // 2w+1 of the range, lane j token j of a tile, and reads code t of its 64
 // tokens as one contiguous 256-byte load.  kPipe codes of each tile are in
 // flight at a time: every code slot is refilled with the code kPipe places
@@ -525,13 +526,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
       }
     }
   }
+  const int ld = dv.d == 128 ? 7 : 6;  // d is 64 or 128
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int x = tid + kScanThreads * u;
-    if (x < nq * dv.d) qkv[(x / dv.d) * 128 + x % dv.d] = qk[u];
+    if (x < nq * dv.d) qkv[((x >> ld) << 7) + (x & (dv.d - 1))] = qk[u];
   }
   for (int x = tid + 2 * kScanThreads; x < nq * dv.d; x += kScanThreads)  // g * d > 2 * NT
-    qkv[(x / dv.d) * 128 + x % dv.d] =
+    qkv[((x >> ld) << 7) + (x & (dv.d - 1))] =
         load_elem<DT>(q, (int64_t)s * dv.g * dv.d + x);
   lloc[tid] = lc[0];
   lloc[kScanThreads + tid] = lc[1];
