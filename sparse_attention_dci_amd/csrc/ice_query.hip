@@ -34,6 +34,7 @@ namespace ice {
 // layer: 232 blocks of 640 instead of 296 of 512, 52.8 instead of 55.5 us
 // per step), since a CU holding two blocks finishes last.
 constexpr int kFinalThreads = 1024;
+static_assert(kFinalThreads == 1 << 10, "the finaliser splits its threads by shifts");
 constexpr int kHashSlots = 8192;    // 2 * kMaxCand
 constexpr int kBndLds = 2048;       // boundary entries ranked in LDS
 constexpr int kBuckets = 2048;
@@ -828,8 +829,11 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
   }
   const uint32_t kl_ld = bounded && w < L ? dv.vcount[s * L + w] : k0e;
   const uint32_t nrr_ld = dv.rr_count[s];
-  const int per = kFinalThreads / L;  // boundary entries prefetched per composite
-  const int lp = min(tid / per, L - 1);
+  // boundary entries prefetched per composite: kFinalThreads / 2^ceil(log2 L),
+  // so a thread's composite and entry come by shifts
+  const int lgl = L > 1 ? 32 - __builtin_clz((uint32_t)(L - 1)) : 0;
+  const int per = kFinalThreads >> lgl;
+  const int lp = min(tid >> (10 - lgl), L - 1);
   const uint32_t ep = (uint32_t)(tid - lp * per);
   const uint32_t nbp = dv.bnd_count[s * L + lp];
   uint32_t cc_ld = 0, nb_ld = 0;
