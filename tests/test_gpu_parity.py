@@ -485,14 +485,15 @@ def test_decode_step_equals_separate_calls(B, dtype, S, g, d, p, m, L, k, n):
     assert e.value.status == B.ICE_ERR_CAPACITY
 
 
-@pytest.mark.parametrize("dtype,g,d,p,k,k0", [
-    ("bf16", 4, 128, 16, 256, 0),   # the 36k layer's shape: 16 pages
-    ("f32", 2, 64, 8, 128, 0),      # 16 pages of 8
-    ("bf16", 2, 128, 8, 256, 0),    # 32 pages of 8: the largest selection waves walk alone
-    ("bf16", 2, 128, 32, 256, 0),   # 8 pages of 32
-    ("bf16", 1, 128, 16, 256, 6),   # a union of at most 24 tokens: fewer pages than 16
+@pytest.mark.parametrize("dtype,g,d,p,k,k0,gqa", [
+    ("bf16", 4, 128, 16, 256, 0, "mean"),   # the 36k layer's shape: 16 pages
+    ("f32", 2, 64, 8, 128, 0, "mean"),      # 16 pages of 8
+    ("bf16", 2, 128, 8, 256, 0, "mean"),    # 32 pages of 8: the largest selection waves walk alone
+    ("bf16", 2, 128, 32, 256, 0, "mean"),   # 8 pages of 32
+    ("bf16", 1, 128, 16, 256, 6, "mean"),   # a union of at most 24 tokens: fewer pages than 16
+    ("bf16", 4, 128, 16, 256, 0, "max"),    # the GQA max mode (pooled walks of 4 heads)
 ])
-def test_decode_step_without_topk_equals_with(B, dtype, g, d, p, k, k0):
+def test_decode_step_without_topk_equals_with(B, dtype, g, d, p, k, k0, gqa):
     """ice_decode_step without a top-k output (the fused attention's waves
     then walk the first 64 ranks for themselves when those hold the whole
     selection) gives the pages and the attention of the same step with the
@@ -502,10 +503,10 @@ def test_decode_step_without_topk_equals_with(B, dtype, g, d, p, k, k0):
     dev = torch.device("cuda")
     K, V, _, _ = _inputs(S, n + steps, d, g, 24, 47, dtype)
     U = W.directions(m * L, d, 47, dtype).to(dev)
-    print(f"[case] decode without top-k {dtype} g={g} d={d} p={p} k={k} k0={k0}", flush=True)
+    print(f"[case] decode without top-k {dtype} g={g} d={d} p={p} k={k} k0={k0} {gqa}", flush=True)
     mk = lambda: B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U,
                          page_size=p, budget_k=k, m=m, L=L, gqa_group=g, k0=k0,
-                         capacity=n + steps)
+                         capacity=n + steps, gqa_mode=gqa)
     a, b = mk(), mk()
     gen = torch.Generator().manual_seed(9)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -519,7 +520,7 @@ def test_decode_step_without_topk_equals_with(B, dtype, g, d, p, k, k0):
         for s in range(S):
             assert torch.equal(pa[s, :int(na[s])], pb[s, :int(nb[s])])
         assert torch.equal(oa, ob)
-    prm = oracle.Params(d=d, p=p, k=k, m=m, L=L, g=g, k0=k0)
+    prm = oracle.Params(d=d, p=p, k=k, m=m, L=L, g=g, k0=k0, gqa_max=gqa == "max")
     st = oracle.OracleStream(prm, _np(K[1, :n]), _np(V[1, :n]), _np(U), n_cap=n + steps)
     for t in range(steps):
         st.insert(_np(K[1, n + t]), _np(V[1, n + t]))
