@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libice.so")
 SOURCES = ["ice_api.cpp", "ice_build.hip", "ice_insert.hip", "ice_query.hip", "ice_attn.hip",
-           "ice_visit.hip", "ice_stats.hip", "ice_merge.hip"]
+           "ice_visit.hip", "ice_stats.hip", "ice_merge.hip", "ice_scan_heads.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -23,8 +23,10 @@
 //               bucket sort by (score desc, token asc), top-k and the page
 //               walk; it leaves a clean histogram for the next query (and
 //               k_qfinal_big does the same for unions above kMaxCand).
+#include <type_traits>
+
 #include "ice_attn_dev.h"
-#include "ice_step_dev.h"
+#include "ice_scan_dev.h"
 
 namespace ice {
 
@@ -106,313 +108,6 @@ __device__ void block_score(const Dev &dv, int s, uint32_t cnt, SlotOf slot_of, 
   }
 }
 
-// ---------------------------------------------------------------- scan
-
-// Buffer resource over a byte range: loads past its end return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
-// Codes are read once per query: non-temporal (nt), so the stream does not
-// push the rest of the step's working set (and the kernels' code) out of L2.
-__device__ __forceinline__ int32_t ld_code(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, /*nt*/ 2);
-}
-
-// Grid (S, max(1, ceil(n / kScanTpb)), passes) of NT-thread blocks.  Block
-// (s, r, h) serves stream s (consecutive blocks take different streams, so
-// with S a multiple of 8 all blocks of a stream land on one XCD and share its
-// L2), the r-th range of kScanTpb = 2 * NT tokens and the GQA max mode's
-// pass h (the mean mode has one): wave w takes tiles 2w and
-// 2w+1 of the range, lane j token j of a tile, and reads code t of its 64
-// tokens as one contiguous 256-byte load.  kPipe codes of each tile are in
-// flight at a time: every code slot is refilled with the code kPipe places
-// later right after it is used.  R = ceil(mL / kPipe) is a template
-// parameter, so the walk over code positions is straight-line code and every
-// wait covers exactly the loads it needs.  The histogram lives in LDS when
-// L <= 6, and only the bins at or below the block's own k0-th bin are added to
-// the global one; with L > 6 every count goes straight to global.
-//
-// Every block first derives the query codes itself (the directions staged in
-// LDS, the arithmetic of ice_step_dev.h), so no prep kernel sits on the
-// query's critical path; the blocks of range 0 publish q_kv and the codes for
-// the later kernels and clear the query's counters.  In a decode step (k_new
-// given) token n - 1 is the new token: the block whose range holds it leaves
-// it out of its code walk, and the block of range 0 (dispatched first, so the
-// insert is off the critical path of the last blocks) projects it on the
-// same staged directions, adds its M values to its own histogram and writes
-// its codes, list entries, page and pool rows at the end.
-constexpr int kPipe = 16;
-
-//
-// GQA max mode: the blocks of pass `head` (the grid holds every head's pass)
-// walk the L composites with that head's own query (its row of q alone) and
-// fill walks head * L .. head * L + L - 1 of the stream's query arrays; the
-// mean mode has one pass, head 0.  In a decode step the range-0 block of every
-// pass projects the new token for its M values; pass 0's also stores it.
-template <int DT, bool LDS_HIST, int R, int NT, bool MULTI>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void k_qscan(Dev dv, int64_t n, const void *q,
-                                                        const void *k_new, const void *v_new,
-                                                        int npass) {
-  constexpr int kScanTpb = 2 * NT;
-  constexpr int W = R * kPipe;  // staged direction columns (>= mL, <= the stored row width)
-  constexpr int W4 = W / 4;
-  constexpr int kStage = (129 * W4 + NT - 1) / NT;
-  // grid (S, ranges, passes): the GQA max mode's passes share the launch
-  // (MULTI; else one pass, head 0 at compile time)
-  const int S = dv.S;
-  const int head = MULTI ? (int)blockIdx.z : 0;
-  const int s = (int)blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int mL = dv.mL, m = dv.m, L = dv.L, d = dv.d, g = dv.g;
-  const int64_t r = blockIdx.y;
-  const int64_t nold = k_new != nullptr ? n - 1 : n;  // tokens already in the index
-  // the blocks of range 0, dispatched first, insert token nold, which keeps
-  // the insert off the last blocks' critical path (no short circuit: no
-  // branch before the kernel arguments are all requested)
-  const bool proj = (k_new != nullptr) & (r == 0);  // every pass's range-0 block projects it
-  const bool ins = proj & (head == 0);                // pass 0's stores it
-  // directions: element e < d of direction t at dl[((e / 16) * W + t) * 16 + e % 16]
-  // (each lane of a query lane group reads its 16 elements as four 16-byte
-  // runs), u_t[d] at ud[t]
-  union __attribute__((aligned(16))) ScanShared {
-    uint32_t hist[LDS_HIST ? 6 * kHistBins : 1];
-    float dl[128 * W];
-  };
-  __shared__ ScanShared sm;
-  __shared__ float ud[W];
-  __shared__ int32_t qc[kMaxMl], nc[kMaxMl];
-  __shared__ uint32_t blim[6];
-  __shared__ __attribute__((aligned(16))) float qkv[128], kv[128];
-  __shared__ double zs[kMaxMl], rs[kMaxMl];
-  __shared__ double qsq_s, ksq_s;
-  __shared__ uint32_t cell_s;
-  __shared__ int32_t loc_s;
-  const int lo = head * L;                          // this pass's first walk
-  const int gq = dv.gmax ? 1 : g;                     // heads folded into this pass's query
-  const int64_t qr0 = (int64_t)s * g + (dv.gmax ? head : 0);  // its first row of q
-  uint32_t *ghist = dv.hist + ((int64_t)s * dv.Lq + lo) * kHistBins;
-
-  // 1. the prep's loads, every one issued before any is used (clamped
-  // addresses, no branches): the directions, heads 0..3 of element tid, the
-  // new key (any valid address when there is none), the insert's scalars
-  const int tot4 = (d + 1) * W4;
-  float4 st4[kStage];
-#pragma unroll
-  for (int k = 0; k < kStage; ++k) {
-    const int x = min(tid + NT * k, tot4 - 1);
-    st4[k] = *reinterpret_cast<const float4 *>(dv.dirs32 + (int64_t)(x / W4) * dv.mLp +
-                                               (x % W4) * 4);
-  }
-  const int te = min(tid & 127, d - 1);
-  float hv[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) hv[j] = load_elem<DT>(q, (qr0 + min(j, gq - 1)) * d + te);
-  const float kx = load_elem<DT>(k_new != nullptr ? k_new : q, (int64_t)s * d + te);
-  const int32_t np0 = dv.npages[s];
-  const double ic = dv.inv_c[s], ic2 = dv.inv_c2[s];
-#pragma unroll
-  for (int k = 0; k < kStage; ++k) {
-    const int x = tid + NT * k;
-    const int e = x / W4, t0 = (x % W4) * 4;
-    const float c4[4] = {st4[k].x, st4[k].y, st4[k].z, st4[k].w};
-    if (e < d) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) sm.dl[((((e >> 4) * W) + t0 + c) << 4) + (e & 15)] = c4[c];
-    } else if (e == d) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) ud[t0 + c] = c4[c];
-    }
-  }
-  float acc = hv[0];  // left fold of the heads
-#pragma unroll
-  for (int j = 1; j < 4; ++j) acc = j < gq ? __fadd_rn(acc, hv[j]) : acc;
-  for (int h0 = 4; h0 < gq; h0 += 4) {  // groups above 4
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hv[j] = load_elem<DT>(q, (qr0 + min(h0 + j, gq - 1)) * d + te);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc = h0 + j < gq ? __fadd_rn(acc, hv[j]) : acc;
-  }
-  if (tid < d) qkv[tid] = __fmul_rn(acc, group_inv(gq));
-  if (proj && tid >= 256 && tid < 256 + d) kv[tid - 256] = kx;
-  lds_barrier();
-
-  // the first kEarly codes of both tiles go out before the chains
-  constexpr int kEarly = 8;
-  const uint32_t tile_bytes = (uint32_t)mL * kCodeTile * 4;
-  const __amdgpu_buffer_rsrc_t rc =
-      byte_range(dv.codes + (int64_t)s * dv.ntile * mL * kCodeTile, (uint32_t)dv.ntile * tile_bytes);
-  const uint32_t oa = (uint32_t)(r * (kScanTpb / 64) + 2 * w) * tile_bytes + lane * 4;
-  int32_t a[kPipe], b[kPipe];
-#pragma unroll
-  for (int x = 0; x < kEarly; ++x) {
-    a[x] = ld_code(rc, oa + x * 256);
-    b[x] = ld_code(rc, oa + tile_bytes + x * 256);
-  }
-
-  // the query's dot products in the blocked order: lane group t (d/16 lanes)
-  // is direction t, group mL the norm; the insert's element-order chains run
-  // on the top threads, it = NT-1-tid (r_t for it < mL, |k|^2 for it = mL)
-  {
-    const int nbk = d >> 4, lnb = d == 128 ? 3 : 2;
-    for (int x = tid; x < (mL + 1) * nbk; x += NT) {  // whole lane groups
-      const int t = x >> lnb, j = x & (nbk - 1);
-      const float *b = t < mL ? sm.dl + ((j * W + t) << 4) : qkv + 16 * j;
-      double z = fma16(qkv + 16 * j, b, 0.0);
-      z = tree_sum(z, nbk);
-      if (j == 0) {
-        if (t < mL)
-          zs[t] = z;
-        else
-          qsq_s = z;
-      }
-    }
-  }
-  const int it = NT - 1 - tid;
-  if (proj && it <= mL) {  // element order: one chain through the blocks
-    double z = 0.0;
-    for (int j = 0; j < (d >> 4); ++j)
-      z = fma16(kv + 16 * j, it < mL ? sm.dl + ((j * W + it) << 4) : kv + 16 * j, z);
-    if (it < mL)
-      rs[it] = z;
-    else
-      ksq_s = z;
-  }
-  lds_barrier();
-  // the rest of the first kPipe codes of both tiles (the chains needed the
-  // registers)
-#pragma unroll
-  for (int x = kEarly; x < kPipe; ++x) {
-    a[x] = ld_code(rc, oa + x * 256);
-    b[x] = ld_code(rc, oa + tile_bytes + x * 256);
-  }
-
-  if (tid < mL) qc[tid] = query_code(zs[tid], qsq_s);
-  if (proj) {
-    if (it < mL) nc[it] = insert_code(rs[it], (double)ud[it], ksq_s, ic, ic2);
-    if (w == 4) {  // the new token's cell: sign bits of r on the first D directions
-      const unsigned long long bal = __ballot(lane < dv.D && rs[lane < mL ? lane : 0] >= 0.0);
-      if (lane == 0) cell_s = (uint32_t)bal & ((1u << dv.D) - 1u);
-    }
-  }
-  lds_barrier();
-  if (r == 0) {  // publication and the query's counters (the rerank list's: first pass only)
-    const int64_t hq = (int64_t)s * dv.Gq + (dv.gmax ? head : 0);
-    if (tid < mL) dv.qcode[hq * mL + tid] = qc[tid];
-    if (tid < d) dv.qkv[hq * d + tid] = qkv[tid];
-    if (tid < L) {
-      dv.cand_count[s * dv.Lq + lo + tid] = 0;
-      dv.bnd_count[s * dv.Lq + lo + tid] = 0;
-    }
-    if (tid == 0 && head == 0) dv.rr_count[s] = 0;
-  }
-  if (LDS_HIST) {  // 16-byte stores (the union is 16-byte aligned: float4 staging)
-    uint4 *h4 = reinterpret_cast<uint4 *>(sm.hist);
-    for (int x = tid; x < L * kHistBins / 4; x += NT) h4[x] = make_uint4(0u, 0u, 0u, 0u);
-    lds_barrier();
-  }
-  uint32_t *hist = sm.hist;
-
-  // 2. M per token and composite.  Composite boundaries depend on the code
-  // position only, so every branch but the ragged tail's is uniform.
-  const int64_t i0 = r * kScanTpb, i1 = min(i0 + kScanTpb, n);
-  const uint32_t ntok = (uint32_t)(i1 > i0 ? i1 - i0 : 0);
-  const int64_t ia = i0 + 128 * w + lane, ib = ia + 64;
-  const int64_t iv = min(i1, nold);  // the new token is added after the walk
-  const bool va = ia < iv, vb = ib < iv;
-  int32_t Ma = 0, Mb = 0;
-  int l = 0, tend = m - 1;
-  int32_t qround[kPipe];  // this round's query codes, uniform (scalar registers)
-#pragma unroll
-  for (int t = 0; t < R * kPipe; ++t) {
-    const int x = t % kPipe;
-    if (x == 0) {
-#pragma unroll
-      for (int y = 0; y < kPipe; ++y)
-        qround[y] = __builtin_amdgcn_readfirstlane(qc[min(t + y, kMaxMl - 1)]);
-    }
-    if (t < mL) {
-      const int32_t qv = qround[x];
-      const int32_t da = a[x] - qv, db = b[x] - qv;  // |da| < 2^31: no overflow
-      Ma = max(Ma, max(da, -da));
-      Mb = max(Mb, max(db, -db));
-    }
-    if (t + kPipe < R * kPipe) {
-      a[x] = ld_code(rc, oa + (t + kPipe) * 256);
-      b[x] = ld_code(rc, oa + tile_bytes + (t + kPipe) * 256);
-    }
-    if (t < mL && t == tend) {  // composite l complete (placeholders never are)
-      uint32_t *mrow = dv.mbuf + ((int64_t)s * dv.Lq + lo + l) * dv.ncap;
-      if (va) {
-        mrow[ia] = (uint32_t)Ma;
-        if (LDS_HIST)
-          atomicAdd(&hist[l * kHistBins + (Ma >> kHistShift)], 1u);
-        else
-          atomicAdd(&ghist[l * kHistBins + (Ma >> kHistShift)], 1u);
-      }
-      if (vb) {
-        mrow[ib] = (uint32_t)Mb;
-        if (LDS_HIST)
-          atomicAdd(&hist[l * kHistBins + (Mb >> kHistShift)], 1u);
-        else
-          atomicAdd(&ghist[l * kHistBins + (Mb >> kHistShift)], 1u);
-      }
-      Ma = 0;
-      Mb = 0;
-      ++l;
-      tend += m;
-    }
-  }
-
-  if (proj && tid == 0) {  // the new token's M of every composite
-    for (int l2 = 0; l2 < L; ++l2) {
-      int32_t M = 0;
-      for (int j = 0; j < m; ++j) {
-        const int32_t dd = nc[l2 * m + j] - qc[l2 * m + j];
-        M = max(M, max(dd, -dd));
-      }
-      dv.mbuf[((int64_t)s * dv.Lq + lo + l2) * dv.ncap + nold] = (uint32_t)M;
-      if (LDS_HIST)
-        atomicAdd(&hist[l2 * kHistBins + (M >> kHistShift)], 1u);
-      else
-        atomicAdd(&ghist[l2 * kHistBins + (M >> kHistShift)], 1u);
-    }
-  }
-
-  // 3. flush the block's histogram.  The k0-th smallest M of the stream is
-  // never in a higher bin than the k0-th smallest of a block holding at least
-  // k0 tokens, so every bin up to the global threshold bin still receives
-  // every block's count.
-  if (LDS_HIST) {
-    lds_barrier();
-    for (int l2 = w; l2 < L; l2 += NT / 64) {
-      uint32_t bb = kHistBins - 1, bl;
-      if (ntok >= (uint32_t)dv.k0 && dv.k0 > 0) {  // the low bins first (almost always there)
-        const uint4 v = reinterpret_cast<const uint4 *>(hist + l2 * kHistBins)[lane];
-        if (!wave_find_bin_low(v, dv.k0, bb, bl)) wave_find_bin(hist + l2 * kHistBins, dv.k0, bb, bl);
-      }
-      if (lane == 0) blim[l2] = bb;
-    }
-    lds_barrier();
-    for (int l2 = 0; l2 < L; ++l2) {
-      const int lim = (int)blim[l2];
-      for (int b = tid; b <= lim; b += NT) {
-        const uint32_t h = hist[l2 * kHistBins + b];
-        if (h) atomicAdd(&ghist[l2 * kHistBins + b], h);
-      }
-    }
-  }
-
-  // 4. the insert's stores: codes and list entries, the page rule, the pool
-  if (ins) {
-    if (tid < mL) insert_code_store(dv, s, nold, tid, nc[tid]);
-    if (tid == 0) loc_s = insert_page_rule(dv, s, nold, cell_s, np0);
-    __syncthreads();
-    if (tid < d) insert_pool_store<DT>(dv, s, loc_s, tid, k_new, v_new);
-  }
-}
-
 // ---------------------------------------------------------------- collect
 
 // Blocks of kScanTpb tokens, mapped to streams as in the scan.  Token i is a
@@ -435,19 +130,22 @@ struct CollectShape {
 };
 
 //
-// GQA max mode: the blocks of pass `head` (the grid holds every head's pass)
-// serve walks head * L + l; every candidate is scored against all g heads
-// (read from q) and ranked by the largest score.
-template <int DT, int NT>
+// A block serves every walk of its stream: the L composites, or in the GQA
+// max mode the g * L (head, composite) walks, head h's walks h * L + l.  A
+// token below or at the threshold in several walks is scored once, against
+// all g heads in the max mode (read from q, ranked by the largest score),
+// and enters the rerank list once.  WIDE (more than 8 walks) keeps M of 16
+// walks per token in registers instead of 8.
+template <int DT, int NT, bool WIDE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape<NT>::kWavesPerEu))) void k_qcollect(
-    Dev dv, int64_t n, bool bounded, const void *q, int npass) {
+    Dev dv, int64_t n, bool bounded, const void *q) {
   constexpr int kScanThreads = NT, kScanTpb = 2 * NT;
-  // the scan's grid (S, ranges, passes)
-  const int head = (int)blockIdx.z;
+  constexpr int kMw = WIDE ? 16 : 8;  // walks whose M a thread holds in registers
+  // grid (S, ranges)
   const int s = (int)blockIdx.x;
   const int64_t rng = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int L = dv.L, Lq = dv.Lq, lo = head * L;
+  const int Lq = dv.Lq, nw = Lq;  // the block's walks: all Lq of the stream
   const int nq = dv.gmax ? dv.g : 1;  // query vectors a candidate is scored against
   __shared__ int32_t bstar[32];  // -1: the composite takes no candidates
   __shared__ uint32_t ccount[32], bcount[32], cbase[32], bbase[32];
@@ -473,32 +171,32 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
   // 1. loads: the low bins of wave w's threshold histogram first (distances
   // are far below the code range, so the threshold bin is almost always among
   // them; the whole histogram is read when it is not), M of both tokens for
-  // the first 8 composites, their page slots, the query (unconditional loads
+  // the first kMw walks, their page slots, the query (unconditional loads
   // at clamped addresses)
   uint4 hlow = make_uint4(0u, 0u, 0u, 0u);
   uint32_t klw = k0e;
-  if (w < L) {
-    hlow = wave_hist_load_low(dv.hist + ((int64_t)s * Lq + lo + w) * kHistBins);
-    if (bounded) klw = min(k0e, dv.vcount[s * Lq + lo + w]);
+  if (w < nw) {
+    hlow = wave_hist_load_low(dv.hist + ((int64_t)s * Lq + w) * kHistBins);
+    if (bounded) klw = min(k0e, dv.vcount[s * Lq + w]);
   }
-  uint32_t Mv[2][8];
+  uint32_t Mv[2][kMw];
   int32_t lc[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int64_t ic = vv[u] ? ii[u] : 0;
 #pragma unroll
-    for (int l = 0; l < 8; ++l)
-      Mv[u][l] = l < L ? dv.mbuf[((int64_t)s * Lq + lo + l) * dv.ncap + ic] : 0u;
+    for (int l = 0; l < kMw; ++l)
+      Mv[u][l] = l < nw ? dv.mbuf[((int64_t)s * Lq + l) * dv.ncap + ic] : 0u;
     lc[u] = dv.loc[(int64_t)s * dv.ncap + ic];
   }
   auto Mof = [&](int u, int l) -> uint32_t {
     uint32_t M = 0;
-    if (l < 8) {
+    if (l < kMw) {
 #pragma unroll
-      for (int x = 0; x < 8; ++x)
+      for (int x = 0; x < kMw; ++x)
         if (x == l) M = Mv[u][x];
     } else {
-      M = dv.mbuf[((int64_t)s * Lq + lo + l) * dv.ncap + (vv[u] ? ii[u] : 0)];
+      M = dv.mbuf[((int64_t)s * Lq + l) * dv.ncap + (vv[u] ? ii[u] : 0)];
     }
     return M;
   };
@@ -510,11 +208,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
     qk[u] = dv.gmax ? load_elem<DT>(q, (int64_t)s * dv.g * dv.d + x) : dv.qkv[(int64_t)s * dv.d + x];
   }
   if (k0e == 0) return;  // after the loads: the kernel arguments arrive in one round
-  for (int l = w; l < L; l += kScanThreads / 64) {
-    const uint32_t *hl = dv.hist + ((int64_t)s * Lq + lo + l) * kHistBins;
+  for (int l = w; l < nw; l += kScanThreads / 64) {
+    const uint32_t *hl = dv.hist + ((int64_t)s * Lq + l) * kHistBins;
     uint32_t kl = klw;
     if (l != w) {  // more composites than waves
-      kl = bounded ? min(k0e, dv.vcount[s * Lq + lo + l]) : k0e;
+      kl = bounded ? min(k0e, dv.vcount[s * Lq + l]) : k0e;
       hlow = wave_hist_load_low(hl);
     }
     uint32_t bb = 0, bl = 0;
@@ -522,8 +220,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
     if (lane == 0) {
       bstar[l] = kl > 0 ? (int32_t)bb : -1;
       if (rng == 0) {  // for the finaliser: b* and the count below it
-        dv.bsel[((int64_t)s * Lq + lo + l) * 2] = bb;
-        dv.bsel[((int64_t)s * Lq + lo + l) * 2 + 1] = bl;
+        dv.bsel[((int64_t)s * Lq + l) * 2] = bb;
+        dv.bsel[((int64_t)s * Lq + l) * 2 + 1] = bl;
       }
     }
   }
@@ -538,7 +236,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
         load_elem<DT>(q, (int64_t)s * dv.g * dv.d + x);
   lloc[tid] = lc[0];
   lloc[kScanThreads + tid] = lc[1];
-  if (tid < L) {
+  if (tid < nw) {
     ccount[tid] = 0;
     bcount[tid] = 0;
   }
@@ -557,23 +255,31 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
     bnd[u] = 0;
     slot[u] = -1;
     if (vv[u]) {
-      for (int l = 0; l < L; ++l) {
-        const uint32_t M = Mof(u, l);
+      auto classify = [&](int l, uint32_t M) {
         const int32_t bb = (int32_t)(M >> kHistShift);
         if (bb < bstar[l]) below[u] |= 1u << l;
         if (bb == bstar[l]) {
           bnd[u] |= 1u << l;
-          atomicAdd(&dv.hist2[((int64_t)s * Lq + lo + l) * kHistBins +
+          atomicAdd(&dv.hist2[((int64_t)s * Lq + l) * kHistBins +
                               ((M >> kSubShift) & (kHistBins - 1))],
                     1u);
         }
+      };
+      if constexpr (WIDE) {  // registers by constant index; walks past 16 from memory
+#pragma unroll
+        for (int l = 0; l < kMw; ++l)
+          if (l < nw) classify(l, Mv[u][l]);
+        for (int l = kMw; l < nw; ++l)
+          classify(l, dv.mbuf[((int64_t)s * Lq + l) * dv.ncap + ii[u]]);
+      } else {
+        for (int l = 0; l < nw; ++l) classify(l, Mof(u, l));
       }
     }
     if (below[u] | bnd[u]) {  // sparse: a few lanes per block
       slot[u] = (int)atomicAdd(&nc, 1u);
       cid[slot[u]] = (int32_t)(ii[u] - i0);
       if (below[u]) atomicAdd(&nrl, 1u);
-      for (int l = 0; l < L; ++l) {
+      for (int l = 0; l < nw; ++l) {
         if ((below[u] >> l) & 1u) atomicAdd(&ccount[l], 1u);
         if ((bnd[u] >> l) & 1u) atomicAdd(&bcount[l], 1u);
       }
@@ -583,9 +289,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
 
   // 3. one device atomic per list for the block, consumed after the scoring
   uint32_t my_c = 0, my_b = 0, my_r = 0;
-  if (tid < L) {
-    my_c = ccount[tid] ? atomicAdd(&dv.cand_count[s * Lq + lo + tid], ccount[tid]) : 0u;
-    my_b = bcount[tid] ? atomicAdd(&dv.bnd_count[s * Lq + lo + tid], bcount[tid]) : 0u;
+  if (tid < nw) {
+    my_c = ccount[tid] ? atomicAdd(&dv.cand_count[s * Lq + tid], ccount[tid]) : 0u;
+    my_b = bcount[tid] ? atomicAdd(&dv.bnd_count[s * Lq + tid], bcount[tid]) : 0u;
   }
   if (tid == 64) my_r = nrl ? atomicAdd(&dv.rr_count[s], nrl) : 0u;
 
@@ -618,7 +324,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
   }
 
   // 5. the appends
-  if (tid < L) {
+  if (tid < nw) {
     cbase[tid] = my_c;
     bbase[tid] = my_b;
     ccount[tid] = 0;
@@ -643,16 +349,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CollectShape
       dv.rr_id[o] = i;
       dv.rr_pg[o] = pg;
     }
-    for (int l = 0; l < L; ++l) {
+    for (int l = 0; l < nw; ++l) {
       if ((below[u] >> l) & 1u)
-        dv.cand[((int64_t)s * Lq + lo + l) * dv.k0 + cbase[l] + atomicAdd(&ccount[l], 1u)] = i;
+        dv.cand[((int64_t)s * Lq + l) * dv.k0 + cbase[l] + atomicAdd(&ccount[l], 1u)] = i;
       if ((bnd[u] >> l) & 1u) {
-        const int64_t o = ((int64_t)s * Lq + lo + l) * dv.ncap + bbase[l] + atomicAdd(&bcount[l], 1u);
+        const int64_t o = ((int64_t)s * Lq + l) * dv.ncap + bbase[l] + atomicAdd(&bcount[l], 1u);
         // the 512-thread shape (80 registers) reads M again (L2-hot) rather
         // than keep its registers over the scoring, which would spill them
         uint32_t Mx;
         if constexpr (NT == 512)
-          Mx = dv.mbuf[((int64_t)s * Lq + lo + l) * dv.ncap + iu];
+          Mx = dv.mbuf[((int64_t)s * Lq + l) * dv.ncap + iu];
         else
           Mx = Mof(u, l);
         dv.bnd[o] = ((unsigned long long)Mx << 32) | (uint32_t)i;
@@ -1756,10 +1462,10 @@ template <int DT, bool LH, int R, int NT>
 static void launch_scan(const Dev &dv, int64_t n, dim3 grid, const void *q, const void *k_new,
                         const void *v_new, hipStream_t st) {
   if (dv.Gq > 1)
-    hipLaunchKernelGGL((k_qscan<DT, LH, R, NT, true>), grid, dim3(NT), 0, st, dv, n, q, k_new,
+    hipLaunchKernelGGL((k_qscan<DT, LH, R, NT, true, 1>), grid, dim3(NT), 0, st, dv, n, q, k_new,
                        v_new, dv.Gq);
   else
-    hipLaunchKernelGGL((k_qscan<DT, LH, R, NT, false>), grid, dim3(NT), 0, st, dv, n, q, k_new,
+    hipLaunchKernelGGL((k_qscan<DT, LH, R, NT, false, 1>), grid, dim3(NT), 0, st, dv, n, q, k_new,
                        v_new, 1);
 }
 
@@ -1778,35 +1484,55 @@ static void launch_scan_r(const Dev &dv, int64_t n, dim3 grid, const void *q,
   }
 }
 
-// Scan and collect over n tokens with NT-thread blocks of 2 * NT tokens.  The
-// GQA max mode's passes (one per head) share each launch: the scan's grid
-// holds every head's blocks, then the visit-budget passes run per head, then
-// one collect covers every head's walks.
-template <int DT, int NT>
-static void scan_collect(const Dev &dv, int64_t n, bool bounded, uint32_t k1, const void *q,
-                         const void *k_new, const void *v_new, hipStream_t st, Timer *tm) {
+// Grid of the scan and the collect: x streams (consecutive blocks take
+// different streams, so with S a multiple of 8 a stream's blocks share an
+// XCD), y token ranges of 2 * NT (at most 2^22 tokens per stream under the
+// page-capacity limit: 4,096 ranges), z the scan's passes.
+template <int NT>
+static dim3 range_grid(const Dev &dv, int64_t n, int passes) {
   const int64_t nrange = (n + 2 * NT - 1) / (2 * NT);
-  // x: streams (consecutive blocks take different streams, so with S a
-  // multiple of 8 a stream's blocks share an XCD), y: token ranges (at most
-  // 2^22 tokens per stream under the page-capacity limit: 4,096 ranges), z:
-  // passes
-  const dim3 grid((unsigned)dv.S, (unsigned)max(nrange, (int64_t)1), (unsigned)dv.Gq);
+  return dim3((unsigned)dv.S, (unsigned)max(nrange, (int64_t)1), (unsigned)passes);
+}
+
+// The scan in NT-thread blocks of 2 * NT tokens, one pass per head in the
+// GQA max mode (the mean mode has one).
+template <int DT, int NT>
+static void launch_scan_nt(const Dev &dv, int64_t n, const void *q, const void *k_new,
+                           const void *v_new, hipStream_t st) {
+  const dim3 grid = range_grid<NT>(dv, n, dv.Gq);
   if (dv.L <= 6)
     launch_scan_r<DT, true, NT>(dv, n, grid, q, k_new, v_new, st);
   else
     launch_scan_r<DT, false, NT>(dv, n, grid, q, k_new, v_new, st);
-  timer_mark(tm, KID_QSCAN, st);
-  if (bounded) {
-    for (int head = 0; head < dv.Gq; ++head)
-      (void)launch_visit_budget(dv, n, k1, head, st);  // a launch error stays for the caller's check
-    timer_mark(tm, KID_VISIT, st);
-  }
-  if (n > 0) {
-    const size_t qbytes = (size_t)(dv.gmax ? dv.g : 1) * 128 * sizeof(float);
-    hipLaunchKernelGGL((k_qcollect<DT, NT>), dim3(grid), dim3(NT), qbytes, st, dv, n, bounded, q,
-                       dv.Gq);
-    timer_mark(tm, KID_QCOLLECT, st);
-  }
+}
+
+// The collect in NT-thread blocks of 2 * NT tokens, every walk of a stream
+// in each block.
+template <int DT, int NT>
+static void launch_collect(const Dev &dv, int64_t n, bool bounded, const void *q,
+                           hipStream_t st) {
+  const dim3 grid = range_grid<NT>(dv, n, 1);
+  const size_t qbytes = (size_t)(dv.gmax ? dv.g : 1) * 128 * sizeof(float);
+  if (dv.Lq > 8)
+    hipLaunchKernelGGL((k_qcollect<DT, NT, true>), grid, dim3(NT), qbytes, st, dv, n, bounded, q);
+  else
+    hipLaunchKernelGGL((k_qcollect<DT, NT, false>), grid, dim3(NT), qbytes, st, dv, n, bounded, q);
+}
+
+// Block shape for `blocks(nt)` blocks of nt threads: 512 by default; when
+// 512-thread blocks would not all get a CU of their own, the smallest of 640,
+// 768 and 1024 that does.
+template <typename Blocks, typename Launch>
+static void by_shape(int64_t cus, Blocks blocks, Launch launch) {
+  auto fits = [&](int nt) { return blocks(nt) <= cus; };
+  if (fits(512) || !fits(1024))
+    launch(std::integral_constant<int, 512>());
+  else if (fits(640))
+    launch(std::integral_constant<int, 640>());
+  else if (fits(768))
+    launch(std::integral_constant<int, 768>());
+  else
+    launch(std::integral_constant<int, 1024>());
 }
 
 // The query over n tokens (token n - 1 inserted by the scan when k_new is
@@ -1834,15 +1560,25 @@ static void query_tail(const Dev &dv, int64_t n, int64_t k1, int32_t *page_ids,
   // the entries a walk may visit: its budget, else all m * n
   const unsigned long long vlimit = bounded ? (unsigned long long)k1 : (unsigned long long)dv.m * n;
   const int64_t cus = dv.ncu;
-  auto fits = [&](int nt) { return dv.S * dv.Gq * ((n + 2 * nt - 1) / (2 * nt)) <= cus; };
-  if (fits(512) || !fits(1024))
-    scan_collect<DT, 512>(dv, n, bounded, (uint32_t)k1, q, k_new, v_new, st, tm);
-  else if (fits(640))
-    scan_collect<DT, 640>(dv, n, bounded, (uint32_t)k1, q, k_new, v_new, st, tm);
-  else if (fits(768))
-    scan_collect<DT, 768>(dv, n, bounded, (uint32_t)k1, q, k_new, v_new, st, tm);
-  else
-    scan_collect<DT, 1024>(dv, n, bounded, (uint32_t)k1, q, k_new, v_new, st, tm);
+  auto ranges = [&](int nt) { return (int64_t)dv.S * ((n + 2 * nt - 1) / (2 * nt)); };
+  // the scan: the GQA max mode's heads in one block when the group allows
+  // it, else one pass per head
+  if (!launch_scan_heads(dv, n, q, k_new, v_new, st))
+    by_shape(cus, [&](int nt) { return ranges(nt) * dv.Gq; }, [&](auto nt) {
+      launch_scan_nt<DT, decltype(nt)::value>(dv, n, q, k_new, v_new, st);
+    });
+  timer_mark(tm, KID_QSCAN, st);
+  if (bounded) {
+    for (int head = 0; head < dv.Gq; ++head)
+      (void)launch_visit_budget(dv, n, (uint32_t)k1, head, st);  // a launch error stays for the caller's check
+    timer_mark(tm, KID_VISIT, st);
+  }
+  if (n > 0) {
+    by_shape(cus, ranges, [&](auto nt) {
+      launch_collect<DT, decltype(nt)::value>(dv, n, bounded, q, st);
+    });
+    timer_mark(tm, KID_QCOLLECT, st);
+  }
   if (dv.Lq * dv.k0 > kMaxCand)
     hipLaunchKernelGGL(k_qfinal_big<DT>, dim3(dv.S), dim3(kFinalThreads), 0, st, dv, n, bounded,
                        page_ids, n_pages, topk_ids, stats, vlimit);

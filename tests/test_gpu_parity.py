@@ -1170,6 +1170,12 @@ def test_blocked_dot_order_cases(B):
     dict(S=2, n=2600, g=3, p=8, k=64, m=3, L=3, d=64, dtype="f32", seed=203),
     dict(S=2, n=4000, g=2, p=16, k=128, m=4, L=2, k1=5000, seed=204),     # bounded walks
     dict(S=1, n=150, g=4, p=16, k=256, m=4, L=2, seed=205),               # fewer tokens than k0
+    # every head in one scan block: 48 directions (three code rounds), 16 walks
+    dict(S=2, n=7001, g=4, p=16, k=64, m=12, L=4, seed=208),
+    # 60 directions, 12 walks (the two-head block's limit)
+    dict(S=3, n=4500, g=2, p=16, k=128, m=10, L=6, seed=209),
+    # 1024-thread scan blocks, more of them than the device holds at once
+    dict(S=96, n=6000, g=4, p=16, k=64, m=4, L=4, seed=210, check=(0, 47, 95)),
 ])
 def test_gqa_max(B, case):
     """GQA max mode: every head walks every composite with its own query codes,
