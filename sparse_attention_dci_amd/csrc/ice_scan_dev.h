@@ -97,7 +97,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(GH == 1 ? 6 
   __shared__ ScanShared sm;
   __shared__ float ud[W];
   __shared__ int32_t qc[GH * kMaxMl], nc[kMaxMl];
-  __shared__ uint32_t blim[kWalks];
+  __shared__ int32_t blim[kWalks];
   __shared__ __attribute__((aligned(16))) float qkv[GH * 128], kv[128];
   __shared__ double zs[GH * kMaxMl], rs[kMaxMl];
   __shared__ double qsq_s[GH], ksq_s;
@@ -247,10 +247,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(GH == 1 ? 6 
   // 2. M per token and walk.  Composite boundaries depend on the code
   // position only, so every branch but the ragged tail's is uniform.
   const int64_t i0 = r * kScanTpb, i1 = min(i0 + kScanTpb, n);
-  const uint32_t ntok = (uint32_t)(i1 > i0 ? i1 - i0 : 0);
   const int64_t ia = i0 + 128 * w + lane, ib = ia + 64;
   const int64_t iv = min(i1, nold);  // the new token is added after the walk
   const bool va = ia < iv, vb = ib < iv;
+  // the tokens each of the block's histograms counts: its range's indexed
+  // tokens, and in the block of range 0 the new token
+  const uint32_t ncount = (uint32_t)(iv > i0 ? iv - i0 : 0) + (proj ? 1u : 0u);
   int32_t Ma[GH], Mb[GH];
 #pragma unroll
   for (int h = 0; h < GH; ++h) Ma[h] = Mb[h] = 0;
@@ -327,18 +329,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(GH == 1 ? 6 
   }
 
   // 3. flush the block's histogram.  The k0-th smallest M of the stream is
-  // never in a higher bin than the k0-th smallest of a block holding at least
-  // k0 tokens, so every bin up to the global threshold bin still receives
-  // every block's count.
+  // never in a higher bin than the k0-th smallest of a block that counted at
+  // least k0 tokens, so every bin up to the global threshold bin still
+  // receives every block's count; a block that counted fewer adds its bins up
+  // to its largest M's (all it holds).
   if (LDS_HIST) {
     lds_barrier();
+    const uint32_t tgt = min(ncount, (uint32_t)max(dv.k0, 0));
     for (int l2 = w; l2 < nw; l2 += NT / 64) {
-      uint32_t bb = kHistBins - 1, bl;
-      if (ntok >= (uint32_t)dv.k0 && dv.k0 > 0) {  // the low bins first (almost always there)
+      int32_t lim = -1;  // no count to add
+      if (tgt > 0) {  // the low bins first (almost always there)
+        uint32_t bb, bl;
         const uint4 v = reinterpret_cast<const uint4 *>(hist + l2 * kHistBins)[lane];
-        if (!wave_find_bin_low(v, dv.k0, bb, bl)) wave_find_bin(hist + l2 * kHistBins, dv.k0, bb, bl);
+        if (!wave_find_bin_low(v, tgt, bb, bl)) wave_find_bin(hist + l2 * kHistBins, tgt, bb, bl);
+        lim = (int32_t)bb;
       }
-      if (lane == 0) blim[l2] = bb;
+      if (lane == 0) blim[l2] = lim;
     }
     lds_barrier();
     if constexpr (GH == 1) {  // every thread takes bin tid of each walk in turn
