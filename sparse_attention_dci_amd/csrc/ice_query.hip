@@ -10,9 +10,10 @@
 // visits 60-85% of all list entries before k0 tokens complete, so it would
 // touch most of them anyway) followed by an exact selection:
 //
-//   k_qscan     the query codes (fp32 GQA mean, fp64 projection; in a
-//               decode step also the new token's insert), then M_i for every
-//               token and composite and a histogram of the top 11 bits of M_i;
+//   k_qscan     (ice_scan_dev.h) the query codes (fp32 GQA mean, fp64
+//               projection; in a decode step also the new token's insert),
+//               then M_i for every token and walk and a histogram of the top
+//               11 bits of M_i;
 //   k_qcollect  tokens in bins below the k0-th smallest bin b* are
 //               candidates, tokens in bin b* are parked with their (M_i, i)
 //               key; both kinds are scored exactly (fp64, ascending element

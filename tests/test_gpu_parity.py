@@ -1176,6 +1176,12 @@ def test_blocked_dot_order_cases(B):
     dict(S=3, n=4500, g=2, p=16, k=128, m=10, L=6, seed=209),
     # 1024-thread scan blocks, more of them than the device holds at once
     dict(S=96, n=6000, g=4, p=16, k=64, m=4, L=4, seed=210, check=(0, 47, 95)),
+    # 24 and 32 walks: one scan pass per head, the collect's walks past its
+    # 16 register slots read from memory
+    dict(S=2, n=3000, g=4, p=16, k=64, m=3, L=6, seed=211),
+    dict(S=2, n=2500, g=8, p=16, k=32, m=2, L=4, seed=212),
+    # bounded walks with every head in one scan block (12 walks)
+    dict(S=2, n=4000, g=4, p=16, k=128, m=4, L=3, k1=3000, seed=213),
 ])
 def test_gqa_max(B, case):
     """GQA max mode: every head walks every composite with its own query codes,
