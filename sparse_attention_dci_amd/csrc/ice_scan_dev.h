@@ -33,8 +33,9 @@ __device__ __forceinline__ int32_t ld_code(__amdgpu_buffer_rsrc_t r, uint32_t of
 // later right after it is used.  R = ceil(mL / kPipe) is a template
 // parameter, so the walk over code positions is straight-line code and every
 // wait covers exactly the loads it needs.  The histogram lives in LDS when
-// L <= 6, and only the bins at or below the block's own k0-th bin are added to
-// the global one; with L > 6 every count goes straight to global.
+// L <= 6, and only the bins at or below the block's own k0-th bin (its
+// largest bin when it counted fewer than k0 tokens) are added to the global
+// one; with L > 6 every count goes straight to global.
 //
 // Every block first derives the query codes itself (the directions staged in
 // LDS, the arithmetic of ice_step_dev.h), so no prep kernel sits on the
