@@ -475,8 +475,8 @@ def main():
     kernels = {}
     fused = "attn" not in avg_us
     for k, us in avg_us.items():
-        # a layer step's bytes over its launches of the kernel (the GQA max mode
-        # runs the scan and the collect once per head)
+        # a layer step's bytes over its launches of the kernel (a kernel
+        # launched more than once per layer step shares them)
         per_step = per_kernel[k][1] / float(args.steps * layers_per_step)
         alg = algorithmic_bytes(w, k, visits, n_cand, attended, fused) / max(per_step, 1.0)
         kernels[k] = {"avg_us": round(us, 3), "alg_bytes": int(alg),
