@@ -613,7 +613,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
     const uint32_t incl = wave_incl_scan(v);
     if (lane <= L) sh.boff[lane] = incl - v;
     if (lane == 0) {
-      sh.nu = dv.gmax ? 0u : nrr;  // max mode: counted as the union is deduplicated
+      sh.nu = nrr;
       sh.ntie = 0;
     }
   }
@@ -625,32 +625,17 @@ __global__ __launch_bounds__(kFinalThreads) void k_qfinal(Dev dv, int64_t n, boo
 
   // B. the scored below-bin candidates and, when they fit, the boundary
   // entries (a composite's entries past the prefetched ones are loaded here)
-  if (!dv.gmax) {  // one pass: the rerank list holds every token once
+  // the rerank list holds every token once: the collect block that holds a
+  // token appends it once, in however many walks it is a candidate (the GQA
+  // max mode's g * L walks included)
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const uint32_t x = tid + kFinalThreads * j;
-      if (x < nrr) {
-        mark(pid[j]);
-        sh.sid[x] = pid[j];
-        sh.skey[x] = pkey[j];
-        sh.spg[x] = ppg[j];
-      }
-    }
-  } else {  // the heads' passes repeat tokens: the first of each joins the union
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const uint32_t x = tid + kFinalThreads * j;
-      const bool fresh = x < nrr && mark(pid[j]);
-      const unsigned long long bal = __ballot(fresh);
-      uint32_t base = 0;
-      if (lane == 0 && bal) base = atomicAdd(&sh.nu, (uint32_t)popc64(bal));
-      base = (uint32_t)__shfl((int)base, 0);
-      if (fresh) {
-        const uint32_t pos = base + (uint32_t)popc64(bal & lanemask_lt());
-        sh.sid[pos] = pid[j];
-        sh.skey[pos] = pkey[j];
-        sh.spg[pos] = ppg[j];
-      }
+  for (int j = 0; j < kPer; ++j) {
+    const uint32_t x = tid + kFinalThreads * j;
+    if (x < nrr) {
+      mark(pid[j]);
+      sh.sid[x] = pid[j];
+      sh.skey[x] = pkey[j];
+      sh.spg[x] = ppg[j];
     }
   }
   if (bnd_lds) {
