@@ -1401,8 +1401,8 @@ def test_merge_lists_tail_limit(B):
 
 # ---------------------------------------------------------------- reuse steps
 
-@pytest.mark.parametrize("r", [1, 3])
-def test_reuse_schedule(B, r):
+@pytest.mark.parametrize("r,gqa", [(1, "mean"), (3, "mean"), (3, "max")])
+def test_reuse_schedule(B, r, gqa):
     """A decode loop that queries every r steps and reuses the last selection in
     between (ice_decode_step_reuse): every step's attention equals the oracle
     attending over the same pages after the same inserts, reuse steps equal
@@ -1413,9 +1413,10 @@ def test_reuse_schedule(B, r):
     K, V, _, _ = _inputs(S, n + steps, d, g, 24, 501, "bf16")
     U = W.directions(m * L, d, 501, "bf16").to(dev)
     mk = lambda: B.Index(K[:, :n].contiguous().to(dev), V[:, :n].contiguous().to(dev), U,
-                         page_size=p, budget_k=k, m=m, L=L, gqa_group=g, capacity=n + steps)
+                         page_size=p, budget_k=k, m=m, L=L, gqa_group=g, capacity=n + steps,
+                         gqa_mode=gqa)
     a, b = mk(), mk()
-    prm = oracle.Params(d=d, p=p, k=k, m=m, L=L, g=g)
+    prm = oracle.Params(d=d, p=p, k=k, m=m, L=L, g=g, gqa_max=gqa == "max")
     sts = [oracle.OracleStream(prm, _np(K[s, :n]), _np(V[s, :n]), _np(U), n_cap=n + steps)
            for s in range(S)]
     gen = torch.Generator().manual_seed(41)
