@@ -59,15 +59,26 @@ __global__ __launch_bounds__(kStatsThreads) void k_qstats(Dev dv, int64_t n,
     const int64_t ist = is[l];
     const int jst = js[l];
     const int h = l / Lc, cmp = l % Lc;
+    constexpr int U = kStatsTpb / kStatsThreads;  // tokens per thread
+    const int64_t ilast = n > 0 ? n - 1 : 0;  // a valid address for every lane
     uint32_t c = 0;
+    // list by list, the thread's U codes requested together (clamped
+    // addresses; tokens past n count nothing)
+#pragma unroll 2
+    for (int j = 0; j < m; ++j) {
+      const int t = cmp * m + j;
+      const int32_t qv = qc[h * mL + t];
+      int32_t cd[U];
 #pragma unroll
-    for (int u = 0; u < kStatsTpb / kStatsThreads; ++u) {
-      const int64_t i = i0 + tid + (int64_t)kStatsThreads * u;
-      if (i >= n) break;
-      for (int j = 0; j < m; ++j) {
-        const int t = cmp * m + j;
-        const uint32_t dd = absdiff(dv.codes[code_index(dv.ntile, mL, s, i, t)], qc[h * mL + t]);
-        c += dd < M || (dd == M && (i < ist || (i == ist && j <= jst)));
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = min(i0 + tid + (int64_t)kStatsThreads * u, ilast);
+        cd[u] = dv.codes[code_index(dv.ntile, mL, s, i, t)];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = i0 + tid + (int64_t)kStatsThreads * u;
+        const uint32_t dd = absdiff(cd[u], qv);
+        c += i < n && (dd < M || (dd == M && (i < ist || (i == ist && j <= jst))));
       }
     }
     const uint32_t tot = wave_incl_scan(c);
