@@ -17,8 +17,8 @@
 
 namespace ice {
 
-constexpr int kStatsThreads = 256;
-constexpr int kStatsTpb = 1024;  // tokens per block (four per thread)
+constexpr int kStatsThreads = 1024;
+constexpr int kStatsTpb = 1024;  // tokens per block (one per thread: 16 waves keep the loads in flight)
 
 // Grid (ceil(n / kStatsTpb), S).
 __global__ __launch_bounds__(kStatsThreads) void k_qstats(Dev dv, int64_t n,
