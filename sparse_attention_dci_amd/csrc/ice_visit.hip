@@ -19,7 +19,7 @@
 
 namespace ice {
 
-constexpr int kVisitThreads = 256;
+constexpr int kVisitThreads = 1024;  // one token of a 1,024-token range per thread: 16 waves keep the code loads in flight
 constexpr uint32_t kLowMask = (1u << (kHistShift - kHistBits)) - 1u;  // the last 9 bits
 
 // GQA max mode: each kernel serves the walks of one head's pass, walk
